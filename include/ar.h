@@ -1,0 +1,215 @@
+/*
+ * ar.h -- barrier-free fixed-order bf16 AllReduce for tensor-parallel decode,
+ *         MI355X (gfx950), C ABI.
+ *
+ * The operation.  Every tensor-parallel rank holds a partial result; the
+ * AllReduce sums the partial results element by element and gives the full
+ * sum to every rank ("Every Microsecond Counts" write-up, page "微秒必争：英伟达
+ * 与苏黎世联邦理工学院如何突破多GPU通信延迟极限", section "张量并行与AllReduce").
+ * Here each element's sum is a left fold over ranks 0..N-1 in IEEE binary32
+ * started from rank 0's value, rounded once to bfloat16 (round to nearest,
+ * ties to even); every rank's output copy holds the same bits.
+ *
+ * How ranks synchronise.  No global memory barrier is used (same page,
+ * section "全局内存屏障": a barrier before reading and one before the next
+ * overwrite).  Validity travels with the data instead (section "四大核心机制"):
+ *   - LL: 8-byte units {2 bf16, 32-bit flag}; a unit whose flag equals the
+ *     call's flag holds the call's data (item 1, LL);
+ *   - sentinel: receive buffers are pre-filled with the bf16 NaN pattern
+ *     0xFFFF; any other value is data; the receiver re-fills what it read
+ *     (item 2, Sentinel; reset()/resetRange() in section "统一原语与API设计");
+ *   - double buffering: consecutive calls use buffer parity epoch & 1, so a
+ *     receipt of call k from a peer proves the peer finished call k-1
+ *     (item 3, double buffering);
+ *   - LL128-style lines: 128-byte lines of 120 payload bytes and an 8-byte
+ *     flag, the flag written after the payload (item 4 gives the 128-byte
+ *     line; its NVLink atomic-add form has no counterpart here).
+ * Algorithms (section "统一原语与API设计", table of variants): one-shot (every
+ * rank reads all N contributions) below 64 KiB per rank, two-shot
+ * (reduce-scatter then all-gather) above.
+ *
+ * Emulation.  On one GPU the N ranks are disjoint sets of workgroups of one
+ * kernel launch; they exchange data only through staging buffers and flag
+ * words in device memory, reached with device-scope coherent accesses.
+ *
+ * Conventions for every entry point:
+ *   - return value: AR_OK (0) or a negative ar_status code; nothing aborts;
+ *   - device pointers are plain hipMalloc (or torch) allocations on the
+ *     device that was current at ar_init; the caller owns them;
+ *   - one process-wide context; calls come from one host thread.
+ */
+#ifndef TPDC_AR_H
+#define TPDC_AR_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum ar_status {
+    AR_OK = 0,
+    AR_ERR_INVALID = -1,    /* an argument breaks the stated contract */
+    AR_ERR_NOT_INIT = -2,   /* ar_init has not succeeded */
+    AR_ERR_STATE = -3,      /* already initialised / wrong call order */
+    AR_ERR_OOM = -4,        /* device allocation failed */
+    AR_ERR_HIP = -5,        /* a HIP runtime call failed (see ar_last_hip_error) */
+    AR_ERR_TIMEOUT = -6     /* a device poll exceeded the watchdog (ar_get_status) */
+};
+
+enum ar_algo { AR_ALGO_AUTO = 0, AR_ALGO_ONESHOT = 1, AR_ALGO_TWOSHOT = 2 };
+
+enum ar_proto {
+    AR_PROTO_AUTO = 0,
+    AR_PROTO_LL = 1,        /* one-shot only */
+    AR_PROTO_LL128 = 2,     /* one-shot or two-shot */
+    AR_PROTO_SENTINEL = 3,  /* one-shot or two-shot */
+    AR_PROTO_DIRECT = 4     /* one-shot only: read peers' inputs in place after
+                               their per-call arrival flag (large messages) */
+};
+
+#define AR_MAX_RANKS 16
+
+/*
+ * ar_init -- create the context on the current HIP device.
+ *   n_ranks:   number of emulated ranks, 1..16.
+ *   max_elems: largest per-rank element count any later call may use, > 0,
+ *              at most 2^28.
+ * Allocates every protocol's staging (per rank x 2 parities), the flag
+ * sequence word and the status record; zeroes flag words and arms sentinel
+ * buffers with 0xFFFF.  Synchronous.
+ * Errors: AR_ERR_INVALID (bad sizes), AR_ERR_STATE (already initialised),
+ * AR_ERR_OOM, AR_ERR_HIP.
+ */
+int ar_init(int n_ranks, size_t max_elems);
+
+/*
+ * ar_allreduce -- one AllReduce call, enqueued on `stream` (asynchronous).
+ *   rank_bufs: HOST array of n_ranks DEVICE pointers, rank r's bf16 input [n];
+ *              copied by value into the launch, so the host array may be
+ *              reused as soon as the call returns (graph-capture safe).
+ *   out:       DEVICE bf16 [n_ranks][n]; rank r's copy at out + r*n.  Must not
+ *              overlap any input.
+ *   n:         elements per rank, 1..max_elems, a multiple of 8.
+ *   epoch:     call number within the current step: 1 for the first call
+ *              after ar_init / ar_reset / ar_step_end, then previous + 1;
+ *              at most 65535.  Buffer parity is epoch & 1.
+ *   stream:    HIP stream (0 = legacy default stream).
+ * All pointers 16-byte aligned.  Inputs must be finite bf16 values; with the
+ * sentinel protocol an input equal to 0xFFFF breaks the contract (a receiver
+ * would wait for it until the watchdog fires).  Inputs must not be modified
+ * until the call has completed on `stream`.  No allocation, memset or host
+ * synchronisation happens here.
+ * Errors: AR_ERR_NOT_INIT, AR_ERR_INVALID (pointer, size, alignment, aliasing,
+ * epoch sequence), AR_ERR_HIP (launch failure).  Device-side failures
+ * (watchdog) are reported later through ar_get_status.
+ */
+int ar_allreduce(const void *const *rank_bufs, void *out, size_t n,
+                 uint32_t epoch, hipStream_t stream);
+
+/*
+ * ar_allreduce_f32_debug -- the same call, but writes the binary32
+ * accumulators (before the bf16 rounding) to out_f32, DEVICE float
+ * [n_ranks][n].  Same contract otherwise; advances the epoch sequence like
+ * ar_allreduce.
+ */
+int ar_allreduce_f32_debug(const void *const *rank_bufs, float *out_f32,
+                           size_t n, uint32_t epoch, hipStream_t stream);
+
+/*
+ * ar_destroy -- free all staging.  The caller must have synchronised every
+ * stream that used the library.  AR_ERR_NOT_INIT if there is no context.
+ */
+int ar_destroy(void);
+
+/*
+ * ar_set_options -- choose the algorithm and protocol for later calls.
+ * AUTO picks by message size S = 2n bytes per rank: S <= 64 KiB -> one-shot
+ * LL; otherwise two-shot LL128 (section "统一原语与API设计", table of
+ * variants).  LL and DIRECT exist only as one-shot.  AR_ERR_INVALID for an
+ * unknown value or an impossible pair.
+ */
+int ar_set_options(int algo, int proto);
+
+/*
+ * ar_set_launch -- tuning: workgroups per rank (0 = automatic) and threads
+ * per workgroup (64, 128 or 256; 0 = 256).  The workgroups per rank are
+ * capped at each call so that the whole grid is resident at once (every
+ * poll then has a running producer).  AR_ERR_INVALID for unsupported values.
+ */
+int ar_set_launch(int wgs_per_rank, int threads);
+
+/*
+ * ar_set_watchdog -- per-poll time budget in microseconds (default 200000).
+ * A poll that exceeds it records {6, rank, source, flag} in the device status
+ * record and its workgroup stops; the other workgroups of that call stop
+ * polling soon after they see the record.  The record stays until ar_reset;
+ * until then outputs of later calls are undefined.  0 restores the default.
+ */
+int ar_set_watchdog(uint32_t budget_us);
+
+/*
+ * ar_step_end -- close a step of calls (typically one emulated decode step of
+ * 2 x layers calls).  Enqueues one tiny kernel on `stream` that advances the
+ * device flag sequence by the step's call count, so that the flags of a
+ * captured hipGraph's replays never repeat; resets the host epoch counter to
+ * 0.  The step must hold an even number of calls (parity keeps alternating).
+ * Errors: AR_ERR_NOT_INIT, AR_ERR_STATE (odd call count), AR_ERR_HIP.
+ */
+int ar_step_end(hipStream_t stream);
+
+/*
+ * ar_set_delays -- test hook: per (call, rank) start delays.  dev_ns is a
+ * DEVICE uint32 table [calls][n_ranks] of nanoseconds; call with flag f uses
+ * row (f - 1) mod calls.  Every workgroup of rank r spins on the constant
+ * 100 MHz clock for that long before its first step.  NULL disables.  The
+ * table must stay alive while calls use it.
+ */
+int ar_set_delays(const uint32_t *dev_ns, size_t calls);
+
+/*
+ * ar_set_timestamps -- measurement hook: DEVICE uint64 table [slots][2].  Call
+ * with flag f folds min(workgroup start) into [slot][0] and max(workgroup end)
+ * into [slot][1], slot = (f - 1) mod slots, in ticks of the constant 100 MHz
+ * clock.  The caller initialises [.][0] to UINT64_MAX and [.][1] to 0.  NULL
+ * disables (the default; the uninstrumented kernels are used then).
+ */
+int ar_set_timestamps(uint64_t *dev_ts, size_t slots);
+
+/*
+ * ar_get_status -- copy the device status record {code, rank, source, flag}
+ * into out[4] (synchronises the device first).  code is 0 or the positive
+ * value of -AR_ERR_TIMEOUT.  Returns AR_ERR_TIMEOUT if a watchdog fired.
+ */
+int ar_get_status(uint32_t out[4]);
+
+/*
+ * ar_reset -- recovery (the resetRange() of section "统一原语与API设计"):
+ * enqueues kernels on `stream` that zero every flag word, re-arm every
+ * sentinel buffer, clear the status record and restart the flag sequence;
+ * resets the host epoch counter.  Graph-capture safe (no memset nodes).
+ */
+int ar_reset(hipStream_t stream);
+
+/* ar_strerror -- static description of a status code. */
+const char *ar_strerror(int status);
+
+/* ar_last_hip_error -- the hipError_t behind the last AR_ERR_HIP. */
+int ar_last_hip_error(void);
+
+/*
+ * ar_query -- introspection for tests and benchmarks.  key:
+ *   0 n_ranks, 1 max_elems, 2 algorithm a call of n elements would use,
+ *   3 its protocol, 4 workgroups it would launch, 5 threads per workgroup,
+ *   6 resident-workgroup capacity of the device for that kernel, 7 the host
+ *   epoch counter.
+ * Returns the value, or a negative status.
+ */
+long long ar_query(int key, size_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPDC_AR_H */

@@ -1,0 +1,182 @@
+"""ctypes binding of libtpdc_ar.so (names follow include/ar.h).
+
+Argument marshalling only: torch tensors give device pointers and streams;
+every step of the AllReduce runs in the library's HIP kernels.
+"""
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libtpdc_ar.so"
+
+AR_OK = 0
+AR_ERR_INVALID = -1
+AR_ERR_NOT_INIT = -2
+AR_ERR_STATE = -3
+AR_ERR_OOM = -4
+AR_ERR_HIP = -5
+AR_ERR_TIMEOUT = -6
+
+AR_ALGO_AUTO, AR_ALGO_ONESHOT, AR_ALGO_TWOSHOT = 0, 1, 2
+AR_PROTO_AUTO, AR_PROTO_LL, AR_PROTO_LL128, AR_PROTO_SENTINEL, AR_PROTO_DIRECT = 0, 1, 2, 3, 4
+MAX_RANKS = 16
+
+_c_int, _c_u32, _c_size, _c_vp = ctypes.c_int, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes), as declared in include/ar.h
+_SIGS = {
+    "ar_init": (_c_int, [_c_int, _c_size]),
+    "ar_allreduce": (_c_int, [ctypes.POINTER(_c_vp), _c_vp, _c_size, _c_u32, _c_vp]),
+    "ar_allreduce_f32_debug": (_c_int, [ctypes.POINTER(_c_vp), _c_vp, _c_size, _c_u32, _c_vp]),
+    "ar_destroy": (_c_int, []),
+    "ar_set_options": (_c_int, [_c_int, _c_int]),
+    "ar_set_launch": (_c_int, [_c_int, _c_int]),
+    "ar_set_watchdog": (_c_int, [_c_u32]),
+    "ar_step_end": (_c_int, [_c_vp]),
+    "ar_set_delays": (_c_int, [_c_vp, _c_size]),
+    "ar_set_timestamps": (_c_int, [_c_vp, _c_size]),
+    "ar_get_status": (_c_int, [ctypes.POINTER(_c_u32)]),
+    "ar_reset": (_c_int, [_c_vp]),
+    "ar_strerror": (ctypes.c_char_p, [_c_int]),
+    "ar_last_hip_error": (_c_int, []),
+    "ar_query": (ctypes.c_longlong, [_c_int, _c_size]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGS)
+
+_lock = threading.Lock()
+_lib = None
+
+
+class ArError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        msg = "%s failed: %d (%s)" % (fn, code, strerror(code))
+        if code == AR_ERR_HIP and _lib is not None:
+            msg += " hipError=%d" % _lib.ar_last_hip_error()
+        super().__init__(msg)
+
+
+def lib_path():
+    return os.environ.get("TPDC_AR_LIB", os.path.join(HERE, _LIB_NAME))
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = lib_path()
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    "HIP library %s is missing: build it with "
+                    "`python -m tp_decode_comms_amd.build` (or __graft_entry__.build())" % path)
+            # The process must run one HIP runtime: load torch's first so that
+            # the library's libamdhip64 dependency binds to that same copy.
+            import torch  # noqa: F401
+            L = ctypes.CDLL(path)
+            for name, (res, args) in _SIGS.items():
+                f = getattr(L, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = L
+        return _lib
+
+
+def strerror(code):
+    if _lib is None:
+        return str(code)
+    return _lib.ar_strerror(int(code)).decode()
+
+
+def _check(fn, rc):
+    if rc != AR_OK:
+        raise ArError(fn, rc)
+    return rc
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t):
+    return t if isinstance(t, int) else t.data_ptr()
+
+
+def init(n_ranks, max_elems):
+    return _check("ar_init", lib().ar_init(int(n_ranks), int(max_elems)))
+
+
+def destroy():
+    return _check("ar_destroy", lib().ar_destroy())
+
+
+def _rank_array(rank_bufs):
+    ptrs = [_ptr(b) for b in rank_bufs]
+    return (_c_vp * len(ptrs))(*ptrs)
+
+
+def allreduce(rank_bufs, out, n, epoch, stream=None, check=True):
+    """rank_bufs: N bf16 device tensors (or pointers) of >= n elements;
+    out: bf16 device tensor [N, n].  Enqueued on `stream` (default: torch's
+    current stream).  Returns the status code (raises unless check=False)."""
+    rc = lib().ar_allreduce(_rank_array(rank_bufs), _ptr(out), int(n), int(epoch),
+                            _stream_handle(stream))
+    return _check("ar_allreduce", rc) if check else rc
+
+
+def allreduce_f32_debug(rank_bufs, out_f32, n, epoch, stream=None, check=True):
+    rc = lib().ar_allreduce_f32_debug(_rank_array(rank_bufs), _ptr(out_f32), int(n), int(epoch),
+                                      _stream_handle(stream))
+    return _check("ar_allreduce_f32_debug", rc) if check else rc
+
+
+def set_options(algo=AR_ALGO_AUTO, proto=AR_PROTO_AUTO):
+    return _check("ar_set_options", lib().ar_set_options(int(algo), int(proto)))
+
+
+def set_launch(wgs_per_rank=0, threads=0):
+    return _check("ar_set_launch", lib().ar_set_launch(int(wgs_per_rank), int(threads)))
+
+
+def set_watchdog(budget_us=0):
+    return _check("ar_set_watchdog", lib().ar_set_watchdog(int(budget_us)))
+
+
+def step_end(stream=None):
+    return _check("ar_step_end", lib().ar_step_end(_stream_handle(stream)))
+
+
+def set_delays(dev_ns=None, calls=0):
+    p = 0 if dev_ns is None else _ptr(dev_ns)
+    return _check("ar_set_delays", lib().ar_set_delays(p or None, int(calls)))
+
+
+def set_timestamps(dev_ts=None, slots=0):
+    p = 0 if dev_ts is None else _ptr(dev_ts)
+    return _check("ar_set_timestamps", lib().ar_set_timestamps(p or None, int(slots)))
+
+
+def get_status():
+    """Returns (code, rank, source, flag) of the device status record."""
+    buf = (_c_u32 * 4)()
+    rc = lib().ar_get_status(buf)
+    if rc not in (AR_OK, AR_ERR_TIMEOUT):
+        raise ArError("ar_get_status", rc)
+    return tuple(int(x) for x in buf)
+
+
+def reset(stream=None):
+    return _check("ar_reset", lib().ar_reset(_stream_handle(stream)))
+
+
+def query(key, n=0):
+    v = lib().ar_query(int(key), int(n))
+    if v < 0:
+        raise ArError("ar_query", int(v))
+    return int(v)

@@ -1,0 +1,511 @@
+// ar_host.hip -- host side of the C ABI declared in include/ar.h.
+//
+// Owns the single process-wide context: staging for every protocol (per
+// rank x 2 parities), the control block (flag-sequence base, status record,
+// arrival flags), launch geometry, the epoch sequence check and the
+// algorithm/protocol choice of the pages' table of variants ("微秒必争…",
+// section "统一原语与API设计": one-shot below 64 KiB, two-shot from 64 KiB).
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/ar.h"
+#include "ar_kernels.h"
+#include "ar_proto.h"
+
+namespace {
+
+using ar::Launch;
+
+constexpr size_t MAX_ELEMS_LIMIT = size_t(1) << 28;
+constexpr uint32_t DEFAULT_WATCHDOG_US = 200000;
+constexpr size_t ONESHOT_LIMIT_BYTES = 64 * 1024;   // per-rank message size
+
+struct Context {
+    bool live = false;
+    int device = -1;
+    int n_ranks = 0;
+    size_t max_elems = 0;
+    int cu_count = 0;
+    // staging
+    char *ll = nullptr;   size_t ll_stride = 0;
+    char *l128 = nullptr; size_t l128_stride = 0;
+    char *s1 = nullptr;   size_t s1_stride = 0;
+    char *srs = nullptr;  char *sag = nullptr; size_t s2_stride = 0;
+    uint32_t *ctl = nullptr;
+    // options
+    int algo = AR_ALGO_AUTO;
+    int proto = AR_PROTO_AUTO;
+    int wgs_per_rank = 0;
+    int threads = 256;
+    uint32_t watchdog_us = DEFAULT_WATCHDOG_US;
+    const uint32_t *delays = nullptr; size_t delay_rows = 0;
+    uint64_t *ts = nullptr; size_t ts_slots = 0;
+    // sequence
+    uint32_t last_epoch = 0;
+    int capacity[ar::K_COUNT][2] = {};   // resident workgroups, [kind][f32]
+    int cap_threads = 0;
+};
+
+Context g;
+int g_last_hip = 0;
+
+int hip_fail(hipError_t e)
+{
+    g_last_hip = (int)e;
+    return AR_ERR_HIP;
+}
+
+bool debug_enabled()
+{
+    static int v = -1;
+    if (v < 0) {
+        const char *e = getenv("AR_DEBUG");
+        v = (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
+    }
+    return v == 1;
+}
+
+size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+size_t slice_len(size_t n, int n_ranks) { return round_up((n + n_ranks - 1) / n_ranks, 8); }
+
+void free_all()
+{
+    char **bufs[] = {&g.ll, &g.l128, &g.s1, &g.srs, &g.sag};
+    for (char **b : bufs) {
+        if (*b) (void)hipFree(*b);
+        *b = nullptr;
+    }
+    if (g.ctl) (void)hipFree(g.ctl);
+    g.ctl = nullptr;
+}
+
+int alloc(char **p, size_t bytes)
+{
+    hipError_t e = hipMalloc((void **)p, bytes);
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) {
+        *p = nullptr;
+        g_last_hip = (int)e;
+        return AR_ERR_OOM;
+    }
+    if (e != hipSuccess) {
+        *p = nullptr;
+        return hip_fail(e);
+    }
+    return AR_OK;
+}
+
+size_t ll_bytes() { return g.ll_stride * 2 * g.n_ranks; }
+size_t l128_bytes() { return g.l128_stride * 2 * g.n_ranks; }
+size_t s1_bytes() { return g.s1_stride * 2 * g.n_ranks * g.n_ranks; }
+size_t s2_bytes() { return g.s2_stride * 2 * g.n_ranks * g.n_ranks; }
+
+// Zero flags, arm sentinels, clear the control block -- kernels only.
+hipError_t rearm(hipStream_t s)
+{
+    hipError_t e;
+    if ((e = ar::launch_fill((uint32_t *)g.ll, ll_bytes() / 4, 0u, s)) != hipSuccess) return e;
+    if ((e = ar::launch_fill((uint32_t *)g.l128, l128_bytes() / 4, 0u, s)) != hipSuccess) return e;
+    if ((e = ar::launch_fill((uint32_t *)g.s1, s1_bytes() / 4, ar::SENT_WORD, s)) != hipSuccess) return e;
+    if ((e = ar::launch_fill((uint32_t *)g.srs, s2_bytes() / 4, ar::SENT_WORD, s)) != hipSuccess) return e;
+    if ((e = ar::launch_fill((uint32_t *)g.sag, s2_bytes() / 4, ar::SENT_WORD, s)) != hipSuccess) return e;
+    return ar::launch_fill(g.ctl, ar::CTL_WORDS, 0u, s);
+}
+
+int compute_capacity(int threads)
+{
+    for (int k = 0; k < ar::K_COUNT; ++k) {
+        for (int f = 0; f < 2; ++f) {
+            int per_cu = 0;
+            hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, ar::kernel_for(k, g.n_ranks, f == 1), threads, 0);
+            if (e != hipSuccess)
+                return hip_fail(e);
+            g.capacity[k][f] = per_cu * g.cu_count;
+        }
+    }
+    g.cap_threads = threads;
+    return AR_OK;
+}
+
+struct Plan {
+    int kind;
+    uint32_t parts;     // workgroups per rank
+    uint32_t threads;
+    uint32_t slice;
+};
+
+int choose_kind(size_t n, int *kind)
+{
+    const size_t bytes = 2 * n;
+    int algo = g.algo, proto = g.proto;
+    if (algo == AR_ALGO_AUTO) {
+        if (proto == AR_PROTO_LL || proto == AR_PROTO_DIRECT)
+            algo = AR_ALGO_ONESHOT;
+        else
+            algo = bytes <= ONESHOT_LIMIT_BYTES ? AR_ALGO_ONESHOT : AR_ALGO_TWOSHOT;
+    }
+    if (proto == AR_PROTO_AUTO)
+        proto = algo == AR_ALGO_ONESHOT ? AR_PROTO_LL : AR_PROTO_LL128;
+    if (algo == AR_ALGO_ONESHOT) {
+        switch (proto) {
+        case AR_PROTO_LL: *kind = ar::K_ONESHOT_LL; return AR_OK;
+        case AR_PROTO_LL128: *kind = ar::K_ONESHOT_LL128; return AR_OK;
+        case AR_PROTO_SENTINEL: *kind = ar::K_ONESHOT_SENTINEL; return AR_OK;
+        case AR_PROTO_DIRECT: *kind = ar::K_ONESHOT_DIRECT; return AR_OK;
+        }
+    } else {
+        switch (proto) {
+        case AR_PROTO_LL128: *kind = ar::K_TWOSHOT_LL128; return AR_OK;
+        case AR_PROTO_SENTINEL: *kind = ar::K_TWOSHOT_SENTINEL; return AR_OK;
+        }
+    }
+    return AR_ERR_INVALID;
+}
+
+// Workgroups per rank.  Work unit: a lane chunk of 8 elements (LL,
+// sentinel, DIRECT) or a wave-wide LL128 line group of 480 elements.  The
+// whole grid must be resident at once.
+int make_plan(size_t n, bool f32, Plan *p)
+{
+    int rc = choose_kind(n, &p->kind);
+    if (rc != AR_OK)
+        return rc;
+    p->threads = (uint32_t)g.threads;
+    const uint32_t N = (uint32_t)g.n_ranks;
+    p->slice = (uint32_t)slice_len(n, g.n_ranks);
+    uint64_t units, per_wg;
+    switch (p->kind) {
+    case ar::K_ONESHOT_LL128:
+        units = (n + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = p->threads / 64; break;
+    case ar::K_TWOSHOT_LL128:
+        units = (p->slice + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = p->threads / 64; break;
+    case ar::K_TWOSHOT_SENTINEL:
+        units = p->slice / 8; per_wg = p->threads; break;
+    default:
+        units = n / 8; per_wg = p->threads; break;
+    }
+    if (g.cap_threads != (int)p->threads) {
+        rc = compute_capacity((int)p->threads);
+        if (rc != AR_OK)
+            return rc;
+    }
+    const uint32_t cap = (uint32_t)g.capacity[p->kind][f32 ? 1 : 0] / N;
+    if (cap == 0)
+        return AR_ERR_INVALID;
+    uint64_t want = g.wgs_per_rank > 0 ? (uint64_t)g.wgs_per_rank : (units + per_wg - 1) / per_wg;
+    if (want == 0) want = 1;
+    if (want > cap) want = cap;
+    p->parts = (uint32_t)want;
+    return AR_OK;
+}
+
+int check_call(const void *const *rank_bufs, const void *out, size_t out_elem_bytes, size_t n,
+               uint32_t epoch)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    if (rank_bufs == nullptr || out == nullptr)
+        return AR_ERR_INVALID;
+    if (n == 0 || n > g.max_elems || (n % 8) != 0)
+        return AR_ERR_INVALID;
+    if (epoch == 0 || epoch > 0xFFFFu || epoch != g.last_epoch + 1)
+        return AR_ERR_INVALID;
+    const uintptr_t o = (uintptr_t)out;
+    if (o % 16)
+        return AR_ERR_INVALID;
+    const uintptr_t o_end = o + out_elem_bytes * n * (size_t)g.n_ranks;
+    for (int r = 0; r < g.n_ranks; ++r) {
+        const uintptr_t b = (uintptr_t)rank_bufs[r];
+        if (b == 0 || b % 16)
+            return AR_ERR_INVALID;
+        const uintptr_t b_end = b + 2 * n;
+        if (b < o_end && o < b_end)
+            return AR_ERR_INVALID;      // output overlaps an input
+    }
+    return AR_OK;
+}
+
+int do_allreduce(const void *const *rank_bufs, void *out, size_t n, uint32_t epoch,
+                 hipStream_t stream, bool f32)
+{
+    int rc = check_call(rank_bufs, out, f32 ? 4 : 2, n, epoch);
+    if (rc != AR_OK)
+        return rc;
+    Plan p;
+    rc = make_plan(n, f32, &p);
+    if (rc != AR_OK)
+        return rc;
+    Launch a;
+    memset(&a, 0, sizeof a);
+    for (int r = 0; r < g.n_ranks; ++r)
+        a.in[r] = rank_bufs[r];
+    a.out = out;
+    a.ll = g.ll; a.l128 = g.l128; a.s1 = g.s1; a.srs = g.srs; a.sag = g.sag;
+    a.ctl = g.ctl;
+    a.ts = g.ts; a.ts_slots = (uint32_t)g.ts_slots;
+    a.delays = g.delays; a.delay_rows = (uint32_t)g.delay_rows;
+    a.ll_stride = (uint32_t)g.ll_stride; a.l128_stride = (uint32_t)g.l128_stride;
+    a.s1_stride = (uint32_t)g.s1_stride; a.s2_stride = (uint32_t)g.s2_stride;
+    a.n = (uint32_t)n;
+    a.n_ranks = (uint32_t)g.n_ranks;
+    a.epoch = epoch;
+    a.parts = p.parts;
+    a.slice = p.slice;
+    uint64_t ticks = (uint64_t)g.watchdog_us * 100u;   // 100 MHz clock
+    a.watchdog_ticks = (uint32_t)std::min<uint64_t>(ticks, 0xFFFFFFFFu);
+    const uint32_t grid = p.parts * (uint32_t)g.n_ranks;
+    if (debug_enabled())
+        fprintf(stderr, "[ar] n=%zu epoch=%u kind=%d grid=%u threads=%u slice=%u f32=%d\n", n,
+                epoch, p.kind, grid, p.threads, p.slice, (int)f32);
+    hipError_t e = ar::launch_ar(p.kind, f32, a, grid, p.threads, stream);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    g.last_epoch = epoch;
+    return AR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ar_init(int n_ranks, size_t max_elems)
+{
+    if (g.live)
+        return AR_ERR_STATE;
+    if (n_ranks < 1 || n_ranks > AR_MAX_RANKS || max_elems == 0 || max_elems > MAX_ELEMS_LIMIT)
+        return AR_ERR_INVALID;
+    hipError_t e = hipGetDevice(&g.device);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    e = hipDeviceGetAttribute(&g.cu_count, hipDeviceAttributeMultiprocessorCount, g.device);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    g.n_ranks = n_ranks;
+    g.max_elems = round_up(max_elems, 8);
+    const size_t me = g.max_elems;
+    g.ll_stride = round_up(me * 4, 256);
+    g.l128_stride = round_up((me + ar::L128_ELEMS - 1) / ar::L128_ELEMS * ar::L128_BYTES, 256);
+    g.s1_stride = round_up(me * 2, 256);
+    g.s2_stride = round_up(slice_len(me, n_ranks) * 2, 256);
+    int rc;
+    if ((rc = alloc(&g.ll, ll_bytes())) != AR_OK ||
+        (rc = alloc(&g.l128, l128_bytes())) != AR_OK ||
+        (rc = alloc(&g.s1, s1_bytes())) != AR_OK ||
+        (rc = alloc(&g.srs, s2_bytes())) != AR_OK ||
+        (rc = alloc(&g.sag, s2_bytes())) != AR_OK ||
+        (rc = alloc((char **)&g.ctl, ar::CTL_WORDS * 4)) != AR_OK) {
+        free_all();
+        return rc;
+    }
+    e = rearm(0);
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        free_all();
+        return hip_fail(e);
+    }
+    g.algo = AR_ALGO_AUTO; g.proto = AR_PROTO_AUTO;
+    g.wgs_per_rank = 0; g.threads = 256;
+    g.watchdog_us = DEFAULT_WATCHDOG_US;
+    g.delays = nullptr; g.delay_rows = 0;
+    g.ts = nullptr; g.ts_slots = 0;
+    g.last_epoch = 0;
+    g.cap_threads = 0;
+    g.live = true;
+    rc = compute_capacity(g.threads);
+    if (rc != AR_OK) {
+        g.live = false;
+        free_all();
+        return rc;
+    }
+    if (debug_enabled())
+        fprintf(stderr, "[ar] init N=%d max_elems=%zu CUs=%d staging=%zu B\n", n_ranks, me,
+                g.cu_count, ll_bytes() + l128_bytes() + s1_bytes() + 2 * s2_bytes());
+    return AR_OK;
+}
+
+int ar_destroy(void)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    free_all();
+    g.live = false;
+    return AR_OK;
+}
+
+int ar_allreduce(const void *const *rank_bufs, void *out, size_t n, uint32_t epoch,
+                 hipStream_t stream)
+{
+    return do_allreduce(rank_bufs, out, n, epoch, stream, false);
+}
+
+int ar_allreduce_f32_debug(const void *const *rank_bufs, float *out_f32, size_t n, uint32_t epoch,
+                           hipStream_t stream)
+{
+    return do_allreduce(rank_bufs, out_f32, n, epoch, stream, true);
+}
+
+int ar_set_options(int algo, int proto)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    if (algo < AR_ALGO_AUTO || algo > AR_ALGO_TWOSHOT)
+        return AR_ERR_INVALID;
+    if (proto < AR_PROTO_AUTO || proto > AR_PROTO_DIRECT)
+        return AR_ERR_INVALID;
+    if (algo == AR_ALGO_TWOSHOT && (proto == AR_PROTO_LL || proto == AR_PROTO_DIRECT))
+        return AR_ERR_INVALID;
+    g.algo = algo;
+    g.proto = proto;
+    return AR_OK;
+}
+
+int ar_set_launch(int wgs_per_rank, int threads)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    if (threads == 0)
+        threads = 256;
+    if (wgs_per_rank < 0 || !(threads == 64 || threads == 128 || threads == 256))
+        return AR_ERR_INVALID;
+    g.wgs_per_rank = wgs_per_rank;
+    g.threads = threads;
+    return AR_OK;
+}
+
+int ar_set_watchdog(uint32_t budget_us)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    g.watchdog_us = budget_us ? budget_us : DEFAULT_WATCHDOG_US;
+    return AR_OK;
+}
+
+int ar_step_end(hipStream_t stream)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    if (g.last_epoch % 2 != 0)
+        return AR_ERR_STATE;
+    if (g.last_epoch > 0) {
+        hipError_t e = ar::launch_step_end(g.ctl, g.last_epoch, g.ll, ll_bytes(), g.l128,
+                                           l128_bytes(), stream);
+        if (e != hipSuccess)
+            return hip_fail(e);
+    }
+    g.last_epoch = 0;
+    return AR_OK;
+}
+
+int ar_set_delays(const uint32_t *dev_ns, size_t calls)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    if (dev_ns != nullptr && (calls == 0 || calls > 0xFFFFFFFFu / (size_t)g.n_ranks / 4))
+        return AR_ERR_INVALID;
+    g.delays = dev_ns;
+    g.delay_rows = dev_ns ? calls : 0;
+    return AR_OK;
+}
+
+int ar_set_timestamps(uint64_t *dev_ts, size_t slots)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    if (dev_ts != nullptr && (slots == 0 || slots > 0xFFFFFFFFu))
+        return AR_ERR_INVALID;
+    g.ts = dev_ts;
+    g.ts_slots = dev_ts ? slots : 0;
+    return AR_OK;
+}
+
+int ar_get_status(uint32_t out[4])
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    if (out == nullptr)
+        return AR_ERR_INVALID;
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess)
+        return hip_fail(e);
+    e = hipMemcpy(out, g.ctl + ar::CTL_STATUS, 16, hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    return out[0] == ar::STATUS_TIMEOUT ? AR_ERR_TIMEOUT : AR_OK;
+}
+
+int ar_reset(hipStream_t stream)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    hipError_t e = rearm(stream);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    g.last_epoch = 0;
+    return AR_OK;
+}
+
+const char *ar_strerror(int status)
+{
+    switch (status) {
+    case AR_OK: return "ok";
+    case AR_ERR_INVALID: return "invalid argument";
+    case AR_ERR_NOT_INIT: return "library not initialised";
+    case AR_ERR_STATE: return "invalid call order or state";
+    case AR_ERR_OOM: return "device out of memory";
+    case AR_ERR_HIP: return "HIP runtime error";
+    case AR_ERR_TIMEOUT: return "device poll exceeded the watchdog";
+    default: return "unknown status";
+    }
+}
+
+int ar_last_hip_error(void) { return g_last_hip; }
+
+long long ar_query(int key, size_t n)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    Plan p;
+    switch (key) {
+    case 0: return g.n_ranks;
+    case 1: return (long long)g.max_elems;
+    case 2:
+    case 3:
+    case 4:
+    case 5: {
+        if (n == 0 || n > g.max_elems || n % 8)
+            return AR_ERR_INVALID;
+        int rc = make_plan(n, false, &p);
+        if (rc != AR_OK)
+            return rc;
+        if (key == 2)
+            return (p.kind == ar::K_TWOSHOT_LL128 || p.kind == ar::K_TWOSHOT_SENTINEL)
+                       ? AR_ALGO_TWOSHOT : AR_ALGO_ONESHOT;
+        if (key == 3) {
+            switch (p.kind) {
+            case ar::K_ONESHOT_LL: return AR_PROTO_LL;
+            case ar::K_ONESHOT_DIRECT: return AR_PROTO_DIRECT;
+            case ar::K_ONESHOT_SENTINEL:
+            case ar::K_TWOSHOT_SENTINEL: return AR_PROTO_SENTINEL;
+            default: return AR_PROTO_LL128;
+            }
+        }
+        if (key == 4) return (long long)p.parts * g.n_ranks;
+        return p.threads;
+    }
+    case 6: {
+        int kind;
+        if (n == 0 || choose_kind(n, &kind) != AR_OK) return AR_ERR_INVALID;
+        return g.capacity[kind][0];
+    }
+    case 7: return g.last_epoch;
+    default: return AR_ERR_INVALID;
+    }
+}
+
+}  // extern "C"
