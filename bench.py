@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Benchmark of the barrier-free fixed-order bf16 AllReduce on one MI355X.
+
+Headline (one JSON line on stdout):
+  value  = AllReduce microseconds per call, p50, for 8 emulated ranks x
+           [1 x 8192] bf16 (16 KiB per rank), one-shot LL, 160 back-to-back
+           calls per emulated decode step captured in one hipGraph;
+  plus   = effective HBM GB/s for 8 ranks x [256 x 8192] bf16 (4 MiB per
+           rank), algorithmic bytes 2*N*S per call, with the roofline of that
+           kernel against the 8 TB/s HBM3E peak.
+A step is one replay of the 160-call graph (one emulated 80-layer decode
+step, two AllReduces per layer).
+
+Timing: CUDA/HIP events on the stream the graph or kernel runs on, around
+each replay (or call); an instrumented pass additionally records, per call,
+the earliest workgroup start and latest workgroup end on the 100 MHz
+constant clock, giving per-call intervals end(k) - end(k-1) (launch gap
+included) and spans end(k) - start(k).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
+"""
+import argparse
+import json
+import os
+import platform
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "AllReduce µs/call p50 (16KB/rank) + effective HBM GB/s (4MB/rank), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+CLOCK_HZ = 100e6
+CALLS_PER_STEP = 160
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def pct(a, q):
+    return float(np.percentile(np.asarray(a, dtype=np.float64), q))
+
+
+def to_dev(torch, arr):
+    return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16).copy()).to("cuda:0")
+
+
+# --------------------------------------------------------------------- C2
+def bench_latency(torch, ar, steps, warmup):
+    import synth
+    N, n = 8, 8192
+    sets = [synth.input_set(2, s) for s in range(4)]
+    ins = [[to_dev(torch, d[r]) for r in range(N)] for d in sets]
+    outs = [torch.empty((N, n), dtype=torch.int16, device="cuda:0") for _ in range(CALLS_PER_STEP)]
+    ar.init(N, n)
+    ar.set_options(ar.AR_ALGO_ONESHOT, ar.AR_PROTO_LL)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def capture():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for k in range(CALLS_PER_STEP):
+                    ar.allreduce(ins[k % 4], outs[k], n, k + 1, stream=stream)
+                ar.step_end(stream=stream)
+        return g
+
+    g = capture()
+    # uninstrumented replays, events around each
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for s in range(steps):
+            ev[s][0].record(stream)
+            g.replay()
+            ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_replay_ms = [a.elapsed_time(b) for a, b in ev]
+    per_call_us = [ms * 1000.0 / CALLS_PER_STEP for ms in per_replay_ms]
+    status = ar.get_status()
+    # parity of the last replay's 160 outputs
+    import oracle
+    want = [oracle.allreduce(list(d)) for d in sets]
+    bad = 0
+    for k in range(CALLS_PER_STEP):
+        got = outs[k].cpu().numpy().view(np.uint16)
+        bad += int((got != want[k % 4]).sum())
+    # instrumented replays: per-call device timestamps
+    slots = CALLS_PER_STEP * steps
+    ts = torch.empty((slots, 2), dtype=torch.int64, device="cuda:0")
+    ts[:, 0] = -1   # UINT64_MAX
+    ts[:, 1] = 0
+    ar.set_timestamps(ts, slots)
+    gi = capture()
+    ar.set_timestamps(None, 0)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            gi.replay()
+    torch.cuda.synchronize()
+    ts[:, 0] = -1
+    ts[:, 1] = 0
+    torch.cuda.synchronize()
+    ev_i = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        for s in range(steps):
+            ev_i[s][0].record(stream)
+            gi.replay()
+            ev_i[s][1].record(stream)
+    torch.cuda.synchronize()
+    tsh = ts.cpu().numpy().view(np.uint64)
+    inst_event_us = [a.elapsed_time(b) * 1000.0 / CALLS_PER_STEP for a, b in ev_i]
+    # slots are indexed by the flag sequence; the graph's replays after the
+    # two warm-ups occupy a contiguous run of slots
+    filled = np.nonzero(tsh[:, 1] != 0)[0]
+    starts = tsh[filled, 0].astype(np.float64)
+    ends = tsh[filled, 1].astype(np.float64)
+    order = np.argsort(ends)
+    ends, starts = ends[order], starts[order]
+    intervals = np.diff(ends) / CLOCK_HZ * 1e6
+    # drop the gap across replay boundaries (the step_end node and the host)
+    keep = np.ones_like(intervals, dtype=bool)
+    keep[CALLS_PER_STEP - 1::CALLS_PER_STEP] = False
+    intervals = intervals[keep[:intervals.size]]
+    spans = (ends - starts) / CLOCK_HZ * 1e6
+    status_i = ar.get_status()
+    ar.destroy()
+    del g, gi
+    return {
+        "workload": "8 ranks x [1x8192] bf16 (16 KiB/rank), N(0,0.5), one-shot LL, "
+                    "160 calls/step in one hipGraph",
+        "event_us_per_call": {"p50": pct(per_call_us, 50), "p99": pct(per_call_us, 99),
+                              "mean": float(np.mean(per_call_us))},
+        "event_ms_per_step": {"p50": pct(per_replay_ms, 50), "mean": float(np.mean(per_replay_ms))},
+        "wall_s": wall,
+        "instrumented": {
+            "interval_us": {"p50": pct(intervals, 50), "p99": pct(intervals, 99),
+                            "mean": float(np.mean(intervals)), "count": int(intervals.size)},
+            "span_us": {"p50": pct(spans, 50), "p99": pct(spans, 99)},
+            "event_us_per_call_mean": float(np.mean(inst_event_us)),
+        },
+        "mismatches": bad,
+        "status": list(status),
+        "status_instrumented": list(status_i),
+    }
+
+
+# --------------------------------------------------------------------- floor
+def bench_floor(torch, steps):
+    """A 160-node graph of minimal kernels (1-element fills): the launch floor."""
+    t = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(CALLS_PER_STEP):
+                t.fill_(1)
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        for s in range(steps):
+            ev[s][0].record(stream)
+            g.replay()
+            ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(b) * 1000.0 / CALLS_PER_STEP for a, b in ev]
+    return {"us_per_node_p50": pct(us, 50), "what": "160-node hipGraph of 1-element fill kernels"}
+
+
+# --------------------------------------------------------------------- C4
+def bench_bandwidth(torch, ar, calls, warmup, algo, proto, label):
+    import synth
+    N, n = 8, 256 * 8192
+    nsets = 8
+    sets = [synth.input_set(4, s) for s in range(nsets)]
+    ins = [[to_dev(torch, d[r]) for r in range(N)] for d in sets]
+    outs = [torch.empty((N, n), dtype=torch.int16, device="cuda:0") for _ in range(nsets)]
+    ar.init(N, n)
+    ar.set_options(algo, proto)
+    grid = ar.query(4, n)
+    threads = ar.query(5, n)
+    stream = torch.cuda.current_stream()
+    epoch = 0
+
+    def call(k):
+        nonlocal epoch
+        epoch += 1
+        if epoch > 65000:
+            ar.step_end()
+            epoch = 1
+        ar.allreduce(ins[k % nsets], outs[k % nsets], n, epoch)
+
+    for k in range(warmup):
+        call(k)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for k in range(calls):
+        ev[k][0].record(stream)
+        call(k)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1000.0 for a, b in ev])
+    status = ar.get_status()
+    import oracle
+    bad = 0
+    for s in range(nsets):
+        want = oracle.allreduce(list(sets[s]))[0]
+        got = outs[s].cpu().numpy().view(np.uint16)
+        bad += int((got != want[None, :]).sum())
+    ar.destroy()
+    b_alg = 2 * N * 2 * n
+    return {
+        "workload": "8 ranks x [256x8192] bf16 (4 MiB/rank), U(-1,1), %s, 8 rotating buffer "
+                    "sets (footprint %d MiB)" % (label, (2 * nsets * N * 2 * n) >> 20),
+        "algo": label,
+        "grid": grid, "threads": threads,
+        "us_per_call": {"p50": float(np.percentile(us, 50)), "p99": float(np.percentile(us, 99)),
+                        "mean": float(us.mean()), "min": float(us.min())},
+        "b_alg_bytes": b_alg,
+        "gbps_p50": b_alg / (np.percentile(us, 50) * 1e-6) / 1e9,
+        "gbps_mean": b_alg / (us.mean() * 1e-6) / 1e9,
+        "mismatches": bad,
+        "status": list(status),
+    }
+
+
+# --------------------------------------------------------------------- CPU
+def cpu_baseline(budget_s=12.0):
+    """The oracle as it stands, on this host's cores: 16 KiB/rank calls."""
+    import oracle
+    import synth
+    data = list(synth.input_set(2, 0))
+    res = {}
+    threads_all = oracle.max_threads()
+    for label, th in (("1thread", 1), ("all", threads_all)):
+        reps = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s / 2:
+            oracle.allreduce(data, threads=th)
+            reps += 1
+        dt = time.perf_counter() - t0
+        res[label] = {"us_per_call": dt / reps * 1e6, "reps": reps, "threads": th}
+    best = min(res.values(), key=lambda r: r["us_per_call"])
+    cpu_model = ""
+    try:
+        out = subprocess.run(["lscpu"], stdout=subprocess.PIPE, text=True).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return {
+        "value": best["us_per_call"], "unit": "us/call", "cores": best["threads"],
+        "kind": "oracle",
+        "sample": "8 ranks x 8192 bf16 (the 16 KiB/rank workload), C oracle producing all "
+                  "8 output copies, repeated for ~%.0f s per thread setting" % (budget_s / 2),
+        "one_thread_us_per_call": res["1thread"]["us_per_call"],
+        "all_threads_us_per_call": res["all"]["us_per_call"],
+        "host_threads": threads_all, "cpu_model": cpu_model, "nproc": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200, help="timed graph replays (160 calls each)")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--bw-calls", type=int, default=200)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--quick", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the N ranks are emulated as workgroup sets of one "
+              "MI355X; runs on %d GPUs are not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py is single-process (one GPU)", file=sys.stderr)
+        sys.exit(2)
+    if args.quick:
+        args.steps, args.bw_calls = min(args.steps, 20), min(args.bw_calls, 20)
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline()
+    import torch
+    import tp_decode_comms_amd as ar
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log("device %s, %d CUs" % (props.name, props.multi_processor_count))
+
+    log("launch floor")
+    floor = bench_floor(torch, args.steps)
+    log("C2 latency: %d steps x 160 calls" % args.steps)
+    lat = bench_latency(torch, ar, args.steps, args.warmup)
+    log("C2 p50 %.3f us/call (events), instrumented interval p50 %.3f us"
+        % (lat["event_us_per_call"]["p50"], lat["instrumented"]["interval_us"]["p50"]))
+    log("C4 bandwidth: two-shot LL128")
+    bw2 = bench_bandwidth(torch, ar, args.bw_calls, args.warmup, ar.AR_ALGO_TWOSHOT,
+                          ar.AR_PROTO_LL128, "two-shot (reduce-scatter + all-gather, LL128 lines)")
+    log("C4 two-shot %.1f GB/s" % bw2["gbps_p50"])
+    log("C4 bandwidth: one-shot DIRECT")
+    bw1 = bench_bandwidth(torch, ar, args.bw_calls, args.warmup, ar.AR_ALGO_ONESHOT,
+                          ar.AR_PROTO_DIRECT, "one-shot (in-place reads after arrival flags)")
+    log("C4 one-shot %.1f GB/s" % bw1["gbps_p50"])
+    best_bw = max((bw2, bw1), key=lambda r: r["gbps_p50"])
+
+    avg_us = best_bw["us_per_call"]["mean"]
+    achieved = best_bw["b_alg_bytes"] / (avg_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": best_bw["algo"],
+                "per_launch_bytes": best_bw["b_alg_bytes"],
+                "avg_launch_us": avg_us}
+    parity_ok = (lat["mismatches"] == 0 and bw2["mismatches"] == 0 and bw1["mismatches"] == 0
+                 and lat["status"][0] == 0 and bw2["status"][0] == 0 and bw1["status"][0] == 0)
+    value = lat["event_us_per_call"]["p50"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(lat["event_ms_per_step"]["mean"], 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": lat["workload"], "n_ranks": 8, "elems_per_rank": 8192,
+                   "calls_per_step": CALLS_PER_STEP, "launch": "hipGraph"},
+        "gbps_4mb": round(best_bw["gbps_p50"], 2),
+        "gbps_4mb_frac_of_peak": round(best_bw["gbps_p50"] / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity_ok": parity_ok,
+        "results": {"latency_16k": lat, "floor": floor, "bw_4m_twoshot": bw2,
+                    "bw_4m_oneshot": bw1},
+        "host": platform.node(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
