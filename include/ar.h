@@ -66,8 +66,10 @@ enum ar_proto {
     AR_PROTO_LL = 1,        /* one-shot only */
     AR_PROTO_LL128 = 2,     /* one-shot or two-shot */
     AR_PROTO_SENTINEL = 3,  /* one-shot or two-shot */
-    AR_PROTO_DIRECT = 4     /* one-shot only: read peers' inputs in place after
-                               their per-call arrival flag (large messages) */
+    AR_PROTO_DIRECT = 4     /* arrival counters instead of staging: one-shot reads
+                               peers' inputs in place; two-shot reads slice q in
+                               place and writes the reduced slice straight into
+                               every rank's output, then completion flags */
 };
 
 #define AR_MAX_RANKS 16
@@ -127,9 +129,9 @@ int ar_destroy(void);
 /*
  * ar_set_options -- choose the algorithm and protocol for later calls.
  * AUTO picks by message size S = 2n bytes per rank: S <= 64 KiB -> one-shot
- * LL; otherwise two-shot LL128 (section "统一原语与API设计", table of
- * variants).  LL and DIRECT exist only as one-shot.  AR_ERR_INVALID for an
- * unknown value or an impossible pair.
+ * LL; otherwise two-shot DIRECT (section "统一原语与API设计", table of
+ * variants: one-shot below 64 KiB, two-shot above).  LL exists only as
+ * one-shot.  AR_ERR_INVALID for an unknown value or an impossible pair.
  */
 int ar_set_options(int algo, int proto);
 
@@ -170,11 +172,13 @@ int ar_step_end(hipStream_t stream);
 int ar_set_delays(const uint32_t *dev_ns, size_t calls);
 
 /*
- * ar_set_timestamps -- measurement hook: DEVICE uint64 table [slots][2].  Call
- * with flag f folds min(workgroup start) into [slot][0] and max(workgroup end)
- * into [slot][1], slot = (f - 1) mod slots, in ticks of the constant 100 MHz
- * clock.  The caller initialises [.][0] to UINT64_MAX and [.][1] to 0.  NULL
- * disables (the default; the uninstrumented kernels are used then).
+ * ar_set_timestamps -- measurement hook: DEVICE uint64 table [slots][64][2].
+ * Workgroup b of the call with flag f folds its start time into
+ * [slot][b % 64][0] (minimum) and its end time into [slot][b % 64][1]
+ * (maximum), slot = (f - 1) mod slots, in ticks of the constant 100 MHz
+ * clock; the call's first start and last end are the minimum and maximum over
+ * the 64 sub-slots.  The caller initialises [.][.][0] to UINT64_MAX and
+ * [.][.][1] to 0.  NULL disables (the default).
  */
 int ar_set_timestamps(uint64_t *dev_ts, size_t slots);
 

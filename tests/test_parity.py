@@ -25,6 +25,7 @@ VARIANTS = [
     ("oneshot-direct", ONE, DIRECT),
     ("twoshot-ll128", TWO, LL128),
     ("twoshot-sentinel", TWO, SENT),
+    ("twoshot-direct", TWO, DIRECT),
 ]
 
 

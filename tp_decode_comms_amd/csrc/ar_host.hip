@@ -36,18 +36,19 @@ struct Context {
     char *s1 = nullptr;   size_t s1_stride = 0;
     char *srs = nullptr;  char *sag = nullptr; size_t s2_stride = 0;
     uint32_t *ctl = nullptr;
+    uint32_t *done = nullptr;           // two-shot DIRECT completion flags
     // options
     int algo = AR_ALGO_AUTO;
     int proto = AR_PROTO_AUTO;
     int wgs_per_rank = 0;
-    int threads = 256;
+    int threads = 0;                    // 0 = chosen per call
     uint32_t watchdog_us = DEFAULT_WATCHDOG_US;
     const uint32_t *delays = nullptr; size_t delay_rows = 0;
     uint64_t *ts = nullptr; size_t ts_slots = 0;
     // sequence
     uint32_t last_epoch = 0;
-    int capacity[ar::K_COUNT][2] = {};   // resident workgroups, [kind][f32]
-    int cap_threads = 0;
+    int capacity[ar::K_COUNT][2][3] = {};   // resident workgroups [kind][f32][64,128,256 threads]
+    bool cap_ready = false;
 };
 
 Context g;
@@ -82,6 +83,8 @@ void free_all()
     }
     if (g.ctl) (void)hipFree(g.ctl);
     g.ctl = nullptr;
+    if (g.done) (void)hipFree(g.done);
+    g.done = nullptr;
 }
 
 int alloc(char **p, size_t bytes)
@@ -103,6 +106,7 @@ size_t ll_bytes() { return g.ll_stride * 2 * g.n_ranks; }
 size_t l128_bytes() { return g.l128_stride * 2 * g.n_ranks; }
 size_t s1_bytes() { return g.s1_stride * 2 * g.n_ranks * g.n_ranks; }
 size_t s2_bytes() { return g.s2_stride * 2 * g.n_ranks * g.n_ranks; }
+size_t done_words() { return (size_t)ar::MAX_RANKS * ar::DONE_STRIDE; }
 
 // Zero flags, arm sentinels, clear the control block -- kernels only.
 hipError_t rearm(hipStream_t s)
@@ -113,22 +117,28 @@ hipError_t rearm(hipStream_t s)
     if ((e = ar::launch_fill((uint32_t *)g.s1, s1_bytes() / 4, ar::SENT_WORD, s)) != hipSuccess) return e;
     if ((e = ar::launch_fill((uint32_t *)g.srs, s2_bytes() / 4, ar::SENT_WORD, s)) != hipSuccess) return e;
     if ((e = ar::launch_fill((uint32_t *)g.sag, s2_bytes() / 4, ar::SENT_WORD, s)) != hipSuccess) return e;
+    if ((e = ar::launch_fill(g.done, done_words(), 0u, s)) != hipSuccess) return e;
     return ar::launch_fill(g.ctl, ar::CTL_WORDS, 0u, s);
 }
 
-int compute_capacity(int threads)
+int thread_index(int threads) { return threads == 64 ? 0 : threads == 128 ? 1 : 2; }
+
+int compute_capacity()
 {
+    const int tcounts[3] = {64, 128, 256};
     for (int k = 0; k < ar::K_COUNT; ++k) {
         for (int f = 0; f < 2; ++f) {
-            int per_cu = 0;
-            hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, ar::kernel_for(k, g.n_ranks, f == 1), threads, 0);
-            if (e != hipSuccess)
-                return hip_fail(e);
-            g.capacity[k][f] = per_cu * g.cu_count;
+            for (int t = 0; t < 3; ++t) {
+                int per_cu = 0;
+                hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &per_cu, ar::kernel_for(k, g.n_ranks, f == 1), tcounts[t], 0);
+                if (e != hipSuccess)
+                    return hip_fail(e);
+                g.capacity[k][f][t] = per_cu * g.cu_count;
+            }
         }
     }
-    g.cap_threads = threads;
+    g.cap_ready = true;
     return AR_OK;
 }
 
@@ -144,13 +154,13 @@ int choose_kind(size_t n, int *kind)
     const size_t bytes = 2 * n;
     int algo = g.algo, proto = g.proto;
     if (algo == AR_ALGO_AUTO) {
-        if (proto == AR_PROTO_LL || proto == AR_PROTO_DIRECT)
+        if (proto == AR_PROTO_LL)
             algo = AR_ALGO_ONESHOT;
         else
             algo = bytes <= ONESHOT_LIMIT_BYTES ? AR_ALGO_ONESHOT : AR_ALGO_TWOSHOT;
     }
     if (proto == AR_PROTO_AUTO)
-        proto = algo == AR_ALGO_ONESHOT ? AR_PROTO_LL : AR_PROTO_LL128;
+        proto = algo == AR_ALGO_ONESHOT ? AR_PROTO_LL : AR_PROTO_DIRECT;
     if (algo == AR_ALGO_ONESHOT) {
         switch (proto) {
         case AR_PROTO_LL: *kind = ar::K_ONESHOT_LL; return AR_OK;
@@ -162,39 +172,55 @@ int choose_kind(size_t n, int *kind)
         switch (proto) {
         case AR_PROTO_LL128: *kind = ar::K_TWOSHOT_LL128; return AR_OK;
         case AR_PROTO_SENTINEL: *kind = ar::K_TWOSHOT_SENTINEL; return AR_OK;
+        case AR_PROTO_DIRECT: *kind = ar::K_TWOSHOT_DIRECT; return AR_OK;
         }
     }
     return AR_ERR_INVALID;
 }
 
-// Workgroups per rank.  Work unit: a lane chunk of 8 elements (LL,
-// sentinel, DIRECT) or a wave-wide LL128 line group of 480 elements.  The
-// whole grid must be resident at once.
+// Launch geometry.  Work unit per kind: a lane chunk of 4 elements (LL), of
+// 8 elements (sentinel, DIRECT one-shot), two 8-element chunks (DIRECT
+// two-shot), or a wave-wide LL128 line group of 480 elements.  Small
+// messages use one-wave workgroups spread over many CUs (each CU then polls
+// little); large ones use 4-wave workgroups.  The whole grid must be
+// resident at once.
 int make_plan(size_t n, bool f32, Plan *p)
 {
     int rc = choose_kind(n, &p->kind);
     if (rc != AR_OK)
         return rc;
-    p->threads = (uint32_t)g.threads;
     const uint32_t N = (uint32_t)g.n_ranks;
     p->slice = (uint32_t)slice_len(n, g.n_ranks);
+    const bool l128 = p->kind == ar::K_ONESHOT_LL128 || p->kind == ar::K_TWOSHOT_LL128;
+    if (g.threads > 0)
+        p->threads = (uint32_t)g.threads;
+    else if (l128 || p->kind == ar::K_TWOSHOT_DIRECT)
+        p->threads = 256;
+    else
+        p->threads = 2 * n <= 256 * 1024 ? 64 : 256;
     uint64_t units, per_wg;
     switch (p->kind) {
+    case ar::K_ONESHOT_LL:
+        units = n / 4; per_wg = p->threads; break;
     case ar::K_ONESHOT_LL128:
         units = (n + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = p->threads / 64; break;
     case ar::K_TWOSHOT_LL128:
         units = (p->slice + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = p->threads / 64; break;
     case ar::K_TWOSHOT_SENTINEL:
         units = p->slice / 8; per_wg = p->threads; break;
+    case ar::K_TWOSHOT_DIRECT:
+        units = p->slice / 8; per_wg = 2 * p->threads; break;
     default:
         units = n / 8; per_wg = p->threads; break;
     }
-    if (g.cap_threads != (int)p->threads) {
-        rc = compute_capacity((int)p->threads);
+    if (!g.cap_ready) {
+        rc = compute_capacity();
         if (rc != AR_OK)
             return rc;
     }
-    const uint32_t cap = (uint32_t)g.capacity[p->kind][f32 ? 1 : 0] / N;
+    uint32_t cap = (uint32_t)g.capacity[p->kind][f32 ? 1 : 0][thread_index((int)p->threads)] / N;
+    if (cap > ar::DONE_STRIDE)
+        cap = ar::DONE_STRIDE;
     if (cap == 0)
         return AR_ERR_INVALID;
     uint64_t want = g.wgs_per_rank > 0 ? (uint64_t)g.wgs_per_rank : (units + per_wg - 1) / per_wg;
@@ -247,6 +273,7 @@ int do_allreduce(const void *const *rank_bufs, void *out, size_t n, uint32_t epo
     a.out = out;
     a.ll = g.ll; a.l128 = g.l128; a.s1 = g.s1; a.srs = g.srs; a.sag = g.sag;
     a.ctl = g.ctl;
+    a.done = g.done;
     a.ts = g.ts; a.ts_slots = (uint32_t)g.ts_slots;
     a.delays = g.delays; a.delay_rows = (uint32_t)g.delay_rows;
     a.ll_stride = (uint32_t)g.ll_stride; a.l128_stride = (uint32_t)g.l128_stride;
@@ -298,7 +325,8 @@ int ar_init(int n_ranks, size_t max_elems)
         (rc = alloc(&g.s1, s1_bytes())) != AR_OK ||
         (rc = alloc(&g.srs, s2_bytes())) != AR_OK ||
         (rc = alloc(&g.sag, s2_bytes())) != AR_OK ||
-        (rc = alloc((char **)&g.ctl, ar::CTL_WORDS * 4)) != AR_OK) {
+        (rc = alloc((char **)&g.ctl, ar::CTL_WORDS * 4)) != AR_OK ||
+        (rc = alloc((char **)&g.done, done_words() * 4)) != AR_OK) {
         free_all();
         return rc;
     }
@@ -310,14 +338,14 @@ int ar_init(int n_ranks, size_t max_elems)
         return hip_fail(e);
     }
     g.algo = AR_ALGO_AUTO; g.proto = AR_PROTO_AUTO;
-    g.wgs_per_rank = 0; g.threads = 256;
+    g.wgs_per_rank = 0; g.threads = 0;
     g.watchdog_us = DEFAULT_WATCHDOG_US;
     g.delays = nullptr; g.delay_rows = 0;
     g.ts = nullptr; g.ts_slots = 0;
     g.last_epoch = 0;
-    g.cap_threads = 0;
+    g.cap_ready = false;
     g.live = true;
-    rc = compute_capacity(g.threads);
+    rc = compute_capacity();
     if (rc != AR_OK) {
         g.live = false;
         free_all();
@@ -358,7 +386,7 @@ int ar_set_options(int algo, int proto)
         return AR_ERR_INVALID;
     if (proto < AR_PROTO_AUTO || proto > AR_PROTO_DIRECT)
         return AR_ERR_INVALID;
-    if (algo == AR_ALGO_TWOSHOT && (proto == AR_PROTO_LL || proto == AR_PROTO_DIRECT))
+    if (algo == AR_ALGO_TWOSHOT && proto == AR_PROTO_LL)
         return AR_ERR_INVALID;
     g.algo = algo;
     g.proto = proto;
@@ -369,9 +397,7 @@ int ar_set_launch(int wgs_per_rank, int threads)
 {
     if (!g.live)
         return AR_ERR_NOT_INIT;
-    if (threads == 0)
-        threads = 256;
-    if (wgs_per_rank < 0 || !(threads == 64 || threads == 128 || threads == 256))
+    if (wgs_per_rank < 0 || !(threads == 0 || threads == 64 || threads == 128 || threads == 256))
         return AR_ERR_INVALID;
     g.wgs_per_rank = wgs_per_rank;
     g.threads = threads;
@@ -394,7 +420,7 @@ int ar_step_end(hipStream_t stream)
         return AR_ERR_STATE;
     if (g.last_epoch > 0) {
         hipError_t e = ar::launch_step_end(g.ctl, g.last_epoch, g.ll, ll_bytes(), g.l128,
-                                           l128_bytes(), stream);
+                                           l128_bytes(), g.done, stream);
         if (e != hipSuccess)
             return hip_fail(e);
     }
@@ -484,12 +510,13 @@ long long ar_query(int key, size_t n)
         if (rc != AR_OK)
             return rc;
         if (key == 2)
-            return (p.kind == ar::K_TWOSHOT_LL128 || p.kind == ar::K_TWOSHOT_SENTINEL)
-                       ? AR_ALGO_TWOSHOT : AR_ALGO_ONESHOT;
+            return (p.kind == ar::K_TWOSHOT_LL128 || p.kind == ar::K_TWOSHOT_SENTINEL ||
+                    p.kind == ar::K_TWOSHOT_DIRECT) ? AR_ALGO_TWOSHOT : AR_ALGO_ONESHOT;
         if (key == 3) {
             switch (p.kind) {
             case ar::K_ONESHOT_LL: return AR_PROTO_LL;
-            case ar::K_ONESHOT_DIRECT: return AR_PROTO_DIRECT;
+            case ar::K_ONESHOT_DIRECT:
+            case ar::K_TWOSHOT_DIRECT: return AR_PROTO_DIRECT;
             case ar::K_ONESHOT_SENTINEL:
             case ar::K_TWOSHOT_SENTINEL: return AR_PROTO_SENTINEL;
             default: return AR_PROTO_LL128;
@@ -501,7 +528,8 @@ long long ar_query(int key, size_t n)
     case 6: {
         int kind;
         if (n == 0 || choose_kind(n, &kind) != AR_OK) return AR_ERR_INVALID;
-        return g.capacity[kind][0];
+        if (!g.cap_ready && compute_capacity() != AR_OK) return AR_ERR_HIP;
+        return g.capacity[kind][0][2];
     }
     case 7: return g.last_epoch;
     default: return AR_ERR_INVALID;

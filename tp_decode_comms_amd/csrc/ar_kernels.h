@@ -15,7 +15,8 @@ enum KernelKind {
     K_ONESHOT_LL128 = 3,
     K_TWOSHOT_LL128 = 4,
     K_TWOSHOT_SENTINEL = 5,
-    K_COUNT = 6
+    K_TWOSHOT_DIRECT = 6,
+    K_COUNT = 7
 };
 
 // device function of a kernel kind for n_ranks (<= 8 or <= 16 instantiation)
@@ -24,7 +25,7 @@ const void *kernel_for(int kind, int n_ranks, bool f32);
 hipError_t launch_ar(int kind, bool f32, const Launch &a, uint32_t grid, uint32_t threads,
                      hipStream_t stream);
 hipError_t launch_step_end(uint32_t *ctl, uint32_t calls, char *ll, size_t ll_bytes, char *l128,
-                           size_t l128_bytes, hipStream_t stream);
+                           size_t l128_bytes, uint32_t *done, hipStream_t stream);
 hipError_t launch_fill(uint32_t *p, size_t words, uint32_t value, hipStream_t stream);
 
 }  // namespace ar

@@ -14,11 +14,19 @@
 //   one-shot: read local value, publish, receive-and-reduce all N, write;
 //   two-shot: reduce-scatter (rank q reduces slice q) then all-gather.
 // Protocols (same page, section "四大核心机制"): LL units, sentinel inboxes,
-// parity double buffering, LL128-style lines; plus DIRECT, which reads peers'
-// inputs in place once their per-call arrival flag is up.
+// parity double buffering, LL128-style lines; plus DIRECT, in which a rank
+// announces its arrival with a counter and peers read its input in place
+// (one-shot) or receive the reduced slices straight into their outputs
+// (two-shot), completion announced by per-workgroup flags.
 //
 // Summation order is the global rank order 0..N-1 for every element on
 // every rank and in both algorithms, so all variants give identical bits.
+//
+// Latency notes (measured on MI355X): a line written by one XCD with the
+// device-scope policy becomes readable by another XCD about 1 us later, and
+// a wave's loads cannot be consumed before its earlier device-scope stores
+// are acknowledged (one in-order counter for both).  Polls therefore keep two
+// batches of loads in flight, and flag words are tiny and read by few lanes.
 #include "ar_proto.h"
 #include "ar_kernels.h"
 
@@ -30,6 +38,8 @@ struct Ctx0 {
     uint64_t t0;
 };
 
+// The flag-sequence base, read coherently (it is advanced by the step-end
+// kernel; a stale copy would make flags repeat).
 __device__ __forceinline__ uint32_t load_seq(const Launch &a)
 {
     return __hip_atomic_load(a.ctl + CTL_SEQ, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -57,52 +67,20 @@ __device__ __forceinline__ void finish(const Launch &a, const Ctx0 &c)
     __syncthreads();
     if (threadIdx.x == 0) {
         uint64_t t1 = clock100();
-        uint32_t slot = (c.flag - 1u) % a.ts_slots;
-        __hip_atomic_fetch_min(a.ts + 2 * slot, c.t0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_max(a.ts + 2 * slot + 1, t1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // 64 sub-slots per call spread the atomics over 64 addresses
+        const uint32_t slot = (c.flag - 1u) % a.ts_slots;
+        uint64_t *p = a.ts + ((size_t)slot * TS_SUB + (blockIdx.x % TS_SUB)) * 2u;
+        __hip_atomic_fetch_min(p, c.t0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_max(p + 1, t1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-template <bool F32>
-__device__ __forceinline__ void store_out8(const Launch &a, uint32_t rank, uint32_t elem,
-                                           const Acc8 &acc)
+__device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
 {
-    // elem is a multiple of 8 inside [0, n)
-    if constexpr (F32) {
-        char *base = (char *)a.out + (size_t)rank * a.n * 4u;
-        __amdgpu_buffer_rsrc_t o = rsrc(base, a.n * 4u);
-        u32x4 lo, hi;
-        lo.x = __float_as_uint(acc.v[0]); lo.y = __float_as_uint(acc.v[1]);
-        lo.z = __float_as_uint(acc.v[2]); lo.w = __float_as_uint(acc.v[3]);
-        hi.x = __float_as_uint(acc.v[4]); hi.y = __float_as_uint(acc.v[5]);
-        hi.z = __float_as_uint(acc.v[6]); hi.w = __float_as_uint(acc.v[7]);
-        st16<CP_PLAIN>(lo, o, elem * 4u);
-        st16<CP_PLAIN>(hi, o, elem * 4u + 16u);
-    } else {
-        char *base = (char *)a.out + (size_t)rank * a.n * 2u;
-        __amdgpu_buffer_rsrc_t o = rsrc(base, a.n * 2u);
-        st16<CP_PLAIN>(acc.bf16(), o, elem * 2u);
-    }
-}
-
-// 4-element variant (LL128 flag lanes): values in acc.v[0..3]
-template <bool F32>
-__device__ __forceinline__ void store_out4(const Launch &a, uint32_t rank, uint32_t elem,
-                                           const Acc8 &acc)
-{
-    if constexpr (F32) {
-        char *base = (char *)a.out + (size_t)rank * a.n * 4u;
-        __amdgpu_buffer_rsrc_t o = rsrc(base, a.n * 4u);
-        u32x4 lo;
-        lo.x = __float_as_uint(acc.v[0]); lo.y = __float_as_uint(acc.v[1]);
-        lo.z = __float_as_uint(acc.v[2]); lo.w = __float_as_uint(acc.v[3]);
-        st16<CP_PLAIN>(lo, o, elem * 4u);
-    } else {
-        char *base = (char *)a.out + (size_t)rank * a.n * 2u;
-        __amdgpu_buffer_rsrc_t o = rsrc(base, a.n * 2u);
-        u32x2 w; w.x = pack_bf16(acc.v[0], acc.v[1]); w.y = pack_bf16(acc.v[2], acc.v[3]);
-        st8<CP_PLAIN>(w, o, elem * 2u);
-    }
+    c.t0 = clock100();
+    c.rank = blockIdx.x % a.n_ranks;
+    c.part = blockIdx.x / a.n_ranks;
+    c.par = a.epoch & 1u;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t in_rsrc(const Launch &a, uint32_t r)
@@ -110,97 +88,194 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t in_rsrc(const Launch &a, uint3
     return rsrc(a.in[r], a.n * 2u);
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const Launch &a, uint32_t r, bool f32)
+{
+    const uint32_t esz = f32 ? 4u : 2u;
+    return rsrc((char *)a.out + (size_t)r * a.n * esz, a.n * esz);
+}
+
+// 8 accumulated elements -> out[rank][elem..elem+8)
+template <bool F32, int CP = CP_PLAIN>
+__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t o, uint32_t elem, const Acc8 &acc)
+{
+    if constexpr (F32) {
+        u32x4 lo, hi;
+        lo.x = __float_as_uint(acc.v[0]); lo.y = __float_as_uint(acc.v[1]);
+        lo.z = __float_as_uint(acc.v[2]); lo.w = __float_as_uint(acc.v[3]);
+        hi.x = __float_as_uint(acc.v[4]); hi.y = __float_as_uint(acc.v[5]);
+        hi.z = __float_as_uint(acc.v[6]); hi.w = __float_as_uint(acc.v[7]);
+        st16<CP>(lo, o, elem * 4u);
+        st16<CP>(hi, o, elem * 4u + 16u);
+    } else {
+        st16<CP>(acc.bf16(), o, elem * 2u);
+    }
+}
+
+// 4 accumulated elements (in v[0..3]) -> out[rank][elem..elem+4)
+template <bool F32>
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t o, uint32_t elem, const float *v)
+{
+    if constexpr (F32) {
+        u32x4 lo;
+        lo.x = __float_as_uint(v[0]); lo.y = __float_as_uint(v[1]);
+        lo.z = __float_as_uint(v[2]); lo.w = __float_as_uint(v[3]);
+        st16<CP_PLAIN>(lo, o, elem * 4u);
+    } else {
+        u32x2 w; w.x = pack_bf16(v[0], v[1]); w.y = pack_bf16(v[2], v[3]);
+        st8<CP_PLAIN>(w, o, elem * 2u);
+    }
+}
+
+// ============================================================ arrivals
+// Rank s announces "my input for this call is final" by adding one to its
+// arrival counter (one workgroup per rank does it, at its very start, with
+// no dependence on any load).  After k calls since the last reset the
+// counter is k, and a call whose flag is f = seq + epoch needs counter >= f.
+__device__ __forceinline__ void raise_arrival(const Launch &a, const Ctx0 &c)
+{
+    if (c.part == 0 && threadIdx.x == 0)
+        __hip_atomic_fetch_add(a.ctl + CTL_ARRIVE + 32u * c.rank, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every wave waits (two polls in flight) until all N arrival counters reach
+// the call's flag.  Lanes 0..N-1 each watch one counter.
+__device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, const Ctl &ctl)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    bool need = lane < a.n_ranks;
+    const uint32_t off = (CTL_ARRIVE + 32u * (lane & 15u)) * 4u;
+    const __amdgpu_buffer_rsrc_t r = rsrc(a.ctl, CTL_WORDS * 4u);
+    Watch w;
+    w.begin(a.watchdog_ticks);
+    uint32_t v0 = need ? ld4<CP_DEV>(r, off) : c.flag, v1;
+    while (true) {
+        compiler_fence();
+        v1 = need ? ld4<CP_DEV>(r, off) : c.flag;
+        if (need && (int32_t)(v0 - c.flag) >= 0)
+            need = false;
+        if (!wave_any(need))
+            return true;
+        if (w.expired(ctl, c.rank, lane, c.flag))
+            return false;
+        compiler_fence();
+        v0 = need ? ld4<CP_DEV>(r, off) : c.flag;
+        if (need && (int32_t)(v1 - c.flag) >= 0)
+            need = false;
+        if (!wave_any(need))
+            return true;
+    }
+}
+
 // ============================================================ one-shot LL
-// Lane work unit: chunk c of 8 elements (16 B of input).  Rank r publishes
-// chunk c as two 16-byte LL stores: elements 0..3 at byte 16c of the first
-// half of its mailbox and elements 4..7 at byte 16c of the second half, so
-// both the stores and every reader's loads are contiguous across a wave.
+// Lane work unit: 4 elements (8 bytes of input) = one 16-byte LL store of
+// two units {2 bf16, flag}.  Rank r publishes once into its own mailbox
+// [r][parity]; every rank reads it.  The receive keeps two batches of loads
+// in flight: while one batch is checked the next is already on its way.
+// One round of the one-shot LL kernel for lane chunk `ch` with input x.
+template <int NMAX, bool F32>
+__device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
+                                         const __amdgpu_buffer_rsrc_t *src,
+                                         __amdgpu_buffer_rsrc_t mine, __amdgpu_buffer_rsrc_t o,
+                                         uint32_t ch, uint32_t C, u32x2 x)
+{
+    const uint32_t N = a.n_ranks;
+    const bool active = ch < C;
+    // publish (send/bcast): one copy, read by all N ranks
+    if (active)
+        st16<CP_DEV>(ll_pack(x.x, x.y, c.flag), mine, ch * 16u);
+    // receive (recvReduce): poll every peer's unit for this chunk
+    uint32_t pend = 0;
+#pragma unroll
+    for (int s = 0; s < NMAX; ++s)
+        if ((uint32_t)s < N && (uint32_t)s != c.rank && active)
+            pend |= 1u << s;
+    u32x4 A0[NMAX], A1[NMAX];
+    u32x2 V[NMAX];
+    auto issue = [&](u32x4 *A) {
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((pend >> s) & 1u)
+                A[s] = ld16<CP_DEV>(src[s], ch * 16u);
+    };
+    auto check = [&](const u32x4 *A) {
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((pend >> s) & 1u)
+                if (ll_ready(A[s], c.flag)) {
+                    pend &= ~(1u << s);
+                    V[s].x = A[s].x;
+                    V[s].y = A[s].z;
+                }
+    };
+    Watch w;
+    w.begin(a.watchdog_ticks);
+    issue(A0);
+    while (true) {
+        compiler_fence();
+        issue(A1);
+        check(A0);
+        if (!wave_any(pend != 0u))
+            break;
+        if (w.expired(ctl, c.rank, pend ? first_bit(pend) : 0u, c.flag))
+            return false;
+        compiler_fence();
+        issue(A0);
+        check(A1);
+        if (!wave_any(pend != 0u))
+            break;
+    }
+    // reduce in global rank order, own value from registers
+    if (active) {
+        Acc4 acc;
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s) {
+            if ((uint32_t)s < N) {
+                const u32x2 v = ((uint32_t)s == c.rank) ? x : V[s];
+                if (s == 0) acc.init(v.x, v.y); else acc.add(v.x, v.y);
+            }
+        }
+        store4<F32>(o, ch * 4u, acc.v);
+    }
+    return true;
+}
+
 template <int NMAX, bool F32>
 __global__ __launch_bounds__(256) void k_oneshot_ll(const Launch a)
 {
     Ctx0 c;
-    c.t0 = clock100();
-    c.rank = blockIdx.x % a.n_ranks;
-    c.part = blockIdx.x / a.n_ranks;
-    const uint32_t N = a.n_ranks;
-    const uint32_t G = a.n >> 3;                    // chunks per rank
-    const uint32_t half = G * 16u;                  // byte offset of the second half
-    const uint32_t mb_bytes = G * 32u;
+    begin(a, c);
+    const uint32_t C = a.n >> 2;                    // 4-element chunks per rank
+    const uint32_t mb_bytes = C * 16u;
     const uint32_t step = a.parts * blockDim.x;
-    const uint32_t rounds = (G + step - 1u) / step;
-    uint32_t seq = load_seq(a);
-    c.flag = seq + a.epoch;
-    c.par = a.epoch & 1u;
+    const uint32_t rounds = (C + step - 1u) / step;
+    const __amdgpu_buffer_rsrc_t inr = in_rsrc(a, c.rank);
+    const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
+    // first-round input load is issued together with the sequence load
+    uint32_t ch = c.part * blockDim.x + threadIdx.x;
+    u32x2 x = {0u, 0u};
+    if (ch < C)
+        x = ld8<CP_PLAIN>(inr, ch * 8u);
+    raise_arrival(a, c);
+    c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
-    __amdgpu_buffer_rsrc_t mine = rsrc(a.ll + (size_t)(c.rank * 2u + c.par) * a.ll_stride, mb_bytes);
     __amdgpu_buffer_rsrc_t src[NMAX];
 #pragma unroll
     for (int s = 0; s < NMAX; ++s)
         src[s] = rsrc(a.ll + (size_t)((uint32_t)s * 2u + c.par) * a.ll_stride, mb_bytes);
-    const __amdgpu_buffer_rsrc_t inr = in_rsrc(a, c.rank);
-
-    for (uint32_t it = 0; it < rounds; ++it) {
-        const uint32_t ch = c.part * blockDim.x + threadIdx.x + it * step;
-        const bool active = ch < G;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (active)
-            x = ld16<CP_PLAIN>(inr, ch * 16u);
-        if (it == 0)
-            start_delay(a, c);
-        // publish (send/bcast): one copy, read by all N ranks
-        if (active) {
-            st16<CP_DEV>(ll_pack(x.x, x.y, c.flag), mine, ch * 16u);
-            st16<CP_DEV>(ll_pack(x.z, x.w, c.flag), mine, half + ch * 16u);
-        }
-        // receive: poll every peer's units for this chunk
-        u32x4 A[NMAX], B[NMAX];
-        uint32_t pend = 0;
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s) {
-            if ((uint32_t)s < N && (uint32_t)s != c.rank && active) {
-                A[s] = ld16<CP_DEV>(src[s], ch * 16u);
-                B[s] = ld16<CP_DEV>(src[s], half + ch * 16u);
-                pend |= 1u << s;
-            }
-        }
-        Watch w;
-        w.begin(a.watchdog_ticks);
-        while (true) {
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((pend >> s) & 1u)
-                    if (ll_ready(A[s], c.flag) && ll_ready(B[s], c.flag))
-                        pend &= ~(1u << s);
-            if (!wave_any(pend != 0u))
-                break;
-            if (w.expired(ctl, c.rank, pend ? first_bit(pend) : 0u, c.flag))
-                return;
-            compiler_fence();
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s) {
-                if ((pend >> s) & 1u) {
-                    A[s] = ld16<CP_DEV>(src[s], ch * 16u);
-                    B[s] = ld16<CP_DEV>(src[s], half + ch * 16u);
-                }
-            }
-        }
-        // reduce in global rank order, own value from registers
-        if (active) {
-            Acc8 acc;
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s) {
-                if ((uint32_t)s < N) {
-                    u32x4 v;
-                    if ((uint32_t)s == c.rank) {
-                        v = x;
-                    } else {
-                        v.x = A[s].x; v.y = A[s].z; v.z = B[s].x; v.w = B[s].z;
-                    }
-                    if (s == 0) acc.init(v); else acc.add(v);
-                }
-            }
-            store_out8<F32>(a, c.rank, ch * 8u, acc);
-        }
+    const __amdgpu_buffer_rsrc_t mine =
+        rsrc(a.ll + (size_t)(c.rank * 2u + c.par) * a.ll_stride, mb_bytes);
+    start_delay(a, c);
+    // round 0 is straight-line code: its poll loads are issued back to back
+    // (inside a loop the compiler's counter bookkeeping would wait before each)
+    if (!ll_round<NMAX, F32>(a, c, ctl, src, mine, o, ch, C, x))
+        return;
+    for (uint32_t it = 1; it < rounds; ++it) {
+        wait_stores();
+        ch += step;
+        x = ch < C ? ld8<CP_PLAIN>(inr, ch * 8u) : u32x2{0u, 0u};
+        if (!ll_round<NMAX, F32>(a, c, ctl, src, mine, o, ch, C, x))
+            return;
     }
     finish(a, c);
 }
@@ -215,71 +290,78 @@ template <int NMAX, bool F32>
 __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
 {
     Ctx0 c;
-    c.t0 = clock100();
-    c.rank = blockIdx.x % a.n_ranks;
-    c.part = blockIdx.x / a.n_ranks;
+    begin(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t G = a.n >> 3;
     const uint32_t bytes = a.n * 2u;
     const uint32_t step = a.parts * blockDim.x;
     const uint32_t rounds = (G + step - 1u) / step;
-    uint32_t seq = load_seq(a);
-    c.flag = seq + a.epoch;
-    c.par = a.epoch & 1u;
-    const Ctl ctl{a.ctl};
     const __amdgpu_buffer_rsrc_t inr = in_rsrc(a, c.rank);
-    // inbox(recv, send) = s1 + ((recv*N + send)*2 + par) * stride
+    const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
+    uint32_t ch = c.part * blockDim.x + threadIdx.x;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (ch < G)
+        x = ld16<CP_PLAIN>(inr, ch * 16u);
+    raise_arrival(a, c);
+    c.flag = load_seq(a) + a.epoch;
+    const Ctl ctl{a.ctl};
     auto inbox = [&](uint32_t recv, uint32_t send) {
         return rsrc(a.s1 + (size_t)((recv * N + send) * 2u + c.par) * a.s1_stride, bytes);
     };
+    start_delay(a, c);
 
-    for (uint32_t it = 0; it < rounds; ++it) {
-        const uint32_t ch = c.part * blockDim.x + threadIdx.x + it * step;
+    auto round = [&](uint32_t ch, u32x4 x) -> bool {
         const bool active = ch < G;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (active)
-            x = ld16<CP_PLAIN>(inr, ch * 16u);
-        if (it == 0)
-            start_delay(a, c);
         if (active) {
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((uint32_t)s < N && (uint32_t)s != c.rank)
                     st16<CP_DEV>(x, inbox((uint32_t)s, c.rank), ch * 16u);
         }
-        u32x4 V[NMAX];
         uint32_t pend = 0;
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s) {
-            if ((uint32_t)s < N && (uint32_t)s != c.rank && active) {
-                V[s] = ld16<CP_DEV>(inbox(c.rank, (uint32_t)s), ch * 16u);
+        for (int s = 0; s < NMAX; ++s)
+            if ((uint32_t)s < N && (uint32_t)s != c.rank && active)
                 pend |= 1u << s;
-            }
-        }
-        Watch w;
-        w.begin(a.watchdog_ticks);
-        while (true) {
+        u32x4 A0[NMAX], A1[NMAX], V[NMAX];
+        auto issue = [&](u32x4 *A) {
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((pend >> s) & 1u)
-                    if (sent_ready(V[s]))
+                    A[s] = ld16<CP_DEV>(inbox(c.rank, (uint32_t)s), ch * 16u);
+        };
+        auto check = [&](const u32x4 *A) {
+#pragma unroll
+            for (int s = 0; s < NMAX; ++s)
+                if ((pend >> s) & 1u)
+                    if (sent_ready(A[s])) {
                         pend &= ~(1u << s);
+                        V[s] = A[s];
+                    }
+        };
+        Watch w;
+        w.begin(a.watchdog_ticks);
+        issue(A0);
+        while (true) {
+            compiler_fence();
+            issue(A1);
+            check(A0);
             if (!wave_any(pend != 0u))
                 break;
             if (w.expired(ctl, c.rank, pend ? first_bit(pend) : 0u, c.flag))
-                return;
+                return false;
             compiler_fence();
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((pend >> s) & 1u)
-                    V[s] = ld16<CP_DEV>(inbox(c.rank, (uint32_t)s), ch * 16u);
+            issue(A0);
+            check(A1);
+            if (!wave_any(pend != 0u))
+                break;
         }
         if (active) {
             Acc8 acc;
 #pragma unroll
             for (int s = 0; s < NMAX; ++s) {
                 if ((uint32_t)s < N) {
-                    u32x4 v = ((uint32_t)s == c.rank) ? x : V[s];
+                    const u32x4 v = ((uint32_t)s == c.rank) ? x : V[s];
                     if (s == 0) acc.init(v); else acc.add(v);
                 }
             }
@@ -288,112 +370,202 @@ __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
             for (int s = 0; s < NMAX; ++s)
                 if ((uint32_t)s < N && (uint32_t)s != c.rank)
                     st16<CP_DEV>(sentinel4(), inbox(c.rank, (uint32_t)s), ch * 16u);
-            store_out8<F32>(a, c.rank, ch * 8u, acc);
+            store8<F32>(o, ch * 8u, acc);
         }
+        return true;
+    };
+    // round 0 straight-line (see the one-shot LL kernel), later rounds looped
+    if (!round(ch, x))
+        return;
+    for (uint32_t it = 1; it < rounds; ++it) {
+        wait_stores();
+        ch += step;
+        x = ch < G ? ld16<CP_PLAIN>(inr, ch * 16u) : u32x4{0u, 0u, 0u, 0u};
+        if (!round(ch, x))
+            return;
     }
     finish(a, c);
 }
 
 // ========================================================= one-shot DIRECT
-// Every workgroup of rank r raises r's arrival flag for this call; a reader
-// of rank s's input waits until s's arrival flag has reached the call's flag
-// and then reads in[s] in place.  Meant for messages too large for staging
-// copies; the input of call k must stay unchanged until call k completes on
-// every rank (the application-level A/B double buffering of the SiFAR page,
-// "SiFAR：无同步All-Reduce技术突破低延迟LLM推理瓶颈", technique one).
-__device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, const Ctl &ctl)
-{
-    const uint32_t lane = threadIdx.x & 63u;
-    bool need = lane < a.n_ranks;
-    uint32_t off = (CTL_ARRIVE + 32u * lane) * 4u;
-    __amdgpu_buffer_rsrc_t r = rsrc(a.ctl, CTL_WORDS * 4u);
-    Watch w;
-    w.begin(a.watchdog_ticks);
-    while (true) {
-        if (need) {
-            uint32_t v = ld4<CP_DEV>(r, off);
-            if ((int32_t)(v - c.flag) >= 0)
-                need = false;
-        }
-        if (!wave_any(need))
-            return true;
-        if (w.expired(ctl, c.rank, lane, c.flag))
-            return false;
-        compiler_fence();
-    }
-}
-
-__device__ __forceinline__ void raise_arrival(const Launch &a, const Ctx0 &c)
-{
-    if (threadIdx.x == 0) {
-        __amdgpu_buffer_rsrc_t r = rsrc(a.ctl, CTL_WORDS * 4u);
-        st4<CP_DEV>(c.flag, r, (CTL_ARRIVE + 32u * c.rank) * 4u);
-    }
-}
-
+// After the arrival counters, each rank reads every peer's input in place
+// with device-coherent loads and reduces.  The input of call k must stay
+// unchanged until call k has completed on every rank (the application-level
+// A/B double buffering of the SiFAR page, "SiFAR：无同步All-Reduce技术突破低
+// 延迟LLM推理瓶颈", technique one).
 template <int NMAX, bool F32>
 __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
 {
     Ctx0 c;
-    c.t0 = clock100();
-    c.rank = blockIdx.x % a.n_ranks;
-    c.part = blockIdx.x / a.n_ranks;
+    begin(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t G = a.n >> 3;
     const uint32_t step = a.parts * blockDim.x;
     const uint32_t rounds = (G + step - 1u) / step;
-    uint32_t seq = load_seq(a);
-    c.flag = seq + a.epoch;
-    c.par = a.epoch & 1u;
+    if (a.delays == nullptr)
+        raise_arrival(a, c);
+    c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
-    start_delay(a, c);
-    raise_arrival(a, c);
+    if (a.delays != nullptr) {
+        start_delay(a, c);
+        raise_arrival(a, c);
+    }
     if (!wait_arrivals(a, c, ctl))
         return;
     __amdgpu_buffer_rsrc_t src[NMAX];
 #pragma unroll
     for (int s = 0; s < NMAX; ++s)
         src[s] = in_rsrc(a, (uint32_t)s < N ? (uint32_t)s : 0u);
-    for (uint32_t it = 0; it < rounds; ++it) {
-        const uint32_t ch = c.part * blockDim.x + threadIdx.x + it * step;
+    const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
+    uint32_t ch = c.part * blockDim.x + threadIdx.x;
+    for (uint32_t it = 0; it < rounds; ++it, ch += step) {
         if (ch >= G)
             continue;
         u32x4 V[NMAX];
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             if ((uint32_t)s < N)
-                V[s] = ld16<CP_PLAIN>(src[s], ch * 16u);
+                V[s] = ld16<CP_DEV>(src[s], ch * 16u);
         Acc8 acc;
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             if ((uint32_t)s < N) {
                 if (s == 0) acc.init(V[s]); else acc.add(V[s]);
             }
-        store_out8<F32>(a, c.rank, ch * 8u, acc);
+        store8<F32>(o, ch * 8u, acc);
+    }
+    finish(a, c);
+}
+
+// ========================================================= two-shot DIRECT
+// Reduce-scatter: rank q reads slice q of every rank's input in place (after
+// the arrival counters) and reduces it; all-gather: it stores the bf16
+// result straight into slice q of every rank's output (the bcast of the
+// reduced value), with device-scope stores.  Each workgroup then waits for
+// its stores to be acknowledged, raises its completion flag, and waits for
+// the completion flags of the same part index of every rank, after which
+// its part of every slice of its own output is known to be complete.
+// Moves exactly the algorithmic bytes: N inputs read once, N outputs written
+// once.
+template <int NMAX, bool F32>
+__global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
+{
+    Ctx0 c;
+    begin(a, c);
+    const uint32_t N = a.n_ranks;
+    const uint32_t q = c.rank;
+    const uint32_t L = a.slice;
+    const uint32_t lo = q * L;
+    const uint32_t Lq = lo >= a.n ? 0u : (a.n - lo < L ? a.n - lo : L);
+    const uint32_t G = Lq >> 3;                     // chunks of my slice
+    const uint32_t step = a.parts * blockDim.x;
+    if (a.delays == nullptr)
+        raise_arrival(a, c);
+    c.flag = load_seq(a) + a.epoch;
+    const Ctl ctl{a.ctl};
+    if (a.delays != nullptr) {
+        start_delay(a, c);
+        raise_arrival(a, c);
+    }
+    if (!wait_arrivals(a, c, ctl))
+        return;
+    __amdgpu_buffer_rsrc_t src[NMAX], dst[NMAX];
+#pragma unroll
+    for (int s = 0; s < NMAX; ++s) {
+        const uint32_t ss = (uint32_t)s < N ? (uint32_t)s : 0u;
+        src[s] = in_rsrc(a, ss);
+        dst[s] = out_rsrc(a, ss, F32);
+    }
+    // two chunks per lane per round keep more loads in flight
+    for (uint32_t ch = c.part * blockDim.x + threadIdx.x; ch < G; ch += 2u * step) {
+        const uint32_t ch2 = ch + step;
+        const bool two = ch2 < G;
+        u32x4 V[NMAX], W[NMAX];
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((uint32_t)s < N) {
+                V[s] = ld16<CP_DEV>(src[s], (lo + ch * 8u) * 2u);
+                W[s] = two ? ld16<CP_DEV>(src[s], (lo + ch2 * 8u) * 2u) : u32x4{0u, 0u, 0u, 0u};
+            }
+        Acc8 acc, acc2;
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((uint32_t)s < N) {
+                if (s == 0) { acc.init(V[s]); acc2.init(W[s]); }
+                else { acc.add(V[s]); acc2.add(W[s]); }
+            }
+#pragma unroll
+        for (int r = 0; r < NMAX; ++r)
+            if ((uint32_t)r < N) {
+                store8<F32, CP_DEV>(dst[r], lo + ch * 8u, acc);
+                if (two)
+                    store8<F32, CP_DEV>(dst[r], lo + ch2 * 8u, acc2);
+            }
+    }
+    // completion: my stores are at the coherence point, then my flag
+    wait_stores();
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t dn = rsrc(a.done, MAX_RANKS * DONE_STRIDE * 4u);
+    if (threadIdx.x == 0)
+        st4<CP_DEV>(c.flag, dn, (q * DONE_STRIDE + c.part) * 4u);
+    // wait for the same part of every rank (wave 0 only; the others are done)
+    if (threadIdx.x < 64u) {
+        const uint32_t lane = threadIdx.x;
+        bool need = lane < N;
+        const uint32_t off = ((lane & 15u) * DONE_STRIDE + c.part) * 4u;
+        Watch w;
+        w.begin(a.watchdog_ticks);
+        while (true) {
+            if (need) {
+                const uint32_t v = ld4<CP_DEV>(dn, off);
+                if ((int32_t)(v - c.flag) >= 0)
+                    need = false;
+            }
+            if (!wave_any(need))
+                break;
+            if (w.expired(ctl, q, lane, c.flag))
+                return;
+            compiler_fence();
+        }
     }
     finish(a, c);
 }
 
 // ============================================================ LL128 lines
-// Writes one lane's share of a line group: payload first; after every
-// payload store of the wave has been acknowledged at the device coherence
-// point, the flag lanes store the line flags.
-__device__ __forceinline__ void l128_publish(__amdgpu_buffer_rsrc_t dst, uint32_t goff,
-                                             uint32_t lane, const L128Lane &ln, u32x4 payload,
-                                             uint32_t flag)
+// Lane mapping of a line group (480 elements, 1024 bytes): see ar_proto.h.
+// A wave handles up to GB groups per batch: it publishes the payload of all
+// of them, waits once for the acknowledgements, then stores their flags;
+// a reader polls the flags of all its groups together, then loads payloads.
+constexpr int GB = 4;
+
+// reads 8 (or 4) elements of a bf16 buffer at element `e`
+template <int CP = CP_PLAIN>
+__device__ __forceinline__ u32x4 ld_elems(__amdgpu_buffer_rsrc_t r, uint32_t e, bool half)
 {
-    const uint32_t off = goff + lane * 16u;
-    if (ln.half) {
+    if (half) {
+        u32x2 p = ld8<CP>(r, e * 2u);
+        u32x4 v; v.x = p.x; v.y = p.y; v.z = 0u; v.w = 0u;
+        return v;
+    }
+    return ld16<CP>(r, e * 2u);
+}
+
+__device__ __forceinline__ void l128_store_payload(__amdgpu_buffer_rsrc_t dst, uint32_t off,
+                                                   bool half, u32x4 payload)
+{
+    if (half) {
         u32x2 p; p.x = payload.x; p.y = payload.y;
         st8<CP_DEV>(p, dst, off);
     } else {
         st16<CP_DEV>(payload, dst, off);
     }
-    wait_stores();
-    if (ln.half) {
-        u32x2 f; f.x = flag; f.y = ~flag;
-        st8<CP_DEV>(f, dst, off + 8u);
-    }
+}
+
+__device__ __forceinline__ void l128_store_flag(__amdgpu_buffer_rsrc_t dst, uint32_t off,
+                                                uint32_t flag)
+{
+    u32x2 f; f.x = flag; f.y = ~flag;
+    st8<CP_DEV>(f, dst, off + 8u);
 }
 
 __device__ __forceinline__ bool l128_flag_ok(u32x2 f, uint32_t flag)
@@ -401,146 +573,161 @@ __device__ __forceinline__ bool l128_flag_ok(u32x2 f, uint32_t flag)
     return f.x == flag && f.y == ~flag;
 }
 
-// Reads one line group of the N sources: flag lanes poll their line flags,
-// the wave votes, then every lane loads its payload.  lim[s] is the number
-// of valid elements of source s in the group index space; a line is polled
-// when any of its elements is valid.  Returns false on watchdog expiry.
-// `skip` names a source the caller already holds (or NMAX for none).
+// Receives GB line groups (slot j valid when gvalid bit j) from the N
+// sources: flag lanes poll the line flags of every (slot, source) still
+// pending, the wave votes, then every lane loads its payloads.  lim[s] is the
+// number of valid elements of source s in group index space; a line is
+// polled only if one of its elements is valid.  skip names a source the
+// caller holds already (or NMAX).  Returns false on watchdog expiry.
 template <int NMAX>
 __device__ __forceinline__ bool l128_receive(const __amdgpu_buffer_rsrc_t *src, uint32_t N,
-                                             uint32_t skip, uint32_t g, uint32_t lane,
-                                             const L128Lane &ln, const uint32_t *lim,
-                                             uint32_t flag, const Ctl &ctl, uint32_t rank,
-                                             uint32_t budget, u32x4 *V)
+                                             uint32_t skip, const uint32_t *g, uint32_t gvalid,
+                                             uint32_t lane, const L128Lane &ln,
+                                             const uint32_t *lim, uint32_t flag, const Ctl &ctl,
+                                             uint32_t rank, uint32_t budget, u32x4 (*V)[NMAX])
 {
-    const uint32_t goff = g * L128_BYTES;
-    const uint32_t off = goff + lane * 16u;
-    const uint32_t e = g * L128_ELEMS + ln.elem;
-    const uint32_t line_first = g * L128_ELEMS + 56u * (lane >> 3);
-    uint32_t pend = 0;
-    u32x2 F[NMAX];
+    uint32_t pend[GB];
+    u32x2 F[GB][NMAX];
 #pragma unroll
-    for (int s = 0; s < NMAX; ++s) {
-        if ((uint32_t)s < N && (uint32_t)s != skip && ln.half && line_first < lim[s]) {
-            F[s] = ld8<CP_DEV>(src[s], off + 8u);
-            pend |= 1u << s;
-        }
+    for (int j = 0; j < GB; ++j) {
+        pend[j] = 0;
+        if (!((gvalid >> j) & 1u))
+            continue;
+        const uint32_t line_first = g[j] * L128_ELEMS + 56u * (lane >> 3);
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((uint32_t)s < N && (uint32_t)s != skip && ln.half && line_first < lim[s]) {
+                F[j][s] = ld8<CP_DEV>(src[s], g[j] * L128_BYTES + lane * 16u + 8u);
+                pend[j] |= 1u << s;
+            }
     }
     Watch w;
     w.begin(budget);
     while (true) {
+        uint32_t any = 0;
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((pend >> s) & 1u)
-                if (l128_flag_ok(F[s], flag))
-                    pend &= ~(1u << s);
-        if (!wave_any(pend != 0u))
+        for (int j = 0; j < GB; ++j) {
+#pragma unroll
+            for (int s = 0; s < NMAX; ++s)
+                if ((pend[j] >> s) & 1u)
+                    if (l128_flag_ok(F[j][s], flag))
+                        pend[j] &= ~(1u << s);
+            any |= pend[j];
+        }
+        if (!wave_any(any != 0u))
             break;
-        if (w.expired(ctl, rank, pend ? first_bit(pend) : 0u, flag))
+        if (w.expired(ctl, rank, any ? first_bit(any) : 0u, flag))
             return false;
         compiler_fence();
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((pend >> s) & 1u)
-                F[s] = ld8<CP_DEV>(src[s], off + 8u);
+        for (int j = 0; j < GB; ++j)
+#pragma unroll
+            for (int s = 0; s < NMAX; ++s)
+                if ((pend[j] >> s) & 1u)
+                    F[j][s] = ld8<CP_DEV>(src[s], g[j] * L128_BYTES + lane * 16u + 8u);
     }
-    // every needed line of the group is complete: read the payloads
+    // every needed line is complete: load the payloads
     compiler_fence();
 #pragma unroll
-    for (int s = 0; s < NMAX; ++s) {
-        if ((uint32_t)s < N && (uint32_t)s != skip && e < lim[s]) {
-            if (ln.half) {
-                u32x2 p = ld8<CP_DEV>(src[s], off);
-                V[s].x = p.x; V[s].y = p.y; V[s].z = 0u; V[s].w = 0u;
-            } else {
-                V[s] = ld16<CP_DEV>(src[s], off);
+    for (int j = 0; j < GB; ++j) {
+        if (!((gvalid >> j) & 1u))
+            continue;
+        const uint32_t e = g[j] * L128_ELEMS + ln.elem;
+        const uint32_t off = g[j] * L128_BYTES + lane * 16u;
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s) {
+            if ((uint32_t)s < N && (uint32_t)s != skip && e < lim[s]) {
+                if (ln.half) {
+                    const u32x2 p = ld8<CP_DEV>(src[s], off);
+                    V[j][s].x = p.x; V[j][s].y = p.y; V[j][s].z = 0u; V[j][s].w = 0u;
+                } else {
+                    V[j][s] = ld16<CP_DEV>(src[s], off);
+                }
             }
         }
     }
     return true;
 }
 
-// reads 8 (or 4) elements of a bf16 buffer at element `e`
-__device__ __forceinline__ u32x4 ld_elems(__amdgpu_buffer_rsrc_t r, uint32_t e, bool half)
-{
-    if (half) {
-        u32x2 p = ld8<CP_PLAIN>(r, e * 2u);
-        u32x4 v; v.x = p.x; v.y = p.y; v.z = 0u; v.w = 0u;
-        return v;
-    }
-    return ld16<CP_PLAIN>(r, e * 2u);
-}
-
 template <bool F32>
-__device__ __forceinline__ void store_lane(const Launch &a, uint32_t rank, uint32_t e, bool half,
+__device__ __forceinline__ void store_lane(__amdgpu_buffer_rsrc_t o, uint32_t e, bool half,
                                            const Acc8 &acc)
 {
-    if (half) store_out4<F32>(a, rank, e, acc); else store_out8<F32>(a, rank, e, acc);
+    if (half) store4<F32>(o, e, acc.v); else store8<F32>(o, e, acc);
 }
 
 // ====================================================== one-shot LL128
-// Rank r publishes its whole input as line groups (480 elements each); each
-// wave owns a set of groups, publishes all of them, then receives and
-// reduces the same groups from every rank.
+// Rank r publishes its whole input as line groups; a wave owns the groups
+// g0, g0 + gstep, ... and handles them GB at a time: publish all payloads,
+// one acknowledgement wait, all flags; then receive and reduce.
 template <int NMAX, bool F32>
 __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 {
     Ctx0 c;
-    c.t0 = clock100();
-    c.rank = blockIdx.x % a.n_ranks;
-    c.part = blockIdx.x / a.n_ranks;
+    begin(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t waves = blockDim.x >> 6;
     const uint32_t groups = (a.n + L128_ELEMS - 1u) / L128_ELEMS;
     const uint32_t gstep = a.parts * waves;
-    const uint32_t g0 = c.part * waves + wave;
     const uint32_t mb_bytes = groups * L128_BYTES;
-    uint32_t seq = load_seq(a);
-    c.flag = seq + a.epoch;
-    c.par = a.epoch & 1u;
+    raise_arrival(a, c);
+    c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     const L128Lane ln = l128_lane(lane);
     const __amdgpu_buffer_rsrc_t inr = in_rsrc(a, c.rank);
+    const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
     __amdgpu_buffer_rsrc_t src[NMAX];
 #pragma unroll
     for (int s = 0; s < NMAX; ++s)
         src[s] = rsrc(a.l128 + (size_t)((uint32_t)s * 2u + c.par) * a.l128_stride, mb_bytes);
-
-    bool first = true;
-    for (uint32_t g = g0; g < groups; g += gstep) {
-        const uint32_t e = g * L128_ELEMS + ln.elem;
-        const bool active = e < a.n;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (active)
-            x = ld_elems(inr, e, ln.half);
-        if (first) { start_delay(a, c); first = false; }
-        l128_publish(src[c.rank], g * L128_BYTES, lane, ln, x, c.flag);
-    }
-    if (first)
-        start_delay(a, c);
-    for (uint32_t g = g0; g < groups; g += gstep) {
-        const uint32_t e = g * L128_ELEMS + ln.elem;
-        const bool active = e < a.n;
-        u32x4 V[NMAX];
-        uint32_t lim[NMAX];
+    const __amdgpu_buffer_rsrc_t mine =
+        rsrc(a.l128 + (size_t)(c.rank * 2u + c.par) * a.l128_stride, mb_bytes);
+    uint32_t lim[NMAX];
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s) lim[s] = a.n;
-        if (!l128_receive<NMAX>(src, N, c.rank, g, lane, ln, lim, c.flag, ctl, c.rank,
+    for (int s = 0; s < NMAX; ++s)
+        lim[s] = a.n;
+    start_delay(a, c);
+
+    for (uint32_t base = c.part * waves + wave; base < groups; base += gstep * GB) {
+        uint32_t g[GB];
+        uint32_t gvalid = 0;
+        u32x4 x[GB];
+#pragma unroll
+        for (int j = 0; j < GB; ++j) {
+            g[j] = base + (uint32_t)j * gstep;
+            if (g[j] < groups)
+                gvalid |= 1u << j;
+            const uint32_t e = g[j] * L128_ELEMS + ln.elem;
+            x[j] = (g[j] < groups && e < a.n) ? ld_elems(inr, e, ln.half) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < GB; ++j)
+            if ((gvalid >> j) & 1u)
+                l128_store_payload(mine, g[j] * L128_BYTES + lane * 16u, ln.half, x[j]);
+        wait_stores();
+#pragma unroll
+        for (int j = 0; j < GB; ++j)
+            if (((gvalid >> j) & 1u) && ln.half)
+                l128_store_flag(mine, g[j] * L128_BYTES + lane * 16u, c.flag);
+        u32x4 V[GB][NMAX];
+        if (!l128_receive<NMAX>(src, N, c.rank, g, gvalid, lane, ln, lim, c.flag, ctl, c.rank,
                                 a.watchdog_ticks, V))
             return;
-        if (active) {
-            u32x4 x = ld_elems(inr, e, ln.half);
+#pragma unroll
+        for (int j = 0; j < GB; ++j) {
+            const uint32_t e = g[j] * L128_ELEMS + ln.elem;
+            if (!((gvalid >> j) & 1u) || e >= a.n)
+                continue;
             Acc8 acc;
 #pragma unroll
-            for (int s = 0; s < NMAX; ++s) {
+            for (int s = 0; s < NMAX; ++s)
                 if ((uint32_t)s < N) {
-                    u32x4 v = ((uint32_t)s == c.rank) ? x : V[s];
+                    const u32x4 v = ((uint32_t)s == c.rank) ? x[j] : V[j][s];
                     if (s == 0) acc.init(v); else acc.add(v);
                 }
-            }
-            store_lane<F32>(a, c.rank, e, ln.half, acc);
+            store_lane<F32>(o, e, ln.half, acc);
         }
     }
     finish(a, c);
@@ -548,17 +735,15 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 
 // ====================================================== two-shot LL128
 // Reduce-scatter: rank q reduces slice q (elements [q*L, q*L + Lq)) reading
-// every rank's input in place after its arrival flag, and publishes the
+// every rank's input in place after the arrival counters, and publishes the
 // bf16 result as line groups.  All-gather: rank q receives every slice's
-// groups and writes them to out[q].  A wave owns the same group indices in
-// both phases, so its own slice's result stays in registers.
+// groups (its own from registers) and writes them to out[q].  Groups are
+// handled GB at a time per wave as in the one-shot kernel.
 template <int NMAX, bool F32>
 __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 {
     Ctx0 c;
-    c.t0 = clock100();
-    c.rank = blockIdx.x % a.n_ranks;
-    c.part = blockIdx.x / a.n_ranks;
+    begin(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t q = c.rank;
     const uint32_t L = a.slice;
@@ -567,40 +752,55 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
     const uint32_t waves = blockDim.x >> 6;
     const uint32_t groups = (L + L128_ELEMS - 1u) / L128_ELEMS;
     const uint32_t gstep = a.parts * waves;
-    const uint32_t g0 = c.part * waves + wave;
     const uint32_t mb_bytes = groups * L128_BYTES;
-    uint32_t seq = load_seq(a);
-    c.flag = seq + a.epoch;
-    c.par = a.epoch & 1u;
+    if (a.delays == nullptr)
+        raise_arrival(a, c);
+    c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     const L128Lane ln = l128_lane(lane);
-    auto slice_len = [&](uint32_t s) -> uint32_t {
-        uint32_t lo = s * L;
-        return lo >= a.n ? 0u : (a.n - lo < L ? a.n - lo : L);
-    };
-    start_delay(a, c);
-    raise_arrival(a, c);
+    if (a.delays != nullptr) {
+        start_delay(a, c);
+        raise_arrival(a, c);
+    }
     if (!wait_arrivals(a, c, ctl))
         return;
+    uint32_t lim[NMAX];
     __amdgpu_buffer_rsrc_t inp[NMAX], stg[NMAX];
 #pragma unroll
     for (int s = 0; s < NMAX; ++s) {
-        uint32_t ss = (uint32_t)s < N ? (uint32_t)s : 0u;
+        const uint32_t ss = (uint32_t)s < N ? (uint32_t)s : 0u;
         inp[s] = in_rsrc(a, ss);
         stg[s] = rsrc(a.l128 + (size_t)(ss * 2u + c.par) * a.l128_stride, mb_bytes);
+        const uint32_t slo = ss * L;
+        lim[s] = ((uint32_t)s >= N || slo >= a.n) ? 0u : (a.n - slo < L ? a.n - slo : L);
     }
-    const uint32_t Lq = slice_len(q);
-    // ---- reduce-scatter
-    for (uint32_t g = g0; g < groups; g += gstep) {
-        const uint32_t e = g * L128_ELEMS + ln.elem;
-        const bool active = e < Lq;
-        u32x4 red = {0u, 0u, 0u, 0u};
-        if (active) {
+    const uint32_t Lq = (q * L >= a.n) ? 0u : (a.n - q * L < L ? a.n - q * L : L);
+    const __amdgpu_buffer_rsrc_t o = out_rsrc(a, q, F32);
+    const __amdgpu_buffer_rsrc_t mine =
+        rsrc(a.l128 + (size_t)(q * 2u + c.par) * a.l128_stride, mb_bytes);
+
+    for (uint32_t base = c.part * waves + wave; base < groups; base += gstep * GB) {
+        uint32_t g[GB];
+        uint32_t gvalid = 0;
+#pragma unroll
+        for (int j = 0; j < GB; ++j) {
+            g[j] = base + (uint32_t)j * gstep;
+            if (g[j] < groups)
+                gvalid |= 1u << j;
+        }
+        // ---- reduce-scatter of up to GB groups
+        u32x4 red[GB];
+#pragma unroll
+        for (int j = 0; j < GB; ++j) {
+            red[j] = u32x4{0u, 0u, 0u, 0u};
+            const uint32_t e = g[j] * L128_ELEMS + ln.elem;
+            if (!((gvalid >> j) & 1u) || e >= Lq)
+                continue;
             u32x4 V[NMAX];
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((uint32_t)s < N)
-                    V[s] = ld_elems(inp[s], q * L + e, ln.half);
+                    V[s] = ld_elems<CP_DEV>(inp[s], q * L + e, ln.half);
             Acc8 acc;
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
@@ -610,39 +810,42 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
             if constexpr (F32) {
                 // debug path: the owner writes its slice's accumulators to every copy
                 for (uint32_t r = 0; r < N; ++r)
-                    store_lane<true>(a, r, q * L + e, ln.half, acc);
+                    store_lane<true>(out_rsrc(a, r, true), q * L + e, ln.half, acc);
             } else {
-                red = acc.bf16();
+                red[j] = acc.bf16();
             }
         }
-        if constexpr (!F32)
-            l128_publish(stg[q], g * L128_BYTES, lane, ln, red, c.flag);
-    }
-    if constexpr (F32) {
-        finish(a, c);
-        return;
-    }
-    // ---- all-gather
-    uint32_t lim[NMAX];
+        if constexpr (F32)
+            continue;
 #pragma unroll
-    for (int s = 0; s < NMAX; ++s)
-        lim[s] = (uint32_t)s < N ? slice_len((uint32_t)s) : 0u;
-    char *outq = (char *)a.out + (size_t)q * a.n * 2u;
-    const __amdgpu_buffer_rsrc_t oq = rsrc(outq, a.n * 2u);
-    for (uint32_t g = g0; g < groups; g += gstep) {
-        const uint32_t e = g * L128_ELEMS + ln.elem;
-        u32x4 V[NMAX];
-        if (!l128_receive<NMAX>(stg, N, (uint32_t)NMAX, g, lane, ln, lim, c.flag, ctl, q,
+        for (int j = 0; j < GB; ++j)
+            if ((gvalid >> j) & 1u)
+                l128_store_payload(mine, g[j] * L128_BYTES + lane * 16u, ln.half, red[j]);
+        wait_stores();
+#pragma unroll
+        for (int j = 0; j < GB; ++j)
+            if (((gvalid >> j) & 1u) && ln.half)
+                l128_store_flag(mine, g[j] * L128_BYTES + lane * 16u, c.flag);
+        // ---- all-gather of the same groups
+        u32x4 V[GB][NMAX];
+        if (!l128_receive<NMAX>(stg, N, q, g, gvalid, lane, ln, lim, c.flag, ctl, q,
                                 a.watchdog_ticks, V))
             return;
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s) {
-            if ((uint32_t)s < N && e < lim[s]) {
-                if (ln.half) {
-                    u32x2 p; p.x = V[s].x; p.y = V[s].y;
-                    st8<CP_PLAIN>(p, oq, ((uint32_t)s * L + e) * 2u);
-                } else {
-                    st16<CP_PLAIN>(V[s], oq, ((uint32_t)s * L + e) * 2u);
+        for (int j = 0; j < GB; ++j) {
+            if (!((gvalid >> j) & 1u))
+                continue;
+            const uint32_t e = g[j] * L128_ELEMS + ln.elem;
+#pragma unroll
+            for (int s = 0; s < NMAX; ++s) {
+                if ((uint32_t)s < N && e < lim[s]) {
+                    const u32x4 v = ((uint32_t)s == q) ? red[j] : V[j][s];
+                    if (ln.half) {
+                        u32x2 p; p.x = v.x; p.y = v.y;
+                        st8<CP_PLAIN>(p, o, ((uint32_t)s * L + e) * 2u);
+                    } else {
+                        st16<CP_PLAIN>(v, o, ((uint32_t)s * L + e) * 2u);
+                    }
                 }
             }
         }
@@ -659,9 +862,7 @@ template <int NMAX, bool F32>
 __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
 {
     Ctx0 c;
-    c.t0 = clock100();
-    c.rank = blockIdx.x % a.n_ranks;
-    c.part = blockIdx.x / a.n_ranks;
+    begin(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t q = c.rank;
     const uint32_t L = a.slice;
@@ -669,9 +870,8 @@ __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
     const uint32_t step = a.parts * blockDim.x;
     const uint32_t rounds = (G + step - 1u) / step;
     const uint32_t ibytes = L * 2u;
-    uint32_t seq = load_seq(a);
-    c.flag = seq + a.epoch;
-    c.par = a.epoch & 1u;
+    raise_arrival(a, c);
+    c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     const __amdgpu_buffer_rsrc_t inq = in_rsrc(a, q);
     auto rs = [&](uint32_t recv, uint32_t send) {
@@ -685,8 +885,7 @@ __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
         return lo >= a.n ? 0u : (a.n - lo < L ? a.n - lo : L);
     };
     const uint32_t Lq = slice_len(q);
-    char *outq = (char *)a.out + (size_t)q * a.n * (F32 ? 4u : 2u);
-    const __amdgpu_buffer_rsrc_t oq = rsrc(outq, a.n * (F32 ? 4u : 2u));
+    const __amdgpu_buffer_rsrc_t oq = out_rsrc(a, q, F32);
 
     for (uint32_t it = 0; it < rounds; ++it) {
         const uint32_t ch = c.part * blockDim.x + threadIdx.x + it * step;
@@ -709,38 +908,56 @@ __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
         }
         // ---- receive my slice from everyone, reduce, re-arm
         const bool act = e < Lq;
-        u32x4 V[NMAX];
         uint32_t pend = 0;
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N && (uint32_t)s != q && act) {
-                V[s] = ld16<CP_DEV>(rs(q, (uint32_t)s), e * 2u);
+            if ((uint32_t)s < N && (uint32_t)s != q && act)
                 pend |= 1u << s;
-            }
-        Watch w;
-        w.begin(a.watchdog_ticks);
-        while (true) {
+        u32x4 A0[NMAX], A1[NMAX], V[NMAX];
+        auto issue_rs = [&](u32x4 *A) {
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((pend >> s) & 1u)
-                    if (sent_ready(V[s]))
+                    A[s] = ld16<CP_DEV>(rs(q, (uint32_t)s), e * 2u);
+        };
+        auto issue_ag = [&](u32x4 *A) {
+#pragma unroll
+            for (int s = 0; s < NMAX; ++s)
+                if ((pend >> s) & 1u)
+                    A[s] = ld16<CP_DEV>(ag(q, (uint32_t)s), e * 2u);
+        };
+        auto check = [&](const u32x4 *A) {
+#pragma unroll
+            for (int s = 0; s < NMAX; ++s)
+                if ((pend >> s) & 1u)
+                    if (sent_ready(A[s])) {
                         pend &= ~(1u << s);
+                        V[s] = A[s];
+                    }
+        };
+        Watch w;
+        w.begin(a.watchdog_ticks);
+        issue_rs(A0);
+        while (true) {
+            compiler_fence();
+            issue_rs(A1);
+            check(A0);
             if (!wave_any(pend != 0u))
                 break;
             if (w.expired(ctl, q, pend ? first_bit(pend) : 0u, c.flag))
                 return;
             compiler_fence();
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((pend >> s) & 1u)
-                    V[s] = ld16<CP_DEV>(rs(q, (uint32_t)s), e * 2u);
+            issue_rs(A0);
+            check(A1);
+            if (!wave_any(pend != 0u))
+                break;
         }
         if (act) {
             Acc8 acc;
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((uint32_t)s < N) {
-                    u32x4 v = ((uint32_t)s == q) ? own : V[s];
+                    const u32x4 v = ((uint32_t)s == q) ? own : V[s];
                     if (s == 0) acc.init(v); else acc.add(v);
                 }
 #pragma unroll
@@ -750,14 +967,14 @@ __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
             if constexpr (F32) {
                 // debug path: the owner writes its slice's accumulators to every copy
                 for (uint32_t r = 0; r < N; ++r)
-                    store_out8<true>(a, r, q * L + e, acc);
+                    store8<true>(out_rsrc(a, r, true), q * L + e, acc);
             } else {
                 const u32x4 red = acc.bf16();
 #pragma unroll
                 for (int r = 0; r < NMAX; ++r)
                     if ((uint32_t)r < N && (uint32_t)r != q)
                         st16<CP_DEV>(red, ag((uint32_t)r, q), e * 2u);
-                store_out8<false>(a, q, q * L + e, acc);
+                st16<CP_PLAIN>(red, oq, (q * L + e) * 2u);
             }
         }
         if constexpr (F32)
@@ -766,26 +983,23 @@ __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
         pend = 0;
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N && (uint32_t)s != q && e < slice_len((uint32_t)s)) {
-                V[s] = ld16<CP_DEV>(ag(q, (uint32_t)s), e * 2u);
+            if ((uint32_t)s < N && (uint32_t)s != q && e < slice_len((uint32_t)s))
                 pend |= 1u << s;
-            }
         w.begin(a.watchdog_ticks);
+        issue_ag(A0);
         while (true) {
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((pend >> s) & 1u)
-                    if (sent_ready(V[s]))
-                        pend &= ~(1u << s);
+            compiler_fence();
+            issue_ag(A1);
+            check(A0);
             if (!wave_any(pend != 0u))
                 break;
             if (w.expired(ctl, q, pend ? first_bit(pend) : 0u, c.flag))
                 return;
             compiler_fence();
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((pend >> s) & 1u)
-                    V[s] = ld16<CP_DEV>(ag(q, (uint32_t)s), e * 2u);
+            issue_ag(A0);
+            check(A1);
+            if (!wave_any(pend != 0u))
+                break;
         }
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
@@ -793,17 +1007,20 @@ __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
                 st16<CP_PLAIN>(V[s], oq, ((uint32_t)s * L + e) * 2u);
                 st16<CP_DEV>(sentinel4(), ag(q, (uint32_t)s), e * 2u);
             }
+        wait_stores();
     }
     finish(a, c);
 }
 
 // ============================================================ maintenance
 // Advances the flag sequence after a step of `calls` calls.  When the
-// sequence nears the top of its 32-bit range, every flag word is cleared and
-// the sequence restarts, so a flag value left in memory long ago can never
-// match a future call.
+// sequence nears the top of its 32-bit range, every flag word (LL units,
+// LL128 lines, arrival counters, completion flags) is cleared and the
+// sequence restarts, so a flag value left in memory long ago can never match
+// a future call.
 __global__ __launch_bounds__(256) void k_step_end(uint32_t *ctl, uint32_t calls, char *ll,
-                                                  size_t ll_bytes, char *l128, size_t l128_bytes)
+                                                  size_t ll_bytes, char *l128, size_t l128_bytes,
+                                                  uint32_t *done)
 {
     __shared__ uint32_t wrap;
     if (threadIdx.x == 0) {
@@ -817,6 +1034,7 @@ __global__ __launch_bounds__(256) void k_step_end(uint32_t *ctl, uint32_t calls,
         for (size_t i = threadIdx.x; i < ll_bytes / 4; i += blockDim.x) w[i] = 0u;
         w = (uint32_t *)l128;
         for (size_t i = threadIdx.x; i < l128_bytes / 4; i += blockDim.x) w[i] = 0u;
+        for (size_t i = threadIdx.x; i < (size_t)MAX_RANKS * DONE_STRIDE; i += blockDim.x) done[i] = 0u;
         for (uint32_t i = threadIdx.x; i < (uint32_t)MAX_RANKS; i += blockDim.x)
             __hip_atomic_store(ctl + CTL_ARRIVE + 32u * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __threadfence();
@@ -850,6 +1068,7 @@ static const void *pick(int kind)
     case K_ONESHOT_LL128: return (const void *)k_oneshot_ll128<NMAX, F32>;
     case K_TWOSHOT_LL128: return (const void *)k_twoshot_ll128<NMAX, F32>;
     case K_TWOSHOT_SENTINEL: return (const void *)k_twoshot_sentinel<NMAX, F32>;
+    case K_TWOSHOT_DIRECT: return (const void *)k_twoshot_direct<NMAX, F32>;
     default: return nullptr;
     }
 }
@@ -872,10 +1091,10 @@ hipError_t launch_ar(int kind, bool f32, const Launch &a, uint32_t grid, uint32_
 }
 
 hipError_t launch_step_end(uint32_t *ctl, uint32_t calls, char *ll, size_t ll_bytes, char *l128,
-                           size_t l128_bytes, hipStream_t stream)
+                           size_t l128_bytes, uint32_t *done, hipStream_t stream)
 {
     hipLaunchKernelGGL(k_step_end, dim3(1), dim3(256), 0, stream, ctl, calls, ll, ll_bytes, l128,
-                       l128_bytes);
+                       l128_bytes, done);
     return hipGetLastError();
 }
 

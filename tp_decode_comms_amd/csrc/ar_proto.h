@@ -43,6 +43,8 @@ constexpr int CTL_STATUS = 32;      // {code, rank, source, flag}
 constexpr int CTL_ARRIVE = 64;      // arrival flag of rank r at CTL_ARRIVE + 32*r
 constexpr int CTL_WORDS = CTL_ARRIVE + 32 * MAX_RANKS;
 constexpr uint32_t STATUS_TIMEOUT = 6;
+constexpr uint32_t DONE_STRIDE = 8192;
+constexpr uint32_t TS_SUB = 64;          // timestamp sub-slots per call   // completion flags per rank (>= workgroups per rank)
 
 // LL128 line group: 8 lines of 128 B = one wave-wide 16 B access; 60 chunks
 // of 8 elements carried as 56 full lanes + 8 half lanes (the lane at
@@ -61,6 +63,7 @@ struct Launch {
     uint32_t *ctl;                // control block (CTL_WORDS)
     uint64_t *ts;                 // timestamps [slots][2] or null
     const uint32_t *delays;       // start delays [rows][N] ns or null
+    uint32_t *done;               // two-shot DIRECT completion flags [rank][DONE_STRIDE]
     uint32_t ll_stride, l128_stride, s1_stride, s2_stride;
     uint32_t n;                   // elements per rank
     uint32_t n_ranks;
@@ -107,11 +110,18 @@ template <int CP> __device__ __forceinline__ void st4(uint32_t v, __amdgpu_buffe
 // Forces re-issue of loads inside a poll loop (no instruction is emitted).
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// Waits until this wave's earlier stores have been acknowledged.  For stores
-// issued with the device-scope policy the acknowledgement means the data is
-// at the device coherence point, so a flag stored afterwards is never seen
-// before the payload.
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits until this wave's earlier vector memory operations have completed:
+// loads have returned and stores have been acknowledged.  For stores issued
+// with the device-scope policy the acknowledgement means the data is at the
+// device coherence point, so a flag stored afterwards is never seen before
+// the payload.  Emitted through the builtin (s_waitcnt vmcnt(0), other
+// counters untouched) so that the compiler's own wait insertion knows the
+// counter is drained.
+__device__ __forceinline__ void wait_stores()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    compiler_fence();
+}
 
 __device__ __forceinline__ uint64_t clock100() { return __builtin_amdgcn_s_memrealtime(); }
 
@@ -134,6 +144,19 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
     return (uint32_t)__builtin_bit_cast(uint16_t, x) |
            ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
+
+// 4-element accumulator (one 8-byte lane chunk).
+struct Acc4 {
+    float v[4];
+    __device__ __forceinline__ void init(uint32_t w0, uint32_t w1)
+    {
+        v[0] = lo_f(w0); v[1] = hi_f(w0); v[2] = lo_f(w1); v[3] = hi_f(w1);
+    }
+    __device__ __forceinline__ void add(uint32_t w0, uint32_t w1)
+    {
+        v[0] += lo_f(w0); v[1] += hi_f(w0); v[2] += lo_f(w1); v[3] += hi_f(w1);
+    }
+};
 
 // 8-element accumulator.  init() starts from rank 0's values; add() is one
 // binary32 addition per element, in the order the caller invokes it.
