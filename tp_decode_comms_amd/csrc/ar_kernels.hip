@@ -387,6 +387,17 @@ __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
     finish(a, c);
 }
 
+// Workgroup form: wave 0 polls, the workgroup barrier releases the others
+// (a quarter of the polling traffic of 4-wave workgroups).
+__device__ __forceinline__ bool wait_arrivals_wg(const Launch &a, const Ctx0 &c, const Ctl &ctl)
+{
+    __shared__ uint32_t ok;
+    if (threadIdx.x < 64u)
+        ok = wait_arrivals(a, c, ctl) ? 1u : 0u;
+    __syncthreads();
+    return ok != 0u;
+}
+
 // ========================================================= one-shot DIRECT
 // After the arrival counters, each rank reads every peer's input in place
 // with device-coherent loads and reduces.  The input of call k must stay
@@ -441,10 +452,10 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
 // Reduce-scatter: rank q reads slice q of every rank's input in place (after
 // the arrival counters) and reduces it; all-gather: it stores the bf16
 // result straight into slice q of every rank's output (the bcast of the
-// reduced value), with device-scope stores.  Each workgroup then waits for
-// its stores to be acknowledged, raises its completion flag, and waits for
-// the completion flags of the same part index of every rank, after which
-// its part of every slice of its own output is known to be complete.
+// reduced value), with streaming device-scope stores.  Each workgroup then
+// waits for its stores to be acknowledged and raises its completion flag;
+// one workgroup per rank waits for every writer's flag, after which every
+// slice of that rank's output is known to be complete.
 // Moves exactly the algorithmic bytes: N inputs read once, N outputs written
 // once.
 template <int NMAX, bool F32>
@@ -467,7 +478,7 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
         start_delay(a, c);
         raise_arrival(a, c);
     }
-    if (!wait_arrivals(a, c, ctl))
+    if (!wait_arrivals_wg(a, c, ctl))
         return;
     __amdgpu_buffer_rsrc_t src[NMAX], dst[NMAX];
 #pragma unroll
@@ -497,33 +508,37 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
 #pragma unroll
         for (int r = 0; r < NMAX; ++r)
             if ((uint32_t)r < N) {
-                store8<F32, CP_DEV>(dst[r], lo + ch * 8u, acc);
+                store8<F32, CP_NT | CP_DEV>(dst[r], lo + ch * 8u, acc);
                 if (two)
-                    store8<F32, CP_DEV>(dst[r], lo + ch2 * 8u, acc2);
+                    store8<F32, CP_NT | CP_DEV>(dst[r], lo + ch2 * 8u, acc2);
             }
     }
-    // completion: my stores are at the coherence point, then my flag
+    // completion: my stores are at the coherence point, then my flag; one
+    // workgroup per rank (part 0) waits for every writer's flag, which
+    // proves that every slice of that rank's output is complete
     wait_stores();
     __syncthreads();
     const __amdgpu_buffer_rsrc_t dn = rsrc(a.done, MAX_RANKS * DONE_STRIDE * 4u);
     if (threadIdx.x == 0)
         st4<CP_DEV>(c.flag, dn, (q * DONE_STRIDE + c.part) * 4u);
-    // wait for the same part of every rank (wave 0 only; the others are done)
-    if (threadIdx.x < 64u) {
+    if (c.part == 0 && threadIdx.x < 64u) {
         const uint32_t lane = threadIdx.x;
-        bool need = lane < N;
-        const uint32_t off = ((lane & 15u) * DONE_STRIDE + c.part) * 4u;
+        const uint32_t total = N * a.parts;            // writers: (rank, part) pairs
         Watch w;
         w.begin(a.watchdog_ticks);
+        uint32_t i = lane;                             // next writer this lane checks
         while (true) {
-            if (need) {
-                const uint32_t v = ld4<CP_DEV>(dn, off);
-                if ((int32_t)(v - c.flag) >= 0)
-                    need = false;
+            // each lane walks its share of the writers, skipping those seen
+            while (i < total) {
+                const uint32_t s = i / a.parts, p = i % a.parts;
+                const uint32_t v = ld4<CP_DEV>(dn, (s * DONE_STRIDE + p) * 4u);
+                if ((int32_t)(v - c.flag) < 0)
+                    break;
+                i += 64u;
             }
-            if (!wave_any(need))
+            if (!wave_any(i < total))
                 break;
-            if (w.expired(ctl, q, lane, c.flag))
+            if (w.expired(ctl, q, i < total ? i / a.parts : 0u, c.flag))
                 return;
             compiler_fence();
         }
