@@ -6,18 +6,22 @@ Headline (one JSON line on stdout):
            [1 x 8192] bf16 (16 KiB per rank), one-shot LL, 160 back-to-back
            calls per emulated decode step captured in one hipGraph;
   plus   = effective HBM GB/s for 8 ranks x [256 x 8192] bf16 (4 MiB per
-           rank), algorithmic bytes 2*N*S per call, with the roofline of that
-           kernel against the 8 TB/s HBM3E peak.
+           rank), algorithmic bytes 2*N*S per call (each rank's input read
+           once, each rank's output copy written once), with the roofline of
+           that kernel against the 8 TB/s HBM3E peak.
 A step is one replay of the 160-call graph (one emulated 80-layer decode
-step, two AllReduces per layer).
+step, two AllReduces per layer).  The other workloads (4 ranks x 4096,
+512 KiB/rank LL128, 16 ranks with start delays) are reported under
+"results".
 
-Timing: CUDA/HIP events on the stream the graph or kernel runs on, around
-each replay (or call); an instrumented pass additionally records, per call,
-the earliest workgroup start and latest workgroup end on the 100 MHz
-constant clock, giving per-call intervals end(k) - end(k-1) (launch gap
-included) and spans end(k) - start(k).
+Timing: HIP events on the stream the graph or kernel runs on; an
+instrumented pass additionally records, per call, the earliest workgroup
+start and latest workgroup end on the 100 MHz constant clock, giving
+per-call intervals end(k) - end(k-1) (launch gap included) and spans
+end(k) - start(k).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
+                       [--only latency|bw|configs|calib]
 """
 import argparse
 import json
@@ -36,6 +40,8 @@ METRIC = "AllReduce µs/call p50 (16KB/rank) + effective HBM GB/s (4MB/rank), 1 
 HBM_PEAK_GBS = 8000.0
 CLOCK_HZ = 100e6
 CALLS_PER_STEP = 160
+ONE, TWO = 1, 2
+LL, LL128, SENT, DIRECT = 1, 2, 3, 4
 
 
 def log(msg):
@@ -50,15 +56,65 @@ def to_dev(torch, arr):
     return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16).copy()).to("cuda:0")
 
 
-# --------------------------------------------------------------------- C2
-def bench_latency(torch, ar, steps, warmup):
-    import synth
-    N, n = 8, 8192
-    sets = [synth.input_set(2, s) for s in range(4)]
-    ins = [[to_dev(torch, d[r]) for r in range(N)] for d in sets]
-    outs = [torch.empty((N, n), dtype=torch.int16, device="cuda:0") for _ in range(CALLS_PER_STEP)]
-    ar.init(N, n)
-    ar.set_options(ar.AR_ALGO_ONESHOT, ar.AR_PROTO_LL)
+def summary(a):
+    a = np.asarray(a, dtype=np.float64)
+    return {"p50": pct(a, 50), "p99": pct(a, 99), "mean": float(a.mean()), "count": int(a.size)}
+
+
+class Workload:
+    """Seeded rotating input sets of one workload on the device."""
+
+    def __init__(self, torch, cid, nsets):
+        import synth
+        self.data = [synth.input_set(cid, s) for s in range(nsets)]
+        self.N, self.n = self.data[0].shape
+        self.ins = [[to_dev(torch, d[r]) for r in range(self.N)] for d in self.data]
+        self.b_alg = 2 * self.N * 2 * self.n          # N*S read + N*S written
+
+    def check(self, outs_and_sets):
+        """Host comparison of (output tensor, set index) pairs with the oracle."""
+        import oracle
+        cache = {}
+        bad = 0
+        for out, s in outs_and_sets:
+            if s not in cache:
+                cache[s] = oracle.allreduce(list(self.data[s]))[0]
+            got = out.cpu().numpy().view(np.uint16)
+            bad += int((got != cache[s][None, :]).sum())
+        return bad
+
+
+def timestamp_stats(tsh, calls_per_replay):
+    """Per-call interval and span from a [slots][64][2] timestamp table."""
+    start_all = tsh[:, :, 0].min(axis=1)
+    end_all = tsh[:, :, 1].max(axis=1)
+    filled = np.nonzero(end_all != 0)[0]
+    starts = start_all[filled].astype(np.float64)
+    ends = end_all[filled].astype(np.float64)
+    order = np.argsort(ends)
+    ends, starts = ends[order], starts[order]
+    intervals = np.diff(ends) / CLOCK_HZ * 1e6
+    # drop the gaps across replay boundaries (step-end node and host launch)
+    keep = np.ones_like(intervals, dtype=bool)
+    keep[calls_per_replay - 1::calls_per_replay] = False
+    intervals = intervals[keep[:intervals.size]]
+    spans = (ends - starts) / CLOCK_HZ * 1e6
+    return intervals, spans
+
+
+def graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays=None,
+              instrumented=True):
+    """`calls` calls (+ step end) captured in one hipGraph and replayed.
+
+    Returns event timings per replay, instrumented per-call intervals/spans,
+    and a bit-exact check of the last replay's outputs."""
+    ar.init(wl.N, wl.n)
+    ar.set_options(algo, proto)
+    if delays is not None:
+        ar.set_delays(delays, delays.shape[0])
+    nsets = len(wl.ins)
+    nbuf = min(calls, 2 * nsets)
+    outs = [torch.empty((wl.N, wl.n), dtype=torch.int16, device="cuda:0") for _ in range(nbuf)]
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
 
@@ -66,98 +122,55 @@ def bench_latency(torch, ar, steps, warmup):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
             with torch.cuda.graph(g, stream=stream):
-                for k in range(CALLS_PER_STEP):
-                    ar.allreduce(ins[k % 4], outs[k], n, k + 1, stream=stream)
+                for k in range(calls):
+                    ar.allreduce(wl.ins[k % nsets], outs[k % nbuf], wl.n, k + 1, stream=stream)
                 ar.step_end(stream=stream)
         return g
 
     g = capture()
-    # uninstrumented replays, events around each
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             g.replay()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    t0 = time.perf_counter()
+          for _ in range(replays)]
     with torch.cuda.stream(stream):
-        for s in range(steps):
-            ev[s][0].record(stream)
+        for r in range(replays):
+            ev[r][0].record(stream)
             g.replay()
-            ev[s][1].record(stream)
+            ev[r][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_replay_ms = [a.elapsed_time(b) for a, b in ev]
-    per_call_us = [ms * 1000.0 / CALLS_PER_STEP for ms in per_replay_ms]
+    per_replay_ms = np.array([a.elapsed_time(b) for a, b in ev])
     status = ar.get_status()
-    # parity of the last replay's 160 outputs
-    import oracle
-    want = [oracle.allreduce(list(d)) for d in sets]
-    bad = 0
-    for k in range(CALLS_PER_STEP):
-        got = outs[k].cpu().numpy().view(np.uint16)
-        bad += int((got != want[k % 4]).sum())
-    # instrumented replays: per-call device timestamps, [slots][64][2]
-    slots = CALLS_PER_STEP * steps
-    ts = torch.empty((slots, 64, 2), dtype=torch.int64, device="cuda:0")
-    ar.set_timestamps(ts, slots)
-    gi = capture()
-    ar.set_timestamps(None, 0)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for _ in range(2):
+    bad = wl.check([(outs[(calls - 1 - j) % nbuf], (calls - 1 - j) % nsets)
+                    for j in range(nbuf)])
+    res = {"event_us_per_call": summary(per_replay_ms * 1000.0 / calls),
+           "event_ms_per_replay": summary(per_replay_ms),
+           "mismatches": bad, "status": list(status)}
+    del g
+    if instrumented:
+        slots = calls * replays
+        ts = torch.empty((slots, 64, 2), dtype=torch.int64, device="cuda:0")
+        ar.set_timestamps(ts, slots)
+        gi = capture()
+        ar.set_timestamps(None, 0)
+        with torch.cuda.stream(stream):
             gi.replay()
-    torch.cuda.synchronize()
-    ts[:, :, 0] = -1          # UINT64_MAX
-    ts[:, :, 1] = 0
-    torch.cuda.synchronize()
-    ev_i = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(steps)]
-    with torch.cuda.stream(stream):
-        for s in range(steps):
-            ev_i[s][0].record(stream)
-            gi.replay()
-            ev_i[s][1].record(stream)
-    torch.cuda.synchronize()
-    tsh = ts.cpu().numpy().view(np.uint64)
-    inst_event_us = [a.elapsed_time(b) * 1000.0 / CALLS_PER_STEP for a, b in ev_i]
-    start_all = tsh[:, :, 0].min(axis=1)
-    end_all = tsh[:, :, 1].max(axis=1)
-    # slots are indexed by the flag sequence; every slot is filled once
-    filled = np.nonzero(end_all != 0)[0]
-    starts = start_all[filled].astype(np.float64)
-    ends = end_all[filled].astype(np.float64)
-    order = np.argsort(ends)
-    ends, starts = ends[order], starts[order]
-    intervals = np.diff(ends) / CLOCK_HZ * 1e6
-    # drop the gap across replay boundaries (the step-end node and the host)
-    keep = np.ones_like(intervals, dtype=bool)
-    keep[CALLS_PER_STEP - 1::CALLS_PER_STEP] = False
-    intervals = intervals[keep[:intervals.size]]
-    spans = (ends - starts) / CLOCK_HZ * 1e6
-    status_i = ar.get_status()
+            ts[:, :, 0] = -1              # UINT64_MAX
+            ts[:, :, 1] = 0
+            for r in range(replays):
+                gi.replay()
+        torch.cuda.synchronize()
+        intervals, spans = timestamp_stats(ts.cpu().numpy().view(np.uint64), calls)
+        res["instrumented"] = {"interval_us": summary(intervals), "span_us": summary(spans)}
+        res["status_instrumented"] = list(ar.get_status())
+        del gi
+    if delays is not None:
+        ar.set_delays(None, 0)
     ar.destroy()
-    del g, gi
-    return {
-        "workload": "8 ranks x [1x8192] bf16 (16 KiB/rank), N(0,0.5), one-shot LL, "
-                    "160 calls/step in one hipGraph",
-        "event_us_per_call": {"p50": pct(per_call_us, 50), "p99": pct(per_call_us, 99),
-                              "mean": float(np.mean(per_call_us))},
-        "event_ms_per_step": {"p50": pct(per_replay_ms, 50), "mean": float(np.mean(per_replay_ms))},
-        "wall_s": wall,
-        "instrumented": {
-            "interval_us": {"p50": pct(intervals, 50), "p99": pct(intervals, 99),
-                            "mean": float(np.mean(intervals)), "count": int(intervals.size)},
-            "span_us": {"p50": pct(spans, 50), "p99": pct(spans, 99)},
-            "event_us_per_call_mean": float(np.mean(inst_event_us)),
-        },
-        "mismatches": bad,
-        "status": list(status),
-        "status_instrumented": list(status_i),
-    }
+    return res
 
 
-# --------------------------------------------------------------------- floor
 def bench_floor(torch, steps):
     """A 160-node graph of minimal kernels (1-element fills): the launch floor."""
     t = torch.zeros(1, dtype=torch.int32, device="cuda:0")
@@ -183,28 +196,20 @@ def bench_floor(torch, steps):
     return {"us_per_node_p50": pct(us, 50), "what": "160-node hipGraph of 1-element fill kernels"}
 
 
-# --------------------------------------------------------------------- C4
-def bench_bandwidth(torch, ar, calls, warmup, algo, proto, label):
-    import synth
-    N, n = 8, 256 * 8192
-    nsets = 8
-    sets = [synth.input_set(4, s) for s in range(nsets)]
-    ins = [[to_dev(torch, d[r]) for r in range(N)] for d in sets]
-    outs = [torch.empty((N, n), dtype=torch.int16, device="cuda:0") for _ in range(nsets)]
-    ar.init(N, n)
+def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label):
+    """Back-to-back stream calls over 8 rotating buffer sets, events per call."""
+    nsets = len(wl.ins)
+    outs = [torch.empty((wl.N, wl.n), dtype=torch.int16, device="cuda:0") for _ in range(nsets)]
+    ar.init(wl.N, wl.n)
     ar.set_options(algo, proto)
-    grid = ar.query(4, n)
-    threads = ar.query(5, n)
+    grid, threads = ar.query(4, wl.n), ar.query(5, wl.n)
     stream = torch.cuda.current_stream()
     epoch = 0
 
     def call(k):
         nonlocal epoch
         epoch += 1
-        if epoch > 65000:
-            ar.step_end()
-            epoch = 1
-        ar.allreduce(ins[k % nsets], outs[k % nsets], n, epoch)
+        ar.allreduce(wl.ins[k % nsets], outs[k % nsets], wl.n, epoch)
 
     for k in range(warmup):
         call(k)
@@ -218,30 +223,30 @@ def bench_bandwidth(torch, ar, calls, warmup, algo, proto, label):
     torch.cuda.synchronize()
     us = np.array([a.elapsed_time(b) * 1000.0 for a, b in ev])
     status = ar.get_status()
-    import oracle
-    bad = 0
-    for s in range(nsets):
-        want = oracle.allreduce(list(sets[s]))[0]
-        got = outs[s].cpu().numpy().view(np.uint16)
-        bad += int((got != want[None, :]).sum())
+    bad = wl.check([(outs[s], s) for s in range(nsets)])
     ar.destroy()
-    b_alg = 2 * N * 2 * n
     return {
         "workload": "8 ranks x [256x8192] bf16 (4 MiB/rank), U(-1,1), %s, 8 rotating buffer "
-                    "sets (footprint %d MiB)" % (label, (2 * nsets * N * 2 * n) >> 20),
-        "algo": label,
-        "grid": grid, "threads": threads,
-        "us_per_call": {"p50": float(np.percentile(us, 50)), "p99": float(np.percentile(us, 99)),
-                        "mean": float(us.mean()), "min": float(us.min())},
-        "b_alg_bytes": b_alg,
-        "gbps_p50": b_alg / (np.percentile(us, 50) * 1e-6) / 1e9,
-        "gbps_mean": b_alg / (us.mean() * 1e-6) / 1e9,
-        "mismatches": bad,
-        "status": list(status),
+                    "sets (footprint %d MiB)" % (label, (2 * nsets * wl.N * 2 * wl.n) >> 20),
+        "algo": label, "grid": grid, "threads": threads,
+        "us_per_call": summary(us),
+        "b_alg_bytes": wl.b_alg,
+        "gbps_p50": wl.b_alg / (np.percentile(us, 50) * 1e-6) / 1e9,
+        "gbps_mean": wl.b_alg / (us.mean() * 1e-6) / 1e9,
+        "mismatches": bad, "status": list(status),
     }
 
 
-# --------------------------------------------------------------------- CPU
+def calib_copy(torch, reps=20):
+    """A plain copy of known size for scaling the FETCH_SIZE/WRITE_SIZE counters."""
+    src = torch.ones(16 * 1024 * 1024, dtype=torch.int16, device="cuda:0")   # 32 MiB
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes_read": 32 << 20, "bytes_written": 32 << 20, "reps": reps}
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle as it stands, on this host's cores: 16 KiB/rank calls."""
     import oracle
@@ -285,6 +290,7 @@ def main():
     ap.add_argument("--bw-calls", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quick", action="store_true")
+    ap.add_argument("--only", default="all", choices=["all", "latency", "bw", "configs", "calib"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the N ranks are emulated as workgroup sets of one "
@@ -295,9 +301,10 @@ def main():
         sys.exit(2)
     if args.quick:
         args.steps, args.bw_calls = min(args.steps, 20), min(args.bw_calls, 20)
+    only = args.only
 
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and only == "all":
         log("cpu baseline (oracle)")
         cpu = cpu_baseline()
     import torch
@@ -305,63 +312,98 @@ def main():
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     log("device %s, %d CUs" % (props.name, props.multi_processor_count))
+    if only == "calib":
+        print(json.dumps({"calib": calib_copy(torch)}), flush=True)
+        return
 
-    log("launch floor")
-    floor = bench_floor(torch, args.steps)
-    log("C2 latency: %d steps x 160 calls" % args.steps)
-    lat = bench_latency(torch, ar, args.steps, args.warmup)
-    log("C2 p50 %.3f us/call (events), instrumented interval p50 %.3f us"
-        % (lat["event_us_per_call"]["p50"], lat["instrumented"]["interval_us"]["p50"]))
-    log("C4 bandwidth: two-shot DIRECT")
-    bw2 = bench_bandwidth(torch, ar, args.bw_calls, args.warmup, ar.AR_ALGO_TWOSHOT,
-                          ar.AR_PROTO_DIRECT, "two-shot (in-place reduce-scatter, reduced slices "
-                          "written straight into every output, completion flags)")
-    log("C4 two-shot DIRECT %.1f GB/s" % bw2["gbps_p50"])
-    log("C4 bandwidth: two-shot LL128")
-    bw3 = bench_bandwidth(torch, ar, args.bw_calls, args.warmup, ar.AR_ALGO_TWOSHOT,
-                          ar.AR_PROTO_LL128, "two-shot (reduce-scatter + all-gather, LL128 lines)")
-    log("C4 two-shot LL128 %.1f GB/s" % bw3["gbps_p50"])
-    log("C4 bandwidth: one-shot DIRECT")
-    bw1 = bench_bandwidth(torch, ar, args.bw_calls, args.warmup, ar.AR_ALGO_ONESHOT,
-                          ar.AR_PROTO_DIRECT, "one-shot (in-place reads after arrival flags)")
-    log("C4 one-shot %.1f GB/s" % bw1["gbps_p50"])
-    best_bw = max((bw2, bw3, bw1), key=lambda r: r["gbps_p50"])
+    results = {}
+    lat = None
+    if only in ("all", "latency"):
+        log("launch floor")
+        results["floor"] = bench_floor(torch, args.steps)
+        log("16 KiB/rank latency: %d steps x 160 calls" % args.steps)
+        wl2 = Workload(torch, 2, 4)
+        lat = graph_run(torch, ar, wl2, ONE, LL, CALLS_PER_STEP, args.steps, args.warmup)
+        lat["workload"] = ("8 ranks x [1x8192] bf16 (16 KiB/rank), N(0,0.5), one-shot LL, "
+                           "160 calls/step in one hipGraph")
+        results["latency_16k"] = lat
+        log("16 KiB p50 %.3f us/call (events), instrumented interval p50 %.3f us, span p50 %.3f"
+            % (lat["event_us_per_call"]["p50"], lat["instrumented"]["interval_us"]["p50"],
+               lat["instrumented"]["span_us"]["p50"]))
+        lat_d = graph_run(torch, ar, wl2, ONE, DIRECT, CALLS_PER_STEP, args.steps, args.warmup,
+                          instrumented=False)
+        results["latency_16k_oneshot_direct"] = lat_d
+        log("16 KiB one-shot DIRECT p50 %.3f us/call" % lat_d["event_us_per_call"]["p50"])
+    bws = []
+    if only in ("all", "bw"):
+        wl4 = Workload(torch, 4, 8)
+        for algo, proto, key, label in (
+                (TWO, DIRECT, "bw_4m_twoshot_direct",
+                 "two-shot (in-place reduce-scatter, reduced slices written straight into every "
+                 "output, completion flags)"),
+                (TWO, LL128, "bw_4m_twoshot_ll128", "two-shot (reduce-scatter + all-gather, "
+                 "LL128 lines)"),
+                (ONE, DIRECT, "bw_4m_oneshot_direct", "one-shot (in-place reads after arrival "
+                 "counters)")):
+            log("4 MiB/rank bandwidth: %s" % key)
+            r = bench_bandwidth(torch, ar, wl4, args.bw_calls, args.warmup, algo, proto, label)
+            results[key] = r
+            bws.append(r)
+            log("  %.1f GB/s (p50 %.2f us/call)" % (r["gbps_p50"], r["us_per_call"]["p50"]))
+        del wl4
+    if only in ("all", "configs"):
+        reps = 3 if args.quick else 10
+        wl1 = Workload(torch, 1, 4)
+        for proto, key in ((SENT, "c1_sentinel"), (LL, "c1_ll")):
+            log("4 ranks x 4096, 1000-call graph, %s" % key)
+            r = graph_run(torch, ar, wl1, ONE, proto, 1000, reps, 2)
+            r["workload"] = "4 ranks x [1x4096] bf16, N(0,1), one-shot, 1000 calls in one hipGraph"
+            results[key] = r
+        wl3 = Workload(torch, 3, 4)
+        for algo, key in ((ONE, "c3_oneshot_ll128"), (TWO, "c3_twoshot_ll128")):
+            log("8 ranks x 512 KiB LL128, 160-call graph, %s" % key)
+            r = graph_run(torch, ar, wl3, algo, LL128, CALLS_PER_STEP, reps * 2, 2)
+            r["workload"] = ("8 ranks x [32x8192] bf16 (512 KiB/rank), N(0,1) + 1% x100, LL128, "
+                             "160 calls in one hipGraph")
+            r["gbps_p50"] = wl3.b_alg / (r["event_us_per_call"]["p50"] * 1e-6) / 1e9
+            results[key] = r
+        del wl3
+        import synth
+        wl5 = Workload(torch, 5, 8)
+        calls5 = 2000 if args.quick else 10000
+        delays = torch.from_numpy(synth.delays_ns(5, calls5).view(np.int32).copy()).to("cuda:0")
+        for algo, key in ((TWO, "c5_twoshot_sentinel"), (ONE, "c5_oneshot_sentinel")):
+            log("16 ranks, %d-call graph with start delays, %s" % (calls5, key))
+            r = graph_run(torch, ar, wl5, algo, SENT, calls5, 1, 1, delays=delays)
+            r["workload"] = ("16 ranks x [8x7168] bf16, N(0,1), seeded U[0,5 us] start delay per "
+                             "(call, rank), %d calls in one hipGraph" % calls5)
+            results[key] = r
+            r2 = graph_run(torch, ar, wl5, algo, SENT, calls5, 1, 1, instrumented=False)
+            results[key + "_nodelay"] = r2
 
-    avg_us = best_bw["us_per_call"]["mean"]
-    achieved = best_bw["b_alg_bytes"] / (avg_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                "kernel": best_bw["algo"],
-                "per_launch_bytes": best_bw["b_alg_bytes"],
-                "avg_launch_us": avg_us}
-    parity_ok = (lat["mismatches"] == 0 and lat["status"][0] == 0 and
-                 all(r["mismatches"] == 0 and r["status"][0] == 0 for r in (bw1, bw2, bw3)))
-    value = lat["event_us_per_call"]["p50"]
-    line = {
-        "metric": METRIC,
-        "value": round(value, 4),
-        "unit": "us/call",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(lat["event_ms_per_step"]["mean"], 5),
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "io_dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": lat["workload"], "n_ranks": 8, "elems_per_rank": 8192,
-                   "calls_per_step": CALLS_PER_STEP, "launch": "hipGraph"},
-        "gbps_4mb": round(best_bw["gbps_p50"], 2),
-        "gbps_4mb_frac_of_peak": round(best_bw["gbps_p50"] / HBM_PEAK_GBS, 4),
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "parity_ok": parity_ok,
-        "results": {"latency_16k": lat, "floor": floor, "bw_4m_twoshot_direct": bw2,
-                    "bw_4m_twoshot_ll128": bw3, "bw_4m_oneshot_direct": bw1},
-        "host": platform.node(),
-    }
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "io_dtype": "bf16", "data": "synthetic", "unit": "us/call"}
+    if lat is not None:
+        line["value"] = round(lat["event_us_per_call"]["p50"], 4)
+        line["ms_per_step"] = round(lat["event_ms_per_replay"]["mean"], 5)
+        line["config"] = {"workload": lat["workload"], "n_ranks": 8, "elems_per_rank": 8192,
+                          "calls_per_step": CALLS_PER_STEP, "launch": "hipGraph"}
+    if bws:
+        best = max(bws, key=lambda r: r["gbps_p50"])
+        avg_us = best["us_per_call"]["mean"]
+        achieved = best["b_alg_bytes"] / (avg_us * 1e-6) / 1e9
+        line["gbps_4mb"] = round(best["gbps_p50"], 2)
+        line["gbps_4mb_frac_of_peak"] = round(best["gbps_p50"] / HBM_PEAK_GBS, 4)
+        line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                            "traffic": None, "kernel": best["algo"],
+                            "per_launch_bytes": best["b_alg_bytes"], "avg_launch_us": avg_us}
+    line["cpu_baseline"] = cpu
+    line["parity_ok"] = all(r.get("mismatches", 0) == 0 and r.get("status", [0])[0] == 0
+                            for k, r in results.items() if isinstance(r, dict) and "status" in r)
+    line["results"] = results
+    line["host"] = platform.node()
     print(json.dumps(line), flush=True)
 
 
