@@ -237,6 +237,30 @@ def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label):
     }
 
 
+def kernel_source_sha():
+    import hashlib
+    csrc = os.path.join(ROOT, "tp_decode_comms_amd", "csrc")
+    data = open(os.path.join(csrc, "ar_kernels.hip"), "rb").read() + \
+        open(os.path.join(csrc, "ar_proto.h"), "rb").read()
+    return hashlib.sha256(data).hexdigest()[:16]
+
+
+def recorded_traffic(kernel_key):
+    """HBM bytes per launch from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE runs scaled by a calibration copy), or None when the kernel
+    source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic_4mib.md")
+    try:
+        for line in open(path):
+            if line.startswith("traffic_bytes_per_launch %s:" % kernel_key):
+                toks = line.split()
+                if toks[-1] == kernel_source_sha():
+                    return int(toks[2])
+    except OSError:
+        pass
+    return None
+
+
 def calib_copy(torch, reps=20):
     """A plain copy of known size for scaling the FETCH_SIZE/WRITE_SIZE counters."""
     src = torch.ones(16 * 1024 * 1024, dtype=torch.int16, device="cuda:0")   # 32 MiB
@@ -395,9 +419,11 @@ def main():
         achieved = best["b_alg_bytes"] / (avg_us * 1e-6) / 1e9
         line["gbps_4mb"] = round(best["gbps_p50"], 2)
         line["gbps_4mb_frac_of_peak"] = round(best["gbps_p50"] / HBM_PEAK_GBS, 4)
+        traffic = recorded_traffic("k_twoshot_direct") if best is results.get(
+            "bw_4m_twoshot_direct") else None
         line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                            "traffic": None, "kernel": best["algo"],
+                            "traffic": traffic, "kernel": best["algo"],
                             "per_launch_bytes": best["b_alg_bytes"], "avg_launch_us": avg_us}
     line["cpu_baseline"] = cpu
     line["parity_ok"] = all(r.get("mismatches", 0) == 0 and r.get("status", [0])[0] == 0
