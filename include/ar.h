@@ -78,7 +78,12 @@ enum ar_proto {
  * ar_init -- create the context on the current HIP device.
  *   n_ranks:   number of emulated ranks, 1..16.
  *   max_elems: largest per-rank element count any later call may use, > 0,
- *              at most 2^28.
+ *              at most 2^28, with n_ranks * max_elems * 4 < 2^32 (every
+ *              staging region and the output tensor are addressed with
+ *              32-bit offsets).  When the one-shot sentinel inboxes
+ *              (4 * n_ranks^2 * max_elems bytes) would exceed that, they are
+ *              not allocated and the one-shot sentinel protocol is refused
+ *              (AR_ERR_INVALID) for this context.
  * Allocates every protocol's staging (per rank x 2 parities), the flag
  * sequence word and the status record; zeroes flag words and arms sentinel
  * buffers with 0xFFFF.  Synchronous.

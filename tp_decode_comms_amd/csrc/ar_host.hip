@@ -87,6 +87,8 @@ void free_all()
     g.done = nullptr;
 }
 
+constexpr size_t REGION_LIMIT = (size_t(1) << 32) - 1;   // one buffer descriptor
+
 int alloc(char **p, size_t bytes)
 {
     hipError_t e = hipMalloc((void **)p, bytes);
@@ -114,7 +116,7 @@ hipError_t rearm(hipStream_t s)
     hipError_t e;
     if ((e = ar::launch_fill((uint32_t *)g.ll, ll_bytes() / 4, 0u, s)) != hipSuccess) return e;
     if ((e = ar::launch_fill((uint32_t *)g.l128, l128_bytes() / 4, 0u, s)) != hipSuccess) return e;
-    if ((e = ar::launch_fill((uint32_t *)g.s1, s1_bytes() / 4, ar::SENT_WORD, s)) != hipSuccess) return e;
+    if (g.s1 && (e = ar::launch_fill((uint32_t *)g.s1, s1_bytes() / 4, ar::SENT_WORD, s)) != hipSuccess) return e;
     if ((e = ar::launch_fill((uint32_t *)g.srs, s2_bytes() / 4, ar::SENT_WORD, s)) != hipSuccess) return e;
     if ((e = ar::launch_fill((uint32_t *)g.sag, s2_bytes() / 4, ar::SENT_WORD, s)) != hipSuccess) return e;
     if ((e = ar::launch_fill(g.done, done_words(), 0u, s)) != hipSuccess) return e;
@@ -165,7 +167,9 @@ int choose_kind(size_t n, int *kind)
         switch (proto) {
         case AR_PROTO_LL: *kind = ar::K_ONESHOT_LL; return AR_OK;
         case AR_PROTO_LL128: *kind = ar::K_ONESHOT_LL128; return AR_OK;
-        case AR_PROTO_SENTINEL: *kind = ar::K_ONESHOT_SENTINEL; return AR_OK;
+        case AR_PROTO_SENTINEL:
+            if (g.s1 == nullptr) return AR_ERR_INVALID;   // inbox region too large
+            *kind = ar::K_ONESHOT_SENTINEL; return AR_OK;
         case AR_PROTO_DIRECT: *kind = ar::K_ONESHOT_DIRECT; return AR_OK;
         }
     } else {
@@ -319,10 +323,16 @@ int ar_init(int n_ranks, size_t max_elems)
     g.l128_stride = round_up((me + ar::L128_ELEMS - 1) / ar::L128_ELEMS * ar::L128_BYTES, 256);
     g.s1_stride = round_up(me * 2, 256);
     g.s2_stride = round_up(slice_len(me, n_ranks) * 2, 256);
+    // every staging region and the output tensor are addressed through one
+    // buffer descriptor with 32-bit offsets; a region that would not fit is
+    // not allocated and its protocol is unavailable for this context
+    if (me * (size_t)n_ranks * 4 > REGION_LIMIT || ll_bytes() > REGION_LIMIT ||
+        l128_bytes() > REGION_LIMIT || s2_bytes() > REGION_LIMIT)
+        return AR_ERR_INVALID;
     int rc;
     if ((rc = alloc(&g.ll, ll_bytes())) != AR_OK ||
         (rc = alloc(&g.l128, l128_bytes())) != AR_OK ||
-        (rc = alloc(&g.s1, s1_bytes())) != AR_OK ||
+        (s1_bytes() <= REGION_LIMIT && (rc = alloc(&g.s1, s1_bytes())) != AR_OK) ||
         (rc = alloc(&g.srs, s2_bytes())) != AR_OK ||
         (rc = alloc(&g.sag, s2_bytes())) != AR_OK ||
         (rc = alloc((char **)&g.ctl, ar::CTL_WORDS * 4)) != AR_OK ||

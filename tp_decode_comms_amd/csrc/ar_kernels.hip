@@ -94,6 +94,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const Launch &a, uint
     return rsrc((char *)a.out + (size_t)r * a.n * esz, a.n * esz);
 }
 
+// All N output copies under one descriptor (the host bounds N*n*4 < 2^32);
+// copy r starts at byte r*n*esz.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_all(const Launch &a, bool f32)
+{
+    const uint32_t esz = f32 ? 4u : 2u;
+    return rsrc(a.out, a.n_ranks * a.n * esz);
+}
+
 // 8 accumulated elements -> out[rank][elem..elem+8)
 template <bool F32, int CP = CP_PLAIN>
 __device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t o, uint32_t elem, const Acc8 &acc)
@@ -172,18 +180,20 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
 // two units {2 bf16, flag}.  Rank r publishes once into its own mailbox
 // [r][parity]; every rank reads it.  The receive keeps two batches of loads
 // in flight: while one batch is checked the next is already on its way.
-// One round of the one-shot LL kernel for lane chunk `ch` with input x.
+// One round of the one-shot LL kernel for lane chunk `ch` with input x.  All
+// mailboxes sit in one region [rank][parity] x ll_stride under descriptor llr.
 template <int NMAX, bool F32>
 __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
-                                         const __amdgpu_buffer_rsrc_t *src,
-                                         __amdgpu_buffer_rsrc_t mine, __amdgpu_buffer_rsrc_t o,
+                                         __amdgpu_buffer_rsrc_t llr, __amdgpu_buffer_rsrc_t o,
                                          uint32_t ch, uint32_t C, u32x2 x)
 {
     const uint32_t N = a.n_ranks;
+    const uint32_t rb = a.ll_stride;
+    const uint32_t lane_off = ch * 16u + c.par * rb;
     const bool active = ch < C;
     // publish (send/bcast): one copy, read by all N ranks
     if (active)
-        st16<CP_DEV>(ll_pack(x.x, x.y, c.flag), mine, ch * 16u);
+        st16<CP_DEV>(ll_pack(x.x, x.y, c.flag), llr, lane_off + c.rank * 2u * rb);
     // receive (recvReduce): poll every peer's unit for this chunk
     uint32_t pend = 0;
 #pragma unroll
@@ -196,7 +206,7 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             if ((pend >> s) & 1u)
-                A[s] = ld16<CP_DEV>(src[s], ch * 16u);
+                A[s] = ld16<CP_DEV>(llr, lane_off + (uint32_t)s * 2u * rb);
     };
     auto check = [&](const u32x4 *A) {
 #pragma unroll
@@ -246,7 +256,6 @@ __global__ __launch_bounds__(256) void k_oneshot_ll(const Launch a)
     Ctx0 c;
     begin(a, c);
     const uint32_t C = a.n >> 2;                    // 4-element chunks per rank
-    const uint32_t mb_bytes = C * 16u;
     const uint32_t step = a.parts * blockDim.x;
     const uint32_t rounds = (C + step - 1u) / step;
     const __amdgpu_buffer_rsrc_t inr = in_rsrc(a, c.rank);
@@ -259,22 +268,17 @@ __global__ __launch_bounds__(256) void k_oneshot_ll(const Launch a)
     raise_arrival(a, c);
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
-    __amdgpu_buffer_rsrc_t src[NMAX];
-#pragma unroll
-    for (int s = 0; s < NMAX; ++s)
-        src[s] = rsrc(a.ll + (size_t)((uint32_t)s * 2u + c.par) * a.ll_stride, mb_bytes);
-    const __amdgpu_buffer_rsrc_t mine =
-        rsrc(a.ll + (size_t)(c.rank * 2u + c.par) * a.ll_stride, mb_bytes);
+    const __amdgpu_buffer_rsrc_t llr = rsrc(a.ll, a.n_ranks * 2u * a.ll_stride);
     start_delay(a, c);
     // round 0 is straight-line code: its poll loads are issued back to back
     // (inside a loop the compiler's counter bookkeeping would wait before each)
-    if (!ll_round<NMAX, F32>(a, c, ctl, src, mine, o, ch, C, x))
+    if (!ll_round<NMAX, F32>(a, c, ctl, llr, o, ch, C, x))
         return;
     for (uint32_t it = 1; it < rounds; ++it) {
         wait_stores();
         ch += step;
         x = ch < C ? ld8<CP_PLAIN>(inr, ch * 8u) : u32x2{0u, 0u};
-        if (!ll_round<NMAX, F32>(a, c, ctl, src, mine, o, ch, C, x))
+        if (!ll_round<NMAX, F32>(a, c, ctl, llr, o, ch, C, x))
             return;
     }
     finish(a, c);
@@ -305,9 +309,11 @@ __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
     raise_arrival(a, c);
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
-    auto inbox = [&](uint32_t recv, uint32_t send) {
-        return rsrc(a.s1 + (size_t)((recv * N + send) * 2u + c.par) * a.s1_stride, bytes);
-    };
+    // all inboxes [recv][send][parity] x s1_stride under one descriptor
+    const uint32_t sb = a.s1_stride;
+    const __amdgpu_buffer_rsrc_t box = rsrc(a.s1, N * N * 2u * sb);
+    const uint32_t par_off = c.par * sb;
+    (void)bytes;
     start_delay(a, c);
 
     auto round = [&](uint32_t ch, u32x4 x) -> bool {
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((uint32_t)s < N && (uint32_t)s != c.rank)
-                    st16<CP_DEV>(x, inbox((uint32_t)s, c.rank), ch * 16u);
+                    st16<CP_DEV>(x, box, ch * 16u + par_off + (((uint32_t)s * N + c.rank) * 2u) * sb);
         }
         uint32_t pend = 0;
 #pragma unroll
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((pend >> s) & 1u)
-                    A[s] = ld16<CP_DEV>(inbox(c.rank, (uint32_t)s), ch * 16u);
+                    A[s] = ld16<CP_DEV>(box, ch * 16u + par_off + ((c.rank * N + (uint32_t)s) * 2u) * sb);
         };
         auto check = [&](const u32x4 *A) {
 #pragma unroll
@@ -369,7 +375,7 @@ __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((uint32_t)s < N && (uint32_t)s != c.rank)
-                    st16<CP_DEV>(sentinel4(), inbox(c.rank, (uint32_t)s), ch * 16u);
+                    st16<CP_DEV>(sentinel4(), box, ch * 16u + par_off + ((c.rank * N + (uint32_t)s) * 2u) * sb);
             store8<F32>(o, ch * 8u, acc);
         }
         return true;
@@ -480,13 +486,11 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     }
     if (!wait_arrivals_wg(a, c, ctl))
         return;
-    __amdgpu_buffer_rsrc_t src[NMAX], dst[NMAX];
+    __amdgpu_buffer_rsrc_t src[NMAX];
 #pragma unroll
-    for (int s = 0; s < NMAX; ++s) {
-        const uint32_t ss = (uint32_t)s < N ? (uint32_t)s : 0u;
-        src[s] = in_rsrc(a, ss);
-        dst[s] = out_rsrc(a, ss, F32);
-    }
+    for (int s = 0; s < NMAX; ++s)
+        src[s] = in_rsrc(a, (uint32_t)s < N ? (uint32_t)s : 0u);
+    const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
     // two chunks per lane per round keep more loads in flight
     for (uint32_t ch = c.part * blockDim.x + threadIdx.x; ch < G; ch += 2u * step) {
         const uint32_t ch2 = ch + step;
@@ -508,9 +512,9 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
 #pragma unroll
         for (int r = 0; r < NMAX; ++r)
             if ((uint32_t)r < N) {
-                store8<F32, CP_NT | CP_DEV>(dst[r], lo + ch * 8u, acc);
+                store8<F32, CP_NT | CP_DEV>(oa, (uint32_t)r * a.n + lo + ch * 8u, acc);
                 if (two)
-                    store8<F32, CP_NT | CP_DEV>(dst[r], lo + ch2 * 8u, acc2);
+                    store8<F32, CP_NT | CP_DEV>(oa, (uint32_t)r * a.n + lo + ch2 * 8u, acc2);
             }
     }
     // completion: my stores are at the coherence point, then my flag; one
@@ -551,7 +555,8 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
 // A wave handles up to GB groups per batch: it publishes the payload of all
 // of them, waits once for the acknowledgements, then stores their flags;
 // a reader polls the flags of all its groups together, then loads payloads.
-constexpr int GB = 4;
+// groups per batch: 4 for up to 8 ranks, 2 for up to 16 (register budget)
+template <int NMAX> struct GroupsPerBatch { static constexpr int value = NMAX <= 8 ? 4 : 2; };
 
 // reads 8 (or 4) elements of a bf16 buffer at element `e`
 template <int CP = CP_PLAIN>
@@ -594,13 +599,17 @@ __device__ __forceinline__ bool l128_flag_ok(u32x2 f, uint32_t flag)
 // number of valid elements of source s in group index space; a line is
 // polled only if one of its elements is valid.  skip names a source the
 // caller holds already (or NMAX).  Returns false on watchdog expiry.
-template <int NMAX>
-__device__ __forceinline__ bool l128_receive(const __amdgpu_buffer_rsrc_t *src, uint32_t N,
-                                             uint32_t skip, const uint32_t *g, uint32_t gvalid,
-                                             uint32_t lane, const L128Lane &ln,
+template <int NMAX, int GB = GroupsPerBatch<NMAX>::value>
+__device__ __forceinline__ bool l128_receive(__amdgpu_buffer_rsrc_t reg, uint32_t rb, uint32_t par,
+                                             uint32_t N, uint32_t skip, const uint32_t *g,
+                                             uint32_t gvalid, uint32_t lane, const L128Lane &ln,
                                              const uint32_t *lim, uint32_t flag, const Ctl &ctl,
                                              uint32_t rank, uint32_t budget, u32x4 (*V)[NMAX])
 {
+    // source s's lines of group g: reg + (s*2 + par)*rb + g*1024 + lane*16
+    auto off = [&](int j, int s) {
+        return ((uint32_t)s * 2u + par) * rb + g[j] * L128_BYTES + lane * 16u;
+    };
     uint32_t pend[GB];
     u32x2 F[GB][NMAX];
 #pragma unroll
@@ -612,7 +621,7 @@ __device__ __forceinline__ bool l128_receive(const __amdgpu_buffer_rsrc_t *src, 
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             if ((uint32_t)s < N && (uint32_t)s != skip && ln.half && line_first < lim[s]) {
-                F[j][s] = ld8<CP_DEV>(src[s], g[j] * L128_BYTES + lane * 16u + 8u);
+                F[j][s] = ld8<CP_DEV>(reg, off(j, s) + 8u);
                 pend[j] |= 1u << s;
             }
     }
@@ -639,7 +648,7 @@ __device__ __forceinline__ bool l128_receive(const __amdgpu_buffer_rsrc_t *src, 
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((pend[j] >> s) & 1u)
-                    F[j][s] = ld8<CP_DEV>(src[s], g[j] * L128_BYTES + lane * 16u + 8u);
+                    F[j][s] = ld8<CP_DEV>(reg, off(j, s) + 8u);
     }
     // every needed line is complete: load the payloads
     compiler_fence();
@@ -648,15 +657,14 @@ __device__ __forceinline__ bool l128_receive(const __amdgpu_buffer_rsrc_t *src, 
         if (!((gvalid >> j) & 1u))
             continue;
         const uint32_t e = g[j] * L128_ELEMS + ln.elem;
-        const uint32_t off = g[j] * L128_BYTES + lane * 16u;
 #pragma unroll
         for (int s = 0; s < NMAX; ++s) {
             if ((uint32_t)s < N && (uint32_t)s != skip && e < lim[s]) {
                 if (ln.half) {
-                    const u32x2 p = ld8<CP_DEV>(src[s], off);
+                    const u32x2 p = ld8<CP_DEV>(reg, off(j, s));
                     V[j][s].x = p.x; V[j][s].y = p.y; V[j][s].z = 0u; V[j][s].w = 0u;
                 } else {
-                    V[j][s] = ld16<CP_DEV>(src[s], off);
+                    V[j][s] = ld16<CP_DEV>(reg, off(j, s));
                 }
             }
         }
@@ -678,6 +686,7 @@ __device__ __forceinline__ void store_lane(__amdgpu_buffer_rsrc_t o, uint32_t e,
 template <int NMAX, bool F32>
 __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 {
+    constexpr int GB = GroupsPerBatch<NMAX>::value;
     Ctx0 c;
     begin(a, c);
     const uint32_t N = a.n_ranks;
@@ -686,19 +695,15 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
     const uint32_t waves = blockDim.x >> 6;
     const uint32_t groups = (a.n + L128_ELEMS - 1u) / L128_ELEMS;
     const uint32_t gstep = a.parts * waves;
-    const uint32_t mb_bytes = groups * L128_BYTES;
     raise_arrival(a, c);
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     const L128Lane ln = l128_lane(lane);
     const __amdgpu_buffer_rsrc_t inr = in_rsrc(a, c.rank);
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
-    __amdgpu_buffer_rsrc_t src[NMAX];
-#pragma unroll
-    for (int s = 0; s < NMAX; ++s)
-        src[s] = rsrc(a.l128 + (size_t)((uint32_t)s * 2u + c.par) * a.l128_stride, mb_bytes);
-    const __amdgpu_buffer_rsrc_t mine =
-        rsrc(a.l128 + (size_t)(c.rank * 2u + c.par) * a.l128_stride, mb_bytes);
+    const uint32_t rb = a.l128_stride;
+    const __amdgpu_buffer_rsrc_t reg = rsrc(a.l128, N * 2u * rb);
+    const uint32_t mine = (c.rank * 2u + c.par) * rb;
     uint32_t lim[NMAX];
 #pragma unroll
     for (int s = 0; s < NMAX; ++s)
@@ -720,15 +725,15 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 #pragma unroll
         for (int j = 0; j < GB; ++j)
             if ((gvalid >> j) & 1u)
-                l128_store_payload(mine, g[j] * L128_BYTES + lane * 16u, ln.half, x[j]);
+                l128_store_payload(reg, mine + g[j] * L128_BYTES + lane * 16u, ln.half, x[j]);
         wait_stores();
 #pragma unroll
         for (int j = 0; j < GB; ++j)
             if (((gvalid >> j) & 1u) && ln.half)
-                l128_store_flag(mine, g[j] * L128_BYTES + lane * 16u, c.flag);
+                l128_store_flag(reg, mine + g[j] * L128_BYTES + lane * 16u, c.flag);
         u32x4 V[GB][NMAX];
-        if (!l128_receive<NMAX>(src, N, c.rank, g, gvalid, lane, ln, lim, c.flag, ctl, c.rank,
-                                a.watchdog_ticks, V))
+        if (!l128_receive<NMAX>(reg, rb, c.par, N, c.rank, g, gvalid, lane, ln, lim, c.flag, ctl,
+                                c.rank, a.watchdog_ticks, V))
             return;
 #pragma unroll
         for (int j = 0; j < GB; ++j) {
@@ -757,6 +762,7 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 template <int NMAX, bool F32>
 __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 {
+    constexpr int GB = GroupsPerBatch<NMAX>::value;
     Ctx0 c;
     begin(a, c);
     const uint32_t N = a.n_ranks;
@@ -767,7 +773,6 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
     const uint32_t waves = blockDim.x >> 6;
     const uint32_t groups = (L + L128_ELEMS - 1u) / L128_ELEMS;
     const uint32_t gstep = a.parts * waves;
-    const uint32_t mb_bytes = groups * L128_BYTES;
     if (a.delays == nullptr)
         raise_arrival(a, c);
     c.flag = load_seq(a) + a.epoch;
@@ -780,19 +785,19 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
     if (!wait_arrivals(a, c, ctl))
         return;
     uint32_t lim[NMAX];
-    __amdgpu_buffer_rsrc_t inp[NMAX], stg[NMAX];
+    __amdgpu_buffer_rsrc_t inp[NMAX];
 #pragma unroll
     for (int s = 0; s < NMAX; ++s) {
         const uint32_t ss = (uint32_t)s < N ? (uint32_t)s : 0u;
         inp[s] = in_rsrc(a, ss);
-        stg[s] = rsrc(a.l128 + (size_t)(ss * 2u + c.par) * a.l128_stride, mb_bytes);
         const uint32_t slo = ss * L;
         lim[s] = ((uint32_t)s >= N || slo >= a.n) ? 0u : (a.n - slo < L ? a.n - slo : L);
     }
     const uint32_t Lq = (q * L >= a.n) ? 0u : (a.n - q * L < L ? a.n - q * L : L);
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, q, F32);
-    const __amdgpu_buffer_rsrc_t mine =
-        rsrc(a.l128 + (size_t)(q * 2u + c.par) * a.l128_stride, mb_bytes);
+    const uint32_t rb = a.l128_stride;
+    const __amdgpu_buffer_rsrc_t reg = rsrc(a.l128, N * 2u * rb);
+    const uint32_t mine = (q * 2u + c.par) * rb;
 
     for (uint32_t base = c.part * waves + wave; base < groups; base += gstep * GB) {
         uint32_t g[GB];
@@ -825,7 +830,7 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
             if constexpr (F32) {
                 // debug path: the owner writes its slice's accumulators to every copy
                 for (uint32_t r = 0; r < N; ++r)
-                    store_lane<true>(out_rsrc(a, r, true), q * L + e, ln.half, acc);
+                    store_lane<true>(out_all(a, true), r * a.n + q * L + e, ln.half, acc);
             } else {
                 red[j] = acc.bf16();
             }
@@ -835,15 +840,15 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 #pragma unroll
         for (int j = 0; j < GB; ++j)
             if ((gvalid >> j) & 1u)
-                l128_store_payload(mine, g[j] * L128_BYTES + lane * 16u, ln.half, red[j]);
+                l128_store_payload(reg, mine + g[j] * L128_BYTES + lane * 16u, ln.half, red[j]);
         wait_stores();
 #pragma unroll
         for (int j = 0; j < GB; ++j)
             if (((gvalid >> j) & 1u) && ln.half)
-                l128_store_flag(mine, g[j] * L128_BYTES + lane * 16u, c.flag);
+                l128_store_flag(reg, mine + g[j] * L128_BYTES + lane * 16u, c.flag);
         // ---- all-gather of the same groups
         u32x4 V[GB][NMAX];
-        if (!l128_receive<NMAX>(stg, N, q, g, gvalid, lane, ln, lim, c.flag, ctl, q,
+        if (!l128_receive<NMAX>(reg, rb, c.par, N, q, g, gvalid, lane, ln, lim, c.flag, ctl, q,
                                 a.watchdog_ticks, V))
             return;
 #pragma unroll
@@ -873,156 +878,166 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 // RS[s][q]; rank s polls RS[s][*], reduces in rank order, re-arms.
 // All-gather: rank q pushes its reduced chunk into AG[r][q] of every peer r
 // and writes it to out[q]; every rank polls AG[q][*], copies to out, re-arms.
+// Inbox regions [recv][send][parity] x s2_stride, one descriptor each.
+template <int NMAX, bool F32>
+__device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
+                                         __amdgpu_buffer_rsrc_t inq, __amdgpu_buffer_rsrc_t rsr,
+                                         __amdgpu_buffer_rsrc_t agr, __amdgpu_buffer_rsrc_t oa,
+                                         uint32_t ch, bool first)
+{
+    const uint32_t N = a.n_ranks;
+    const uint32_t q = c.rank;
+    const uint32_t L = a.slice;
+    const uint32_t sb = a.s2_stride;
+    const uint32_t e = ch * 8u;                     // element offset inside a slice
+    const uint32_t esz = F32 ? 4u : 2u;
+    const uint32_t lane_off = e * 2u + c.par * sb;
+    auto slice_len = [&](uint32_t s) -> uint32_t {
+        const uint32_t lo = s * L;
+        return lo >= a.n ? 0u : (a.n - lo < L ? a.n - lo : L);
+    };
+    // inbox offsets: receiver-major [recv][send]
+    auto box = [&](uint32_t recv, uint32_t send) { return lane_off + (recv * N + send) * 2u * sb; };
+    const uint32_t Lq = slice_len(q);
+    // ---- push my parts of every slice
+    u32x4 own = {0u, 0u, 0u, 0u};
+    u32x4 X[NMAX];
+#pragma unroll
+    for (int s = 0; s < NMAX; ++s)
+        if ((uint32_t)s < N && e < slice_len((uint32_t)s))
+            X[s] = ld16<CP_PLAIN>(inq, ((uint32_t)s * L + e) * 2u);
+    if (first)
+        start_delay(a, c);
+#pragma unroll
+    for (int s = 0; s < NMAX; ++s) {
+        if ((uint32_t)s < N && e < slice_len((uint32_t)s)) {
+            if ((uint32_t)s == q) own = X[s];
+            else st16<CP_DEV>(X[s], rsr, box((uint32_t)s, q));
+        }
+    }
+    // ---- receive my slice from everyone, reduce, re-arm
+    const bool act = e < Lq;
+    uint32_t pend = 0;
+#pragma unroll
+    for (int s = 0; s < NMAX; ++s)
+        if ((uint32_t)s < N && (uint32_t)s != q && act)
+            pend |= 1u << s;
+    u32x4 A0[NMAX], A1[NMAX], V[NMAX];
+    auto issue = [&](u32x4 *A, __amdgpu_buffer_rsrc_t reg) {
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((pend >> s) & 1u)
+                A[s] = ld16<CP_DEV>(reg, box(q, (uint32_t)s));
+    };
+    auto check = [&](const u32x4 *A) {
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((pend >> s) & 1u)
+                if (sent_ready(A[s])) {
+                    pend &= ~(1u << s);
+                    V[s] = A[s];
+                }
+    };
+    Watch w;
+    w.begin(a.watchdog_ticks);
+    issue(A0, rsr);
+    while (true) {
+        compiler_fence();
+        issue(A1, rsr);
+        check(A0);
+        if (!wave_any(pend != 0u))
+            break;
+        if (w.expired(ctl, q, pend ? first_bit(pend) : 0u, c.flag))
+            return false;
+        compiler_fence();
+        issue(A0, rsr);
+        check(A1);
+        if (!wave_any(pend != 0u))
+            break;
+    }
+    if (act) {
+        Acc8 acc;
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((uint32_t)s < N) {
+                const u32x4 v = ((uint32_t)s == q) ? own : V[s];
+                if (s == 0) acc.init(v); else acc.add(v);
+            }
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((uint32_t)s < N && (uint32_t)s != q)
+                st16<CP_DEV>(sentinel4(), rsr, box(q, (uint32_t)s));
+        if constexpr (F32) {
+            // debug path: the owner writes its slice's accumulators to every copy
+            for (uint32_t r = 0; r < N; ++r)
+                store8<true>(oa, r * a.n + q * L + e, acc);
+        } else {
+            const u32x4 red = acc.bf16();
+#pragma unroll
+            for (int r = 0; r < NMAX; ++r)
+                if ((uint32_t)r < N && (uint32_t)r != q)
+                    st16<CP_DEV>(red, agr, box((uint32_t)r, q));
+            st16<CP_PLAIN>(red, oa, (q * a.n + q * L + e) * esz);
+        }
+    }
+    if constexpr (F32)
+        return true;
+    // ---- all-gather: receive every other slice's reduced chunk
+    pend = 0;
+#pragma unroll
+    for (int s = 0; s < NMAX; ++s)
+        if ((uint32_t)s < N && (uint32_t)s != q && e < slice_len((uint32_t)s))
+            pend |= 1u << s;
+    w.begin(a.watchdog_ticks);
+    issue(A0, agr);
+    while (true) {
+        compiler_fence();
+        issue(A1, agr);
+        check(A0);
+        if (!wave_any(pend != 0u))
+            break;
+        if (w.expired(ctl, q, pend ? first_bit(pend) : 0u, c.flag))
+            return false;
+        compiler_fence();
+        issue(A0, agr);
+        check(A1);
+        if (!wave_any(pend != 0u))
+            break;
+    }
+#pragma unroll
+    for (int s = 0; s < NMAX; ++s)
+        if ((uint32_t)s < N && (uint32_t)s != q && e < slice_len((uint32_t)s)) {
+            st16<CP_PLAIN>(V[s], oa, (q * a.n + (uint32_t)s * L + e) * esz);
+            st16<CP_DEV>(sentinel4(), agr, box(q, (uint32_t)s));
+        }
+    return true;
+}
+
 template <int NMAX, bool F32>
 __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
 {
     Ctx0 c;
     begin(a, c);
     const uint32_t N = a.n_ranks;
-    const uint32_t q = c.rank;
-    const uint32_t L = a.slice;
-    const uint32_t G = L >> 3;                      // chunks per slice
+    const uint32_t G = a.slice >> 3;                // chunks per slice
     const uint32_t step = a.parts * blockDim.x;
     const uint32_t rounds = (G + step - 1u) / step;
-    const uint32_t ibytes = L * 2u;
     raise_arrival(a, c);
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
-    const __amdgpu_buffer_rsrc_t inq = in_rsrc(a, q);
-    auto rs = [&](uint32_t recv, uint32_t send) {
-        return rsrc(a.srs + (size_t)((recv * N + send) * 2u + c.par) * a.s2_stride, ibytes);
-    };
-    auto ag = [&](uint32_t recv, uint32_t send) {
-        return rsrc(a.sag + (size_t)((recv * N + send) * 2u + c.par) * a.s2_stride, ibytes);
-    };
-    auto slice_len = [&](uint32_t s) -> uint32_t {
-        uint32_t lo = s * L;
-        return lo >= a.n ? 0u : (a.n - lo < L ? a.n - lo : L);
-    };
-    const uint32_t Lq = slice_len(q);
-    const __amdgpu_buffer_rsrc_t oq = out_rsrc(a, q, F32);
-
-    for (uint32_t it = 0; it < rounds; ++it) {
-        const uint32_t ch = c.part * blockDim.x + threadIdx.x + it * step;
-        const uint32_t e = ch * 8u;                 // element offset inside a slice
-        // ---- push my parts of every slice
-        u32x4 own = {0u, 0u, 0u, 0u};
-        u32x4 X[NMAX];
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N && e < slice_len((uint32_t)s))
-                X[s] = ld16<CP_PLAIN>(inq, ((uint32_t)s * L + e) * 2u);
-        if (it == 0)
-            start_delay(a, c);
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s) {
-            if ((uint32_t)s < N && e < slice_len((uint32_t)s)) {
-                if ((uint32_t)s == q) own = X[s];
-                else st16<CP_DEV>(X[s], rs((uint32_t)s, q), e * 2u);
-            }
-        }
-        // ---- receive my slice from everyone, reduce, re-arm
-        const bool act = e < Lq;
-        uint32_t pend = 0;
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N && (uint32_t)s != q && act)
-                pend |= 1u << s;
-        u32x4 A0[NMAX], A1[NMAX], V[NMAX];
-        auto issue_rs = [&](u32x4 *A) {
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((pend >> s) & 1u)
-                    A[s] = ld16<CP_DEV>(rs(q, (uint32_t)s), e * 2u);
-        };
-        auto issue_ag = [&](u32x4 *A) {
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((pend >> s) & 1u)
-                    A[s] = ld16<CP_DEV>(ag(q, (uint32_t)s), e * 2u);
-        };
-        auto check = [&](const u32x4 *A) {
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((pend >> s) & 1u)
-                    if (sent_ready(A[s])) {
-                        pend &= ~(1u << s);
-                        V[s] = A[s];
-                    }
-        };
-        Watch w;
-        w.begin(a.watchdog_ticks);
-        issue_rs(A0);
-        while (true) {
-            compiler_fence();
-            issue_rs(A1);
-            check(A0);
-            if (!wave_any(pend != 0u))
-                break;
-            if (w.expired(ctl, q, pend ? first_bit(pend) : 0u, c.flag))
-                return;
-            compiler_fence();
-            issue_rs(A0);
-            check(A1);
-            if (!wave_any(pend != 0u))
-                break;
-        }
-        if (act) {
-            Acc8 acc;
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((uint32_t)s < N) {
-                    const u32x4 v = ((uint32_t)s == q) ? own : V[s];
-                    if (s == 0) acc.init(v); else acc.add(v);
-                }
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((uint32_t)s < N && (uint32_t)s != q)
-                    st16<CP_DEV>(sentinel4(), rs(q, (uint32_t)s), e * 2u);
-            if constexpr (F32) {
-                // debug path: the owner writes its slice's accumulators to every copy
-                for (uint32_t r = 0; r < N; ++r)
-                    store8<true>(out_rsrc(a, r, true), q * L + e, acc);
-            } else {
-                const u32x4 red = acc.bf16();
-#pragma unroll
-                for (int r = 0; r < NMAX; ++r)
-                    if ((uint32_t)r < N && (uint32_t)r != q)
-                        st16<CP_DEV>(red, ag((uint32_t)r, q), e * 2u);
-                st16<CP_PLAIN>(red, oq, (q * L + e) * 2u);
-            }
-        }
-        if constexpr (F32)
-            continue;
-        // ---- all-gather: receive every other slice's reduced chunk
-        pend = 0;
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N && (uint32_t)s != q && e < slice_len((uint32_t)s))
-                pend |= 1u << s;
-        w.begin(a.watchdog_ticks);
-        issue_ag(A0);
-        while (true) {
-            compiler_fence();
-            issue_ag(A1);
-            check(A0);
-            if (!wave_any(pend != 0u))
-                break;
-            if (w.expired(ctl, q, pend ? first_bit(pend) : 0u, c.flag))
-                return;
-            compiler_fence();
-            issue_ag(A0);
-            check(A1);
-            if (!wave_any(pend != 0u))
-                break;
-        }
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N && (uint32_t)s != q && e < slice_len((uint32_t)s)) {
-                st16<CP_PLAIN>(V[s], oq, ((uint32_t)s * L + e) * 2u);
-                st16<CP_DEV>(sentinel4(), ag(q, (uint32_t)s), e * 2u);
-            }
+    const __amdgpu_buffer_rsrc_t inq = in_rsrc(a, c.rank);
+    const __amdgpu_buffer_rsrc_t rsr = rsrc(a.srs, N * N * 2u * a.s2_stride);
+    const __amdgpu_buffer_rsrc_t agr = rsrc(a.sag, N * N * 2u * a.s2_stride);
+    const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
+    uint32_t ch = c.part * blockDim.x + threadIdx.x;
+    // round 0 straight-line (see the one-shot LL kernel), later rounds looped
+    if (!ts_round<NMAX, F32>(a, c, ctl, inq, rsr, agr, oa, ch, true))
+        return;
+    for (uint32_t it = 1; it < rounds; ++it) {
         wait_stores();
+        ch += step;
+        if (!ts_round<NMAX, F32>(a, c, ctl, inq, rsr, agr, oa, ch, false))
+            return;
     }
     finish(a, c);
 }
