@@ -66,7 +66,7 @@ enum ar_proto {
     AR_PROTO_LL = 1,        /* one-shot only */
     AR_PROTO_LL128 = 2,     /* one-shot or two-shot */
     AR_PROTO_SENTINEL = 3,  /* one-shot or two-shot */
-    AR_PROTO_DIRECT = 4     /* arrival counters instead of staging: one-shot reads
+    AR_PROTO_DIRECT = 4     /* arrival flags instead of staging: one-shot reads
                                peers' inputs in place; two-shot reads slice q in
                                place and writes the reduced slice straight into
                                every rank's output, then completion flags */

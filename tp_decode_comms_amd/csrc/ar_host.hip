@@ -229,6 +229,17 @@ int make_plan(size_t n, bool f32, Plan *p)
         return AR_ERR_INVALID;
     uint64_t want = g.wgs_per_rank > 0 ? (uint64_t)g.wgs_per_rank : (units + per_wg - 1) / per_wg;
     if (want == 0) want = 1;
+    if (g.wgs_per_rank == 0) {
+        // a multiple of the XCD count puts part p of every rank on XCD p % 8
+        // (round-robin dispatch), so each part's exchange stays in one L2;
+        // surplus workgroups find no work and only take part in the flags
+        const uint64_t X = ar::XCDS;
+        const uint64_t up = (want + X - 1) / X * X;
+        if (up <= cap)
+            want = up;
+        else if (cap >= X)
+            want = cap / X * X;
+    }
     if (want > cap) want = cap;
     p->parts = (uint32_t)want;
     return AR_OK;

@@ -1,13 +1,15 @@
 // ar_kernels.hip -- gfx950 kernels of the barrier-free fixed-order AllReduce.
 //
-// One launch = one AllReduce call for all N emulated ranks.  Workgroup b
-// belongs to rank b % N and covers part b / N of that rank's work, so with
-// the hardware's round-robin workgroup-to-XCD dispatch every rank of an
-// 8-rank call lives on one XCD and every exchange between ranks crosses XCD
-// L2 caches, as exchanges between GPUs cross the fabric.  Workgroups of one
-// part index depend only on each other, and the host never launches more
-// workgroups than the device holds at once, so every poll has a resident
-// producer.
+// One launch = one AllReduce call for all N emulated ranks; each workgroup
+// covers one part of one rank's work (mapping in begin()).  The hardware
+// dispatches workgroups to the 8 XCDs round-robin by index, and the host
+// makes `parts` a multiple of 8, so part p of every rank runs on XCD p % 8:
+// all traffic of one part (mailboxes, inboxes, lines, arrival and completion
+// flags) stays inside one XCD's L2.  Correctness does not depend on that
+// placement (every flag and staging access is device-coherent); only latency
+// does.  Workgroups of one part index depend only on each other and are
+// dispatched together, and the host never launches more workgroups than the
+// device holds at once, so every poll has a producer that runs.
 //
 // Algorithms ("Every Microsecond Counts" write-up, page "微秒必争…", section
 // "统一原语与API设计" and its table of variants):
@@ -23,10 +25,13 @@
 // every rank and in both algorithms, so all variants give identical bits.
 //
 // Latency notes (measured on MI355X): a line written by one XCD with the
-// device-scope policy becomes readable by another XCD about 1 us later, and
-// a wave's loads cannot be consumed before its earlier device-scope stores
-// are acknowledged (one in-order counter for both).  Polls therefore keep two
-// batches of loads in flight, and flag words are tiny and read by few lanes.
+// device-scope policy becomes readable by another XCD about 1 us later, by
+// the same XCD about 0.5-0.9 us later; a wave's loads cannot be consumed
+// before its earlier stores are acknowledged (one in-order counter for
+// both).  Polls therefore keep two batches of loads in flight, start only
+// after the wave's own publish is acknowledged (a poll issued earlier mostly
+// returns stale data and costs a second round trip), and flag words are tiny
+// and read by few lanes.
 #include "ar_proto.h"
 #include "ar_kernels.h"
 
@@ -78,8 +83,16 @@ __device__ __forceinline__ void finish(const Launch &a, const Ctx0 &c)
 __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
 {
     c.t0 = clock100();
-    c.rank = blockIdx.x % a.n_ranks;
-    c.part = blockIdx.x / a.n_ranks;
+    // blocks of X*N consecutive workgroups, rank-major over X consecutive
+    // parts: with X = 8 (parts a multiple of 8) part p lands on XCD p % 8;
+    // every workgroup's peers (same part, other ranks) sit in its own block
+    // and parts 0..7 of every rank (arrival writers, completion waiters) in
+    // the first, so progress never needs more than one block resident
+    const uint32_t X = (a.parts % (uint32_t)XCDS) == 0u ? (uint32_t)XCDS : 1u;
+    const uint32_t span = X * a.n_ranks;
+    const uint32_t w = blockIdx.x % span;
+    c.rank = w / X;
+    c.part = (blockIdx.x / span) * X + w % X;
     c.par = a.epoch & 1u;
 }
 
@@ -135,24 +148,31 @@ __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t o, uint32_t elem, 
 }
 
 // ============================================================ arrivals
-// Rank s announces "my input for this call is final" by adding one to its
-// arrival counter (one workgroup per rank does it, at its very start, with
-// no dependence on any load).  After k calls since the last reset the
-// counter is k, and a call whose flag is f = seq + epoch needs counter >= f.
-__device__ __forceinline__ void raise_arrival(const Launch &a, const Ctx0 &c)
+// Rank s announces "my input for this call is final" by storing the call's
+// flag f = seq + epoch into its arrival word, at its very start and with no
+// dependence on any load.  Flags grow monotonically between wraps, so a
+// reader needs word >= f (wrap-safe compare).  The word is replicated per
+// XCD: parts x < 8 of rank s write copy x, and part p reads copy p % 8,
+// which the same-XCD part of every peer wrote.  Only kinds that read peers'
+// data in place (DIRECT) use arrivals.
+__device__ __forceinline__ uint32_t arrive_off(uint32_t copy, uint32_t rank)
 {
-    if (c.part == 0 && threadIdx.x == 0)
-        __hip_atomic_fetch_add(a.ctl + CTL_ARRIVE + 32u * c.rank, 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+    return (CTL_ARRIVE + 32u * (copy * MAX_RANKS + rank)) * 4u;
 }
 
-// Every wave waits (two polls in flight) until all N arrival counters reach
-// the call's flag.  Lanes 0..N-1 each watch one counter.
+__device__ __forceinline__ void raise_arrival(const Launch &a, const Ctx0 &c)
+{
+    if (c.part < (uint32_t)XCDS && threadIdx.x == 0)
+        st4<CP_DEV>(c.flag, rsrc(a.ctl, CTL_WORDS * 4u), arrive_off(c.part, c.rank));
+}
+
+// Every wave waits (two polls in flight) until all N arrival words of its
+// XCD's copy reach the call's flag.  Lanes 0..N-1 each watch one word.
 __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, const Ctl &ctl)
 {
     const uint32_t lane = threadIdx.x & 63u;
     bool need = lane < a.n_ranks;
-    const uint32_t off = (CTL_ARRIVE + 32u * (lane & 15u)) * 4u;
+    const uint32_t off = arrive_off(c.part % (uint32_t)XCDS, lane & (MAX_RANKS - 1u));
     const __amdgpu_buffer_rsrc_t r = rsrc(a.ctl, CTL_WORDS * 4u);
     Watch w;
     w.begin(a.watchdog_ticks);
@@ -194,6 +214,7 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
     // publish (send/bcast): one copy, read by all N ranks
     if (active)
         st16<CP_DEV>(ll_pack(x.x, x.y, c.flag), llr, lane_off + c.rank * 2u * rb);
+    wait_stores();                  // first poll only after the publish is acknowledged
     // receive (recvReduce): poll every peer's unit for this chunk
     uint32_t pend = 0;
 #pragma unroll
@@ -265,7 +286,6 @@ __global__ __launch_bounds__(256) void k_oneshot_ll(const Launch a)
     u32x2 x = {0u, 0u};
     if (ch < C)
         x = ld8<CP_PLAIN>(inr, ch * 8u);
-    raise_arrival(a, c);
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     const __amdgpu_buffer_rsrc_t llr = rsrc(a.ll, a.n_ranks * 2u * a.ll_stride);
@@ -306,7 +326,6 @@ __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
     u32x4 x = {0u, 0u, 0u, 0u};
     if (ch < G)
         x = ld16<CP_PLAIN>(inr, ch * 16u);
-    raise_arrival(a, c);
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     // all inboxes [recv][send][parity] x s1_stride under one descriptor
@@ -405,7 +424,7 @@ __device__ __forceinline__ bool wait_arrivals_wg(const Launch &a, const Ctx0 &c,
 }
 
 // ========================================================= one-shot DIRECT
-// After the arrival counters, each rank reads every peer's input in place
+// After the arrival flags, each rank reads every peer's input in place
 // with device-coherent loads and reduces.  The input of call k must stay
 // unchanged until call k has completed on every rank (the application-level
 // A/B double buffering of the SiFAR page, "SiFAR：无同步All-Reduce技术突破低
@@ -419,14 +438,10 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
     const uint32_t G = a.n >> 3;
     const uint32_t step = a.parts * blockDim.x;
     const uint32_t rounds = (G + step - 1u) / step;
-    if (a.delays == nullptr)
-        raise_arrival(a, c);
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
-    if (a.delays != nullptr) {
-        start_delay(a, c);
-        raise_arrival(a, c);
-    }
+    start_delay(a, c);
+    raise_arrival(a, c);
     if (!wait_arrivals(a, c, ctl))
         return;
     __amdgpu_buffer_rsrc_t src[NMAX];
@@ -456,7 +471,7 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
 
 // ========================================================= two-shot DIRECT
 // Reduce-scatter: rank q reads slice q of every rank's input in place (after
-// the arrival counters) and reduces it; all-gather: it stores the bf16
+// the arrival flags) and reduces it; all-gather: it stores the bf16
 // result straight into slice q of every rank's output (the bcast of the
 // reduced value), with streaming device-scope stores.  Each workgroup then
 // waits for its stores to be acknowledged and raises its completion flag;
@@ -476,14 +491,10 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     const uint32_t Lq = lo >= a.n ? 0u : (a.n - lo < L ? a.n - lo : L);
     const uint32_t G = Lq >> 3;                     // chunks of my slice
     const uint32_t step = a.parts * blockDim.x;
-    if (a.delays == nullptr)
-        raise_arrival(a, c);
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
-    if (a.delays != nullptr) {
-        start_delay(a, c);
-        raise_arrival(a, c);
-    }
+    start_delay(a, c);
+    raise_arrival(a, c);
     if (!wait_arrivals_wg(a, c, ctl))
         return;
     __amdgpu_buffer_rsrc_t src[NMAX];
@@ -517,24 +528,28 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
                     store8<F32, CP_NT | CP_DEV>(oa, (uint32_t)r * a.n + lo + ch2 * 8u, acc2);
             }
     }
-    // completion: my stores are at the coherence point, then my flag; one
-    // workgroup per rank (part 0) waits for every writer's flag, which
-    // proves that every slice of that rank's output is complete
+    // completion: my stores are at the coherence point, then my flag.  Part
+    // x < 8 of each rank waits for the flags of the writers (s, p) with
+    // p % 8 == x, which run on its own XCD; together the up-to-8 waiters of
+    // rank q see every writer, which proves that every slice of q's output
+    // is complete before q's workgroups exit.
     wait_stores();
     __syncthreads();
     const __amdgpu_buffer_rsrc_t dn = rsrc(a.done, MAX_RANKS * DONE_STRIDE * 4u);
     if (threadIdx.x == 0)
         st4<CP_DEV>(c.flag, dn, (q * DONE_STRIDE + c.part) * 4u);
-    if (c.part == 0 && threadIdx.x < 64u) {
+    if (c.part < (uint32_t)XCDS && threadIdx.x < 64u) {
         const uint32_t lane = threadIdx.x;
-        const uint32_t total = N * a.parts;            // writers: (rank, part) pairs
+        const uint32_t x = c.part;
+        const uint32_t per = (a.parts - x + XCDS - 1u) / XCDS;   // parts x, x+8, ...
+        const uint32_t total = N * per;                // writers this waiter covers
         Watch w;
         w.begin(a.watchdog_ticks);
         uint32_t i = lane;                             // next writer this lane checks
         while (true) {
             // each lane walks its share of the writers, skipping those seen
             while (i < total) {
-                const uint32_t s = i / a.parts, p = i % a.parts;
+                const uint32_t s = i / per, p = x + XCDS * (i % per);
                 const uint32_t v = ld4<CP_DEV>(dn, (s * DONE_STRIDE + p) * 4u);
                 if ((int32_t)(v - c.flag) < 0)
                     break;
@@ -542,7 +557,7 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
             }
             if (!wave_any(i < total))
                 break;
-            if (w.expired(ctl, q, i < total ? i / a.parts : 0u, c.flag))
+            if (w.expired(ctl, q, i < total ? i / per : 0u, c.flag))
                 return;
             compiler_fence();
         }
@@ -695,7 +710,6 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
     const uint32_t waves = blockDim.x >> 6;
     const uint32_t groups = (a.n + L128_ELEMS - 1u) / L128_ELEMS;
     const uint32_t gstep = a.parts * waves;
-    raise_arrival(a, c);
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     const L128Lane ln = l128_lane(lane);
@@ -755,7 +769,7 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 
 // ====================================================== two-shot LL128
 // Reduce-scatter: rank q reduces slice q (elements [q*L, q*L + Lq)) reading
-// every rank's input in place after the arrival counters, and publishes the
+// every rank's input in place after the arrival flags, and publishes the
 // bf16 result as line groups.  All-gather: rank q receives every slice's
 // groups (its own from registers) and writes them to out[q].  Groups are
 // handled GB at a time per wave as in the one-shot kernel.
@@ -773,15 +787,11 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
     const uint32_t waves = blockDim.x >> 6;
     const uint32_t groups = (L + L128_ELEMS - 1u) / L128_ELEMS;
     const uint32_t gstep = a.parts * waves;
-    if (a.delays == nullptr)
-        raise_arrival(a, c);
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     const L128Lane ln = l128_lane(lane);
-    if (a.delays != nullptr) {
-        start_delay(a, c);
-        raise_arrival(a, c);
-    }
+    start_delay(a, c);
+    raise_arrival(a, c);
     if (!wait_arrivals(a, c, ctl))
         return;
     uint32_t lim[NMAX];
@@ -1022,7 +1032,6 @@ __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
     const uint32_t G = a.slice >> 3;                // chunks per slice
     const uint32_t step = a.parts * blockDim.x;
     const uint32_t rounds = (G + step - 1u) / step;
-    raise_arrival(a, c);
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     const __amdgpu_buffer_rsrc_t inq = in_rsrc(a, c.rank);
@@ -1045,7 +1054,7 @@ __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
 // ============================================================ maintenance
 // Advances the flag sequence after a step of `calls` calls.  When the
 // sequence nears the top of its 32-bit range, every flag word (LL units,
-// LL128 lines, arrival counters, completion flags) is cleared and the
+// LL128 lines, arrival flags, completion flags) is cleared and the
 // sequence restarts, so a flag value left in memory long ago can never match
 // a future call.
 __global__ __launch_bounds__(256) void k_step_end(uint32_t *ctl, uint32_t calls, char *ll,
@@ -1065,7 +1074,7 @@ __global__ __launch_bounds__(256) void k_step_end(uint32_t *ctl, uint32_t calls,
         w = (uint32_t *)l128;
         for (size_t i = threadIdx.x; i < l128_bytes / 4; i += blockDim.x) w[i] = 0u;
         for (size_t i = threadIdx.x; i < (size_t)MAX_RANKS * DONE_STRIDE; i += blockDim.x) done[i] = 0u;
-        for (uint32_t i = threadIdx.x; i < (uint32_t)MAX_RANKS; i += blockDim.x)
+        for (uint32_t i = threadIdx.x; i < (uint32_t)(MAX_RANKS * XCDS); i += blockDim.x)
             __hip_atomic_store(ctl + CTL_ARRIVE + 32u * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __threadfence();
     }

@@ -40,8 +40,13 @@ constexpr uint32_t SENT_WORD = 0xFFFFFFFFu;   // two sentinel bf16 (0xFFFF)
 // control block layout (uint32 words); each field on its own 128-byte line
 constexpr int CTL_SEQ = 0;          // flag-sequence base
 constexpr int CTL_STATUS = 32;      // {code, rank, source, flag}
-constexpr int CTL_ARRIVE = 64;      // arrival flag of rank r at CTL_ARRIVE + 32*r
-constexpr int CTL_WORDS = CTL_ARRIVE + 32 * MAX_RANKS;
+// Workgroups are dispatched to the XCDs round-robin by workgroup index, so
+// with `parts` a multiple of XCDS part p of every rank runs on XCD p % XCDS.
+constexpr int XCDS = 8;
+// arrival flag of rank r, copy x (read and written by workgroups of parts
+// p = x mod XCDS) at CTL_ARRIVE + 32*(x*MAX_RANKS + r), one 128-byte line each
+constexpr int CTL_ARRIVE = 64;
+constexpr int CTL_WORDS = CTL_ARRIVE + 32 * MAX_RANKS * XCDS;
 constexpr uint32_t STATUS_TIMEOUT = 6;
 constexpr uint32_t DONE_STRIDE = 8192;
 constexpr uint32_t TS_SUB = 64;          // timestamp sub-slots per call   // completion flags per rank (>= workgroups per rank)
