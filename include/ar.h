@@ -30,7 +30,11 @@
  *
  * Emulation.  On one GPU the N ranks are disjoint sets of workgroups of one
  * kernel launch; they exchange data only through staging buffers and flag
- * words in device memory, reached with device-scope coherent accesses.
+ * words in device memory.  Part p of every rank's work runs on XCD p % 8
+ * (the hardware dispatches workgroups to the 8 XCDs round-robin), so one
+ * part's exchange stays inside one XCD's L2.  Staging and flag accesses are
+ * device-scope coherent, or -- once ar_init has verified the placement --
+ * XCD-local (see ar_set_scope).
  *
  * Conventions for every entry point:
  *   - return value: AR_OK (0) or a negative ar_status code; nothing aborts;
@@ -56,7 +60,15 @@ enum ar_status {
     AR_ERR_STATE = -3,      /* already initialised / wrong call order */
     AR_ERR_OOM = -4,        /* device allocation failed */
     AR_ERR_HIP = -5,        /* a HIP runtime call failed (see ar_last_hip_error) */
-    AR_ERR_TIMEOUT = -6     /* a device poll exceeded the watchdog (ar_get_status) */
+    AR_ERR_TIMEOUT = -6,    /* a device poll exceeded the watchdog (ar_get_status) */
+    AR_ERR_PLACEMENT = -7   /* an XCD-local launch ran a workgroup on an unexpected
+                               XCD (ar_get_status); use AR_SCOPE_DEVICE */
+};
+
+enum ar_scope {
+    AR_SCOPE_AUTO = 0,      /* XCD-local when ar_init verified the placement and
+                               the launch's part count is a multiple of 8 */
+    AR_SCOPE_DEVICE = 1     /* device scope always: correct on any placement */
 };
 
 enum ar_algo { AR_ALGO_AUTO = 0, AR_ALGO_ONESHOT = 1, AR_ALGO_TWOSHOT = 2 };
@@ -149,6 +161,19 @@ int ar_set_options(int algo, int proto);
 int ar_set_launch(int wgs_per_rank, int threads);
 
 /*
+ * ar_set_scope -- coherence scope of the staging buffers and flag words
+ * (enum ar_scope; default AR_SCOPE_AUTO).  XCD-local scope serves every
+ * exchange from the L2 of the XCD its writer and reader share: stores at
+ * workgroup scope and streaming workgroup-scope polls instead of
+ * device-scope accesses.  It relies on the round-robin placement, which
+ * ar_init checks with a probe launch (ar_query key 9); every workgroup of an
+ * XCD-local launch also checks its own XCD and, on a mismatch, records
+ * AR_ERR_PLACEMENT, which makes the peers' polls give up.  The fp32 debug
+ * path always uses device scope.  Returns AR_ERR_INVALID for other values.
+ */
+int ar_set_scope(int scope);
+
+/*
  * ar_set_watchdog -- per-poll time budget in microseconds (default 200000).
  * A poll that exceeds it records {6, rank, source, flag} in the device status
  * record and its workgroup stops; the other workgroups of that call stop
@@ -189,8 +214,10 @@ int ar_set_timestamps(uint64_t *dev_ts, size_t slots);
 
 /*
  * ar_get_status -- copy the device status record {code, rank, source, flag}
- * into out[4] (synchronises the device first).  code is 0 or the positive
- * value of -AR_ERR_TIMEOUT.  Returns AR_ERR_TIMEOUT if a watchdog fired.
+ * into out[4] (synchronises the device first).  code is 0, 6 (a watchdog
+ * fired: rank that gave up, source it waited for, call flag) or 7 (XCD-local
+ * placement violated: rank, XCD it ran on, part).  Returns AR_OK,
+ * AR_ERR_TIMEOUT or AR_ERR_PLACEMENT accordingly.
  */
 int ar_get_status(uint32_t out[4]);
 
@@ -213,7 +240,8 @@ int ar_last_hip_error(void);
  *   0 n_ranks, 1 max_elems, 2 algorithm a call of n elements would use,
  *   3 its protocol, 4 workgroups it would launch, 5 threads per workgroup,
  *   6 resident-workgroup capacity of the device for that kernel, 7 the host
- *   epoch counter.
+ *   epoch counter, 8 1 if a call of n elements would use XCD-local scope
+ *   (else 0), 9 1 if ar_init verified the round-robin XCD placement.
  * Returns the value, or a negative status.
  */
 long long ar_query(int key, size_t n);

@@ -42,12 +42,13 @@ def empty_out(N, n, f32=False):
 
 
 @contextlib.contextmanager
-def ar_context(N, max_elems, algo=0, proto=0, wgs=0, threads=0, watchdog_us=0):
+def ar_context(N, max_elems, algo=0, proto=0, wgs=0, threads=0, watchdog_us=0, scope=0):
     import tp_decode_comms_amd as ar
     ar.init(N, max_elems)
     try:
         ar.set_options(algo, proto)
         ar.set_launch(wgs, threads)
+        ar.set_scope(scope)
         ar.set_watchdog(watchdog_us)
         yield ar
     finally:
@@ -74,7 +75,7 @@ def assert_bits_equal(got, want, what=""):
 def check_status_clean():
     import tp_decode_comms_amd as ar
     st = ar.get_status()
-    assert st[0] == 0, "watchdog fired: %r" % (st,)
+    assert st[0] == 0, "device status not clean (6 watchdog, 7 placement): %r" % (st,)
 
 
 __all__ = ["synth", "oracle"]

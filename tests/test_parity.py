@@ -45,14 +45,20 @@ def _run_calls(ar, datas, n, calls, out_list=None, f32=False):
     return outs
 
 
+SCOPES = [("auto", 0), ("device", 1)]
+
+
+@pytest.mark.parametrize("scope_name,scope", SCOPES, ids=[s[0] for s in SCOPES])
 @pytest.mark.parametrize("name,algo,proto", VARIANTS, ids=[v[0] for v in VARIANTS])
 @pytest.mark.parametrize("N,n", [(8, 8192), (8, 4096 + 8), (4, 20008), (2, 968), (16, 3592),
                                  (8, 262144 + 480 * 3 + 16)])
-def test_variant_matches_oracle(name, algo, proto, N, n):
-    log("variant %s N=%d n=%d" % (name, N, n))
+def test_variant_matches_oracle(name, algo, proto, N, n, scope_name, scope):
+    """Every variant in both coherence scopes: XCD-local (auto, where the
+    placement allows it) and device scope."""
+    log("variant %s N=%d n=%d scope=%s" % (name, N, n, scope_name))
     datas = [synth.random_bits(1000 + 10 * s + N, (N, n), finite_only=True, avoid=0xFFFF)
              for s in range(3)]
-    with ar_context(N, n + 64, algo, proto) as ar:
+    with ar_context(N, n + 64, algo, proto, scope=scope) as ar:
         outs = _run_calls(ar, datas, n, 6)
         check_status_clean()
     for k, out in enumerate(outs):
@@ -165,3 +171,16 @@ def test_rejects_bad_calls():
         assert a.allreduce(ins, out, n, 1) == 0
         torch.cuda.synchronize()
     assert_bits_equal(host_bits(out), expect(data))
+
+
+def test_xcd_local_scope_is_used():
+    """On MI355X the round-robin placement verifies, and the small-message
+    and bandwidth shapes launch with the XCD-local scope; AR_SCOPE_DEVICE
+    turns it off."""
+    import tp_decode_comms_amd as ar
+    with ar_context(8, 1 << 21) as a:
+        assert a.query(9, 0) == 1
+        for n in (8192, 32 * 8192, 256 * 8192):
+            assert a.query(8, n) == 1, n
+        a.set_scope(ar.AR_SCOPE_DEVICE)
+        assert a.query(8, 8192) == 0

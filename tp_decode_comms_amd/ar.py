@@ -17,6 +17,8 @@ AR_ERR_STATE = -3
 AR_ERR_OOM = -4
 AR_ERR_HIP = -5
 AR_ERR_TIMEOUT = -6
+AR_ERR_PLACEMENT = -7
+AR_SCOPE_AUTO, AR_SCOPE_DEVICE = 0, 1
 
 AR_ALGO_AUTO, AR_ALGO_ONESHOT, AR_ALGO_TWOSHOT = 0, 1, 2
 AR_PROTO_AUTO, AR_PROTO_LL, AR_PROTO_LL128, AR_PROTO_SENTINEL, AR_PROTO_DIRECT = 0, 1, 2, 3, 4
@@ -32,6 +34,7 @@ _SIGS = {
     "ar_destroy": (_c_int, []),
     "ar_set_options": (_c_int, [_c_int, _c_int]),
     "ar_set_launch": (_c_int, [_c_int, _c_int]),
+    "ar_set_scope": (_c_int, [_c_int]),
     "ar_set_watchdog": (_c_int, [_c_u32]),
     "ar_step_end": (_c_int, [_c_vp]),
     "ar_set_delays": (_c_int, [_c_vp, _c_size]),
@@ -144,6 +147,10 @@ def set_launch(wgs_per_rank=0, threads=0):
     return _check("ar_set_launch", lib().ar_set_launch(int(wgs_per_rank), int(threads)))
 
 
+def set_scope(scope=AR_SCOPE_AUTO):
+    return _check("ar_set_scope", lib().ar_set_scope(int(scope)))
+
+
 def set_watchdog(budget_us=0):
     return _check("ar_set_watchdog", lib().ar_set_watchdog(int(budget_us)))
 
@@ -166,7 +173,7 @@ def get_status():
     """Returns (code, rank, source, flag) of the device status record."""
     buf = (_c_u32 * 4)()
     rc = lib().ar_get_status(buf)
-    if rc not in (AR_OK, AR_ERR_TIMEOUT):
+    if rc not in (AR_OK, AR_ERR_TIMEOUT, AR_ERR_PLACEMENT):
         raise ArError("ar_get_status", rc)
     return tuple(int(x) for x in buf)
 

@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "../../include/ar.h"
 #include "ar_kernels.h"
@@ -41,6 +42,8 @@ struct Context {
     int algo = AR_ALGO_AUTO;
     int proto = AR_PROTO_AUTO;
     int wgs_per_rank = 0;
+    int scope = AR_SCOPE_AUTO;
+    bool placement_ok = false;   // round-robin XCD dispatch verified at init
     int threads = 0;                    // 0 = chosen per call
     uint32_t watchdog_us = DEFAULT_WATCHDOG_US;
     const uint32_t *delays = nullptr; size_t delay_rows = 0;
@@ -133,9 +136,17 @@ int compute_capacity()
             for (int t = 0; t < 3; ++t) {
                 int per_cu = 0;
                 hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &per_cu, ar::kernel_for(k, g.n_ranks, f == 1), tcounts[t], 0);
+                    &per_cu, ar::kernel_for(k, g.n_ranks, f == 1, false), tcounts[t], 0);
                 if (e != hipSuccess)
                     return hip_fail(e);
+                if (f == 0) {           // bf16: the XCD-local variant too
+                    int per_cu_local = 0;
+                    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                        &per_cu_local, ar::kernel_for(k, g.n_ranks, false, true), tcounts[t], 0);
+                    if (e != hipSuccess)
+                        return hip_fail(e);
+                    per_cu = std::min(per_cu, per_cu_local);
+                }
                 g.capacity[k][f][t] = per_cu * g.cu_count;
             }
         }
@@ -149,6 +160,7 @@ struct Plan {
     uint32_t parts;     // workgroups per rank
     uint32_t threads;
     uint32_t slice;
+    bool local;         // XCD-local coherence scope
 };
 
 int choose_kind(size_t n, int *kind)
@@ -242,6 +254,7 @@ int make_plan(size_t n, bool f32, Plan *p)
     }
     if (want > cap) want = cap;
     p->parts = (uint32_t)want;
+    p->local = !f32 && g.scope == AR_SCOPE_AUTO && g.placement_ok && p->parts % ar::XCDS == 0;
     return AR_OK;
 }
 
@@ -271,6 +284,33 @@ int check_call(const void *const *rank_bufs, const void *out, size_t out_elem_by
     return AR_OK;
 }
 
+// Checks that workgroup b of a launch runs on XCD b % 8 for grids of both
+// workgroup sizes in use; the XCD-local scope is only enabled if it does.
+hipError_t verify_placement(bool *ok)
+{
+    *ok = false;
+    const uint32_t grid = 4096;
+    uint32_t *d = nullptr;
+    hipError_t e = hipMalloc((void **)&d, grid * 4);
+    if (e != hipSuccess)
+        return e;
+    std::vector<uint32_t> h(grid);
+    bool good = true;
+    for (uint32_t threads : {64u, 256u}) {
+        if ((e = ar::launch_fill(d, grid, 0xFFFFFFFFu, 0)) != hipSuccess ||
+            (e = ar::launch_xcc_map(d, grid, threads, 0)) != hipSuccess ||
+            (e = hipMemcpy(h.data(), d, grid * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+            break;
+        for (uint32_t b = 0; b < grid; ++b)
+            good = good && h[b] == b % ar::XCDS;
+    }
+    hipError_t ef = hipFree(d);
+    if (e == hipSuccess)
+        e = ef;
+    *ok = e == hipSuccess && good;
+    return e;
+}
+
 int do_allreduce(const void *const *rank_bufs, void *out, size_t n, uint32_t epoch,
                  hipStream_t stream, bool f32)
 {
@@ -298,13 +338,18 @@ int do_allreduce(const void *const *rank_bufs, void *out, size_t n, uint32_t epo
     a.epoch = epoch;
     a.parts = p.parts;
     a.slice = p.slice;
+    // workgroup layout: blocks of 8 parts x N ranks when parts % 8 == 0 (so
+    // part p runs on XCD p % 8), else rank-interleaved (blocks of N)
+    a.xshift = p.parts % ar::XCDS == 0 ? 3u : 0u;
+    a.span = (uint32_t)g.n_ranks << a.xshift;
+    a.span_magic = a.span > 1 ? (uint32_t)(((1ull << 32) + a.span - 1) / a.span) : 0u;
     uint64_t ticks = (uint64_t)g.watchdog_us * 100u;   // 100 MHz clock
     a.watchdog_ticks = (uint32_t)std::min<uint64_t>(ticks, 0xFFFFFFFFu);
     const uint32_t grid = p.parts * (uint32_t)g.n_ranks;
     if (debug_enabled())
-        fprintf(stderr, "[ar] n=%zu epoch=%u kind=%d grid=%u threads=%u slice=%u f32=%d\n", n,
-                epoch, p.kind, grid, p.threads, p.slice, (int)f32);
-    hipError_t e = ar::launch_ar(p.kind, f32, a, grid, p.threads, stream);
+        fprintf(stderr, "[ar] n=%zu epoch=%u kind=%d grid=%u threads=%u slice=%u f32=%d local=%d\n",
+                n, epoch, p.kind, grid, p.threads, p.slice, (int)f32, (int)p.local);
+    hipError_t e = ar::launch_ar(p.kind, f32, p.local, a, grid, p.threads, stream);
     if (e != hipSuccess)
         return hip_fail(e);
     g.last_epoch = epoch;
@@ -353,6 +398,8 @@ int ar_init(int n_ranks, size_t max_elems)
     }
     e = rearm(0);
     if (e == hipSuccess)
+        e = verify_placement(&g.placement_ok);
+    if (e == hipSuccess)
         e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         free_all();
@@ -360,6 +407,7 @@ int ar_init(int n_ranks, size_t max_elems)
     }
     g.algo = AR_ALGO_AUTO; g.proto = AR_PROTO_AUTO;
     g.wgs_per_rank = 0; g.threads = 0;
+    g.scope = AR_SCOPE_AUTO;
     g.watchdog_us = DEFAULT_WATCHDOG_US;
     g.delays = nullptr; g.delay_rows = 0;
     g.ts = nullptr; g.ts_slots = 0;
@@ -425,6 +473,16 @@ int ar_set_launch(int wgs_per_rank, int threads)
     return AR_OK;
 }
 
+int ar_set_scope(int scope)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    if (scope != AR_SCOPE_AUTO && scope != AR_SCOPE_DEVICE)
+        return AR_ERR_INVALID;
+    g.scope = scope;
+    return AR_OK;
+}
+
 int ar_set_watchdog(uint32_t budget_us)
 {
     if (!g.live)
@@ -483,7 +541,9 @@ int ar_get_status(uint32_t out[4])
     e = hipMemcpy(out, g.ctl + ar::CTL_STATUS, 16, hipMemcpyDeviceToHost);
     if (e != hipSuccess)
         return hip_fail(e);
-    return out[0] == ar::STATUS_TIMEOUT ? AR_ERR_TIMEOUT : AR_OK;
+    if (out[0] == ar::STATUS_TIMEOUT)
+        return AR_ERR_TIMEOUT;
+    return out[0] == ar::STATUS_PLACEMENT ? AR_ERR_PLACEMENT : AR_OK;
 }
 
 int ar_reset(hipStream_t stream)
@@ -507,6 +567,7 @@ const char *ar_strerror(int status)
     case AR_ERR_OOM: return "device out of memory";
     case AR_ERR_HIP: return "HIP runtime error";
     case AR_ERR_TIMEOUT: return "device poll exceeded the watchdog";
+    case AR_ERR_PLACEMENT: return "workgroup ran on an unexpected XCD under XCD-local scope";
     default: return "unknown status";
     }
 }
@@ -553,6 +614,13 @@ long long ar_query(int key, size_t n)
         return g.capacity[kind][0][2];
     }
     case 7: return g.last_epoch;
+    case 8: {
+        if (n == 0 || n > g.max_elems || n % 8)
+            return AR_ERR_INVALID;
+        int rc = make_plan(n, false, &p);
+        return rc != AR_OK ? rc : (p.local ? 1 : 0);
+    }
+    case 9: return g.placement_ok ? 1 : 0;
     default: return AR_ERR_INVALID;
     }
 }

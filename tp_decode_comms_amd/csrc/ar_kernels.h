@@ -19,11 +19,14 @@ enum KernelKind {
     K_COUNT = 7
 };
 
-// device function of a kernel kind for n_ranks (<= 8 or <= 16 instantiation)
-const void *kernel_for(int kind, int n_ranks, bool f32);
+// device function of a kernel kind for n_ranks (<= 8 or <= 16 instantiation);
+// local selects the XCD-local coherence scope (bf16 kernels only)
+const void *kernel_for(int kind, int n_ranks, bool f32, bool local);
 
-hipError_t launch_ar(int kind, bool f32, const Launch &a, uint32_t grid, uint32_t threads,
-                     hipStream_t stream);
+hipError_t launch_ar(int kind, bool f32, bool local, const Launch &a, uint32_t grid,
+                     uint32_t threads, hipStream_t stream);
+// out[b] = XCD index of workgroup b, for b < grid
+hipError_t launch_xcc_map(uint32_t *out, uint32_t grid, uint32_t threads, hipStream_t stream);
 hipError_t launch_step_end(uint32_t *ctl, uint32_t calls, char *ll, size_t ll_bytes, char *l128,
                            size_t l128_bytes, uint32_t *done, hipStream_t stream);
 hipError_t launch_fill(uint32_t *p, size_t words, uint32_t value, hipStream_t stream);

@@ -43,11 +43,13 @@ struct Ctx0 {
     uint64_t t0;
 };
 
-// The flag-sequence base, read coherently (it is advanced by the step-end
-// kernel; a stale copy would make flags repeat).
+// The flag-sequence base.  Only the step-end kernel and the host's re-arm
+// kernels write it, always in an earlier launch; the launch boundary makes
+// that write visible, so a plain load suffices (no launch writes it while
+// an AllReduce kernel runs).
 __device__ __forceinline__ uint32_t load_seq(const Launch &a)
 {
-    return __hip_atomic_load(a.ctl + CTL_SEQ, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return ld4<CP_PLAIN>(rsrc(a.ctl, CTL_WORDS * 4u), CTL_SEQ * 4u);
 }
 
 __device__ __forceinline__ void start_delay(const Launch &a, const Ctx0 &c)
@@ -80,6 +82,7 @@ __device__ __forceinline__ void finish(const Launch &a, const Ctx0 &c)
     }
 }
 
+template <bool LOCAL>
 __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
 {
     c.t0 = clock100();
@@ -88,11 +91,17 @@ __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
     // every workgroup's peers (same part, other ranks) sit in its own block
     // and parts 0..7 of every rank (arrival writers, completion waiters) in
     // the first, so progress never needs more than one block resident
-    const uint32_t X = (a.parts % (uint32_t)XCDS) == 0u ? (uint32_t)XCDS : 1u;
-    const uint32_t span = X * a.n_ranks;
-    const uint32_t w = blockIdx.x % span;
-    c.rank = w / X;
-    c.part = (blockIdx.x / span) * X + w % X;
+    // (the host passes X as a shift and span = X*N with its reciprocal
+    // ceil(2^32 / span), exact for every grid below 2^24 workgroups)
+    const uint32_t b = blockIdx.x;
+    const uint32_t blk = a.span == 1u ? b : __umulhi(b, a.span_magic);
+    const uint32_t w = b - blk * a.span;
+    c.rank = w >> a.xshift;
+    c.part = (blk << a.xshift) + (w & ((1u << a.xshift) - 1u));
+    // XCD-local scope is only coherent if this workgroup runs where the
+    // placement puts it: a violation is recorded (peers' polls then give up)
+    if (LOCAL && xcc_id() != c.part % (uint32_t)XCDS && threadIdx.x == 0)
+        Ctl{a.ctl}.fail(c.rank, xcc_id(), c.part, STATUS_PLACEMENT);
     c.par = a.epoch & 1u;
 }
 
@@ -160,14 +169,16 @@ __device__ __forceinline__ uint32_t arrive_off(uint32_t copy, uint32_t rank)
     return (CTL_ARRIVE + 32u * (copy * MAX_RANKS + rank)) * 4u;
 }
 
+template <bool LOCAL>
 __device__ __forceinline__ void raise_arrival(const Launch &a, const Ctx0 &c)
 {
     if (c.part < (uint32_t)XCDS && threadIdx.x == 0)
-        st4<CP_DEV>(c.flag, rsrc(a.ctl, CTL_WORDS * 4u), arrive_off(c.part, c.rank));
+        st4<Pol<LOCAL>::ST>(c.flag, rsrc(a.ctl, CTL_WORDS * 4u), arrive_off(c.part, c.rank));
 }
 
 // Every wave waits (two polls in flight) until all N arrival words of its
 // XCD's copy reach the call's flag.  Lanes 0..N-1 each watch one word.
+template <bool LOCAL>
 __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, const Ctl &ctl)
 {
     const uint32_t lane = threadIdx.x & 63u;
@@ -176,10 +187,10 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
     const __amdgpu_buffer_rsrc_t r = rsrc(a.ctl, CTL_WORDS * 4u);
     Watch w;
     w.begin(a.watchdog_ticks);
-    uint32_t v0 = need ? ld4<CP_DEV>(r, off) : c.flag, v1;
+    uint32_t v0 = need ? ld4<Pol<LOCAL>::LD>(r, off) : c.flag, v1;
     while (true) {
         compiler_fence();
-        v1 = need ? ld4<CP_DEV>(r, off) : c.flag;
+        v1 = need ? ld4<Pol<LOCAL>::LD>(r, off) : c.flag;
         if (need && (int32_t)(v0 - c.flag) >= 0)
             need = false;
         if (!wave_any(need))
@@ -187,7 +198,7 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
         if (w.expired(ctl, c.rank, lane, c.flag))
             return false;
         compiler_fence();
-        v0 = need ? ld4<CP_DEV>(r, off) : c.flag;
+        v0 = need ? ld4<Pol<LOCAL>::LD>(r, off) : c.flag;
         if (need && (int32_t)(v1 - c.flag) >= 0)
             need = false;
         if (!wave_any(need))
@@ -202,7 +213,7 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
 // in flight: while one batch is checked the next is already on its way.
 // One round of the one-shot LL kernel for lane chunk `ch` with input x.  All
 // mailboxes sit in one region [rank][parity] x ll_stride under descriptor llr.
-template <int NMAX, bool F32>
+template <int NMAX, bool F32, bool LOCAL>
 __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
                                          __amdgpu_buffer_rsrc_t llr, __amdgpu_buffer_rsrc_t o,
                                          uint32_t ch, uint32_t C, u32x2 x)
@@ -213,7 +224,7 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
     const bool active = ch < C;
     // publish (send/bcast): one copy, read by all N ranks
     if (active)
-        st16<CP_DEV>(ll_pack(x.x, x.y, c.flag), llr, lane_off + c.rank * 2u * rb);
+        st16<Pol<LOCAL>::ST>(ll_pack(x.x, x.y, c.flag), llr, lane_off + c.rank * 2u * rb);
     wait_stores();                  // first poll only after the publish is acknowledged
     // receive (recvReduce): poll every peer's unit for this chunk
     uint32_t pend = 0;
@@ -227,7 +238,7 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             if ((pend >> s) & 1u)
-                A[s] = ld16<CP_DEV>(llr, lane_off + (uint32_t)s * 2u * rb);
+                A[s] = ld16<Pol<LOCAL>::LD>(llr, lane_off + (uint32_t)s * 2u * rb);
     };
     auto check = [&](const u32x4 *A) {
 #pragma unroll
@@ -271,11 +282,11 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
     return true;
 }
 
-template <int NMAX, bool F32>
+template <int NMAX, bool F32, bool LOCAL>
 __global__ __launch_bounds__(256) void k_oneshot_ll(const Launch a)
 {
     Ctx0 c;
-    begin(a, c);
+    begin<LOCAL>(a, c);
     const uint32_t C = a.n >> 2;                    // 4-element chunks per rank
     const uint32_t step = a.parts * blockDim.x;
     const uint32_t rounds = (C + step - 1u) / step;
@@ -292,13 +303,13 @@ __global__ __launch_bounds__(256) void k_oneshot_ll(const Launch a)
     start_delay(a, c);
     // round 0 is straight-line code: its poll loads are issued back to back
     // (inside a loop the compiler's counter bookkeeping would wait before each)
-    if (!ll_round<NMAX, F32>(a, c, ctl, llr, o, ch, C, x))
+    if (!ll_round<NMAX, F32, LOCAL>(a, c, ctl, llr, o, ch, C, x))
         return;
     for (uint32_t it = 1; it < rounds; ++it) {
         wait_stores();
         ch += step;
         x = ch < C ? ld8<CP_PLAIN>(inr, ch * 8u) : u32x2{0u, 0u};
-        if (!ll_round<NMAX, F32>(a, c, ctl, llr, o, ch, C, x))
+        if (!ll_round<NMAX, F32, LOCAL>(a, c, ctl, llr, o, ch, C, x))
             return;
     }
     finish(a, c);
@@ -310,11 +321,11 @@ __global__ __launch_bounds__(256) void k_oneshot_ll(const Launch a)
 // the sentinel, reduces, and re-arms the slots it consumed.  The receipt of
 // a peer's call-k data proves the peer finished call k-1 (double buffering),
 // so the re-arm of parity k&1 always lands before the peer's call k+2 write.
-template <int NMAX, bool F32>
+template <int NMAX, bool F32, bool LOCAL>
 __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
 {
     Ctx0 c;
-    begin(a, c);
+    begin<LOCAL>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t G = a.n >> 3;
     const uint32_t bytes = a.n * 2u;
@@ -341,7 +352,7 @@ __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((uint32_t)s < N && (uint32_t)s != c.rank)
-                    st16<CP_DEV>(x, box, ch * 16u + par_off + (((uint32_t)s * N + c.rank) * 2u) * sb);
+                    st16<Pol<LOCAL>::ST>(x, box, ch * 16u + par_off + (((uint32_t)s * N + c.rank) * 2u) * sb);
         }
         uint32_t pend = 0;
 #pragma unroll
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((pend >> s) & 1u)
-                    A[s] = ld16<CP_DEV>(box, ch * 16u + par_off + ((c.rank * N + (uint32_t)s) * 2u) * sb);
+                    A[s] = ld16<Pol<LOCAL>::LD>(box, ch * 16u + par_off + ((c.rank * N + (uint32_t)s) * 2u) * sb);
         };
         auto check = [&](const u32x4 *A) {
 #pragma unroll
@@ -394,7 +405,7 @@ __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((uint32_t)s < N && (uint32_t)s != c.rank)
-                    st16<CP_DEV>(sentinel4(), box, ch * 16u + par_off + ((c.rank * N + (uint32_t)s) * 2u) * sb);
+                    st16<Pol<LOCAL>::ST>(sentinel4(), box, ch * 16u + par_off + ((c.rank * N + (uint32_t)s) * 2u) * sb);
             store8<F32>(o, ch * 8u, acc);
         }
         return true;
@@ -414,11 +425,12 @@ __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
 
 // Workgroup form: wave 0 polls, the workgroup barrier releases the others
 // (a quarter of the polling traffic of 4-wave workgroups).
+template <bool LOCAL>
 __device__ __forceinline__ bool wait_arrivals_wg(const Launch &a, const Ctx0 &c, const Ctl &ctl)
 {
     __shared__ uint32_t ok;
     if (threadIdx.x < 64u)
-        ok = wait_arrivals(a, c, ctl) ? 1u : 0u;
+        ok = wait_arrivals<LOCAL>(a, c, ctl) ? 1u : 0u;
     __syncthreads();
     return ok != 0u;
 }
@@ -429,11 +441,11 @@ __device__ __forceinline__ bool wait_arrivals_wg(const Launch &a, const Ctx0 &c,
 // unchanged until call k has completed on every rank (the application-level
 // A/B double buffering of the SiFAR page, "SiFAR：无同步All-Reduce技术突破低
 // 延迟LLM推理瓶颈", technique one).
-template <int NMAX, bool F32>
+template <int NMAX, bool F32, bool LOCAL>
 __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
 {
     Ctx0 c;
-    begin(a, c);
+    begin<LOCAL>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t G = a.n >> 3;
     const uint32_t step = a.parts * blockDim.x;
@@ -441,8 +453,8 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     start_delay(a, c);
-    raise_arrival(a, c);
-    if (!wait_arrivals(a, c, ctl))
+    raise_arrival<LOCAL>(a, c);
+    if (!wait_arrivals<LOCAL>(a, c, ctl))
         return;
     __amdgpu_buffer_rsrc_t src[NMAX];
 #pragma unroll
@@ -479,11 +491,11 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
 // slice of that rank's output is known to be complete.
 // Moves exactly the algorithmic bytes: N inputs read once, N outputs written
 // once.
-template <int NMAX, bool F32>
+template <int NMAX, bool F32, bool LOCAL>
 __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
 {
     Ctx0 c;
-    begin(a, c);
+    begin<LOCAL>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t q = c.rank;
     const uint32_t L = a.slice;
@@ -494,8 +506,8 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     start_delay(a, c);
-    raise_arrival(a, c);
-    if (!wait_arrivals_wg(a, c, ctl))
+    raise_arrival<LOCAL>(a, c);
+    if (!wait_arrivals_wg<LOCAL>(a, c, ctl))
         return;
     __amdgpu_buffer_rsrc_t src[NMAX];
 #pragma unroll
@@ -537,7 +549,7 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     __syncthreads();
     const __amdgpu_buffer_rsrc_t dn = rsrc(a.done, MAX_RANKS * DONE_STRIDE * 4u);
     if (threadIdx.x == 0)
-        st4<CP_DEV>(c.flag, dn, (q * DONE_STRIDE + c.part) * 4u);
+        st4<Pol<LOCAL>::ST>(c.flag, dn, (q * DONE_STRIDE + c.part) * 4u);
     if (c.part < (uint32_t)XCDS && threadIdx.x < 64u) {
         const uint32_t lane = threadIdx.x;
         const uint32_t x = c.part;
@@ -550,7 +562,7 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
             // each lane walks its share of the writers, skipping those seen
             while (i < total) {
                 const uint32_t s = i / per, p = x + XCDS * (i % per);
-                const uint32_t v = ld4<CP_DEV>(dn, (s * DONE_STRIDE + p) * 4u);
+                const uint32_t v = ld4<Pol<LOCAL>::LD>(dn, (s * DONE_STRIDE + p) * 4u);
                 if ((int32_t)(v - c.flag) < 0)
                     break;
                 i += 64u;
@@ -585,22 +597,24 @@ __device__ __forceinline__ u32x4 ld_elems(__amdgpu_buffer_rsrc_t r, uint32_t e, 
     return ld16<CP>(r, e * 2u);
 }
 
+template <bool LOCAL>
 __device__ __forceinline__ void l128_store_payload(__amdgpu_buffer_rsrc_t dst, uint32_t off,
                                                    bool half, u32x4 payload)
 {
     if (half) {
         u32x2 p; p.x = payload.x; p.y = payload.y;
-        st8<CP_DEV>(p, dst, off);
+        st8<Pol<LOCAL>::ST>(p, dst, off);
     } else {
-        st16<CP_DEV>(payload, dst, off);
+        st16<Pol<LOCAL>::ST>(payload, dst, off);
     }
 }
 
+template <bool LOCAL>
 __device__ __forceinline__ void l128_store_flag(__amdgpu_buffer_rsrc_t dst, uint32_t off,
                                                 uint32_t flag)
 {
     u32x2 f; f.x = flag; f.y = ~flag;
-    st8<CP_DEV>(f, dst, off + 8u);
+    st8<Pol<LOCAL>::ST>(f, dst, off + 8u);
 }
 
 __device__ __forceinline__ bool l128_flag_ok(u32x2 f, uint32_t flag)
@@ -614,7 +628,7 @@ __device__ __forceinline__ bool l128_flag_ok(u32x2 f, uint32_t flag)
 // number of valid elements of source s in group index space; a line is
 // polled only if one of its elements is valid.  skip names a source the
 // caller holds already (or NMAX).  Returns false on watchdog expiry.
-template <int NMAX, int GB = GroupsPerBatch<NMAX>::value>
+template <int NMAX, bool LOCAL, int GB = GroupsPerBatch<NMAX>::value>
 __device__ __forceinline__ bool l128_receive(__amdgpu_buffer_rsrc_t reg, uint32_t rb, uint32_t par,
                                              uint32_t N, uint32_t skip, const uint32_t *g,
                                              uint32_t gvalid, uint32_t lane, const L128Lane &ln,
@@ -636,7 +650,7 @@ __device__ __forceinline__ bool l128_receive(__amdgpu_buffer_rsrc_t reg, uint32_
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             if ((uint32_t)s < N && (uint32_t)s != skip && ln.half && line_first < lim[s]) {
-                F[j][s] = ld8<CP_DEV>(reg, off(j, s) + 8u);
+                F[j][s] = ld8<Pol<LOCAL>::LD>(reg, off(j, s) + 8u);
                 pend[j] |= 1u << s;
             }
     }
@@ -663,7 +677,7 @@ __device__ __forceinline__ bool l128_receive(__amdgpu_buffer_rsrc_t reg, uint32_
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((pend[j] >> s) & 1u)
-                    F[j][s] = ld8<CP_DEV>(reg, off(j, s) + 8u);
+                    F[j][s] = ld8<Pol<LOCAL>::LD>(reg, off(j, s) + 8u);
     }
     // every needed line is complete: load the payloads
     compiler_fence();
@@ -676,10 +690,10 @@ __device__ __forceinline__ bool l128_receive(__amdgpu_buffer_rsrc_t reg, uint32_
         for (int s = 0; s < NMAX; ++s) {
             if ((uint32_t)s < N && (uint32_t)s != skip && e < lim[s]) {
                 if (ln.half) {
-                    const u32x2 p = ld8<CP_DEV>(reg, off(j, s));
+                    const u32x2 p = ld8<Pol<LOCAL>::LD>(reg, off(j, s));
                     V[j][s].x = p.x; V[j][s].y = p.y; V[j][s].z = 0u; V[j][s].w = 0u;
                 } else {
-                    V[j][s] = ld16<CP_DEV>(reg, off(j, s));
+                    V[j][s] = ld16<Pol<LOCAL>::LD>(reg, off(j, s));
                 }
             }
         }
@@ -698,12 +712,12 @@ __device__ __forceinline__ void store_lane(__amdgpu_buffer_rsrc_t o, uint32_t e,
 // Rank r publishes its whole input as line groups; a wave owns the groups
 // g0, g0 + gstep, ... and handles them GB at a time: publish all payloads,
 // one acknowledgement wait, all flags; then receive and reduce.
-template <int NMAX, bool F32>
+template <int NMAX, bool F32, bool LOCAL>
 __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 {
     constexpr int GB = GroupsPerBatch<NMAX>::value;
     Ctx0 c;
-    begin(a, c);
+    begin<LOCAL>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
@@ -739,14 +753,14 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 #pragma unroll
         for (int j = 0; j < GB; ++j)
             if ((gvalid >> j) & 1u)
-                l128_store_payload(reg, mine + g[j] * L128_BYTES + lane * 16u, ln.half, x[j]);
+                l128_store_payload<LOCAL>(reg, mine + g[j] * L128_BYTES + lane * 16u, ln.half, x[j]);
         wait_stores();
 #pragma unroll
         for (int j = 0; j < GB; ++j)
             if (((gvalid >> j) & 1u) && ln.half)
-                l128_store_flag(reg, mine + g[j] * L128_BYTES + lane * 16u, c.flag);
+                l128_store_flag<LOCAL>(reg, mine + g[j] * L128_BYTES + lane * 16u, c.flag);
         u32x4 V[GB][NMAX];
-        if (!l128_receive<NMAX>(reg, rb, c.par, N, c.rank, g, gvalid, lane, ln, lim, c.flag, ctl,
+        if (!l128_receive<NMAX, LOCAL>(reg, rb, c.par, N, c.rank, g, gvalid, lane, ln, lim, c.flag, ctl,
                                 c.rank, a.watchdog_ticks, V))
             return;
 #pragma unroll
@@ -773,12 +787,12 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 // bf16 result as line groups.  All-gather: rank q receives every slice's
 // groups (its own from registers) and writes them to out[q].  Groups are
 // handled GB at a time per wave as in the one-shot kernel.
-template <int NMAX, bool F32>
+template <int NMAX, bool F32, bool LOCAL>
 __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 {
     constexpr int GB = GroupsPerBatch<NMAX>::value;
     Ctx0 c;
-    begin(a, c);
+    begin<LOCAL>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t q = c.rank;
     const uint32_t L = a.slice;
@@ -791,8 +805,8 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
     const Ctl ctl{a.ctl};
     const L128Lane ln = l128_lane(lane);
     start_delay(a, c);
-    raise_arrival(a, c);
-    if (!wait_arrivals(a, c, ctl))
+    raise_arrival<LOCAL>(a, c);
+    if (!wait_arrivals<LOCAL>(a, c, ctl))
         return;
     uint32_t lim[NMAX];
     __amdgpu_buffer_rsrc_t inp[NMAX];
@@ -850,15 +864,15 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 #pragma unroll
         for (int j = 0; j < GB; ++j)
             if ((gvalid >> j) & 1u)
-                l128_store_payload(reg, mine + g[j] * L128_BYTES + lane * 16u, ln.half, red[j]);
+                l128_store_payload<LOCAL>(reg, mine + g[j] * L128_BYTES + lane * 16u, ln.half, red[j]);
         wait_stores();
 #pragma unroll
         for (int j = 0; j < GB; ++j)
             if (((gvalid >> j) & 1u) && ln.half)
-                l128_store_flag(reg, mine + g[j] * L128_BYTES + lane * 16u, c.flag);
+                l128_store_flag<LOCAL>(reg, mine + g[j] * L128_BYTES + lane * 16u, c.flag);
         // ---- all-gather of the same groups
         u32x4 V[GB][NMAX];
-        if (!l128_receive<NMAX>(reg, rb, c.par, N, q, g, gvalid, lane, ln, lim, c.flag, ctl, q,
+        if (!l128_receive<NMAX, LOCAL>(reg, rb, c.par, N, q, g, gvalid, lane, ln, lim, c.flag, ctl, q,
                                 a.watchdog_ticks, V))
             return;
 #pragma unroll
@@ -889,7 +903,7 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 // All-gather: rank q pushes its reduced chunk into AG[r][q] of every peer r
 // and writes it to out[q]; every rank polls AG[q][*], copies to out, re-arms.
 // Inbox regions [recv][send][parity] x s2_stride, one descriptor each.
-template <int NMAX, bool F32>
+template <int NMAX, bool F32, bool LOCAL>
 __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
                                          __amdgpu_buffer_rsrc_t inq, __amdgpu_buffer_rsrc_t rsr,
                                          __amdgpu_buffer_rsrc_t agr, __amdgpu_buffer_rsrc_t oa,
@@ -922,7 +936,7 @@ __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const C
     for (int s = 0; s < NMAX; ++s) {
         if ((uint32_t)s < N && e < slice_len((uint32_t)s)) {
             if ((uint32_t)s == q) own = X[s];
-            else st16<CP_DEV>(X[s], rsr, box((uint32_t)s, q));
+            else st16<Pol<LOCAL>::ST>(X[s], rsr, box((uint32_t)s, q));
         }
     }
     // ---- receive my slice from everyone, reduce, re-arm
@@ -937,7 +951,7 @@ __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const C
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             if ((pend >> s) & 1u)
-                A[s] = ld16<CP_DEV>(reg, box(q, (uint32_t)s));
+                A[s] = ld16<Pol<LOCAL>::LD>(reg, box(q, (uint32_t)s));
     };
     auto check = [&](const u32x4 *A) {
 #pragma unroll
@@ -976,7 +990,7 @@ __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const C
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             if ((uint32_t)s < N && (uint32_t)s != q)
-                st16<CP_DEV>(sentinel4(), rsr, box(q, (uint32_t)s));
+                st16<Pol<LOCAL>::ST>(sentinel4(), rsr, box(q, (uint32_t)s));
         if constexpr (F32) {
             // debug path: the owner writes its slice's accumulators to every copy
             for (uint32_t r = 0; r < N; ++r)
@@ -986,7 +1000,7 @@ __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const C
 #pragma unroll
             for (int r = 0; r < NMAX; ++r)
                 if ((uint32_t)r < N && (uint32_t)r != q)
-                    st16<CP_DEV>(red, agr, box((uint32_t)r, q));
+                    st16<Pol<LOCAL>::ST>(red, agr, box((uint32_t)r, q));
             st16<CP_PLAIN>(red, oa, (q * a.n + q * L + e) * esz);
         }
     }
@@ -1018,16 +1032,16 @@ __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const C
     for (int s = 0; s < NMAX; ++s)
         if ((uint32_t)s < N && (uint32_t)s != q && e < slice_len((uint32_t)s)) {
             st16<CP_PLAIN>(V[s], oa, (q * a.n + (uint32_t)s * L + e) * esz);
-            st16<CP_DEV>(sentinel4(), agr, box(q, (uint32_t)s));
+            st16<Pol<LOCAL>::ST>(sentinel4(), agr, box(q, (uint32_t)s));
         }
     return true;
 }
 
-template <int NMAX, bool F32>
+template <int NMAX, bool F32, bool LOCAL>
 __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
 {
     Ctx0 c;
-    begin(a, c);
+    begin<LOCAL>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t G = a.slice >> 3;                // chunks per slice
     const uint32_t step = a.parts * blockDim.x;
@@ -1040,12 +1054,12 @@ __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
     const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
     uint32_t ch = c.part * blockDim.x + threadIdx.x;
     // round 0 straight-line (see the one-shot LL kernel), later rounds looped
-    if (!ts_round<NMAX, F32>(a, c, ctl, inq, rsr, agr, oa, ch, true))
+    if (!ts_round<NMAX, F32, LOCAL>(a, c, ctl, inq, rsr, agr, oa, ch, true))
         return;
     for (uint32_t it = 1; it < rounds; ++it) {
         wait_stores();
         ch += step;
-        if (!ts_round<NMAX, F32>(a, c, ctl, inq, rsr, agr, oa, ch, false))
+        if (!ts_round<NMAX, F32, LOCAL>(a, c, ctl, inq, rsr, agr, oa, ch, false))
             return;
     }
     finish(a, c);
@@ -1096,37 +1110,53 @@ __global__ __launch_bounds__(256) void k_fill(uint32_t *p, size_t words, uint32_
         p[i] = value;
 }
 
+// Records the XCD of every workgroup: out[b] = XCC_ID of workgroup b.
+__global__ __launch_bounds__(256) void k_xcc_map(uint32_t *out, uint32_t n)
+{
+    if (threadIdx.x == 0 && blockIdx.x < n)
+        out[blockIdx.x] = xcc_id();
+}
+
 // ------------------------------------------------------------ dispatch
-template <int NMAX, bool F32>
+template <int NMAX, bool F32, bool LOCAL>
 static const void *pick(int kind)
 {
     switch (kind) {
-    case K_ONESHOT_LL: return (const void *)k_oneshot_ll<NMAX, F32>;
-    case K_ONESHOT_SENTINEL: return (const void *)k_oneshot_sentinel<NMAX, F32>;
-    case K_ONESHOT_DIRECT: return (const void *)k_oneshot_direct<NMAX, F32>;
-    case K_ONESHOT_LL128: return (const void *)k_oneshot_ll128<NMAX, F32>;
-    case K_TWOSHOT_LL128: return (const void *)k_twoshot_ll128<NMAX, F32>;
-    case K_TWOSHOT_SENTINEL: return (const void *)k_twoshot_sentinel<NMAX, F32>;
-    case K_TWOSHOT_DIRECT: return (const void *)k_twoshot_direct<NMAX, F32>;
+    case K_ONESHOT_LL: return (const void *)k_oneshot_ll<NMAX, F32, LOCAL>;
+    case K_ONESHOT_SENTINEL: return (const void *)k_oneshot_sentinel<NMAX, F32, LOCAL>;
+    case K_ONESHOT_DIRECT: return (const void *)k_oneshot_direct<NMAX, F32, LOCAL>;
+    case K_ONESHOT_LL128: return (const void *)k_oneshot_ll128<NMAX, F32, LOCAL>;
+    case K_TWOSHOT_LL128: return (const void *)k_twoshot_ll128<NMAX, F32, LOCAL>;
+    case K_TWOSHOT_SENTINEL: return (const void *)k_twoshot_sentinel<NMAX, F32, LOCAL>;
+    case K_TWOSHOT_DIRECT: return (const void *)k_twoshot_direct<NMAX, F32, LOCAL>;
     default: return nullptr;
     }
 }
 
-const void *kernel_for(int kind, int n_ranks, bool f32)
+// The fp32 debug kernels always use device scope.
+const void *kernel_for(int kind, int n_ranks, bool f32, bool local)
 {
+    if (f32)
+        return n_ranks <= 8 ? pick<8, true, false>(kind) : pick<16, true, false>(kind);
     if (n_ranks <= 8)
-        return f32 ? pick<8, true>(kind) : pick<8, false>(kind);
-    return f32 ? pick<16, true>(kind) : pick<16, false>(kind);
+        return local ? pick<8, false, true>(kind) : pick<8, false, false>(kind);
+    return local ? pick<16, false, true>(kind) : pick<16, false, false>(kind);
 }
 
-hipError_t launch_ar(int kind, bool f32, const Launch &a, uint32_t grid, uint32_t threads,
-                     hipStream_t stream)
+hipError_t launch_ar(int kind, bool f32, bool local, const Launch &a, uint32_t grid,
+                     uint32_t threads, hipStream_t stream)
 {
-    const void *fn = kernel_for(kind, (int)a.n_ranks, f32);
+    const void *fn = kernel_for(kind, (int)a.n_ranks, f32, local);
     if (fn == nullptr)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&a};
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
+}
+
+hipError_t launch_xcc_map(uint32_t *out, uint32_t grid, uint32_t threads, hipStream_t stream)
+{
+    hipLaunchKernelGGL(k_xcc_map, dim3(grid), dim3(threads), 0, stream, out, grid);
+    return hipGetLastError();
 }
 
 hipError_t launch_step_end(uint32_t *ctl, uint32_t calls, char *ll, size_t ll_bytes, char *l128,

@@ -31,8 +31,20 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // gfx950 buffer-instruction cache-policy bits
 constexpr int CP_PLAIN = 0;
+constexpr int CP_WG = 1;            // sc0: workgroup scope (coherent in the XCD's L2)
 constexpr int CP_NT = 2;
 constexpr int CP_DEV = 16;          // sc1: device-scope coherent
+
+// Policies of the staging and flag traffic.  Device scope is coherent
+// wherever the two sides run.  XCD-local scope (LOCAL) requires writer and
+// reader on one XCD -- which the part-to-XCD placement provides -- and then
+// serves both from that XCD's L2: stores at workgroup scope, polls streaming
+// at workgroup scope (they skip the CU's L1, so a repeated poll cannot hit a
+// stale L1 line).  Measured on 8 ranks x 16 KiB: about 0.2-0.5 us less per call.
+template <bool LOCAL> struct Pol {
+    static constexpr int ST = LOCAL ? CP_WG : CP_DEV;
+    static constexpr int LD = LOCAL ? (CP_NT | CP_WG) : CP_DEV;
+};
 
 constexpr int MAX_RANKS = 16;
 constexpr uint32_t SENT_WORD = 0xFFFFFFFFu;   // two sentinel bf16 (0xFFFF)
@@ -48,8 +60,9 @@ constexpr int XCDS = 8;
 constexpr int CTL_ARRIVE = 64;
 constexpr int CTL_WORDS = CTL_ARRIVE + 32 * MAX_RANKS * XCDS;
 constexpr uint32_t STATUS_TIMEOUT = 6;
-constexpr uint32_t DONE_STRIDE = 8192;
-constexpr uint32_t TS_SUB = 64;          // timestamp sub-slots per call   // completion flags per rank (>= workgroups per rank)
+constexpr uint32_t STATUS_PLACEMENT = 7;  // XCD-local launch on an unexpected XCD
+constexpr uint32_t DONE_STRIDE = 8192;    // completion flags per rank (>= workgroups per rank)
+constexpr uint32_t TS_SUB = 64;           // timestamp sub-slots per call
 
 // LL128 line group: 8 lines of 128 B = one wave-wide 16 B access; 60 chunks
 // of 8 elements carried as 56 full lanes + 8 half lanes (the lane at
@@ -76,6 +89,9 @@ struct Launch {
     uint32_t parts;               // workgroups per rank
     uint32_t slice;               // two-shot slice length (multiple of 8)
     uint32_t watchdog_ticks;
+    uint32_t span;                // workgroups per placement block: N << xshift
+    uint32_t span_magic;          // ceil(2^32 / span) (span > 1)
+    uint32_t xshift;              // log2 of parts per rank in a block (3, or 0)
     uint32_t ts_slots;
     uint32_t delay_rows;
 };
@@ -129,6 +145,12 @@ __device__ __forceinline__ void wait_stores()
 }
 
 __device__ __forceinline__ uint64_t clock100() { return __builtin_amdgcn_s_memrealtime(); }
+
+// index of the XCD this wave runs on (hardware register XCC_ID, bits 3:0)
+__device__ __forceinline__ uint32_t xcc_id()
+{
+    return (uint32_t)__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15u;
+}
 
 __device__ __forceinline__ bool wave_any(bool p)
 {
@@ -238,10 +260,11 @@ struct Ctl {
     {
         return __hip_atomic_load(p + CTL_STATUS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __device__ __forceinline__ void fail(uint32_t rank, uint32_t src, uint32_t flag) const
+    __device__ __forceinline__ void fail(uint32_t rank, uint32_t src, uint32_t flag,
+                                         uint32_t code = STATUS_TIMEOUT) const
     {
         uint32_t expected = 0;
-        if (__hip_atomic_compare_exchange_strong(p + CTL_STATUS, &expected, STATUS_TIMEOUT,
+        if (__hip_atomic_compare_exchange_strong(p + CTL_STATUS, &expected, code,
                                                  __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT)) {
             __hip_atomic_store(p + CTL_STATUS + 1, rank, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
