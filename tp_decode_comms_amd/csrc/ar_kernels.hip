@@ -162,11 +162,13 @@ __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t o, uint32_t elem, 
 // dependence on any load.  Flags grow monotonically between wraps, so a
 // reader needs word >= f (wrap-safe compare).  The word is replicated per
 // XCD: parts x < 8 of rank s write copy x, and part p reads copy p % 8,
-// which the same-XCD part of every peer wrote.  Only kinds that read peers'
-// data in place (DIRECT) use arrivals.
+// which the same-XCD part of every peer wrote.  The N words of one copy
+// share one 128-byte line, so a reader polls a single line (polls of lines
+// written during the launch are costly for the L2).  Only kinds that read
+// peers' data in place (DIRECT) use arrivals.
 __device__ __forceinline__ uint32_t arrive_off(uint32_t copy, uint32_t rank)
 {
-    return (CTL_ARRIVE + 32u * (copy * MAX_RANKS + rank)) * 4u;
+    return (CTL_ARRIVE + 32u * copy + rank) * 4u;
 }
 
 template <bool LOCAL>
@@ -540,29 +542,36 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
                     store8<F32, CP_NT | CP_DEV>(oa, (uint32_t)r * a.n + lo + ch2 * 8u, acc2);
             }
     }
-    // completion: my stores are at the coherence point, then my flag.  Part
-    // x < 8 of each rank waits for the flags of the writers (s, p) with
-    // p % 8 == x, which run on its own XCD; together the up-to-8 waiters of
-    // rank q see every writer, which proves that every slice of q's output
-    // is complete before q's workgroups exit.
+    // completion: my stores are at the coherence point, then my flag.  The
+    // flags of the writers on one XCD (parts p with p % 8 == x) are packed
+    // together: writer (s, p) owns word x*N*P8 + s*P8 + p/8, P8 = ceil(parts/8).
+    // One waiter per rank and XCD -- a part of the last block, which streams
+    // last, so polling (reads of freshly written lines, which slow the other
+    // writers' streams) is short -- waits for all flags of its XCD; together
+    // the waiters of rank q see every writer, which proves that every slice
+    // of q's output is complete before q's workgroups exit.
     wait_stores();
     __syncthreads();
+    const uint32_t P8 = (a.parts + XCDS - 1u) / XCDS;
     const __amdgpu_buffer_rsrc_t dn = rsrc(a.done, MAX_RANKS * DONE_STRIDE * 4u);
     if (threadIdx.x == 0)
-        st4<Pol<LOCAL>::ST>(c.flag, dn, (q * DONE_STRIDE + c.part) * 4u);
-    if (c.part < (uint32_t)XCDS && threadIdx.x < 64u) {
+        st4<Pol<LOCAL>::ST>(c.flag, dn, ((c.part % XCDS) * N * P8 + q * P8 + c.part / XCDS) * 4u);
+    const bool waiter = a.parts % (uint32_t)XCDS == 0u ? c.part >= a.parts - (uint32_t)XCDS
+                                                       : c.part < (uint32_t)XCDS;
+    if (waiter && threadIdx.x < 64u) {
         const uint32_t lane = threadIdx.x;
-        const uint32_t x = c.part;
+        const uint32_t x = c.part % XCDS;
         const uint32_t per = (a.parts - x + XCDS - 1u) / XCDS;   // parts x, x+8, ...
         const uint32_t total = N * per;                // writers this waiter covers
+        const uint32_t base = x * N * P8;
         Watch w;
         w.begin(a.watchdog_ticks);
         uint32_t i = lane;                             // next writer this lane checks
         while (true) {
             // each lane walks its share of the writers, skipping those seen
             while (i < total) {
-                const uint32_t s = i / per, p = x + XCDS * (i % per);
-                const uint32_t v = ld4<Pol<LOCAL>::LD>(dn, (s * DONE_STRIDE + p) * 4u);
+                const uint32_t s = i / per, jj = i % per;
+                const uint32_t v = ld4<Pol<LOCAL>::LD>(dn, (base + s * P8 + jj) * 4u);
                 if ((int32_t)(v - c.flag) < 0)
                     break;
                 i += 64u;
@@ -1088,8 +1097,8 @@ __global__ __launch_bounds__(256) void k_step_end(uint32_t *ctl, uint32_t calls,
         w = (uint32_t *)l128;
         for (size_t i = threadIdx.x; i < l128_bytes / 4; i += blockDim.x) w[i] = 0u;
         for (size_t i = threadIdx.x; i < (size_t)MAX_RANKS * DONE_STRIDE; i += blockDim.x) done[i] = 0u;
-        for (uint32_t i = threadIdx.x; i < (uint32_t)(MAX_RANKS * XCDS); i += blockDim.x)
-            __hip_atomic_store(ctl + CTL_ARRIVE + 32u * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (uint32_t i = threadIdx.x; i < (uint32_t)(32 * XCDS); i += blockDim.x)
+            __hip_atomic_store(ctl + CTL_ARRIVE + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __threadfence();
     }
     __syncthreads();

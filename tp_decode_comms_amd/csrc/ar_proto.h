@@ -56,12 +56,13 @@ constexpr int CTL_STATUS = 32;      // {code, rank, source, flag}
 // with `parts` a multiple of XCDS part p of every rank runs on XCD p % XCDS.
 constexpr int XCDS = 8;
 // arrival flag of rank r, copy x (read and written by workgroups of parts
-// p = x mod XCDS) at CTL_ARRIVE + 32*(x*MAX_RANKS + r), one 128-byte line each
+// p = x mod XCDS) at word CTL_ARRIVE + 32*x + r: one 128-byte line per copy
 constexpr int CTL_ARRIVE = 64;
-constexpr int CTL_WORDS = CTL_ARRIVE + 32 * MAX_RANKS * XCDS;
+constexpr int CTL_WORDS = CTL_ARRIVE + 32 * XCDS;
+static_assert(MAX_RANKS <= 32, "one arrival line holds every rank of a copy");
 constexpr uint32_t STATUS_TIMEOUT = 6;
 constexpr uint32_t STATUS_PLACEMENT = 7;  // XCD-local launch on an unexpected XCD
-constexpr uint32_t DONE_STRIDE = 8192;    // completion flags per rank (>= workgroups per rank)
+constexpr uint32_t DONE_STRIDE = 8192;    // completion-flag words per rank (>= workgroups per rank)
 constexpr uint32_t TS_SUB = 64;           // timestamp sub-slots per call
 
 // LL128 line group: 8 lines of 128 B = one wave-wide 16 B access; 60 chunks
@@ -81,7 +82,7 @@ struct Launch {
     uint32_t *ctl;                // control block (CTL_WORDS)
     uint64_t *ts;                 // timestamps [slots][2] or null
     const uint32_t *delays;       // start delays [rows][N] ns or null
-    uint32_t *done;               // two-shot DIRECT completion flags [rank][DONE_STRIDE]
+    uint32_t *done;               // two-shot DIRECT completion flags (MAX_RANKS*DONE_STRIDE words)
     uint32_t ll_stride, l128_stride, s1_stride, s2_stride;
     uint32_t n;                   // elements per rank
     uint32_t n_ranks;
