@@ -146,7 +146,9 @@ def graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays=None,
                     for j in range(nbuf)])
     res = {"event_us_per_call": summary(per_replay_ms * 1000.0 / calls),
            "event_ms_per_replay": summary(per_replay_ms),
-           "mismatches": bad, "status": list(status)}
+           "mismatches": bad, "status": list(status),
+           "xcd_local_scope": bool(ar.query(8, wl.n)),
+           "placement_verified": bool(ar.query(9, 0))}
     del g
     if instrumented:
         slots = calls * replays
@@ -203,6 +205,7 @@ def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label):
     ar.init(wl.N, wl.n)
     ar.set_options(algo, proto)
     grid, threads = ar.query(4, wl.n), ar.query(5, wl.n)
+    local = bool(ar.query(8, wl.n))
     stream = torch.cuda.current_stream()
     epoch = 0
 
@@ -228,7 +231,7 @@ def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label):
     return {
         "workload": "8 ranks x [256x8192] bf16 (4 MiB/rank), U(-1,1), %s, 8 rotating buffer "
                     "sets (footprint %d MiB)" % (label, (2 * nsets * wl.N * 2 * wl.n) >> 20),
-        "algo": label, "grid": grid, "threads": threads,
+        "algo": label, "grid": grid, "threads": threads, "xcd_local_scope": local,
         "us_per_call": summary(us),
         "b_alg_bytes": wl.b_alg,
         "gbps_p50": wl.b_alg / (np.percentile(us, 50) * 1e-6) / 1e9,

@@ -30,11 +30,11 @@
  *
  * Emulation.  On one GPU the N ranks are disjoint sets of workgroups of one
  * kernel launch; they exchange data only through staging buffers and flag
- * words in device memory.  Part p of every rank's work runs on XCD p % 8
- * (the hardware dispatches workgroups to the 8 XCDs round-robin), so one
- * part's exchange stays inside one XCD's L2.  Staging and flag accesses are
- * device-scope coherent, or -- once ar_init has verified the placement --
- * XCD-local (see ar_set_scope).
+ * words in device memory.  Part p of every rank's work runs on one XCD
+ * (the hardware deals workgroups to the 8 XCDs round-robin), so one part's
+ * exchange stays inside one XCD's L2.  Staging and flag accesses are
+ * device-scope coherent, or -- once ar_init has verified the round-robin
+ * dispatch -- XCD-local (see ar_set_scope).
  *
  * Conventions for every entry point:
  *   - return value: AR_OK (0) or a negative ar_status code; nothing aborts;
@@ -60,9 +60,7 @@ enum ar_status {
     AR_ERR_STATE = -3,      /* already initialised / wrong call order */
     AR_ERR_OOM = -4,        /* device allocation failed */
     AR_ERR_HIP = -5,        /* a HIP runtime call failed (see ar_last_hip_error) */
-    AR_ERR_TIMEOUT = -6,    /* a device poll exceeded the watchdog (ar_get_status) */
-    AR_ERR_PLACEMENT = -7   /* an XCD-local launch ran a workgroup on an unexpected
-                               XCD (ar_get_status); use AR_SCOPE_DEVICE */
+    AR_ERR_TIMEOUT = -6     /* a device poll exceeded the watchdog (ar_get_status) */
 };
 
 enum ar_scope {
@@ -165,11 +163,12 @@ int ar_set_launch(int wgs_per_rank, int threads);
  * (enum ar_scope; default AR_SCOPE_AUTO).  XCD-local scope serves every
  * exchange from the L2 of the XCD its writer and reader share: stores at
  * workgroup scope and streaming workgroup-scope polls instead of
- * device-scope accesses.  It relies on the round-robin placement, which
- * ar_init checks with a probe launch (ar_query key 9); every workgroup of an
- * XCD-local launch also checks its own XCD and, on a mismatch, records
- * AR_ERR_PLACEMENT, which makes the peers' polls give up.  The fp32 debug
- * path always uses device scope.  Returns AR_ERR_INVALID for other values.
+ * device-scope accesses.  Each workgroup of such a launch takes the low
+ * bits of its part index from the XCD it runs on, which keeps the exchanges
+ * XCD-local whichever XCD the round-robin dispatch starts from; ar_init
+ * checks the round-robin order with probe launches (ar_query key 9) and
+ * leaves the scope off if it does not hold.  The fp32 debug path always uses
+ * device scope.  Returns AR_ERR_INVALID for other values.
  */
 int ar_set_scope(int scope);
 
@@ -214,10 +213,9 @@ int ar_set_timestamps(uint64_t *dev_ts, size_t slots);
 
 /*
  * ar_get_status -- copy the device status record {code, rank, source, flag}
- * into out[4] (synchronises the device first).  code is 0, 6 (a watchdog
- * fired: rank that gave up, source it waited for, call flag) or 7 (XCD-local
- * placement violated: rank, XCD it ran on, part).  Returns AR_OK,
- * AR_ERR_TIMEOUT or AR_ERR_PLACEMENT accordingly.
+ * into out[4] (synchronises the device first).  code is 0 or 6 (a watchdog
+ * fired: rank that gave up, source it waited for, call flag).  Returns
+ * AR_ERR_TIMEOUT if a watchdog fired, else AR_OK.
  */
 int ar_get_status(uint32_t out[4]);
 

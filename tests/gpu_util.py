@@ -75,7 +75,7 @@ def assert_bits_equal(got, want, what=""):
 def check_status_clean():
     import tp_decode_comms_amd as ar
     st = ar.get_status()
-    assert st[0] == 0, "device status not clean (6 watchdog, 7 placement): %r" % (st,)
+    assert st[0] == 0, "watchdog fired: %r" % (st,)
 
 
 __all__ = ["synth", "oracle"]

@@ -17,7 +17,6 @@ AR_ERR_STATE = -3
 AR_ERR_OOM = -4
 AR_ERR_HIP = -5
 AR_ERR_TIMEOUT = -6
-AR_ERR_PLACEMENT = -7
 AR_SCOPE_AUTO, AR_SCOPE_DEVICE = 0, 1
 
 AR_ALGO_AUTO, AR_ALGO_ONESHOT, AR_ALGO_TWOSHOT = 0, 1, 2
@@ -173,7 +172,7 @@ def get_status():
     """Returns (code, rank, source, flag) of the device status record."""
     buf = (_c_u32 * 4)()
     rc = lib().ar_get_status(buf)
-    if rc not in (AR_OK, AR_ERR_TIMEOUT, AR_ERR_PLACEMENT):
+    if rc not in (AR_OK, AR_ERR_TIMEOUT):
         raise ArError("ar_get_status", rc)
     return tuple(int(x) for x in buf)
 

@@ -284,8 +284,9 @@ int check_call(const void *const *rank_bufs, const void *out, size_t out_elem_by
     return AR_OK;
 }
 
-// Checks that workgroup b of a launch runs on XCD b % 8 for grids of both
-// workgroup sizes in use; the XCD-local scope is only enabled if it does.
+// Checks that a launch's workgroups are dealt to the 8 XCDs round-robin:
+// workgroup b on XCD (b + o) % 8 for one offset o per launch, for grids of
+// both workgroup sizes in use.  The XCD-local scope is only enabled if so.
 hipError_t verify_placement(bool *ok)
 {
     *ok = false;
@@ -301,8 +302,18 @@ hipError_t verify_placement(bool *ok)
             (e = ar::launch_xcc_map(d, grid, threads, 0)) != hipSuccess ||
             (e = hipMemcpy(h.data(), d, grid * 4, hipMemcpyDeviceToHost)) != hipSuccess)
             break;
+        uint32_t bad = 0, first = grid;
+        const uint32_t o = h[0] % ar::XCDS;
         for (uint32_t b = 0; b < grid; ++b)
-            good = good && h[b] == b % ar::XCDS;
+            if (h[b] != (b + o) % ar::XCDS) {
+                ++bad;
+                if (first == grid) first = b;
+            }
+        if (bad && debug_enabled())
+            fprintf(stderr, "[ar] placement check (%u threads): %u of %u workgroups off the "
+                    "round-robin order (offset %u), first b=%u on XCD %u\n", threads, bad, grid, o,
+                    first, h[first]);
+        good = good && bad == 0;
     }
     hipError_t ef = hipFree(d);
     if (e == hipSuccess)
@@ -541,9 +552,7 @@ int ar_get_status(uint32_t out[4])
     e = hipMemcpy(out, g.ctl + ar::CTL_STATUS, 16, hipMemcpyDeviceToHost);
     if (e != hipSuccess)
         return hip_fail(e);
-    if (out[0] == ar::STATUS_TIMEOUT)
-        return AR_ERR_TIMEOUT;
-    return out[0] == ar::STATUS_PLACEMENT ? AR_ERR_PLACEMENT : AR_OK;
+    return out[0] == ar::STATUS_TIMEOUT ? AR_ERR_TIMEOUT : AR_OK;
 }
 
 int ar_reset(hipStream_t stream)
@@ -567,7 +576,6 @@ const char *ar_strerror(int status)
     case AR_ERR_OOM: return "device out of memory";
     case AR_ERR_HIP: return "HIP runtime error";
     case AR_ERR_TIMEOUT: return "device poll exceeded the watchdog";
-    case AR_ERR_PLACEMENT: return "workgroup ran on an unexpected XCD under XCD-local scope";
     default: return "unknown status";
     }
 }

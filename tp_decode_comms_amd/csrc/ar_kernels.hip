@@ -5,9 +5,10 @@
 // dispatches workgroups to the 8 XCDs round-robin by index, and the host
 // makes `parts` a multiple of 8, so part p of every rank runs on XCD p % 8:
 // all traffic of one part (mailboxes, inboxes, lines, arrival and completion
-// flags) stays inside one XCD's L2.  Correctness does not depend on that
-// placement (every flag and staging access is device-coherent); only latency
-// does.  Workgroups of one part index depend only on each other and are
+// flags) stays inside one XCD's L2.  With device-scope accesses correctness
+// does not depend on that placement, only latency does; the XCD-local scope
+// derives the part from the XCD each workgroup runs on, so its exchanges are
+// XCD-local by construction.  Workgroups of one part index depend only on each other and are
 // dispatched together, and the host never launches more workgroups than the
 // device holds at once, so every poll has a producer that runs.
 //
@@ -97,11 +98,15 @@ __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
     const uint32_t blk = a.span == 1u ? b : __umulhi(b, a.span_magic);
     const uint32_t w = b - blk * a.span;
     c.rank = w >> a.xshift;
-    c.part = (blk << a.xshift) + (w & ((1u << a.xshift) - 1u));
-    // XCD-local scope is only coherent if this workgroup runs where the
-    // placement puts it: a violation is recorded (peers' polls then give up)
-    if (LOCAL && xcc_id() != c.part % (uint32_t)XCDS && threadIdx.x == 0)
-        Ctl{a.ctl}.fail(c.rank, xcc_id(), c.part, STATUS_PLACEMENT);
+    // The XCD-local scope takes the low three part bits from the XCD the
+    // workgroup actually runs on.  Dispatch is round-robin from some XCD o
+    // (o = 0 normally; a profiler can shift it), so within each group of 8
+    // consecutive workgroups of one rank the XCDs are a rotation of 0..7:
+    // the mapping stays one-to-one and part p always runs on XCD p % 8,
+    // whatever o is.  (ar_init checks the round-robin order before it
+    // enables this scope.)
+    const uint32_t lo = LOCAL ? xcc_id() : (w & ((1u << a.xshift) - 1u));
+    c.part = (blk << a.xshift) + lo;
     c.par = a.epoch & 1u;
 }
 

@@ -37,10 +37,10 @@ constexpr int CP_DEV = 16;          // sc1: device-scope coherent
 
 // Policies of the staging and flag traffic.  Device scope is coherent
 // wherever the two sides run.  XCD-local scope (LOCAL) requires writer and
-// reader on one XCD -- which the part-to-XCD placement provides -- and then
+// reader on one XCD -- which the part-to-XCD mapping guarantees -- and then
 // serves both from that XCD's L2: stores at workgroup scope, polls streaming
 // at workgroup scope (they skip the CU's L1, so a repeated poll cannot hit a
-// stale L1 line).  Measured on 8 ranks x 16 KiB: about 0.2-0.5 us less per call.
+// stale L1 line).  Measured on 8 ranks x 16 KiB: about 0.1-0.2 us less per call.
 template <bool LOCAL> struct Pol {
     static constexpr int ST = LOCAL ? CP_WG : CP_DEV;
     static constexpr int LD = LOCAL ? (CP_NT | CP_WG) : CP_DEV;
@@ -53,7 +53,7 @@ constexpr uint32_t SENT_WORD = 0xFFFFFFFFu;   // two sentinel bf16 (0xFFFF)
 constexpr int CTL_SEQ = 0;          // flag-sequence base
 constexpr int CTL_STATUS = 32;      // {code, rank, source, flag}
 // Workgroups are dispatched to the XCDs round-robin by workgroup index, so
-// with `parts` a multiple of XCDS part p of every rank runs on XCD p % XCDS.
+// with `parts` a multiple of XCDS part p of every rank shares an XCD.
 constexpr int XCDS = 8;
 // arrival flag of rank r, copy x (read and written by workgroups of parts
 // p = x mod XCDS) at word CTL_ARRIVE + 32*x + r: one 128-byte line per copy
@@ -61,7 +61,6 @@ constexpr int CTL_ARRIVE = 64;
 constexpr int CTL_WORDS = CTL_ARRIVE + 32 * XCDS;
 static_assert(MAX_RANKS <= 32, "one arrival line holds every rank of a copy");
 constexpr uint32_t STATUS_TIMEOUT = 6;
-constexpr uint32_t STATUS_PLACEMENT = 7;  // XCD-local launch on an unexpected XCD
 constexpr uint32_t DONE_STRIDE = 8192;    // completion-flag words per rank (>= workgroups per rank)
 constexpr uint32_t TS_SUB = 64;           // timestamp sub-slots per call
 
