@@ -41,7 +41,7 @@ HBM_PEAK_GBS = 8000.0
 CLOCK_HZ = 100e6
 CALLS_PER_STEP = 160
 ONE, TWO = 1, 2
-LL, LL128, SENT, DIRECT = 1, 2, 3, 4
+LL, LL128, SENT, DIRECT, BARRIER = 1, 2, 3, 4, 5
 
 
 def log(msg):
@@ -361,6 +361,14 @@ def main():
                           instrumented=False)
         results["latency_16k_oneshot_direct"] = lat_d
         log("16 KiB one-shot DIRECT p50 %.3f us/call" % lat_d["event_us_per_call"]["p50"])
+        # the barrier-ful baseline: the DIRECT reads, fold and writes between two
+        # device-wide barriers; the difference is what the flags save per call
+        lat_b = graph_run(torch, ar, wl2, ONE, BARRIER, CALLS_PER_STEP, args.steps, args.warmup,
+                          instrumented=False)
+        results["latency_16k_oneshot_barrier"] = lat_b
+        results["barrier_cost_16k_us"] = round(lat_b["event_us_per_call"]["p50"] -
+                                               lat_d["event_us_per_call"]["p50"], 4)
+        log("16 KiB one-shot barrier-ful p50 %.3f us/call" % lat_b["event_us_per_call"]["p50"])
     bws = []
     if only in ("all", "bw"):
         wl4 = Workload(torch, 4, 8)
@@ -371,12 +379,18 @@ def main():
                 (TWO, LL128, "bw_4m_twoshot_ll128", "two-shot (reduce-scatter + all-gather, "
                  "LL128 lines)"),
                 (ONE, DIRECT, "bw_4m_oneshot_direct", "one-shot (in-place reads after arrival "
-                 "counters)")):
+                 "flags)"),
+                (TWO, BARRIER, "bw_4m_twoshot_barrier", "two-shot barrier-ful baseline (the "
+                 "two-shot DIRECT work between two device-wide barriers)")):
             log("4 MiB/rank bandwidth: %s" % key)
             r = bench_bandwidth(torch, ar, wl4, args.bw_calls, args.warmup, algo, proto, label)
             results[key] = r
             bws.append(r)
             log("  %.1f GB/s (p50 %.2f us/call)" % (r["gbps_p50"], r["us_per_call"]["p50"]))
+        bws = [r for r in bws if r is not results["bw_4m_twoshot_barrier"]]
+        results["barrier_cost_4m_us"] = round(
+            results["bw_4m_twoshot_barrier"]["us_per_call"]["p50"] -
+            results["bw_4m_twoshot_direct"]["us_per_call"]["p50"], 4)
         del wl4
     if only in ("all", "configs"):
         reps = 3 if args.quick else 10

@@ -76,10 +76,16 @@ enum ar_proto {
     AR_PROTO_LL = 1,        /* one-shot only */
     AR_PROTO_LL128 = 2,     /* one-shot or two-shot */
     AR_PROTO_SENTINEL = 3,  /* one-shot or two-shot */
-    AR_PROTO_DIRECT = 4     /* arrival flags instead of staging: one-shot reads
+    AR_PROTO_DIRECT = 4,    /* arrival flags instead of staging: one-shot reads
                                peers' inputs in place; two-shot reads slice q in
                                place and writes the reduced slice straight into
                                every rank's output, then completion flags */
+    AR_PROTO_BARRIER = 5    /* measured baseline, not barrier-free: the DIRECT
+                               reads, fold and writes between two device-wide
+                               barriers over all ranks' workgroups (before the
+                               reads, after the writes), the classic structure of
+                               section "全局内存屏障"; the grid stays within half the
+                               device's resident-workgroup capacity */
 };
 
 #define AR_MAX_RANKS 16

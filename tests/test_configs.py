@@ -26,7 +26,7 @@ from gpu_util import ar_context, check_status_clean, log, torch_mod
 pytestmark = pytest.mark.gpu
 
 ONE, TWO = 1, 2
-LL, LL128, SENT, DIRECT = 1, 2, 3, 4
+LL, LL128, SENT, DIRECT, BARRIER = 1, 2, 3, 4, 5
 
 
 def _dev(arr):
@@ -140,9 +140,10 @@ def test_config3_ll128_graph(algo):
     assert bad == 0
 
 
-@pytest.mark.parametrize("algo,proto", [(TWO, DIRECT), (ONE, DIRECT), (TWO, LL128), (TWO, SENT)],
+@pytest.mark.parametrize("algo,proto", [(TWO, DIRECT), (ONE, DIRECT), (TWO, LL128), (TWO, SENT),
+                                        (TWO, BARRIER)],
                          ids=["twoshot-direct", "oneshot-direct", "twoshot-ll128",
-                              "twoshot-sentinel"])
+                              "twoshot-sentinel", "twoshot-barrier"])
 def test_config4_rotating_sets(algo, proto):
     log("config 4, algo %d proto %d" % (algo, proto))
     sets = Sets(4, 8)
@@ -203,11 +204,11 @@ def test_protocol_switch_between_calls():
     torch = torch_mod()
     sets = Sets(2, 4)
     combos = [(ONE, LL), (ONE, SENT), (TWO, DIRECT), (ONE, LL128), (TWO, LL128), (TWO, SENT),
-              (ONE, DIRECT)]
+              (ONE, DIRECT), (ONE, BARRIER), (TWO, BARRIER)]
     with ar_context(8, sets.n) as ar:
         out = torch.empty((8, sets.n), dtype=torch.int16, device="cuda:0")
         bad = torch.zeros((), dtype=torch.int64, device="cuda:0")
-        for k in range(70):
+        for k in range(90):
             algo, proto = combos[k % len(combos)]
             ar.set_options(algo, proto)
             s = k % 4

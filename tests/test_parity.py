@@ -17,7 +17,7 @@ from gpu_util import (ar_context, assert_bits_equal, check_status_clean, dev_bit
 pytestmark = pytest.mark.gpu
 
 ONE, TWO = 1, 2
-LL, LL128, SENT, DIRECT = 1, 2, 3, 4
+LL, LL128, SENT, DIRECT, BARRIER = 1, 2, 3, 4, 5
 VARIANTS = [
     ("oneshot-ll", ONE, LL),
     ("oneshot-sentinel", ONE, SENT),
@@ -26,6 +26,8 @@ VARIANTS = [
     ("twoshot-ll128", TWO, LL128),
     ("twoshot-sentinel", TWO, SENT),
     ("twoshot-direct", TWO, DIRECT),
+    ("oneshot-barrier", ONE, BARRIER),     # the barrier-ful baseline
+    ("twoshot-barrier", TWO, BARRIER),
 ]
 
 

@@ -183,12 +183,14 @@ int choose_kind(size_t n, int *kind)
             if (g.s1 == nullptr) return AR_ERR_INVALID;   // inbox region too large
             *kind = ar::K_ONESHOT_SENTINEL; return AR_OK;
         case AR_PROTO_DIRECT: *kind = ar::K_ONESHOT_DIRECT; return AR_OK;
+        case AR_PROTO_BARRIER: *kind = ar::K_ONESHOT_BARRIER; return AR_OK;
         }
     } else {
         switch (proto) {
         case AR_PROTO_LL128: *kind = ar::K_TWOSHOT_LL128; return AR_OK;
         case AR_PROTO_SENTINEL: *kind = ar::K_TWOSHOT_SENTINEL; return AR_OK;
         case AR_PROTO_DIRECT: *kind = ar::K_TWOSHOT_DIRECT; return AR_OK;
+        case AR_PROTO_BARRIER: *kind = ar::K_TWOSHOT_BARRIER; return AR_OK;
         }
     }
     return AR_ERR_INVALID;
@@ -210,7 +212,7 @@ int make_plan(size_t n, bool f32, Plan *p)
     const bool l128 = p->kind == ar::K_ONESHOT_LL128 || p->kind == ar::K_TWOSHOT_LL128;
     if (g.threads > 0)
         p->threads = (uint32_t)g.threads;
-    else if (l128 || p->kind == ar::K_TWOSHOT_DIRECT)
+    else if (l128 || p->kind == ar::K_TWOSHOT_DIRECT || p->kind == ar::K_TWOSHOT_BARRIER)
         p->threads = 256;
     else
         p->threads = 2 * n <= 256 * 1024 ? 64 : 256;
@@ -237,6 +239,13 @@ int make_plan(size_t n, bool f32, Plan *p)
     uint32_t cap = (uint32_t)g.capacity[p->kind][f32 ? 1 : 0][thread_index((int)p->threads)] / N;
     if (cap > ar::DONE_STRIDE)
         cap = ar::DONE_STRIDE;
+    if (p->kind == ar::K_ONESHOT_BARRIER || p->kind == ar::K_TWOSHOT_BARRIER) {
+        // a grid barrier needs every workgroup resident at once: stay within
+        // half the occupancy-derived capacity (the watchdog bounds the rest)
+        cap /= 2;
+        if (cap > ar::DONE_STRIDE)
+            cap = ar::DONE_STRIDE;
+    }
     if (cap == 0)
         return AR_ERR_INVALID;
     uint64_t want = g.wgs_per_rank > 0 ? (uint64_t)g.wgs_per_rank : (units + per_wg - 1) / per_wg;
@@ -464,7 +473,7 @@ int ar_set_options(int algo, int proto)
         return AR_ERR_NOT_INIT;
     if (algo < AR_ALGO_AUTO || algo > AR_ALGO_TWOSHOT)
         return AR_ERR_INVALID;
-    if (proto < AR_PROTO_AUTO || proto > AR_PROTO_DIRECT)
+    if (proto < AR_PROTO_AUTO || proto > AR_PROTO_BARRIER)
         return AR_ERR_INVALID;
     if (algo == AR_ALGO_TWOSHOT && proto == AR_PROTO_LL)
         return AR_ERR_INVALID;
@@ -601,12 +610,15 @@ long long ar_query(int key, size_t n)
             return rc;
         if (key == 2)
             return (p.kind == ar::K_TWOSHOT_LL128 || p.kind == ar::K_TWOSHOT_SENTINEL ||
-                    p.kind == ar::K_TWOSHOT_DIRECT) ? AR_ALGO_TWOSHOT : AR_ALGO_ONESHOT;
+                    p.kind == ar::K_TWOSHOT_DIRECT || p.kind == ar::K_TWOSHOT_BARRIER)
+                       ? AR_ALGO_TWOSHOT : AR_ALGO_ONESHOT;
         if (key == 3) {
             switch (p.kind) {
             case ar::K_ONESHOT_LL: return AR_PROTO_LL;
             case ar::K_ONESHOT_DIRECT:
             case ar::K_TWOSHOT_DIRECT: return AR_PROTO_DIRECT;
+            case ar::K_ONESHOT_BARRIER:
+            case ar::K_TWOSHOT_BARRIER: return AR_PROTO_BARRIER;
             case ar::K_ONESHOT_SENTINEL:
             case ar::K_TWOSHOT_SENTINEL: return AR_PROTO_SENTINEL;
             default: return AR_PROTO_LL128;

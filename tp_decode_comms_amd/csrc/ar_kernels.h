@@ -16,7 +16,9 @@ enum KernelKind {
     K_TWOSHOT_LL128 = 4,
     K_TWOSHOT_SENTINEL = 5,
     K_TWOSHOT_DIRECT = 6,
-    K_COUNT = 7
+    K_ONESHOT_BARRIER = 7,
+    K_TWOSHOT_BARRIER = 8,
+    K_COUNT = 9
 };
 
 // device function of a kernel kind for n_ranks (<= 8 or <= 16 instantiation);

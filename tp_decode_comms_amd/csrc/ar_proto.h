@@ -58,7 +58,14 @@ constexpr int XCDS = 8;
 // arrival flag of rank r, copy x (read and written by workgroups of parts
 // p = x mod XCDS) at word CTL_ARRIVE + 32*x + r: one 128-byte line per copy
 constexpr int CTL_ARRIVE = 64;
-constexpr int CTL_WORDS = CTL_ARRIVE + 32 * XCDS;
+// grid barrier of the barrier-ful baseline (one line per word): the arrival
+// counters of the 8 workgroup groups, the group counter, and the XCDS
+// copies of the top and of the bottom barrier's generation word
+constexpr int CTL_BAR_GROUP = CTL_ARRIVE + 32 * XCDS;
+constexpr int CTL_BAR_COUNT = CTL_BAR_GROUP + 32 * XCDS;
+constexpr int CTL_BAR_TOP = CTL_BAR_COUNT + 32;
+constexpr int CTL_BAR_BOTTOM = CTL_BAR_TOP + 32 * XCDS;
+constexpr int CTL_WORDS = CTL_BAR_BOTTOM + 32 * XCDS;
 static_assert(MAX_RANKS <= 32, "one arrival line holds every rank of a copy");
 constexpr uint32_t STATUS_TIMEOUT = 6;
 constexpr uint32_t DONE_STRIDE = 8192;    // completion-flag words per rank (>= workgroups per rank)
