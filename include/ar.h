@@ -158,9 +158,11 @@ int ar_set_options(int algo, int proto);
 
 /*
  * ar_set_launch -- tuning: workgroups per rank (0 = automatic) and threads
- * per workgroup (64, 128 or 256; 0 = 256).  The workgroups per rank are
- * capped at each call so that the whole grid is resident at once (every
- * poll then has a running producer).  AR_ERR_INVALID for unsupported values.
+ * per workgroup (64, 128 or 256; 0 = automatic).  The one-shot LL kernel
+ * always uses 256 threads (its 4 waves share the peers of 64 chunks).  The
+ * workgroups per rank are capped at each call so that the whole grid is
+ * resident at once (every poll then has a running producer).
+ * AR_ERR_INVALID for unsupported values.
  */
 int ar_set_launch(int wgs_per_rank, int threads);
 

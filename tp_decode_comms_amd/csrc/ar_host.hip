@@ -210,7 +210,9 @@ int make_plan(size_t n, bool f32, Plan *p)
     const uint32_t N = (uint32_t)g.n_ranks;
     p->slice = (uint32_t)slice_len(n, g.n_ranks);
     const bool l128 = p->kind == ar::K_ONESHOT_LL128 || p->kind == ar::K_TWOSHOT_LL128;
-    if (g.threads > 0)
+    if (p->kind == ar::K_ONESHOT_LL)
+        p->threads = 256;               // 4 waves share the peers of 64 chunks
+    else if (g.threads > 0)
         p->threads = (uint32_t)g.threads;
     else if (l128 || p->kind == ar::K_TWOSHOT_DIRECT || p->kind == ar::K_TWOSHOT_BARRIER)
         p->threads = 256;
@@ -219,7 +221,7 @@ int make_plan(size_t n, bool f32, Plan *p)
     uint64_t units, per_wg;
     switch (p->kind) {
     case ar::K_ONESHOT_LL:
-        units = n / 4; per_wg = p->threads; break;
+        units = n / 4; per_wg = 64; break;
     case ar::K_ONESHOT_LL128:
         units = (n + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = p->threads / 64; break;
     case ar::K_TWOSHOT_LL128:

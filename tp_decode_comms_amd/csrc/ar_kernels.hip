@@ -216,47 +216,71 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
 // ============================================================ one-shot LL
 // Lane work unit: 4 elements (8 bytes of input) = one 16-byte LL store of
 // two units {2 bf16, flag}.  Rank r publishes once into its own mailbox
-// [r][parity]; every rank reads it.  The receive keeps two batches of loads
-// in flight: while one batch is checked the next is already on its way.
-// One round of the one-shot LL kernel for lane chunk `ch` with input x.  All
-// mailboxes sit in one region [rank][parity] x ll_stride under descriptor llr.
+// [r][parity]; every rank reads it.  All mailboxes sit in one region
+// [rank][parity] x ll_stride under one descriptor.
+//
+// A workgroup of LL_WAVES waves owns 64 chunks per round.  Wave 0 loads the
+// input and publishes it; once the publish is acknowledged, wave w receives
+// the peers s with s % LL_WAVES == w and stages their units in LDS (the
+// peer tiles, [N][64] x 8 bytes); after a workgroup barrier wave 0 reduces
+// the N units of each chunk from LDS in global rank order and writes the
+// result.  Splitting the peers over the waves matters on this chip: a poll
+// of lines written during the launch costs about 60 ns per load instruction
+// on top of the L2 latency, so 7 peers polled by one wave take ~0.85 us and
+// 2 per wave ~0.5 us.  Each wave's receive keeps two batches of loads in
+// flight: while one batch is checked the next is already on its way.
+constexpr int LL_WAVES = 4;
+
 template <int NMAX, bool F32, bool LOCAL>
 __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
                                          __amdgpu_buffer_rsrc_t llr, __amdgpu_buffer_rsrc_t o,
-                                         uint32_t ch, uint32_t C, u32x2 x)
+                                         uint32_t ch, uint32_t C, u32x2 x, u32x2 (*stage)[64],
+                                         uint32_t *failed)
 {
+    constexpr int PW = (NMAX + LL_WAVES - 1) / LL_WAVES;   // peer slots per wave
     const uint32_t N = a.n_ranks;
     const uint32_t rb = a.ll_stride;
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t lane_off = ch * 16u + c.par * rb;
     const bool active = ch < C;
     // publish (send/bcast): one copy, read by all N ranks
-    if (active)
-        st16<Pol<LOCAL>::ST>(ll_pack(x.x, x.y, c.flag), llr, lane_off + c.rank * 2u * rb);
-    wait_stores();                  // first poll only after the publish is acknowledged
-    // receive (recvReduce): poll every peer's unit for this chunk
+    if (wave == 0u) {
+        if (active)
+            st16<Pol<LOCAL>::ST>(ll_pack(x.x, x.y, c.flag), llr, lane_off + c.rank * 2u * rb);
+        stage[c.rank][lane] = x;
+        wait_stores();
+    }
+    // polls start once the publish is acknowledged: an earlier poll mostly
+    // returns stale data and costs a second round trip
+    __syncthreads();
+    // receive (recv): this wave's peers s = wave + LL_WAVES * j
     uint32_t pend = 0;
 #pragma unroll
-    for (int s = 0; s < NMAX; ++s)
-        if ((uint32_t)s < N && (uint32_t)s != c.rank && active)
-            pend |= 1u << s;
-    u32x4 A0[NMAX], A1[NMAX];
-    u32x2 V[NMAX];
+    for (int j = 0; j < PW; ++j) {
+        const uint32_t s = wave + (uint32_t)(LL_WAVES * j);
+        if (s < N && s != c.rank && active)
+            pend |= 1u << j;
+    }
+    u32x4 A0[PW], A1[PW];
+    u32x2 V[PW];
     auto issue = [&](u32x4 *A) {
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((pend >> s) & 1u)
-                A[s] = ld16<Pol<LOCAL>::LD>(llr, lane_off + (uint32_t)s * 2u * rb);
+        for (int j = 0; j < PW; ++j)
+            if ((pend >> j) & 1u)
+                A[j] = ld16<Pol<LOCAL>::LD>(llr, lane_off +
+                                            (wave + (uint32_t)(LL_WAVES * j)) * 2u * rb);
     };
     auto check = [&](const u32x4 *A) {
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((pend >> s) & 1u)
-                if (ll_ready(A[s], c.flag)) {
-                    pend &= ~(1u << s);
-                    V[s].x = A[s].x;
-                    V[s].y = A[s].z;
+        for (int j = 0; j < PW; ++j)
+            if ((pend >> j) & 1u)
+                if (ll_ready(A[j], c.flag)) {
+                    pend &= ~(1u << j);
+                    V[j].x = A[j].x;
+                    V[j].y = A[j].z;
                 }
     };
+    uint32_t mine = pend;                           // slots this lane stages
     Watch w;
     w.begin(a.watchdog_ticks);
     issue(A0);
@@ -266,43 +290,58 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
         check(A0);
         if (!wave_any(pend != 0u))
             break;
-        if (w.expired(ctl, c.rank, pend ? first_bit(pend) : 0u, c.flag))
-            return false;
+        if (w.expired(ctl, c.rank, pend ? wave + LL_WAVES * first_bit(pend) : 0u, c.flag)) {
+            *failed = 1u;                           // every wave still meets the barrier
+            break;
+        }
         compiler_fence();
         issue(A0);
         check(A1);
         if (!wave_any(pend != 0u))
             break;
     }
-    // reduce in global rank order, own value from registers
-    if (active) {
+#pragma unroll
+    for (int j = 0; j < PW; ++j)
+        if ((mine >> j) & 1u)
+            stage[wave + LL_WAVES * j][lane] = V[j];
+    __syncthreads();
+    if (*failed)
+        return false;
+    // recvReduce: global rank order from the staged tile
+    if (wave == 0u && active) {
         Acc4 acc;
 #pragma unroll
         for (int s = 0; s < NMAX; ++s) {
             if ((uint32_t)s < N) {
-                const u32x2 v = ((uint32_t)s == c.rank) ? x : V[s];
+                const u32x2 v = stage[s][lane];
                 if (s == 0) acc.init(v.x, v.y); else acc.add(v.x, v.y);
             }
         }
         store4<F32>(o, ch * 4u, acc.v);
     }
+    __syncthreads();                                // the tile is reused next round
     return true;
 }
 
 template <int NMAX, bool F32, bool LOCAL>
 __global__ __launch_bounds__(256) void k_oneshot_ll(const Launch a)
 {
+    __shared__ u32x2 stage[NMAX][64];
+    __shared__ uint32_t failed;
     Ctx0 c;
     begin<LOCAL>(a, c);
     const uint32_t C = a.n >> 2;                    // 4-element chunks per rank
-    const uint32_t step = a.parts * blockDim.x;
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t step = a.parts * 64u;
     const uint32_t rounds = (C + step - 1u) / step;
     const __amdgpu_buffer_rsrc_t inr = in_rsrc(a, c.rank);
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
+    if (threadIdx.x == 0)
+        failed = 0u;
     // first-round input load is issued together with the sequence load
-    uint32_t ch = c.part * blockDim.x + threadIdx.x;
+    uint32_t ch = c.part * 64u + lane;
     u32x2 x = {0u, 0u};
-    if (ch < C)
+    if (wave == 0u && ch < C)
         x = ld8<CP_PLAIN>(inr, ch * 8u);
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
@@ -310,13 +349,12 @@ __global__ __launch_bounds__(256) void k_oneshot_ll(const Launch a)
     start_delay(a, c);
     // round 0 is straight-line code: its poll loads are issued back to back
     // (inside a loop the compiler's counter bookkeeping would wait before each)
-    if (!ll_round<NMAX, F32, LOCAL>(a, c, ctl, llr, o, ch, C, x))
+    if (!ll_round<NMAX, F32, LOCAL>(a, c, ctl, llr, o, ch, C, x, stage, &failed))
         return;
     for (uint32_t it = 1; it < rounds; ++it) {
-        wait_stores();
         ch += step;
-        x = ch < C ? ld8<CP_PLAIN>(inr, ch * 8u) : u32x2{0u, 0u};
-        if (!ll_round<NMAX, F32, LOCAL>(a, c, ctl, llr, o, ch, C, x))
+        x = (wave == 0u && ch < C) ? ld8<CP_PLAIN>(inr, ch * 8u) : u32x2{0u, 0u};
+        if (!ll_round<NMAX, F32, LOCAL>(a, c, ctl, llr, o, ch, C, x, stage, &failed))
             return;
     }
     finish(a, c);
