@@ -210,7 +210,8 @@ int make_plan(size_t n, bool f32, Plan *p)
     const uint32_t N = (uint32_t)g.n_ranks;
     p->slice = (uint32_t)slice_len(n, g.n_ranks);
     const bool l128 = p->kind == ar::K_ONESHOT_LL128 || p->kind == ar::K_TWOSHOT_LL128;
-    if (p->kind == ar::K_ONESHOT_LL)
+    if (p->kind == ar::K_ONESHOT_LL || p->kind == ar::K_ONESHOT_SENTINEL ||
+        p->kind == ar::K_TWOSHOT_SENTINEL)
         p->threads = 256;               // 4 waves share the peers of 64 chunks
     else if (g.threads > 0)
         p->threads = (uint32_t)g.threads;
@@ -226,8 +227,10 @@ int make_plan(size_t n, bool f32, Plan *p)
         units = (n + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = p->threads / 64; break;
     case ar::K_TWOSHOT_LL128:
         units = (p->slice + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = p->threads / 64; break;
+    case ar::K_ONESHOT_SENTINEL:
+        units = n / 8; per_wg = 64; break;
     case ar::K_TWOSHOT_SENTINEL:
-        units = p->slice / 8; per_wg = p->threads; break;
+        units = p->slice / 8; per_wg = 64; break;
     case ar::K_TWOSHOT_DIRECT:
         units = p->slice / 8; per_wg = 2 * p->threads; break;
     default:

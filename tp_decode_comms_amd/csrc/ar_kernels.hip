@@ -366,103 +366,135 @@ __global__ __launch_bounds__(256) void k_oneshot_ll(const Launch a)
 // the sentinel, reduces, and re-arms the slots it consumed.  The receipt of
 // a peer's call-k data proves the peer finished call k-1 (double buffering),
 // so the re-arm of parity k&1 always lands before the peer's call k+2 write.
+//
+// As in the one-shot LL kernel, a workgroup of 4 waves owns 64 chunks (of 8
+// elements) per round and the peers are split over the waves: wave w pushes
+// the chunk into the inboxes of the peers s with s % 4 == w, and once those
+// stores are acknowledged it receives the same peers' chunks from its own
+// inbox, re-arms their slots and stages the values in LDS; after a
+// workgroup barrier wave 0 reduces the tile in global rank order.
+constexpr int SENT_WAVES = 4;
+
+template <int NMAX, bool F32, bool LOCAL>
+__device__ __forceinline__ bool sent_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
+                                           __amdgpu_buffer_rsrc_t box,
+                                           __amdgpu_buffer_rsrc_t o, uint32_t ch, uint32_t G,
+                                           u32x4 x, u32x4 (*stage)[64], uint32_t *failed)
+{
+    constexpr int PW = (NMAX + SENT_WAVES - 1) / SENT_WAVES;
+    const uint32_t N = a.n_ranks;
+    const uint32_t sb = a.s1_stride;
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const bool active = ch < G;
+    // inboxes [recv][send][parity] x s1_stride under one descriptor
+    auto slot = [&](uint32_t recv, uint32_t send) {
+        return ch * 16u + c.par * sb + ((recv * N + send) * 2u) * sb;
+    };
+    uint32_t pend = 0;
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+        const uint32_t s = wave + (uint32_t)(SENT_WAVES * j);
+        if (s < N && s != c.rank && active)
+            pend |= 1u << j;
+    }
+    const uint32_t mine = pend;
+    // push (send) to this wave's peers
+#pragma unroll
+    for (int j = 0; j < PW; ++j)
+        if ((mine >> j) & 1u)
+            st16<Pol<LOCAL>::ST>(x, box, slot(wave + (uint32_t)(SENT_WAVES * j), c.rank));
+    if (wave == 0u)
+        stage[c.rank][lane] = x;
+    wait_stores();                  // receive only after the pushes are acknowledged
+    u32x4 A0[PW], A1[PW], V[PW];
+    auto issue = [&](u32x4 *A) {
+#pragma unroll
+        for (int j = 0; j < PW; ++j)
+            if ((pend >> j) & 1u)
+                A[j] = ld16<Pol<LOCAL>::LD>(box, slot(c.rank, wave + (uint32_t)(SENT_WAVES * j)));
+    };
+    auto check = [&](const u32x4 *A) {
+#pragma unroll
+        for (int j = 0; j < PW; ++j)
+            if ((pend >> j) & 1u)
+                if (sent_ready(A[j])) {
+                    pend &= ~(1u << j);
+                    V[j] = A[j];
+                }
+    };
+    Watch w;
+    w.begin(a.watchdog_ticks);
+    issue(A0);
+    while (true) {
+        compiler_fence();
+        issue(A1);
+        check(A0);
+        if (!wave_any(pend != 0u))
+            break;
+        if (w.expired(ctl, c.rank, pend ? wave + SENT_WAVES * first_bit(pend) : 0u, c.flag)) {
+            *failed = 1u;                           // every wave still meets the barrier
+            break;
+        }
+        compiler_fence();
+        issue(A0);
+        check(A1);
+        if (!wave_any(pend != 0u))
+            break;
+    }
+    // re-arm what was consumed (resetRange) and stage it
+#pragma unroll
+    for (int j = 0; j < PW; ++j)
+        if ((mine >> j) & 1u) {
+            const uint32_t s = wave + (uint32_t)(SENT_WAVES * j);
+            st16<Pol<LOCAL>::ST>(sentinel4(), box, slot(c.rank, s));
+            stage[s][lane] = V[j];
+        }
+    __syncthreads();
+    if (*failed)
+        return false;
+    if (wave == 0u && active) {
+        Acc8 acc;
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((uint32_t)s < N) {
+                const u32x4 v = stage[s][lane];
+                if (s == 0) acc.init(v); else acc.add(v);
+            }
+        store8<F32>(o, ch * 8u, acc);
+    }
+    __syncthreads();                                // the tile is reused next round
+    return true;
+}
+
 template <int NMAX, bool F32, bool LOCAL>
 __global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
 {
+    __shared__ u32x4 stage[NMAX][64];
+    __shared__ uint32_t failed;
     Ctx0 c;
     begin<LOCAL>(a, c);
-    const uint32_t N = a.n_ranks;
     const uint32_t G = a.n >> 3;
-    const uint32_t bytes = a.n * 2u;
-    const uint32_t step = a.parts * blockDim.x;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t step = a.parts * 64u;
     const uint32_t rounds = (G + step - 1u) / step;
     const __amdgpu_buffer_rsrc_t inr = in_rsrc(a, c.rank);
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
-    uint32_t ch = c.part * blockDim.x + threadIdx.x;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (ch < G)
-        x = ld16<CP_PLAIN>(inr, ch * 16u);
+    if (threadIdx.x == 0)
+        failed = 0u;
+    // every wave pushes the chunk, so every wave loads it (the loads meet in L2)
+    uint32_t ch = c.part * 64u + lane;
+    u32x4 x = ch < G ? ld16<CP_PLAIN>(inr, ch * 16u) : u32x4{0u, 0u, 0u, 0u};
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
-    // all inboxes [recv][send][parity] x s1_stride under one descriptor
-    const uint32_t sb = a.s1_stride;
-    const __amdgpu_buffer_rsrc_t box = rsrc(a.s1, N * N * 2u * sb);
-    const uint32_t par_off = c.par * sb;
-    (void)bytes;
+    const __amdgpu_buffer_rsrc_t box = rsrc(a.s1, a.n_ranks * a.n_ranks * 2u * a.s1_stride);
     start_delay(a, c);
-
-    auto round = [&](uint32_t ch, u32x4 x) -> bool {
-        const bool active = ch < G;
-        if (active) {
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((uint32_t)s < N && (uint32_t)s != c.rank)
-                    st16<Pol<LOCAL>::ST>(x, box, ch * 16u + par_off + (((uint32_t)s * N + c.rank) * 2u) * sb);
-        }
-        uint32_t pend = 0;
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N && (uint32_t)s != c.rank && active)
-                pend |= 1u << s;
-        u32x4 A0[NMAX], A1[NMAX], V[NMAX];
-        auto issue = [&](u32x4 *A) {
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((pend >> s) & 1u)
-                    A[s] = ld16<Pol<LOCAL>::LD>(box, ch * 16u + par_off + ((c.rank * N + (uint32_t)s) * 2u) * sb);
-        };
-        auto check = [&](const u32x4 *A) {
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((pend >> s) & 1u)
-                    if (sent_ready(A[s])) {
-                        pend &= ~(1u << s);
-                        V[s] = A[s];
-                    }
-        };
-        Watch w;
-        w.begin(a.watchdog_ticks);
-        issue(A0);
-        while (true) {
-            compiler_fence();
-            issue(A1);
-            check(A0);
-            if (!wave_any(pend != 0u))
-                break;
-            if (w.expired(ctl, c.rank, pend ? first_bit(pend) : 0u, c.flag))
-                return false;
-            compiler_fence();
-            issue(A0);
-            check(A1);
-            if (!wave_any(pend != 0u))
-                break;
-        }
-        if (active) {
-            Acc8 acc;
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s) {
-                if ((uint32_t)s < N) {
-                    const u32x4 v = ((uint32_t)s == c.rank) ? x : V[s];
-                    if (s == 0) acc.init(v); else acc.add(v);
-                }
-            }
-            // re-arm what was consumed (resetRange), then write the result
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((uint32_t)s < N && (uint32_t)s != c.rank)
-                    st16<Pol<LOCAL>::ST>(sentinel4(), box, ch * 16u + par_off + ((c.rank * N + (uint32_t)s) * 2u) * sb);
-            store8<F32>(o, ch * 8u, acc);
-        }
-        return true;
-    };
     // round 0 straight-line (see the one-shot LL kernel), later rounds looped
-    if (!round(ch, x))
+    if (!sent_round<NMAX, F32, LOCAL>(a, c, ctl, box, o, ch, G, x, stage, &failed))
         return;
     for (uint32_t it = 1; it < rounds; ++it) {
-        wait_stores();
         ch += step;
         x = ch < G ? ld16<CP_PLAIN>(inr, ch * 16u) : u32x4{0u, 0u, 0u, 0u};
-        if (!round(ch, x))
+        if (!sent_round<NMAX, F32, LOCAL>(a, c, ctl, box, o, ch, G, x, stage, &failed))
             return;
     }
     finish(a, c);
@@ -1106,16 +1138,25 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 // All-gather: rank q pushes its reduced chunk into AG[r][q] of every peer r
 // and writes it to out[q]; every rank polls AG[q][*], copies to out, re-arms.
 // Inbox regions [recv][send][parity] x s2_stride, one descriptor each.
+//
+// A workgroup of 4 waves owns 64 chunks of every slice per round, and the
+// peers are split over the waves as in the one-shot kernels: wave w pushes
+// the slices of, and receives from, the peers s with s % 4 == w.  The
+// received slice-q chunks are staged in LDS and reduced by wave 0, which
+// puts the bf16 result in LDS for every wave's all-gather pushes.
 template <int NMAX, bool F32, bool LOCAL>
 __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
                                          __amdgpu_buffer_rsrc_t inq, __amdgpu_buffer_rsrc_t rsr,
                                          __amdgpu_buffer_rsrc_t agr, __amdgpu_buffer_rsrc_t oa,
-                                         uint32_t ch, bool first)
+                                         uint32_t ch, u32x4 (*stage)[64], u32x4 *red,
+                                         uint32_t *failed)
 {
+    constexpr int PW = (NMAX + SENT_WAVES - 1) / SENT_WAVES;
     const uint32_t N = a.n_ranks;
     const uint32_t q = c.rank;
     const uint32_t L = a.slice;
     const uint32_t sb = a.s2_stride;
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t e = ch * 8u;                     // element offset inside a slice
     const uint32_t esz = F32 ? 4u : 2u;
     const uint32_t lane_off = e * 2u + c.par * sb;
@@ -1125,144 +1166,154 @@ __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const C
     };
     // inbox offsets: receiver-major [recv][send]
     auto box = [&](uint32_t recv, uint32_t send) { return lane_off + (recv * N + send) * 2u * sb; };
-    const uint32_t Lq = slice_len(q);
-    // ---- push my parts of every slice
-    u32x4 own = {0u, 0u, 0u, 0u};
-    u32x4 X[NMAX];
+    auto peer = [&](int j) { return wave + (uint32_t)(SENT_WAVES * j); };
+    const bool act = e < slice_len(q);
+    // ---- push my parts of this wave's slices
+    u32x4 X[PW];
+    uint32_t push = 0;
 #pragma unroll
-    for (int s = 0; s < NMAX; ++s)
-        if ((uint32_t)s < N && e < slice_len((uint32_t)s))
-            X[s] = ld16<CP_PLAIN>(inq, ((uint32_t)s * L + e) * 2u);
-    if (first)
-        start_delay(a, c);
-#pragma unroll
-    for (int s = 0; s < NMAX; ++s) {
-        if ((uint32_t)s < N && e < slice_len((uint32_t)s)) {
-            if ((uint32_t)s == q) own = X[s];
-            else st16<Pol<LOCAL>::ST>(X[s], rsr, box((uint32_t)s, q));
+    for (int j = 0; j < PW; ++j)
+        if (peer(j) < N && peer(j) != q && e < slice_len(peer(j))) {
+            X[j] = ld16<CP_PLAIN>(inq, (peer(j) * L + e) * 2u);
+            push |= 1u << j;
         }
-    }
-    // ---- receive my slice from everyone, reduce, re-arm
-    const bool act = e < Lq;
-    uint32_t pend = 0;
+    if (wave == 0u && act)
+        stage[q][lane] = ld16<CP_PLAIN>(inq, (q * L + e) * 2u);
 #pragma unroll
-    for (int s = 0; s < NMAX; ++s)
-        if ((uint32_t)s < N && (uint32_t)s != q && act)
-            pend |= 1u << s;
-    u32x4 A0[NMAX], A1[NMAX], V[NMAX];
+    for (int j = 0; j < PW; ++j)
+        if ((push >> j) & 1u)
+            st16<Pol<LOCAL>::ST>(X[j], rsr, box(peer(j), q));
+    wait_stores();                  // receive only after the pushes are acknowledged
+    u32x4 A0[PW], A1[PW], V[PW];
+    uint32_t pend = 0;
     auto issue = [&](u32x4 *A, __amdgpu_buffer_rsrc_t reg) {
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((pend >> s) & 1u)
-                A[s] = ld16<Pol<LOCAL>::LD>(reg, box(q, (uint32_t)s));
+        for (int j = 0; j < PW; ++j)
+            if ((pend >> j) & 1u)
+                A[j] = ld16<Pol<LOCAL>::LD>(reg, box(q, peer(j)));
     };
     auto check = [&](const u32x4 *A) {
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((pend >> s) & 1u)
-                if (sent_ready(A[s])) {
-                    pend &= ~(1u << s);
-                    V[s] = A[s];
+        for (int j = 0; j < PW; ++j)
+            if ((pend >> j) & 1u)
+                if (sent_ready(A[j])) {
+                    pend &= ~(1u << j);
+                    V[j] = A[j];
                 }
     };
-    Watch w;
-    w.begin(a.watchdog_ticks);
-    issue(A0, rsr);
-    while (true) {
-        compiler_fence();
-        issue(A1, rsr);
-        check(A0);
-        if (!wave_any(pend != 0u))
-            break;
-        if (w.expired(ctl, q, pend ? first_bit(pend) : 0u, c.flag))
-            return false;
-        compiler_fence();
-        issue(A0, rsr);
-        check(A1);
-        if (!wave_any(pend != 0u))
-            break;
-    }
-    if (act) {
+    auto receive = [&](__amdgpu_buffer_rsrc_t reg) {
+        Watch w;
+        w.begin(a.watchdog_ticks);
+        issue(A0, reg);
+        while (true) {
+            compiler_fence();
+            issue(A1, reg);
+            check(A0);
+            if (!wave_any(pend != 0u))
+                break;
+            if (w.expired(ctl, q, pend ? peer((int)first_bit(pend)) : 0u, c.flag)) {
+                *failed = 1u;                       // every wave still meets the barrier
+                break;
+            }
+            compiler_fence();
+            issue(A0, reg);
+            check(A1);
+            if (!wave_any(pend != 0u))
+                break;
+        }
+    };
+    // ---- receive my slice from this wave's peers, re-arm, stage
+#pragma unroll
+    for (int j = 0; j < PW; ++j)
+        if (peer(j) < N && peer(j) != q && act)
+            pend |= 1u << j;
+    uint32_t mine = pend;
+    receive(rsr);
+#pragma unroll
+    for (int j = 0; j < PW; ++j)
+        if ((mine >> j) & 1u) {
+            st16<Pol<LOCAL>::ST>(sentinel4(), rsr, box(q, peer(j)));
+            stage[peer(j)][lane] = V[j];
+        }
+    __syncthreads();
+    if (*failed)
+        return false;
+    if (wave == 0u && act) {
         Acc8 acc;
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             if ((uint32_t)s < N) {
-                const u32x4 v = ((uint32_t)s == q) ? own : V[s];
+                const u32x4 v = stage[s][lane];
                 if (s == 0) acc.init(v); else acc.add(v);
             }
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N && (uint32_t)s != q)
-                st16<Pol<LOCAL>::ST>(sentinel4(), rsr, box(q, (uint32_t)s));
         if constexpr (F32) {
             // debug path: the owner writes its slice's accumulators to every copy
             for (uint32_t r = 0; r < N; ++r)
                 store8<true>(oa, r * a.n + q * L + e, acc);
         } else {
-            const u32x4 red = acc.bf16();
-#pragma unroll
-            for (int r = 0; r < NMAX; ++r)
-                if ((uint32_t)r < N && (uint32_t)r != q)
-                    st16<Pol<LOCAL>::ST>(red, agr, box((uint32_t)r, q));
-            st16<CP_PLAIN>(red, oa, (q * a.n + q * L + e) * esz);
+            const u32x4 rv = acc.bf16();
+            red[lane] = rv;
+            st16<CP_PLAIN>(rv, oa, (q * a.n + q * L + e) * esz);
         }
     }
+    __syncthreads();
     if constexpr (F32)
         return true;
-    // ---- all-gather: receive every other slice's reduced chunk
+    // ---- all-gather: push the reduced chunk to this wave's peers
+    if (act) {
+        const u32x4 rv = red[lane];
+#pragma unroll
+        for (int j = 0; j < PW; ++j)
+            if (peer(j) < N && peer(j) != q)
+                st16<Pol<LOCAL>::ST>(rv, agr, box(peer(j), q));
+    }
+    wait_stores();
+    // ---- receive every other slice's reduced chunk from this wave's peers
     pend = 0;
 #pragma unroll
-    for (int s = 0; s < NMAX; ++s)
-        if ((uint32_t)s < N && (uint32_t)s != q && e < slice_len((uint32_t)s))
-            pend |= 1u << s;
-    w.begin(a.watchdog_ticks);
-    issue(A0, agr);
-    while (true) {
-        compiler_fence();
-        issue(A1, agr);
-        check(A0);
-        if (!wave_any(pend != 0u))
-            break;
-        if (w.expired(ctl, q, pend ? first_bit(pend) : 0u, c.flag))
-            return false;
-        compiler_fence();
-        issue(A0, agr);
-        check(A1);
-        if (!wave_any(pend != 0u))
-            break;
-    }
+    for (int j = 0; j < PW; ++j)
+        if (peer(j) < N && peer(j) != q && e < slice_len(peer(j)))
+            pend |= 1u << j;
+    mine = pend;
+    receive(agr);
 #pragma unroll
-    for (int s = 0; s < NMAX; ++s)
-        if ((uint32_t)s < N && (uint32_t)s != q && e < slice_len((uint32_t)s)) {
-            st16<CP_PLAIN>(V[s], oa, (q * a.n + (uint32_t)s * L + e) * esz);
-            st16<Pol<LOCAL>::ST>(sentinel4(), agr, box(q, (uint32_t)s));
+    for (int j = 0; j < PW; ++j)
+        if ((mine >> j) & 1u) {
+            st16<CP_PLAIN>(V[j], oa, (q * a.n + peer(j) * L + e) * esz);
+            st16<Pol<LOCAL>::ST>(sentinel4(), agr, box(q, peer(j)));
         }
-    return true;
+    __syncthreads();                                // the tiles are reused next round
+    return *failed == 0u;
 }
 
 template <int NMAX, bool F32, bool LOCAL>
 __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
 {
+    __shared__ u32x4 stage[NMAX][64];
+    __shared__ u32x4 red[64];
+    __shared__ uint32_t failed;
     Ctx0 c;
     begin<LOCAL>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t G = a.slice >> 3;                // chunks per slice
-    const uint32_t step = a.parts * blockDim.x;
+    const uint32_t step = a.parts * 64u;
     const uint32_t rounds = (G + step - 1u) / step;
+    if (threadIdx.x == 0)
+        failed = 0u;
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     const __amdgpu_buffer_rsrc_t inq = in_rsrc(a, c.rank);
     const __amdgpu_buffer_rsrc_t rsr = rsrc(a.srs, N * N * 2u * a.s2_stride);
     const __amdgpu_buffer_rsrc_t agr = rsrc(a.sag, N * N * 2u * a.s2_stride);
     const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
-    uint32_t ch = c.part * blockDim.x + threadIdx.x;
+    uint32_t ch = c.part * 64u + (threadIdx.x & 63u);
+    start_delay(a, c);
     // round 0 straight-line (see the one-shot LL kernel), later rounds looped
-    if (!ts_round<NMAX, F32, LOCAL>(a, c, ctl, inq, rsr, agr, oa, ch, true))
+    if (!ts_round<NMAX, F32, LOCAL>(a, c, ctl, inq, rsr, agr, oa, ch, stage, red, &failed))
         return;
     for (uint32_t it = 1; it < rounds; ++it) {
-        wait_stores();
         ch += step;
-        if (!ts_round<NMAX, F32, LOCAL>(a, c, ctl, inq, rsr, agr, oa, ch, false))
+        if (!ts_round<NMAX, F32, LOCAL>(a, c, ctl, inq, rsr, agr, oa, ch, stage, red, &failed))
             return;
     }
     finish(a, c);
