@@ -158,9 +158,9 @@ int ar_set_options(int algo, int proto);
 
 /*
  * ar_set_launch -- tuning: workgroups per rank (0 = automatic) and threads
- * per workgroup (64, 128 or 256; 0 = automatic).  The LL and sentinel
- * kernels always use 256 threads (their 4 waves share the peers of 64
- * chunks).  The
+ * per workgroup (64, 128 or 256; 0 = automatic).  The LL, sentinel and
+ * LL128 kernels always use 256 threads (their 4 waves share the peers of a
+ * tile).  The
  * workgroups per rank are capped at each call so that the whole grid is
  * resident at once (every poll then has a running producer).
  * AR_ERR_INVALID for unsupported values.

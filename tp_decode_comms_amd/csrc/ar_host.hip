@@ -211,8 +211,8 @@ int make_plan(size_t n, bool f32, Plan *p)
     p->slice = (uint32_t)slice_len(n, g.n_ranks);
     const bool l128 = p->kind == ar::K_ONESHOT_LL128 || p->kind == ar::K_TWOSHOT_LL128;
     if (p->kind == ar::K_ONESHOT_LL || p->kind == ar::K_ONESHOT_SENTINEL ||
-        p->kind == ar::K_TWOSHOT_SENTINEL)
-        p->threads = 256;               // 4 waves share the peers of 64 chunks
+        p->kind == ar::K_TWOSHOT_SENTINEL || l128)
+        p->threads = 256;               // 4 waves share the peers of a tile
     else if (g.threads > 0)
         p->threads = (uint32_t)g.threads;
     else if (l128 || p->kind == ar::K_TWOSHOT_DIRECT || p->kind == ar::K_TWOSHOT_BARRIER)
@@ -223,10 +223,10 @@ int make_plan(size_t n, bool f32, Plan *p)
     switch (p->kind) {
     case ar::K_ONESHOT_LL:
         units = n / 4; per_wg = 64; break;
-    case ar::K_ONESHOT_LL128:
-        units = (n + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = p->threads / 64; break;
+    case ar::K_ONESHOT_LL128:       // batches of 4 line groups (2 above 8 ranks)
+        units = (n + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = N <= 8 ? 4 : 2; break;
     case ar::K_TWOSHOT_LL128:
-        units = (p->slice + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = p->threads / 64; break;
+        units = (p->slice + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = N <= 8 ? 4 : 2; break;
     case ar::K_ONESHOT_SENTINEL:
         units = n / 8; per_wg = 64; break;
     case ar::K_TWOSHOT_SENTINEL:

@@ -814,11 +814,15 @@ __global__ __launch_bounds__(256) void k_twoshot_barrier(const Launch a)
 
 // ============================================================ LL128 lines
 // Lane mapping of a line group (480 elements, 1024 bytes): see ar_proto.h.
-// A wave handles up to GB groups per batch: it publishes the payload of all
-// of them, waits once for the acknowledgements, then stores their flags;
-// a reader polls the flags of all its groups together, then loads payloads.
-// groups per batch: 4 for up to 8 ranks, 2 for up to 16 (register budget)
+// A workgroup of 4 waves handles GW line groups per batch, one per
+// publishing wave: the wave publishes its group's payload, waits for the
+// acknowledgement, then stores the line flags.  The receive is split over
+// the waves as in the LL and sentinel kernels: wave w takes every group of
+// the batch from the peers s with s % 4 == w, polling their line flags
+// together and then loading the payloads.
+// groups per batch: 4 for up to 8 ranks, 2 for up to 16 (LDS tile budget)
 template <int NMAX> struct GroupsPerBatch { static constexpr int value = NMAX <= 8 ? 4 : 2; };
+constexpr int L128_WAVES = 4;
 
 // reads 8 (or 4) elements of a bf16 buffer at element `e`
 template <int CP = CP_PLAIN>
@@ -857,36 +861,38 @@ __device__ __forceinline__ bool l128_flag_ok(u32x2 f, uint32_t flag)
     return f.x == flag && f.y == ~flag;
 }
 
-// Receives GB line groups (slot j valid when gvalid bit j) from the N
-// sources: flag lanes poll the line flags of every (slot, source) still
-// pending, the wave votes, then every lane loads its payloads.  lim[s] is the
-// number of valid elements of source s in group index space; a line is
-// polled only if one of its elements is valid.  skip names a source the
-// caller holds already (or NMAX).  Returns false on watchdog expiry.
-template <int NMAX, bool LOCAL, int GB = GroupsPerBatch<NMAX>::value>
-__device__ __forceinline__ bool l128_receive(__amdgpu_buffer_rsrc_t reg, uint32_t rb, uint32_t par,
-                                             uint32_t N, uint32_t skip, const uint32_t *g,
-                                             uint32_t gvalid, uint32_t lane, const L128Lane &ln,
-                                             const uint32_t *lim, uint32_t flag, const Ctl &ctl,
-                                             uint32_t rank, uint32_t budget, u32x4 (*V)[NMAX])
+// Receives the GW line groups g[k] (valid when bit k of gvalid) from this
+// wave's peers s = wave + 4j (PW slots; bit j of pmask marks a real peer):
+// flag lanes poll the line flags of every (group, peer) still pending, the
+// wave votes, then every lane loads its payloads into V[k][j].  lim[j] is
+// the number of valid elements of peer j in group index space; a line is
+// polled only if one of its elements is valid.  Returns false on watchdog
+// expiry.
+template <int GW, int PW, bool LOCAL>
+__device__ __forceinline__ bool l128_recv(__amdgpu_buffer_rsrc_t reg, uint32_t rb, uint32_t par,
+                                          const uint32_t *g, uint32_t gvalid, uint32_t pmask,
+                                          uint32_t wave, uint32_t lane, const L128Lane &ln,
+                                          const uint32_t *lim, uint32_t flag, const Ctl &ctl,
+                                          uint32_t rank, uint32_t budget, u32x4 (*V)[PW])
 {
-    // source s's lines of group g: reg + (s*2 + par)*rb + g*1024 + lane*16
-    auto off = [&](int j, int s) {
-        return ((uint32_t)s * 2u + par) * rb + g[j] * L128_BYTES + lane * 16u;
+    // peer s's lines of group g: reg + (s*2 + par)*rb + g*1024 + lane*16
+    auto off = [&](int k, int j) {
+        return ((wave + (uint32_t)(L128_WAVES * j)) * 2u + par) * rb + g[k] * L128_BYTES +
+               lane * 16u;
     };
-    uint32_t pend[GB];
-    u32x2 F[GB][NMAX];
+    uint32_t pend[GW];
+    u32x2 F[GW][PW];
 #pragma unroll
-    for (int j = 0; j < GB; ++j) {
-        pend[j] = 0;
-        if (!((gvalid >> j) & 1u))
+    for (int k = 0; k < GW; ++k) {
+        pend[k] = 0;
+        if (!((gvalid >> k) & 1u))
             continue;
-        const uint32_t line_first = g[j] * L128_ELEMS + 56u * (lane >> 3);
+        const uint32_t line_first = g[k] * L128_ELEMS + 56u * (lane >> 3);
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N && (uint32_t)s != skip && ln.half && line_first < lim[s]) {
-                F[j][s] = ld8<Pol<LOCAL>::LD>(reg, off(j, s) + 8u);
-                pend[j] |= 1u << s;
+        for (int j = 0; j < PW; ++j)
+            if (((pmask >> j) & 1u) && ln.half && line_first < lim[j]) {
+                F[k][j] = ld8<Pol<LOCAL>::LD>(reg, off(k, j) + 8u);
+                pend[k] |= 1u << j;
             }
     }
     Watch w;
@@ -894,41 +900,41 @@ __device__ __forceinline__ bool l128_receive(__amdgpu_buffer_rsrc_t reg, uint32_
     while (true) {
         uint32_t any = 0;
 #pragma unroll
-        for (int j = 0; j < GB; ++j) {
+        for (int k = 0; k < GW; ++k) {
 #pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((pend[j] >> s) & 1u)
-                    if (l128_flag_ok(F[j][s], flag))
-                        pend[j] &= ~(1u << s);
-            any |= pend[j];
+            for (int j = 0; j < PW; ++j)
+                if ((pend[k] >> j) & 1u)
+                    if (l128_flag_ok(F[k][j], flag))
+                        pend[k] &= ~(1u << j);
+            any |= pend[k];
         }
         if (!wave_any(any != 0u))
             break;
-        if (w.expired(ctl, rank, any ? first_bit(any) : 0u, flag))
+        if (w.expired(ctl, rank, any ? wave + L128_WAVES * first_bit(any) : 0u, flag))
             return false;
         compiler_fence();
 #pragma unroll
-        for (int j = 0; j < GB; ++j)
+        for (int k = 0; k < GW; ++k)
 #pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((pend[j] >> s) & 1u)
-                    F[j][s] = ld8<Pol<LOCAL>::LD>(reg, off(j, s) + 8u);
+            for (int j = 0; j < PW; ++j)
+                if ((pend[k] >> j) & 1u)
+                    F[k][j] = ld8<Pol<LOCAL>::LD>(reg, off(k, j) + 8u);
     }
     // every needed line is complete: load the payloads
     compiler_fence();
 #pragma unroll
-    for (int j = 0; j < GB; ++j) {
-        if (!((gvalid >> j) & 1u))
+    for (int k = 0; k < GW; ++k) {
+        if (!((gvalid >> k) & 1u))
             continue;
-        const uint32_t e = g[j] * L128_ELEMS + ln.elem;
+        const uint32_t e = g[k] * L128_ELEMS + ln.elem;
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s) {
-            if ((uint32_t)s < N && (uint32_t)s != skip && e < lim[s]) {
+        for (int j = 0; j < PW; ++j) {
+            if (((pmask >> j) & 1u) && e < lim[j]) {
                 if (ln.half) {
-                    const u32x2 p = ld8<Pol<LOCAL>::LD>(reg, off(j, s));
-                    V[j][s].x = p.x; V[j][s].y = p.y; V[j][s].z = 0u; V[j][s].w = 0u;
+                    const u32x2 p = ld8<Pol<LOCAL>::LD>(reg, off(k, j));
+                    V[k][j].x = p.x; V[k][j].y = p.y; V[k][j].z = 0u; V[k][j].w = 0u;
                 } else {
-                    V[j][s] = ld16<Pol<LOCAL>::LD>(reg, off(j, s));
+                    V[k][j] = ld16<Pol<LOCAL>::LD>(reg, off(k, j));
                 }
             }
         }
@@ -944,21 +950,25 @@ __device__ __forceinline__ void store_lane(__amdgpu_buffer_rsrc_t o, uint32_t e,
 }
 
 // ====================================================== one-shot LL128
-// Rank r publishes its whole input as line groups; a wave owns the groups
-// g0, g0 + gstep, ... and handles them GB at a time: publish all payloads,
-// one acknowledgement wait, all flags; then receive and reduce.
+// Rank r publishes its whole input as line groups.  Batch b of a workgroup
+// covers groups (part + b*parts)*GW + k, k < GW; wave k < GW publishes
+// group k.  Every wave receives the batch from its peers into an LDS tile
+// [N][GW][64 lanes]; after a workgroup barrier each publishing wave reduces
+// its group in global rank order and writes it.
 template <int NMAX, bool F32, bool LOCAL>
 __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 {
-    constexpr int GB = GroupsPerBatch<NMAX>::value;
+    constexpr int GW = GroupsPerBatch<NMAX>::value;
+    constexpr int PW = (NMAX + L128_WAVES - 1) / L128_WAVES;
+    __shared__ u32x4 stage[NMAX][GW][64];
+    __shared__ uint32_t failed;
     Ctx0 c;
     begin<LOCAL>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t waves = blockDim.x >> 6;
     const uint32_t groups = (a.n + L128_ELEMS - 1u) / L128_ELEMS;
-    const uint32_t gstep = a.parts * waves;
+    const uint32_t batches = (groups + GW - 1u) / GW;
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     const L128Lane ln = l128_lane(lane);
@@ -966,52 +976,68 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
     const uint32_t rb = a.l128_stride;
     const __amdgpu_buffer_rsrc_t reg = rsrc(a.l128, N * 2u * rb);
-    const uint32_t mine = (c.rank * 2u + c.par) * rb;
-    uint32_t lim[NMAX];
+    const uint32_t mine_off = (c.rank * 2u + c.par) * rb;
+    uint32_t pmask = 0, lim[PW];
 #pragma unroll
-    for (int s = 0; s < NMAX; ++s)
-        lim[s] = a.n;
+    for (int j = 0; j < PW; ++j) {
+        const uint32_t s = wave + (uint32_t)(L128_WAVES * j);
+        lim[j] = a.n;
+        if (s < N && s != c.rank)
+            pmask |= 1u << j;
+    }
+    if (threadIdx.x == 0)
+        failed = 0u;
     start_delay(a, c);
 
-    for (uint32_t base = c.part * waves + wave; base < groups; base += gstep * GB) {
-        uint32_t g[GB];
+    for (uint32_t b = c.part; b < batches; b += a.parts) {
+        uint32_t g[GW];
         uint32_t gvalid = 0;
-        u32x4 x[GB];
 #pragma unroll
-        for (int j = 0; j < GB; ++j) {
-            g[j] = base + (uint32_t)j * gstep;
-            if (g[j] < groups)
-                gvalid |= 1u << j;
-            const uint32_t e = g[j] * L128_ELEMS + ln.elem;
-            x[j] = (g[j] < groups && e < a.n) ? ld_elems(inr, e, ln.half) : u32x4{0u, 0u, 0u, 0u};
+        for (int k = 0; k < GW; ++k) {
+            g[k] = b * GW + (uint32_t)k;
+            if (g[k] < groups)
+                gvalid |= 1u << k;
         }
+        // publish: wave k < GW owns group g[k]
+        const bool pub = wave < (uint32_t)GW && ((gvalid >> wave) & 1u);
+        const uint32_t gm = b * GW + wave;
+        const uint32_t em = gm * L128_ELEMS + ln.elem;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (pub) {
+            if (em < a.n)
+                x = ld_elems(inr, em, ln.half);
+            l128_store_payload<LOCAL>(reg, mine_off + gm * L128_BYTES + lane * 16u, ln.half, x);
+            wait_stores();
+            if (ln.half)
+                l128_store_flag<LOCAL>(reg, mine_off + gm * L128_BYTES + lane * 16u, c.flag);
+            stage[c.rank][wave][lane] = x;
+        }
+        // receive the batch from this wave's peers
+        u32x4 V[GW][PW];
+        if (!l128_recv<GW, PW, LOCAL>(reg, rb, c.par, g, gvalid, pmask, wave, lane, ln, lim,
+                                      c.flag, ctl, c.rank, a.watchdog_ticks, V))
+            failed = 1u;                            // every wave still meets the barrier
 #pragma unroll
-        for (int j = 0; j < GB; ++j)
-            if ((gvalid >> j) & 1u)
-                l128_store_payload<LOCAL>(reg, mine + g[j] * L128_BYTES + lane * 16u, ln.half, x[j]);
-        wait_stores();
+        for (int k = 0; k < GW; ++k)
+            if ((gvalid >> k) & 1u)
 #pragma unroll
-        for (int j = 0; j < GB; ++j)
-            if (((gvalid >> j) & 1u) && ln.half)
-                l128_store_flag<LOCAL>(reg, mine + g[j] * L128_BYTES + lane * 16u, c.flag);
-        u32x4 V[GB][NMAX];
-        if (!l128_receive<NMAX, LOCAL>(reg, rb, c.par, N, c.rank, g, gvalid, lane, ln, lim, c.flag, ctl,
-                                c.rank, a.watchdog_ticks, V))
+                for (int j = 0; j < PW; ++j)
+                    if ((pmask >> j) & 1u)
+                        stage[wave + L128_WAVES * j][k][lane] = V[k][j];
+        __syncthreads();
+        if (failed)
             return;
-#pragma unroll
-        for (int j = 0; j < GB; ++j) {
-            const uint32_t e = g[j] * L128_ELEMS + ln.elem;
-            if (!((gvalid >> j) & 1u) || e >= a.n)
-                continue;
+        if (pub && em < a.n) {
             Acc8 acc;
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((uint32_t)s < N) {
-                    const u32x4 v = ((uint32_t)s == c.rank) ? x[j] : V[j][s];
+                    const u32x4 v = stage[s][wave][lane];
                     if (s == 0) acc.init(v); else acc.add(v);
                 }
-            store_lane<F32>(o, e, ln.half, acc);
+            store_lane<F32>(o, em, ln.half, acc);
         }
+        __syncthreads();                            // the tile is reused next batch
     }
     finish(a, c);
 }
@@ -1020,12 +1046,14 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 // Reduce-scatter: rank q reduces slice q (elements [q*L, q*L + Lq)) reading
 // every rank's input in place after the arrival flags, and publishes the
 // bf16 result as line groups.  All-gather: rank q receives every slice's
-// groups (its own from registers) and writes them to out[q].  Groups are
-// handled GB at a time per wave as in the one-shot kernel.
+// groups (its own from registers) and writes them to out[q].  Batches and
+// publishing waves as in the one-shot kernel; wave w receives the batch of
+// the slices of the peers s with s % 4 == w straight into out[q].
 template <int NMAX, bool F32, bool LOCAL>
 __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 {
-    constexpr int GB = GroupsPerBatch<NMAX>::value;
+    constexpr int GW = GroupsPerBatch<NMAX>::value;
+    constexpr int PW = (NMAX + L128_WAVES - 1) / L128_WAVES;
     Ctx0 c;
     begin<LOCAL>(a, c);
     const uint32_t N = a.n_ranks;
@@ -1033,9 +1061,8 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
     const uint32_t L = a.slice;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t waves = blockDim.x >> 6;
     const uint32_t groups = (L + L128_ELEMS - 1u) / L128_ELEMS;
-    const uint32_t gstep = a.parts * waves;
+    const uint32_t batches = (groups + GW - 1u) / GW;
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     const L128Lane ln = l128_lane(lane);
@@ -1043,87 +1070,93 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
     raise_arrival<LOCAL>(a, c);
     if (!wait_arrivals<LOCAL>(a, c, ctl))
         return;
-    uint32_t lim[NMAX];
-    __amdgpu_buffer_rsrc_t inp[NMAX];
-#pragma unroll
-    for (int s = 0; s < NMAX; ++s) {
-        const uint32_t ss = (uint32_t)s < N ? (uint32_t)s : 0u;
-        inp[s] = in_rsrc(a, ss);
-        const uint32_t slo = ss * L;
-        lim[s] = ((uint32_t)s >= N || slo >= a.n) ? 0u : (a.n - slo < L ? a.n - slo : L);
-    }
-    const uint32_t Lq = (q * L >= a.n) ? 0u : (a.n - q * L < L ? a.n - q * L : L);
+    auto slice_len = [&](uint32_t s) -> uint32_t {
+        const uint32_t lo = s * L;
+        return (s >= N || lo >= a.n) ? 0u : (a.n - lo < L ? a.n - lo : L);
+    };
+    const uint32_t Lq = slice_len(q);
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, q, F32);
     const uint32_t rb = a.l128_stride;
     const __amdgpu_buffer_rsrc_t reg = rsrc(a.l128, N * 2u * rb);
-    const uint32_t mine = (q * 2u + c.par) * rb;
+    const uint32_t mine_off = (q * 2u + c.par) * rb;
+    uint32_t pmask = 0, lim[PW];
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+        const uint32_t s = wave + (uint32_t)(L128_WAVES * j);
+        lim[j] = slice_len(s);
+        if (s < N && s != q)
+            pmask |= 1u << j;
+    }
 
-    for (uint32_t base = c.part * waves + wave; base < groups; base += gstep * GB) {
-        uint32_t g[GB];
+    for (uint32_t b = c.part; b < batches; b += a.parts) {
+        uint32_t g[GW];
         uint32_t gvalid = 0;
 #pragma unroll
-        for (int j = 0; j < GB; ++j) {
-            g[j] = base + (uint32_t)j * gstep;
-            if (g[j] < groups)
-                gvalid |= 1u << j;
+        for (int k = 0; k < GW; ++k) {
+            g[k] = b * GW + (uint32_t)k;
+            if (g[k] < groups)
+                gvalid |= 1u << k;
         }
-        // ---- reduce-scatter of up to GB groups
-        u32x4 red[GB];
+        // ---- reduce-scatter of this wave's group, publish, own copy
+        const bool pub = wave < (uint32_t)GW && ((gvalid >> wave) & 1u);
+        const uint32_t gm = b * GW + wave;
+        const uint32_t em = gm * L128_ELEMS + ln.elem;
+        if (pub) {
+            u32x4 red = {0u, 0u, 0u, 0u};
+            if (em < Lq) {
+                u32x4 V[NMAX];
 #pragma unroll
-        for (int j = 0; j < GB; ++j) {
-            red[j] = u32x4{0u, 0u, 0u, 0u};
-            const uint32_t e = g[j] * L128_ELEMS + ln.elem;
-            if (!((gvalid >> j) & 1u) || e >= Lq)
-                continue;
-            u32x4 V[NMAX];
+                for (int s = 0; s < NMAX; ++s)
+                    if ((uint32_t)s < N)
+                        V[s] = ld_elems<CP_DEV>(in_rsrc(a, (uint32_t)s), q * L + em, ln.half);
+                Acc8 acc;
 #pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((uint32_t)s < N)
-                    V[s] = ld_elems<CP_DEV>(inp[s], q * L + e, ln.half);
-            Acc8 acc;
-#pragma unroll
-            for (int s = 0; s < NMAX; ++s)
-                if ((uint32_t)s < N) {
-                    if (s == 0) acc.init(V[s]); else acc.add(V[s]);
+                for (int s = 0; s < NMAX; ++s)
+                    if ((uint32_t)s < N) {
+                        if (s == 0) acc.init(V[s]); else acc.add(V[s]);
+                    }
+                if constexpr (F32) {
+                    // debug path: the owner writes its slice's accumulators to every copy
+                    for (uint32_t r = 0; r < N; ++r)
+                        store_lane<true>(out_all(a, true), r * a.n + q * L + em, ln.half, acc);
+                } else {
+                    red = acc.bf16();
+                    if (ln.half) {
+                        u32x2 p; p.x = red.x; p.y = red.y;
+                        st8<CP_PLAIN>(p, o, (q * L + em) * 2u);
+                    } else {
+                        st16<CP_PLAIN>(red, o, (q * L + em) * 2u);
+                    }
                 }
-            if constexpr (F32) {
-                // debug path: the owner writes its slice's accumulators to every copy
-                for (uint32_t r = 0; r < N; ++r)
-                    store_lane<true>(out_all(a, true), r * a.n + q * L + e, ln.half, acc);
-            } else {
-                red[j] = acc.bf16();
+            }
+            if constexpr (!F32) {
+                l128_store_payload<LOCAL>(reg, mine_off + gm * L128_BYTES + lane * 16u, ln.half, red);
+                wait_stores();
+                if (ln.half)
+                    l128_store_flag<LOCAL>(reg, mine_off + gm * L128_BYTES + lane * 16u, c.flag);
             }
         }
         if constexpr (F32)
             continue;
-#pragma unroll
-        for (int j = 0; j < GB; ++j)
-            if ((gvalid >> j) & 1u)
-                l128_store_payload<LOCAL>(reg, mine + g[j] * L128_BYTES + lane * 16u, ln.half, red[j]);
-        wait_stores();
-#pragma unroll
-        for (int j = 0; j < GB; ++j)
-            if (((gvalid >> j) & 1u) && ln.half)
-                l128_store_flag<LOCAL>(reg, mine + g[j] * L128_BYTES + lane * 16u, c.flag);
-        // ---- all-gather of the same groups
-        u32x4 V[GB][NMAX];
-        if (!l128_receive<NMAX, LOCAL>(reg, rb, c.par, N, q, g, gvalid, lane, ln, lim, c.flag, ctl, q,
-                                a.watchdog_ticks, V))
+        // ---- all-gather of the batch from this wave's peers
+        u32x4 V[GW][PW];
+        if (!l128_recv<GW, PW, LOCAL>(reg, rb, c.par, g, gvalid, pmask, wave, lane, ln, lim,
+                                      c.flag, ctl, q, a.watchdog_ticks, V))
             return;
 #pragma unroll
-        for (int j = 0; j < GB; ++j) {
-            if (!((gvalid >> j) & 1u))
+        for (int k = 0; k < GW; ++k) {
+            if (!((gvalid >> k) & 1u))
                 continue;
-            const uint32_t e = g[j] * L128_ELEMS + ln.elem;
+            const uint32_t e = g[k] * L128_ELEMS + ln.elem;
 #pragma unroll
-            for (int s = 0; s < NMAX; ++s) {
-                if ((uint32_t)s < N && e < lim[s]) {
-                    const u32x4 v = ((uint32_t)s == q) ? red[j] : V[j][s];
+            for (int j = 0; j < PW; ++j) {
+                const uint32_t s = wave + (uint32_t)(L128_WAVES * j);
+                if (((pmask >> j) & 1u) && e < lim[j]) {
                     if (ln.half) {
-                        u32x2 p; p.x = v.x; p.y = v.y;
-                        st8<CP_PLAIN>(p, o, ((uint32_t)s * L + e) * 2u);
+                        u32x2 p; p.x = V[k][j].x; p.y = V[k][j].y;
+                        st8<CP_PLAIN>(p, o, (s * L + e) * 2u);
                     } else {
-                        st16<CP_PLAIN>(v, o, ((uint32_t)s * L + e) * 2u);
+                        st16<CP_PLAIN>(V[k][j], o, (s * L + e) * 2u);
                     }
                 }
             }
