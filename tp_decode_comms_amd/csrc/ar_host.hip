@@ -50,7 +50,7 @@ struct Context {
     uint64_t *ts = nullptr; size_t ts_slots = 0;
     // sequence
     uint32_t last_epoch = 0;
-    int capacity[ar::K_COUNT][2][3] = {};   // resident workgroups [kind][f32][64,128,256 threads]
+    int capacity[ar::K_COUNT][2][5] = {};   // resident workgroups [kind][f32][64..1024 threads]
     bool cap_ready = false;
 };
 
@@ -126,25 +126,38 @@ hipError_t rearm(hipStream_t s)
     return ar::launch_fill(g.ctl, ar::CTL_WORDS, 0u, s);
 }
 
-int thread_index(int threads) { return threads == 64 ? 0 : threads == 128 ? 1 : 2; }
+int thread_index(int threads)
+{
+    return threads <= 64 ? 0 : threads <= 128 ? 1 : threads <= 256 ? 2 : threads <= 512 ? 3 : 4;
+}
 
 int compute_capacity()
 {
-    const int tcounts[3] = {64, 128, 256};
+    const int tcounts[5] = {64, 128, 256, 512, 1024};
     for (int k = 0; k < ar::K_COUNT; ++k) {
         for (int f = 0; f < 2; ++f) {
-            for (int t = 0; t < 3; ++t) {
+            for (int t = 0; t < 5; ++t) {
                 int per_cu = 0;
                 hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
                     &per_cu, ar::kernel_for(k, g.n_ranks, f == 1, false), tcounts[t], 0);
+                if (e != hipSuccess && t >= 3) {
+                    // block sizes above a kernel's launch bound: unusable
+                    (void)hipGetLastError();
+                    g.capacity[k][f][t] = 0;
+                    continue;
+                }
                 if (e != hipSuccess)
                     return hip_fail(e);
                 if (f == 0) {           // bf16: the XCD-local variant too
                     int per_cu_local = 0;
                     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
                         &per_cu_local, ar::kernel_for(k, g.n_ranks, false, true), tcounts[t], 0);
-                    if (e != hipSuccess)
+                    if (e != hipSuccess && t >= 3) {
+                        (void)hipGetLastError();
+                        per_cu_local = 0;
+                    } else if (e != hipSuccess) {
                         return hip_fail(e);
+                    }
                     per_cu = std::min(per_cu, per_cu_local);
                 }
                 g.capacity[k][f][t] = per_cu * g.cu_count;
@@ -210,8 +223,12 @@ int make_plan(size_t n, bool f32, Plan *p)
     const uint32_t N = (uint32_t)g.n_ranks;
     p->slice = (uint32_t)slice_len(n, g.n_ranks);
     const bool l128 = p->kind == ar::K_ONESHOT_LL128 || p->kind == ar::K_TWOSHOT_LL128;
-    if (p->kind == ar::K_ONESHOT_LL || p->kind == ar::K_ONESHOT_SENTINEL ||
-        p->kind == ar::K_TWOSHOT_SENTINEL || l128)
+    if (p->kind == ar::K_ONESHOT_LL) {
+        // one wave per rank (a power of two >= N): each wave receives one peer
+        uint32_t w = 1;
+        while (w < N) w <<= 1;
+        p->threads = 64 * w;
+    } else if (p->kind == ar::K_ONESHOT_SENTINEL || p->kind == ar::K_TWOSHOT_SENTINEL || l128)
         p->threads = 256;               // 4 waves share the peers of a tile
     else if (g.threads > 0)
         p->threads = (uint32_t)g.threads;

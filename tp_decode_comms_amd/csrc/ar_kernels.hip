@@ -219,25 +219,23 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
 // [r][parity]; every rank reads it.  All mailboxes sit in one region
 // [rank][parity] x ll_stride under one descriptor.
 //
-// A workgroup of LL_WAVES waves owns 64 chunks per round.  Wave 0 loads the
-// input and publishes it; once the publish is acknowledged, wave w receives
-// the peers s with s % LL_WAVES == w and stages their units in LDS (the
-// peer tiles, [N][64] x 8 bytes); after a workgroup barrier wave 0 reduces
-// the N units of each chunk from LDS in global rank order and writes the
-// result.  Splitting the peers over the waves matters on this chip: a poll
-// of lines written during the launch costs about 60 ns per load instruction
-// on top of the L2 latency, so 7 peers polled by one wave take ~0.85 us and
-// 2 per wave ~0.5 us.  Each wave's receive keeps two batches of loads in
-// flight: while one batch is checked the next is already on its way.
-constexpr int LL_WAVES = 4;
-
+// A workgroup of W >= N waves (one per rank, a power of two) owns 64
+// chunks per round.  Wave 0 loads the input and publishes it; once the
+// publish is acknowledged, wave s receives peer s and stages its units in
+// LDS (the peer tiles, [N][64] x 8 bytes); after a workgroup barrier wave 0
+// reduces the N units of each chunk from LDS in global rank order and
+// writes the result.  Splitting the peers over the waves matters on this
+// chip: a poll of lines written during the launch costs about 60 ns per
+// load instruction on top of the L2 latency, so 7 peers polled by one wave
+// take ~0.85 us, 2 per wave ~0.55 us and 1 per wave ~0.4 us.  Each wave's
+// receive keeps two loads in flight: while one is checked the next is
+// already on its way.
 template <int NMAX, bool F32, bool LOCAL>
 __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
                                          __amdgpu_buffer_rsrc_t llr, __amdgpu_buffer_rsrc_t o,
                                          uint32_t ch, uint32_t C, u32x2 x, u32x2 (*stage)[64],
                                          uint32_t *failed)
 {
-    constexpr int PW = (NMAX + LL_WAVES - 1) / LL_WAVES;   // peer slots per wave
     const uint32_t N = a.n_ranks;
     const uint32_t rb = a.ll_stride;
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
@@ -253,57 +251,42 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
     // polls start once the publish is acknowledged: an earlier poll mostly
     // returns stale data and costs a second round trip
     __syncthreads();
-    // receive (recv): this wave's peers s = wave + LL_WAVES * j
-    uint32_t pend = 0;
-#pragma unroll
-    for (int j = 0; j < PW; ++j) {
-        const uint32_t s = wave + (uint32_t)(LL_WAVES * j);
-        if (s < N && s != c.rank && active)
-            pend |= 1u << j;
-    }
-    u32x4 A0[PW], A1[PW];
-    u32x2 V[PW];
-    auto issue = [&](u32x4 *A) {
-#pragma unroll
-        for (int j = 0; j < PW; ++j)
-            if ((pend >> j) & 1u)
-                A[j] = ld16<Pol<LOCAL>::LD>(llr, lane_off +
-                                            (wave + (uint32_t)(LL_WAVES * j)) * 2u * rb);
-    };
-    auto check = [&](const u32x4 *A) {
-#pragma unroll
-        for (int j = 0; j < PW; ++j)
-            if ((pend >> j) & 1u)
-                if (ll_ready(A[j], c.flag)) {
-                    pend &= ~(1u << j);
-                    V[j].x = A[j].x;
-                    V[j].y = A[j].z;
-                }
-    };
-    uint32_t mine = pend;                           // slots this lane stages
+    // receive (recv): this wave's peer is rank `wave`
+    const bool mine = wave < N && wave != c.rank && active;
+    bool pend = mine;
+    const uint32_t src = lane_off + wave * 2u * rb;
+    u32x4 A0, A1;
+    u32x2 V = {0u, 0u};
     Watch w;
     w.begin(a.watchdog_ticks);
-    issue(A0);
+    if (pend)
+        A0 = ld16<Pol<LOCAL>::LD>(llr, src);
     while (true) {
         compiler_fence();
-        issue(A1);
-        check(A0);
-        if (!wave_any(pend != 0u))
+        if (pend)
+            A1 = ld16<Pol<LOCAL>::LD>(llr, src);
+        if (pend && ll_ready(A0, c.flag)) {
+            pend = false;
+            V.x = A0.x; V.y = A0.z;
+        }
+        if (!wave_any(pend))
             break;
-        if (w.expired(ctl, c.rank, pend ? wave + LL_WAVES * first_bit(pend) : 0u, c.flag)) {
+        if (w.expired(ctl, c.rank, wave, c.flag)) {
             *failed = 1u;                           // every wave still meets the barrier
             break;
         }
         compiler_fence();
-        issue(A0);
-        check(A1);
-        if (!wave_any(pend != 0u))
+        if (pend)
+            A0 = ld16<Pol<LOCAL>::LD>(llr, src);
+        if (pend && ll_ready(A1, c.flag)) {
+            pend = false;
+            V.x = A1.x; V.y = A1.z;
+        }
+        if (!wave_any(pend))
             break;
     }
-#pragma unroll
-    for (int j = 0; j < PW; ++j)
-        if ((mine >> j) & 1u)
-            stage[wave + LL_WAVES * j][lane] = V[j];
+    if (mine)
+        stage[wave][lane] = V;
     __syncthreads();
     if (*failed)
         return false;
@@ -324,7 +307,7 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
 }
 
 template <int NMAX, bool F32, bool LOCAL>
-__global__ __launch_bounds__(256) void k_oneshot_ll(const Launch a)
+__global__ __launch_bounds__(1024) void k_oneshot_ll(const Launch a)
 {
     __shared__ u32x2 stage[NMAX][64];
     __shared__ uint32_t failed;
@@ -334,6 +317,11 @@ __global__ __launch_bounds__(256) void k_oneshot_ll(const Launch a)
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t step = a.parts * 64u;
     const uint32_t rounds = (C + step - 1u) / step;
+    if ((blockDim.x >> 6) < a.n_ranks) {            // the host launches a wave per rank
+        if (threadIdx.x == 0)                       // (never otherwise: report, do nothing)
+            Ctl{a.ctl}.fail(c.rank, blockDim.x, a.epoch);
+        return;
+    }
     const __amdgpu_buffer_rsrc_t inr = in_rsrc(a, c.rank);
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
     if (threadIdx.x == 0)
