@@ -49,6 +49,9 @@ def lib():
             L.oracle_allreduce_f32.restype = None
             L.oracle_max_threads.argtypes = []
             L.oracle_max_threads.restype = ctypes.c_int
+            L.oracle_gemv_f64.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int]
+            L.oracle_gemv_f64.restype = None
             _lib = L
         return _lib
 
@@ -103,3 +106,15 @@ def f32_add_bits(a: int, b: int) -> int:
 
 def max_threads() -> int:
     return int(lib().oracle_max_threads())
+
+
+def gemv(W, x, threads=0):
+    """y[m] = sum_k W[m,k] * x[k] for bf16 patterns W [M, K] and x [K], as
+    binary64 (the exact products summed in order; see ar_oracle.c)."""
+    W = np.ascontiguousarray(W, dtype=np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    M, K = W.shape
+    assert x.shape == (K,)
+    y = np.empty(M, dtype=np.float64)
+    lib().oracle_gemv_f64(W.ctypes.data, x.ctypes.data, M, K, y.ctypes.data, int(threads))
+    return y

@@ -140,3 +140,35 @@ int oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Decode-step projection feeding the AllReduce (the overlap harness's
+ * compute step).  In a tensor-parallel decode layer each rank multiplies its
+ * weight shard by its share of the activation and the AllReduce sums the
+ * per-rank partial products ("vLLM 分布式推理核心" page, section 一: the
+ * row-parallel layers end in an AllReduce).  For one rank:
+ *
+ *   y[m] = sum over k of W[m][k] * x[k]      W: [M][K] bf16 row-major, x: [K]
+ *
+ * The definition is the exact real sum.  Computed here in binary64: every
+ * product of two bfloat16 values (8-bit significands) is exact in binary64,
+ * and the sequential sum over k adds at most K rounding errors of 2^-53
+ * each, far below anything a binary32 kernel can resolve.
+ */
+void oracle_gemv_f64(const uint16_t *W, const uint16_t *x, size_t M, size_t K, double *y,
+                     int threads)
+{
+    long long m;
+#ifdef _OPENMP
+    if (threads > 0)
+        omp_set_num_threads(threads);
+#pragma omp parallel for schedule(static) if (threads != 1)
+#endif
+    for (m = 0; m < (long long)M; ++m) {
+        double s = 0.0;
+        for (size_t k = 0; k < K; ++k)
+            s += (double)widen_bf16(W[(size_t)m * K + k]) * (double)widen_bf16(x[k]);
+        y[m] = s;
+    }
+    (void)threads;
+}
