@@ -21,7 +21,7 @@ per-call intervals end(k) - end(k-1) (launch gap included) and spans
 end(k) - start(k).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
-                       [--only latency|bw|configs|calib]
+                       [--only latency|bw|overlap|configs|calib]
 """
 import argparse
 import json
@@ -240,6 +240,99 @@ def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label):
     }
 
 
+def bench_overlap(torch, ar, layers=20, replays=10, warmup=2):
+    """Compute/communication overlap harness: the decode projection (bf16
+    GEMV, 8 ranks x [8192 x 1024], the step that produces the AllReduce
+    input) and the 16 KiB/rank LL AllReduce, each alone, chained (projection
+    -> AllReduce per layer on one stream) and concurrent on two streams
+    (independent data; fork/join events inside one hipGraph)."""
+    import synth
+    N, M, K = 8, 8192, 1024
+    rng = np.random.default_rng(20261202)
+    mk = lambda a: to_dev(torch, (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16))
+    Wd = [mk(rng.normal(0.0, 1.0 / np.sqrt(K), size=(M, K))) for _ in range(N)]
+    xd = [mk(rng.normal(0.0, 1.0, size=K)) for _ in range(N)]
+    yd = [torch.empty(M, dtype=torch.int16, device="cuda:0") for _ in range(N)]
+    wl = Workload(torch, 2, 4)
+    outs = [torch.empty((N, M), dtype=torch.int16, device="cuda:0") for _ in range(layers)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ar.init(N, M)
+    ar.set_options(ONE, LL)
+
+    def timed(build):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s1):
+            with torch.cuda.graph(g, stream=s1):
+                build()
+        with torch.cuda.stream(s1):
+            for _ in range(warmup):
+                g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(replays)]
+        with torch.cuda.stream(s1):
+            for a, b in ev:
+                a.record(s1)
+                g.replay()
+                b.record(s1)
+        torch.cuda.synchronize()
+        del g
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1000.0 / layers
+
+    def gemvs(stream, cap=0):
+        for _ in range(layers):
+            ar.gemv(Wd, xd, yd, M, K, stream=stream, max_workgroups=cap)
+
+    def ars(stream, src):
+        for k in range(layers):
+            ar.allreduce(src(k), outs[k], M, k + 1, stream=stream)
+        ar.step_end(stream=stream)
+
+    def chain():
+        for k in range(layers):
+            ar.gemv(Wd, xd, yd, M, K, stream=s1)
+            ar.allreduce(yd, outs[k], M, k + 1, stream=s1)
+        ar.step_end(stream=s1)
+
+    def concurrent(cap):
+        fork = torch.cuda.Event()
+        fork.record(s1)
+        s2.wait_event(fork)
+        gemvs(s1, cap)
+        ars(s2, lambda k: wl.ins[k % len(wl.ins)])
+        join = torch.cuda.Event()
+        join.record(s2)
+        s1.wait_event(join)
+
+    # the budgeted projection keeps to half the wave slots of the GPU, leaving
+    # room for the AllReduce's 256 workgroups of 8 waves
+    budget = 1024
+    t_gemv = timed(lambda: gemvs(s1))
+    t_gemv_b = timed(lambda: gemvs(s1, budget))
+    t_ar = timed(lambda: ars(s1, lambda k: wl.ins[k % len(wl.ins)]))
+    t_chain = timed(chain)
+    t_both = timed(lambda: concurrent(0))
+    t_both_b = timed(lambda: concurrent(budget))
+    bad = wl.check([(outs[k], k % len(wl.ins)) for k in range(layers)])
+    status = ar.get_status()
+    ar.destroy()
+    gemv_bytes = N * M * K * 2
+    return {
+        "workload": "decode projection 8 ranks x bf16 [8192 x 1024] (16 MiB of weights per rank) "
+                    "and 8 ranks x 16 KiB one-shot LL AllReduce, %d layers per hipGraph" % layers,
+        "gemv_us": round(t_gemv, 3), "gemv_gbps": round(gemv_bytes / (t_gemv * 1e-6) / 1e9, 1),
+        "allreduce_us": round(t_ar, 3),
+        "chained_layer_us": round(t_chain, 3),
+        "concurrent_pair_us": round(t_both, 3),
+        "hidden_fraction_of_allreduce": round((t_gemv + t_ar - t_both) / t_ar, 3),
+        "gemv_budgeted_workgroups": budget,
+        "gemv_budgeted_us": round(t_gemv_b, 3),
+        "concurrent_pair_budgeted_us": round(t_both_b, 3),
+        "hidden_fraction_budgeted": round((t_gemv_b + t_ar - t_both_b) / t_ar, 3),
+        "mismatches": bad, "status": list(status),
+    }
+
+
 def kernel_source_sha():
     import hashlib
     csrc = os.path.join(ROOT, "tp_decode_comms_amd", "csrc")
@@ -317,7 +410,8 @@ def main():
     ap.add_argument("--bw-calls", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quick", action="store_true")
-    ap.add_argument("--only", default="all", choices=["all", "latency", "bw", "configs", "calib"])
+    ap.add_argument("--only", default="all",
+                    choices=["all", "latency", "bw", "overlap", "configs", "calib"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the N ranks are emulated as workgroup sets of one "
@@ -392,6 +486,10 @@ def main():
             results["bw_4m_twoshot_barrier"]["us_per_call"]["p50"] -
             results["bw_4m_twoshot_direct"]["us_per_call"]["p50"], 4)
         del wl4
+    if only in ("all", "overlap"):
+        log("overlap harness: projection GEMV and AllReduce")
+        results["overlap"] = bench_overlap(torch, ar, replays=3 if args.quick else 10)
+        log("  %r" % {k: v for k, v in results["overlap"].items() if k != "workload"})
     if only in ("all", "configs"):
         reps = 3 if args.quick else 10
         wl1 = Workload(torch, 1, 4)

@@ -1,4 +1,4 @@
-"""The C-ABI library loads and exports every entry point include/ar.h
+"""The C-ABI library loads and exports every entry point include/*.h
 declares, and its host-side validation works without a GPU (no compute
 calls are made here)."""
 import ctypes
@@ -8,13 +8,16 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ar.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ar_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"\b(ar_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -66,3 +69,17 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(a, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         a.lib()
+
+
+def test_gemv_validation_without_device(lib):
+    import tp_decode_comms_amd.ar as a
+    P = ctypes.c_void_p * 1
+    good = P(16)
+    assert lib.ar_gemv_bf16(None, good, good, 8, 8, 1, 0, None) == a.AR_ERR_INVALID
+    assert lib.ar_gemv_bf16(good, good, good, 0, 8, 1, 0, None) == a.AR_ERR_INVALID   # M = 0
+    assert lib.ar_gemv_bf16(good, good, good, 8, 12, 1, 0, None) == a.AR_ERR_INVALID  # K % 8
+    assert lib.ar_gemv_bf16(good, good, good, 8, 8, 0, 0, None) == a.AR_ERR_INVALID   # n_ranks
+    assert lib.ar_gemv_bf16(good, good, good, 8, 8, 17, 0, None) == a.AR_ERR_INVALID
+    assert lib.ar_gemv_bf16(P(8), good, P(4096), 8, 8, 1, 0, None) == a.AR_ERR_INVALID  # unaligned W
+    assert lib.ar_gemv_bf16(good, good, P(16), 8, 8, 1, 0, None) == a.AR_ERR_INVALID  # y aliases W
+    assert lib.ar_gemv_bf16(good, good, P(4096), 8, 8, 1, -1, None) == a.AR_ERR_INVALID

@@ -44,6 +44,9 @@ _SIGS = {
     "ar_strerror": (ctypes.c_char_p, [_c_int]),
     "ar_last_hip_error": (_c_int, []),
     "ar_query": (ctypes.c_longlong, [_c_int, _c_size]),
+    # include/ar_gemv.h (compute step of the overlap harness)
+    "ar_gemv_bf16": (_c_int, [ctypes.POINTER(_c_vp), ctypes.POINTER(_c_vp), ctypes.POINTER(_c_vp),
+                              _c_size, _c_size, _c_int, _c_int, _c_vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -131,6 +134,14 @@ def allreduce(rank_bufs, out, n, epoch, stream=None, check=True):
     rc = lib().ar_allreduce(_rank_array(rank_bufs), _ptr(out), int(n), int(epoch),
                             _stream_handle(stream))
     return _check("ar_allreduce", rc) if check else rc
+
+
+def gemv(weights, xs, ys, M, K, stream=None, max_workgroups=0, check=True):
+    """y_r = W_r x_r for every rank: weights N bf16 device tensors [M, K],
+    xs N bf16 [K], ys N bf16 [M] (include/ar_gemv.h)."""
+    rc = lib().ar_gemv_bf16(_rank_array(weights), _rank_array(xs), _rank_array(ys), int(M), int(K),
+                            len(weights), int(max_workgroups), _stream_handle(stream))
+    return _check("ar_gemv_bf16", rc) if check else rc
 
 
 def allreduce_f32_debug(rank_bufs, out_f32, n, epoch, stream=None, check=True):
