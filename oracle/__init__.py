@@ -52,6 +52,10 @@ def lib():
             L.oracle_gemv_f64.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                           ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int]
             L.oracle_gemv_f64.restype = None
+            L.oracle_add_rmsnorm.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p,
+                                             ctypes.c_void_p]
+            L.oracle_add_rmsnorm.restype = None
             _lib = L
         return _lib
 
@@ -118,3 +122,18 @@ def gemv(W, x, threads=0):
     y = np.empty(M, dtype=np.float64)
     lib().oracle_gemv_f64(W.ctypes.data, x.ctypes.data, M, K, y.ctypes.data, int(threads))
     return y
+
+
+def add_rmsnorm(a, res, gamma, eps):
+    """Residual add and RMS norm after the AllReduce (see ar_oracle.c):
+    returns (h bf16 patterns, y as unrounded binary64)."""
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    res = np.ascontiguousarray(res, dtype=np.uint16)
+    gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+    n = a.size
+    assert res.size == n and gamma.size == n
+    h = np.empty(n, dtype=np.uint16)
+    y = np.empty(n, dtype=np.float64)
+    lib().oracle_add_rmsnorm(a.ctypes.data, res.ctypes.data, gamma.ctypes.data, n, float(eps),
+                             h.ctypes.data, y.ctypes.data)
+    return h, y

@@ -33,6 +33,7 @@
 #include <stdint.h>
 #include <stddef.h>
 #include <string.h>
+#include <math.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -171,4 +172,37 @@ void oracle_gemv_f64(const uint16_t *W, const uint16_t *x, size_t M, size_t K, d
         y[m] = s;
     }
     (void)threads;
+}
+
+/*
+ * The op after the AllReduce in a decode layer ("vLLM 分布式推理核心" page,
+ * sections 一 and 二: the compute stream resumes with the next LayerNorm once
+ * the AllReduce completes).  The page names the op without defining it;
+ * reading used here: the residual add followed by the RMS form of the layer
+ * norm with a weight (no centring), as in the 70B-class decoders the page
+ * targets:
+ *
+ *   h[i] = bf16_rne( f32(a[i]) + f32(res[i]) )          a = the AllReduce result
+ *   y[i] = h[i] * gamma[i] / sqrt( (1/n) * sum_j h[j]^2 + eps )
+ *
+ * h is a plain binary32 addition rounded once, so it has one exact answer.
+ * y is returned unrounded in binary64 (h, gamma exact; the sum of squares of
+ * bf16 values is exact in binary64 up to n roundings of 2^-53); a kernel's
+ * bf16 result is held to one bf16 ulp of it.
+ */
+void oracle_add_rmsnorm(const uint16_t *a, const uint16_t *res, const uint16_t *gamma, size_t n,
+                        float eps, uint16_t *h_out, double *y_out)
+{
+    double ss = 0.0;
+    for (size_t i = 0; i < n; ++i) {
+        float s = widen_bf16(a[i]) + widen_bf16(res[i]);
+        uint32_t bits;
+        memcpy(&bits, &s, sizeof bits);
+        h_out[i] = oracle_f32_to_bf16(bits);
+        const double hv = (double)widen_bf16(h_out[i]);
+        ss += hv * hv;
+    }
+    const double inv = 1.0 / sqrt(ss / (double)n + (double)eps);
+    for (size_t i = 0; i < n; ++i)
+        y_out[i] = (double)widen_bf16(h_out[i]) * (double)widen_bf16(gamma[i]) * inv;
 }

@@ -17,7 +17,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11",
            "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra", "-Werror",
-           SRC, "-o", tmp]
+           SRC, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
