@@ -333,6 +333,96 @@ def bench_overlap(torch, ar, layers=20, replays=10, warmup=2):
     }
 
 
+def bench_norm(torch, ar, replays=20, warmup=3, layers=80):
+    """The AllReduce with the residual add + RMS norm fused into its launch
+    against the unfused sequence (AllReduce, then the stand-alone norm
+    kernel) and against the bare AllReduce, on the 16 KiB/rank decode shape:
+    160 calls (80 layers x 2) per hipGraph.  h must match the oracle bit for
+    bit, fused and unfused y must agree bit for bit, and y must lie within
+    one bf16 unit in the last place of the oracle's exact value."""
+    import oracle
+    import synth
+    N, n = 8, 8192
+    calls = 2 * layers
+    wl = Workload(torch, 2, 4)
+    res, gamma = synth.norm_operands(2, 0, replicated=True)
+    rs = [to_dev(torch, res[r]) for r in range(N)]
+    g = to_dev(torch, gamma)
+    eps = synth.NORM_EPS
+    mk = lambda: [torch.empty((N, n), dtype=torch.int16, device="cuda:0") for _ in range(4)]
+    outs, hs, ys, uh, uy = mk(), mk(), mk(), mk(), mk()
+    stream = torch.cuda.Stream()
+    ar.init(N, n)
+    ar.set_options(ONE, LL)
+
+    def timed(build):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(gr, stream=stream):
+                build()
+                ar.step_end(stream=stream)
+            for _ in range(warmup):
+                gr.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(replays)]
+        with torch.cuda.stream(stream):
+            for a, b in ev:
+                a.record(stream)
+                gr.replay()
+                b.record(stream)
+        torch.cuda.synchronize()
+        del gr
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1000.0 / calls
+
+    def bare():
+        for k in range(calls):
+            ar.allreduce(wl.ins[k % 4], outs[k % 4], n, k + 1, stream=stream)
+
+    def fused():
+        for k in range(calls):
+            ar.allreduce_add_rmsnorm(wl.ins[k % 4], rs, g, eps, hs[k % 4], ys[k % 4], 1, n, k + 1,
+                                     stream=stream)
+
+    def unfused():
+        for k in range(calls):
+            ar.allreduce(wl.ins[k % 4], outs[k % 4], n, k + 1, stream=stream)
+            ar.add_rmsnorm(outs[k % 4], rs, g, eps, uh[k % 4], uy[k % 4], 1, n, stream=stream)
+
+    t_bare = timed(bare)
+    t_fused = timed(fused)
+    t_unfused = timed(unfused)
+    status = ar.get_status()
+    ar.destroy()
+    bad = 0
+    worst_ulp = 0.0
+    for s in range(4):
+        a = oracle.allreduce(list(wl.data[s]))[0]
+        h_want, y_want = oracle.add_rmsnorm(a, res[0], gamma, eps)
+        for r in range(N):
+            h = hs[s][r].cpu().numpy().view(np.uint16)
+            y = ys[s][r].cpu().numpy().view(np.uint16)
+            bad += int((h != h_want).sum())
+            bad += int((y != uy[s][r].cpu().numpy().view(np.uint16)).sum())
+            bad += int((h != uh[s][r].cpu().numpy().view(np.uint16)).sum())
+            yv = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            ulp = np.ldexp(1.0, np.frexp(np.abs(y_want))[1] - 8)
+            worst_ulp = max(worst_ulp, float(np.max(np.abs(yv - y_want) / ulp)))
+    if worst_ulp > 1.0:
+        bad += 1
+    return {
+        "workload": "8 ranks x [1x8192] bf16 AllReduce + residual add + RMS norm (hidden 8192, "
+                    "eps %g), 160 calls per hipGraph" % eps,
+        "fused_us_per_call": round(t_fused, 4),
+        "unfused_us_per_call": round(t_unfused, 4),
+        "allreduce_only_us_per_call": round(t_bare, 4),
+        "norm_cost_fused_us": round(t_fused - t_bare, 4),
+        "norm_cost_unfused_us": round(t_unfused - t_bare, 4),
+        "y_max_ulp_vs_exact": round(worst_ulp, 4),
+        "mismatches": bad, "status": list(status),
+    }
+
+
 def kernel_source_sha():
     import hashlib
     csrc = os.path.join(ROOT, "tp_decode_comms_amd", "csrc")
@@ -411,7 +501,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quick", action="store_true")
     ap.add_argument("--only", default="all",
-                    choices=["all", "latency", "bw", "overlap", "configs", "calib"])
+                    choices=["all", "latency", "bw", "overlap", "norm", "configs", "calib"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the N ranks are emulated as workgroup sets of one "
@@ -490,6 +580,10 @@ def main():
         log("overlap harness: projection GEMV and AllReduce")
         results["overlap"] = bench_overlap(torch, ar, replays=3 if args.quick else 10)
         log("  %r" % {k: v for k, v in results["overlap"].items() if k != "workload"})
+    if only in ("all", "norm"):
+        log("fused AllReduce + residual add + RMS norm")
+        results["norm_16k"] = bench_norm(torch, ar, replays=5 if args.quick else 20)
+        log("  %r" % {k: v for k, v in results["norm_16k"].items() if k != "workload"})
     if only in ("all", "configs"):
         reps = 3 if args.quick else 10
         wl1 = Workload(torch, 1, 4)

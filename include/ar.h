@@ -133,6 +133,57 @@ int ar_allreduce(const void *const *rank_bufs, void *out, size_t n,
                  uint32_t epoch, hipStream_t stream);
 
 /*
+ * ar_allreduce_add_rmsnorm -- one AllReduce call (one-shot, LL protocol)
+ * with the operation that follows it in a decode layer fused into the same
+ * launch: the residual add and the RMS norm ("vLLM 分布式推理核心" page,
+ * section 一: after the AllReduce the compute stream resumes with the norm;
+ * the page names the op without defining it, and the weighted RMS form with
+ * a residual add is what is computed).  For every rank r and row i of
+ * `rows` rows of `hidden` elements (n = rows * hidden):
+ *     a       = the AllReduce result (bf16, bit-identical to ar_allreduce)
+ *     h[e]    = bf16_rne( f32(a[e]) + f32(residual_r[e]) )
+ *     y[e]    = bf16_rne( (f32(h[e]) * s_i) * f32(gamma[e mod hidden]) ),
+ *     s_i     = 1 / sqrt( S_i / hidden + eps ),  S_i = binary32 sum of h^2
+ *               over row i, in a fixed order that does not depend on the
+ *               launch geometry (256-element blocks of 64 x 4 elements).
+ *   rank_bufs: HOST array of n_ranks DEVICE pointers, bf16 [n] (as ar_allreduce).
+ *   residual:  HOST array of n_ranks DEVICE pointers, rank r's bf16 residual [n].
+ *   gamma:     DEVICE bf16 [hidden], the norm weight, shared by all ranks.
+ *   eps:       finite, >= 0.
+ *   out_h:     DEVICE bf16 [n_ranks][n], the updated residual stream h.
+ *   out_y:     DEVICE bf16 [n_ranks][n], the normalised rows y.
+ *   rows:      >= 1;  hidden: a multiple of 256, 256..65536;
+ *              rows * hidden <= max_elems.
+ *   epoch, stream: as ar_allreduce; the call takes the next epoch of the
+ *              same sequence, so it mixes freely with ar_allreduce calls.
+ * All pointers 16-byte aligned; out_h and out_y must overlap neither each
+ * other nor any input, residual or gamma.  The a values themselves are not
+ * written out.  h is exact; y is within one bf16 unit in the last place of
+ * the exact value (binary32 sum, division, square root and products).  The
+ * whole grid must be resident at once, so the launch stays within half the
+ * device's capacity.  No allocation, memset or host synchronisation.
+ * Errors: as ar_allreduce (AR_ERR_INVALID also for the norm operands).
+ */
+int ar_allreduce_add_rmsnorm(const void *const *rank_bufs, const void *const *residual,
+                             const void *gamma, float eps, void *out_h, void *out_y,
+                             size_t rows, size_t hidden, uint32_t epoch, hipStream_t stream);
+
+/*
+ * ar_add_rmsnorm -- the same residual add and RMS norm as a kernel of its
+ * own, applied to an AllReduce result already in memory (the unfused
+ * sequence: ar_allreduce, then this call).
+ *   a:         DEVICE bf16 [n_ranks][n], e.g. ar_allreduce's out.
+ *   residual, gamma, eps, out_h, out_y, rows, hidden: as ar_allreduce_add_rmsnorm;
+ *              out_h and out_y must not overlap a either.
+ * Needs an initialised context (for n_ranks and max_elems); uses no epoch.
+ * Same arithmetic and summation order as the fused call, so for the same a
+ * both give identical h and y.  One workgroup of 1024 threads per (rank, row).
+ * Errors: AR_ERR_NOT_INIT, AR_ERR_INVALID, AR_ERR_HIP.
+ */
+int ar_add_rmsnorm(const void *a, const void *const *residual, const void *gamma, float eps,
+                   void *out_h, void *out_y, size_t rows, size_t hidden, hipStream_t stream);
+
+/*
  * ar_allreduce_f32_debug -- the same call, but writes the binary32
  * accumulators (before the bf16 rounding) to out_f32, DEVICE float
  * [n_ranks][n].  Same contract otherwise; advances the epoch sequence like
@@ -185,8 +236,9 @@ int ar_set_scope(int scope);
 /*
  * ar_set_watchdog -- per-poll time budget in microseconds (default 200000).
  * A poll that exceeds it records {6, rank, source, flag} in the device status
- * record and its workgroup stops; the other workgroups of that call stop
- * polling soon after they see the record.  The record stays until ar_reset;
+ * record and its workgroup stops (in the fused norm's wait for the row's
+ * block sums, source is the waiting rank itself); the other workgroups of
+ * that call stop polling soon after they see the record.  The record stays until ar_reset;
  * until then outputs of later calls are undefined.  0 restores the default.
  */
 int ar_set_watchdog(uint32_t budget_us);

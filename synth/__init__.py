@@ -121,3 +121,25 @@ def random_bits(seed: int, shape, finite_only: bool = True, avoid: int = None) -
     if avoid is not None:
         x = np.where(x == avoid, np.uint16(0), x).astype(np.uint16)
     return x
+
+
+NORM_EPS = 1e-5
+
+
+def norm_operands(cid: int, set_idx: int, n_ranks: int = None, replicated: bool = False):
+    """Operands of the residual add + RMS norm after workload `cid`'s AllReduce:
+    residuals uint16 [N, n] drawn N(0, 2) (the residual stream), gamma uint16
+    [hidden] drawn N(1, 0.2) (a trained norm weight's typical spread).  With
+    replicated=True every rank holds the same residual, as in tensor-parallel
+    decode; otherwise each rank's is drawn separately, so that a kernel which
+    mixes up ranks' residuals cannot pass."""
+    w = WORKLOADS[cid]
+    N = w.n_ranks if n_ranks is None else n_ranks
+    base = SEED_BASE + 100000 + 1000 * cid + 20 * set_idx     # apart from the input seeds
+    res = []
+    for r in range(N):
+        rng = np.random.Generator(np.random.PCG64(base + (0 if replicated else r)))
+        res.append(draw(rng, w.n, "normal", 2.0))
+    rng = np.random.Generator(np.random.PCG64(base + 19))
+    gamma = _to_bf16_bits(rng.normal(1.0, 0.2, size=w.hidden).astype(np.float32))
+    return np.stack(res), gamma

@@ -58,6 +58,9 @@ def test_host_validation_without_device(lib):
     assert lib.ar_query(0, 0) == a.AR_ERR_NOT_INIT
     ptrs = (ctypes.c_void_p * 1)(0)
     assert lib.ar_allreduce(ptrs, None, 8, 1, None) == a.AR_ERR_NOT_INIT
+    assert lib.ar_allreduce_add_rmsnorm(ptrs, ptrs, 16, 1e-5, 16, 16, 1, 256, 1,
+                                        None) == a.AR_ERR_NOT_INIT
+    assert lib.ar_add_rmsnorm(16, ptrs, 16, 1e-5, 16, 16, 1, 256, None) == a.AR_ERR_NOT_INIT
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert lib.ar_strerror(code)
     assert lib.ar_strerror(-99) == b"unknown status"

@@ -31,6 +31,11 @@ _SIGS = {
     "ar_init": (_c_int, [_c_int, _c_size]),
     "ar_allreduce": (_c_int, [ctypes.POINTER(_c_vp), _c_vp, _c_size, _c_u32, _c_vp]),
     "ar_allreduce_f32_debug": (_c_int, [ctypes.POINTER(_c_vp), _c_vp, _c_size, _c_u32, _c_vp]),
+    "ar_allreduce_add_rmsnorm": (_c_int, [ctypes.POINTER(_c_vp), ctypes.POINTER(_c_vp), _c_vp,
+                                          ctypes.c_float, _c_vp, _c_vp, _c_size, _c_size, _c_u32,
+                                          _c_vp]),
+    "ar_add_rmsnorm": (_c_int, [_c_vp, ctypes.POINTER(_c_vp), _c_vp, ctypes.c_float, _c_vp, _c_vp,
+                                _c_size, _c_size, _c_vp]),
     "ar_destroy": (_c_int, []),
     "ar_set_options": (_c_int, [_c_int, _c_int]),
     "ar_set_launch": (_c_int, [_c_int, _c_int]),
@@ -134,6 +139,26 @@ def allreduce(rank_bufs, out, n, epoch, stream=None, check=True):
     rc = lib().ar_allreduce(_rank_array(rank_bufs), _ptr(out), int(n), int(epoch),
                             _stream_handle(stream))
     return _check("ar_allreduce", rc) if check else rc
+
+
+def allreduce_add_rmsnorm(rank_bufs, residuals, gamma, eps, out_h, out_y, rows, hidden, epoch,
+                          stream=None, check=True):
+    """AllReduce with the residual add and RMS norm fused behind it:
+    residuals N bf16 device tensors [rows*hidden], gamma bf16 [hidden],
+    out_h / out_y bf16 [N, rows*hidden].  Takes the next epoch like allreduce."""
+    rc = lib().ar_allreduce_add_rmsnorm(_rank_array(rank_bufs), _rank_array(residuals),
+                                        _ptr(gamma), float(eps), _ptr(out_h), _ptr(out_y),
+                                        int(rows), int(hidden), int(epoch), _stream_handle(stream))
+    return _check("ar_allreduce_add_rmsnorm", rc) if check else rc
+
+
+def add_rmsnorm(a, residuals, gamma, eps, out_h, out_y, rows, hidden, stream=None, check=True):
+    """The same residual add and RMS norm as a kernel of its own, on an
+    AllReduce result a [N, rows*hidden] already in memory."""
+    rc = lib().ar_add_rmsnorm(_ptr(a), _rank_array(residuals), _ptr(gamma), float(eps),
+                              _ptr(out_h), _ptr(out_y), int(rows), int(hidden),
+                              _stream_handle(stream))
+    return _check("ar_add_rmsnorm", rc) if check else rc
 
 
 def gemv(weights, xs, ys, M, K, stream=None, max_workgroups=0, check=True):

@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "../../include/ar.h"
@@ -38,6 +39,8 @@ struct Context {
     char *srs = nullptr;  char *sag = nullptr; size_t s2_stride = 0;
     uint32_t *ctl = nullptr;
     uint32_t *done = nullptr;           // two-shot DIRECT completion flags
+    uint32_t *stats = nullptr;          // fused norm: per-block sums of squares {sum, flag}
+    size_t stats_stride = 0;            // entries per rank
     // options
     int algo = AR_ALGO_AUTO;
     int proto = AR_PROTO_AUTO;
@@ -88,6 +91,8 @@ void free_all()
     g.ctl = nullptr;
     if (g.done) (void)hipFree(g.done);
     g.done = nullptr;
+    if (g.stats) (void)hipFree(g.stats);
+    g.stats = nullptr;
 }
 
 constexpr size_t REGION_LIMIT = (size_t(1) << 32) - 1;   // one buffer descriptor
@@ -112,6 +117,7 @@ size_t l128_bytes() { return g.l128_stride * 2 * g.n_ranks; }
 size_t s1_bytes() { return g.s1_stride * 2 * g.n_ranks * g.n_ranks; }
 size_t s2_bytes() { return g.s2_stride * 2 * g.n_ranks * g.n_ranks; }
 size_t done_words() { return (size_t)ar::MAX_RANKS * ar::DONE_STRIDE; }
+size_t stats_bytes() { return g.stats_stride * 8 * g.n_ranks; }
 
 // Zero flags, arm sentinels, clear the control block -- kernels only.
 hipError_t rearm(hipStream_t s)
@@ -123,6 +129,7 @@ hipError_t rearm(hipStream_t s)
     if ((e = ar::launch_fill((uint32_t *)g.srs, s2_bytes() / 4, ar::SENT_WORD, s)) != hipSuccess) return e;
     if ((e = ar::launch_fill((uint32_t *)g.sag, s2_bytes() / 4, ar::SENT_WORD, s)) != hipSuccess) return e;
     if ((e = ar::launch_fill(g.done, done_words(), 0u, s)) != hipSuccess) return e;
+    if ((e = ar::launch_fill(g.stats, stats_bytes() / 4, 0u, s)) != hipSuccess) return e;
     return ar::launch_fill(g.ctl, ar::CTL_WORDS, 0u, s);
 }
 
@@ -136,6 +143,8 @@ int compute_capacity()
     const int tcounts[5] = {64, 128, 256, 512, 1024};
     for (int k = 0; k < ar::K_COUNT; ++k) {
         for (int f = 0; f < 2; ++f) {
+            if (ar::kernel_for(k, g.n_ranks, f == 1, false) == nullptr)
+                continue;                       // no such variant (capacity stays 0)
             for (int t = 0; t < 5; ++t) {
                 int per_cu = 0;
                 hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
@@ -215,15 +224,13 @@ int choose_kind(size_t n, int *kind)
 // messages use one-wave workgroups spread over many CUs (each CU then polls
 // little); large ones use 4-wave workgroups.  The whole grid must be
 // resident at once.
-int make_plan(size_t n, bool f32, Plan *p)
+int plan_geometry(size_t n, bool f32, Plan *p)
 {
-    int rc = choose_kind(n, &p->kind);
-    if (rc != AR_OK)
-        return rc;
+    int rc;
     const uint32_t N = (uint32_t)g.n_ranks;
     p->slice = (uint32_t)slice_len(n, g.n_ranks);
     const bool l128 = p->kind == ar::K_ONESHOT_LL128 || p->kind == ar::K_TWOSHOT_LL128;
-    if (p->kind == ar::K_ONESHOT_LL) {
+    if (p->kind == ar::K_ONESHOT_LL || p->kind == ar::K_ONESHOT_LL_NORM) {
         // one wave per rank (a power of two >= N): each wave receives one peer
         uint32_t w = 1;
         while (w < N) w <<= 1;
@@ -239,6 +246,7 @@ int make_plan(size_t n, bool f32, Plan *p)
     uint64_t units, per_wg;
     switch (p->kind) {
     case ar::K_ONESHOT_LL:
+    case ar::K_ONESHOT_LL_NORM:
         units = n / 4; per_wg = 64; break;
     case ar::K_ONESHOT_LL128:       // batches of 4 line groups (2 above 8 ranks)
         units = (n + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = N <= 8 ? 4 : 2; break;
@@ -261,9 +269,11 @@ int make_plan(size_t n, bool f32, Plan *p)
     uint32_t cap = (uint32_t)g.capacity[p->kind][f32 ? 1 : 0][thread_index((int)p->threads)] / N;
     if (cap > ar::DONE_STRIDE)
         cap = ar::DONE_STRIDE;
-    if (p->kind == ar::K_ONESHOT_BARRIER || p->kind == ar::K_TWOSHOT_BARRIER) {
-        // a grid barrier needs every workgroup resident at once: stay within
-        // half the occupancy-derived capacity (the watchdog bounds the rest)
+    if (p->kind == ar::K_ONESHOT_BARRIER || p->kind == ar::K_TWOSHOT_BARRIER ||
+        p->kind == ar::K_ONESHOT_LL_NORM) {
+        // a grid barrier (or the norm's row-wide wait) needs every workgroup
+        // resident at once: stay within half the occupancy-derived capacity
+        // (the watchdog bounds the rest)
         cap /= 2;
         if (cap > ar::DONE_STRIDE)
             cap = ar::DONE_STRIDE;
@@ -287,6 +297,14 @@ int make_plan(size_t n, bool f32, Plan *p)
     p->parts = (uint32_t)want;
     p->local = !f32 && g.scope == AR_SCOPE_AUTO && g.placement_ok && p->parts % ar::XCDS == 0;
     return AR_OK;
+}
+
+int make_plan(size_t n, bool f32, Plan *p)
+{
+    int rc = choose_kind(n, &p->kind);
+    if (rc != AR_OK)
+        return rc;
+    return plan_geometry(n, f32, p);
 }
 
 int check_call(const void *const *rank_bufs, const void *out, size_t out_elem_bytes, size_t n,
@@ -353,17 +371,10 @@ hipError_t verify_placement(bool *ok)
     return e;
 }
 
-int do_allreduce(const void *const *rank_bufs, void *out, size_t n, uint32_t epoch,
-                 hipStream_t stream, bool f32)
+void fill_launch(const void *const *rank_bufs, void *out, size_t n, uint32_t epoch, const Plan &p,
+                 Launch *ap)
 {
-    int rc = check_call(rank_bufs, out, f32 ? 4 : 2, n, epoch);
-    if (rc != AR_OK)
-        return rc;
-    Plan p;
-    rc = make_plan(n, f32, &p);
-    if (rc != AR_OK)
-        return rc;
-    Launch a;
+    Launch &a = *ap;
     memset(&a, 0, sizeof a);
     for (int r = 0; r < g.n_ranks; ++r)
         a.in[r] = rank_bufs[r];
@@ -387,6 +398,20 @@ int do_allreduce(const void *const *rank_bufs, void *out, size_t n, uint32_t epo
     a.span_magic = a.span > 1 ? (uint32_t)(((1ull << 32) + a.span - 1) / a.span) : 0u;
     uint64_t ticks = (uint64_t)g.watchdog_us * 100u;   // 100 MHz clock
     a.watchdog_ticks = (uint32_t)std::min<uint64_t>(ticks, 0xFFFFFFFFu);
+}
+
+int do_allreduce(const void *const *rank_bufs, void *out, size_t n, uint32_t epoch,
+                 hipStream_t stream, bool f32)
+{
+    int rc = check_call(rank_bufs, out, f32 ? 4 : 2, n, epoch);
+    if (rc != AR_OK)
+        return rc;
+    Plan p;
+    rc = make_plan(n, f32, &p);
+    if (rc != AR_OK)
+        return rc;
+    Launch a;
+    fill_launch(rank_bufs, out, n, epoch, p, &a);
     const uint32_t grid = p.parts * (uint32_t)g.n_ranks;
     if (debug_enabled())
         fprintf(stderr, "[ar] n=%zu epoch=%u kind=%d grid=%u threads=%u slice=%u f32=%d local=%d\n",
@@ -397,6 +422,98 @@ int do_allreduce(const void *const *rank_bufs, void *out, size_t n, uint32_t epo
     g.last_epoch = epoch;
     return AR_OK;
 }
+
+
+bool overlap(const void *a, size_t an, const void *b, size_t bn)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + bn && y < x + an;
+}
+
+// Checks of the residual add + RMS norm operands shared by the fused and
+// the stand-alone entry points: rows x hidden per rank, hidden a multiple of
+// 256 up to 65536, 16-byte aligned operands, outputs h and y [N][n] disjoint
+// from each other and from every operand read (src [N] arrays of n elements,
+// residuals, gamma).
+int check_norm(const void *const *src, size_t src_count, const void *const *residual,
+               const void *gamma, float eps, const void *out_h, const void *out_y, size_t rows,
+               size_t hidden, size_t *n_out)
+{
+    if (residual == nullptr || gamma == nullptr || out_h == nullptr || out_y == nullptr ||
+        src == nullptr)
+        return AR_ERR_INVALID;
+    if (hidden < ar::NORM_BLOCK_ELEMS || hidden % ar::NORM_BLOCK_ELEMS != 0 ||
+        hidden > ar::NORM_HIDDEN_LIMIT || rows == 0 || rows > g.max_elems / hidden)
+        return AR_ERR_INVALID;
+    if (!std::isfinite(eps) || eps < 0.0f)
+        return AR_ERR_INVALID;
+    const size_t n = rows * hidden;
+    const size_t out_bytes = 2 * n * (size_t)g.n_ranks;
+    const void *ptrs[] = {gamma, out_h, out_y};
+    for (const void *q : ptrs)
+        if ((uintptr_t)q % 16)
+            return AR_ERR_INVALID;
+    if (overlap(out_h, out_bytes, out_y, out_bytes) || overlap(out_h, out_bytes, gamma, 2 * hidden) ||
+        overlap(out_y, out_bytes, gamma, 2 * hidden))
+        return AR_ERR_INVALID;
+    for (int r = 0; r < g.n_ranks; ++r) {
+        const void *q = residual[r];
+        if (q == nullptr || (uintptr_t)q % 16 || overlap(out_h, out_bytes, q, 2 * n) ||
+            overlap(out_y, out_bytes, q, 2 * n))
+            return AR_ERR_INVALID;
+    }
+    for (size_t r = 0; r < src_count; ++r) {
+        const void *q = src[r];
+        const size_t len = src_count == 1 ? out_bytes : 2 * n;
+        if (q == nullptr || (uintptr_t)q % 16 || overlap(out_h, out_bytes, q, len) ||
+            overlap(out_y, out_bytes, q, len))
+            return AR_ERR_INVALID;
+    }
+    *n_out = n;
+    return AR_OK;
+}
+
+int do_allreduce_norm(const void *const *rank_bufs, const void *const *residual, const void *gamma,
+                      float eps, void *out_h, void *out_y, size_t rows, size_t hidden,
+                      uint32_t epoch, hipStream_t stream)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    size_t n = 0;
+    int rc = check_norm(rank_bufs, (size_t)g.n_ranks, residual, gamma, eps, out_h, out_y, rows,
+                        hidden, &n);
+    if (rc != AR_OK)
+        return rc;
+    rc = check_call(rank_bufs, out_h, 2, n, epoch);
+    if (rc != AR_OK)
+        return rc;
+    Plan p;
+    p.kind = ar::K_ONESHOT_LL_NORM;
+    rc = plan_geometry(n, false, &p);
+    if (rc != AR_OK)
+        return rc;
+    ar::NormLaunch L;
+    memset(&L, 0, sizeof L);
+    fill_launch(rank_bufs, out_h, n, epoch, p, &L.base);
+    for (int r = 0; r < g.n_ranks; ++r)
+        L.res[r] = residual[r];
+    L.gamma = gamma;
+    L.y = out_y;
+    L.stats = g.stats;
+    L.stats_stride = (uint32_t)g.stats_stride;
+    L.hidden = (uint32_t)hidden;
+    L.eps = eps;
+    const uint32_t grid = p.parts * (uint32_t)g.n_ranks;
+    if (debug_enabled())
+        fprintf(stderr, "[ar] norm rows=%zu hidden=%zu epoch=%u grid=%u threads=%u local=%d\n",
+                rows, hidden, epoch, grid, p.threads, (int)p.local);
+    hipError_t e = ar::launch_ll_norm(p.local, L, grid, p.threads, stream);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    g.last_epoch = epoch;
+    return AR_OK;
+}
+
 
 }  // namespace
 
@@ -421,6 +538,7 @@ int ar_init(int n_ranks, size_t max_elems)
     g.l128_stride = round_up((me + ar::L128_ELEMS - 1) / ar::L128_ELEMS * ar::L128_BYTES, 256);
     g.s1_stride = round_up(me * 2, 256);
     g.s2_stride = round_up(slice_len(me, n_ranks) * 2, 256);
+    g.stats_stride = (me + ar::NORM_BLOCK_ELEMS - 1) / ar::NORM_BLOCK_ELEMS;
     // every staging region and the output tensor are addressed through one
     // buffer descriptor with 32-bit offsets; a region that would not fit is
     // not allocated and its protocol is unavailable for this context
@@ -434,7 +552,8 @@ int ar_init(int n_ranks, size_t max_elems)
         (rc = alloc(&g.srs, s2_bytes())) != AR_OK ||
         (rc = alloc(&g.sag, s2_bytes())) != AR_OK ||
         (rc = alloc((char **)&g.ctl, ar::CTL_WORDS * 4)) != AR_OK ||
-        (rc = alloc((char **)&g.done, done_words() * 4)) != AR_OK) {
+        (rc = alloc((char **)&g.done, done_words() * 4)) != AR_OK ||
+        (rc = alloc((char **)&g.stats, stats_bytes())) != AR_OK) {
         free_all();
         return rc;
     }
@@ -481,6 +600,32 @@ int ar_allreduce(const void *const *rank_bufs, void *out, size_t n, uint32_t epo
                  hipStream_t stream)
 {
     return do_allreduce(rank_bufs, out, n, epoch, stream, false);
+}
+
+int ar_allreduce_add_rmsnorm(const void *const *rank_bufs, const void *const *residual,
+                             const void *gamma, float eps, void *out_h, void *out_y, size_t rows,
+                             size_t hidden, uint32_t epoch, hipStream_t stream)
+{
+    return do_allreduce_norm(rank_bufs, residual, gamma, eps, out_h, out_y, rows, hidden, epoch,
+                             stream);
+}
+
+int ar_add_rmsnorm(const void *a, const void *const *residual, const void *gamma, float eps,
+                   void *out_h, void *out_y, size_t rows, size_t hidden, hipStream_t stream)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    size_t n = 0;
+    const void *src[1] = {a};
+    int rc = check_norm(src, 1, residual, gamma, eps, out_h, out_y, rows, hidden, &n);
+    if (rc != AR_OK)
+        return rc;
+    hipError_t e = ar::launch_add_rmsnorm(a, residual, gamma, eps, out_h, out_y,
+                                          (uint32_t)g.n_ranks, (uint32_t)rows, (uint32_t)hidden,
+                                          stream);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    return AR_OK;
 }
 
 int ar_allreduce_f32_debug(const void *const *rank_bufs, float *out_f32, size_t n, uint32_t epoch,
@@ -541,7 +686,7 @@ int ar_step_end(hipStream_t stream)
         return AR_ERR_STATE;
     if (g.last_epoch > 0) {
         hipError_t e = ar::launch_step_end(g.ctl, g.last_epoch, g.ll, ll_bytes(), g.l128,
-                                           l128_bytes(), g.done, stream);
+                                           l128_bytes(), g.done, g.stats, stats_bytes(), stream);
         if (e != hipSuccess)
             return hip_fail(e);
     }

@@ -7,6 +7,12 @@
 namespace ar {
 
 struct Launch;
+struct NormLaunch;
+
+// residual add + RMS norm: the row length is a multiple of the 256-element
+// block of one partial sum, at most 65536
+constexpr size_t NORM_BLOCK_ELEMS = 256;
+constexpr size_t NORM_HIDDEN_LIMIT = 65536;
 
 enum KernelKind {
     K_ONESHOT_LL = 0,
@@ -18,7 +24,8 @@ enum KernelKind {
     K_TWOSHOT_DIRECT = 6,
     K_ONESHOT_BARRIER = 7,
     K_TWOSHOT_BARRIER = 8,
-    K_COUNT = 9
+    K_ONESHOT_LL_NORM = 9,      // one-shot LL + residual add + RMS norm (bf16 only)
+    K_COUNT = 10
 };
 
 // device function of a kernel kind for n_ranks (<= 8 or <= 16 instantiation);
@@ -27,10 +34,18 @@ const void *kernel_for(int kind, int n_ranks, bool f32, bool local);
 
 hipError_t launch_ar(int kind, bool f32, bool local, const Launch &a, uint32_t grid,
                      uint32_t threads, hipStream_t stream);
+hipError_t launch_ll_norm(bool local, const NormLaunch &L, uint32_t grid, uint32_t threads,
+                          hipStream_t stream);
+// stand-alone residual add + RMS norm of an AllReduce result: one workgroup
+// of 1024 threads per (rank, row)
+hipError_t launch_add_rmsnorm(const void *a, const void *const *res, const void *gamma, float eps,
+                              void *h, void *y, uint32_t n_ranks, uint32_t rows, uint32_t hidden,
+                              hipStream_t stream);
 // out[b] = XCD index of workgroup b, for b < grid
 hipError_t launch_xcc_map(uint32_t *out, uint32_t grid, uint32_t threads, hipStream_t stream);
 hipError_t launch_step_end(uint32_t *ctl, uint32_t calls, char *ll, size_t ll_bytes, char *l128,
-                           size_t l128_bytes, uint32_t *done, hipStream_t stream);
+                           size_t l128_bytes, uint32_t *done, uint32_t *stats, size_t stats_bytes,
+                           hipStream_t stream);
 hipError_t launch_fill(uint32_t *p, size_t words, uint32_t value, hipStream_t stream);
 
 }  // namespace ar

@@ -35,6 +35,7 @@
 // and read by few lanes.
 #include "ar_proto.h"
 #include "ar_kernels.h"
+#include "norm_math.h"
 
 namespace ar {
 
@@ -230,11 +231,13 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
 // take ~0.85 us, 2 per wave ~0.55 us and 1 per wave ~0.4 us.  Each wave's
 // receive keeps two loads in flight: while one is checked the next is
 // already on its way.
-template <int NMAX, bool F32, bool LOCAL>
+//
+// `epi(ch, v)` consumes the reduced chunk (4 binary32 sums in v) on wave 0;
+// all lanes of wave 0 call it together when the round's chunks are in range.
+template <int NMAX, bool LOCAL, typename Epi>
 __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
-                                         __amdgpu_buffer_rsrc_t llr, __amdgpu_buffer_rsrc_t o,
-                                         uint32_t ch, uint32_t C, u32x2 x, u32x2 (*stage)[64],
-                                         uint32_t *failed)
+                                         __amdgpu_buffer_rsrc_t llr, uint32_t ch, uint32_t C,
+                                         u32x2 x, u32x2 (*stage)[64], uint32_t *failed, Epi &&epi)
 {
     const uint32_t N = a.n_ranks;
     const uint32_t rb = a.ll_stride;
@@ -300,7 +303,7 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
                 if (s == 0) acc.init(v.x, v.y); else acc.add(v.x, v.y);
             }
         }
-        store4<F32>(o, ch * 4u, acc.v);
+        epi(ch, acc.v);
     }
     __syncthreads();                                // the tile is reused next round
     return true;
@@ -337,13 +340,158 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll(const Launch a)
     start_delay(a, c);
     // round 0 is straight-line code: its poll loads are issued back to back
     // (inside a loop the compiler's counter bookkeeping would wait before each)
-    if (!ll_round<NMAX, F32, LOCAL>(a, c, ctl, llr, o, ch, C, x, stage, &failed))
+    auto out4 = [&](uint32_t cch, const float *v) { store4<F32>(o, cch * 4u, v); };
+    if (!ll_round<NMAX, LOCAL>(a, c, ctl, llr, ch, C, x, stage, &failed, out4))
         return;
     for (uint32_t it = 1; it < rounds; ++it) {
         ch += step;
         x = (wave == 0u && ch < C) ? ld8<CP_PLAIN>(inr, ch * 8u) : u32x2{0u, 0u};
-        if (!ll_round<NMAX, F32, LOCAL>(a, c, ctl, llr, o, ch, C, x, stage, &failed))
+        if (!ll_round<NMAX, LOCAL>(a, c, ctl, llr, ch, C, x, stage, &failed, out4))
             return;
+    }
+    finish(a, c);
+}
+
+// ================================================ one-shot LL + add + norm
+// The AllReduce with the layer's residual add and RMS norm behind it in the
+// same launch (the op that follows the AllReduce in the decode loop,
+// "vLLM 分布式推理核心" page, section 一; arithmetic in norm_math.h).  The
+// LL rounds run as in k_oneshot_ll; on wave 0 each round's reduced chunk a
+// becomes h = bf16(a + res), which is written out, and the round's 256
+// elements (one norm block, never split by a row end since the row length
+// is a multiple of 256) give one partial sum of squares, published with the
+// call's flag as one 8-byte store {sum, flag} at device scope -- the blocks
+// of a row are spread over all XCDs.  After its last round wave 0 waits for
+// the block sums of each row it holds (two polls in flight), folds them in
+// the fixed order, and writes y = bf16(h * r * gamma): h of round 0 from
+// registers, of later rounds re-read from its own writes.  Every workgroup
+// of a row folds the same sums in the same order, so all of them use the
+// same r.  The wait spans all workgroups of a rank, so the whole grid must
+// be resident at once (the host keeps it to half the device's capacity).
+template <bool LOCAL>
+__device__ __forceinline__ bool row_rinv(const NormLaunch &L, const Ctx0 &c, const Ctl &ctl,
+                                         __amdgpu_buffer_rsrc_t sr, uint32_t row, uint32_t B,
+                                         float *rinv)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t base = c.rank * L.stats_stride + row * B;
+    float part = 0.0f;
+    for (uint32_t g0 = 0; g0 < B; g0 += 64u) {
+        const uint32_t j = g0 + lane;
+        bool need = j < B;
+        const uint32_t off = (base + (need ? j : 0u)) * 8u;
+        float got = 0.0f;
+        Watch w;
+        w.begin(L.base.watchdog_ticks);
+        u32x2 v0 = need ? ld8<CP_DEV>(sr, off) : u32x2{0u, 0u}, v1;
+        while (true) {
+            compiler_fence();
+            v1 = need ? ld8<CP_DEV>(sr, off) : u32x2{0u, 0u};
+            if (need && v0.y == c.flag) {
+                need = false;
+                got = __uint_as_float(v0.x);
+            }
+            if (!wave_any(need))
+                break;
+            if (w.expired(ctl, c.rank, c.rank, c.flag))
+                return false;
+            compiler_fence();
+            v0 = need ? ld8<CP_DEV>(sr, off) : u32x2{0u, 0u};
+            if (need && v1.y == c.flag) {
+                need = false;
+                got = __uint_as_float(v1.x);
+            }
+            if (!wave_any(need))
+                break;
+        }
+        part = g0 == 0u ? got : part + got;
+    }
+    *rinv = rms_inv(wave_sum(part), L.hidden, L.eps);
+    return true;
+}
+
+template <int NMAX, bool LOCAL>
+__global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
+{
+    const Launch &a = L.base;
+    __shared__ u32x2 stage[NMAX][64];
+    __shared__ uint32_t failed;
+    Ctx0 c;
+    begin<LOCAL>(a, c);
+    const uint32_t C = a.n >> 2;                    // 4-element chunks per rank
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t step = a.parts * 64u;
+    const uint32_t rounds = (C + step - 1u) / step;
+    if ((blockDim.x >> 6) < a.n_ranks) {            // the host launches a wave per rank
+        if (threadIdx.x == 0)
+            Ctl{a.ctl}.fail(c.rank, blockDim.x, a.epoch);
+        return;
+    }
+    const uint32_t nb = a.n * 2u;
+    const __amdgpu_buffer_rsrc_t inr = in_rsrc(a, c.rank);
+    const __amdgpu_buffer_rsrc_t resr = rsrc(L.res[c.rank], nb);
+    const __amdgpu_buffer_rsrc_t gr = rsrc(L.gamma, L.hidden * 2u);
+    const __amdgpu_buffer_rsrc_t oh = rsrc((char *)a.out + (size_t)c.rank * nb, nb);
+    const __amdgpu_buffer_rsrc_t oy = rsrc((char *)L.y + (size_t)c.rank * nb, nb);
+    const __amdgpu_buffer_rsrc_t sr = rsrc(L.stats, a.n_ranks * L.stats_stride * 8u);
+    if (threadIdx.x == 0)
+        failed = 0u;
+    uint32_t ch = c.part * 64u + lane;
+    u32x2 x = {0u, 0u}, rw = {0u, 0u}, g0 = {0u, 0u};
+    if (wave == 0u && ch < C) {
+        x = ld8<CP_PLAIN>(inr, ch * 8u);
+        rw = ld8<CP_PLAIN>(resr, ch * 8u);
+        g0 = ld8<CP_PLAIN>(gr, ((ch * 4u) % L.hidden) * 2u);
+    }
+    c.flag = load_seq(a) + a.epoch;
+    const Ctl ctl{a.ctl};
+    const __amdgpu_buffer_rsrc_t llr = rsrc(a.ll, a.n_ranks * 2u * a.ll_stride);
+    start_delay(a, c);
+    u32x2 hk = {0u, 0u};
+    auto epi = [&](uint32_t cch, const float *v) {
+        u32x2 aw;
+        aw.x = pack_bf16(v[0], v[1]);
+        aw.y = pack_bf16(v[2], v[3]);
+        const u32x2 hw = add_round4(aw, rw);
+        st8<CP_PLAIN>(hw, oh, cch * 8u);
+        hk = hw;
+        const float s = wave_sum(sumsq4(hw));
+        if (lane == 0u) {
+            u32x2 e; e.x = __float_as_uint(s); e.y = c.flag;
+            st8<CP_DEV>(e, sr, (c.rank * L.stats_stride + (cch >> 6)) * 8u);
+        }
+    };
+    if (!ll_round<NMAX, LOCAL>(a, c, ctl, llr, ch, C, x, stage, &failed, epi))
+        return;
+    const u32x2 h0 = hk;
+    for (uint32_t it = 1; it < rounds; ++it) {
+        ch += step;
+        const bool ld = wave == 0u && ch < C;
+        x = ld ? ld8<CP_PLAIN>(inr, ch * 8u) : u32x2{0u, 0u};
+        rw = ld ? ld8<CP_PLAIN>(resr, ch * 8u) : u32x2{0u, 0u};
+        if (!ll_round<NMAX, LOCAL>(a, c, ctl, llr, ch, C, x, stage, &failed, epi))
+            return;
+    }
+    // normalise (wave 0; the other waves go straight to finish's barrier)
+    if (wave == 0u) {
+        const uint32_t B = L.hidden / NORM_BLOCK;
+        uint32_t have = 0xFFFFFFFFu;
+        float r = 0.0f;
+        for (uint32_t it = 0; it < rounds; ++it) {
+            const uint32_t c0 = c.part * 64u + it * step;      // first chunk (wave-uniform)
+            if (c0 >= C)
+                break;
+            const uint32_t row = (c0 >> 6) / B;
+            if (row != have) {
+                if (!row_rinv<LOCAL>(L, c, ctl, sr, row, B, &r))
+                    break;                                      // watchdog: status recorded
+                have = row;
+            }
+            const uint32_t cc = c0 + lane;
+            const u32x2 hw = it == 0u ? h0 : ld8<CP_PLAIN>(oh, cc * 8u);
+            const u32x2 gw = it == 0u ? g0 : ld8<CP_PLAIN>(gr, ((cc * 4u) % L.hidden) * 2u);
+            st8<CP_PLAIN>(scale4(hw, gw, r), oy, cc * 8u);
+        }
     }
     finish(a, c);
 }
@@ -1345,10 +1493,11 @@ __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
 // sequence nears the top of its 32-bit range, every flag word (LL units,
 // LL128 lines, arrival flags, completion flags) is cleared and the
 // sequence restarts, so a flag value left in memory long ago can never match
-// a future call.
+// a future call.  (The norm statistics region holds flags too.)
 __global__ __launch_bounds__(256) void k_step_end(uint32_t *ctl, uint32_t calls, char *ll,
                                                   size_t ll_bytes, char *l128, size_t l128_bytes,
-                                                  uint32_t *done)
+                                                  uint32_t *done, uint32_t *stats,
+                                                  size_t stats_bytes)
 {
     __shared__ uint32_t wrap;
     if (threadIdx.x == 0) {
@@ -1363,6 +1512,7 @@ __global__ __launch_bounds__(256) void k_step_end(uint32_t *ctl, uint32_t calls,
         w = (uint32_t *)l128;
         for (size_t i = threadIdx.x; i < l128_bytes / 4; i += blockDim.x) w[i] = 0u;
         for (size_t i = threadIdx.x; i < (size_t)MAX_RANKS * DONE_STRIDE; i += blockDim.x) done[i] = 0u;
+        for (size_t i = threadIdx.x; i < stats_bytes / 4; i += blockDim.x) stats[i] = 0u;
         for (uint32_t i = threadIdx.x; i < (uint32_t)(CTL_WORDS - CTL_ARRIVE); i += blockDim.x)
             __hip_atomic_store(ctl + CTL_ARRIVE + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __threadfence();
@@ -1406,6 +1556,8 @@ static const void *pick(int kind)
     case K_TWOSHOT_DIRECT: return (const void *)k_twoshot_direct<NMAX, F32, LOCAL>;
     case K_ONESHOT_BARRIER: return (const void *)k_oneshot_barrier<NMAX, F32, LOCAL>;
     case K_TWOSHOT_BARRIER: return (const void *)k_twoshot_barrier<NMAX, F32, LOCAL>;
+    case K_ONESHOT_LL_NORM:         // bf16 only
+        return F32 ? nullptr : (const void *)k_oneshot_ll_norm<NMAX, LOCAL>;
     default: return nullptr;
     }
 }
@@ -1430,6 +1582,16 @@ hipError_t launch_ar(int kind, bool f32, bool local, const Launch &a, uint32_t g
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
 }
 
+hipError_t launch_ll_norm(bool local, const NormLaunch &L, uint32_t grid, uint32_t threads,
+                          hipStream_t stream)
+{
+    const void *fn = kernel_for(K_ONESHOT_LL_NORM, (int)L.base.n_ranks, false, local);
+    if (fn == nullptr)
+        return hipErrorInvalidValue;
+    void *args[] = {(void *)&L};
+    return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
+}
+
 hipError_t launch_xcc_map(uint32_t *out, uint32_t grid, uint32_t threads, hipStream_t stream)
 {
     hipLaunchKernelGGL(k_xcc_map, dim3(grid), dim3(threads), 0, stream, out, grid);
@@ -1437,10 +1599,11 @@ hipError_t launch_xcc_map(uint32_t *out, uint32_t grid, uint32_t threads, hipStr
 }
 
 hipError_t launch_step_end(uint32_t *ctl, uint32_t calls, char *ll, size_t ll_bytes, char *l128,
-                           size_t l128_bytes, uint32_t *done, hipStream_t stream)
+                           size_t l128_bytes, uint32_t *done, uint32_t *stats, size_t stats_bytes,
+                           hipStream_t stream)
 {
     hipLaunchKernelGGL(k_step_end, dim3(1), dim3(256), 0, stream, ctl, calls, ll, ll_bytes, l128,
-                       l128_bytes, done);
+                       l128_bytes, done, stats, stats_bytes);
     return hipGetLastError();
 }
 

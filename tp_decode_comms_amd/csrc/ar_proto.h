@@ -103,6 +103,21 @@ struct Launch {
     uint32_t delay_rows;
 };
 
+// The one-shot LL AllReduce with the residual add and RMS norm fused behind
+// it.  base.out receives h [N][n]; y [N][n] the normalised rows.  Each
+// 256-element block's sum of squares is published as {binary32 bits, flag}
+// in stats[rank * stats_stride + block].
+struct NormLaunch {
+    Launch base;
+    const void *res[MAX_RANKS];   // rank residuals, bf16 [n]
+    const void *gamma;            // norm weight, bf16 [hidden], shared by all ranks
+    void *y;                      // [N][n] bf16
+    uint32_t *stats;              // [N][stats_stride] x 2 words
+    uint32_t stats_stride;        // entries per rank (>= n / 256)
+    uint32_t hidden;              // row length, a multiple of 256
+    float eps;
+};
+
 // ---------------------------------------------------------------- buffers
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes)
 {
