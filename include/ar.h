@@ -80,12 +80,21 @@ enum ar_proto {
                                peers' inputs in place; two-shot reads slice q in
                                place and writes the reduced slice straight into
                                every rank's output, then completion flags */
-    AR_PROTO_BARRIER = 5    /* measured baseline, not barrier-free: the DIRECT
+    AR_PROTO_BARRIER = 5,   /* measured baseline, not barrier-free: the DIRECT
                                reads, fold and writes between two device-wide
                                barriers over all ranks' workgroups (before the
                                reads, after the writes), the classic structure of
                                section "全局内存屏障"; the grid stays within half the
                                device's resident-workgroup capacity */
+    AR_PROTO_ATOMIC = 6     /* two-shot only: the atomic two-phase algorithm of
+                               section "四大核心机制" item 4 -- every rank adds its
+                               values into shared 128-byte lines {counter,
+                               31 x binary32} with atomics and counts itself in;
+                               a rank reads a line once its counter reaches N.
+                               Sums are taken in arrival order, so the result is
+                               NOT the fixed-order fold: before the bf16 rounding
+                               it is within (N-1) * 2^-24 * sum_r |x_r| of the
+                               exact sum, and all N copies agree */
 };
 
 #define AR_MAX_RANKS 16

@@ -56,6 +56,9 @@ def lib():
                                              ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p,
                                              ctypes.c_void_p]
             L.oracle_add_rmsnorm.restype = None
+            L.oracle_sum_abs_f64.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                             ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+            L.oracle_sum_abs_f64.restype = None
             _lib = L
         return _lib
 
@@ -137,3 +140,17 @@ def add_rmsnorm(a, res, gamma, eps):
     lib().oracle_add_rmsnorm(a.ctypes.data, res.ctypes.data, gamma.ctypes.data, n, float(eps),
                              h.ctypes.data, y.ctypes.data)
     return h, y
+
+
+def sum_abs(inputs):
+    """Per element, the binary64 sum over ranks and the sum of magnitudes
+    (reference of the arrival-order atomic variant; see ar_oracle.c):
+    returns (sum, abs_sum), float64 [n] each."""
+    arrs = [np.ascontiguousarray(x, dtype=np.uint16) for x in inputs]
+    N = len(arrs)
+    n = arrs[0].size
+    ptrs = (ctypes.c_void_p * N)(*[a.ctypes.data for a in arrs])
+    s = np.empty(n, dtype=np.float64)
+    a = np.empty(n, dtype=np.float64)
+    lib().oracle_sum_abs_f64(ptrs, N, n, s.ctypes.data, a.ctypes.data)
+    return s, a

@@ -206,3 +206,29 @@ void oracle_add_rmsnorm(const uint16_t *a, const uint16_t *res, const uint16_t *
     for (size_t i = 0; i < n; ++i)
         y_out[i] = (double)widen_bf16(h_out[i]) * (double)widen_bf16(gamma[i]) * inv;
 }
+
+/*
+ * Reference for the atomic-lines variant ("微秒必争…" page, section
+ * "四大核心机制", item 4: ranks add into shared blocks with hardware atomics,
+ * so the order of the additions is the order of arrival).  No single
+ * binary32 result is "the" answer; what such a sum fixes is its distance
+ * from the exact sum: any order of N-1 binary32 additions of the N widened
+ * values lies within gamma_{N-1} * sum_r |x_r| of it (recursive summation
+ * bound, gamma_k = k u / (1 - k u), u = 2^-24).  This returns, per element,
+ * the binary64 sum (left to right; for bf16 inputs it is the exact sum
+ * unless the values span more than about 40 binades) and sum_r |x_r|.
+ */
+void oracle_sum_abs_f64(const uint16_t *const *in, int n_ranks, size_t n, double *sum,
+                        double *abs_sum)
+{
+    for (size_t i = 0; i < n; ++i) {
+        double s = 0.0, a = 0.0;
+        for (int r = 0; r < n_ranks; ++r) {
+            const double v = (double)widen_bf16(in[r][i]);
+            s += v;
+            a += fabs(v);
+        }
+        sum[i] = s;
+        abs_sum[i] = a;
+    }
+}

@@ -143,3 +143,15 @@ def norm_operands(cid: int, set_idx: int, n_ranks: int = None, replicated: bool 
     rng = np.random.Generator(np.random.PCG64(base + 19))
     gamma = _to_bf16_bits(rng.normal(1.0, 0.2, size=w.hidden).astype(np.float32))
     return np.stack(res), gamma
+
+
+def bounded_bits(seed: int, shape, exp_lo: int = -30, exp_hi: int = 30) -> np.ndarray:
+    """Random finite bfloat16 patterns with unbiased exponents in [exp_lo,
+    exp_hi) and random sign and mantissa: wide dynamic range, no overflow
+    when up to 16 of them are summed (edge cases of the arrival-order
+    variant, whose bound assumes no overflow)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint32) << 15
+    expo = rng.integers(127 + exp_lo, 127 + exp_hi, size=shape, dtype=np.uint32) << 7
+    mant = rng.integers(0, 128, size=shape, dtype=np.uint32)
+    return (sign | expo | mant).astype(np.uint16)

@@ -53,3 +53,20 @@ def test_y_violations_interval():
     assert y_violations(one, y).size == 0
     assert y_violations(up, y).size == 1
     assert y_violations(np.array([0x3F7F], dtype=np.uint16), y).size == 1
+
+
+def test_atomic_interval():
+    """The atomic variant's acceptance interval: for an exactly representable
+    sum only that value passes; where the slack straddles a rounding
+    boundary both neighbours pass, and nothing further out."""
+    from atomic_util import bf16_violations, slack
+    s = np.array([3.0])
+    a = np.array([3.0])
+    assert bf16_violations(np.array([0x4040], np.uint16), s, a, 2).size == 0      # 3.0
+    assert bf16_violations(np.array([0x4041], np.uint16), s, a, 2).size == 1
+    # a sum sitting on the midpoint between 1 and 1 + 2^-7, with a large sum|x|
+    s = np.array([1.0 + 2.0 ** -8])
+    a = np.array([2.0 ** 10])
+    assert slack(8, a)[0] > 2.0 ** -14
+    for bits, bad in ((0x3F80, 0), (0x3F81, 0), (0x3F82, 1), (0x3F7F, 1)):
+        assert bf16_violations(np.array([bits], np.uint16), s, a, 8).size == bad, hex(bits)

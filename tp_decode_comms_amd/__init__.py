@@ -8,7 +8,7 @@ loading fails loudly when the library is missing.
 from .ar import (  # noqa: F401
     AR_ALGO_AUTO, AR_ALGO_ONESHOT, AR_ALGO_TWOSHOT,
     AR_PROTO_AUTO, AR_PROTO_LL, AR_PROTO_LL128, AR_PROTO_SENTINEL, AR_PROTO_DIRECT,
-    AR_PROTO_BARRIER,
+    AR_PROTO_BARRIER, AR_PROTO_ATOMIC,
     AR_SCOPE_AUTO, AR_SCOPE_DEVICE,
     ArError, lib, lib_path, init, destroy, allreduce, allreduce_f32_debug, allreduce_add_rmsnorm,
     add_rmsnorm, gemv, set_options,

@@ -22,6 +22,7 @@ AR_SCOPE_AUTO, AR_SCOPE_DEVICE = 0, 1
 AR_ALGO_AUTO, AR_ALGO_ONESHOT, AR_ALGO_TWOSHOT = 0, 1, 2
 AR_PROTO_AUTO, AR_PROTO_LL, AR_PROTO_LL128, AR_PROTO_SENTINEL, AR_PROTO_DIRECT = 0, 1, 2, 3, 4
 AR_PROTO_BARRIER = 5
+AR_PROTO_ATOMIC = 6
 MAX_RANKS = 16
 
 _c_int, _c_u32, _c_size, _c_vp = ctypes.c_int, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_void_p

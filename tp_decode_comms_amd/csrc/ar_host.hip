@@ -40,6 +40,7 @@ struct Context {
     uint32_t *ctl = nullptr;
     uint32_t *done = nullptr;           // two-shot DIRECT completion flags
     uint32_t *stats = nullptr;          // fused norm: per-block sums of squares {sum, flag}
+    char *acc = nullptr;  size_t acc_stride = 0;   // atomic lines, per parity
     size_t stats_stride = 0;            // entries per rank
     // options
     int algo = AR_ALGO_AUTO;
@@ -82,7 +83,7 @@ size_t slice_len(size_t n, int n_ranks) { return round_up((n + n_ranks - 1) / n_
 
 void free_all()
 {
-    char **bufs[] = {&g.ll, &g.l128, &g.s1, &g.srs, &g.sag};
+    char **bufs[] = {&g.ll, &g.l128, &g.s1, &g.srs, &g.sag, &g.acc};
     for (char **b : bufs) {
         if (*b) (void)hipFree(*b);
         *b = nullptr;
@@ -118,6 +119,7 @@ size_t s1_bytes() { return g.s1_stride * 2 * g.n_ranks * g.n_ranks; }
 size_t s2_bytes() { return g.s2_stride * 2 * g.n_ranks * g.n_ranks; }
 size_t done_words() { return (size_t)ar::MAX_RANKS * ar::DONE_STRIDE; }
 size_t stats_bytes() { return g.stats_stride * 8 * g.n_ranks; }
+size_t acc_bytes() { return g.acc_stride * 2; }
 
 // Zero flags, arm sentinels, clear the control block -- kernels only.
 hipError_t rearm(hipStream_t s)
@@ -130,6 +132,7 @@ hipError_t rearm(hipStream_t s)
     if ((e = ar::launch_fill((uint32_t *)g.sag, s2_bytes() / 4, ar::SENT_WORD, s)) != hipSuccess) return e;
     if ((e = ar::launch_fill(g.done, done_words(), 0u, s)) != hipSuccess) return e;
     if ((e = ar::launch_fill(g.stats, stats_bytes() / 4, 0u, s)) != hipSuccess) return e;
+    if ((e = ar::launch_fill((uint32_t *)g.acc, acc_bytes() / 4, 0u, s)) != hipSuccess) return e;
     return ar::launch_fill(g.ctl, ar::CTL_WORDS, 0u, s);
 }
 
@@ -192,6 +195,8 @@ int choose_kind(size_t n, int *kind)
     if (algo == AR_ALGO_AUTO) {
         if (proto == AR_PROTO_LL)
             algo = AR_ALGO_ONESHOT;
+        else if (proto == AR_PROTO_ATOMIC)
+            algo = AR_ALGO_TWOSHOT;
         else
             algo = bytes <= ONESHOT_LIMIT_BYTES ? AR_ALGO_ONESHOT : AR_ALGO_TWOSHOT;
     }
@@ -206,6 +211,7 @@ int choose_kind(size_t n, int *kind)
             *kind = ar::K_ONESHOT_SENTINEL; return AR_OK;
         case AR_PROTO_DIRECT: *kind = ar::K_ONESHOT_DIRECT; return AR_OK;
         case AR_PROTO_BARRIER: *kind = ar::K_ONESHOT_BARRIER; return AR_OK;
+        default: break;                 // the atomic lines are a two-phase algorithm
         }
     } else {
         switch (proto) {
@@ -213,6 +219,7 @@ int choose_kind(size_t n, int *kind)
         case AR_PROTO_SENTINEL: *kind = ar::K_TWOSHOT_SENTINEL; return AR_OK;
         case AR_PROTO_DIRECT: *kind = ar::K_TWOSHOT_DIRECT; return AR_OK;
         case AR_PROTO_BARRIER: *kind = ar::K_TWOSHOT_BARRIER; return AR_OK;
+        case AR_PROTO_ATOMIC: *kind = ar::K_TWOSHOT_ATOMIC; return AR_OK;
         }
     }
     return AR_ERR_INVALID;
@@ -239,7 +246,8 @@ int plan_geometry(size_t n, bool f32, Plan *p)
         p->threads = 256;               // 4 waves share the peers of a tile
     else if (g.threads > 0)
         p->threads = (uint32_t)g.threads;
-    else if (l128 || p->kind == ar::K_TWOSHOT_DIRECT || p->kind == ar::K_TWOSHOT_BARRIER)
+    else if (l128 || p->kind == ar::K_TWOSHOT_DIRECT || p->kind == ar::K_TWOSHOT_BARRIER ||
+             p->kind == ar::K_TWOSHOT_ATOMIC)
         p->threads = 256;
     else
         p->threads = 2 * n <= 256 * 1024 ? 64 : 256;
@@ -258,6 +266,8 @@ int plan_geometry(size_t n, bool f32, Plan *p)
         units = p->slice / 8; per_wg = 64; break;
     case ar::K_TWOSHOT_DIRECT:
         units = p->slice / 8; per_wg = 2 * p->threads; break;
+    case ar::K_TWOSHOT_ATOMIC:      // lines of 31 elements, two per wave
+        units = (n + ar::ATOM_LINE_ELEMS - 1) / ar::ATOM_LINE_ELEMS; per_wg = p->threads / 32; break;
     default:
         units = n / 8; per_wg = p->threads; break;
     }
@@ -382,6 +392,7 @@ void fill_launch(const void *const *rank_bufs, void *out, size_t n, uint32_t epo
     a.ll = g.ll; a.l128 = g.l128; a.s1 = g.s1; a.srs = g.srs; a.sag = g.sag;
     a.ctl = g.ctl;
     a.done = g.done;
+    a.acc = g.acc; a.acc_stride = (uint32_t)g.acc_stride;
     a.ts = g.ts; a.ts_slots = (uint32_t)g.ts_slots;
     a.delays = g.delays; a.delay_rows = (uint32_t)g.delay_rows;
     a.ll_stride = (uint32_t)g.ll_stride; a.l128_stride = (uint32_t)g.l128_stride;
@@ -539,11 +550,12 @@ int ar_init(int n_ranks, size_t max_elems)
     g.s1_stride = round_up(me * 2, 256);
     g.s2_stride = round_up(slice_len(me, n_ranks) * 2, 256);
     g.stats_stride = (me + ar::NORM_BLOCK_ELEMS - 1) / ar::NORM_BLOCK_ELEMS;
+    g.acc_stride = round_up((me + ar::ATOM_LINE_ELEMS - 1) / ar::ATOM_LINE_ELEMS * 128, 256);
     // every staging region and the output tensor are addressed through one
     // buffer descriptor with 32-bit offsets; a region that would not fit is
     // not allocated and its protocol is unavailable for this context
     if (me * (size_t)n_ranks * 4 > REGION_LIMIT || ll_bytes() > REGION_LIMIT ||
-        l128_bytes() > REGION_LIMIT || s2_bytes() > REGION_LIMIT)
+        l128_bytes() > REGION_LIMIT || s2_bytes() > REGION_LIMIT || acc_bytes() > REGION_LIMIT)
         return AR_ERR_INVALID;
     int rc;
     if ((rc = alloc(&g.ll, ll_bytes())) != AR_OK ||
@@ -553,7 +565,8 @@ int ar_init(int n_ranks, size_t max_elems)
         (rc = alloc(&g.sag, s2_bytes())) != AR_OK ||
         (rc = alloc((char **)&g.ctl, ar::CTL_WORDS * 4)) != AR_OK ||
         (rc = alloc((char **)&g.done, done_words() * 4)) != AR_OK ||
-        (rc = alloc((char **)&g.stats, stats_bytes())) != AR_OK) {
+        (rc = alloc((char **)&g.stats, stats_bytes())) != AR_OK ||
+        (rc = alloc(&g.acc, acc_bytes())) != AR_OK) {
         free_all();
         return rc;
     }
@@ -640,9 +653,11 @@ int ar_set_options(int algo, int proto)
         return AR_ERR_NOT_INIT;
     if (algo < AR_ALGO_AUTO || algo > AR_ALGO_TWOSHOT)
         return AR_ERR_INVALID;
-    if (proto < AR_PROTO_AUTO || proto > AR_PROTO_BARRIER)
+    if (proto < AR_PROTO_AUTO || proto > AR_PROTO_ATOMIC)
         return AR_ERR_INVALID;
     if (algo == AR_ALGO_TWOSHOT && proto == AR_PROTO_LL)
+        return AR_ERR_INVALID;
+    if (algo == AR_ALGO_ONESHOT && proto == AR_PROTO_ATOMIC)
         return AR_ERR_INVALID;
     g.algo = algo;
     g.proto = proto;
@@ -777,7 +792,8 @@ long long ar_query(int key, size_t n)
             return rc;
         if (key == 2)
             return (p.kind == ar::K_TWOSHOT_LL128 || p.kind == ar::K_TWOSHOT_SENTINEL ||
-                    p.kind == ar::K_TWOSHOT_DIRECT || p.kind == ar::K_TWOSHOT_BARRIER)
+                    p.kind == ar::K_TWOSHOT_DIRECT || p.kind == ar::K_TWOSHOT_BARRIER ||
+                    p.kind == ar::K_TWOSHOT_ATOMIC)
                        ? AR_ALGO_TWOSHOT : AR_ALGO_ONESHOT;
         if (key == 3) {
             switch (p.kind) {
@@ -788,6 +804,7 @@ long long ar_query(int key, size_t n)
             case ar::K_TWOSHOT_BARRIER: return AR_PROTO_BARRIER;
             case ar::K_ONESHOT_SENTINEL:
             case ar::K_TWOSHOT_SENTINEL: return AR_PROTO_SENTINEL;
+            case ar::K_TWOSHOT_ATOMIC: return AR_PROTO_ATOMIC;
             default: return AR_PROTO_LL128;
             }
         }

@@ -13,6 +13,8 @@ struct NormLaunch;
 // block of one partial sum, at most 65536
 constexpr size_t NORM_BLOCK_ELEMS = 256;
 constexpr size_t NORM_HIDDEN_LIMIT = 65536;
+// atomic lines: 128 bytes = a 4-byte counter and 31 binary32 sums
+constexpr size_t ATOM_LINE_ELEMS = 31;
 
 enum KernelKind {
     K_ONESHOT_LL = 0,
@@ -25,7 +27,8 @@ enum KernelKind {
     K_ONESHOT_BARRIER = 7,
     K_TWOSHOT_BARRIER = 8,
     K_ONESHOT_LL_NORM = 9,      // one-shot LL + residual add + RMS norm (bf16 only)
-    K_COUNT = 10
+    K_TWOSHOT_ATOMIC = 10,      // atomic lines (arrival-order sums: not bit-exact)
+    K_COUNT = 11
 };
 
 // device function of a kernel kind for n_ranks (<= 8 or <= 16 instantiation);

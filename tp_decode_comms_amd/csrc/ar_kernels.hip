@@ -1488,6 +1488,111 @@ __global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
     finish(a, c);
 }
 
+// =========================================================== atomic lines
+// The atomic two-phase algorithm of [EMC] ("四大核心机制", item 4: 128-byte
+// blocks whose first 4 bytes are an atomic counter; every rank adds its data
+// into the shared block with hardware atomics and bumps the counter; a block
+// is complete when its counter reads N), on one GPU: binary32 atomic adds
+// (performed where the device's atomics are, coherent for all workgroups)
+// into lines of {counter, 31 x binary32} in a shared accumulator region.
+//   phase 1 (reduce-scatter into the shared lines): each rank adds its 31
+//     values of the line, waits until the adds are acknowledged, then adds 1
+//     to the counter;
+//   phase 2 (gather): each rank polls the counter until it reaches N, reads
+//     the 31 sums and writes its output copy.
+// The line cleans itself: after its read each rank adds 1 more, and the
+// rank whose increment brings the counter to 2N (the last reader) zeroes
+// the line.  So a line is zero again before the next call on that parity
+// buffer can start (that call follows a call in which every rank completed
+// this one), whatever protocols the calls in between used.
+// The sums are taken in arrival order, so unlike every other kernel here the
+// result is not the fixed-order fold: it is within (N-1) * 2^-24 * sum|x| of
+// the exact sum before the bf16 rounding, and all N output copies agree.
+// Lane layout: a wave holds two lines, a half-wave each; lane j of a half
+// is the counter (j = 0) or element j-1 of the line.
+constexpr uint32_t ATOM_ELEMS = (uint32_t)ATOM_LINE_ELEMS;     // binary32 sums per 128-byte line
+constexpr uint32_t ATOM_LINE = 128;
+
+template <int NMAX, bool F32, bool LOCAL>
+__global__ __launch_bounds__(256) void k_twoshot_atomic(const Launch a)
+{
+    Ctx0 c;
+    begin<LOCAL>(a, c);
+    const uint32_t N = a.n_ranks;
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t half = lane >> 5, j = lane & 31u;
+    const uint32_t lines = (a.n + ATOM_ELEMS - 1u) / ATOM_ELEMS;
+    const uint32_t per_wg = (blockDim.x >> 6) * 2u;             // lines per workgroup round
+    const uint32_t step = a.parts * per_wg;
+    const __amdgpu_buffer_rsrc_t inr = in_rsrc(a, c.rank);
+    const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
+    // accumulator lines [parity][line] x 128 B, zero between calls
+    const __amdgpu_buffer_rsrc_t acc = rsrc(a.acc, 2u * a.acc_stride);
+    const Ctl ctl{a.ctl};
+    c.flag = load_seq(a) + a.epoch;
+    start_delay(a, c);
+    for (uint32_t l0 = c.part * per_wg; l0 < lines; l0 += step) {
+        const uint32_t line = l0 + wave * 2u + half;
+        const bool live = line < lines;
+        const uint32_t e = line * ATOM_ELEMS + j - 1u;           // element of data lanes
+        const bool data = live && j != 0u && e < a.n;
+        const uint32_t base = c.par * a.acc_stride + line * ATOM_LINE;
+        // phase 1: add this rank's values, then count this rank in
+        if (data) {
+            const uint32_t w = ld4<CP_PLAIN>(inr, (e & ~1u) * 2u);
+            const float v = (e & 1u) ? hi_f(w) : lo_f(w);
+            (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, acc, base + 4u * j, 0, 0);
+        }
+        wait_stores();                                          // the adds are performed
+        if (live && j == 0u)
+            (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, acc, base, 0, 0);
+        // phase 2: wait for all N ranks' adds (two polls in flight)
+        bool pend = live && j == 0u;
+        Watch w;
+        w.begin(a.watchdog_ticks);
+        uint32_t v0 = pend ? ld4<CP_DEV>(acc, base) : 0u, v1;
+        bool ok = true;
+        while (true) {
+            compiler_fence();
+            v1 = pend ? ld4<CP_DEV>(acc, base) : 0u;
+            if (pend && v0 >= N)
+                pend = false;
+            if (!wave_any(pend))
+                break;
+            if (w.expired(ctl, c.rank, line, c.flag)) {
+                ok = false;
+                break;
+            }
+            compiler_fence();
+            v0 = pend ? ld4<CP_DEV>(acc, base) : 0u;
+            if (pend && v1 >= N)
+                pend = false;
+            if (!wave_any(pend))
+                break;
+        }
+        if (!ok)
+            break;                      // status recorded; every wave still reaches finish()
+        const uint32_t sb = data ? ld4<CP_DEV>(acc, base + 4u * j) : 0u;
+        const float sum = __uint_as_float(sb);
+        wait_stores();                                          // the read has returned
+        // count this rank's read; the last reader zeroes the line
+        uint32_t before = 0u;
+        if (live && j == 0u)
+            before = (uint32_t)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, acc, base, 0, 0);
+        const uint64_t last = __builtin_amdgcn_ballot_w64(live && j == 0u && before == 2u * N - 1u);
+        if ((last >> (32u * half)) & 1u)
+            st4<CP_DEV>(0u, acc, base + 4u * j);
+        if (data) {
+            if constexpr (F32)
+                st4<CP_PLAIN>(__float_as_uint(sum), o, e * 4u);
+            else
+                __builtin_amdgcn_raw_buffer_store_b16(
+                    (uint16_t)__builtin_bit_cast(uint16_t, (__bf16)sum), o, e * 2u, 0, CP_PLAIN);
+        }
+    }
+    finish(a, c);
+}
+
 // ============================================================ maintenance
 // Advances the flag sequence after a step of `calls` calls.  When the
 // sequence nears the top of its 32-bit range, every flag word (LL units,
@@ -1556,6 +1661,7 @@ static const void *pick(int kind)
     case K_TWOSHOT_DIRECT: return (const void *)k_twoshot_direct<NMAX, F32, LOCAL>;
     case K_ONESHOT_BARRIER: return (const void *)k_oneshot_barrier<NMAX, F32, LOCAL>;
     case K_TWOSHOT_BARRIER: return (const void *)k_twoshot_barrier<NMAX, F32, LOCAL>;
+    case K_TWOSHOT_ATOMIC: return (const void *)k_twoshot_atomic<NMAX, F32, LOCAL>;
     case K_ONESHOT_LL_NORM:         // bf16 only
         return F32 ? nullptr : (const void *)k_oneshot_ll_norm<NMAX, LOCAL>;
     default: return nullptr;

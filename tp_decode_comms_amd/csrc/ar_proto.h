@@ -89,7 +89,8 @@ struct Launch {
     uint64_t *ts;                 // timestamps [slots][2] or null
     const uint32_t *delays;       // start delays [rows][N] ns or null
     uint32_t *done;               // two-shot DIRECT completion flags (MAX_RANKS*DONE_STRIDE words)
-    uint32_t ll_stride, l128_stride, s1_stride, s2_stride;
+    char *acc;                    // atomic accumulator lines [parity] x acc_stride, zero between calls
+    uint32_t ll_stride, l128_stride, s1_stride, s2_stride, acc_stride;
     uint32_t n;                   // elements per rank
     uint32_t n_ranks;
     uint32_t epoch;
