@@ -252,6 +252,16 @@ def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact=True
         ev[k][1].record(stream)
     torch.cuda.synchronize()
     us = np.array([a.elapsed_time(b) * 1000.0 for a, b in ev])
+    # the same calls back to back with one event pair around the whole
+    # region: the average launch duration, gaps between launches included
+    # but no event packet between the calls
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for k in range(calls):
+        call(k)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    region_us = r0.elapsed_time(r1) * 1000.0 / calls
     status = ar.get_status()
     worst = None
     if exact:
@@ -265,6 +275,8 @@ def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact=True
                     "sets (footprint %d MiB)" % (label, (2 * nsets * wl.N * 2 * wl.n) >> 20),
         "algo": label, "grid": grid, "threads": threads, "xcd_local_scope": local,
         "us_per_call": summary(us),
+        "region_us_per_call": region_us,
+        "gbps_region": wl.b_alg / (region_us * 1e-6) / 1e9,
         "b_alg_bytes": wl.b_alg,
         "gbps_p50": wl.b_alg / (np.percentile(us, 50) * 1e-6) / 1e9,
         "gbps_mean": wl.b_alg / (us.mean() * 1e-6) / 1e9,
@@ -603,7 +615,8 @@ def main():
             r = bench_bandwidth(torch, ar, wl4, args.bw_calls, args.warmup, algo, proto, label)
             results[key] = r
             bws.append(r)
-            log("  %.1f GB/s (p50 %.2f us/call)" % (r["gbps_p50"], r["us_per_call"]["p50"]))
+            log("  %.1f GB/s back to back (%.2f us/call); per-call events p50 %.2f us"
+                % (r["gbps_region"], r["region_us_per_call"], r["us_per_call"]["p50"]))
         bws = [r for r in bws if r is not results["bw_4m_twoshot_barrier"]]
         results["barrier_cost_4m_us"] = round(
             results["bw_4m_twoshot_barrier"]["us_per_call"]["p50"] -
@@ -673,17 +686,21 @@ def main():
         line["config"] = {"workload": lat["workload"], "n_ranks": 8, "elems_per_rank": 8192,
                           "calls_per_step": CALLS_PER_STEP, "launch": "hipGraph"}
     if bws:
-        best = max(bws, key=lambda r: r["gbps_p50"])
-        avg_us = best["us_per_call"]["mean"]
+        # throughput of back-to-back calls: events around the whole timed
+        # region (an event packet between calls would add its own gap)
+        best = max(bws, key=lambda r: r["gbps_region"])
+        avg_us = best["region_us_per_call"]
         achieved = best["b_alg_bytes"] / (avg_us * 1e-6) / 1e9
-        line["gbps_4mb"] = round(best["gbps_p50"], 2)
-        line["gbps_4mb_frac_of_peak"] = round(best["gbps_p50"] / HBM_PEAK_GBS, 4)
+        line["gbps_4mb"] = round(best["gbps_region"], 2)
+        line["gbps_4mb_frac_of_peak"] = round(best["gbps_region"] / HBM_PEAK_GBS, 4)
+        line["gbps_4mb_per_call_events_p50"] = round(best["gbps_p50"], 2)
         traffic = recorded_traffic("k_twoshot_direct") if best is results.get(
             "bw_4m_twoshot_direct") else None
         line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                             "traffic": traffic, "kernel": best["algo"],
-                            "per_launch_bytes": best["b_alg_bytes"], "avg_launch_us": avg_us}
+                            "per_launch_bytes": best["b_alg_bytes"], "avg_launch_us": avg_us,
+                            "avg_launch_us_with_per_call_events": best["us_per_call"]["mean"]}
     line["cpu_baseline"] = cpu
     line["parity_ok"] = all(r.get("mismatches", 0) == 0 and r.get("status", [0])[0] == 0
                             for k, r in results.items() if isinstance(r, dict) and "status" in r)

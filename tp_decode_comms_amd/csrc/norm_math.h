@@ -10,9 +10,9 @@
 // with S the binary32 sum of h[j]^2 over the row.  S is always formed in one
 // order, whichever kernel computes it: per 256-element block (64 lanes x 4
 // consecutive elements), each lane sums its 4 squares left to right with
-// fused multiply-adds, then the 64 lane sums meet in a xor butterfly
-// (offsets 32, 16, ..., 1); the row's block sums are then folded the same
-// way, lane l holding blocks l, l+64, l+128, ... added in that order.  Both
+// fused multiply-adds, then the 64 lane sums meet in the fixed tree of
+// wave_sum(); the row's block sums are then folded the same way, lane l
+// holding blocks l, l+64, l+128, ... added in that order.  Both
 // the fused kernel (each workgroup round yields one block's sum; the sums
 // meet through memory) and the stand-alone kernel (one workgroup per row,
 // block sums in LDS) follow it, so their h and y agree bit for bit.
@@ -48,15 +48,28 @@ __device__ __forceinline__ float sumsq4(u32x2 h)
     return s;
 }
 
-// Wave-wide sum by xor butterfly.  Binary32 addition commutes, so the two
-// lanes of every pair compute the same bits at every level and all 64 lanes
-// end with one identical result.
+// Wave-wide sum in a fixed tree.  Within each 16-lane row four DPP steps
+// pair lane i with i^1, i^2 (quad permutes), then the mirror lane of its
+// 8-lane half and of its row; binary32 addition commutes, so both lanes of
+// every pair compute the same bits and the whole row ends with one value.
+// The four row sums are then read as uniform values and added as
+// (r0 + r1) + (r2 + r3), so all 64 lanes return identical bits.
+template <int CTRL> __device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1)
-        v += __shfl_xor(v, k, 64);
-    return v;
+    v += dpp<0xB1>(v);          // quad_perm(1,0,3,2): lane i ^ 1
+    v += dpp<0x4E>(v);          // quad_perm(2,3,0,1): lane i ^ 2
+    v += dpp<0x141>(v);         // row_half_mirror: lane 7 - i within 8
+    v += dpp<0x140>(v);         // row_mirror: lane 15 - i within 16
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // r = 1 / sqrt(S / hidden + eps): IEEE division and square root
