@@ -265,7 +265,7 @@ int plan_geometry(size_t n, bool f32, Plan *p)
     case ar::K_TWOSHOT_SENTINEL:
         units = p->slice / 8; per_wg = 64; break;
     case ar::K_TWOSHOT_DIRECT:
-        units = p->slice / 8; per_wg = 2 * p->threads; break;
+        units = p->slice / 8; per_wg = ar::TWOSHOT_DIRECT_CHUNKS * p->threads; break;
     case ar::K_TWOSHOT_ATOMIC:      // lines of 31 elements, two per wave
         units = (n + ar::ATOM_LINE_ELEMS - 1) / ar::ATOM_LINE_ELEMS; per_wg = p->threads / 32; break;
     default:

@@ -13,6 +13,8 @@ struct NormLaunch;
 // block of one partial sum, at most 65536
 constexpr size_t NORM_BLOCK_ELEMS = 256;
 constexpr size_t NORM_HIDDEN_LIMIT = 65536;
+// two-shot DIRECT: 8-element chunks each lane reduces per round
+constexpr uint32_t TWOSHOT_DIRECT_CHUNKS = 2;
 // atomic lines: 128 bytes = a 4-byte counter and 31 binary32 sums
 constexpr size_t ATOM_LINE_ELEMS = 31;
 

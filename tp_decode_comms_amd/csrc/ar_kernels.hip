@@ -704,6 +704,10 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
 // slice of that rank's output is known to be complete.
 // Moves exactly the algorithmic bytes: N inputs read once, N outputs written
 // once.
+constexpr uint32_t TS_CPI = TWOSHOT_DIRECT_CHUNKS;   // chunks per lane per round
+constexpr int TS_LD = CP_DEV;                       // input loads
+constexpr int TS_ST = CP_NT | CP_DEV;               // output stores (streaming)
+
 template <int NMAX, bool F32, bool LOCAL>
 __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
 {
@@ -727,30 +731,38 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     for (int s = 0; s < NMAX; ++s)
         src[s] = in_rsrc(a, (uint32_t)s < N ? (uint32_t)s : 0u);
     const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
-    // two chunks per lane per round keep more loads in flight
-    for (uint32_t ch = c.part * blockDim.x + threadIdx.x; ch < G; ch += 2u * step) {
-        const uint32_t ch2 = ch + step;
-        const bool two = ch2 < G;
-        u32x4 V[NMAX], W[NMAX];
+    // TS_CPI chunks per lane per round keep more loads in flight (2 measured
+    // best: 1 or a streaming load policy lose 5-20% at 4 MiB per rank)
+    for (uint32_t ch = c.part * blockDim.x + threadIdx.x; ch < G; ch += TS_CPI * step) {
+        u32x4 V[TS_CPI][NMAX];
+        bool in[TS_CPI];
+#pragma unroll
+        for (int k = 0; k < TS_CPI; ++k)
+            in[k] = ch + k * step < G;
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             if ((uint32_t)s < N) {
-                V[s] = ld16<CP_DEV>(src[s], (lo + ch * 8u) * 2u);
-                W[s] = two ? ld16<CP_DEV>(src[s], (lo + ch2 * 8u) * 2u) : u32x4{0u, 0u, 0u, 0u};
-            }
-        Acc8 acc, acc2;
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N) {
-                if (s == 0) { acc.init(V[s]); acc2.init(W[s]); }
-                else { acc.add(V[s]); acc2.add(W[s]); }
+                for (int k = 0; k < TS_CPI; ++k)
+                    V[k][s] = in[k] ? ld16<TS_LD>(src[s], (lo + (ch + k * step) * 8u) * 2u)
+                                    : u32x4{0u, 0u, 0u, 0u};
             }
+        Acc8 acc[TS_CPI];
+#pragma unroll
+        for (int k = 0; k < TS_CPI; ++k)
+#pragma unroll
+            for (int s = 0; s < NMAX; ++s)
+                if ((uint32_t)s < N) {
+                    if (s == 0) acc[k].init(V[k][s]);
+                    else acc[k].add(V[k][s]);
+                }
 #pragma unroll
         for (int r = 0; r < NMAX; ++r)
             if ((uint32_t)r < N) {
-                store8<F32, CP_NT | CP_DEV>(oa, (uint32_t)r * a.n + lo + ch * 8u, acc);
-                if (two)
-                    store8<F32, CP_NT | CP_DEV>(oa, (uint32_t)r * a.n + lo + ch2 * 8u, acc2);
+#pragma unroll
+                for (int k = 0; k < TS_CPI; ++k)
+                    if (in[k])
+                        store8<F32, TS_ST>(oa, (uint32_t)r * a.n + lo + (ch + k * step) * 8u, acc[k]);
             }
     }
     // completion: my stores are at the coherence point, then my flag.  The
