@@ -724,8 +724,28 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     const Ctl ctl{a.ctl};
     start_delay(a, c);
     raise_arrival<LOCAL>(a, c);
+    // A rank's own input needs no arrival flag: the waves that do not poll
+    // load their first round's own chunks before the wait, so HBM is busy
+    // while the flags travel (the polling wave cannot: its loads return in
+    // order, so a pending data load would delay every poll behind it).
+    const uint32_t ch0 = c.part * blockDim.x + threadIdx.x;
+    const __amdgpu_buffer_rsrc_t srcq = in_rsrc(a, q);
+    u32x4 own[TS_CPI];
+    const bool poller = threadIdx.x < 64u;
+    if (!poller) {
+#pragma unroll
+        for (int k = 0; k < TS_CPI; ++k)
+            own[k] = ch0 + k * step < G ? ld16<TS_LD>(srcq, (lo + (ch0 + k * step) * 8u) * 2u)
+                                        : u32x4{0u, 0u, 0u, 0u};
+    }
     if (!wait_arrivals_wg<LOCAL>(a, c, ctl))
         return;
+    if (poller) {
+#pragma unroll
+        for (int k = 0; k < TS_CPI; ++k)
+            own[k] = ch0 + k * step < G ? ld16<TS_LD>(srcq, (lo + (ch0 + k * step) * 8u) * 2u)
+                                        : u32x4{0u, 0u, 0u, 0u};
+    }
     __amdgpu_buffer_rsrc_t src[NMAX];
 #pragma unroll
     for (int s = 0; s < NMAX; ++s)
@@ -733,9 +753,10 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
     // TS_CPI chunks per lane per round keep more loads in flight (2 measured
     // best: 1 or a streaming load policy lose 5-20% at 4 MiB per rank)
-    for (uint32_t ch = c.part * blockDim.x + threadIdx.x; ch < G; ch += TS_CPI * step) {
+    for (uint32_t ch = ch0; ch < G; ch += TS_CPI * step) {
         u32x4 V[TS_CPI][NMAX];
         bool in[TS_CPI];
+        const bool first = ch == ch0;
 #pragma unroll
         for (int k = 0; k < TS_CPI; ++k)
             in[k] = ch + k * step < G;
@@ -744,8 +765,9 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
             if ((uint32_t)s < N) {
 #pragma unroll
                 for (int k = 0; k < TS_CPI; ++k)
-                    V[k][s] = in[k] ? ld16<TS_LD>(src[s], (lo + (ch + k * step) * 8u) * 2u)
-                                    : u32x4{0u, 0u, 0u, 0u};
+                    V[k][s] = (first && (uint32_t)s == q) ? own[k]
+                              : in[k] ? ld16<TS_LD>(src[s], (lo + (ch + k * step) * 8u) * 2u)
+                                      : u32x4{0u, 0u, 0u, 0u};
             }
         Acc8 acc[TS_CPI];
 #pragma unroll
