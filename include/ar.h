@@ -103,9 +103,12 @@ enum ar_proto {
  * ar_init -- create the context on the current HIP device.
  *   n_ranks:   number of emulated ranks, 1..16.
  *   max_elems: largest per-rank element count any later call may use, > 0,
- *              at most 2^28, with n_ranks * max_elems * 4 < 2^32 (every
- *              staging region and the output tensor are addressed with
- *              32-bit offsets).  When the one-shot sentinel inboxes
+ *              at most 2^28.  Every staging region and the output tensor are
+ *              addressed with 32-bit offsets, so each must stay below 2^32
+ *              bytes; the binding one is the LL region,
+ *              2 * n_ranks * round_up(4 * max_elems, 256) bytes, which gives
+ *              max_elems <= 2^29 / n_ranks - 64 (2^26 - 64 for 8 ranks,
+ *              128 MiB of bf16 per rank).  When the one-shot sentinel inboxes
  *              (4 * n_ranks^2 * max_elems bytes) would exceed that, they are
  *              not allocated and the one-shot sentinel protocol is refused
  *              (AR_ERR_INVALID) for this context.
