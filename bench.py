@@ -701,6 +701,14 @@ def main():
                             "traffic": traffic, "kernel": best["algo"],
                             "per_launch_bytes": best["b_alg_bytes"], "avg_launch_us": avg_us,
                             "avg_launch_us_with_per_call_events": best["us_per_call"]["mean"]}
+    if lat is not None and "floor" in results:
+        # the latency kernel is bound by the launch floor plus its in-XCD
+        # hops, not by HBM: how close the call is to an empty graph node
+        fl = results["floor"]["us_per_node_p50"]
+        line["latency_floor"] = {"bound": "launch", "floor_us": round(fl, 4),
+                                 "achieved_us": line["value"],
+                                 "frac": round(fl / line["value"], 4),
+                                 "kernel_work_us": round(line["value"] - fl, 4)}
     line["cpu_baseline"] = cpu
     line["parity_ok"] = all(r.get("mismatches", 0) == 0 and r.get("status", [0])[0] == 0
                             for k, r in results.items() if isinstance(r, dict) and "status" in r)
