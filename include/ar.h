@@ -212,10 +212,15 @@ int ar_destroy(void);
 
 /*
  * ar_set_options -- choose the algorithm and protocol for later calls.
- * AUTO picks by message size S = 2n bytes per rank: S <= 64 KiB -> one-shot
- * LL; otherwise two-shot DIRECT (section "统一原语与API设计", table of
- * variants: one-shot below 64 KiB, two-shot above).  LL exists only as
- * one-shot.  AR_ERR_INVALID for an unknown value or an impossible pair.
+ * AUTO picks by message size S = 2n bytes per rank, as measured on MI355X
+ * (the pages' table of variants in section "统一原语与API设计" puts the
+ * one-shot/two-shot crossover at 64 KB on NVLink; in-place one-shot reads
+ * stay ahead much longer here): S <= 16 KiB -> one-shot LL; S < 1 MiB ->
+ * one-shot DIRECT; otherwise two-shot DIRECT.  With a protocol fixed and
+ * the algorithm AUTO, one-shot is used up to that protocol's crossover
+ * (sentinel 64 KiB, LL128 256 KiB, DIRECT and barrier just below 1 MiB);
+ * LL is always one-shot and the atomic lines always two-shot.
+ * AR_ERR_INVALID for an unknown value or an impossible pair.
  */
 int ar_set_options(int algo, int proto);
 

@@ -186,3 +186,17 @@ def test_xcd_local_scope_is_used():
             assert a.query(8, n) == 1, n
         a.set_scope(ar.AR_SCOPE_DEVICE)
         assert a.query(8, 8192) == 0
+
+
+def test_auto_selection():
+    """AUTO follows the crossovers measured on MI355X (include/ar.h)."""
+    with ar_context(8, 1 << 20) as a:
+        for kib, algo, proto in ((4, ONE, LL), (16, ONE, LL), (32, ONE, DIRECT), (512, ONE, DIRECT),
+                                 (1024 - 16, ONE, DIRECT), (1024, TWO, DIRECT)):
+            n = kib * 512
+            assert (a.query(2, n), a.query(3, n)) == (algo, proto), kib
+        for p, last_one in ((SENT, 64), (LL128, 256), (DIRECT, 1024 - 16)):
+            a.set_options(0, p)
+            assert a.query(2, last_one * 512) == ONE, (p, last_one)
+            nxt = 1024 if p == DIRECT else 2 * last_one
+            assert a.query(2, nxt * 512) == TWO, (p, nxt)

@@ -3,8 +3,8 @@
 // Owns the single process-wide context: staging for every protocol (per
 // rank x 2 parities), the control block (flag-sequence base, status record,
 // arrival flags), launch geometry, the epoch sequence check and the
-// algorithm/protocol choice of the pages' table of variants ("微秒必争…",
-// section "统一原语与API设计": one-shot below 64 KiB, two-shot from 64 KiB).
+// algorithm/protocol choice (the pages' table of variants, "微秒必争…",
+// section "统一原语与API设计", re-measured for this chip: see oneshot_limit).
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -24,7 +24,24 @@ using ar::Launch;
 
 constexpr size_t MAX_ELEMS_LIMIT = size_t(1) << 28;
 constexpr uint32_t DEFAULT_WATCHDOG_US = 200000;
-constexpr size_t ONESHOT_LIMIT_BYTES = 64 * 1024;   // per-rank message size
+// Automatic selection by per-rank message size S = 2n bytes, from a sweep
+// of every algorithm/protocol pair on MI355X (8 ranks, 4 KiB - 4 MiB, graphs
+// of calls).  The pages' table (one-shot below 64 KB, two-shot above) was
+// drawn for NVLink; here the in-place one-shot stays ahead much longer:
+//   LL one-shot up to 16 KiB (ties with one-shot DIRECT there),
+//   one-shot DIRECT below 1 MiB (e.g. 256 KiB: 3.5 us vs 5.8 two-shot),
+//   two-shot DIRECT from 1 MiB (1 MiB: 7.3 vs 7.9; 4 MiB: 14.1 vs 18.7).
+// With a protocol fixed and the algorithm left to AUTO, the one-shot limit
+// is that protocol's own crossover.
+constexpr size_t AUTO_LL_MAX_BYTES = 16 * 1024;
+size_t oneshot_limit(int proto)
+{
+    switch (proto) {
+    case AR_PROTO_SENTINEL: return 64 * 1024;          // two-shot ahead from 128 KiB
+    case AR_PROTO_LL128: return 256 * 1024;            // two-shot ahead from 512 KiB
+    default: return 1024 * 1024 - 1;                   // DIRECT, barrier, AUTO
+    }
+}
 
 struct Context {
     bool live = false;
@@ -198,10 +215,11 @@ int choose_kind(size_t n, int *kind)
         else if (proto == AR_PROTO_ATOMIC)
             algo = AR_ALGO_TWOSHOT;
         else
-            algo = bytes <= ONESHOT_LIMIT_BYTES ? AR_ALGO_ONESHOT : AR_ALGO_TWOSHOT;
+            algo = bytes <= oneshot_limit(proto) ? AR_ALGO_ONESHOT : AR_ALGO_TWOSHOT;
     }
     if (proto == AR_PROTO_AUTO)
-        proto = algo == AR_ALGO_ONESHOT ? AR_PROTO_LL : AR_PROTO_DIRECT;
+        proto = algo == AR_ALGO_TWOSHOT ? AR_PROTO_DIRECT
+                : bytes <= AUTO_LL_MAX_BYTES ? AR_PROTO_LL : AR_PROTO_DIRECT;
     if (algo == AR_ALGO_ONESHOT) {
         switch (proto) {
         case AR_PROTO_LL: *kind = ar::K_ONESHOT_LL; return AR_OK;
