@@ -377,19 +377,22 @@ def bench_overlap(torch, ar, layers=20, replays=10, warmup=2):
     }
 
 
-def bench_norm(torch, ar, replays=20, warmup=3, layers=80):
+def bench_norm(torch, ar, cid=2, replays=20, warmup=3, layers=80):
     """The AllReduce with the residual add + RMS norm fused into its launch
     against the unfused sequence (AllReduce, then the stand-alone norm
-    kernel) and against the bare AllReduce, on the 16 KiB/rank decode shape:
-    160 calls (80 layers x 2) per hipGraph.  h must match the oracle bit for
-    bit, fused and unfused y must agree bit for bit, and y must lie within
-    one bf16 unit in the last place of the oracle's exact value."""
+    kernel) and against the bare AllReduce: 160 calls (80 layers x 2) per
+    hipGraph, on the 16 KiB/rank decode shape (workload 2, one-shot LL) or
+    the batched 512 KiB/rank shape (workload 3, automatic choice: the
+    in-place one-shot).  h must match the oracle bit for bit, fused and
+    unfused y must agree bit for bit, and y must lie within one bf16 unit in
+    the last place of the oracle's exact value."""
     import oracle
     import synth
-    N, n = 8, 8192
+    w = synth.WORKLOADS[cid]
+    N, n, rows, hidden = w.n_ranks, w.n, w.rows, w.hidden
     calls = 2 * layers
-    wl = Workload(torch, 2, 4)
-    res, gamma = synth.norm_operands(2, 0, replicated=True)
+    wl = Workload(torch, cid, 4)
+    res, gamma = synth.norm_operands(cid, 0, replicated=True)
     rs = [to_dev(torch, res[r]) for r in range(N)]
     g = to_dev(torch, gamma)
     eps = synth.NORM_EPS
@@ -397,7 +400,8 @@ def bench_norm(torch, ar, replays=20, warmup=3, layers=80):
     outs, hs, ys, uh, uy = mk(), mk(), mk(), mk(), mk()
     stream = torch.cuda.Stream()
     ar.init(N, n)
-    ar.set_options(ONE, LL)
+    if cid == 2:
+        ar.set_options(ONE, LL)
 
     def timed(build):
         gr = torch.cuda.CUDAGraph()
@@ -425,13 +429,14 @@ def bench_norm(torch, ar, replays=20, warmup=3, layers=80):
 
     def fused():
         for k in range(calls):
-            ar.allreduce_add_rmsnorm(wl.ins[k % 4], rs, g, eps, hs[k % 4], ys[k % 4], 1, n, k + 1,
-                                     stream=stream)
+            ar.allreduce_add_rmsnorm(wl.ins[k % 4], rs, g, eps, hs[k % 4], ys[k % 4], rows, hidden,
+                                     k + 1, stream=stream)
 
     def unfused():
         for k in range(calls):
             ar.allreduce(wl.ins[k % 4], outs[k % 4], n, k + 1, stream=stream)
-            ar.add_rmsnorm(outs[k % 4], rs, g, eps, uh[k % 4], uy[k % 4], 1, n, stream=stream)
+            ar.add_rmsnorm(outs[k % 4], rs, g, eps, uh[k % 4], uy[k % 4], rows, hidden,
+                           stream=stream)
 
     t_bare = timed(bare)
     t_fused = timed(fused)
@@ -442,7 +447,10 @@ def bench_norm(torch, ar, replays=20, warmup=3, layers=80):
     worst_ulp = 0.0
     for s in range(4):
         a = oracle.allreduce(list(wl.data[s]))[0]
-        h_want, y_want = oracle.add_rmsnorm(a, res[0], gamma, eps)
+        parts = [oracle.add_rmsnorm(a[i * hidden:(i + 1) * hidden], res[0][i * hidden:(i + 1) * hidden],
+                                    gamma, eps) for i in range(rows)]
+        h_want = np.concatenate([p[0] for p in parts])
+        y_want = np.concatenate([p[1] for p in parts])
         for r in range(N):
             h = hs[s][r].cpu().numpy().view(np.uint16)
             y = ys[s][r].cpu().numpy().view(np.uint16)
@@ -455,8 +463,9 @@ def bench_norm(torch, ar, replays=20, warmup=3, layers=80):
     if worst_ulp > 1.0:
         bad += 1
     return {
-        "workload": "8 ranks x [1x8192] bf16 AllReduce + residual add + RMS norm (hidden 8192, "
-                    "eps %g), 160 calls per hipGraph" % eps,
+        "workload": "%d ranks x [%dx%d] bf16 AllReduce + residual add + RMS norm (eps %g), %s, "
+                    "160 calls per hipGraph" % (N, rows, hidden, eps,
+                                                "one-shot LL" if cid == 2 else "automatic choice"),
         "fused_us_per_call": round(t_fused, 4),
         "unfused_us_per_call": round(t_unfused, 4),
         "allreduce_only_us_per_call": round(t_bare, 4),
@@ -645,8 +654,10 @@ def main():
         del wl4a
     if only in ("all", "norm"):
         log("fused AllReduce + residual add + RMS norm")
-        results["norm_16k"] = bench_norm(torch, ar, replays=5 if args.quick else 20)
+        results["norm_16k"] = bench_norm(torch, ar, 2, replays=5 if args.quick else 20)
         log("  %r" % {k: v for k, v in results["norm_16k"].items() if k != "workload"})
+        results["norm_512k"] = bench_norm(torch, ar, 3, replays=3 if args.quick else 10)
+        log("  %r" % {k: v for k, v in results["norm_512k"].items() if k != "workload"})
     if only in ("all", "configs"):
         reps = 3 if args.quick else 10
         wl1 = Workload(torch, 1, 4)

@@ -172,8 +172,15 @@ int ar_allreduce(const void *const *rank_bufs, void *out, size_t n,
  * other nor any input, residual or gamma.  The a values themselves are not
  * written out.  h is exact; y is within one bf16 unit in the last place of
  * the exact value (binary32 sum, division, square root and products).  The
- * whole grid must be resident at once, so the launch stays within half the
- * device's capacity.  No allocation, memset or host synchronisation.
+ * kernel follows the message: up to 16 KiB per rank the one-shot LL; above
+ * it the in-place one-shot (DIRECT), with one workgroup per rank and row
+ * for 8 or more rows of at most 8192 elements, else spread over several
+ * workgroups per row.  The LL and the spread forms exchange each row's
+ * partial sums between workgroups, so their whole grid must be resident at
+ * once (the launch stays within half the device's capacity).  ar_set_options
+ * may fix LL or DIRECT (one-shot); other protocols and two-shot have no
+ * fused form (AR_ERR_INVALID).  All three forms give the same bits.  No
+ * allocation, memset or host synchronisation.
  * Errors: as ar_allreduce (AR_ERR_INVALID also for the norm operands).
  */
 int ar_allreduce_add_rmsnorm(const void *const *rank_bufs, const void *const *residual,

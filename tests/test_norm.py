@@ -20,6 +20,8 @@ from norm_util import expected, y_violations
 pytestmark = pytest.mark.gpu
 
 EPS = synth.NORM_EPS
+LL, DIRECT = 1, 4
+PROTOS = [(LL, "ll"), (DIRECT, "direct")]
 
 
 def _operands(data, res, gamma):
@@ -43,14 +45,16 @@ def _check(h_dev, y_dev, h_want, y_want, what):
                                                            float(y_want.ravel()[i])))
 
 
-def _run_case(data, res, gamma, rows, hidden, eps=EPS, calls=2, wgs=0, scope=0):
-    """`calls` fused calls with the same operands; checks the last one, and
-    that the stand-alone kernel on the AllReduce result gives the same bits."""
+def _run_case(data, res, gamma, rows, hidden, eps=EPS, calls=2, wgs=0, scope=0, proto=0):
+    """`calls` fused calls with the same operands (on the one-shot LL or the
+    in-place one-shot as `proto` fixes it, else by size); checks the last
+    one, and that the stand-alone kernel on the AllReduce result gives the
+    same bits."""
     N, n = data.shape
     a = oracle.allreduce(list(data))[0]
     h_want, y_want = expected(a, res, gamma, eps, rows, hidden, oracle)
     ins, rs, g = _operands(data, res, gamma)
-    with ar_context(N, n, wgs=wgs, scope=scope) as ar:
+    with ar_context(N, n, proto=proto, wgs=wgs, scope=scope) as ar:
         oh, oy = _outs(N, n)
         for k in range(calls):
             ar.allreduce_add_rmsnorm(ins, rs, g, eps, oh, oy, rows, hidden, k + 1)
@@ -60,6 +64,7 @@ def _run_case(data, res, gamma, rows, hidden, eps=EPS, calls=2, wgs=0, scope=0):
         # unfused: AllReduce, then the stand-alone kernel
         torch = torch_mod()
         out = torch.empty((N, n), dtype=torch.int16, device="cuda:0")
+        ar.set_options(0, 0)
         ar.allreduce(ins, out, n, calls + 1)
         uh, uy = _outs(N, n)
         ar.add_rmsnorm(out, rs, g, eps, uh, uy, rows, hidden)
@@ -69,21 +74,23 @@ def _run_case(data, res, gamma, rows, hidden, eps=EPS, calls=2, wgs=0, scope=0):
         assert_bits_equal(host_bits(uy), host_bits(oy), "unfused vs fused y")
 
 
+@pytest.mark.parametrize("proto", [0, LL, DIRECT], ids=["auto", "ll", "direct"])
 @pytest.mark.parametrize("cid", [1, 2, 3, 5], ids=["c1", "c2", "c3", "c5"])
-def test_workload_shapes(cid):
+def test_workload_shapes(cid, proto):
     w = synth.WORKLOADS[cid]
-    log("norm workload %d" % cid)
+    log("norm workload %d proto %d" % (cid, proto))
     data = synth.input_set(cid, 0)
     res, gamma = synth.norm_operands(cid, 0)
-    _run_case(data, res, gamma, w.rows, w.hidden)
+    _run_case(data, res, gamma, w.rows, w.hidden, proto=proto)
 
 
+@pytest.mark.parametrize("proto,pname", PROTOS, ids=[p[1] for p in PROTOS])
 @pytest.mark.parametrize("scope", [0, 1], ids=["auto", "device"])
-def test_replicated_residual_scopes(scope):
-    log("norm replicated residual, scope %d" % scope)
+def test_replicated_residual_scopes(scope, proto, pname):
+    log("norm replicated residual, scope %d, %s" % (scope, pname))
     data = synth.input_set(2, 1)
     res, gamma = synth.norm_operands(2, 1, replicated=True)
-    _run_case(data, res, gamma, 1, 8192, scope=scope)
+    _run_case(data, res, gamma, 1, 8192, scope=scope, proto=proto)
 
 
 @pytest.mark.parametrize("N,rows,hidden,wgs", [
@@ -95,18 +102,28 @@ def test_replicated_residual_scopes(scope):
     (2, 5, 512, 1),        # 1 workgroup per rank walks every row
     (16, 2, 7168, 0),      # 16 ranks
     (1, 2, 4096, 0),       # one rank: h = a + res
+    # row-wise in-place kernel (8 or more rows of at most 8192 elements)
+    (8, 8, 256, 0),        # one block per row: 15 of 16 waves idle
+    (4, 9, 8192, 0),       # 32 blocks per row (2 per wave); 9 rows: device scope
+    (8, 16, 7168, 0),      # 28 blocks: some waves hold 2, some 1
+    (16, 8, 1280, 0),      # 16 ranks, 5 blocks per row
+    (1, 8, 4096, 0),       # one rank
+    (8, 40, 8192, 0),      # more rows than fit at once: the cross-workgroup kernel
+    (2, 8, 16384, 0),      # rows too long for it: the cross-workgroup kernel
 ], ids=lambda v: str(v))
-def test_blocking_edges(N, rows, hidden, wgs):
-    log("norm edge N=%d rows=%d hidden=%d wgs=%d" % (N, rows, hidden, wgs))
+@pytest.mark.parametrize("proto,pname", PROTOS, ids=[p[1] for p in PROTOS])
+def test_blocking_edges(N, rows, hidden, wgs, proto, pname):
+    log("norm edge N=%d rows=%d hidden=%d wgs=%d %s" % (N, rows, hidden, wgs, pname))
     rng = np.random.Generator(np.random.PCG64(7100 + N * 131 + rows * 17 + hidden))
     n = rows * hidden
     data = synth.draw(rng, N * n, "normal", 1.0).reshape(N, n)
     res = synth.draw(rng, N * n, "normal", 2.0).reshape(N, n)
     gamma = synth.draw(rng, hidden, "uniform", 1.5)
-    _run_case(data, res, gamma, rows, hidden, wgs=wgs)
+    _run_case(data, res, gamma, rows, hidden, wgs=wgs, proto=proto)
 
 
-def test_cancelled_row_and_zero_eps():
+@pytest.mark.parametrize("proto,pname", PROTOS, ids=[p[1] for p in PROTOS])
+def test_cancelled_row_and_zero_eps(proto, pname):
     """A row whose residual cancels the AllReduce result exactly (h = 0, so
     y = 0 with eps > 0), and eps = 0 on rows that are not all zero."""
     log("norm cancelled row")
@@ -118,17 +135,18 @@ def test_cancelled_row_and_zero_eps():
     res = synth.draw(rng, N * n, "normal", 2.0).reshape(N, n)
     res[:, hidden:2 * hidden] = a[hidden:2 * hidden] ^ np.uint16(0x8000)   # -a: exact zero
     gamma = synth.draw(rng, hidden, "normal", 1.0)
-    _run_case(data, res, gamma, rows, hidden, eps=1e-5)
+    _run_case(data, res, gamma, rows, hidden, eps=1e-5, proto=proto)
     res2 = synth.draw(rng, N * n, "normal", 2.0).reshape(N, n)
-    _run_case(data, res2, gamma, rows, hidden, eps=0.0)
+    _run_case(data, res2, gamma, rows, hidden, eps=0.0, proto=proto)
 
 
-def test_graph_decode_step_mixed_with_plain_allreduce():
+@pytest.mark.parametrize("proto,pname", PROTOS, ids=[p[1] for p in PROTOS])
+def test_graph_decode_step_mixed_with_plain_allreduce(proto, pname):
     """A decode step as a hipGraph: per layer an AllReduce and a fused
     AllReduce + norm (80 layers, 160 calls of one epoch sequence), replayed
     with the step end; every call's outputs checked after every replay."""
     torch = torch_mod()
-    log("norm graph")
+    log("norm graph %s" % pname)
     w = synth.WORKLOADS[2]
     N, n = w.n_ranks, w.n
     sets = [synth.input_set(2, s) for s in range(4)]
@@ -138,7 +156,7 @@ def test_graph_decode_step_mixed_with_plain_allreduce():
     ins = [rank_tensors(d) for d in sets]
     rs, g = rank_tensors(res), dev_bits(gamma)
     layers = 80
-    with ar_context(N, n) as ar:
+    with ar_context(N, n, proto=proto) as ar:
         outs = [torch.empty((N, n), dtype=torch.int16, device="cuda:0") for _ in range(layers)]
         hs = [torch.empty((N, n), dtype=torch.int16, device="cuda:0") for _ in range(layers)]
         ys = [torch.empty((N, n), dtype=torch.int16, device="cuda:0") for _ in range(layers)]
@@ -195,6 +213,11 @@ def test_norm_argument_validation():
         assert call(ins=[oy[2]] + ins[1:]) == bad          # input inside out_y
         assert call(g=g[1:]) == bad                        # misaligned gamma
         assert call(epoch=2) == bad                        # epoch sequence
+        ar.set_options(0, 3)
+        assert call() == bad                               # sentinel: no fused form
+        ar.set_options(2, 4)
+        assert call() == bad                               # two-shot: no fused form
+        ar.set_options(0, 0)
         assert call() == arm.ar.AR_OK
         torch.cuda.synchronize()
         check_status_clean()

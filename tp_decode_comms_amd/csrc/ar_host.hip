@@ -266,7 +266,7 @@ int plan_geometry(size_t n, bool f32, Plan *p)
     else if (g.threads > 0)
         p->threads = (uint32_t)g.threads;
     else if (l128 || p->kind == ar::K_TWOSHOT_DIRECT || p->kind == ar::K_TWOSHOT_BARRIER ||
-             p->kind == ar::K_TWOSHOT_ATOMIC)
+             p->kind == ar::K_TWOSHOT_ATOMIC || p->kind == ar::K_ONESHOT_DIRECT_NORM)
         p->threads = 256;
     else
         p->threads = 2 * n <= 256 * 1024 ? 64 : 256;
@@ -285,6 +285,8 @@ int plan_geometry(size_t n, bool f32, Plan *p)
         units = p->slice / 8; per_wg = 64; break;
     case ar::K_TWOSHOT_DIRECT:
         units = p->slice / 8; per_wg = ar::TWOSHOT_DIRECT_CHUNKS * p->threads; break;
+    case ar::K_ONESHOT_DIRECT_NORM: // one 256-element norm block per wave
+        units = n / ar::NORM_BLOCK_ELEMS; per_wg = p->threads / 64; break;
     case ar::K_TWOSHOT_ATOMIC:      // lines of 31 elements, two per wave
         units = (n + ar::ATOM_LINE_ELEMS - 1) / ar::ATOM_LINE_ELEMS; per_wg = p->threads / 32; break;
     default:
@@ -299,7 +301,7 @@ int plan_geometry(size_t n, bool f32, Plan *p)
     if (cap > ar::DONE_STRIDE)
         cap = ar::DONE_STRIDE;
     if (p->kind == ar::K_ONESHOT_BARRIER || p->kind == ar::K_TWOSHOT_BARRIER ||
-        p->kind == ar::K_ONESHOT_LL_NORM) {
+        p->kind == ar::K_ONESHOT_LL_NORM || p->kind == ar::K_ONESHOT_DIRECT_NORM) {
         // a grid barrier (or the norm's row-wide wait) needs every workgroup
         // resident at once: stay within half the occupancy-derived capacity
         // (the watchdog bounds the rest)
@@ -523,11 +525,35 @@ int do_allreduce_norm(const void *const *rank_bufs, const void *const *residual,
     rc = check_call(rank_bufs, out_h, 2, n, epoch);
     if (rc != AR_OK)
         return rc;
+    // the fused epilogue rides on the one-shot LL or the in-place one-shot:
+    // LL for messages up to the automatic LL limit, DIRECT above (or as the
+    // protocol option fixes it); no other protocol has a fused form.  The
+    // in-place form goes row-wise (a workgroup per rank and row) for 8 or
+    // more rows of up to 8192 elements when they fit the device at once.
     Plan p;
-    p.kind = ar::K_ONESHOT_LL_NORM;
-    rc = plan_geometry(n, false, &p);
-    if (rc != AR_OK)
+    if (g.proto == AR_PROTO_LL || (g.proto == AR_PROTO_AUTO && 2 * n <= AUTO_LL_MAX_BYTES))
+        p.kind = ar::K_ONESHOT_LL_NORM;
+    else if (g.proto == AR_PROTO_AUTO || g.proto == AR_PROTO_DIRECT)
+        p.kind = ar::K_ONESHOT_DIRECT_NORM;
+    else
+        return AR_ERR_INVALID;
+    if (g.algo == AR_ALGO_TWOSHOT)
+        return AR_ERR_INVALID;
+    if (!g.cap_ready && (rc = compute_capacity()) != AR_OK)
         return rc;
+    const size_t rows_cap = (size_t)g.capacity[ar::K_ONESHOT_ROWS_NORM][0][4] / g.n_ranks;
+    if (p.kind == ar::K_ONESHOT_DIRECT_NORM && rows >= ar::ROWS_NORM_MIN_ROWS &&
+        hidden <= ar::ROWS_NORM_MAX_HIDDEN && rows <= rows_cap) {
+        p.kind = ar::K_ONESHOT_ROWS_NORM;
+        p.threads = 1024;
+        p.parts = (uint32_t)rows;
+        p.slice = (uint32_t)slice_len(n, g.n_ranks);
+        p.local = g.scope == AR_SCOPE_AUTO && g.placement_ok && p.parts % ar::XCDS == 0;
+    } else {
+        rc = plan_geometry(n, false, &p);
+        if (rc != AR_OK)
+            return rc;
+    }
     ar::NormLaunch L;
     memset(&L, 0, sizeof L);
     fill_launch(rank_bufs, out_h, n, epoch, p, &L.base);
@@ -541,9 +567,9 @@ int do_allreduce_norm(const void *const *rank_bufs, const void *const *residual,
     L.eps = eps;
     const uint32_t grid = p.parts * (uint32_t)g.n_ranks;
     if (debug_enabled())
-        fprintf(stderr, "[ar] norm rows=%zu hidden=%zu epoch=%u grid=%u threads=%u local=%d\n",
-                rows, hidden, epoch, grid, p.threads, (int)p.local);
-    hipError_t e = ar::launch_ll_norm(p.local, L, grid, p.threads, stream);
+        fprintf(stderr, "[ar] norm kind=%d rows=%zu hidden=%zu epoch=%u grid=%u threads=%u local=%d\n",
+                p.kind, rows, hidden, epoch, grid, p.threads, (int)p.local);
+    hipError_t e = ar::launch_norm(p.kind, p.local, L, grid, p.threads, stream);
     if (e != hipSuccess)
         return hip_fail(e);
     g.last_epoch = epoch;

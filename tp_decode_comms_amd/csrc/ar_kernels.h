@@ -13,6 +13,10 @@ struct NormLaunch;
 // block of one partial sum, at most 65536
 constexpr size_t NORM_BLOCK_ELEMS = 256;
 constexpr size_t NORM_HIDDEN_LIMIT = 65536;
+// the row-wise fused kernel: one 16-wave workgroup per (rank, row), for at
+// least this many rows of at most ROWS_NORM_MAX_HIDDEN elements
+constexpr size_t ROWS_NORM_MIN_ROWS = 8;
+constexpr size_t ROWS_NORM_MAX_HIDDEN = 8192;
 // two-shot DIRECT: 8-element chunks each lane reduces per round
 constexpr uint32_t TWOSHOT_DIRECT_CHUNKS = 2;
 // atomic lines: 128 bytes = a 4-byte counter and 31 binary32 sums
@@ -30,7 +34,9 @@ enum KernelKind {
     K_TWOSHOT_BARRIER = 8,
     K_ONESHOT_LL_NORM = 9,      // one-shot LL + residual add + RMS norm (bf16 only)
     K_TWOSHOT_ATOMIC = 10,      // atomic lines (arrival-order sums: not bit-exact)
-    K_COUNT = 11
+    K_ONESHOT_DIRECT_NORM = 11, // one-shot DIRECT + residual add + RMS norm (bf16 only)
+    K_ONESHOT_ROWS_NORM = 12,   // the same, one workgroup per (rank, row)
+    K_COUNT = 13
 };
 
 // device function of a kernel kind for n_ranks (<= 8 or <= 16 instantiation);
@@ -39,8 +45,10 @@ const void *kernel_for(int kind, int n_ranks, bool f32, bool local);
 
 hipError_t launch_ar(int kind, bool f32, bool local, const Launch &a, uint32_t grid,
                      uint32_t threads, hipStream_t stream);
-hipError_t launch_ll_norm(bool local, const NormLaunch &L, uint32_t grid, uint32_t threads,
-                          hipStream_t stream);
+// the fused AllReduce + residual add + RMS norm (kind K_ONESHOT_LL_NORM,
+// K_ONESHOT_DIRECT_NORM or K_ONESHOT_ROWS_NORM)
+hipError_t launch_norm(int kind, bool local, const NormLaunch &L, uint32_t grid, uint32_t threads,
+                       hipStream_t stream);
 // stand-alone residual add + RMS norm of an AllReduce result: one workgroup
 // of 1024 threads per (rank, row)
 hipError_t launch_add_rmsnorm(const void *a, const void *const *res, const void *gamma, float eps,

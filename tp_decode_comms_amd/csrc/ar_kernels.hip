@@ -496,6 +496,252 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
     finish(a, c);
 }
 
+// ============================================ one-shot DIRECT + add + norm
+// The same fused epilogue on the in-place one-shot, for messages where the
+// one-shot DIRECT is the faster AllReduce (batched decode: rows x hidden of
+// tens to hundreds of KiB per rank).  Each wave owns a run of consecutive
+// 256-element norm blocks: after the arrival flags it reads 8 bytes per lane
+// from every rank's input in place, folds them in rank order, and continues
+// as the LL-fused kernel does (h, each block's sum of squares published
+// with the call's flag, the row's sums folded in the fixed order, y).  The blocks and
+// every fold are those of norm_math.h, so h and y equal the LL-fused and
+// the stand-alone kernels' bit for bit.  Waves work independently; a wave
+// whose wait gives up records it and skips its work but still reaches
+// finish().  All workgroups of a rank must be resident at once.
+template <int NMAX, bool LOCAL>
+__global__ __launch_bounds__(256) void k_oneshot_direct_norm(const NormLaunch L)
+{
+    const Launch &a = L.base;
+    Ctx0 c;
+    begin<LOCAL>(a, c);
+    const uint32_t N = a.n_ranks;
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t blocks = a.n / NORM_BLOCK;                  // per rank
+    // wave v of the rank owns a run of R consecutive blocks (R even): runs
+    // stay within one row where R divides the row's block count, so a wave
+    // waits for one row's sums, and it reduces its blocks in pairs whose
+    // loads are in flight together
+    const uint32_t W = a.parts * (blockDim.x >> 6);
+    const uint32_t v = c.part * (blockDim.x >> 6) + wave;
+    const uint32_t R = (((blocks + W - 1u) / W) + 1u) & ~1u;
+    const uint32_t bbeg = v * R;
+    const uint32_t bend = bbeg + R < blocks ? bbeg + R : blocks;
+    const uint32_t nb = a.n * 2u;
+    const __amdgpu_buffer_rsrc_t resr = rsrc(L.res[c.rank], nb);
+    const __amdgpu_buffer_rsrc_t gr = rsrc(L.gamma, L.hidden * 2u);
+    const __amdgpu_buffer_rsrc_t oh = rsrc((char *)a.out + (size_t)c.rank * nb, nb);
+    const __amdgpu_buffer_rsrc_t oy = rsrc((char *)L.y + (size_t)c.rank * nb, nb);
+    const __amdgpu_buffer_rsrc_t sr = rsrc(L.stats, a.n_ranks * L.stats_stride * 8u);
+    // the first pair's residual and weight do not depend on any flag
+    const uint32_t e0 = bbeg * NORM_BLOCK + lane * 4u;
+    u32x2 r0 = {0u, 0u}, r1 = {0u, 0u}, g0 = {0u, 0u}, g1 = {0u, 0u};
+    if (bbeg < bend) {
+        r0 = ld8<CP_PLAIN>(resr, e0 * 2u);
+        g0 = ld8<CP_PLAIN>(gr, (e0 % L.hidden) * 2u);
+        if (bbeg + 1u < bend) {
+            r1 = ld8<CP_PLAIN>(resr, (e0 + NORM_BLOCK) * 2u);
+            g1 = ld8<CP_PLAIN>(gr, ((e0 + NORM_BLOCK) % L.hidden) * 2u);
+        }
+    }
+    c.flag = load_seq(a) + a.epoch;
+    const Ctl ctl{a.ctl};
+    start_delay(a, c);
+    raise_arrival<LOCAL>(a, c);
+    bool ok = wait_arrivals<LOCAL>(a, c, ctl);
+    __amdgpu_buffer_rsrc_t src[NMAX];
+#pragma unroll
+    for (int s = 0; s < NMAX; ++s)
+        src[s] = in_rsrc(a, (uint32_t)s < N ? (uint32_t)s : 0u);
+    u32x2 h0 = {0u, 0u}, h1 = {0u, 0u};
+    for (uint32_t b = bbeg; ok && b < bend; b += 2u) {
+        const bool two = b + 1u < bend;
+        const uint32_t e = b * NORM_BLOCK + lane * 4u;
+        u32x2 V[NMAX], U[NMAX];
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((uint32_t)s < N) {
+                V[s] = ld8<CP_DEV>(src[s], e * 2u);
+                U[s] = two ? ld8<CP_DEV>(src[s], (e + NORM_BLOCK) * 2u) : u32x2{0u, 0u};
+            }
+        const bool first = b == bbeg;
+        const u32x2 rw = first ? r0 : ld8<CP_PLAIN>(resr, e * 2u);
+        const u32x2 rw2 = first ? r1 : two ? ld8<CP_PLAIN>(resr, (e + NORM_BLOCK) * 2u)
+                                           : u32x2{0u, 0u};
+        Acc4 acc, acc2;
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((uint32_t)s < N) {
+                if (s == 0) { acc.init(V[s].x, V[s].y); acc2.init(U[s].x, U[s].y); }
+                else { acc.add(V[s].x, V[s].y); acc2.add(U[s].x, U[s].y); }
+            }
+        u32x2 aw, aw2;
+        aw.x = pack_bf16(acc.v[0], acc.v[1]);
+        aw.y = pack_bf16(acc.v[2], acc.v[3]);
+        aw2.x = pack_bf16(acc2.v[0], acc2.v[1]);
+        aw2.y = pack_bf16(acc2.v[2], acc2.v[3]);
+        const u32x2 hw = add_round4(aw, rw), hw2 = add_round4(aw2, rw2);
+        st8<CP_PLAIN>(hw, oh, e * 2u);
+        if (two)
+            st8<CP_PLAIN>(hw2, oh, (e + NORM_BLOCK) * 2u);
+        if (first) {
+            h0 = hw;
+            h1 = hw2;
+        }
+        const float sq = wave_sum(sumsq4(hw));
+        const float sq2 = wave_sum(sumsq4(hw2));
+        if (lane < (two ? 2u : 1u)) {
+            u32x2 en; en.x = __float_as_uint(lane == 0u ? sq : sq2); en.y = c.flag;
+            st8<CP_DEV>(en, sr, (c.rank * L.stats_stride + b + lane) * 8u);
+        }
+    }
+    // normalise this wave's blocks (one wait per row they touch)
+    const uint32_t B = L.hidden / NORM_BLOCK;
+    uint32_t have = 0xFFFFFFFFu;
+    float r = 0.0f;
+    for (uint32_t b = bbeg; ok && b < bend; ++b) {
+        const uint32_t row = b / B;
+        if (row != have) {
+            if (!row_rinv<LOCAL>(L, c, ctl, sr, row, B, &r)) {
+                ok = false;                                    // watchdog: status recorded
+                break;
+            }
+            have = row;
+        }
+        const uint32_t e = b * NORM_BLOCK + lane * 4u;
+        const u32x2 hw = b == bbeg ? h0 : b == bbeg + 1u ? h1 : ld8<CP_PLAIN>(oh, e * 2u);
+        const u32x2 gw = b == bbeg ? g0 : b == bbeg + 1u ? g1 : ld8<CP_PLAIN>(gr, (e % L.hidden) * 2u);
+        st8<CP_PLAIN>(scale4(hw, gw, r), oy, e * 2u);
+    }
+    finish(a, c);
+}
+
+// ================================= one-shot DIRECT + add + norm, row-wise
+// For batched decode (8 or more rows per rank) a workgroup of 16 waves owns
+// one (rank, row): after the arrival flags wave w reduces the row's blocks
+// w, w+16, ... in place (8 bytes per lane from every rank's input, both
+// blocks of a pair in flight together), adds the residual, writes h and
+// puts each block's sum of squares in LDS; the row's sum is then folded in
+// LDS and y written -- the stand-alone kernel's structure (norm.hip) with
+// the AllReduce in front, so the sums, their order and the bits are the
+// same.  No workgroup waits for another's sums.  Rows of up to 8192
+// elements (2 blocks per wave, kept in registers: at 50 VGPRs two such
+// workgroups fit a CU; with 4 blocks per wave one did, and a batch of 32
+// rows took 8.8 us per call instead of 7.6).
+constexpr uint32_t ROWS_WAVES = 16;
+constexpr uint32_t ROWS_PER_WAVE = 2;
+
+template <int NMAX, bool LOCAL>
+__global__ __launch_bounds__(1024) void k_oneshot_rows_norm(const NormLaunch L)
+{
+    const Launch &a = L.base;
+    __shared__ float bsum[ROWS_WAVES * ROWS_PER_WAVE];
+    __shared__ float rinv_s;
+    Ctx0 c;
+    begin<LOCAL>(a, c);
+    const uint32_t N = a.n_ranks;
+    const uint32_t row = c.part;                          // one part per row
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const uint32_t B = L.hidden / NORM_BLOCK;
+    const uint32_t rows = a.n / L.hidden;
+    const bool live = row < rows && (blockDim.x >> 6) == ROWS_WAVES;
+    const uint32_t nb = a.n * 2u;
+    const __amdgpu_buffer_rsrc_t resr = rsrc(L.res[c.rank], nb);
+    const __amdgpu_buffer_rsrc_t gr = rsrc(L.gamma, L.hidden * 2u);
+    const __amdgpu_buffer_rsrc_t oh = rsrc((char *)a.out + (size_t)c.rank * nb, nb);
+    const __amdgpu_buffer_rsrc_t oy = rsrc((char *)L.y + (size_t)c.rank * nb, nb);
+    const uint32_t row0 = row * L.hidden;
+    // residual and weight need no flag: the waves that do not poll load
+    // them before the arrival wait, the polling wave after it
+    u32x2 rk[ROWS_PER_WAVE], gk[ROWS_PER_WAVE];
+    const bool poller = wave == 0u;
+    if (!poller) {
+#pragma unroll
+        for (int k = 0; k < (int)ROWS_PER_WAVE; ++k) {
+            const uint32_t j = wave + ROWS_WAVES * k;
+            const uint32_t col = j * NORM_BLOCK + lane * 4u;
+            rk[k] = live && j < B ? ld8<CP_PLAIN>(resr, (row0 + col) * 2u) : u32x2{0u, 0u};
+            gk[k] = live && j < B ? ld8<CP_PLAIN>(gr, col * 2u) : u32x2{0u, 0u};
+        }
+    }
+    c.flag = load_seq(a) + a.epoch;
+    const Ctl ctl{a.ctl};
+    start_delay(a, c);
+    raise_arrival<LOCAL>(a, c);
+    if (!wait_arrivals_wg<LOCAL>(a, c, ctl))
+        return;                                           // every wave returns here
+    if (poller) {
+#pragma unroll
+        for (int k = 0; k < (int)ROWS_PER_WAVE; ++k) {
+            const uint32_t j = wave + ROWS_WAVES * k;
+            const uint32_t col = j * NORM_BLOCK + lane * 4u;
+            rk[k] = live && j < B ? ld8<CP_PLAIN>(resr, (row0 + col) * 2u) : u32x2{0u, 0u};
+            gk[k] = live && j < B ? ld8<CP_PLAIN>(gr, col * 2u) : u32x2{0u, 0u};
+        }
+    }
+    __amdgpu_buffer_rsrc_t src[NMAX];
+#pragma unroll
+    for (int s = 0; s < NMAX; ++s)
+        src[s] = in_rsrc(a, (uint32_t)s < N ? (uint32_t)s : 0u);
+    u32x2 hk[ROWS_PER_WAVE];
+#pragma unroll
+    for (int k = 0; k < (int)ROWS_PER_WAVE; k += 2) {
+        const uint32_t j = wave + ROWS_WAVES * k, j2 = j + ROWS_WAVES;
+        const bool in1 = live && j < B, in2 = live && j2 < B;
+        const uint32_t e = row0 + j * NORM_BLOCK + lane * 4u;
+        const uint32_t e2 = e + ROWS_WAVES * NORM_BLOCK;
+        u32x2 V[NMAX], U[NMAX];
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((uint32_t)s < N) {
+                V[s] = in1 ? ld8<CP_DEV>(src[s], e * 2u) : u32x2{0u, 0u};
+                U[s] = in2 ? ld8<CP_DEV>(src[s], e2 * 2u) : u32x2{0u, 0u};
+            }
+        Acc4 acc, acc2;
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            if ((uint32_t)s < N) {
+                if (s == 0) { acc.init(V[s].x, V[s].y); acc2.init(U[s].x, U[s].y); }
+                else { acc.add(V[s].x, V[s].y); acc2.add(U[s].x, U[s].y); }
+            }
+        u32x2 aw, aw2;
+        aw.x = pack_bf16(acc.v[0], acc.v[1]);
+        aw.y = pack_bf16(acc.v[2], acc.v[3]);
+        aw2.x = pack_bf16(acc2.v[0], acc2.v[1]);
+        aw2.y = pack_bf16(acc2.v[2], acc2.v[3]);
+        hk[k] = add_round4(aw, rk[k]);
+        hk[k + 1] = add_round4(aw2, rk[k + 1]);
+        if (in1) {
+            st8<CP_PLAIN>(hk[k], oh, e * 2u);
+            const float sq = wave_sum(sumsq4(hk[k]));
+            if (lane == 0u)
+                bsum[j] = sq;
+        }
+        if (in2) {
+            st8<CP_PLAIN>(hk[k + 1], oh, e2 * 2u);
+            const float sq = wave_sum(sumsq4(hk[k + 1]));
+            if (lane == 0u)
+                bsum[j2] = sq;
+        }
+    }
+    __syncthreads();
+    if (wave == 0u) {
+        // the fold of norm_math.h: lane l holds blocks l, l+64, ... (B <= 32 here)
+        const float part = lane < B ? bsum[lane] : 0.0f;
+        const float r = rms_inv(wave_sum(part), L.hidden, L.eps);
+        if (lane == 0u)
+            rinv_s = r;
+    }
+    __syncthreads();
+    const float r = rinv_s;
+#pragma unroll
+    for (int k = 0; k < (int)ROWS_PER_WAVE; ++k) {
+        const uint32_t j = wave + ROWS_WAVES * k;
+        if (live && j < B)
+            st8<CP_PLAIN>(scale4(hk[k], gk[k], r), oy, (row0 + j * NORM_BLOCK + lane * 4u) * 2u);
+    }
+    finish(a, c);
+}
+
 // ======================================================= one-shot sentinel
 // Push model: rank q writes chunk c of its input into every peer's inbox
 // [peer][q][parity]; each receiver polls its own inbox until no element is
@@ -1698,6 +1944,10 @@ static const void *pick(int kind)
     case K_TWOSHOT_ATOMIC: return (const void *)k_twoshot_atomic<NMAX, F32, LOCAL>;
     case K_ONESHOT_LL_NORM:         // bf16 only
         return F32 ? nullptr : (const void *)k_oneshot_ll_norm<NMAX, LOCAL>;
+    case K_ONESHOT_DIRECT_NORM:     // bf16 only
+        return F32 ? nullptr : (const void *)k_oneshot_direct_norm<NMAX, LOCAL>;
+    case K_ONESHOT_ROWS_NORM:       // bf16 only
+        return F32 ? nullptr : (const void *)k_oneshot_rows_norm<NMAX, LOCAL>;
     default: return nullptr;
     }
 }
@@ -1722,10 +1972,12 @@ hipError_t launch_ar(int kind, bool f32, bool local, const Launch &a, uint32_t g
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
 }
 
-hipError_t launch_ll_norm(bool local, const NormLaunch &L, uint32_t grid, uint32_t threads,
-                          hipStream_t stream)
+hipError_t launch_norm(int kind, bool local, const NormLaunch &L, uint32_t grid, uint32_t threads,
+                       hipStream_t stream)
 {
-    const void *fn = kernel_for(K_ONESHOT_LL_NORM, (int)L.base.n_ranks, false, local);
+    if (kind != K_ONESHOT_LL_NORM && kind != K_ONESHOT_DIRECT_NORM && kind != K_ONESHOT_ROWS_NORM)
+        return hipErrorInvalidValue;
+    const void *fn = kernel_for(kind, (int)L.base.n_ranks, false, local);
     if (fn == nullptr)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&L};
