@@ -225,7 +225,7 @@ int ar_destroy(void);
  * stay ahead much longer here): S <= 16 KiB -> one-shot LL; S < 1 MiB ->
  * one-shot DIRECT; otherwise two-shot DIRECT.  With a protocol fixed and
  * the algorithm AUTO, one-shot is used up to that protocol's crossover
- * (sentinel 64 KiB, LL128 256 KiB, DIRECT and barrier just below 1 MiB);
+ * (sentinel 64 KiB, LL128 128 KiB, DIRECT and barrier just below 1 MiB);
  * LL is always one-shot and the atomic lines always two-shot.
  * AR_ERR_INVALID for an unknown value or an impossible pair.
  */

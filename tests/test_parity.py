@@ -195,7 +195,7 @@ def test_auto_selection():
                                  (1024 - 16, ONE, DIRECT), (1024, TWO, DIRECT)):
             n = kib * 512
             assert (a.query(2, n), a.query(3, n)) == (algo, proto), kib
-        for p, last_one in ((SENT, 64), (LL128, 256), (DIRECT, 1024 - 16)):
+        for p, last_one in ((SENT, 64), (LL128, 128), (DIRECT, 1024 - 16)):
             a.set_options(0, p)
             assert a.query(2, last_one * 512) == ONE, (p, last_one)
             nxt = 1024 if p == DIRECT else 2 * last_one

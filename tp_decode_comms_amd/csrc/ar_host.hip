@@ -39,7 +39,7 @@ size_t oneshot_limit(int proto)
 {
     switch (proto) {
     case AR_PROTO_SENTINEL: return 64 * 1024;          // two-shot ahead from 128 KiB
-    case AR_PROTO_LL128: return 256 * 1024;            // two-shot ahead from 512 KiB
+    case AR_PROTO_LL128: return 128 * 1024;            // two-shot ahead from 256 KiB
     default: return 1024 * 1024 - 1;                   // DIRECT, barrier, AUTO
     }
 }
@@ -73,6 +73,7 @@ struct Context {
     // sequence
     uint32_t last_epoch = 0;
     int capacity[ar::K_COUNT][2][5] = {};   // resident workgroups [kind][f32][64..1024 threads]
+    int cap_l128[2][2][3] = {};             // LL128 at 256 threads [two-shot][f32][1, 2, 4 groups]
     bool cap_ready = false;
 };
 
@@ -164,12 +165,12 @@ int compute_capacity()
     const int tcounts[5] = {64, 128, 256, 512, 1024};
     for (int k = 0; k < ar::K_COUNT; ++k) {
         for (int f = 0; f < 2; ++f) {
-            if (ar::kernel_for(k, g.n_ranks, f == 1, false) == nullptr)
+            if (ar::kernel_for(k, g.n_ranks, f == 1, false, 0) == nullptr)
                 continue;                       // no such variant (capacity stays 0)
             for (int t = 0; t < 5; ++t) {
                 int per_cu = 0;
                 hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &per_cu, ar::kernel_for(k, g.n_ranks, f == 1, false), tcounts[t], 0);
+                    &per_cu, ar::kernel_for(k, g.n_ranks, f == 1, false, 0), tcounts[t], 0);
                 if (e != hipSuccess && t >= 3) {
                     // block sizes above a kernel's launch bound: unusable
                     (void)hipGetLastError();
@@ -181,7 +182,7 @@ int compute_capacity()
                 if (f == 0) {           // bf16: the XCD-local variant too
                     int per_cu_local = 0;
                     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                        &per_cu_local, ar::kernel_for(k, g.n_ranks, false, true), tcounts[t], 0);
+                        &per_cu_local, ar::kernel_for(k, g.n_ranks, false, true, 0), tcounts[t], 0);
                     if (e != hipSuccess && t >= 3) {
                         (void)hipGetLastError();
                         per_cu_local = 0;
@@ -194,12 +195,30 @@ int compute_capacity()
             }
         }
     }
+    // LL128 per batch size (its LDS tile grows with the groups per batch)
+    const int gws[3] = {1, 2, 4};
+    for (int two = 0; two < 2; ++two)
+        for (int f = 0; f < 2; ++f)
+            for (int i = 0; i < 3; ++i) {
+                const int kind = two ? ar::K_TWOSHOT_LL128 : ar::K_ONESHOT_LL128;
+                int best = 1 << 30;
+                for (int local = 0; local < (f ? 1 : 2); ++local) {
+                    int per_cu = 0;
+                    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                        &per_cu, ar::kernel_for(kind, g.n_ranks, f == 1, local == 1, gws[i]), 256, 0);
+                    if (e != hipSuccess)
+                        return hip_fail(e);
+                    best = std::min(best, per_cu);
+                }
+                g.cap_l128[two][f][i] = best * g.cu_count;
+            }
     g.cap_ready = true;
     return AR_OK;
 }
 
 struct Plan {
     int kind;
+    int gw = 0;         // LL128: line groups per batch
     uint32_t parts;     // workgroups per rank
     uint32_t threads;
     uint32_t slice;
@@ -256,6 +275,14 @@ int plan_geometry(size_t n, bool f32, Plan *p)
     const uint32_t N = (uint32_t)g.n_ranks;
     p->slice = (uint32_t)slice_len(n, g.n_ranks);
     const bool l128 = p->kind == ar::K_ONESHOT_LL128 || p->kind == ar::K_TWOSHOT_LL128;
+    if (l128) {
+        // line groups per batch, from a sweep at 8 ranks (ar_kernels.hip)
+        const size_t bytes = 2 * n;
+        if (p->kind == ar::K_ONESHOT_LL128)
+            p->gw = bytes <= 64 * 1024 ? 1 : 2;
+        else
+            p->gw = bytes <= 1024 * 1024 ? 1 : (N <= 8 ? 4 : 2);
+    }
     if (p->kind == ar::K_ONESHOT_LL || p->kind == ar::K_ONESHOT_LL_NORM) {
         // one wave per rank (a power of two >= N): each wave receives one peer
         uint32_t w = 1;
@@ -275,10 +302,10 @@ int plan_geometry(size_t n, bool f32, Plan *p)
     case ar::K_ONESHOT_LL:
     case ar::K_ONESHOT_LL_NORM:
         units = n / 4; per_wg = 64; break;
-    case ar::K_ONESHOT_LL128:       // batches of 4 line groups (2 above 8 ranks)
-        units = (n + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = N <= 8 ? 4 : 2; break;
+    case ar::K_ONESHOT_LL128:       // batches of gw line groups (at most 2 above 8 ranks)
+        units = (n + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = (uint64_t)p->gw; break;
     case ar::K_TWOSHOT_LL128:
-        units = (p->slice + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = N <= 8 ? 4 : 2; break;
+        units = (p->slice + ar::L128_ELEMS - 1) / ar::L128_ELEMS; per_wg = (uint64_t)p->gw; break;
     case ar::K_ONESHOT_SENTINEL:
         units = n / 8; per_wg = 64; break;
     case ar::K_TWOSHOT_SENTINEL:
@@ -298,6 +325,9 @@ int plan_geometry(size_t n, bool f32, Plan *p)
             return rc;
     }
     uint32_t cap = (uint32_t)g.capacity[p->kind][f32 ? 1 : 0][thread_index((int)p->threads)] / N;
+    if (l128)
+        cap = (uint32_t)g.cap_l128[p->kind == ar::K_TWOSHOT_LL128][f32 ? 1 : 0]
+                                  [p->gw == 1 ? 0 : p->gw == 2 ? 1 : 2] / N;
     if (cap > ar::DONE_STRIDE)
         cap = ar::DONE_STRIDE;
     if (p->kind == ar::K_ONESHOT_BARRIER || p->kind == ar::K_TWOSHOT_BARRIER ||
@@ -454,7 +484,7 @@ int do_allreduce(const void *const *rank_bufs, void *out, size_t n, uint32_t epo
     if (debug_enabled())
         fprintf(stderr, "[ar] n=%zu epoch=%u kind=%d grid=%u threads=%u slice=%u f32=%d local=%d\n",
                 n, epoch, p.kind, grid, p.threads, p.slice, (int)f32, (int)p.local);
-    hipError_t e = ar::launch_ar(p.kind, f32, p.local, a, grid, p.threads, stream);
+    hipError_t e = ar::launch_ar(p.kind, f32, p.local, p.gw, a, grid, p.threads, stream);
     if (e != hipSuccess)
         return hip_fail(e);
     g.last_epoch = epoch;

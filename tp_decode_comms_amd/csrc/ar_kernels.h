@@ -41,9 +41,11 @@ enum KernelKind {
 
 // device function of a kernel kind for n_ranks (<= 8 or <= 16 instantiation);
 // local selects the XCD-local coherence scope (bf16 kernels only)
-const void *kernel_for(int kind, int n_ranks, bool f32, bool local);
+// gw: line groups per batch of the LL128 kinds (1, 2 or 4; 0 = the largest
+// available), ignored by the others
+const void *kernel_for(int kind, int n_ranks, bool f32, bool local, int gw);
 
-hipError_t launch_ar(int kind, bool f32, bool local, const Launch &a, uint32_t grid,
+hipError_t launch_ar(int kind, bool f32, bool local, int gw, const Launch &a, uint32_t grid,
                      uint32_t threads, hipStream_t stream);
 // the fused AllReduce + residual add + RMS norm (kind K_ONESHOT_LL_NORM,
 // K_ONESHOT_DIRECT_NORM or K_ONESHOT_ROWS_NORM)

@@ -1236,8 +1236,12 @@ __global__ __launch_bounds__(256) void k_twoshot_barrier(const Launch a)
 // the waves as in the LL and sentinel kernels: wave w takes every group of
 // the batch from the peers s with s % 4 == w, polling their line flags
 // together and then loading the payloads.
-// groups per batch: 4 for up to 8 ranks, 2 for up to 16 (LDS tile budget)
-template <int NMAX> struct GroupsPerBatch { static constexpr int value = NMAX <= 8 ? 4 : 2; };
+// Line groups per batch (GW) is a template parameter chosen by the host per
+// call: small batches spread a message over more workgroups (more of the
+// chip, shorter serial chains), large ones amortise the per-batch hops on
+// big messages (measured at 8 ranks: one-shot 16-64 KiB best with 1 group
+// per batch, 256-512 KiB with 2; two-shot up to 1 MiB with 1, from 2 MiB
+// with 4).  At most 2 above 8 ranks (LDS tile budget).
 constexpr int L128_WAVES = 4;
 
 // reads 8 (or 4) elements of a bf16 buffer at element `e`
@@ -1371,10 +1375,9 @@ __device__ __forceinline__ void store_lane(__amdgpu_buffer_rsrc_t o, uint32_t e,
 // group k.  Every wave receives the batch from its peers into an LDS tile
 // [N][GW][64 lanes]; after a workgroup barrier each publishing wave reduces
 // its group in global rank order and writes it.
-template <int NMAX, bool F32, bool LOCAL>
+template <int NMAX, bool F32, bool LOCAL, int GW>
 __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 {
-    constexpr int GW = GroupsPerBatch<NMAX>::value;
     constexpr int PW = (NMAX + L128_WAVES - 1) / L128_WAVES;
     __shared__ u32x4 stage[NMAX][GW][64];
     __shared__ uint32_t failed;
@@ -1465,10 +1468,9 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 // groups (its own from registers) and writes them to out[q].  Batches and
 // publishing waves as in the one-shot kernel; wave w receives the batch of
 // the slices of the peers s with s % 4 == w straight into out[q].
-template <int NMAX, bool F32, bool LOCAL>
+template <int NMAX, bool F32, bool LOCAL, int GW>
 __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 {
-    constexpr int GW = GroupsPerBatch<NMAX>::value;
     constexpr int PW = (NMAX + L128_WAVES - 1) / L128_WAVES;
     Ctx0 c;
     begin<LOCAL>(a, c);
@@ -1928,15 +1930,34 @@ __global__ __launch_bounds__(256) void k_xcc_map(uint32_t *out, uint32_t n)
 }
 
 // ------------------------------------------------------------ dispatch
+// LL128 kernels by line groups per batch (1, 2, or 4 up to 8 ranks)
 template <int NMAX, bool F32, bool LOCAL>
-static const void *pick(int kind)
+static const void *pick_ll128(bool two, int gw)
+{
+    if (gw == 1)
+        return two ? (const void *)k_twoshot_ll128<NMAX, F32, LOCAL, 1>
+                   : (const void *)k_oneshot_ll128<NMAX, F32, LOCAL, 1>;
+    if constexpr (NMAX > 8) {
+        return two ? (const void *)k_twoshot_ll128<NMAX, F32, LOCAL, 2>
+                   : (const void *)k_oneshot_ll128<NMAX, F32, LOCAL, 2>;
+    } else {
+        if (gw == 2)
+            return two ? (const void *)k_twoshot_ll128<NMAX, F32, LOCAL, 2>
+                       : (const void *)k_oneshot_ll128<NMAX, F32, LOCAL, 2>;
+        return two ? (const void *)k_twoshot_ll128<NMAX, F32, LOCAL, 4>
+                   : (const void *)k_oneshot_ll128<NMAX, F32, LOCAL, 4>;
+    }
+}
+
+template <int NMAX, bool F32, bool LOCAL>
+static const void *pick(int kind, int gw)
 {
     switch (kind) {
     case K_ONESHOT_LL: return (const void *)k_oneshot_ll<NMAX, F32, LOCAL>;
     case K_ONESHOT_SENTINEL: return (const void *)k_oneshot_sentinel<NMAX, F32, LOCAL>;
     case K_ONESHOT_DIRECT: return (const void *)k_oneshot_direct<NMAX, F32, LOCAL>;
-    case K_ONESHOT_LL128: return (const void *)k_oneshot_ll128<NMAX, F32, LOCAL>;
-    case K_TWOSHOT_LL128: return (const void *)k_twoshot_ll128<NMAX, F32, LOCAL>;
+    case K_ONESHOT_LL128: return pick_ll128<NMAX, F32, LOCAL>(false, gw);
+    case K_TWOSHOT_LL128: return pick_ll128<NMAX, F32, LOCAL>(true, gw);
     case K_TWOSHOT_SENTINEL: return (const void *)k_twoshot_sentinel<NMAX, F32, LOCAL>;
     case K_TWOSHOT_DIRECT: return (const void *)k_twoshot_direct<NMAX, F32, LOCAL>;
     case K_ONESHOT_BARRIER: return (const void *)k_oneshot_barrier<NMAX, F32, LOCAL>;
@@ -1953,19 +1974,19 @@ static const void *pick(int kind)
 }
 
 // The fp32 debug kernels always use device scope.
-const void *kernel_for(int kind, int n_ranks, bool f32, bool local)
+const void *kernel_for(int kind, int n_ranks, bool f32, bool local, int gw)
 {
     if (f32)
-        return n_ranks <= 8 ? pick<8, true, false>(kind) : pick<16, true, false>(kind);
+        return n_ranks <= 8 ? pick<8, true, false>(kind, gw) : pick<16, true, false>(kind, gw);
     if (n_ranks <= 8)
-        return local ? pick<8, false, true>(kind) : pick<8, false, false>(kind);
-    return local ? pick<16, false, true>(kind) : pick<16, false, false>(kind);
+        return local ? pick<8, false, true>(kind, gw) : pick<8, false, false>(kind, gw);
+    return local ? pick<16, false, true>(kind, gw) : pick<16, false, false>(kind, gw);
 }
 
-hipError_t launch_ar(int kind, bool f32, bool local, const Launch &a, uint32_t grid,
+hipError_t launch_ar(int kind, bool f32, bool local, int gw, const Launch &a, uint32_t grid,
                      uint32_t threads, hipStream_t stream)
 {
-    const void *fn = kernel_for(kind, (int)a.n_ranks, f32, local);
+    const void *fn = kernel_for(kind, (int)a.n_ranks, f32, local, gw);
     if (fn == nullptr)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&a};
@@ -1977,7 +1998,7 @@ hipError_t launch_norm(int kind, bool local, const NormLaunch &L, uint32_t grid,
 {
     if (kind != K_ONESHOT_LL_NORM && kind != K_ONESHOT_DIRECT_NORM && kind != K_ONESHOT_ROWS_NORM)
         return hipErrorInvalidValue;
-    const void *fn = kernel_for(kind, (int)L.base.n_ranks, false, local);
+    const void *fn = kernel_for(kind, (int)L.base.n_ranks, false, local, 0);
     if (fn == nullptr)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&L};
