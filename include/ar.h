@@ -234,9 +234,9 @@ int ar_set_options(int algo, int proto);
 /*
  * ar_set_launch -- tuning: workgroups per rank (0 = automatic) and threads
  * per workgroup (64, 128 or 256; 0 = automatic).  The LL kernel always
- * uses one wave per rank (64 x the next power of two >= N threads) and the
- * sentinel and LL128 kernels 256 threads: their waves share the peers of a
- * tile.  The
+ * uses one wave per rank (64 x the next power of two >= N threads), the
+ * sentinel kernels 512 threads and the LL128 kernels 256: their waves share
+ * the peers of a tile.  The
  * workgroups per rank are capped at each call so that the whole grid is
  * resident at once (every poll then has a running producer).
  * AR_ERR_INVALID for unsupported values.

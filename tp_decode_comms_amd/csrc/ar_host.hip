@@ -288,7 +288,9 @@ int plan_geometry(size_t n, bool f32, Plan *p)
         uint32_t w = 1;
         while (w < N) w <<= 1;
         p->threads = 64 * w;
-    } else if (p->kind == ar::K_ONESHOT_SENTINEL || p->kind == ar::K_TWOSHOT_SENTINEL || l128)
+    } else if (p->kind == ar::K_ONESHOT_SENTINEL || p->kind == ar::K_TWOSHOT_SENTINEL)
+        p->threads = 512;               // 8 waves share the peers of a tile
+    else if (l128)
         p->threads = 256;               // 4 waves share the peers of a tile
     else if (g.threads > 0)
         p->threads = (uint32_t)g.threads;

@@ -749,13 +749,16 @@ __global__ __launch_bounds__(1024) void k_oneshot_rows_norm(const NormLaunch L)
 // a peer's call-k data proves the peer finished call k-1 (double buffering),
 // so the re-arm of parity k&1 always lands before the peer's call k+2 write.
 //
-// As in the one-shot LL kernel, a workgroup of 4 waves owns 64 chunks (of 8
-// elements) per round and the peers are split over the waves: wave w pushes
-// the chunk into the inboxes of the peers s with s % 4 == w, and once those
-// stores are acknowledged it receives the same peers' chunks from its own
-// inbox, re-arms their slots and stages the values in LDS; after a
-// workgroup barrier wave 0 reduces the tile in global rank order.
-constexpr int SENT_WAVES = 4;
+// As in the one-shot LL kernel, a workgroup of SENT_WAVES = 8 waves owns 64
+// chunks (of 8 elements) per round and the peers are split over the waves:
+// wave w pushes the chunk into the inboxes of the peers s with s % 8 == w,
+// and once those stores are acknowledged it receives the same peers' chunks
+// from its own inbox, re-arms their slots and stages the values in LDS;
+// after a workgroup barrier wave 0 reduces the tile in global rank order.
+// (8 waves rather than 4, same-box A/B: 4 ranks x 8 KiB 2.67 -> 2.46 us,
+// 8 x 16 KiB 3.36 -> 2.96, 16 ranks x 112 KiB two-shot 8.9 -> 6.8; the
+// 16-rank one-shot 17.3 -> 17.8.)
+constexpr int SENT_WAVES = 8;
 
 template <int NMAX, bool F32, bool LOCAL>
 __device__ __forceinline__ bool sent_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
@@ -849,7 +852,7 @@ __device__ __forceinline__ bool sent_round(const Launch &a, const Ctx0 &c, const
 }
 
 template <int NMAX, bool F32, bool LOCAL>
-__global__ __launch_bounds__(256) void k_oneshot_sentinel(const Launch a)
+__global__ __launch_bounds__(512) void k_oneshot_sentinel(const Launch a)
 {
     __shared__ u32x4 stage[NMAX][64];
     __shared__ uint32_t failed;
@@ -1590,9 +1593,9 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 // and writes it to out[q]; every rank polls AG[q][*], copies to out, re-arms.
 // Inbox regions [recv][send][parity] x s2_stride, one descriptor each.
 //
-// A workgroup of 4 waves owns 64 chunks of every slice per round, and the
-// peers are split over the waves as in the one-shot kernels: wave w pushes
-// the slices of, and receives from, the peers s with s % 4 == w.  The
+// A workgroup of SENT_WAVES waves owns 64 chunks of every slice per round,
+// and the peers are split over the waves as in the one-shot kernels: wave w
+// pushes the slices of, and receives from, the peers s with s % 8 == w.  The
 // received slice-q chunks are staged in LDS and reduced by wave 0, which
 // puts the bf16 result in LDS for every wave's all-gather pushes.
 template <int NMAX, bool F32, bool LOCAL>
@@ -1738,7 +1741,7 @@ __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const C
 }
 
 template <int NMAX, bool F32, bool LOCAL>
-__global__ __launch_bounds__(256) void k_twoshot_sentinel(const Launch a)
+__global__ __launch_bounds__(512) void k_twoshot_sentinel(const Launch a)
 {
     __shared__ u32x4 stage[NMAX][64];
     __shared__ u32x4 red[64];
