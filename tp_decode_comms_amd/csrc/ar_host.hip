@@ -403,8 +403,10 @@ int check_call(const void *const *rank_bufs, const void *out, size_t out_elem_by
 }
 
 // Checks that a launch's workgroups are dealt to the 8 XCDs round-robin:
-// workgroup b on XCD (b + o) % 8 for one offset o per launch, for grids of
-// both workgroup sizes in use.  The XCD-local scope is only enabled if so.
+// the workgroup with linear index b on XCD (b + o) % 8 for one offset o per
+// launch, for both workgroup sizes in use and for a flat grid as well as
+// the AllReduce grid shape (8, N, blocks).  The XCD-local scope is only
+// enabled if so.
 hipError_t verify_placement(bool *ok)
 {
     *ok = false;
@@ -415,23 +417,30 @@ hipError_t verify_placement(bool *ok)
         return e;
     std::vector<uint32_t> h(grid);
     bool good = true;
-    for (uint32_t threads : {64u, 256u}) {
-        if ((e = ar::launch_fill(d, grid, 0xFFFFFFFFu, 0)) != hipSuccess ||
-            (e = ar::launch_xcc_map(d, grid, threads, 0)) != hipSuccess ||
-            (e = hipMemcpy(h.data(), d, grid * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+    const uint32_t N = (uint32_t)g.n_ranks;
+    const uint32_t shapes[2][3] = {{grid, 1, 1}, {ar::XCDS, N, grid / (ar::XCDS * N)}};
+    for (const auto &sh : shapes) {
+        const uint32_t total = sh[0] * sh[1] * sh[2];
+        for (uint32_t threads : {64u, 256u}) {
+            if ((e = ar::launch_fill(d, grid, 0xFFFFFFFFu, 0)) != hipSuccess ||
+                (e = ar::launch_xcc_map(d, sh[0], sh[1], sh[2], threads, 0)) != hipSuccess ||
+                (e = hipMemcpy(h.data(), d, grid * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+                break;
+            uint32_t bad = 0, first = total;
+            const uint32_t o = h[0] % ar::XCDS;
+            for (uint32_t b = 0; b < total; ++b)
+                if (h[b] != (b + o) % ar::XCDS) {
+                    ++bad;
+                    if (first == total) first = b;
+                }
+            if (bad && debug_enabled())
+                fprintf(stderr, "[ar] placement check (grid %ux%ux%u, %u threads): %u of %u "
+                        "workgroups off the round-robin order (offset %u), first b=%u on XCD %u\n",
+                        sh[0], sh[1], sh[2], threads, bad, total, o, first, h[first]);
+            good = good && bad == 0;
+        }
+        if (e != hipSuccess)
             break;
-        uint32_t bad = 0, first = grid;
-        const uint32_t o = h[0] % ar::XCDS;
-        for (uint32_t b = 0; b < grid; ++b)
-            if (h[b] != (b + o) % ar::XCDS) {
-                ++bad;
-                if (first == grid) first = b;
-            }
-        if (bad && debug_enabled())
-            fprintf(stderr, "[ar] placement check (%u threads): %u of %u workgroups off the "
-                    "round-robin order (offset %u), first b=%u on XCD %u\n", threads, bad, grid, o,
-                    first, h[first]);
-        good = good && bad == 0;
     }
     hipError_t ef = hipFree(d);
     if (e == hipSuccess)
@@ -461,11 +470,9 @@ void fill_launch(const void *const *rank_bufs, void *out, size_t n, uint32_t epo
     a.epoch = epoch;
     a.parts = p.parts;
     a.slice = p.slice;
-    // workgroup layout: blocks of 8 parts x N ranks when parts % 8 == 0 (so
-    // part p runs on XCD p % 8), else rank-interleaved (blocks of N)
+    // workgroup layout: grid (8, N, parts / 8) when parts % 8 == 0 (blocks
+    // of 8 parts x N ranks, so part p runs on XCD p % 8), else (1, N, parts)
     a.xshift = p.parts % ar::XCDS == 0 ? 3u : 0u;
-    a.span = (uint32_t)g.n_ranks << a.xshift;
-    a.span_magic = a.span > 1 ? (uint32_t)(((1ull << 32) + a.span - 1) / a.span) : 0u;
     uint64_t ticks = (uint64_t)g.watchdog_us * 100u;   // 100 MHz clock
     a.watchdog_ticks = (uint32_t)std::min<uint64_t>(ticks, 0xFFFFFFFFu);
 }
@@ -486,7 +493,7 @@ int do_allreduce(const void *const *rank_bufs, void *out, size_t n, uint32_t epo
     if (debug_enabled())
         fprintf(stderr, "[ar] n=%zu epoch=%u kind=%d grid=%u threads=%u slice=%u f32=%d local=%d\n",
                 n, epoch, p.kind, grid, p.threads, p.slice, (int)f32, (int)p.local);
-    hipError_t e = ar::launch_ar(p.kind, f32, p.local, p.gw, a, grid, p.threads, stream);
+    hipError_t e = ar::launch_ar(p.kind, f32, p.local, p.gw, a, p.threads, stream);
     if (e != hipSuccess)
         return hip_fail(e);
     g.last_epoch = epoch;
@@ -601,7 +608,7 @@ int do_allreduce_norm(const void *const *rank_bufs, const void *const *residual,
     if (debug_enabled())
         fprintf(stderr, "[ar] norm kind=%d rows=%zu hidden=%zu epoch=%u grid=%u threads=%u local=%d\n",
                 p.kind, rows, hidden, epoch, grid, p.threads, (int)p.local);
-    hipError_t e = ar::launch_norm(p.kind, p.local, L, grid, p.threads, stream);
+    hipError_t e = ar::launch_norm(p.kind, p.local, L, p.threads, stream);
     if (e != hipSuccess)
         return hip_fail(e);
     g.last_epoch = epoch;

@@ -45,19 +45,23 @@ enum KernelKind {
 // available), ignored by the others
 const void *kernel_for(int kind, int n_ranks, bool f32, bool local, int gw);
 
-hipError_t launch_ar(int kind, bool f32, bool local, int gw, const Launch &a, uint32_t grid,
-                     uint32_t threads, hipStream_t stream);
+// grid (2^xshift, N, parts >> xshift) from the launch record (parts must be a
+// multiple of 2^xshift)
+hipError_t launch_ar(int kind, bool f32, bool local, int gw, const Launch &a, uint32_t threads,
+                     hipStream_t stream);
 // the fused AllReduce + residual add + RMS norm (kind K_ONESHOT_LL_NORM,
 // K_ONESHOT_DIRECT_NORM or K_ONESHOT_ROWS_NORM)
-hipError_t launch_norm(int kind, bool local, const NormLaunch &L, uint32_t grid, uint32_t threads,
+hipError_t launch_norm(int kind, bool local, const NormLaunch &L, uint32_t threads,
                        hipStream_t stream);
 // stand-alone residual add + RMS norm of an AllReduce result: one workgroup
 // of 1024 threads per (rank, row)
 hipError_t launch_add_rmsnorm(const void *a, const void *const *res, const void *gamma, float eps,
                               void *h, void *y, uint32_t n_ranks, uint32_t rows, uint32_t hidden,
                               hipStream_t stream);
-// out[b] = XCD index of workgroup b, for b < grid
-hipError_t launch_xcc_map(uint32_t *out, uint32_t grid, uint32_t threads, hipStream_t stream);
+// out[b] = XCD index of the workgroup with linear index b = x + gx (y + gy z),
+// over a gx x gy x gz grid
+hipError_t launch_xcc_map(uint32_t *out, uint32_t gx, uint32_t gy, uint32_t gz, uint32_t threads,
+                          hipStream_t stream);
 hipError_t launch_step_end(uint32_t *ctl, uint32_t calls, char *ll, size_t ll_bytes, char *l128,
                            size_t l128_bytes, uint32_t *done, uint32_t *stats, size_t stats_bytes,
                            hipStream_t stream);

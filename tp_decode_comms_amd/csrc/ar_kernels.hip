@@ -45,6 +45,13 @@ struct Ctx0 {
     uint64_t t0;
 };
 
+// The workgroup's position in dispatch order, x + X (y + N z) on the grid
+// (X, N, parts / X) described at begin().
+__device__ __forceinline__ uint32_t linear_id(const Launch &a)
+{
+    return ((blockIdx.z * a.n_ranks + blockIdx.y) << a.xshift) + blockIdx.x;
+}
+
 // The flag-sequence base.  Only the step-end kernel and the host's re-arm
 // kernels write it, always in an earlier launch; the launch boundary makes
 // that write visible, so a plain load suffices (no launch writes it while
@@ -78,7 +85,7 @@ __device__ __forceinline__ void finish(const Launch &a, const Ctx0 &c)
         uint64_t t1 = clock100();
         // 64 sub-slots per call spread the atomics over 64 addresses
         const uint32_t slot = (c.flag - 1u) % a.ts_slots;
-        uint64_t *p = a.ts + ((size_t)slot * TS_SUB + (blockIdx.x % TS_SUB)) * 2u;
+        uint64_t *p = a.ts + ((size_t)slot * TS_SUB + (linear_id(a) % TS_SUB)) * 2u;
         __hip_atomic_fetch_min(p, c.t0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_fetch_max(p + 1, t1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -88,26 +95,38 @@ template <bool LOCAL>
 __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
 {
     c.t0 = clock100();
-    // blocks of X*N consecutive workgroups, rank-major over X consecutive
-    // parts: with X = 8 (parts a multiple of 8) part p lands on XCD p % 8;
-    // every workgroup's peers (same part, other ranks) sit in its own block
-    // and parts 0..7 of every rank (arrival writers, completion waiters) in
-    // the first, so progress never needs more than one block resident
-    // (the host passes X as a shift and span = X*N with its reciprocal
-    // ceil(2^32 / span), exact for every grid below 2^24 workgroups)
-    const uint32_t b = blockIdx.x;
-    const uint32_t blk = a.span == 1u ? b : __umulhi(b, a.span_magic);
-    const uint32_t w = b - blk * a.span;
-    c.rank = w >> a.xshift;
+    // The grid is (X, N, parts / X) with X = 2^xshift consecutive parts of
+    // one rank along x (X = 8 when parts is a multiple of 8, else 1): the
+    // rank is blockIdx.y and the part (blockIdx.z << xshift) + blockIdx.x.
+    // Workgroups are dispatched in linear order x + X (y + N z), so blocks
+    // of X*N consecutive workgroups hold parts zX .. zX+X-1 of every rank:
+    // with X = 8 part p lands on XCD p % 8, every workgroup's peers (same
+    // part, other ranks) sit in its own block, and parts 0..7 of every rank
+    // (arrival writers, completion waiters) in the first, so progress never
+    // needs more than one block resident.  Rank and part come from the
+    // workgroup id itself, so nothing in the prologue waits for a load
+    // before the rank's own pointers can be fetched.
+    c.rank = blockIdx.y;
     // The XCD-local scope takes the low three part bits from the XCD the
     // workgroup actually runs on.  Dispatch is round-robin from some XCD o
     // (o = 0 normally; a profiler can shift it), so within each group of 8
     // consecutive workgroups of one rank the XCDs are a rotation of 0..7:
     // the mapping stays one-to-one and part p always runs on XCD p % 8,
-    // whatever o is.  (ar_init checks the round-robin order before it
-    // enables this scope.)
-    const uint32_t lo = LOCAL ? xcc_id() : (w & ((1u << a.xshift) - 1u));
-    c.part = (blk << a.xshift) + lo;
+    // whatever o is.  (ar_init checks the round-robin order, for this grid
+    // shape too, before it enables this scope.)
+    const uint32_t lo = LOCAL ? xcc_id() : blockIdx.x;
+    // The launch record lives in memory that is read cold at every launch:
+    // each round of dependent loads from it costs a memory round trip before
+    // the first data load can go out.  Handing the fields every kernel uses
+    // to an empty asm statement makes the compiler issue all of them at once
+    // (the rank's own input pointer included, whose address depends only on
+    // blockIdx.y) behind a single wait.
+    // (blockDim.x is read from the launch's hidden arguments, so it is one
+    // of them.)
+    asm volatile("" ::"s"(a.in[c.rank]), "s"(a.out), "s"(a.ctl), "s"(a.n), "s"(a.n_ranks),
+                 "s"(a.epoch), "s"(a.parts), "s"(a.slice), "s"(a.xshift), "s"(a.delays),
+                 "s"(blockDim.x));
+    c.part = (blockIdx.z << a.xshift) + lo;
     c.par = a.epoch & 1u;
 }
 
@@ -319,7 +338,6 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll(const Launch a)
     const uint32_t C = a.n >> 2;                    // 4-element chunks per rank
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t step = a.parts * 64u;
-    const uint32_t rounds = (C + step - 1u) / step;
     if ((blockDim.x >> 6) < a.n_ranks) {            // the host launches a wave per rank
         if (threadIdx.x == 0)                       // (never otherwise: report, do nothing)
             Ctl{a.ctl}.fail(c.rank, blockDim.x, a.epoch);
@@ -343,7 +361,9 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll(const Launch a)
     auto out4 = [&](uint32_t cch, const float *v) { store4<F32>(o, cch * 4u, v); };
     if (!ll_round<NMAX, LOCAL>(a, c, ctl, llr, ch, C, x, stage, &failed, out4))
         return;
-    for (uint32_t it = 1; it < rounds; ++it) {
+    // later rounds while the workgroup has chunks left (the same rounds for
+    // every peer of the part)
+    for (uint32_t base = c.part * 64u + step; base < C; base += step) {
         ch += step;
         x = (wave == 0u && ch < C) ? ld8<CP_PLAIN>(inr, ch * 8u) : u32x2{0u, 0u};
         if (!ll_round<NMAX, LOCAL>(a, c, ctl, llr, ch, C, x, stage, &failed, out4))
@@ -911,7 +931,6 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
     const uint32_t N = a.n_ranks;
     const uint32_t G = a.n >> 3;
     const uint32_t step = a.parts * blockDim.x;
-    const uint32_t rounds = (G + step - 1u) / step;
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     start_delay(a, c);
@@ -923,10 +942,7 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
     for (int s = 0; s < NMAX; ++s)
         src[s] = in_rsrc(a, (uint32_t)s < N ? (uint32_t)s : 0u);
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
-    uint32_t ch = c.part * blockDim.x + threadIdx.x;
-    for (uint32_t it = 0; it < rounds; ++it, ch += step) {
-        if (ch >= G)
-            continue;
+    for (uint32_t ch = c.part * blockDim.x + threadIdx.x; ch < G; ch += step) {
         u32x4 V[NMAX];
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
@@ -977,24 +993,33 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     // load their first round's own chunks before the wait, so HBM is busy
     // while the flags travel (the polling wave cannot: its loads return in
     // order, so a pending data load would delay every poll behind it).
+    //
+    // Every load below is issued unconditionally; a chunk outside the slice
+    // gets an offset past the end of its buffer, for which the buffer
+    // instruction returns zeros without touching memory.  A conditional load
+    // merged with a fallback value makes the compiler wait for every earlier
+    // load (the load counter is in order) before each one, and the N sources
+    // would then be fetched one after another.
     const uint32_t ch0 = c.part * blockDim.x + threadIdx.x;
     const __amdgpu_buffer_rsrc_t srcq = in_rsrc(a, q);
-    u32x4 own[TS_CPI];
     const bool poller = threadIdx.x < 64u;
+    u32x4 own[TS_CPI];
+#pragma unroll
+    for (int k = 0; k < TS_CPI; ++k)
+        own[k] = u32x4{0u, 0u, 0u, 0u};
     if (!poller) {
 #pragma unroll
         for (int k = 0; k < TS_CPI; ++k)
-            own[k] = ch0 + k * step < G ? ld16<TS_LD>(srcq, (lo + (ch0 + k * step) * 8u) * 2u)
-                                        : u32x4{0u, 0u, 0u, 0u};
+            own[k] = ld16<TS_LD>(srcq, ch0 + k * step < G ? (lo + (ch0 + k * step) * 8u) * 2u
+                                                          : OFF_NONE);
     }
     if (!wait_arrivals_wg<LOCAL>(a, c, ctl))
         return;
-    if (poller) {
-#pragma unroll
-        for (int k = 0; k < TS_CPI; ++k)
-            own[k] = ch0 + k * step < G ? ld16<TS_LD>(srcq, (lo + (ch0 + k * step) * 8u) * 2u)
-                                        : u32x4{0u, 0u, 0u, 0u};
-    }
+    // The prefetched chunks landed during the flag round trip; draining them
+    // here leaves no load in flight, so the round's loads below issue back to
+    // back (a pending load would make the compiler wait before reusing its
+    // address registers).
+    wait_stores();
     __amdgpu_buffer_rsrc_t src[NMAX];
 #pragma unroll
     for (int s = 0; s < NMAX; ++s)
@@ -1002,38 +1027,60 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
     // TS_CPI chunks per lane per round keep more loads in flight (2 measured
     // best: 1 or a streaming load policy lose 5-20% at 4 MiB per rank)
+    const uint32_t esz = F32 ? 4u : 2u;
     for (uint32_t ch = ch0; ch < G; ch += TS_CPI * step) {
         u32x4 V[TS_CPI][NMAX];
         bool in[TS_CPI];
-        const bool first = ch == ch0;
+        uint32_t off[TS_CPI];
+        // the non-polling waves hold their own chunks of the first round
+        // already: those slots' loads go past the end (zeros, no traffic)
+        // and the fold takes `own` instead
+        const bool pre = ch == ch0 && !poller;
 #pragma unroll
-        for (int k = 0; k < TS_CPI; ++k)
+        for (int k = 0; k < TS_CPI; ++k) {
             in[k] = ch + k * step < G;
+            off[k] = in[k] ? (lo + (ch + k * step) * 8u) * 2u : OFF_NONE;
+        }
+        // all NMAX slots are loaded (those of absent ranks past the end), so
+        // that the loads form one straight run the compiler does not split
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N) {
 #pragma unroll
-                for (int k = 0; k < TS_CPI; ++k)
-                    V[k][s] = (first && (uint32_t)s == q) ? own[k]
-                              : in[k] ? ld16<TS_LD>(src[s], (lo + (ch + k * step) * 8u) * 2u)
-                                      : u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int k = 0; k < TS_CPI; ++k)
+                V[k][s] = ld16<TS_LD>(src[s], ((uint32_t)s >= N || (pre && (uint32_t)s == q))
+                                                  ? OFF_NONE : off[k]);
         Acc8 acc[TS_CPI];
 #pragma unroll
         for (int k = 0; k < TS_CPI; ++k)
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((uint32_t)s < N) {
-                    if (s == 0) acc[k].init(V[k][s]);
-                    else acc[k].add(V[k][s]);
+                    const u32x4 x = (pre && (uint32_t)s == q) ? own[k] : V[k][s];
+                    if (s == 0) acc[k].init(x);
+                    else acc[k].add(x);
                 }
+        // the round's loads are all consumed (those of absent ranks too), so
+        // the next round's loads again issue without waits
+        wait_stores();
 #pragma unroll
         for (int r = 0; r < NMAX; ++r)
             if ((uint32_t)r < N) {
 #pragma unroll
-                for (int k = 0; k < TS_CPI; ++k)
-                    if (in[k])
-                        store8<F32, TS_ST>(oa, (uint32_t)r * a.n + lo + (ch + k * step) * 8u, acc[k]);
+                for (int k = 0; k < TS_CPI; ++k) {
+                    const uint32_t o = in[k] ? ((uint32_t)r * a.n + lo + (ch + k * step) * 8u) * esz
+                                             : OFF_NONE;
+                    if constexpr (F32) {
+                        u32x4 l, h;
+                        l.x = __float_as_uint(acc[k].v[0]); l.y = __float_as_uint(acc[k].v[1]);
+                        l.z = __float_as_uint(acc[k].v[2]); l.w = __float_as_uint(acc[k].v[3]);
+                        h.x = __float_as_uint(acc[k].v[4]); h.y = __float_as_uint(acc[k].v[5]);
+                        h.z = __float_as_uint(acc[k].v[6]); h.w = __float_as_uint(acc[k].v[7]);
+                        st16<TS_ST>(l, oa, o);
+                        st16<TS_ST>(h, oa, o + 16u);
+                    } else {
+                        st16<TS_ST>(acc[k].bf16(), oa, o);
+                    }
+                }
             }
     }
     // completion: my stores are at the coherence point, then my flag.  The
@@ -1110,8 +1157,8 @@ __device__ __forceinline__ bool grid_barrier(const Launch &a, const Ctx0 &c, con
     __syncthreads();
     __shared__ uint32_t ok;
     if (threadIdx.x == 0) {
-        const uint32_t G = gridDim.x;
-        const uint32_t grp = blockIdx.x % (uint32_t)XCDS;
+        const uint32_t G = a.parts * a.n_ranks;
+        const uint32_t grp = linear_id(a) % (uint32_t)XCDS;
         const uint32_t groups = G < (uint32_t)XCDS ? G : (uint32_t)XCDS;
         const uint32_t size = (G - grp + XCDS - 1u) / XCDS;     // workgroups in my group
         uint32_t *gcnt = a.ctl + CTL_BAR_GROUP + 32u * grp;
@@ -1136,7 +1183,7 @@ __device__ __forceinline__ bool grid_barrier(const Launch &a, const Ctx0 &c, con
             }
         }
         if (!last) {
-            uint32_t *gen = a.ctl + gen_base + 32u * (blockIdx.x % (uint32_t)XCDS);
+            uint32_t *gen = a.ctl + gen_base + 32u * grp;
             Watch w;
             w.begin(a.watchdog_ticks);
             while ((int32_t)(__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
@@ -1925,11 +1972,13 @@ __global__ __launch_bounds__(256) void k_fill(uint32_t *p, size_t words, uint32_
         p[i] = value;
 }
 
-// Records the XCD of every workgroup: out[b] = XCC_ID of workgroup b.
-__global__ __launch_bounds__(256) void k_xcc_map(uint32_t *out, uint32_t n)
+// Records the XCD of every workgroup: out[b] = XCC_ID of the workgroup with
+// linear index b = x + gx (y + gy z) (grid gx x gy x gz).
+__global__ __launch_bounds__(256) void k_xcc_map(uint32_t *out, uint32_t n, uint32_t gx, uint32_t gy)
 {
-    if (threadIdx.x == 0 && blockIdx.x < n)
-        out[blockIdx.x] = xcc_id();
+    const uint32_t b = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    if (threadIdx.x == 0 && b < n)
+        out[b] = xcc_id();
 }
 
 // ------------------------------------------------------------ dispatch
@@ -1986,31 +2035,39 @@ const void *kernel_for(int kind, int n_ranks, bool f32, bool local, int gw)
     return local ? pick<16, false, true>(kind, gw) : pick<16, false, false>(kind, gw);
 }
 
-hipError_t launch_ar(int kind, bool f32, bool local, int gw, const Launch &a, uint32_t grid,
-                     uint32_t threads, hipStream_t stream)
+// The grid of a launch record: (X, N, parts / X), X = 2^xshift.
+static dim3 grid_of(const Launch &a)
 {
-    const void *fn = kernel_for(kind, (int)a.n_ranks, f32, local, gw);
-    if (fn == nullptr)
-        return hipErrorInvalidValue;
-    void *args[] = {(void *)&a};
-    return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
+    return dim3(1u << a.xshift, a.n_ranks, a.parts >> a.xshift);
 }
 
-hipError_t launch_norm(int kind, bool local, const NormLaunch &L, uint32_t grid, uint32_t threads,
+hipError_t launch_ar(int kind, bool f32, bool local, int gw, const Launch &a, uint32_t threads,
+                     hipStream_t stream)
+{
+    const void *fn = kernel_for(kind, (int)a.n_ranks, f32, local, gw);
+    if (fn == nullptr || (a.parts & ((1u << a.xshift) - 1u)) != 0u)
+        return hipErrorInvalidValue;
+    void *args[] = {(void *)&a};
+    return hipLaunchKernel(fn, grid_of(a), dim3(threads), args, 0, stream);
+}
+
+hipError_t launch_norm(int kind, bool local, const NormLaunch &L, uint32_t threads,
                        hipStream_t stream)
 {
     if (kind != K_ONESHOT_LL_NORM && kind != K_ONESHOT_DIRECT_NORM && kind != K_ONESHOT_ROWS_NORM)
         return hipErrorInvalidValue;
     const void *fn = kernel_for(kind, (int)L.base.n_ranks, false, local, 0);
-    if (fn == nullptr)
+    if (fn == nullptr || (L.base.parts & ((1u << L.base.xshift) - 1u)) != 0u)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&L};
-    return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
+    return hipLaunchKernel(fn, grid_of(L.base), dim3(threads), args, 0, stream);
 }
 
-hipError_t launch_xcc_map(uint32_t *out, uint32_t grid, uint32_t threads, hipStream_t stream)
+hipError_t launch_xcc_map(uint32_t *out, uint32_t gx, uint32_t gy, uint32_t gz, uint32_t threads,
+                          hipStream_t stream)
 {
-    hipLaunchKernelGGL(k_xcc_map, dim3(grid), dim3(threads), 0, stream, out, grid);
+    hipLaunchKernelGGL(k_xcc_map, dim3(gx, gy, gz), dim3(threads), 0, stream, out, gx * gy * gz,
+                       gx, gy);
     return hipGetLastError();
 }
 

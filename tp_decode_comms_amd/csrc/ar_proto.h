@@ -97,9 +97,7 @@ struct Launch {
     uint32_t parts;               // workgroups per rank
     uint32_t slice;               // two-shot slice length (multiple of 8)
     uint32_t watchdog_ticks;
-    uint32_t span;                // workgroups per placement block: N << xshift
-    uint32_t span_magic;          // ceil(2^32 / span) (span > 1)
-    uint32_t xshift;              // log2 of parts per rank in a block (3, or 0)
+    uint32_t xshift;              // log2 of parts per rank in a block (3, or 0): grid (2^xshift, N, parts >> xshift)
     uint32_t ts_slots;
     uint32_t delay_rows;
 };
@@ -125,6 +123,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                              0x00020000);
 }
+
+// A byte offset past the end of every buffer the kernels address (the host
+// keeps each buffer below 2^31 bytes): a raw buffer load at it returns zeros
+// without a memory access, a store at it is dropped.  It lets a load that
+// must be skipped still be issued unconditionally.
+constexpr uint32_t OFF_NONE = 0x80000000u;
 
 template <int CP> __device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
