@@ -312,7 +312,8 @@ int plan_geometry(size_t n, bool f32, Plan *p)
         units = n / 8; per_wg = 64; break;
     case ar::K_TWOSHOT_SENTINEL:
         units = p->slice / 8; per_wg = 64; break;
-    case ar::K_TWOSHOT_DIRECT:
+    case ar::K_TWOSHOT_DIRECT:       // the barrier-ful baseline shares its data phase
+    case ar::K_TWOSHOT_BARRIER:
         units = p->slice / 8; per_wg = ar::TWOSHOT_DIRECT_CHUNKS * p->threads; break;
     case ar::K_ONESHOT_DIRECT_NORM: // one 256-element norm block per wave
         units = n / ar::NORM_BLOCK_ELEMS; per_wg = p->threads / 64; break;

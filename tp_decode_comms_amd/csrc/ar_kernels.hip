@@ -917,125 +917,71 @@ __device__ __forceinline__ bool wait_arrivals_wg(const Launch &a, const Ctx0 &c,
     return ok != 0u;
 }
 
-// ========================================================= one-shot DIRECT
-// After the arrival flags, each rank reads every peer's input in place
-// with device-coherent loads and reduces.  The input of call k must stay
-// unchanged until call k has completed on every rank (the application-level
-// A/B double buffering of the SiFAR page, "SiFAR：无同步All-Reduce技术突破低
-// 延迟LLM推理瓶颈", technique one).
-template <int NMAX, bool F32, bool LOCAL>
-__global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
+// ============================================== in-place data phases
+// Shared by the flag kernels (DIRECT) and their barrier-ful baselines, so
+// that the two differ only in how they synchronise.
+
+// Descriptors of every rank's input, built before a kernel's first wait so
+// that reading the input pointers from the launch record is not a round of
+// loads between the synchronisation and the first data load.  Slots of
+// absent ranks hold null pointers and are only ever addressed past the end.
+template <int NMAX>
+__device__ __forceinline__ void input_rsrcs(const Launch &a, __amdgpu_buffer_rsrc_t (&src)[NMAX])
 {
-    Ctx0 c;
-    begin<LOCAL>(a, c);
-    const uint32_t N = a.n_ranks;
-    const uint32_t G = a.n >> 3;
-    const uint32_t step = a.parts * blockDim.x;
-    c.flag = load_seq(a) + a.epoch;
-    const Ctl ctl{a.ctl};
-    start_delay(a, c);
-    raise_arrival<LOCAL>(a, c);
-    if (!wait_arrivals<LOCAL>(a, c, ctl))
-        return;
-    __amdgpu_buffer_rsrc_t src[NMAX];
 #pragma unroll
-    for (int s = 0; s < NMAX; ++s)
-        src[s] = in_rsrc(a, (uint32_t)s < N ? (uint32_t)s : 0u);
-    const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
-    for (uint32_t ch = c.part * blockDim.x + threadIdx.x; ch < G; ch += step) {
+    for (int s = 0; s < NMAX; ++s) {
+        src[s] = in_rsrc(a, (uint32_t)s);
+        asm volatile("" ::"s"(src[s]));
+    }
+}
+
+// One-shot: out[rank][8ch .. 8ch+8) = fold over every input, for the
+// workgroup's chunks ch = ch0, ch0 + step, ...  Loads are issued
+// unconditionally (absent ranks past the end: zeros, no traffic), so the
+// compiler keeps the N loads of a chunk in one run instead of waiting for
+// earlier loads before each (the load counter is in order).
+template <int NMAX, bool F32>
+__device__ __forceinline__ void oneshot_data(const Launch &a, const __amdgpu_buffer_rsrc_t (&src)[NMAX],
+                                             __amdgpu_buffer_rsrc_t o, uint32_t G, uint32_t ch0,
+                                             uint32_t step)
+{
+    const uint32_t N = a.n_ranks;
+    for (uint32_t ch = ch0; ch < G; ch += step) {
         u32x4 V[NMAX];
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N)
-                V[s] = ld16<CP_DEV>(src[s], ch * 16u);
+            V[s] = ld16<CP_DEV>(src[s], (uint32_t)s < N ? ch * 16u : OFF_NONE);
         Acc8 acc;
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             if ((uint32_t)s < N) {
                 if (s == 0) acc.init(V[s]); else acc.add(V[s]);
             }
+        wait_stores();                  // every load consumed: the next chunk's run has no waits
         store8<F32>(o, ch * 8u, acc);
     }
-    finish(a, c);
 }
 
-// ========================================================= two-shot DIRECT
-// Reduce-scatter: rank q reads slice q of every rank's input in place (after
-// the arrival flags) and reduces it; all-gather: it stores the bf16
-// result straight into slice q of every rank's output (the bcast of the
-// reduced value), with streaming device-scope stores.  Each workgroup then
-// waits for its stores to be acknowledged and raises its completion flag;
-// one workgroup per rank waits for every writer's flag, after which every
-// slice of that rank's output is known to be complete.
-// Moves exactly the algorithmic bytes: N inputs read once, N outputs written
-// once.
+// Two-shot: rank q's slice [lo, lo + 8G) of every input, folded in rank
+// order and stored into that slice of every rank's output (streaming
+// device-scope stores), TS_CPI chunks per lane per round.
 constexpr uint32_t TS_CPI = TWOSHOT_DIRECT_CHUNKS;   // chunks per lane per round
 constexpr int TS_LD = CP_DEV;                       // input loads
 constexpr int TS_ST = CP_NT | CP_DEV;               // output stores (streaming)
 
-template <int NMAX, bool F32, bool LOCAL>
-__global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
+template <int NMAX, bool F32>
+__device__ __forceinline__ void twoshot_data(const Launch &a, const __amdgpu_buffer_rsrc_t (&src)[NMAX],
+                                             __amdgpu_buffer_rsrc_t oa, uint32_t lo, uint32_t G,
+                                             uint32_t ch0, uint32_t step)
 {
-    Ctx0 c;
-    begin<LOCAL>(a, c);
     const uint32_t N = a.n_ranks;
-    const uint32_t q = c.rank;
-    const uint32_t L = a.slice;
-    const uint32_t lo = q * L;
-    const uint32_t Lq = lo >= a.n ? 0u : (a.n - lo < L ? a.n - lo : L);
-    const uint32_t G = Lq >> 3;                     // chunks of my slice
-    const uint32_t step = a.parts * blockDim.x;
-    c.flag = load_seq(a) + a.epoch;
-    const Ctl ctl{a.ctl};
-    start_delay(a, c);
-    raise_arrival<LOCAL>(a, c);
-    // A rank's own input needs no arrival flag: the waves that do not poll
-    // load their first round's own chunks before the wait, so HBM is busy
-    // while the flags travel (the polling wave cannot: its loads return in
-    // order, so a pending data load would delay every poll behind it).
-    //
-    // Every load below is issued unconditionally; a chunk outside the slice
-    // gets an offset past the end of its buffer, for which the buffer
-    // instruction returns zeros without touching memory.  A conditional load
-    // merged with a fallback value makes the compiler wait for every earlier
-    // load (the load counter is in order) before each one, and the N sources
-    // would then be fetched one after another.
-    const uint32_t ch0 = c.part * blockDim.x + threadIdx.x;
-    const __amdgpu_buffer_rsrc_t srcq = in_rsrc(a, q);
-    const bool poller = threadIdx.x < 64u;
-    u32x4 own[TS_CPI];
-#pragma unroll
-    for (int k = 0; k < TS_CPI; ++k)
-        own[k] = u32x4{0u, 0u, 0u, 0u};
-    if (!poller) {
-#pragma unroll
-        for (int k = 0; k < TS_CPI; ++k)
-            own[k] = ld16<TS_LD>(srcq, ch0 + k * step < G ? (lo + (ch0 + k * step) * 8u) * 2u
-                                                          : OFF_NONE);
-    }
-    if (!wait_arrivals_wg<LOCAL>(a, c, ctl))
-        return;
-    // The prefetched chunks landed during the flag round trip; draining them
-    // here leaves no load in flight, so the round's loads below issue back to
-    // back (a pending load would make the compiler wait before reusing its
-    // address registers).
-    wait_stores();
-    __amdgpu_buffer_rsrc_t src[NMAX];
-#pragma unroll
-    for (int s = 0; s < NMAX; ++s)
-        src[s] = in_rsrc(a, (uint32_t)s < N ? (uint32_t)s : 0u);
-    const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
-    // TS_CPI chunks per lane per round keep more loads in flight (2 measured
-    // best: 1 or a streaming load policy lose 5-20% at 4 MiB per rank)
     const uint32_t esz = F32 ? 4u : 2u;
+    // TS_CPI chunks per lane per round keep more loads in flight (2 measured
+    // best at 4 MiB per rank: 1, 3 and 4 lose 6-9%)
     for (uint32_t ch = ch0; ch < G; ch += TS_CPI * step) {
         u32x4 V[TS_CPI][NMAX];
         bool in[TS_CPI];
         uint32_t off[TS_CPI];
-        // the non-polling waves hold their own chunks of the first round
-        // already: those slots' loads go past the end (zeros, no traffic)
-        // and the fold takes `own` instead
-        const bool pre = ch == ch0 && !poller;
 #pragma unroll
         for (int k = 0; k < TS_CPI; ++k) {
             in[k] = ch + k * step < G;
@@ -1047,17 +993,15 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
         for (int s = 0; s < NMAX; ++s)
 #pragma unroll
             for (int k = 0; k < TS_CPI; ++k)
-                V[k][s] = ld16<TS_LD>(src[s], ((uint32_t)s >= N || (pre && (uint32_t)s == q))
-                                                  ? OFF_NONE : off[k]);
+                V[k][s] = ld16<TS_LD>(src[s], (uint32_t)s < N ? off[k] : OFF_NONE);
         Acc8 acc[TS_CPI];
 #pragma unroll
         for (int k = 0; k < TS_CPI; ++k)
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((uint32_t)s < N) {
-                    const u32x4 x = (pre && (uint32_t)s == q) ? own[k] : V[k][s];
-                    if (s == 0) acc[k].init(x);
-                    else acc[k].add(x);
+                    if (s == 0) acc[k].init(V[k][s]);
+                    else acc[k].add(V[k][s]);
                 }
         // the round's loads are all consumed (those of absent ranks too), so
         // the next round's loads again issue without waits
@@ -1083,6 +1027,71 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
                 }
             }
     }
+}
+
+// ========================================================= one-shot DIRECT
+// After the arrival flags, each rank reads every peer's input in place
+// with device-coherent loads and reduces.  The input of call k must stay
+// unchanged until call k has completed on every rank (the application-level
+// A/B double buffering of the SiFAR page, "SiFAR：无同步All-Reduce技术突破低
+// 延迟LLM推理瓶颈", technique one).
+template <int NMAX, bool F32, bool LOCAL>
+__global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
+{
+    Ctx0 c;
+    begin<LOCAL>(a, c);
+    const uint32_t G = a.n >> 3;
+    const uint32_t step = a.parts * blockDim.x;
+    c.flag = load_seq(a) + a.epoch;
+    const Ctl ctl{a.ctl};
+    start_delay(a, c);
+    raise_arrival<LOCAL>(a, c);
+    __amdgpu_buffer_rsrc_t src[NMAX];
+    input_rsrcs<NMAX>(a, src);
+    const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
+    if (!wait_arrivals<LOCAL>(a, c, ctl))
+        return;
+    oneshot_data<NMAX, F32>(a, src, o, G, c.part * blockDim.x + threadIdx.x, step);
+    finish(a, c);
+}
+
+// ========================================================= two-shot DIRECT
+// Reduce-scatter: rank q reads slice q of every rank's input in place (after
+// the arrival flags) and reduces it; all-gather: it stores the bf16
+// result straight into slice q of every rank's output (the bcast of the
+// reduced value), with streaming device-scope stores.  Each workgroup then
+// waits for its stores to be acknowledged and raises its completion flag;
+// one workgroup per rank waits for every writer's flag, after which every
+// slice of that rank's output is known to be complete.
+// Moves exactly the algorithmic bytes: N inputs read once, N outputs written
+// once.
+template <int NMAX, bool F32, bool LOCAL>
+__global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
+{
+    Ctx0 c;
+    begin<LOCAL>(a, c);
+    const uint32_t N = a.n_ranks;
+    const uint32_t q = c.rank;
+    const uint32_t L = a.slice;
+    const uint32_t lo = q * L;
+    const uint32_t Lq = lo >= a.n ? 0u : (a.n - lo < L ? a.n - lo : L);
+    const uint32_t G = Lq >> 3;                     // chunks of my slice
+    const uint32_t step = a.parts * blockDim.x;
+    c.flag = load_seq(a) + a.epoch;
+    const Ctl ctl{a.ctl};
+    start_delay(a, c);
+    raise_arrival<LOCAL>(a, c);
+    // Every input is read after the arrival wait, the rank's own too: with
+    // the prologue down to one launch-record round and the sequence load,
+    // the flags arrive about when loads could first be issued, and loading
+    // the own chunks ahead of the wait measured slower (8 x 4 MiB: 12.39 vs
+    // 12.64 us per call).
+    __amdgpu_buffer_rsrc_t src[NMAX];
+    input_rsrcs<NMAX>(a, src);
+    const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
+    if (!wait_arrivals_wg<LOCAL>(a, c, ctl))
+        return;
+    twoshot_data<NMAX, F32>(a, src, oa, lo, G, c.part * blockDim.x + threadIdx.x, step);
     // completion: my stores are at the coherence point, then my flag.  The
     // flags of the writers on one XCD (parts p with p % 8 == x) are packed
     // together: writer (s, p) owns word x*N*P8 + s*P8 + p/8, P8 = ceil(parts/8).
@@ -1107,21 +1116,23 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
         const uint32_t base = x * N * P8;
         Watch w;
         w.begin(a.watchdog_ticks);
-        uint32_t i = lane;                             // next writer this lane checks
-        while (true) {
-            // each lane walks its share of the writers, skipping those seen
-            while (i < total) {
-                const uint32_t s = i / per, jj = i % per;
-                const uint32_t v = ld4<Pol<LOCAL>::LD>(dn, (base + s * P8 + jj) * 4u);
-                if ((int32_t)(v - c.flag) < 0)
+        // each lane waits for its share of the writers in turn, two polls of
+        // the word in flight: while one value is checked the next is on its way
+        for (uint32_t i = lane; i < total; i += 64u) {
+            const uint32_t off = (base + (i / per) * P8 + i % per) * 4u;
+            uint32_t v0 = ld4<Pol<LOCAL>::LD>(dn, off), v1;
+            while (true) {
+                compiler_fence();
+                v1 = ld4<Pol<LOCAL>::LD>(dn, off);
+                if ((int32_t)(v0 - c.flag) >= 0)
                     break;
-                i += 64u;
+                if (w.expired(ctl, q, i / per, c.flag))
+                    return;
+                compiler_fence();
+                v0 = ld4<Pol<LOCAL>::LD>(dn, off);
+                if ((int32_t)(v1 - c.flag) >= 0)
+                    break;
             }
-            if (!wave_any(i < total))
-                break;
-            if (w.expired(ctl, q, i < total ? i / per : 0u, c.flag))
-                return;
-            compiler_fence();
         }
     }
     finish(a, c);
@@ -1208,29 +1219,17 @@ __global__ __launch_bounds__(256) void k_oneshot_barrier(const Launch a)
 {
     Ctx0 c;
     begin<LOCAL>(a, c);
-    const uint32_t N = a.n_ranks;
     const uint32_t G = a.n >> 3;
     const uint32_t step = a.parts * blockDim.x;
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     start_delay(a, c);
+    __amdgpu_buffer_rsrc_t src[NMAX];
+    input_rsrcs<NMAX>(a, src);
+    const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
     if (!grid_barrier(a, c, ctl, CTL_BAR_TOP))
         return;
-    const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
-    for (uint32_t ch = c.part * blockDim.x + threadIdx.x; ch < G; ch += step) {
-        u32x4 V[NMAX];
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N)
-                V[s] = ld16<CP_DEV>(in_rsrc(a, (uint32_t)s), ch * 16u);
-        Acc8 acc;
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N) {
-                if (s == 0) acc.init(V[s]); else acc.add(V[s]);
-            }
-        store8<F32>(o, ch * 8u, acc);
-    }
+    oneshot_data<NMAX, F32>(a, src, o, G, c.part * blockDim.x + threadIdx.x, step);
     if (!grid_barrier(a, c, ctl, CTL_BAR_BOTTOM))
         return;
     finish(a, c);
@@ -1243,7 +1242,6 @@ __global__ __launch_bounds__(256) void k_twoshot_barrier(const Launch a)
 {
     Ctx0 c;
     begin<LOCAL>(a, c);
-    const uint32_t N = a.n_ranks;
     const uint32_t q = c.rank;
     const uint32_t L = a.slice;
     const uint32_t lo = q * L;
@@ -1253,26 +1251,12 @@ __global__ __launch_bounds__(256) void k_twoshot_barrier(const Launch a)
     c.flag = load_seq(a) + a.epoch;
     const Ctl ctl{a.ctl};
     start_delay(a, c);
+    __amdgpu_buffer_rsrc_t src[NMAX];
+    input_rsrcs<NMAX>(a, src);
+    const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
     if (!grid_barrier(a, c, ctl, CTL_BAR_TOP))
         return;
-    const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
-    for (uint32_t ch = c.part * blockDim.x + threadIdx.x; ch < G; ch += step) {
-        u32x4 V[NMAX];
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N)
-                V[s] = ld16<CP_DEV>(in_rsrc(a, (uint32_t)s), (lo + ch * 8u) * 2u);
-        Acc8 acc;
-#pragma unroll
-        for (int s = 0; s < NMAX; ++s)
-            if ((uint32_t)s < N) {
-                if (s == 0) acc.init(V[s]); else acc.add(V[s]);
-            }
-#pragma unroll
-        for (int r = 0; r < NMAX; ++r)
-            if ((uint32_t)r < N)
-                store8<F32, CP_NT | CP_DEV>(oa, (uint32_t)r * a.n + lo + ch * 8u, acc);
-    }
+    twoshot_data<NMAX, F32>(a, src, oa, lo, G, c.part * blockDim.x + threadIdx.x, step);
     if (!grid_barrier(a, c, ctl, CTL_BAR_BOTTOM))
         return;
     finish(a, c);
