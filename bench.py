@@ -7,8 +7,11 @@ Headline (one JSON line on stdout):
            calls per emulated decode step captured in one hipGraph;
   plus   = effective HBM GB/s for 8 ranks x [256 x 8192] bf16 (4 MiB per
            rank), algorithmic bytes 2*N*S per call (each rank's input read
-           once, each rank's output copy written once), with the roofline of
-           that kernel against the 8 TB/s HBM3E peak.
+           once, each rank's output copy written once) over the average
+           period of 160 back-to-back calls captured in one hipGraph, with
+           the roofline of that kernel against the 8 TB/s HBM3E peak (the
+           same calls launched from the host loop and with an event pair
+           around each are reported under "results").
 A step is one replay of the 160-call graph (one emulated 80-layer decode
 step, two AllReduces per layer).  The other workloads (4 ranks x 4096,
 512 KiB/rank LL128, 16 ranks with start delays) are reported under
@@ -225,8 +228,10 @@ def bench_floor(torch, steps):
     return {"us_per_node_p50": pct(us, 50), "what": "160-node hipGraph of 1-element fill kernels"}
 
 
-def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact=True):
-    """Back-to-back stream calls over 8 rotating buffer sets, events per call."""
+def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact=True, graph_calls=160,
+                    graph_replays=3):
+    """Back-to-back stream calls over 8 rotating buffer sets, events per call;
+    then the same calls captured in one hipGraph and replayed back to back."""
     nsets = len(wl.ins)
     outs = [torch.empty((wl.N, wl.n), dtype=torch.int16, device="cuda:0") for _ in range(nsets)]
     ar.init(wl.N, wl.n)
@@ -262,6 +267,33 @@ def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact=True
     r1.record(stream)
     torch.cuda.synchronize()
     region_us = r0.elapsed_time(r1) * 1000.0 / calls
+    # graph pass: graph_calls calls (the 8 sets in rotation) and the step end
+    # in one hipGraph, replayed back to back with one event pair around the
+    # replays.  Dispatches follow each other without the host in the loop,
+    # as they do under a profiler's kernel trace, whose per-dispatch
+    # durations this period therefore matches.
+    graph = {}
+    if graph_calls > 0:
+        gs = torch.cuda.Stream()
+        ar.step_end(stream=stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(g, stream=gs):
+                for k in range(graph_calls):
+                    ar.allreduce(wl.ins[k % nsets], outs[k % nsets], wl.n, k + 1, stream=gs)
+                ar.step_end(stream=gs)
+            g.replay()
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record(gs)
+            for _ in range(graph_replays):
+                g.replay()
+            g1.record(gs)
+        torch.cuda.synchronize()
+        gus = g0.elapsed_time(g1) * 1000.0 / (graph_calls * graph_replays)
+        graph = {"graph_us_per_call": gus, "gbps_graph": wl.b_alg / (gus * 1e-6) / 1e9,
+                 "graph_calls": graph_calls, "graph_replays": graph_replays}
+        del g
     status = ar.get_status()
     worst = None
     if exact:
@@ -281,6 +313,7 @@ def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact=True
         "gbps_p50": wl.b_alg / (np.percentile(us, 50) * 1e-6) / 1e9,
         "gbps_mean": wl.b_alg / (us.mean() * 1e-6) / 1e9,
         "mismatches": bad, "status": list(status),
+        **graph,
     }
 
 
@@ -624,12 +657,17 @@ def main():
             r = bench_bandwidth(torch, ar, wl4, args.bw_calls, args.warmup, algo, proto, label)
             results[key] = r
             bws.append(r)
-            log("  %.1f GB/s back to back (%.2f us/call); per-call events p50 %.2f us"
-                % (r["gbps_region"], r["region_us_per_call"], r["us_per_call"]["p50"]))
+            log("  %.1f GB/s in a graph (%.2f us/call); %.1f GB/s stream back to back "
+                "(%.2f us/call); per-call events p50 %.2f us"
+                % (r["gbps_graph"], r["graph_us_per_call"], r["gbps_region"],
+                   r["region_us_per_call"], r["us_per_call"]["p50"]))
         bws = [r for r in bws if r is not results["bw_4m_twoshot_barrier"]]
         results["barrier_cost_4m_us"] = round(
             results["bw_4m_twoshot_barrier"]["us_per_call"]["p50"] -
             results["bw_4m_twoshot_direct"]["us_per_call"]["p50"], 4)
+        results["barrier_cost_4m_us_graph"] = round(
+            results["bw_4m_twoshot_barrier"]["graph_us_per_call"] -
+            results["bw_4m_twoshot_direct"]["graph_us_per_call"], 4)
         del wl4
     if only in ("all", "overlap"):
         log("overlap harness: projection GEMV and AllReduce")
@@ -647,7 +685,8 @@ def main():
             % (r["event_us_per_call"]["p50"], r["max_ulp_vs_fixed_order"]))
         wl4a = Workload(torch, 4, 8)
         r = bench_bandwidth(torch, ar, wl4a, max(args.bw_calls // 4, 10), args.warmup, TWO, ATOMIC,
-                            "atomic lines (arrival-order sums, not bit-exact)", exact=False)
+                            "atomic lines (arrival-order sums, not bit-exact)", exact=False,
+                            graph_calls=0)
         results["bw_4m_atomic"] = r
         log("  4 MiB atomic %.1f GB/s (p50 %.2f us/call), max %.2f ulp"
             % (r["gbps_p50"], r["us_per_call"]["p50"], r["max_ulp_vs_fixed_order"]))
@@ -699,11 +738,14 @@ def main():
     if bws:
         # throughput of back-to-back calls: events around the whole timed
         # region (an event packet between calls would add its own gap)
-        best = max(bws, key=lambda r: r["gbps_region"])
-        avg_us = best["region_us_per_call"]
+        # (the graph pass: dispatches back to back without the host in the
+        # loop, the timing a profiler's kernel trace agrees with)
+        best = max(bws, key=lambda r: r.get("gbps_graph", r["gbps_region"]))
+        avg_us = best.get("graph_us_per_call", best["region_us_per_call"])
         achieved = best["b_alg_bytes"] / (avg_us * 1e-6) / 1e9
-        line["gbps_4mb"] = round(best["gbps_region"], 2)
-        line["gbps_4mb_frac_of_peak"] = round(best["gbps_region"] / HBM_PEAK_GBS, 4)
+        line["gbps_4mb"] = round(achieved, 2)
+        line["gbps_4mb_frac_of_peak"] = round(achieved / HBM_PEAK_GBS, 4)
+        line["gbps_4mb_stream_back_to_back"] = round(best["gbps_region"], 2)
         line["gbps_4mb_per_call_events_p50"] = round(best["gbps_p50"], 2)
         traffic = recorded_traffic("k_twoshot_direct") if best is results.get(
             "bw_4m_twoshot_direct") else None
@@ -711,6 +753,7 @@ def main():
                             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                             "traffic": traffic, "kernel": best["algo"],
                             "per_launch_bytes": best["b_alg_bytes"], "avg_launch_us": avg_us,
+                            "avg_launch_us_stream_back_to_back": best["region_us_per_call"],
                             "avg_launch_us_with_per_call_events": best["us_per_call"]["mean"]}
     if lat is not None and "floor" in results:
         # the latency kernel is bound by the launch floor plus its in-XCD

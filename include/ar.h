@@ -222,8 +222,9 @@ int ar_destroy(void);
  * AUTO picks by message size S = 2n bytes per rank, as measured on MI355X
  * (the pages' table of variants in section "统一原语与API设计" puts the
  * one-shot/two-shot crossover at 64 KB on NVLink; in-place one-shot reads
- * stay ahead much longer here): S <= 16 KiB -> one-shot LL; S < 1 MiB ->
- * one-shot DIRECT; otherwise two-shot DIRECT.  With a protocol fixed and
+ * stay ahead much longer here): S < 1 MiB -> one-shot DIRECT; otherwise
+ * two-shot DIRECT.  (The fused ar_allreduce_add_rmsnorm uses its LL form
+ * up to S = 16 KiB under AUTO.)  With a protocol fixed and
  * the algorithm AUTO, one-shot is used up to that protocol's crossover
  * (sentinel 64 KiB, LL128 128 KiB, DIRECT and barrier just below 1 MiB);
  * LL is always one-shot and the atomic lines always two-shot.

@@ -191,7 +191,7 @@ def test_xcd_local_scope_is_used():
 def test_auto_selection():
     """AUTO follows the crossovers measured on MI355X (include/ar.h)."""
     with ar_context(8, 1 << 20) as a:
-        for kib, algo, proto in ((4, ONE, LL), (16, ONE, LL), (32, ONE, DIRECT), (512, ONE, DIRECT),
+        for kib, algo, proto in ((4, ONE, DIRECT), (16, ONE, DIRECT), (32, ONE, DIRECT), (512, ONE, DIRECT),
                                  (1024 - 16, ONE, DIRECT), (1024, TWO, DIRECT)):
             n = kib * 512
             assert (a.query(2, n), a.query(3, n)) == (algo, proto), kib

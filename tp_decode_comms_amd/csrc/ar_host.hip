@@ -26,14 +26,16 @@ constexpr size_t MAX_ELEMS_LIMIT = size_t(1) << 28;
 constexpr uint32_t DEFAULT_WATCHDOG_US = 200000;
 // Automatic selection by per-rank message size S = 2n bytes, from a sweep
 // of every algorithm/protocol pair on MI355X (8 ranks, 4 KiB - 4 MiB, graphs
-// of calls).  The pages' table (one-shot below 64 KB, two-shot above) was
+// of 40 calls).  The pages' table (one-shot below 64 KB, two-shot above) was
 // drawn for NVLink; here the in-place one-shot stays ahead much longer:
-//   LL one-shot up to 16 KiB (ties with one-shot DIRECT there),
-//   one-shot DIRECT below 1 MiB (e.g. 256 KiB: 3.5 us vs 5.8 two-shot),
-//   two-shot DIRECT from 1 MiB (1 MiB: 7.3 vs 7.9; 4 MiB: 14.1 vs 18.7).
+//   one-shot DIRECT below 1 MiB (4 KiB: 2.47 us vs 2.70 one-shot LL;
+//   16 KiB: 2.54 vs 2.87; 256 KiB: 3.62 vs 5.42 two-shot DIRECT),
+//   two-shot DIRECT from 1 MiB (1 MiB: 5.98 vs 7.07; 4 MiB: 12.65 vs 24.78).
 // With a protocol fixed and the algorithm left to AUTO, the one-shot limit
 // is that protocol's own crossover.
-constexpr size_t AUTO_LL_MAX_BYTES = 16 * 1024;
+// The fused AllReduce + norm keeps its LL form up to 16 KiB (its in-place
+// form was not re-measured against it after the prologue changes).
+constexpr size_t AUTO_NORM_LL_MAX_BYTES = 16 * 1024;
 constexpr uint64_t ONESHOT_DIRECT_MAX_PARTS = 128;
 size_t oneshot_limit(int proto)
 {
@@ -238,8 +240,7 @@ int choose_kind(size_t n, int *kind)
             algo = bytes <= oneshot_limit(proto) ? AR_ALGO_ONESHOT : AR_ALGO_TWOSHOT;
     }
     if (proto == AR_PROTO_AUTO)
-        proto = algo == AR_ALGO_TWOSHOT ? AR_PROTO_DIRECT
-                : bytes <= AUTO_LL_MAX_BYTES ? AR_PROTO_LL : AR_PROTO_DIRECT;
+        proto = AR_PROTO_DIRECT;
     if (algo == AR_ALGO_ONESHOT) {
         switch (proto) {
         case AR_PROTO_LL: *kind = ar::K_ONESHOT_LL; return AR_OK;
@@ -566,12 +567,12 @@ int do_allreduce_norm(const void *const *rank_bufs, const void *const *residual,
     if (rc != AR_OK)
         return rc;
     // the fused epilogue rides on the one-shot LL or the in-place one-shot:
-    // LL for messages up to the automatic LL limit, DIRECT above (or as the
-    // protocol option fixes it); no other protocol has a fused form.  The
+    // LL for messages up to 16 KiB, DIRECT above (or as the protocol option
+    // fixes it); no other protocol has a fused form.  The
     // in-place form goes row-wise (a workgroup per rank and row) for 8 or
     // more rows of up to 8192 elements when they fit the device at once.
     Plan p;
-    if (g.proto == AR_PROTO_LL || (g.proto == AR_PROTO_AUTO && 2 * n <= AUTO_LL_MAX_BYTES))
+    if (g.proto == AR_PROTO_LL || (g.proto == AR_PROTO_AUTO && 2 * n <= AUTO_NORM_LL_MAX_BYTES))
         p.kind = ar::K_ONESHOT_LL_NORM;
     else if (g.proto == AR_PROTO_AUTO || g.proto == AR_PROTO_DIRECT)
         p.kind = ar::K_ONESHOT_DIRECT_NORM;
