@@ -649,6 +649,12 @@ int ar_init(int n_ranks, size_t max_elems)
     if (me * (size_t)n_ranks * 4 > REGION_LIMIT || ll_bytes() > REGION_LIMIT ||
         l128_bytes() > REGION_LIMIT || s2_bytes() > REGION_LIMIT || acc_bytes() > REGION_LIMIT)
         return AR_ERR_INVALID;
+    // the kernels skip a load or store by sending it to offset ar::OFF_NONE,
+    // which must lie past the end of every input and output descriptor (the
+    // largest is all N output copies in binary32); the LL region bound above
+    // already implies it
+    if (me * (size_t)n_ranks * 4 > (size_t)ar::OFF_NONE)
+        return AR_ERR_INVALID;
     int rc;
     if ((rc = alloc(&g.ll, ll_bytes())) != AR_OK ||
         (rc = alloc(&g.l128, l128_bytes())) != AR_OK ||
