@@ -54,11 +54,14 @@ __device__ __forceinline__ uint32_t linear_id(const Launch &a)
 
 // The flag-sequence base.  Only the step-end kernel and the host's re-arm
 // kernels write it, always in an earlier launch; the launch boundary makes
-// that write visible, so a plain load suffices (no launch writes it while
-// an AllReduce kernel runs).
+// that write visible, and no launch writes it while an AllReduce kernel
+// runs, so it is read as constant memory: a scalar load, served by the
+// scalar cache a CU's waves share (every wave of the launch reads this
+// word; 8 x 16 KiB LL: 2.63 -> 2.58 us per call against a vector load).
 __device__ __forceinline__ uint32_t load_seq(const Launch &a)
 {
-    return ld4<CP_PLAIN>(rsrc(a.ctl, CTL_WORDS * 4u), CTL_SEQ * 4u);
+    typedef const __attribute__((address_space(4))) uint32_t const_u32;
+    return *((const_u32 *)a.ctl + CTL_SEQ);
 }
 
 __device__ __forceinline__ void start_delay(const Launch &a, const Ctx0 &c)
