@@ -280,19 +280,20 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
     const bool mine = wave < N && wave != c.rank && active;
     bool pend = mine;
     const uint32_t src = lane_off + wave * 2u * rb;
-    u32x4 A0, A1;
-    u32x2 V = {0u, 0u};
     Watch w;
     w.begin(a.watchdog_ticks);
-    if (pend)
-        A0 = ld16<Pol<LOCAL>::LD>(llr, src);
+    // Poll loads are issued by every lane, those with nothing (left) to
+    // receive at OFF_NONE (zeros, no traffic): a load under a branch would
+    // make the compiler wait for both polls in flight instead of the older.
+    // A unit goes to the LDS tile as soon as it is seen valid, so nothing
+    // after the loop reads a poll register.
+    u32x4 A0 = ld16<Pol<LOCAL>::LD>(llr, pend ? src : OFF_NONE), A1;
     while (true) {
         compiler_fence();
-        if (pend)
-            A1 = ld16<Pol<LOCAL>::LD>(llr, src);
+        A1 = ld16<Pol<LOCAL>::LD>(llr, pend ? src : OFF_NONE);
         if (pend && ll_ready(A0, c.flag)) {
             pend = false;
-            V.x = A0.x; V.y = A0.z;
+            stage[wave][lane] = u32x2{A0.x, A0.z};
         }
         if (!wave_any(pend))
             break;
@@ -301,33 +302,40 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
             break;
         }
         compiler_fence();
-        if (pend)
-            A0 = ld16<Pol<LOCAL>::LD>(llr, src);
+        A0 = ld16<Pol<LOCAL>::LD>(llr, pend ? src : OFF_NONE);
         if (pend && ll_ready(A1, c.flag)) {
             pend = false;
-            V.x = A1.x; V.y = A1.z;
+            stage[wave][lane] = u32x2{A1.x, A1.z};
         }
         if (!wave_any(pend))
             break;
     }
-    if (mine)
-        stage[wave][lane] = V;
-    __syncthreads();
+    lds_barrier();
     if (*failed)
         return false;
-    // recvReduce: global rank order from the staged tile
+    // recvReduce: global rank order from the staged tile.  Every row of the
+    // tile is read (rows of absent ranks hold stale values and are not
+    // folded), so the reads go out together instead of one wait per rank.
     if (wave == 0u && active) {
+        u32x2 t[NMAX];
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            t[s] = stage[s][lane];
         Acc4 acc;
 #pragma unroll
         for (int s = 0; s < NMAX; ++s) {
             if ((uint32_t)s < N) {
-                const u32x2 v = stage[s][lane];
-                if (s == 0) acc.init(v.x, v.y); else acc.add(v.x, v.y);
+                if (s == 0) acc.init(t[s].x, t[s].y); else acc.add(t[s].x, t[s].y);
             }
         }
         epi(ch, acc.v);
     }
-    __syncthreads();                                // the tile is reused next round
+    // The poll still in flight when the receive loop ended is waited for
+    // only here, after the output is on its way: keeping both poll
+    // registers live until now stops the compiler from reusing one of them
+    // (and waiting for its load) before the tile is read.
+    asm volatile("" ::"v"(A0), "v"(A1));
+    lds_barrier();                                  // the tile is reused next round
     return true;
 }
 
@@ -338,6 +346,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll(const Launch a)
     __shared__ uint32_t failed;
     Ctx0 c;
     begin<LOCAL>(a, c);
+    asm volatile("" ::"s"(a.ll), "s"(a.ll_stride));  // mailboxes: with the first load round
     const uint32_t C = a.n >> 2;                    // 4-element chunks per rank
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t step = a.parts * 64u;

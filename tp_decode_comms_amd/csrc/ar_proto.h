@@ -171,6 +171,20 @@ __device__ __forceinline__ void wait_stores()
     compiler_fence();
 }
 
+// Workgroup barrier for exchanges through LDS only: waits for this wave's
+// LDS operations (lgkmcnt(0); vector memory counters untouched), then
+// s_barrier.  __syncthreads() also waits for every outstanding vector
+// memory operation, which after a poll loop means the poll still in flight
+// -- a round trip nobody needs when the barrier only orders the LDS tile.
+// The compiler fences keep the LDS accesses on their side of it.
+__device__ __forceinline__ void lds_barrier()
+{
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
+
 __device__ __forceinline__ uint64_t clock100() { return __builtin_amdgcn_s_memrealtime(); }
 
 // index of the XCD this wave runs on (hardware register XCC_ID, bits 3:0)
