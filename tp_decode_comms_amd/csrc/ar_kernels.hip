@@ -823,12 +823,17 @@ __device__ __forceinline__ bool sent_round(const Launch &a, const Ctx0 &c, const
     if (wave == 0u)
         stage[c.rank][lane] = x;
     wait_stores();                  // receive only after the pushes are acknowledged
-    u32x4 A0[PW], A1[PW], V[PW];
+    // Poll loads are issued by every lane, slots with nothing (left) to
+    // receive at OFF_NONE (zeros, no traffic), so the compiler keeps the two
+    // polls in flight; a slot goes to the LDS tile as soon as it is seen
+    // complete, so nothing after the loop reads a poll register.
+    u32x4 A0[PW], A1[PW];
     auto issue = [&](u32x4 *A) {
 #pragma unroll
         for (int j = 0; j < PW; ++j)
-            if ((pend >> j) & 1u)
-                A[j] = ld16<Pol<LOCAL>::LD>(box, slot(c.rank, wave + (uint32_t)(SENT_WAVES * j)));
+            A[j] = ld16<Pol<LOCAL>::LD>(box, ((pend >> j) & 1u)
+                                                 ? slot(c.rank, wave + (uint32_t)(SENT_WAVES * j))
+                                                 : OFF_NONE);
     };
     auto check = [&](const u32x4 *A) {
 #pragma unroll
@@ -836,7 +841,7 @@ __device__ __forceinline__ bool sent_round(const Launch &a, const Ctx0 &c, const
             if ((pend >> j) & 1u)
                 if (sent_ready(A[j])) {
                     pend &= ~(1u << j);
-                    V[j] = A[j];
+                    stage[wave + SENT_WAVES * j][lane] = A[j];
                 }
     };
     Watch w;
@@ -858,27 +863,34 @@ __device__ __forceinline__ bool sent_round(const Launch &a, const Ctx0 &c, const
         if (!wave_any(pend != 0u))
             break;
     }
-    // re-arm what was consumed (resetRange) and stage it
-#pragma unroll
-    for (int j = 0; j < PW; ++j)
-        if ((mine >> j) & 1u) {
-            const uint32_t s = wave + (uint32_t)(SENT_WAVES * j);
-            st16<Pol<LOCAL>::ST>(sentinel4(), box, slot(c.rank, s));
-            stage[s][lane] = V[j];
-        }
-    __syncthreads();
+    lds_barrier();                  // the tile only: the polls in flight are waited for below
     if (*failed)
         return false;
     if (wave == 0u && active) {
+        // every row of the tile at once (rows of absent ranks are not folded)
+        u32x4 t[NMAX];
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            t[s] = stage[s][lane];
         Acc8 acc;
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             if ((uint32_t)s < N) {
-                const u32x4 v = stage[s][lane];
-                if (s == 0) acc.init(v); else acc.add(v);
+                if (s == 0) acc.init(t[s]); else acc.add(t[s]);
             }
         store8<F32>(o, ch * 8u, acc);
     }
+    // re-arm what was consumed (resetRange), off the path to the output;
+    // the barrier below waits for these stores (and the polls still in
+    // flight, whose registers stay reserved until here) before the next
+    // round's pushes
+#pragma unroll
+    for (int j = 0; j < PW; ++j)
+        if ((mine >> j) & 1u)
+            st16<Pol<LOCAL>::ST>(sentinel4(), box, slot(c.rank, wave + (uint32_t)(SENT_WAVES * j)));
+#pragma unroll
+    for (int j = 0; j < PW; ++j)
+        asm volatile("" ::"v"(A0[j]), "v"(A1[j]));
     __syncthreads();                                // the tile is reused next round
     return true;
 }
@@ -1728,20 +1740,22 @@ __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const C
     receive(rsr);
 #pragma unroll
     for (int j = 0; j < PW; ++j)
-        if ((mine >> j) & 1u) {
-            st16<Pol<LOCAL>::ST>(sentinel4(), rsr, box(q, peer(j)));
+        if ((mine >> j) & 1u)
             stage[peer(j)][lane] = V[j];
-        }
-    __syncthreads();
+    lds_barrier();                  // the tile only (the re-arm follows the reduce)
     if (*failed)
         return false;
     if (wave == 0u && act) {
+        // every row of the tile at once (rows of absent ranks are not folded)
+        u32x4 t[NMAX];
+#pragma unroll
+        for (int s = 0; s < NMAX; ++s)
+            t[s] = stage[s][lane];
         Acc8 acc;
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             if ((uint32_t)s < N) {
-                const u32x4 v = stage[s][lane];
-                if (s == 0) acc.init(v); else acc.add(v);
+                if (s == 0) acc.init(t[s]); else acc.add(t[s]);
             }
         if constexpr (F32) {
             // debug path: the owner writes its slice's accumulators to every copy
@@ -1753,6 +1767,12 @@ __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const C
             st16<CP_PLAIN>(rv, oa, (q * a.n + q * L + e) * esz);
         }
     }
+    // re-arm the consumed reduce-scatter slots (resetRange); the round's
+    // closing barrier waits for these stores before the next round's pushes
+#pragma unroll
+    for (int j = 0; j < PW; ++j)
+        if ((mine >> j) & 1u)
+            st16<Pol<LOCAL>::ST>(sentinel4(), rsr, box(q, peer(j)));
     __syncthreads();
     if constexpr (F32)
         return true;
