@@ -1501,20 +1501,24 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
                 for (int j = 0; j < PW; ++j)
                     if ((pmask >> j) & 1u)
                         stage[wave + L128_WAVES * j][k][lane] = V[k][j];
-        __syncthreads();
+        lds_barrier();
         if (failed)
             return;
         if (pub && em < a.n) {
+            // every row of the tile at once (rows of absent ranks are not folded)
+            u32x4 t[NMAX];
+#pragma unroll
+            for (int s = 0; s < NMAX; ++s)
+                t[s] = stage[s][wave][lane];
             Acc8 acc;
 #pragma unroll
             for (int s = 0; s < NMAX; ++s)
                 if ((uint32_t)s < N) {
-                    const u32x4 v = stage[s][wave][lane];
-                    if (s == 0) acc.init(v); else acc.add(v);
+                    if (s == 0) acc.init(t[s]); else acc.add(t[s]);
                 }
             store_lane<F32>(o, em, ln.half, acc);
         }
-        __syncthreads();                            // the tile is reused next batch
+        lds_barrier();                              // the tile is reused next batch
     }
     finish(a, c);
 }
@@ -1544,6 +1548,8 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
     const L128Lane ln = l128_lane(lane);
     start_delay(a, c);
     raise_arrival<LOCAL>(a, c);
+    __amdgpu_buffer_rsrc_t src[NMAX];
+    input_rsrcs<NMAX>(a, src);
     if (!wait_arrivals<LOCAL>(a, c, ctl))
         return;
     auto slice_len = [&](uint32_t s) -> uint32_t {
@@ -1580,11 +1586,24 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
         if (pub) {
             u32x4 red = {0u, 0u, 0u, 0u};
             if (em < Lq) {
+                // one straight run of loads (absent ranks past the end); a
+                // half lane's 4 elements are the upper half of the 16 bytes
+                // that end with them (its element index is at least 56, so
+                // the load starts inside the buffer and ends where they end)
+                const uint32_t eo = (q * L + em - (ln.half ? 4u : 0u)) * 2u;
                 u32x4 V[NMAX];
 #pragma unroll
                 for (int s = 0; s < NMAX; ++s)
-                    if ((uint32_t)s < N)
-                        V[s] = ld_elems<CP_DEV>(in_rsrc(a, (uint32_t)s), q * L + em, ln.half);
+                    V[s] = ld16<CP_DEV>(src[s], (uint32_t)s < N ? eo : OFF_NONE);
+                if (ln.half) {
+#pragma unroll
+                    for (int s = 0; s < NMAX; ++s) {
+                        V[s].x = V[s].z;
+                        V[s].y = V[s].w;
+                        V[s].z = 0u;
+                        V[s].w = 0u;
+                    }
+                }
                 Acc8 acc;
 #pragma unroll
                 for (int s = 0; s < NMAX; ++s)
