@@ -28,9 +28,9 @@ constexpr uint32_t DEFAULT_WATCHDOG_US = 200000;
 // of every algorithm/protocol pair on MI355X (8 ranks, 4 KiB - 4 MiB, graphs
 // of 40 calls).  The pages' table (one-shot below 64 KB, two-shot above) was
 // drawn for NVLink; here the in-place one-shot stays ahead much longer:
-//   one-shot DIRECT below 1 MiB (4 KiB: 2.47 us vs 2.70 one-shot LL;
-//   16 KiB: 2.54 vs 2.87; 256 KiB: 3.62 vs 5.42 two-shot DIRECT),
-//   two-shot DIRECT from 1 MiB (1 MiB: 5.98 vs 7.07; 4 MiB: 12.65 vs 24.78).
+//   one-shot DIRECT below 1 MiB (4 KiB: 2.51 us vs 2.59 one-shot LL;
+//   16 KiB: 2.60 vs 2.72; 256 KiB: 3.63 vs 5.41 two-shot DIRECT),
+//   two-shot DIRECT from 1 MiB (1 MiB: 5.99 vs 7.18; 4 MiB: 12.99 vs 24.52).
 // With a protocol fixed and the algorithm left to AUTO, the one-shot limit
 // is that protocol's own crossover.
 // The fused AllReduce + norm keeps its LL form up to 16 KiB (its in-place

@@ -124,10 +124,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
                                              0x00020000);
 }
 
-// A byte offset past the end of every buffer the kernels address (the host
-// keeps each buffer below 2^31 bytes): a raw buffer load at it returns zeros
-// without a memory access, a store at it is dropped.  It lets a load that
-// must be skipped still be issued unconditionally.
+// A byte offset past the end of every input and output descriptor (ar_init
+// keeps them below 2^31 bytes): a raw buffer load at it returns zeros
+// without a memory access, a store at it is dropped.  It lets a load or
+// store that must be skipped still be issued unconditionally.  The poll
+// loops also send the loads of lanes with nothing left to receive there;
+// in a staging region of 2 GiB or more that offset can fall inside it,
+// which is harmless for a load whose value is discarded (no store ever uses
+// it on a staging descriptor).
 constexpr uint32_t OFF_NONE = 0x80000000u;
 
 template <int CP> __device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
