@@ -184,6 +184,18 @@ __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t o, uint32_t elem, 
     }
 }
 
+// 2 accumulated elements (in v[0..1]) -> out[rank][elem..elem+2)
+template <bool F32>
+__device__ __forceinline__ void store2(__amdgpu_buffer_rsrc_t o, uint32_t elem, const float *v)
+{
+    if constexpr (F32) {
+        u32x2 w; w.x = __float_as_uint(v[0]); w.y = __float_as_uint(v[1]);
+        st8<CP_PLAIN>(w, o, elem * 4u);
+    } else {
+        st4<CP_PLAIN>(pack_bf16(v[0], v[1]), o, elem * 2u);
+    }
+}
+
 // ============================================================ arrivals
 // Rank s announces "my input for this call is final" by storing the call's
 // flag f = seq + epoch into its arrival word, at its very start and with no
@@ -256,7 +268,7 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
 //
 // `epi(ch, v)` consumes the reduced chunk (4 binary32 sums in v) on wave 0;
 // all lanes of wave 0 call it together when the round's chunks are in range.
-template <int NMAX, bool LOCAL, typename Epi>
+template <int NMAX, bool LOCAL, bool SPLIT, typename Epi>
 __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
                                          __amdgpu_buffer_rsrc_t llr, uint32_t ch, uint32_t C,
                                          u32x2 x, u32x2 (*stage)[64], uint32_t *failed, Epi &&epi)
@@ -316,19 +328,36 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
     // recvReduce: global rank order from the staged tile.  Every row of the
     // tile is read (rows of absent ranks hold stale values and are not
     // folded), so the reads go out together instead of one wait per rank.
-    if (wave == 0u && active) {
+    // With SPLIT, two waves share the fold, each taking one 32-bit word (two
+    // elements) of every chunk: the fold is a chain of dependent additions
+    // on one wave, so halving it shortens the tail of the call.
+    const uint32_t nfold = SPLIT && (blockDim.x >> 6) >= 2u ? 2u : 1u;
+    if (wave < nfold && active) {
         u32x2 t[NMAX];
 #pragma unroll
         for (int s = 0; s < NMAX; ++s)
             t[s] = stage[s][lane];
-        Acc4 acc;
+        if (nfold == 2u) {
+            float v[2];
 #pragma unroll
-        for (int s = 0; s < NMAX; ++s) {
-            if ((uint32_t)s < N) {
-                if (s == 0) acc.init(t[s].x, t[s].y); else acc.add(t[s].x, t[s].y);
+            for (int s = 0; s < NMAX; ++s) {
+                if ((uint32_t)s < N) {
+                    const uint32_t w = wave == 0u ? t[s].x : t[s].y;
+                    if (s == 0) { v[0] = lo_f(w); v[1] = hi_f(w); }
+                    else { v[0] += lo_f(w); v[1] += hi_f(w); }
+                }
             }
+            epi(ch, wave, v, 2);
+        } else {
+            Acc4 acc;
+#pragma unroll
+            for (int s = 0; s < NMAX; ++s) {
+                if ((uint32_t)s < N) {
+                    if (s == 0) acc.init(t[s].x, t[s].y); else acc.add(t[s].x, t[s].y);
+                }
+            }
+            epi(ch, 0u, acc.v, 4);
         }
-        epi(ch, acc.v);
     }
     // The poll still in flight when the receive loop ended is waited for
     // only here, after the output is on its way: keeping both poll
@@ -370,15 +399,19 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll(const Launch a)
     start_delay(a, c);
     // round 0 is straight-line code: its poll loads are issued back to back
     // (inside a loop the compiler's counter bookkeeping would wait before each)
-    auto out4 = [&](uint32_t cch, const float *v) { store4<F32>(o, cch * 4u, v); };
-    if (!ll_round<NMAX, LOCAL>(a, c, ctl, llr, ch, C, x, stage, &failed, out4))
+    // the fold's output: all 4 elements of a chunk, or word `w` (2 elements)
+    auto out = [&](uint32_t cch, uint32_t w, const float *v, int cnt) {
+        if (cnt == 4) store4<F32>(o, cch * 4u, v);
+        else store2<F32>(o, cch * 4u + 2u * w, v);
+    };
+    if (!ll_round<NMAX, LOCAL, true>(a, c, ctl, llr, ch, C, x, stage, &failed, out))
         return;
     // later rounds while the workgroup has chunks left (the same rounds for
     // every peer of the part)
     for (uint32_t base = c.part * 64u + step; base < C; base += step) {
         ch += step;
         x = (wave == 0u && ch < C) ? ld8<CP_PLAIN>(inr, ch * 8u) : u32x2{0u, 0u};
-        if (!ll_round<NMAX, LOCAL>(a, c, ctl, llr, ch, C, x, stage, &failed, out4))
+        if (!ll_round<NMAX, LOCAL, true>(a, c, ctl, llr, ch, C, x, stage, &failed, out))
             return;
     }
     finish(a, c);
@@ -480,7 +513,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
     const __amdgpu_buffer_rsrc_t llr = rsrc(a.ll, a.n_ranks * 2u * a.ll_stride);
     start_delay(a, c);
     u32x2 hk = {0u, 0u};
-    auto epi = [&](uint32_t cch, const float *v) {
+    auto epi = [&](uint32_t cch, uint32_t, const float *v, int) {   // always 4 elements (no split)
         u32x2 aw;
         aw.x = pack_bf16(v[0], v[1]);
         aw.y = pack_bf16(v[2], v[3]);
@@ -493,7 +526,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
             st8<CP_DEV>(e, sr, (c.rank * L.stats_stride + (cch >> 6)) * 8u);
         }
     };
-    if (!ll_round<NMAX, LOCAL>(a, c, ctl, llr, ch, C, x, stage, &failed, epi))
+    if (!ll_round<NMAX, LOCAL, false>(a, c, ctl, llr, ch, C, x, stage, &failed, epi))
         return;
     const u32x2 h0 = hk;
     for (uint32_t it = 1; it < rounds; ++it) {
@@ -501,7 +534,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
         const bool ld = wave == 0u && ch < C;
         x = ld ? ld8<CP_PLAIN>(inr, ch * 8u) : u32x2{0u, 0u};
         rw = ld ? ld8<CP_PLAIN>(resr, ch * 8u) : u32x2{0u, 0u};
-        if (!ll_round<NMAX, LOCAL>(a, c, ctl, llr, ch, C, x, stage, &failed, epi))
+        if (!ll_round<NMAX, LOCAL, false>(a, c, ctl, llr, ch, C, x, stage, &failed, epi))
             return;
     }
     // normalise (wave 0; the other waves go straight to finish's barrier)
