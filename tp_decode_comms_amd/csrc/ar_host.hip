@@ -37,6 +37,10 @@ constexpr uint32_t DEFAULT_WATCHDOG_US = 200000;
 // form was not re-measured against it after the prologue changes).
 constexpr size_t AUTO_NORM_LL_MAX_BYTES = 16 * 1024;
 constexpr uint64_t ONESHOT_DIRECT_MAX_PARTS = 128;
+// Largest per-rank message (bytes) for which the in-place one-shot gives each
+// lane 4 elements instead of 8 (latency-bound sizes, where the fold's
+// instruction count per lane shows).
+constexpr size_t ONESHOT_UNIT4_MAX_BYTES = 64 * 1024;
 size_t oneshot_limit(int proto)
 {
     switch (proto) {
@@ -225,6 +229,7 @@ struct Plan {
     uint32_t threads;
     uint32_t slice;
     bool local;         // XCD-local coherence scope
+    bool unit4 = false; // in-place one-shot: 4-element lane units
 };
 
 int choose_kind(size_t n, int *kind)
@@ -320,6 +325,10 @@ int plan_geometry(size_t n, bool f32, Plan *p)
         units = n / ar::NORM_BLOCK_ELEMS; per_wg = p->threads / 64; break;
     case ar::K_TWOSHOT_ATOMIC:      // lines of 31 elements, two per wave
         units = (n + ar::ATOM_LINE_ELEMS - 1) / ar::ATOM_LINE_ELEMS; per_wg = p->threads / 32; break;
+    case ar::K_ONESHOT_DIRECT:      // the barrier-ful baseline shares its data phase
+    case ar::K_ONESHOT_BARRIER:
+        p->unit4 = 2 * n <= ONESHOT_UNIT4_MAX_BYTES;
+        units = p->unit4 ? n / 4 : n / 8; per_wg = p->threads; break;
     default:
         units = n / 8; per_wg = p->threads; break;
     }
@@ -475,6 +484,7 @@ void fill_launch(const void *const *rank_bufs, void *out, size_t n, uint32_t epo
     // workgroup layout: grid (8, N, parts / 8) when parts % 8 == 0 (blocks
     // of 8 parts x N ranks, so part p runs on XCD p % 8), else (1, N, parts)
     a.xshift = p.parts % ar::XCDS == 0 ? 3u : 0u;
+    a.unit4 = p.unit4 ? 1u : 0u;
     uint64_t ticks = (uint64_t)g.watchdog_us * 100u;   // 100 MHz clock
     a.watchdog_ticks = (uint32_t)std::min<uint64_t>(ticks, 0xFFFFFFFFu);
 }

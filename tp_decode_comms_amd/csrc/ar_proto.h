@@ -100,6 +100,7 @@ struct Launch {
     uint32_t xshift;              // log2 of parts per rank in a block (3, or 0): grid (2^xshift, N, parts >> xshift)
     uint32_t ts_slots;
     uint32_t delay_rows;
+    uint32_t unit4;               // in-place one-shot: lanes take 4 elements (8 bytes), not 8
 };
 
 // The one-shot LL AllReduce with the residual add and RMS norm fused behind
