@@ -67,6 +67,22 @@ def test_variant_matches_oracle(name, algo, proto, N, n, scope_name, scope):
         assert_bits_equal(host_bits(out), expect(datas[k % 3]), "%s call %d" % (name, k + 1))
 
 
+@pytest.mark.parametrize("name,algo,proto", [("oneshot-direct", ONE, DIRECT), ("oneshot-barrier", ONE, BARRIER)],
+                         ids=["oneshot-direct", "oneshot-barrier"])
+@pytest.mark.parametrize("N,n", [(8, 32768), (8, 32768 + 8), (3, 32768), (3, 32768 + 8), (16, 8), (5, 4096 + 8)])
+def test_oneshot_lane_unit_boundary(name, algo, proto, N, n):
+    """The in-place one-shot gives each lane 4 elements up to 64 KiB per rank
+    and 8 above: both sides of the switch, and the smallest call, bit-exact."""
+    log("lane units %s N=%d n=%d" % (name, N, n))
+    datas = [synth.random_bits(5000 + 10 * s + N, (N, n), finite_only=True, avoid=0xFFFF)
+             for s in range(3)]
+    with ar_context(N, n, algo, proto) as ar:
+        outs = _run_calls(ar, datas, n, 6)
+        check_status_clean()
+    for k, out in enumerate(outs):
+        assert_bits_equal(host_bits(out), expect(datas[k % 3]), "%s call %d" % (name, k + 1))
+
+
 @pytest.mark.parametrize("name,algo,proto", VARIANTS, ids=[v[0] for v in VARIANTS])
 def test_single_rank_identity(name, algo, proto):
     n = 2048 + 8
