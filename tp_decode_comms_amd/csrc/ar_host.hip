@@ -269,9 +269,10 @@ int choose_kind(size_t n, int *kind)
     return AR_ERR_INVALID;
 }
 
-// Launch geometry.  Work unit per kind: a lane chunk of 4 elements (LL), of
-// 8 elements (sentinel, DIRECT one-shot), two 8-element chunks (DIRECT
-// two-shot), or a wave-wide LL128 line group of 480 elements.  Small
+// Launch geometry.  Work unit per kind: a lane chunk of 4 elements (LL; the
+// DIRECT one-shot up to 64 KiB per rank), of 8 elements (sentinel; the
+// DIRECT one-shot above that), two 8-element chunks (DIRECT two-shot), or a
+// wave-wide LL128 line group of 480 elements.  Small
 // messages use one-wave workgroups spread over many CUs (each CU then polls
 // little); large ones use 4-wave workgroups.  The whole grid must be
 // resident at once.
