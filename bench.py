@@ -108,6 +108,27 @@ class Workload:
         return bad, worst
 
 
+def device_facts(torch, ar, props):
+    """What the device reports about itself, beside the datasheet peak the
+    roofline uses: the XCD round-robin check and the constant-clock rate
+    come from the library's own context (a small one, destroyed again)."""
+    ar.init(8, 8192)
+    try:
+        facts = {"name": props.name, "arch": props.gcnArchName,
+                 "compute_units": props.multi_processor_count,
+                 "compute_units_library": ar.query(11),
+                 "memory_bytes": props.total_memory,
+                 "l2_bytes_per_xcd": props.L2_cache_size,
+                 "wavefront": props.warp_size,
+                 "lds_bytes_per_workgroup": props.shared_memory_per_block,
+                 "constant_clock_khz": ar.query(10),
+                 "xcd_round_robin_verified": bool(ar.query(9)),
+                 "hbm_peak_gbps_datasheet": HBM_PEAK_GBS}
+    finally:
+        ar.destroy()
+    return facts
+
+
 def timestamp_stats(tsh, calls_per_replay):
     """Per-call interval and span from a [slots][64][2] timestamp table."""
     start_all = tsh[:, :, 0].min(axis=1)
@@ -614,6 +635,8 @@ def main():
         print(json.dumps({"calib": calib_copy(torch)}), flush=True)
         return
 
+    device = device_facts(torch, ar, props)
+    log("device facts: %s" % json.dumps(device))
     results = {}
     lat = None
     if only in ("all", "latency"):
@@ -768,6 +791,7 @@ def main():
                             for k, r in results.items() if isinstance(r, dict) and "status" in r)
     line["results"] = results
     line["host"] = platform.node()
+    line["device"] = device
     print(json.dumps(line), flush=True)
 
 

@@ -115,8 +115,12 @@ enum ar_proto {
  * Allocates every protocol's staging (per rank x 2 parities), the flag
  * sequence word and the status record; zeroes flag words and arms sentinel
  * buffers with 0xFFFF.  Synchronous.
- * Errors: AR_ERR_INVALID (bad sizes), AR_ERR_STATE (already initialised),
- * AR_ERR_OOM, AR_ERR_HIP.
+ * The kernels' timers (watchdog budgets, start delays, call timestamps)
+ * count the device's constant clock at 100 MHz, the rate MI355X reports as
+ * hipDeviceAttributeWallClockRate; a device reporting another rate is
+ * refused.
+ * Errors: AR_ERR_INVALID (bad sizes, or a constant clock other than
+ * 100 MHz), AR_ERR_STATE (already initialised), AR_ERR_OOM, AR_ERR_HIP.
  */
 int ar_init(int n_ranks, size_t max_elems);
 
@@ -326,7 +330,8 @@ int ar_last_hip_error(void);
  *   3 its protocol, 4 workgroups it would launch, 5 threads per workgroup,
  *   6 resident-workgroup capacity of the device for that kernel, 7 the host
  *   epoch counter, 8 1 if a call of n elements would use XCD-local scope
- *   (else 0), 9 1 if ar_init verified the round-robin XCD placement.
+ *   (else 0), 9 1 if ar_init verified the round-robin XCD placement,
+ *   10 the constant-clock rate in kHz, 11 the device's compute-unit count.
  * Returns the value, or a negative status.
  */
 long long ar_query(int key, size_t n);

@@ -204,6 +204,16 @@ def test_xcd_local_scope_is_used():
         assert a.query(8, 8192) == 0
 
 
+def test_device_clock_and_units():
+    """ar_init accepted the device only because its constant clock runs at
+    the 100 MHz the kernels' timers count; the compute-unit count it plans
+    grids with is the device's."""
+    torch = torch_mod()
+    with ar_context(2, 1024) as a:
+        assert a.query(10, 0) == 100000
+        assert a.query(11, 0) == torch.cuda.get_device_properties(0).multi_processor_count
+
+
 def test_auto_selection():
     """AUTO follows the crossovers measured on MI355X (include/ar.h)."""
     with ar_context(8, 1 << 20) as a:

@@ -41,6 +41,8 @@ constexpr uint64_t ONESHOT_DIRECT_MAX_PARTS = 128;
 // lane 4 elements instead of 8 (latency-bound sizes, where the fold's
 // instruction count per lane shows).
 constexpr size_t ONESHOT_UNIT4_MAX_BYTES = 64 * 1024;
+// rate of the constant clock the kernels' timers count (100 MHz)
+constexpr int WALL_CLOCK_KHZ = 100000;
 size_t oneshot_limit(int proto)
 {
     switch (proto) {
@@ -56,6 +58,7 @@ struct Context {
     int n_ranks = 0;
     size_t max_elems = 0;
     int cu_count = 0;
+    int wall_khz = 0;   // constant-clock rate (hipDeviceAttributeWallClockRate)
     // staging
     char *ll = nullptr;   size_t ll_stride = 0;
     char *l128 = nullptr; size_t l128_stride = 0;
@@ -645,6 +648,14 @@ int ar_init(int n_ranks, size_t max_elems)
     e = hipDeviceGetAttribute(&g.cu_count, hipDeviceAttributeMultiprocessorCount, g.device);
     if (e != hipSuccess)
         return hip_fail(e);
+    // the kernels' timers (watchdog budgets, start delays, call timestamps)
+    // count the constant clock at 100 ticks per microsecond, the rate
+    // MI355X reports; a device whose clock runs otherwise is refused
+    e = hipDeviceGetAttribute(&g.wall_khz, hipDeviceAttributeWallClockRate, g.device);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    if (g.wall_khz != WALL_CLOCK_KHZ)
+        return AR_ERR_INVALID;
     g.n_ranks = n_ranks;
     g.max_elems = round_up(max_elems, 8);
     const size_t me = g.max_elems;
@@ -934,6 +945,8 @@ long long ar_query(int key, size_t n)
         return rc != AR_OK ? rc : (p.local ? 1 : 0);
     }
     case 9: return g.placement_ok ? 1 : 0;
+    case 10: return g.wall_khz;
+    case 11: return g.cu_count;
     default: return AR_ERR_INVALID;
     }
 }
