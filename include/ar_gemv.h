@@ -10,8 +10,9 @@
  *
  *   y_r[m] = bf16_rne( sum over k of W_r[m][k] * x_r[k] )   r = 0..n_ranks-1
  *
- * accumulated in binary32 (each wave owns one row: a lane sums its 8-element
- * chunks in order, then the 64 lanes combine in a fixed butterfly), so the
+ * accumulated in binary32 (each wave owns four consecutive rows; per row a
+ * lane sums its 8-element chunks in order, then the 64 lanes combine in a
+ * fixed butterfly), so the
  * result is deterministic but, unlike the AllReduce, not bit-identical to a
  * sequential sum; the tests hold it to the binary32 error bound of that
  * summation order.  It is not part of the AllReduce path; the overlap
@@ -38,7 +39,8 @@ extern "C" {
  *   x:  host array of n_ranks device pointers to bf16 [K], 16-byte aligned;
  *   y:  host array of n_ranks device pointers to bf16 [M] (outputs; must
  *       not overlap W or x), 2-byte aligned;
- *   M >= 1 rows; K >= 8 with K % 8 == 0 and M*K*2 < 2^32; 1 <= n_ranks <= 16;
+ *   M >= 1 rows; K >= 8 with K % 8 == 0, K <= 2^28 and M*K*2 < 2^32;
+ *   1 <= n_ranks <= 16;
  *   max_workgroups: cap on the grid (256-thread workgroups, 4 rows each,
  *       rows beyond the grid are processed grid-stride); 0 = automatic
  *       (up to 8192).  A cap leaves CUs free for a concurrent AllReduce.

@@ -86,3 +86,4 @@ def test_gemv_validation_without_device(lib):
     assert lib.ar_gemv_bf16(P(8), good, P(4096), 8, 8, 1, 0, None) == a.AR_ERR_INVALID  # unaligned W
     assert lib.ar_gemv_bf16(good, good, P(16), 8, 8, 1, 0, None) == a.AR_ERR_INVALID  # y aliases W
     assert lib.ar_gemv_bf16(good, good, P(4096), 8, 8, 1, -1, None) == a.AR_ERR_INVALID
+    assert lib.ar_gemv_bf16(good, good, P(1 << 33), 1, (1 << 28) + 8, 1, 0, None) == a.AR_ERR_INVALID  # K
