@@ -564,23 +564,43 @@ def calib_copy(torch, reps=20):
     return {"bytes_read": 32 << 20, "bytes_written": 32 << 20, "reps": reps}
 
 
+def _time_calls(fn, budget_s, min_reps, max_reps=None):
+    """Per-call wall times (s) of fn() for about budget_s seconds."""
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while len(times) < min_reps or (time.perf_counter() < t_end and
+                                    (max_reps is None or len(times) < max_reps)):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return np.asarray(times)
+
+
 def cpu_baseline(budget_s=12.0):
-    """The oracle as it stands, on this host's cores: 16 KiB/rank calls."""
+    """The oracle as it stands, on this host's cores: the 16 KiB/rank calls
+    (the headline workload, about budget_s seconds), and the 4 MiB/rank call
+    (20 calls per thread setting) in GB/s on the same algorithmic bytes as
+    the GPU figure.  Medians of per-call times."""
     import oracle
     import synth
     data = list(synth.input_set(2, 0))
     res = {}
     threads_all = oracle.max_threads()
     for label, th in (("1thread", 1), ("all", threads_all)):
-        reps = 0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s / 2:
-            oracle.allreduce(data, threads=th)
-            reps += 1
-        dt = time.perf_counter() - t0
-        res[label] = {"us_per_call": dt / reps * 1e6, "reps": reps, "threads": th}
+        t = _time_calls(lambda: oracle.allreduce(data, threads=th), budget_s / 2, 1000)
+        res[label] = {"us_per_call": float(np.median(t)) * 1e6, "mean_us": float(t.mean()) * 1e6,
+                      "reps": int(t.size), "threads": th}
     best = min(res.values(), key=lambda r: r["us_per_call"])
-    cpu_model = ""
+    big = list(synth.input_set(4, 0))
+    b_alg = 2 * len(big) * big[0].size * 2
+    res4 = {}
+    for label, th in (("1thread", 1), ("all", threads_all)):
+        t = _time_calls(lambda: oracle.allreduce(big, threads=th), 0.0, 20)
+        med = float(np.median(t))
+        res4[label] = {"us_per_call": med * 1e6, "gbps": b_alg / med / 1e9, "reps": int(t.size),
+                       "threads": th}
+    del big
+    cpu_model, governor = "", ""
     try:
         out = subprocess.run(["lscpu"], stdout=subprocess.PIPE, text=True).stdout
         for line in out.splitlines():
@@ -588,14 +608,24 @@ def cpu_baseline(budget_s=12.0):
                 cpu_model = line.split(":", 1)[1].strip()
     except Exception:
         pass
+    try:
+        with open("/sys/devices/system/cpu/cpu0/cpufreq/scaling_governor") as f:
+            governor = f.read().strip()
+    except OSError:
+        governor = "unavailable"
     return {
         "value": best["us_per_call"], "unit": "us/call", "cores": best["threads"],
         "kind": "oracle",
         "sample": "8 ranks x 8192 bf16 (the 16 KiB/rank workload), C oracle producing all "
-                  "8 output copies, repeated for ~%.0f s per thread setting" % (budget_s / 2),
+                  "8 output copies, ~%.0f s per thread setting (median of per-call times)"
+                  % (budget_s / 2),
         "one_thread_us_per_call": res["1thread"]["us_per_call"],
         "all_threads_us_per_call": res["all"]["us_per_call"],
-        "host_threads": threads_all, "cpu_model": cpu_model, "nproc": os.cpu_count(),
+        "reps": {k: v["reps"] for k, v in res.items()},
+        "oracle_4mib": {"workload": "8 ranks x [256x8192] bf16 (4 MiB/rank), U(-1,1), 20 calls",
+                        "b_alg_bytes": b_alg, "one_thread": res4["1thread"], "all_threads": res4["all"]},
+        "host_threads": threads_all, "cpu_model": cpu_model, "governor": governor,
+        "nproc": os.cpu_count(),
     }
 
 
