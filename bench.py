@@ -724,7 +724,7 @@ def main():
         del wl4
     if only in ("all", "overlap"):
         log("overlap harness: projection GEMV and AllReduce")
-        results["overlap"] = bench_overlap(torch, ar, replays=3 if args.quick else 10)
+        results["overlap"] = bench_overlap(torch, ar, replays=10 if args.quick else 50)
         log("  %r" % {k: v for k, v in results["overlap"].items() if k != "workload"})
     if only in ("all", "atomic"):
         log("atomic lines (arrival-order sums): 16 KiB/rank graph and 4 MiB/rank stream")
