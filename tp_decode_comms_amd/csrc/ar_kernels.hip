@@ -1753,12 +1753,16 @@ __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const C
     // ---- push my parts of this wave's slices
     u32x4 X[PW];
     uint32_t push = 0;
+    // loads of this wave's parts, and below the polls, are issued by every
+    // lane (nothing to move: at OFF_NONE), so they go out in one run instead
+    // of each waiting behind a branch (16 ranks x 57344: 6.11 -> 5.68 us)
 #pragma unroll
-    for (int j = 0; j < PW; ++j)
-        if (peer(j) < N && peer(j) != q && e < slice_len(peer(j))) {
-            X[j] = ld16<CP_PLAIN>(inq, (peer(j) * L + e) * 2u);
+    for (int j = 0; j < PW; ++j) {
+        const bool pj = peer(j) < N && peer(j) != q && e < slice_len(peer(j));
+        X[j] = ld16<CP_PLAIN>(inq, pj ? (peer(j) * L + e) * 2u : OFF_NONE);
+        if (pj)
             push |= 1u << j;
-        }
+    }
     if (wave == 0u && act)
         stage[q][lane] = ld16<CP_PLAIN>(inq, (q * L + e) * 2u);
 #pragma unroll
@@ -1771,8 +1775,7 @@ __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const C
     auto issue = [&](u32x4 *A, __amdgpu_buffer_rsrc_t reg) {
 #pragma unroll
         for (int j = 0; j < PW; ++j)
-            if ((pend >> j) & 1u)
-                A[j] = ld16<Pol<LOCAL>::LD>(reg, box(q, peer(j)));
+            A[j] = ld16<Pol<LOCAL>::LD>(reg, ((pend >> j) & 1u) ? box(q, peer(j)) : OFF_NONE);
     };
     auto check = [&](const u32x4 *A) {
 #pragma unroll
