@@ -18,10 +18,17 @@ step, two AllReduces per layer).  The other workloads (4 ranks x 4096,
 "results".
 
 Timing: HIP events on the stream the graph or kernel runs on; an
-instrumented pass additionally records, per call, the earliest workgroup
-start and latest workgroup end on the 100 MHz constant clock, giving
-per-call intervals end(k) - end(k-1) (launch gap included) and spans
-end(k) - start(k).
+instrumented pass additionally has every wave write its own record {start,
+first synchronisation satisfied, last data store issued, end} on the 100 MHz
+constant clock (plain stores, no atomics or waits), giving per-call
+intervals end(k) - end(k-1) (launch gap included), spans end(k) - start(k)
+and the call's phases.  The headline value is the per-call interval p50
+when the instrumented mean agrees with the uninstrumented event mean within
+5%, else the event figure (the JSON line says which).
+
+Every leg runs under its own guard: a leg that fails records its error under
+"results" and the JSON line is still printed (parity_ok false); after a
+device-side failure no further GPU leg runs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
                        [--only latency|bw|overlap|configs|calib]
@@ -129,22 +136,100 @@ def device_facts(torch, ar, props):
     return facts
 
 
+class Epochs:
+    """Epoch bookkeeping of a stream of calls: epochs 1, 2, ... within a step,
+    a step closed after CALLS_PER_STEP calls (as a decode step would) or on
+    demand.  The library requires epoch = previous + 1 (at most 65535) after
+    ar_init / ar_step_end; this keeps to that for any number of calls."""
+
+    def __init__(self, ar, per_step=CALLS_PER_STEP):
+        self.ar, self.per_step, self.epoch = ar, per_step, 0
+
+    def next(self, stream=None):
+        if self.epoch == self.per_step:
+            self.close(stream)
+        self.epoch += 1
+        return self.epoch
+
+    def close(self, stream=None):
+        if self.epoch:
+            self.ar.step_end(stream=stream)
+        self.epoch = 0
+
+
+US_PER_TICK = 1e6 / CLOCK_HZ
+
+
 def timestamp_stats(tsh, calls_per_replay):
-    """Per-call interval and span from a [slots][64][2] timestamp table."""
-    start_all = tsh[:, :, 0].min(axis=1)
-    end_all = tsh[:, :, 1].max(axis=1)
-    filled = np.nonzero(end_all != 0)[0]
-    starts = start_all[filled].astype(np.float64)
-    ends = end_all[filled].astype(np.float64)
-    order = np.argsort(ends)
-    ends, starts = ends[order], starts[order]
-    intervals = np.diff(ends) / CLOCK_HZ * 1e6
+    """Per-call figures from a [slots][records][4] table of per-wave records
+    {start, sync, data, end} (ticks; records never written stay 0): the
+    interval end(k) - end(k-1) between back-to-back calls of a replay, the
+    span end - start, the launch gap start(k) - end(k-1), and the call's
+    phases relative to its start: when its last wave passed its first
+    synchronisation, issued its last data store, and ended."""
+    t = tsh.astype(np.float64)
+    live = tsh[:, :, 3] != 0
+    keep_slot = live.any(axis=1)
+    t, live = t[keep_slot], live[keep_slot]
+    big = np.where(live, t[:, :, 0], np.inf)
+    start = big.min(axis=1)
+    end = np.where(live, t[:, :, 3], -np.inf).max(axis=1)
+    order = np.argsort(end)
+    t, live, start, end = t[order], live[order], start[order], end[order]
+
+    def last(field):
+        v = np.where(live & (t[:, :, field] != 0), t[:, :, field], -np.inf).max(axis=1)
+        return (v - start) * US_PER_TICK
+
     # drop the gaps across replay boundaries (step-end node and host launch)
-    keep = np.ones_like(intervals, dtype=bool)
-    keep[calls_per_replay - 1::calls_per_replay] = False
-    intervals = intervals[keep[:intervals.size]]
-    spans = (ends - starts) / CLOCK_HZ * 1e6
-    return intervals, spans
+    within = np.ones(end.size - 1, dtype=bool)
+    within[calls_per_replay - 1::calls_per_replay] = False
+    intervals = np.diff(end)[within] * US_PER_TICK
+    gaps = (start[1:] - end[:-1])[within] * US_PER_TICK
+    spans = (end - start) * US_PER_TICK
+    starts = np.where(live, t[:, :, 0], np.nan)
+    waits = np.where(live & (t[:, :, 1] != 0), t[:, :, 1] - t[:, :, 0], np.nan)
+    with np.errstate(all="ignore"):
+        phases = {"last_start_us": (np.nanmax(starts, axis=1) - start) * US_PER_TICK,
+                  "median_start_us": (np.nanmedian(starts, axis=1) - start) * US_PER_TICK,
+                  "median_wave_sync_wait_us": np.nanmedian(waits, axis=1) * US_PER_TICK,
+                  "last_sync_us": last(1), "last_data_us": last(2), "end_us": spans}
+    return intervals, spans, gaps, phases
+
+
+def instrumented_replays(torch, ar, capture, stream, n, calls, replays, phases=False):
+    """Replays a graph captured with the timestamp table on: one untimed
+    replay, then `replays` timed ones.  Returns the per-call statistics and
+    the event time of the same replays (to compare with the uninstrumented
+    figure).  With `phases` the kernels also mark their synchronisation and
+    data phases (two more clock reads per wave, which lengthen the call)."""
+    records = ar.query(4, n) * ar.query(5, n) // 64          # waves per call
+    slots = calls * (replays + 1)
+    ts = torch.zeros((slots, records, 4), dtype=torch.int64, device="cuda:0")
+    ar.set_timestamps(ts, slots, records, phases)
+    try:
+        gi = capture()
+    finally:
+        ar.set_timestamps(None, 0, 0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        gi.replay()
+        ts.zero_()
+        e0.record(stream)
+        for _ in range(replays):
+            gi.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    del gi
+    intervals, spans, gaps, ph = timestamp_stats(ts.cpu().numpy().view(np.uint64), calls)
+    del ts
+    out = {"interval_us": summary(intervals), "span_us": summary(spans),
+           "launch_gap_us": summary(gaps),
+           "event_us_per_call_instrumented": e0.elapsed_time(e1) * 1000.0 / (calls * replays),
+           "records_per_call": records, "replays": replays, "phase_marks": bool(phases)}
+    keys = ph if phases else ("last_start_us", "median_start_us", "end_us")
+    out["phases_p50_us"] = {k: pct(ph[k], 50) for k in keys}
+    return out
 
 
 def graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays=None,
@@ -154,6 +239,15 @@ def graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays=None,
     Returns event timings per replay, instrumented per-call intervals/spans,
     and a bit-exact check of the last replay's outputs."""
     ar.init(wl.N, wl.n)
+    try:
+        return _graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays,
+                          instrumented, exact)
+    finally:
+        torch.cuda.synchronize()
+        ar.destroy()
+
+
+def _graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays, instrumented, exact):
     ar.set_options(algo, proto)
     if delays is not None:
         ar.set_delays(delays, delays.shape[0])
@@ -196,31 +290,21 @@ def graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays=None,
     res = {"event_us_per_call": summary(per_replay_ms * 1000.0 / calls),
            "event_ms_per_replay": summary(per_replay_ms),
            "mismatches": bad, "status": list(status),
+           "rounds_per_call": ar.query(12, wl.n),
            "xcd_local_scope": bool(ar.query(8, wl.n)),
            "placement_verified": bool(ar.query(9, 0))}
     if worst is not None:
         res["max_ulp_vs_fixed_order"] = round(worst, 3)
     del g
     if instrumented:
-        slots = calls * replays
-        ts = torch.empty((slots, 64, 2), dtype=torch.int64, device="cuda:0")
-        ar.set_timestamps(ts, slots)
-        gi = capture()
-        ar.set_timestamps(None, 0)
-        with torch.cuda.stream(stream):
-            gi.replay()
-            ts[:, :, 0] = -1              # UINT64_MAX
-            ts[:, :, 1] = 0
-            for r in range(replays):
-                gi.replay()
-        torch.cuda.synchronize()
-        intervals, spans = timestamp_stats(ts.cpu().numpy().view(np.uint64), calls)
-        res["instrumented"] = {"interval_us": summary(intervals), "span_us": summary(spans)}
+        res["instrumented"] = instrumented_replays(torch, ar, capture, stream, wl.n, calls,
+                                                   min(replays, 10))
         res["status_instrumented"] = list(ar.get_status())
-        del gi
+        ev_mean = res["event_us_per_call"]["mean"]
+        res["instrumented"]["agreement"] = round(
+            res["instrumented"]["interval_us"]["mean"] / ev_mean - 1.0, 4)
     if delays is not None:
         ar.set_delays(None, 0)
-    ar.destroy()
     return res
 
 
@@ -250,22 +334,32 @@ def bench_floor(torch, steps):
 
 
 def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact=True, graph_calls=160,
-                    graph_replays=3):
+                    graph_replays=3, instrumented=False):
     """Back-to-back stream calls over 8 rotating buffer sets, events per call;
-    then the same calls captured in one hipGraph and replayed back to back."""
+    then the same calls captured in one hipGraph and replayed back to back
+    (optionally once more with the per-wave timestamp table: the call's
+    phases)."""
+    ar.init(wl.N, wl.n)
+    try:
+        return _bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact,
+                                graph_calls, graph_replays, instrumented)
+    finally:
+        torch.cuda.synchronize()
+        ar.destroy()
+
+
+def _bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact, graph_calls,
+                     graph_replays, instrumented):
     nsets = len(wl.ins)
     outs = [torch.empty((wl.N, wl.n), dtype=torch.int16, device="cuda:0") for _ in range(nsets)]
-    ar.init(wl.N, wl.n)
     ar.set_options(algo, proto)
     grid, threads = ar.query(4, wl.n), ar.query(5, wl.n)
     local = bool(ar.query(8, wl.n))
     stream = torch.cuda.current_stream()
-    epoch = 0
+    ep = Epochs(ar)
 
     def call(k):
-        nonlocal epoch
-        epoch += 1
-        ar.allreduce(wl.ins[k % nsets], outs[k % nsets], wl.n, epoch)
+        ar.allreduce(wl.ins[k % nsets], outs[k % nsets], wl.n, ep.next())
 
     for k in range(warmup):
         call(k)
@@ -288,6 +382,7 @@ def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact=True
     r1.record(stream)
     torch.cuda.synchronize()
     region_us = r0.elapsed_time(r1) * 1000.0 / calls
+    ep.close(stream)
     # graph pass: graph_calls calls (the 8 sets in rotation) and the step end
     # in one hipGraph, replayed back to back with one event pair around the
     # replays.  Dispatches follow each other without the host in the loop,
@@ -296,14 +391,19 @@ def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact=True
     graph = {}
     if graph_calls > 0:
         gs = torch.cuda.Stream()
-        ar.step_end(stream=stream)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
+
+        def capture():
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(gs):
+                with torch.cuda.graph(g, stream=gs):
+                    for k in range(graph_calls):
+                        ar.allreduce(wl.ins[k % nsets], outs[k % nsets], wl.n, k + 1, stream=gs)
+                    ar.step_end(stream=gs)
+            return g
+
+        g = capture()
         with torch.cuda.stream(gs):
-            with torch.cuda.graph(g, stream=gs):
-                for k in range(graph_calls):
-                    ar.allreduce(wl.ins[k % nsets], outs[k % nsets], wl.n, k + 1, stream=gs)
-                ar.step_end(stream=gs)
             g.replay()
             g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             g0.record(gs)
@@ -315,18 +415,21 @@ def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact=True
         graph = {"graph_us_per_call": gus, "gbps_graph": wl.b_alg / (gus * 1e-6) / 1e9,
                  "graph_calls": graph_calls, "graph_replays": graph_replays}
         del g
+        if instrumented:
+            graph["instrumented"] = instrumented_replays(torch, ar, capture, gs, wl.n, graph_calls,
+                                                         graph_replays, phases=True)
     status = ar.get_status()
     worst = None
     if exact:
         bad = wl.check([(outs[s], s) for s in range(nsets)])
     else:
         bad, worst = wl.check_bound([(outs[s], s) for s in range(nsets)])
-    ar.destroy()
     extra = {} if worst is None else {"max_ulp_vs_fixed_order": round(worst, 3)}
     return {**extra,
         "workload": "8 ranks x [256x8192] bf16 (4 MiB/rank), U(-1,1), %s, 8 rotating buffer "
                     "sets (footprint %d MiB)" % (label, (2 * nsets * wl.N * 2 * wl.n) >> 20),
         "algo": label, "grid": grid, "threads": threads, "xcd_local_scope": local,
+        "rounds_per_call": ar.query(12, wl.n),
         "us_per_call": summary(us),
         "region_us_per_call": region_us,
         "gbps_region": wl.b_alg / (region_us * 1e-6) / 1e9,
@@ -355,6 +458,15 @@ def bench_overlap(torch, ar, layers=20, replays=10, warmup=2):
     outs = [torch.empty((N, M), dtype=torch.int16, device="cuda:0") for _ in range(layers)]
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     ar.init(N, M)
+    try:
+        return _bench_overlap(torch, ar, layers, replays, warmup, N, M, K, Wd, xd, yd, wl, outs,
+                              s1, s2)
+    finally:
+        torch.cuda.synchronize()
+        ar.destroy()
+
+
+def _bench_overlap(torch, ar, layers, replays, warmup, N, M, K, Wd, xd, yd, wl, outs, s1, s2):
     ar.set_options(ONE, LL)
 
     def timed(build):
@@ -413,7 +525,6 @@ def bench_overlap(torch, ar, layers=20, replays=10, warmup=2):
     t_both_b = timed(lambda: concurrent(budget))
     bad = wl.check([(outs[k], k % len(wl.ins)) for k in range(layers)])
     status = ar.get_status()
-    ar.destroy()
     gemv_bytes = N * M * K * 2
     return {
         "workload": "decode projection 8 ranks x bf16 [8192 x 1024] (16 MiB of weights per rank) "
@@ -454,6 +565,17 @@ def bench_norm(torch, ar, cid=2, replays=20, warmup=3, layers=80):
     outs, hs, ys, uh, uy = mk(), mk(), mk(), mk(), mk()
     stream = torch.cuda.Stream()
     ar.init(N, n)
+    try:
+        return _bench_norm(torch, ar, cid, replays, warmup, N, n, rows, hidden, calls, wl, res,
+                           gamma, rs, g, eps, outs, hs, ys, uh, uy, stream)
+    finally:
+        torch.cuda.synchronize()
+        ar.destroy()
+
+
+def _bench_norm(torch, ar, cid, replays, warmup, N, n, rows, hidden, calls, wl, res, gamma, rs, g,
+                eps, outs, hs, ys, uh, uy, stream):
+    import oracle
     if cid == 2:
         ar.set_options(ONE, LL)
 
@@ -496,7 +618,6 @@ def bench_norm(torch, ar, cid=2, replays=20, warmup=3, layers=80):
     t_fused = timed(fused)
     t_unfused = timed(unfused)
     status = ar.get_status()
-    ar.destroy()
     bad = 0
     worst_ulp = 0.0
     for s in range(4):
@@ -629,6 +750,68 @@ def cpu_baseline(budget_s=12.0):
     }
 
 
+def _is_device_failure(exc):
+    """True for failures after which the GPU should not be used again in this
+    process: HIP runtime errors (as raised by torch or reported by the library)."""
+    import tp_decode_comms_amd as ar
+    if isinstance(exc, ar.ArError):
+        return exc.code == ar.ar.AR_ERR_HIP
+    text = str(exc)
+    return "HIP error" in text or "hipError" in text or "CUDA error" in text
+
+
+class Legs:
+    """Runs the bench legs one by one; a failing leg records its error and the
+    rest continue (none after a device-side failure)."""
+
+    def __init__(self):
+        self.results = {}
+        self.stopped = False
+
+    def run(self, key, fn):
+        if self.stopped:
+            self.results[key] = {"skipped": "an earlier leg failed on the device"}
+            return None
+        try:
+            r = fn()
+        except Exception as exc:            # recorded, the line is still printed
+            msg = "%s: %s" % (type(exc).__name__, exc)
+            log("leg %s failed: %s" % (key, msg))
+            self.results[key] = {"error": msg}
+            if _is_device_failure(exc):
+                self.stopped = True
+            return None
+        self.results[key] = r
+        return r
+
+
+def parity_ok(results):
+    """Every leg ran, compared equal and left a clean status record."""
+    ok = True
+    for k, r in results.items():
+        if not isinstance(r, dict):
+            continue
+        if "error" in r or "skipped" in r:
+            ok = False
+        if r.get("mismatches", 0) != 0:
+            ok = False
+        for key in ("status", "status_instrumented"):
+            if key in r and r[key][0] != 0:
+                ok = False
+    return ok
+
+
+def headline_latency(lat):
+    """The per-call p50/p99 from the instrumented intervals when their mean
+    agrees with the uninstrumented event mean within 5%; else the event
+    figure (replay time / calls)."""
+    inst = lat.get("instrumented")
+    if inst is not None and abs(inst["agreement"]) <= 0.05:
+        return inst["interval_us"]["p50"], inst["interval_us"]["p99"], "instrumented per-call interval"
+    ev = lat["event_us_per_call"]
+    return ev["p50"], ev["p99"], "events around each replay / calls per replay"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -667,105 +850,122 @@ def main():
 
     device = device_facts(torch, ar, props)
     log("device facts: %s" % json.dumps(device))
-    results = {}
+    legs = Legs()
+    results = legs.results
     lat = None
     if only in ("all", "latency"):
         log("launch floor")
-        results["floor"] = bench_floor(torch, args.steps)
+        legs.run("floor", lambda: bench_floor(torch, args.steps))
         log("16 KiB/rank latency: %d steps x 160 calls" % args.steps)
         wl2 = Workload(torch, 2, 4)
-        lat = graph_run(torch, ar, wl2, ONE, LL, CALLS_PER_STEP, args.steps, args.warmup)
-        lat["workload"] = ("8 ranks x [1x8192] bf16 (16 KiB/rank), N(0,0.5), one-shot LL, "
-                           "160 calls/step in one hipGraph")
-        results["latency_16k"] = lat
-        log("16 KiB p50 %.3f us/call (events), instrumented interval p50 %.3f us, span p50 %.3f"
-            % (lat["event_us_per_call"]["p50"], lat["instrumented"]["interval_us"]["p50"],
-               lat["instrumented"]["span_us"]["p50"]))
-        lat_d = graph_run(torch, ar, wl2, ONE, DIRECT, CALLS_PER_STEP, args.steps, args.warmup,
-                          instrumented=False)
-        results["latency_16k_oneshot_direct"] = lat_d
-        log("16 KiB one-shot DIRECT p50 %.3f us/call" % lat_d["event_us_per_call"]["p50"])
+        lat = legs.run("latency_16k", lambda: graph_run(torch, ar, wl2, ONE, LL, CALLS_PER_STEP,
+                                                        args.steps, args.warmup))
+        if lat is not None:
+            lat["workload"] = ("8 ranks x [1x8192] bf16 (16 KiB/rank), N(0,0.5), one-shot LL, "
+                               "160 calls/step in one hipGraph")
+            log("16 KiB p50 %.3f us/call (events), instrumented interval p50 %.3f us (mean %+.1f%% "
+                "vs events), span p50 %.3f" % (
+                    lat["event_us_per_call"]["p50"], lat["instrumented"]["interval_us"]["p50"],
+                    100 * lat["instrumented"]["agreement"], lat["instrumented"]["span_us"]["p50"]))
+        lat_d = legs.run("latency_16k_oneshot_direct", lambda: graph_run(
+            torch, ar, wl2, ONE, DIRECT, CALLS_PER_STEP, args.steps, args.warmup,
+            instrumented=False))
+        if lat_d is not None:
+            log("16 KiB one-shot DIRECT p50 %.3f us/call" % lat_d["event_us_per_call"]["p50"])
         # the barrier-ful baseline: the DIRECT reads, fold and writes between two
         # device-wide barriers; the difference is what the flags save per call
-        lat_b = graph_run(torch, ar, wl2, ONE, BARRIER, CALLS_PER_STEP, args.steps, args.warmup,
-                          instrumented=False)
-        results["latency_16k_oneshot_barrier"] = lat_b
-        results["barrier_cost_16k_us"] = round(lat_b["event_us_per_call"]["p50"] -
-                                               lat_d["event_us_per_call"]["p50"], 4)
-        log("16 KiB one-shot barrier-ful p50 %.3f us/call" % lat_b["event_us_per_call"]["p50"])
+        lat_b = legs.run("latency_16k_oneshot_barrier", lambda: graph_run(
+            torch, ar, wl2, ONE, BARRIER, CALLS_PER_STEP, args.steps, args.warmup,
+            instrumented=False))
+        if lat_b is not None and lat_d is not None:
+            results["barrier_cost_16k_us"] = round(lat_b["event_us_per_call"]["p50"] -
+                                                   lat_d["event_us_per_call"]["p50"], 4)
+            log("16 KiB one-shot barrier-ful p50 %.3f us/call" % lat_b["event_us_per_call"]["p50"])
     bws = []
     if only in ("all", "bw"):
         wl4 = Workload(torch, 4, 8)
-        for algo, proto, key, label in (
+        for algo, proto, key, label, inst in (
                 (TWO, DIRECT, "bw_4m_twoshot_direct",
                  "two-shot (in-place reduce-scatter, reduced slices written straight into every "
-                 "output, completion flags)"),
+                 "output, completion flags)", True),
                 (TWO, LL128, "bw_4m_twoshot_ll128", "two-shot (reduce-scatter + all-gather, "
-                 "LL128 lines)"),
+                 "LL128 lines)", False),
                 (ONE, DIRECT, "bw_4m_oneshot_direct", "one-shot (in-place reads after arrival "
-                 "flags)"),
+                 "flags)", False),
                 (TWO, BARRIER, "bw_4m_twoshot_barrier", "two-shot barrier-ful baseline (the "
-                 "two-shot DIRECT work between two device-wide barriers)")):
+                 "two-shot DIRECT work between two device-wide barriers)", False)):
             log("4 MiB/rank bandwidth: %s" % key)
-            r = bench_bandwidth(torch, ar, wl4, args.bw_calls, args.warmup, algo, proto, label)
-            results[key] = r
-            bws.append(r)
+            r = legs.run(key, lambda: bench_bandwidth(torch, ar, wl4, args.bw_calls, args.warmup,
+                                                      algo, proto, label, instrumented=inst))
+            if r is None:
+                continue
+            if key != "bw_4m_twoshot_barrier":
+                bws.append(r)
             log("  %.1f GB/s in a graph (%.2f us/call); %.1f GB/s stream back to back "
                 "(%.2f us/call); per-call events p50 %.2f us"
                 % (r["gbps_graph"], r["graph_us_per_call"], r["gbps_region"],
                    r["region_us_per_call"], r["us_per_call"]["p50"]))
-        bws = [r for r in bws if r is not results["bw_4m_twoshot_barrier"]]
-        results["barrier_cost_4m_us"] = round(
-            results["bw_4m_twoshot_barrier"]["us_per_call"]["p50"] -
-            results["bw_4m_twoshot_direct"]["us_per_call"]["p50"], 4)
-        results["barrier_cost_4m_us_graph"] = round(
-            results["bw_4m_twoshot_barrier"]["graph_us_per_call"] -
-            results["bw_4m_twoshot_direct"]["graph_us_per_call"], 4)
+            if "instrumented" in r:
+                log("  phases (p50 over calls, us from call start): %r, launch gap p50 %.3f"
+                    % (r["instrumented"]["phases_p50_us"],
+                       r["instrumented"]["launch_gap_us"]["p50"]))
+        tb, td = results.get("bw_4m_twoshot_barrier"), results.get("bw_4m_twoshot_direct")
+        if tb and td and "error" not in tb and "error" not in td and "skipped" not in tb \
+                and "skipped" not in td:
+            results["barrier_cost_4m_us"] = round(tb["us_per_call"]["p50"] -
+                                                  td["us_per_call"]["p50"], 4)
+            results["barrier_cost_4m_us_graph"] = round(tb["graph_us_per_call"] -
+                                                        td["graph_us_per_call"], 4)
         del wl4
     if only in ("all", "overlap"):
         log("overlap harness: projection GEMV and AllReduce")
-        results["overlap"] = bench_overlap(torch, ar, replays=10 if args.quick else 50)
-        log("  %r" % {k: v for k, v in results["overlap"].items() if k != "workload"})
+        r = legs.run("overlap", lambda: bench_overlap(torch, ar, replays=10 if args.quick else 50))
+        if r is not None:
+            log("  %r" % {k: v for k, v in r.items() if k != "workload"})
     if only in ("all", "atomic"):
         log("atomic lines (arrival-order sums): 16 KiB/rank graph and 4 MiB/rank stream")
         wl2a = Workload(torch, 2, 4)
-        r = graph_run(torch, ar, wl2a, TWO, ATOMIC, CALLS_PER_STEP, max(args.steps // 4, 5),
-                      args.warmup, instrumented=False, exact=False)
-        r["workload"] = ("8 ranks x [1x8192] bf16 (16 KiB/rank), N(0,0.5), atomic lines, "
-                         "160 calls/step in one hipGraph")
-        results["latency_16k_atomic"] = r
-        log("  16 KiB atomic p50 %.3f us/call, max %.2f ulp from the fixed-order result"
-            % (r["event_us_per_call"]["p50"], r["max_ulp_vs_fixed_order"]))
+        r = legs.run("latency_16k_atomic", lambda: graph_run(
+            torch, ar, wl2a, TWO, ATOMIC, CALLS_PER_STEP, max(args.steps // 4, 5), args.warmup,
+            instrumented=False, exact=False))
+        if r is not None:
+            r["workload"] = ("8 ranks x [1x8192] bf16 (16 KiB/rank), N(0,0.5), atomic lines, "
+                             "160 calls/step in one hipGraph")
+            log("  16 KiB atomic p50 %.3f us/call, max %.2f ulp from the fixed-order result"
+                % (r["event_us_per_call"]["p50"], r["max_ulp_vs_fixed_order"]))
         wl4a = Workload(torch, 4, 8)
-        r = bench_bandwidth(torch, ar, wl4a, max(args.bw_calls // 4, 10), args.warmup, TWO, ATOMIC,
-                            "atomic lines (arrival-order sums, not bit-exact)", exact=False,
-                            graph_calls=0)
-        results["bw_4m_atomic"] = r
-        log("  4 MiB atomic %.1f GB/s (p50 %.2f us/call), max %.2f ulp"
-            % (r["gbps_p50"], r["us_per_call"]["p50"], r["max_ulp_vs_fixed_order"]))
+        r = legs.run("bw_4m_atomic", lambda: bench_bandwidth(
+            torch, ar, wl4a, max(args.bw_calls // 4, 10), args.warmup, TWO, ATOMIC,
+            "atomic lines (arrival-order sums, not bit-exact)", exact=False, graph_calls=0))
+        if r is not None:
+            log("  4 MiB atomic %.1f GB/s (p50 %.2f us/call), max %.2f ulp"
+                % (r["gbps_p50"], r["us_per_call"]["p50"], r["max_ulp_vs_fixed_order"]))
         del wl4a
     if only in ("all", "norm"):
         log("fused AllReduce + residual add + RMS norm")
-        results["norm_16k"] = bench_norm(torch, ar, 2, replays=5 if args.quick else 20)
-        log("  %r" % {k: v for k, v in results["norm_16k"].items() if k != "workload"})
-        results["norm_512k"] = bench_norm(torch, ar, 3, replays=3 if args.quick else 10)
-        log("  %r" % {k: v for k, v in results["norm_512k"].items() if k != "workload"})
+        for key, cid, reps in (("norm_16k", 2, 5 if args.quick else 20),
+                               ("norm_512k", 3, 3 if args.quick else 10)):
+            r = legs.run(key, lambda: bench_norm(torch, ar, cid, replays=reps))
+            if r is not None:
+                log("  %r" % {k: v for k, v in r.items() if k != "workload"})
     if only in ("all", "configs"):
         reps = 3 if args.quick else 10
         wl1 = Workload(torch, 1, 4)
         for proto, key in ((SENT, "c1_sentinel"), (LL, "c1_ll")):
             log("4 ranks x 4096, 1000-call graph, %s" % key)
-            r = graph_run(torch, ar, wl1, ONE, proto, 1000, reps, 2)
-            r["workload"] = "4 ranks x [1x4096] bf16, N(0,1), one-shot, 1000 calls in one hipGraph"
-            results[key] = r
+            r = legs.run(key, lambda: graph_run(torch, ar, wl1, ONE, proto, 1000, reps, 2))
+            if r is not None:
+                r["workload"] = ("4 ranks x [1x4096] bf16, N(0,1), one-shot, 1000 calls in one "
+                                 "hipGraph")
         wl3 = Workload(torch, 3, 4)
         for algo, key in ((ONE, "c3_oneshot_ll128"), (TWO, "c3_twoshot_ll128")):
             log("8 ranks x 512 KiB LL128, 160-call graph, %s" % key)
-            r = graph_run(torch, ar, wl3, algo, LL128, CALLS_PER_STEP, reps * 2, 2)
-            r["workload"] = ("8 ranks x [32x8192] bf16 (512 KiB/rank), N(0,1) + 1% x100, LL128, "
-                             "160 calls in one hipGraph")
-            r["gbps_p50"] = wl3.b_alg / (r["event_us_per_call"]["p50"] * 1e-6) / 1e9
-            results[key] = r
+            r = legs.run(key, lambda: graph_run(torch, ar, wl3, algo, LL128, CALLS_PER_STEP,
+                                                reps * 2, 2))
+            if r is not None:
+                r["workload"] = ("8 ranks x [32x8192] bf16 (512 KiB/rank), N(0,1) + 1% x100, "
+                                 "LL128, 160 calls in one hipGraph")
+                r["gbps_p50"] = wl3.b_alg / (r["event_us_per_call"]["p50"] * 1e-6) / 1e9
         del wl3
         import synth
         wl5 = Workload(torch, 5, 8)
@@ -773,26 +973,29 @@ def main():
         delays = torch.from_numpy(synth.delays_ns(5, calls5).view(np.int32).copy()).to("cuda:0")
         for algo, key in ((TWO, "c5_twoshot_sentinel"), (ONE, "c5_oneshot_sentinel")):
             log("16 ranks, %d-call graph with start delays, %s" % (calls5, key))
-            r = graph_run(torch, ar, wl5, algo, SENT, calls5, 1, 1, delays=delays)
-            r["workload"] = ("16 ranks x [8x7168] bf16, N(0,1), seeded U[0,5 us] start delay per "
-                             "(call, rank), %d calls in one hipGraph" % calls5)
-            results[key] = r
-            r2 = graph_run(torch, ar, wl5, algo, SENT, calls5, 1, 1, instrumented=False)
-            results[key + "_nodelay"] = r2
+            r = legs.run(key, lambda: graph_run(torch, ar, wl5, algo, SENT, calls5, 1, 1,
+                                                delays=delays, instrumented=False))
+            if r is not None:
+                r["workload"] = ("16 ranks x [8x7168] bf16, N(0,1), seeded U[0,5 us] start delay "
+                                 "per (call, rank), %d calls in one hipGraph" % calls5)
+            legs.run(key + "_nodelay", lambda: graph_run(torch, ar, wl5, algo, SENT, calls5, 1, 1,
+                                                         instrumented=False))
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-            "io_dtype": "bf16", "data": "synthetic", "unit": "us/call"}
+            "io_dtype": "bf16", "data": "synthetic", "unit": "us/call", "value": None}
     if lat is not None:
-        line["value"] = round(lat["event_us_per_call"]["p50"], 4)
+        p50, p99, source = headline_latency(lat)
+        line["value"] = round(p50, 4)
+        line["p99"] = round(p99, 4)
+        line["value_source"] = source
+        line["value_events_p50"] = round(lat["event_us_per_call"]["p50"], 4)
         line["ms_per_step"] = round(lat["event_ms_per_replay"]["mean"], 5)
         line["config"] = {"workload": lat["workload"], "n_ranks": 8, "elems_per_rank": 8192,
                           "calls_per_step": CALLS_PER_STEP, "launch": "hipGraph"}
     if bws:
-        # throughput of back-to-back calls: events around the whole timed
-        # region (an event packet between calls would add its own gap)
-        # (the graph pass: dispatches back to back without the host in the
-        # loop, the timing a profiler's kernel trace agrees with)
+        # the graph pass: dispatches back to back without the host in the
+        # loop, the timing a profiler's kernel trace agrees with
         best = max(bws, key=lambda r: r.get("gbps_graph", r["gbps_region"]))
         avg_us = best.get("graph_us_per_call", best["region_us_per_call"])
         achieved = best["b_alg_bytes"] / (avg_us * 1e-6) / 1e9
@@ -808,17 +1011,19 @@ def main():
                             "per_launch_bytes": best["b_alg_bytes"], "avg_launch_us": avg_us,
                             "avg_launch_us_stream_back_to_back": best["region_us_per_call"],
                             "avg_launch_us_with_per_call_events": best["us_per_call"]["mean"]}
-    if lat is not None and "floor" in results:
+    fl = results.get("floor")
+    if lat is not None and fl is not None and "us_per_node_p50" in fl:
         # the latency kernel is bound by the launch floor plus its in-XCD
         # hops, not by HBM: how close the call is to an empty graph node
-        fl = results["floor"]["us_per_node_p50"]
-        line["latency_floor"] = {"bound": "launch", "floor_us": round(fl, 4),
+        f = fl["us_per_node_p50"]
+        line["latency_floor"] = {"bound": "launch", "floor_us": round(f, 4),
                                  "achieved_us": line["value"],
-                                 "frac": round(fl / line["value"], 4),
-                                 "kernel_work_us": round(line["value"] - fl, 4)}
+                                 "frac": round(f / line["value"], 4),
+                                 "kernel_work_us": round(line["value"] - f, 4)}
     line["cpu_baseline"] = cpu
-    line["parity_ok"] = all(r.get("mismatches", 0) == 0 and r.get("status", [0])[0] == 0
-                            for k, r in results.items() if isinstance(r, dict) and "status" in r)
+    line["parity_ok"] = parity_ok(results)
+    line["failed_legs"] = sorted(k for k, r in results.items()
+                                 if isinstance(r, dict) and ("error" in r or "skipped" in r))
     line["results"] = results
     line["host"] = platform.node()
     line["device"] = device

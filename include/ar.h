@@ -274,13 +274,27 @@ int ar_set_watchdog(uint32_t budget_us);
 
 /*
  * ar_step_end -- close a step of calls (typically one emulated decode step of
- * 2 x layers calls).  Enqueues one tiny kernel on `stream` that advances the
- * device flag sequence by the step's call count, so that the flags of a
+ * 2 x layers calls: the 160 AllReduces per token of an 80-layer model,
+ * "vLLM 分布式推理核心" page, section 一).  Enqueues one tiny kernel on
+ * `stream` that advances the device's round sequence by the rounds of the
+ * step's calls and its call count by their number, so that the flags of a
  * captured hipGraph's replays never repeat; resets the host epoch counter to
- * 0.  The step must hold an even number of calls (parity keeps alternating).
- * Errors: AR_ERR_NOT_INIT, AR_ERR_STATE (odd call count), AR_ERR_HIP.
+ * 0.  Buffer parity follows the global round number, so a step may hold any
+ * number of calls.  When the round sequence passes 0xF0000000 the kernel
+ * clears every flag word and restarts it at 0.  A step holds at most 2^27
+ * rounds (ar_allreduce refuses a call beyond that).
+ * Errors: AR_ERR_NOT_INIT, AR_ERR_HIP.
  */
 int ar_step_end(hipStream_t stream);
+
+/*
+ * ar_set_sequence -- test hook: sets the device round sequence to `seq`
+ * (<= 0xF0000000) with a kernel on `stream`, so that a test can run steps
+ * across the sequence's restart.  Only between steps (AR_ERR_STATE after a
+ * call of an open step).  Errors: AR_ERR_NOT_INIT, AR_ERR_STATE,
+ * AR_ERR_INVALID, AR_ERR_HIP.
+ */
+int ar_set_sequence(uint32_t seq, hipStream_t stream);
 
 /*
  * ar_set_delays -- test hook: per (call, rank) start delays.  dev_ns is a
@@ -292,15 +306,23 @@ int ar_step_end(hipStream_t stream);
 int ar_set_delays(const uint32_t *dev_ns, size_t calls);
 
 /*
- * ar_set_timestamps -- measurement hook: DEVICE uint64 table [slots][64][2].
- * Workgroup b of the call with flag f folds its start time into
- * [slot][b % 64][0] (minimum) and its end time into [slot][b % 64][1]
- * (maximum), slot = (f - 1) mod slots, in ticks of the constant 100 MHz
- * clock; the call's first start and last end are the minimum and maximum over
- * the 64 sub-slots.  The caller initialises [.][.][0] to UINT64_MAX and
- * [.][.][1] to 0.  NULL disables (the default).
+ * ar_set_timestamps -- measurement hook (time completion at the consumer,
+ * not at the asynchronous return: the small-message essay, section 6.2):
+ * DEVICE uint64 table [slots][records_per_slot][4].  Every wave w (position
+ * in dispatch order: workgroup index x waves per workgroup + wave) of the
+ * call numbered c (calls counted from 1 since ar_init / ar_reset, across
+ * steps) with w < records_per_slot writes record [(c - 1) mod slots][w] =
+ * {start, first synchronisation satisfied, last data store issued, end}, in
+ * ticks of the constant 100 MHz clock, with plain stores (no atomics, waits
+ * or barriers).  The two middle fields are written only when `phases` is
+ * nonzero (else 0): each is one more read of the clock, which lengthens the
+ * call.  A call's start is the minimum of its records' starts, its end the
+ * maximum of their ends.  NULL disables (the default).  records_per_slot
+ * should be at least the launch's wave count (ar_query keys 4 and 5).
+ * Errors: AR_ERR_NOT_INIT, AR_ERR_INVALID (zero sizes, or a table above
+ * 2^40 records).
  */
-int ar_set_timestamps(uint64_t *dev_ts, size_t slots);
+int ar_set_timestamps(uint64_t *dev_ts, size_t slots, size_t records_per_slot, int phases);
 
 /*
  * ar_get_status -- copy the device status record {code, rank, source, flag}
@@ -335,6 +357,9 @@ int ar_last_hip_error(void);
  * Returns the value, or a negative status.
  */
 long long ar_query(int key, size_t n);
+/*   (continued) 12 rounds (flags) a call of n elements would take, 13 rounds of
+ *   the open step so far, 14 the device round sequence (n == 0) or call count
+ *   (n != 0), read after a device synchronisation. */
 
 #ifdef __cplusplus
 }

@@ -183,9 +183,11 @@ def test_rejects_bad_calls():
         assert a.allreduce(ins, ins[0], n // 8, 1, check=False) == ar.ar.AR_ERR_INVALID  # aliasing
         assert a.allreduce(ins, out, n, 1) == 0
         assert a.allreduce(ins, out, n, 1, check=False) == ar.ar.AR_ERR_INVALID   # repeat
-        assert a.lib().ar_step_end(None) == ar.ar.AR_ERR_STATE                    # odd count
         assert a.allreduce(ins, out, n, 2) == 0
-        assert a.lib().ar_step_end(None) == 0
+        assert a.allreduce(ins, out, n, 3) == 0
+        assert a.query(7) == 3 and a.query(13) >= 3
+        assert a.lib().ar_step_end(None) == 0           # any number of calls closes a step
+        assert a.query(7) == 0 and a.query(13) == 0
         assert a.allreduce(ins, out, n, 1) == 0
         torch.cuda.synchronize()
     assert_bits_equal(host_bits(out), expect(data))

@@ -44,7 +44,8 @@ _SIGS = {
     "ar_set_watchdog": (_c_int, [_c_u32]),
     "ar_step_end": (_c_int, [_c_vp]),
     "ar_set_delays": (_c_int, [_c_vp, _c_size]),
-    "ar_set_timestamps": (_c_int, [_c_vp, _c_size]),
+    "ar_set_timestamps": (_c_int, [_c_vp, _c_size, _c_size, _c_int]),
+    "ar_set_sequence": (_c_int, [_c_u32, _c_vp]),
     "ar_get_status": (_c_int, [ctypes.POINTER(_c_u32)]),
     "ar_reset": (_c_int, [_c_vp]),
     "ar_strerror": (ctypes.c_char_p, [_c_int]),
@@ -201,9 +202,17 @@ def set_delays(dev_ns=None, calls=0):
     return _check("ar_set_delays", lib().ar_set_delays(p or None, int(calls)))
 
 
-def set_timestamps(dev_ts=None, slots=0):
+def set_timestamps(dev_ts=None, slots=0, records_per_slot=0, phases=False):
+    """dev_ts: uint64/int64 device tensor [slots, records_per_slot, 4]."""
     p = 0 if dev_ts is None else _ptr(dev_ts)
-    return _check("ar_set_timestamps", lib().ar_set_timestamps(p or None, int(slots)))
+    return _check("ar_set_timestamps",
+                  lib().ar_set_timestamps(p or None, int(slots), int(records_per_slot),
+                                          1 if phases else 0))
+
+
+def set_sequence(seq, stream=None):
+    """Test hook: sets the device round sequence (between steps)."""
+    return _check("ar_set_sequence", lib().ar_set_sequence(int(seq), _stream_handle(stream)))
 
 
 def get_status():

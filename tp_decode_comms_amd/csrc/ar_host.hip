@@ -9,6 +9,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+#include <strings.h>
 
 #include <algorithm>
 #include <cmath>
@@ -78,9 +79,10 @@ struct Context {
     int threads = 0;                    // 0 = chosen per call
     uint32_t watchdog_us = DEFAULT_WATCHDOG_US;
     const uint32_t *delays = nullptr; size_t delay_rows = 0;
-    uint64_t *ts = nullptr; size_t ts_slots = 0;
+    uint64_t *ts = nullptr; size_t ts_slots = 0, ts_stride = 0; bool ts_phases = false;
     // sequence
     uint32_t last_epoch = 0;
+    uint64_t step_rounds = 0;           // rounds of the current step's calls so far
     int capacity[ar::K_COUNT][2][5] = {};   // resident workgroups [kind][f32][64..1024 threads]
     int cap_l128[2][2][3] = {};             // LL128 at 256 threads [two-shot][f32][1, 2, 4 groups]
     bool cap_ready = false;
@@ -93,6 +95,48 @@ int hip_fail(hipError_t e)
 {
     g_last_hip = (int)e;
     return AR_ERR_HIP;
+}
+
+// Start-up defaults from the environment (read by ar_init, as NCCL reads
+// NCCL_ALGO / NCCL_PROTO): AR_ALGO = auto | oneshot | twoshot, AR_PROTO =
+// auto | ll | ll128 | sentinel | direct | barrier | atomic, AR_WATCHDOG_MS =
+// a positive integer.  A value that does not parse, or an impossible
+// algorithm/protocol pair, makes ar_init fail with AR_ERR_INVALID.
+int env_choice(const char *name, const char *const *names, int count, int *out)
+{
+    const char *e = getenv(name);
+    if (e == nullptr || *e == 0)
+        return AR_OK;
+    for (int i = 0; i < count; ++i)
+        if (strcasecmp(e, names[i]) == 0) {
+            *out = i;
+            return AR_OK;
+        }
+    return AR_ERR_INVALID;
+}
+
+int apply_env(int *algo, int *proto, uint32_t *watchdog_us)
+{
+    static const char *const algos[] = {"auto", "oneshot", "twoshot"};
+    static const char *const protos[] = {"auto", "ll", "ll128", "sentinel", "direct", "barrier",
+                                         "atomic"};
+    int rc = env_choice("AR_ALGO", algos, 3, algo);
+    if (rc == AR_OK)
+        rc = env_choice("AR_PROTO", protos, 7, proto);
+    if (rc != AR_OK)
+        return rc;
+    if ((*algo == AR_ALGO_TWOSHOT && *proto == AR_PROTO_LL) ||
+        (*algo == AR_ALGO_ONESHOT && *proto == AR_PROTO_ATOMIC))
+        return AR_ERR_INVALID;
+    const char *w = getenv("AR_WATCHDOG_MS");
+    if (w != nullptr && *w != 0) {
+        char *end = nullptr;
+        const long ms = strtol(w, &end, 10);
+        if (end == w || *end != 0 || ms <= 0 || ms > 4000000)
+            return AR_ERR_INVALID;
+        *watchdog_us = (uint32_t)ms * 1000u;
+    }
+    return AR_OK;
 }
 
 bool debug_enabled()
@@ -233,7 +277,29 @@ struct Plan {
     uint32_t slice;
     bool local;         // XCD-local coherence scope
     bool unit4 = false; // in-place one-shot: 4-element lane units
+    uint32_t rounds = 1; // rounds of the call (each takes its own flag)
 };
+
+uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+// Rounds a call walks: the loop count of its part 0 (every part walks at
+// most as many).  Kinds without rounds take one flag.
+uint32_t rounds_of(const Plan &p, size_t n)
+{
+    uint64_t r = 1;
+    switch (p.kind) {
+    case ar::K_ONESHOT_LL:
+    case ar::K_ONESHOT_LL_NORM: r = ceil_div(n / 4, (uint64_t)p.parts * 64); break;
+    case ar::K_ONESHOT_SENTINEL: r = ceil_div(n / 8, (uint64_t)p.parts * 64); break;
+    case ar::K_TWOSHOT_SENTINEL: r = ceil_div(p.slice / 8, (uint64_t)p.parts * 64); break;
+    case ar::K_ONESHOT_LL128:
+        r = ceil_div(ceil_div(ceil_div(n, ar::L128_ELEMS), (uint64_t)p.gw), p.parts); break;
+    case ar::K_TWOSHOT_LL128:
+        r = ceil_div(ceil_div(ceil_div(p.slice, ar::L128_ELEMS), (uint64_t)p.gw), p.parts); break;
+    default: break;
+    }
+    return r == 0 ? 1u : (uint32_t)r;
+}
 
 int choose_kind(size_t n, int *kind)
 {
@@ -380,6 +446,7 @@ int plan_geometry(size_t n, bool f32, Plan *p)
         want = ONESHOT_DIRECT_MAX_PARTS;
     p->parts = (uint32_t)want;
     p->local = !f32 && g.scope == AR_SCOPE_AUTO && g.placement_ok && p->parts % ar::XCDS == 0;
+    p->rounds = rounds_of(*p, n);
     return AR_OK;
 }
 
@@ -476,13 +543,15 @@ void fill_launch(const void *const *rank_bufs, void *out, size_t n, uint32_t epo
     a.ctl = g.ctl;
     a.done = g.done;
     a.acc = g.acc; a.acc_stride = (uint32_t)g.acc_stride;
-    a.ts = g.ts; a.ts_slots = (uint32_t)g.ts_slots;
+    a.ts = g.ts; a.ts_slots = (uint32_t)g.ts_slots; a.ts_stride = (uint32_t)g.ts_stride;
+    a.ts_phases = g.ts_phases ? 1u : 0u;
     a.delays = g.delays; a.delay_rows = (uint32_t)g.delay_rows;
     a.ll_stride = (uint32_t)g.ll_stride; a.l128_stride = (uint32_t)g.l128_stride;
     a.s1_stride = (uint32_t)g.s1_stride; a.s2_stride = (uint32_t)g.s2_stride;
     a.n = (uint32_t)n;
     a.n_ranks = (uint32_t)g.n_ranks;
     a.epoch = epoch;
+    a.rbase = (uint32_t)g.step_rounds;
     a.parts = p.parts;
     a.slice = p.slice;
     // workgroup layout: grid (8, N, parts / 8) when parts % 8 == 0 (blocks
@@ -503,16 +572,20 @@ int do_allreduce(const void *const *rank_bufs, void *out, size_t n, uint32_t epo
     rc = make_plan(n, f32, &p);
     if (rc != AR_OK)
         return rc;
+    if (g.step_rounds + p.rounds > ar::STEP_ROUNDS_MAX)
+        return AR_ERR_INVALID;          // close the step with ar_step_end first
     Launch a;
     fill_launch(rank_bufs, out, n, epoch, p, &a);
     const uint32_t grid = p.parts * (uint32_t)g.n_ranks;
     if (debug_enabled())
-        fprintf(stderr, "[ar] n=%zu epoch=%u kind=%d grid=%u threads=%u slice=%u f32=%d local=%d\n",
-                n, epoch, p.kind, grid, p.threads, p.slice, (int)f32, (int)p.local);
+        fprintf(stderr, "[ar] n=%zu epoch=%u kind=%d grid=%u threads=%u slice=%u rounds=%u f32=%d "
+                "local=%d\n", n, epoch, p.kind, grid, p.threads, p.slice, p.rounds, (int)f32,
+                (int)p.local);
     hipError_t e = ar::launch_ar(p.kind, f32, p.local, p.gw, a, p.threads, stream);
     if (e != hipSuccess)
         return hip_fail(e);
     g.last_epoch = epoch;
+    g.step_rounds += p.rounds;
     return AR_OK;
 }
 
@@ -609,6 +682,8 @@ int do_allreduce_norm(const void *const *rank_bufs, const void *const *residual,
         if (rc != AR_OK)
             return rc;
     }
+    if (g.step_rounds + p.rounds > ar::STEP_ROUNDS_MAX)
+        return AR_ERR_INVALID;
     ar::NormLaunch L;
     memset(&L, 0, sizeof L);
     fill_launch(rank_bufs, out_h, n, epoch, p, &L.base);
@@ -628,6 +703,7 @@ int do_allreduce_norm(const void *const *rank_bufs, const void *const *residual,
     if (e != hipSuccess)
         return hip_fail(e);
     g.last_epoch = epoch;
+    g.step_rounds += p.rounds;
     return AR_OK;
 }
 
@@ -641,6 +717,10 @@ int ar_init(int n_ranks, size_t max_elems)
     if (g.live)
         return AR_ERR_STATE;
     if (n_ranks < 1 || n_ranks > AR_MAX_RANKS || max_elems == 0 || max_elems > MAX_ELEMS_LIMIT)
+        return AR_ERR_INVALID;
+    int env_algo = AR_ALGO_AUTO, env_proto = AR_PROTO_AUTO;
+    uint32_t env_watchdog = DEFAULT_WATCHDOG_US;
+    if (apply_env(&env_algo, &env_proto, &env_watchdog) != AR_OK)
         return AR_ERR_INVALID;
     hipError_t e = hipGetDevice(&g.device);
     if (e != hipSuccess)
@@ -699,13 +779,14 @@ int ar_init(int n_ranks, size_t max_elems)
         free_all();
         return hip_fail(e);
     }
-    g.algo = AR_ALGO_AUTO; g.proto = AR_PROTO_AUTO;
+    g.algo = env_algo; g.proto = env_proto;
     g.wgs_per_rank = 0; g.threads = 0;
     g.scope = AR_SCOPE_AUTO;
-    g.watchdog_us = DEFAULT_WATCHDOG_US;
+    g.watchdog_us = env_watchdog;
     g.delays = nullptr; g.delay_rows = 0;
-    g.ts = nullptr; g.ts_slots = 0;
+    g.ts = nullptr; g.ts_slots = 0; g.ts_stride = 0; g.ts_phases = false;
     g.last_epoch = 0;
+    g.step_rounds = 0;
     g.cap_ready = false;
     g.live = true;
     rc = compute_capacity();
@@ -809,7 +890,7 @@ int ar_set_watchdog(uint32_t budget_us)
 {
     if (!g.live)
         return AR_ERR_NOT_INIT;
-    g.watchdog_us = budget_us ? budget_us : DEFAULT_WATCHDOG_US;
+    g.watchdog_us = budget_us ? budget_us : DEFAULT_WATCHDOG_US;   // 0: the built-in default
     return AR_OK;
 }
 
@@ -817,15 +898,29 @@ int ar_step_end(hipStream_t stream)
 {
     if (!g.live)
         return AR_ERR_NOT_INIT;
-    if (g.last_epoch % 2 != 0)
-        return AR_ERR_STATE;
     if (g.last_epoch > 0) {
-        hipError_t e = ar::launch_step_end(g.ctl, g.last_epoch, g.ll, ll_bytes(), g.l128,
-                                           l128_bytes(), g.done, g.stats, stats_bytes(), stream);
+        hipError_t e = ar::launch_step_end(g.ctl, g.last_epoch, (uint32_t)g.step_rounds, g.ll,
+                                           ll_bytes(), g.l128, l128_bytes(), g.done, g.stats,
+                                           stats_bytes(), stream);
         if (e != hipSuccess)
             return hip_fail(e);
     }
     g.last_epoch = 0;
+    g.step_rounds = 0;
+    return AR_OK;
+}
+
+int ar_set_sequence(uint32_t seq, hipStream_t stream)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    if (g.last_epoch != 0)
+        return AR_ERR_STATE;            // only between steps
+    if (seq > ar::SEQ_WRAP)
+        return AR_ERR_INVALID;
+    hipError_t e = ar::launch_set_seq(g.ctl, seq, stream);
+    if (e != hipSuccess)
+        return hip_fail(e);
     return AR_OK;
 }
 
@@ -840,14 +935,18 @@ int ar_set_delays(const uint32_t *dev_ns, size_t calls)
     return AR_OK;
 }
 
-int ar_set_timestamps(uint64_t *dev_ts, size_t slots)
+int ar_set_timestamps(uint64_t *dev_ts, size_t slots, size_t records_per_slot, int phases)
 {
     if (!g.live)
         return AR_ERR_NOT_INIT;
-    if (dev_ts != nullptr && (slots == 0 || slots > 0xFFFFFFFFu))
+    if (dev_ts != nullptr && (slots == 0 || slots > 0xFFFFFFFFu || records_per_slot == 0 ||
+                              records_per_slot > 0xFFFFFFFFu ||
+                              slots > ((size_t)1 << 40) / records_per_slot))
         return AR_ERR_INVALID;
     g.ts = dev_ts;
     g.ts_slots = dev_ts ? slots : 0;
+    g.ts_stride = dev_ts ? records_per_slot : 0;
+    g.ts_phases = dev_ts != nullptr && phases != 0;
     return AR_OK;
 }
 
@@ -874,6 +973,7 @@ int ar_reset(hipStream_t stream)
     if (e != hipSuccess)
         return hip_fail(e);
     g.last_epoch = 0;
+    g.step_rounds = 0;
     return AR_OK;
 }
 
@@ -947,6 +1047,22 @@ long long ar_query(int key, size_t n)
     case 9: return g.placement_ok ? 1 : 0;
     case 10: return g.wall_khz;
     case 11: return g.cu_count;
+    case 12: {
+        if (n == 0 || n > g.max_elems || n % 8)
+            return AR_ERR_INVALID;
+        int rc = make_plan(n, false, &p);
+        return rc != AR_OK ? rc : (long long)p.rounds;
+    }
+    case 13: return (long long)g.step_rounds;
+    case 14: {
+        uint32_t w[2] = {0, 0};
+        hipError_t e = hipDeviceSynchronize();
+        if (e == hipSuccess)
+            e = hipMemcpy(w, g.ctl + ar::CTL_SEQ, 8, hipMemcpyDeviceToHost);
+        if (e != hipSuccess)
+            return hip_fail(e);
+        return n == 0 ? (long long)w[0] : (long long)w[1];
+    }
     default: return AR_ERR_INVALID;
     }
 }

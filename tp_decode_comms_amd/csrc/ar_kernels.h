@@ -62,9 +62,10 @@ hipError_t launch_add_rmsnorm(const void *a, const void *const *res, const void 
 // over a gx x gy x gz grid
 hipError_t launch_xcc_map(uint32_t *out, uint32_t gx, uint32_t gy, uint32_t gz, uint32_t threads,
                           hipStream_t stream);
-hipError_t launch_step_end(uint32_t *ctl, uint32_t calls, char *ll, size_t ll_bytes, char *l128,
-                           size_t l128_bytes, uint32_t *done, uint32_t *stats, size_t stats_bytes,
-                           hipStream_t stream);
+hipError_t launch_step_end(uint32_t *ctl, uint32_t calls, uint32_t rounds, char *ll,
+                           size_t ll_bytes, char *l128, size_t l128_bytes, uint32_t *done,
+                           uint32_t *stats, size_t stats_bytes, hipStream_t stream);
+hipError_t launch_set_seq(uint32_t *ctl, uint32_t seq, hipStream_t stream);
 hipError_t launch_fill(uint32_t *p, size_t words, uint32_t value, hipStream_t stream);
 
 }  // namespace ar

@@ -40,9 +40,12 @@
 namespace ar {
 
 // ------------------------------------------------------------------ common
+// flag: the flag of the call's first round (round j uses flag + j); call:
+// the call's number since the last reset (start delays, measurement slots,
+// status records); par: buffer parity of the first round (flag & 1).
 struct Ctx0 {
-    uint32_t rank, part, flag, par;
-    uint64_t t0;
+    uint32_t rank, part, flag, call, par;
+    uint64_t t0, t_sync, t_data;
 };
 
 // The workgroup's position in dispatch order, x + X (y + N z) on the grid
@@ -52,16 +55,20 @@ __device__ __forceinline__ uint32_t linear_id(const Launch &a)
     return ((blockIdx.z * a.n_ranks + blockIdx.y) << a.xshift) + blockIdx.x;
 }
 
-// The flag-sequence base.  Only the step-end kernel and the host's re-arm
-// kernels write it, always in an earlier launch; the launch boundary makes
-// that write visible, and no launch writes it while an AllReduce kernel
-// runs, so it is read as constant memory: a scalar load, served by the
-// scalar cache a CU's waves share (every wave of the launch reads this
-// word; 8 x 16 KiB LL: 2.63 -> 2.58 us per call against a vector load).
-__device__ __forceinline__ uint32_t load_seq(const Launch &a)
+// The two sequence words {round sequence, call count} of the step.  Only the
+// step-end kernel and the host's re-arm kernels write them, always in an
+// earlier launch; the launch boundary makes that write visible, and no launch
+// writes them while an AllReduce kernel runs, so they are read as constant
+// memory: one scalar load, served by the scalar cache a CU's waves share
+// (every wave of the launch reads them; 8 x 16 KiB LL: 2.63 -> 2.58 us per
+// call against a vector load).
+__device__ __forceinline__ void load_seq(const Launch &a, Ctx0 &c)
 {
-    typedef const __attribute__((address_space(4))) uint32_t const_u32;
-    return *((const_u32 *)a.ctl + CTL_SEQ);
+    typedef const __attribute__((address_space(4))) u32x2 const_u32x2;
+    const u32x2 s = *((const_u32x2 *)a.ctl + CTL_SEQ / 2);
+    c.flag = s.x + a.rbase + 1u;
+    c.call = s.y + a.epoch;
+    c.par = c.flag & 1u;
 }
 
 __device__ __forceinline__ void start_delay(const Launch &a, const Ctx0 &c)
@@ -69,7 +76,7 @@ __device__ __forceinline__ void start_delay(const Launch &a, const Ctx0 &c)
     if (a.delays == nullptr)
         return;
     __amdgpu_buffer_rsrc_t d = rsrc(a.delays, a.delay_rows * a.n_ranks * 4u);
-    uint32_t row = (c.flag - 1u) % a.delay_rows;
+    uint32_t row = (c.call - 1u) % a.delay_rows;
     uint32_t ns = ld4<CP_PLAIN>(d, (row * a.n_ranks + c.rank) * 4u);
     uint64_t ticks = ns / 10u;
     if (ticks > 1000000u)                 // at most 10 ms per call
@@ -78,26 +85,50 @@ __device__ __forceinline__ void start_delay(const Launch &a, const Ctx0 &c)
         __builtin_amdgcn_s_sleep(1);
 }
 
+// Phase marks (only with a timestamp table asking for them): `mark` records
+// the clock, `mark_once` only the first time.  Each read of the constant
+// clock is a scalar-memory instruction whose result the next LDS or scalar
+// wait also waits for, so marks on the critical path lengthen the call
+// (8 x 16 KiB LL: +0.37 us per call with both marks); a table without them
+// records only the start (read anyway) and the end.
+__device__ __forceinline__ void mark(const Launch &a, uint64_t &t)
+{
+    if (a.ts != nullptr && a.ts_phases != 0u)
+        t = clock100();
+}
+__device__ __forceinline__ void mark_once(const Launch &a, uint64_t &t)
+{
+    if (a.ts != nullptr && a.ts_phases != 0u && t == 0u)
+        t = clock100();
+}
+
+// Each wave's lane 0 writes its own record {start, first synchronisation
+// satisfied, last data store issued, end} with plain stores: no atomic, no
+// wait for earlier stores and no barrier, so the measured call runs as it
+// does without the table.  Record index: the wave's position in dispatch
+// order; slot (call - 1) mod slots.
 __device__ __forceinline__ void finish(const Launch &a, const Ctx0 &c)
 {
     if (a.ts == nullptr)
         return;
-    wait_stores();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint64_t t1 = clock100();
-        // 64 sub-slots per call spread the atomics over 64 addresses
-        const uint32_t slot = (c.flag - 1u) % a.ts_slots;
-        uint64_t *p = a.ts + ((size_t)slot * TS_SUB + (linear_id(a) % TS_SUB)) * 2u;
-        __hip_atomic_fetch_min(p, c.t0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_max(p + 1, t1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    const uint32_t w = linear_id(a) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if ((threadIdx.x & 63u) != 0u || w >= a.ts_stride)
+        return;
+    const uint64_t t1 = clock100();
+    const uint32_t slot = (c.call - 1u) % a.ts_slots;
+    uint64_t *p = a.ts + ((size_t)slot * a.ts_stride + w) * TS_FIELDS;
+    p[0] = c.t0;
+    p[1] = c.t_sync;
+    p[2] = c.t_data;
+    p[3] = t1;
 }
 
 template <bool LOCAL>
 __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
 {
     c.t0 = clock100();
+    c.t_sync = 0u;
+    c.t_data = 0u;
     // The grid is (X, N, parts / X) with X = 2^xshift consecutive parts of
     // one rank along x (X = 8 when parts is a multiple of 8, else 1): the
     // rank is blockIdx.y and the part (blockIdx.z << xshift) + blockIdx.x.
@@ -127,10 +158,9 @@ __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
     // (blockDim.x is read from the launch's hidden arguments, so it is one
     // of them.)
     asm volatile("" ::"s"(a.in[c.rank]), "s"(a.out), "s"(a.ctl), "s"(a.n), "s"(a.n_ranks),
-                 "s"(a.epoch), "s"(a.parts), "s"(a.slice), "s"(a.xshift), "s"(a.delays),
-                 "s"(blockDim.x));
+                 "s"(a.epoch), "s"(a.rbase), "s"(a.parts), "s"(a.slice), "s"(a.xshift),
+                 "s"(a.delays), "s"(blockDim.x));
     c.part = (blockIdx.z << a.xshift) + lo;
-    c.par = a.epoch & 1u;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t in_rsrc(const Launch &a, uint32_t r)
@@ -237,7 +267,7 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
             need = false;
         if (!wave_any(need))
             return true;
-        if (w.expired(ctl, c.rank, lane, c.flag))
+        if (w.expired(ctl, c.rank, lane, c.call))
             return false;
         compiler_fence();
         v0 = need ? ld4<Pol<LOCAL>::LD>(r, off) : c.flag;
@@ -269,7 +299,7 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
 // `epi(ch, v)` consumes the reduced chunk (4 binary32 sums in v) on wave 0;
 // all lanes of wave 0 call it together when the round's chunks are in range.
 template <int NMAX, bool LOCAL, bool SPLIT, typename Epi>
-__device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
+__device__ __forceinline__ bool ll_round(const Launch &a, Ctx0 &c, const Ctl &ctl,
                                          __amdgpu_buffer_rsrc_t llr, uint32_t ch, uint32_t C,
                                          u32x2 x, u32x2 (*stage)[64], uint32_t *failed, Epi &&epi)
 {
@@ -309,7 +339,7 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
         }
         if (!wave_any(pend))
             break;
-        if (w.expired(ctl, c.rank, wave, c.flag)) {
+        if (w.expired(ctl, c.rank, wave, c.call)) {
             *failed = 1u;                           // every wave still meets the barrier
             break;
         }
@@ -322,6 +352,7 @@ __device__ __forceinline__ bool ll_round(const Launch &a, const Ctx0 &c, const C
         if (!wave_any(pend))
             break;
     }
+    mark_once(a, c.t_sync);
     lds_barrier();
     if (*failed)
         return false;
@@ -393,7 +424,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll(const Launch a)
     u32x2 x = {0u, 0u};
     if (wave == 0u && ch < C)
         x = ld8<CP_PLAIN>(inr, ch * 8u);
-    c.flag = load_seq(a) + a.epoch;
+    load_seq(a, c);
     const Ctl ctl{a.ctl};
     const __amdgpu_buffer_rsrc_t llr = rsrc(a.ll, a.n_ranks * 2u * a.ll_stride);
     start_delay(a, c);
@@ -414,6 +445,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll(const Launch a)
         if (!ll_round<NMAX, LOCAL, true>(a, c, ctl, llr, ch, C, x, stage, &failed, out))
             return;
     }
+    mark(a, c.t_data);
     finish(a, c);
 }
 
@@ -458,7 +490,7 @@ __device__ __forceinline__ bool row_rinv(const NormLaunch &L, const Ctx0 &c, con
             }
             if (!wave_any(need))
                 break;
-            if (w.expired(ctl, c.rank, c.rank, c.flag))
+            if (w.expired(ctl, c.rank, c.rank, c.call))
                 return false;
             compiler_fence();
             v0 = need ? ld8<CP_DEV>(sr, off) : u32x2{0u, 0u};
@@ -508,7 +540,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
         rw = ld8<CP_PLAIN>(resr, ch * 8u);
         g0 = ld8<CP_PLAIN>(gr, ((ch * 4u) % L.hidden) * 2u);
     }
-    c.flag = load_seq(a) + a.epoch;
+    load_seq(a, c);
     const Ctl ctl{a.ctl};
     const __amdgpu_buffer_rsrc_t llr = rsrc(a.ll, a.n_ranks * 2u * a.ll_stride);
     start_delay(a, c);
@@ -558,6 +590,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
             st8<CP_PLAIN>(scale4(hw, gw, r), oy, cc * 8u);
         }
     }
+    mark(a, c.t_data);
     finish(a, c);
 }
 
@@ -608,11 +641,12 @@ __global__ __launch_bounds__(256) void k_oneshot_direct_norm(const NormLaunch L)
             g1 = ld8<CP_PLAIN>(gr, ((e0 + NORM_BLOCK) % L.hidden) * 2u);
         }
     }
-    c.flag = load_seq(a) + a.epoch;
+    load_seq(a, c);
     const Ctl ctl{a.ctl};
     start_delay(a, c);
     raise_arrival<LOCAL>(a, c);
     bool ok = wait_arrivals<LOCAL>(a, c, ctl);
+    mark(a, c.t_sync);
     __amdgpu_buffer_rsrc_t src[NMAX];
 #pragma unroll
     for (int s = 0; s < NMAX; ++s)
@@ -677,6 +711,7 @@ __global__ __launch_bounds__(256) void k_oneshot_direct_norm(const NormLaunch L)
         const u32x2 gw = b == bbeg ? g0 : b == bbeg + 1u ? g1 : ld8<CP_PLAIN>(gr, (e % L.hidden) * 2u);
         st8<CP_PLAIN>(scale4(hw, gw, r), oy, e * 2u);
     }
+    mark(a, c.t_data);
     finish(a, c);
 }
 
@@ -728,12 +763,13 @@ __global__ __launch_bounds__(1024) void k_oneshot_rows_norm(const NormLaunch L)
             gk[k] = live && j < B ? ld8<CP_PLAIN>(gr, col * 2u) : u32x2{0u, 0u};
         }
     }
-    c.flag = load_seq(a) + a.epoch;
+    load_seq(a, c);
     const Ctl ctl{a.ctl};
     start_delay(a, c);
     raise_arrival<LOCAL>(a, c);
     if (!wait_arrivals_wg<LOCAL>(a, c, ctl))
         return;                                           // every wave returns here
+    mark(a, c.t_sync);
     if (poller) {
 #pragma unroll
         for (int k = 0; k < (int)ROWS_PER_WAVE; ++k) {
@@ -804,6 +840,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_rows_norm(const NormLaunch L)
         if (live && j < B)
             st8<CP_PLAIN>(scale4(hk[k], gk[k], r), oy, (row0 + j * NORM_BLOCK + lane * 4u) * 2u);
     }
+    mark(a, c.t_data);
     finish(a, c);
 }
 
@@ -826,7 +863,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_rows_norm(const NormLaunch L)
 constexpr int SENT_WAVES = 8;
 
 template <int NMAX, bool F32, bool LOCAL>
-__device__ __forceinline__ bool sent_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
+__device__ __forceinline__ bool sent_round(const Launch &a, Ctx0 &c, const Ctl &ctl,
                                            __amdgpu_buffer_rsrc_t box,
                                            __amdgpu_buffer_rsrc_t o, uint32_t ch, uint32_t G,
                                            u32x4 x, u32x4 (*stage)[64], uint32_t *failed)
@@ -886,7 +923,7 @@ __device__ __forceinline__ bool sent_round(const Launch &a, const Ctx0 &c, const
         check(A0);
         if (!wave_any(pend != 0u))
             break;
-        if (w.expired(ctl, c.rank, pend ? wave + SENT_WAVES * first_bit(pend) : 0u, c.flag)) {
+        if (w.expired(ctl, c.rank, pend ? wave + SENT_WAVES * first_bit(pend) : 0u, c.call)) {
             *failed = 1u;                           // every wave still meets the barrier
             break;
         }
@@ -896,6 +933,7 @@ __device__ __forceinline__ bool sent_round(const Launch &a, const Ctx0 &c, const
         if (!wave_any(pend != 0u))
             break;
     }
+    mark_once(a, c.t_sync);
     lds_barrier();                  // the tile only: the polls in flight are waited for below
     if (*failed)
         return false;
@@ -946,7 +984,7 @@ __global__ __launch_bounds__(512) void k_oneshot_sentinel(const Launch a)
     // every wave pushes the chunk, so every wave loads it (the loads meet in L2)
     uint32_t ch = c.part * 64u + lane;
     u32x4 x = ch < G ? ld16<CP_PLAIN>(inr, ch * 16u) : u32x4{0u, 0u, 0u, 0u};
-    c.flag = load_seq(a) + a.epoch;
+    load_seq(a, c);
     const Ctl ctl{a.ctl};
     const __amdgpu_buffer_rsrc_t box = rsrc(a.s1, a.n_ranks * a.n_ranks * 2u * a.s1_stride);
     start_delay(a, c);
@@ -959,6 +997,7 @@ __global__ __launch_bounds__(512) void k_oneshot_sentinel(const Launch a)
         if (!sent_round<NMAX, F32, LOCAL>(a, c, ctl, box, o, ch, G, x, stage, &failed))
             return;
     }
+    mark(a, c.t_data);
     finish(a, c);
 }
 
@@ -1120,7 +1159,7 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
     begin<LOCAL>(a, c);
     const uint32_t G = a.unit4 ? a.n >> 2 : a.n >> 3;          // lane units of 4 or 8 elements
     const uint32_t step = a.parts * blockDim.x;
-    c.flag = load_seq(a) + a.epoch;
+    load_seq(a, c);
     const Ctl ctl{a.ctl};
     start_delay(a, c);
     raise_arrival<LOCAL>(a, c);
@@ -1129,7 +1168,9 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
     if (!wait_arrivals<LOCAL>(a, c, ctl))
         return;
+    mark(a, c.t_sync);
     oneshot_data<NMAX, F32>(a, src, o, G, c.part * blockDim.x + threadIdx.x, step);
+    mark(a, c.t_data);
     finish(a, c);
 }
 
@@ -1155,7 +1196,7 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     const uint32_t Lq = lo >= a.n ? 0u : (a.n - lo < L ? a.n - lo : L);
     const uint32_t G = Lq >> 3;                     // chunks of my slice
     const uint32_t step = a.parts * blockDim.x;
-    c.flag = load_seq(a) + a.epoch;
+    load_seq(a, c);
     const Ctl ctl{a.ctl};
     start_delay(a, c);
     raise_arrival<LOCAL>(a, c);
@@ -1169,7 +1210,9 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
     if (!wait_arrivals_wg<LOCAL>(a, c, ctl))
         return;
+    mark(a, c.t_sync);
     twoshot_data<NMAX, F32>(a, src, oa, lo, G, c.part * blockDim.x + threadIdx.x, step);
+    mark(a, c.t_data);
     // completion: my stores are at the coherence point, then my flag.  The
     // flags of the writers on one XCD (parts p with p % 8 == x) are packed
     // together: writer (s, p) owns word x*N*P8 + s*P8 + p/8, P8 = ceil(parts/8).
@@ -1204,7 +1247,7 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
                 v1 = ld4<Pol<LOCAL>::LD>(dn, off);
                 if ((int32_t)(v0 - c.flag) >= 0)
                     break;
-                if (w.expired(ctl, q, i / per, c.flag))
+                if (w.expired(ctl, q, i / per, c.call))
                     return;
                 compiler_fence();
                 v0 = ld4<Pol<LOCAL>::LD>(dn, off);
@@ -1277,7 +1320,7 @@ __device__ __forceinline__ bool grid_barrier(const Launch &a, const Ctx0 &c, con
             w.begin(a.watchdog_ticks);
             while ((int32_t)(__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
                              c.flag) < 0) {
-                if (w.expired(ctl, c.rank, 0u, c.flag)) {
+                if (w.expired(ctl, c.rank, 0u, c.call)) {
                     good = 0;
                     break;
                 }
@@ -1299,7 +1342,7 @@ __global__ __launch_bounds__(256) void k_oneshot_barrier(const Launch a)
     begin<LOCAL>(a, c);
     const uint32_t G = a.unit4 ? a.n >> 2 : a.n >> 3;          // lane units of 4 or 8 elements
     const uint32_t step = a.parts * blockDim.x;
-    c.flag = load_seq(a) + a.epoch;
+    load_seq(a, c);
     const Ctl ctl{a.ctl};
     start_delay(a, c);
     __amdgpu_buffer_rsrc_t src[NMAX];
@@ -1307,7 +1350,9 @@ __global__ __launch_bounds__(256) void k_oneshot_barrier(const Launch a)
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
     if (!grid_barrier(a, c, ctl, CTL_BAR_TOP))
         return;
+    mark(a, c.t_sync);
     oneshot_data<NMAX, F32>(a, src, o, G, c.part * blockDim.x + threadIdx.x, step);
+    mark(a, c.t_data);
     if (!grid_barrier(a, c, ctl, CTL_BAR_BOTTOM))
         return;
     finish(a, c);
@@ -1326,7 +1371,7 @@ __global__ __launch_bounds__(256) void k_twoshot_barrier(const Launch a)
     const uint32_t Lq = lo >= a.n ? 0u : (a.n - lo < L ? a.n - lo : L);
     const uint32_t G = Lq >> 3;
     const uint32_t step = a.parts * blockDim.x;
-    c.flag = load_seq(a) + a.epoch;
+    load_seq(a, c);
     const Ctl ctl{a.ctl};
     start_delay(a, c);
     __amdgpu_buffer_rsrc_t src[NMAX];
@@ -1334,7 +1379,9 @@ __global__ __launch_bounds__(256) void k_twoshot_barrier(const Launch a)
     const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
     if (!grid_barrier(a, c, ctl, CTL_BAR_TOP))
         return;
+    mark(a, c.t_sync);
     twoshot_data<NMAX, F32>(a, src, oa, lo, G, c.part * blockDim.x + threadIdx.x, step);
+    mark(a, c.t_data);
     if (!grid_barrier(a, c, ctl, CTL_BAR_BOTTOM))
         return;
     finish(a, c);
@@ -1405,7 +1452,8 @@ __device__ __forceinline__ bool l128_recv(__amdgpu_buffer_rsrc_t reg, uint32_t r
                                           const uint32_t *g, uint32_t gvalid, uint32_t pmask,
                                           uint32_t wave, uint32_t lane, const L128Lane &ln,
                                           const uint32_t *lim, uint32_t flag, const Ctl &ctl,
-                                          uint32_t rank, uint32_t budget, u32x4 (*V)[PW])
+                                          uint32_t rank, uint32_t call, uint32_t budget,
+                                          u32x4 (*V)[PW])
 {
     // peer s's lines of group g: reg + (s*2 + par)*rb + g*1024 + lane*16
     auto off = [&](int k, int j) {
@@ -1448,7 +1496,7 @@ __device__ __forceinline__ bool l128_recv(__amdgpu_buffer_rsrc_t reg, uint32_t r
         }
         if (!wave_any(any != 0u))
             break;
-        if (w.expired(ctl, rank, any ? wave + L128_WAVES * first_bit(any) : 0u, flag))
+        if (w.expired(ctl, rank, any ? wave + L128_WAVES * first_bit(any) : 0u, call))
             return false;
         compiler_fence();
 #pragma unroll
@@ -1501,7 +1549,7 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t groups = (a.n + L128_ELEMS - 1u) / L128_ELEMS;
     const uint32_t batches = (groups + GW - 1u) / GW;
-    c.flag = load_seq(a) + a.epoch;
+    load_seq(a, c);
     const Ctl ctl{a.ctl};
     const L128Lane ln = l128_lane(lane);
     const __amdgpu_buffer_rsrc_t inr = in_rsrc(a, c.rank);
@@ -1547,8 +1595,9 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
         // receive the batch from this wave's peers
         u32x4 V[GW][PW];
         if (!l128_recv<GW, PW, LOCAL>(reg, rb, c.par, g, gvalid, pmask, wave, lane, ln, lim,
-                                      c.flag, ctl, c.rank, a.watchdog_ticks, V))
+                                      c.flag, ctl, c.rank, c.call, a.watchdog_ticks, V))
             failed = 1u;                            // every wave still meets the barrier
+        mark_once(a, c.t_sync);
 #pragma unroll
         for (int k = 0; k < GW; ++k)
             if ((gvalid >> k) & 1u)
@@ -1575,6 +1624,7 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
         }
         lds_barrier();                              // the tile is reused next batch
     }
+    mark(a, c.t_data);
     finish(a, c);
 }
 
@@ -1598,7 +1648,7 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t groups = (L + L128_ELEMS - 1u) / L128_ELEMS;
     const uint32_t batches = (groups + GW - 1u) / GW;
-    c.flag = load_seq(a) + a.epoch;
+    load_seq(a, c);
     const Ctl ctl{a.ctl};
     const L128Lane ln = l128_lane(lane);
     start_delay(a, c);
@@ -1607,6 +1657,7 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
     input_rsrcs<NMAX>(a, src);
     if (!wait_arrivals<LOCAL>(a, c, ctl))
         return;
+    mark(a, c.t_sync);
     auto slice_len = [&](uint32_t s) -> uint32_t {
         const uint32_t lo = s * L;
         return (s >= N || lo >= a.n) ? 0u : (a.n - lo < L ? a.n - lo : L);
@@ -1691,7 +1742,7 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
         // ---- all-gather of the batch from this wave's peers
         u32x4 V[GW][PW];
         if (!l128_recv<GW, PW, LOCAL>(reg, rb, c.par, g, gvalid, pmask, wave, lane, ln, lim,
-                                      c.flag, ctl, q, a.watchdog_ticks, V))
+                                      c.flag, ctl, q, c.call, a.watchdog_ticks, V))
             return;
 #pragma unroll
         for (int k = 0; k < GW; ++k) {
@@ -1712,6 +1763,7 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
             }
         }
     }
+    mark(a, c.t_data);
     finish(a, c);
 }
 
@@ -1728,7 +1780,7 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 // received slice-q chunks are staged in LDS and reduced by wave 0, which
 // puts the bf16 result in LDS for every wave's all-gather pushes.
 template <int NMAX, bool F32, bool LOCAL>
-__device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const Ctl &ctl,
+__device__ __forceinline__ bool ts_round(const Launch &a, Ctx0 &c, const Ctl &ctl,
                                          __amdgpu_buffer_rsrc_t inq, __amdgpu_buffer_rsrc_t rsr,
                                          __amdgpu_buffer_rsrc_t agr, __amdgpu_buffer_rsrc_t oa,
                                          uint32_t ch, u32x4 (*stage)[64], u32x4 *red,
@@ -1797,7 +1849,7 @@ __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const C
             check(A0);
             if (!wave_any(pend != 0u))
                 break;
-            if (w.expired(ctl, q, pend ? peer((int)first_bit(pend)) : 0u, c.flag)) {
+            if (w.expired(ctl, q, pend ? peer((int)first_bit(pend)) : 0u, c.call)) {
                 *failed = 1u;                       // every wave still meets the barrier
                 break;
             }
@@ -1815,6 +1867,7 @@ __device__ __forceinline__ bool ts_round(const Launch &a, const Ctx0 &c, const C
             pend |= 1u << j;
     uint32_t mine = pend;
     receive(rsr);
+    mark_once(a, c.t_sync);
 #pragma unroll
     for (int j = 0; j < PW; ++j)
         if ((mine >> j) & 1u)
@@ -1894,7 +1947,7 @@ __global__ __launch_bounds__(512) void k_twoshot_sentinel(const Launch a)
     const uint32_t rounds = (G + step - 1u) / step;
     if (threadIdx.x == 0)
         failed = 0u;
-    c.flag = load_seq(a) + a.epoch;
+    load_seq(a, c);
     const Ctl ctl{a.ctl};
     const __amdgpu_buffer_rsrc_t inq = in_rsrc(a, c.rank);
     const __amdgpu_buffer_rsrc_t rsr = rsrc(a.srs, N * N * 2u * a.s2_stride);
@@ -1910,6 +1963,7 @@ __global__ __launch_bounds__(512) void k_twoshot_sentinel(const Launch a)
         if (!ts_round<NMAX, F32, LOCAL>(a, c, ctl, inq, rsr, agr, oa, ch, stage, red, &failed))
             return;
     }
+    mark(a, c.t_data);
     finish(a, c);
 }
 
@@ -1954,7 +2008,7 @@ __global__ __launch_bounds__(256) void k_twoshot_atomic(const Launch a)
     // accumulator lines [parity][line] x 128 B, zero between calls
     const __amdgpu_buffer_rsrc_t acc = rsrc(a.acc, 2u * a.acc_stride);
     const Ctl ctl{a.ctl};
-    c.flag = load_seq(a) + a.epoch;
+    load_seq(a, c);
     start_delay(a, c);
     for (uint32_t l0 = c.part * per_wg; l0 < lines; l0 += step) {
         const uint32_t line = l0 + wave * 2u + half;
@@ -1984,7 +2038,7 @@ __global__ __launch_bounds__(256) void k_twoshot_atomic(const Launch a)
                 pend = false;
             if (!wave_any(pend))
                 break;
-            if (w.expired(ctl, c.rank, line, c.flag)) {
+            if (w.expired(ctl, c.rank, line, c.call)) {
                 ok = false;
                 break;
             }
@@ -1997,6 +2051,7 @@ __global__ __launch_bounds__(256) void k_twoshot_atomic(const Launch a)
         }
         if (!ok)
             break;                      // status recorded; every wave still reaches finish()
+        mark_once(a, c.t_sync);
         const uint32_t sb = data ? ld4<CP_DEV>(acc, base + 4u * j) : 0u;
         const float sum = __uint_as_float(sb);
         wait_stores();                                          // the read has returned
@@ -2015,25 +2070,28 @@ __global__ __launch_bounds__(256) void k_twoshot_atomic(const Launch a)
                     (uint16_t)__builtin_bit_cast(uint16_t, (__bf16)sum), o, e * 2u, 0, CP_PLAIN);
         }
     }
+    mark(a, c.t_data);
     finish(a, c);
 }
 
 // ============================================================ maintenance
-// Advances the flag sequence after a step of `calls` calls.  When the
-// sequence nears the top of its 32-bit range, every flag word (LL units,
-// LL128 lines, arrival flags, completion flags) is cleared and the
-// sequence restarts, so a flag value left in memory long ago can never match
-// a future call.  (The norm statistics region holds flags too.)
-__global__ __launch_bounds__(256) void k_step_end(uint32_t *ctl, uint32_t calls, char *ll,
-                                                  size_t ll_bytes, char *l128, size_t l128_bytes,
-                                                  uint32_t *done, uint32_t *stats,
-                                                  size_t stats_bytes)
+// Closes a step of `calls` calls holding `rounds` rounds: advances the call
+// count and the round sequence.  Round flags grow monotonically between
+// clears; when the sequence passes SEQ_WRAP every flag word (LL units, LL128
+// lines, arrival, barrier and completion flags, norm block sums) is cleared
+// and the sequence restarts at 0, so a flag value left in memory can never
+// match a later round.  (The host keeps a step below STEP_ROUNDS_MAX rounds,
+// so no flag of a step reaches 2^32.)
+__global__ __launch_bounds__(256) void k_step_end(uint32_t *ctl, uint32_t calls, uint32_t rounds,
+                                                  char *ll, size_t ll_bytes, char *l128,
+                                                  size_t l128_bytes, uint32_t *done,
+                                                  uint32_t *stats, size_t stats_bytes)
 {
     __shared__ uint32_t wrap;
     if (threadIdx.x == 0) {
         uint32_t s = __hip_atomic_load(ctl + CTL_SEQ, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t next = s + calls;
-        wrap = (next > 0xFFFE0000u || next < s) ? 1u : 0u;
+        uint32_t next = s + rounds;
+        wrap = (next > SEQ_WRAP || next < s) ? 1u : 0u;
     }
     __syncthreads();
     if (wrap) {
@@ -2050,9 +2108,19 @@ __global__ __launch_bounds__(256) void k_step_end(uint32_t *ctl, uint32_t calls,
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t s = __hip_atomic_load(ctl + CTL_SEQ, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(ctl + CTL_SEQ, wrap ? 0u : s + calls, __ATOMIC_RELAXED,
+        uint32_t k = __hip_atomic_load(ctl + CTL_CALLS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ctl + CTL_SEQ, wrap ? 0u : s + rounds, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ctl + CTL_CALLS, k + calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+
+// Sets the round sequence to `seq` (a test hook: lets a test run steps
+// across the sequence's restart without 2^28 steps before it).
+__global__ __launch_bounds__(64) void k_set_seq(uint32_t *ctl, uint32_t seq)
+{
+    if (threadIdx.x == 0)
+        __hip_atomic_store(ctl + CTL_SEQ, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Fills `words` uint32 words with `value` (graph-capture safe replacement
@@ -2164,12 +2232,18 @@ hipError_t launch_xcc_map(uint32_t *out, uint32_t gx, uint32_t gy, uint32_t gz, 
     return hipGetLastError();
 }
 
-hipError_t launch_step_end(uint32_t *ctl, uint32_t calls, char *ll, size_t ll_bytes, char *l128,
-                           size_t l128_bytes, uint32_t *done, uint32_t *stats, size_t stats_bytes,
-                           hipStream_t stream)
+hipError_t launch_step_end(uint32_t *ctl, uint32_t calls, uint32_t rounds, char *ll,
+                           size_t ll_bytes, char *l128, size_t l128_bytes, uint32_t *done,
+                           uint32_t *stats, size_t stats_bytes, hipStream_t stream)
 {
-    hipLaunchKernelGGL(k_step_end, dim3(1), dim3(256), 0, stream, ctl, calls, ll, ll_bytes, l128,
-                       l128_bytes, done, stats, stats_bytes);
+    hipLaunchKernelGGL(k_step_end, dim3(1), dim3(256), 0, stream, ctl, calls, rounds, ll, ll_bytes,
+                       l128, l128_bytes, done, stats, stats_bytes);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_seq(uint32_t *ctl, uint32_t seq, hipStream_t stream)
+{
+    hipLaunchKernelGGL(k_set_seq, dim3(1), dim3(64), 0, stream, ctl, seq);
     return hipGetLastError();
 }
 

@@ -49,9 +49,11 @@ template <bool LOCAL> struct Pol {
 constexpr int MAX_RANKS = 16;
 constexpr uint32_t SENT_WORD = 0xFFFFFFFFu;   // two sentinel bf16 (0xFFFF)
 
-// control block layout (uint32 words); each field on its own 128-byte line
-constexpr int CTL_SEQ = 0;          // flag-sequence base
-constexpr int CTL_STATUS = 32;      // {code, rank, source, flag}
+// control block layout (uint32 words); each field on its own 128-byte line,
+// except the two sequence words, which every launch reads together
+constexpr int CTL_SEQ = 0;          // round-sequence base: flag of a step's first round - 1
+constexpr int CTL_CALLS = 1;        // call-count base: number of calls before the step
+constexpr int CTL_STATUS = 32;      // {code, rank, source, call}
 // Workgroups are dispatched to the XCDs round-robin by workgroup index, so
 // with `parts` a multiple of XCDS part p of every rank shares an XCD.
 constexpr int XCDS = 8;
@@ -69,7 +71,15 @@ constexpr int CTL_WORDS = CTL_BAR_BOTTOM + 32 * XCDS;
 static_assert(MAX_RANKS <= 32, "one arrival line holds every rank of a copy");
 constexpr uint32_t STATUS_TIMEOUT = 6;
 constexpr uint32_t DONE_STRIDE = 8192;    // completion-flag words per rank (>= workgroups per rank)
-constexpr uint32_t TS_SUB = 64;           // timestamp sub-slots per call
+// Flags of a step stay below this value: the step-end kernel restarts the
+// round sequence (clearing every flag word) before a step could reach it,
+// and the host refuses a step of more than STEP_ROUNDS_MAX rounds, so no
+// flag wraps around 2^32 between two clears.
+constexpr uint32_t SEQ_WRAP = 0xF0000000u;
+constexpr uint32_t STEP_ROUNDS_MAX = 0x08000000u;
+// measurement records per wave: {start, first synchronisation satisfied,
+// last data store issued, end}, constant-clock ticks
+constexpr uint32_t TS_FIELDS = 4;
 
 // LL128 line group: 8 lines of 128 B = one wave-wide 16 B access; 60 chunks
 // of 8 elements carried as 56 full lanes + 8 half lanes (the lane at
@@ -86,19 +96,23 @@ struct Launch {
     char *srs;                    // sentinel 2-shot RS inbox [recv][send][parity] x s2_stride
     char *sag;                    // sentinel 2-shot AG inbox [recv][send][parity] x s2_stride
     uint32_t *ctl;                // control block (CTL_WORDS)
-    uint64_t *ts;                 // timestamps [slots][2] or null
+    uint64_t *ts;                 // timestamps [slots][ts_stride][TS_FIELDS] or null
     const uint32_t *delays;       // start delays [rows][N] ns or null
     uint32_t *done;               // two-shot DIRECT completion flags (MAX_RANKS*DONE_STRIDE words)
     char *acc;                    // atomic accumulator lines [parity] x acc_stride, zero between calls
     uint32_t ll_stride, l128_stride, s1_stride, s2_stride, acc_stride;
     uint32_t n;                   // elements per rank
     uint32_t n_ranks;
-    uint32_t epoch;
+    uint32_t epoch;               // call number within the step (1, 2, ...)
+    uint32_t rbase;               // rounds of the step's earlier calls: round j's flag is
+                                  // seq + rbase + 1 + j
     uint32_t parts;               // workgroups per rank
     uint32_t slice;               // two-shot slice length (multiple of 8)
     uint32_t watchdog_ticks;
     uint32_t xshift;              // log2 of parts per rank in a block (3, or 0): grid (2^xshift, N, parts >> xshift)
     uint32_t ts_slots;
+    uint32_t ts_stride;           // records per slot (>= waves of the launch to be recorded)
+    uint32_t ts_phases;           // nonzero: also record the two phase marks
     uint32_t delay_rows;
     uint32_t unit4;               // in-place one-shot: lanes take 4 elements (8 bytes), not 8
 };
