@@ -100,27 +100,34 @@ enum ar_proto {
 #define AR_MAX_RANKS 16
 
 /*
- * ar_init -- create the context on the current HIP device.
+ * ar_init -- create the context on the current HIP device (the C ABI's
+ * counterpart of the pages' NCCL-compatible drop-in: "SiFAR" page, section
+ * on deployment; the operation itself: "微秒必争…", section "张量并行与
+ * AllReduce").
  *   n_ranks:   number of emulated ranks, 1..16.
  *   max_elems: largest per-rank element count any later call may use, > 0,
- *              at most 2^28.  Every staging region and the output tensor are
- *              addressed with 32-bit offsets, so each must stay below 2^32
- *              bytes; the binding one is the LL region,
- *              2 * n_ranks * round_up(4 * max_elems, 256) bytes, which gives
- *              max_elems <= 2^29 / n_ranks - 64 (2^26 - 64 for 8 ranks,
- *              128 MiB of bf16 per rank).  When the one-shot sentinel inboxes
- *              (4 * n_ranks^2 * max_elems bytes) would exceed that, they are
- *              not allocated and the one-shot sentinel protocol is refused
- *              (AR_ERR_INVALID) for this context.
- * Allocates every protocol's staging (per rank x 2 parities), the flag
- * sequence word and the status record; zeroes flag words and arms sentinel
- * buffers with 0xFFFF.  Synchronous.
+ *              rounded up to a multiple of 8.  All n_ranks output copies of
+ *              the binary32 debug path must span at most 2^31 bytes, which
+ *              gives max_elems <= 2^29 / n_ranks (2^26 for 8 ranks, 128 MiB
+ *              of bf16 per rank).
+ * Allocates every protocol's staging: fixed-size windows per rank (LL,
+ * LL128) or per (receiver, sender) inbox pair (sentinel) and buffer, of
+ * min(what a max_elems message needs in one round, 1 MiB (LL, LL128) or
+ * 256 KiB (sentinel)) -- larger messages walk their rounds through them
+ * (ar_set_staging) -- plus the two sequence words, the status record and the
+ * flag words of the arrival, completion and barrier handshakes; zeroes flag
+ * words and arms sentinel buffers with 0xFFFF.  Synchronous.
+ * Start-up defaults may come from the environment: AR_ALGO (auto, oneshot,
+ * twoshot), AR_PROTO (auto, ll, ll128, sentinel, direct, barrier, atomic)
+ * and AR_WATCHDOG_MS (a positive integer), as NCCL reads NCCL_ALGO and
+ * NCCL_PROTO; a value that does not parse, or an impossible pair, fails.
  * The kernels' timers (watchdog budgets, start delays, call timestamps)
  * count the device's constant clock at 100 MHz, the rate MI355X reports as
  * hipDeviceAttributeWallClockRate; a device reporting another rate is
  * refused.
- * Errors: AR_ERR_INVALID (bad sizes, or a constant clock other than
- * 100 MHz), AR_ERR_STATE (already initialised), AR_ERR_OOM, AR_ERR_HIP.
+ * Errors: AR_ERR_INVALID (bad sizes, a bad environment override, or a
+ * constant clock other than 100 MHz), AR_ERR_STATE (already initialised),
+ * AR_ERR_OOM, AR_ERR_HIP.
  */
 int ar_init(int n_ranks, size_t max_elems);
 
@@ -263,6 +270,25 @@ int ar_set_launch(int wgs_per_rank, int threads);
 int ar_set_scope(int scope);
 
 /*
+ * ar_set_staging -- size of the staging window the staged protocols walk
+ * their rounds through (the double buffering of "微秒必争…", section
+ * "四大核心机制", item 3: a message larger than one exchange goes in rounds
+ * through buffers 0 and 1, and receiving a peer's round k permits
+ * overwriting the buffer of round k-1).  ar_init allocates, per rank and
+ * buffer, min(what the largest message needs, 1 MiB) for LL and LL128, and
+ * per (receiver, sender) inbox and buffer min(need, 256 KiB) for the
+ * sentinel protocol; this call limits the window actually used to
+ * window_bytes (a multiple of 1024, at least 4096; 0 = the whole
+ * allocation).  Each call then runs as many parts as one round of each fits
+ * the window (1 KiB per part and round; LL128: 1 KiB per line group of a
+ * batch) and as many rounds as the message needs; round j of a call uses
+ * buffer (f + j) & 1 with flag f + j, where f is the call's first flag.
+ * Takes effect for the following calls.  Errors: AR_ERR_NOT_INIT,
+ * AR_ERR_INVALID.
+ */
+int ar_set_staging(size_t window_bytes);
+
+/*
  * ar_set_watchdog -- per-poll time budget in microseconds (default 200000).
  * A poll that exceeds it records {6, rank, source, flag} in the device status
  * record and its workgroup stops (in the fused norm's wait for the row's
@@ -359,7 +385,9 @@ int ar_last_hip_error(void);
 long long ar_query(int key, size_t n);
 /*   (continued) 12 rounds (flags) a call of n elements would take, 13 rounds of
  *   the open step so far, 14 the device round sequence (n == 0) or call count
- *   (n != 0), read after a device synchronisation. */
+ *   (n != 0), read after a device synchronisation, 15 the staging window
+ *   (bytes per rank or inbox pair and buffer) the protocol of a call of n
+ *   elements walks (0 for protocols without staging). */
 
 #ifdef __cplusplus
 }

@@ -217,3 +217,88 @@ def test_protocol_switch_between_calls():
         torch.cuda.synchronize()
         check_status_clean()
     assert int(bad.item()) == 0
+
+
+# ---- fixed-size staging: the workloads with windows far smaller than their
+# messages, so every call walks many rounds through the two buffers and each
+# buffer is overwritten within a call (the double buffer's permit at work)
+
+def _rounds(ar, n):
+    return ar.query(12, n)
+
+
+def test_config2_graph_small_window_rounds():
+    """16 KiB LL messages through a 4 KiB window: 8 rounds per call, 160
+    calls per graph, every call of every replay checked."""
+    log("config 2, LL, 4 KiB window")
+    sets = Sets(2, 4)
+    with ar_context(8, sets.n, ONE, LL) as ar:
+        ar.set_staging(4096)
+        assert ar.query(15, sets.n) == 4096 and _rounds(ar, sets.n) == 8
+        bad = _graph_steps(ar, sets, replays=5)
+        check_status_clean()
+    assert bad == 0
+
+
+@pytest.mark.parametrize("algo", [ONE, TWO], ids=["oneshot", "twoshot"])
+def test_config3_ll128_small_window(algo):
+    """512 KiB LL128 messages through a 16 KiB window (the one-shot's lines
+    are 546 KiB per rank, the two-shot's 68 KiB per slice)."""
+    log("config 3, LL128, 16 KiB window, algo %d" % algo)
+    sets = Sets(3, 4)
+    with ar_context(8, sets.n, algo, LL128) as ar:
+        ar.set_staging(16384)
+        assert _rounds(ar, sets.n) >= 3
+        bad = _graph_steps(ar, sets, replays=2)
+        check_status_clean()
+    assert bad == 0
+
+
+@pytest.mark.parametrize("algo,proto", [(TWO, LL128), (TWO, SENT), (ONE, LL128)],
+                         ids=["twoshot-ll128", "twoshot-sentinel", "oneshot-ll128"])
+def test_config4_small_window(algo, proto):
+    """4 MiB messages through a 64 KiB window (64 times smaller than the
+    message), 8 rotating buffer sets."""
+    log("config 4, 64 KiB window, algo %d proto %d" % (algo, proto))
+    sets = Sets(4, 8)
+    with ar_context(8, sets.n, algo, proto) as ar:
+        ar.set_staging(65536)
+        assert ar.query(15, sets.n) == 65536 and _rounds(ar, sets.n) >= 8
+        bad = _stream_calls(ar, sets, 24, nbuf=2)
+        check_status_clean()
+    assert bad == 0
+
+
+@pytest.mark.parametrize("algo", [TWO, ONE], ids=["twoshot", "oneshot"])
+def test_config5_delays_small_window_10000_calls(algo):
+    """16 ranks with seeded 0-5 us start delays, 10,000 calls, sentinel
+    inboxes of 4 KiB per pair and buffer (the one-shot's 112 KiB messages take
+    28 rounds per call, the two-shot's 7 KiB slices 2)."""
+    log("config 5, sentinel, 4 KiB window, algo %d" % algo)
+    torch = torch_mod()
+    sets = Sets(5, 8)
+    calls = 10000
+    delays = torch.from_numpy(synth.delays_ns(5, calls).view(np.int32).copy()).to("cuda:0")
+    with ar_context(16, sets.n, algo, SENT) as ar:
+        ar.set_staging(4096)
+        assert _rounds(ar, sets.n) >= 2
+        ar.set_delays(delays, calls)
+        bad = _stream_calls(ar, sets, calls, nbuf=8)
+        ar.set_delays(None, 0)
+        check_status_clean()
+    assert bad == 0
+
+
+def test_staging_window_validation():
+    import tp_decode_comms_amd as arm
+    with ar_context(8, 1 << 20) as ar:
+        lib = arm.lib()
+        assert lib.ar_set_staging(1024) == arm.ar.AR_ERR_INVALID       # below 4 KiB
+        assert lib.ar_set_staging(5000) == arm.ar.AR_ERR_INVALID       # not a multiple of 1 KiB
+        assert lib.ar_set_staging(8192) == 0
+        ar.set_options(ONE, LL)
+        assert ar.query(15, 8192) == 8192
+        ar.set_staging(0)
+        assert ar.query(15, 8192) == 1 << 20                         # LL: 1 MiB per rank, buffer
+        ar.set_options(TWO, DIRECT)
+        assert ar.query(15, 8192) == 0                                # no staging

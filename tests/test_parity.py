@@ -48,19 +48,25 @@ def _run_calls(ar, datas, n, calls, out_list=None, f32=False):
 
 
 SCOPES = [("auto", 0), ("device", 1)]
+WINDOWS = [("window-all", 0), ("window-4k", 4096)]
 
 
+@pytest.mark.parametrize("win_name,window", WINDOWS, ids=[w[0] for w in WINDOWS])
 @pytest.mark.parametrize("scope_name,scope", SCOPES, ids=[s[0] for s in SCOPES])
 @pytest.mark.parametrize("name,algo,proto", VARIANTS, ids=[v[0] for v in VARIANTS])
 @pytest.mark.parametrize("N,n", [(8, 8192), (8, 4096 + 8), (4, 20008), (2, 968), (16, 3592),
                                  (8, 262144 + 480 * 3 + 16)])
-def test_variant_matches_oracle(name, algo, proto, N, n, scope_name, scope):
+def test_variant_matches_oracle(name, algo, proto, N, n, scope_name, scope, win_name, window):
     """Every variant in both coherence scopes: XCD-local (auto, where the
-    placement allows it) and device scope."""
-    log("variant %s N=%d n=%d scope=%s" % (name, N, n, scope_name))
+    placement allows it) and device scope; the staged protocols with their
+    whole staging window and with a 4 KiB window, which walks the larger
+    messages in many rounds through the two buffers (the window does not
+    apply to the protocols without staging)."""
+    log("variant %s N=%d n=%d scope=%s %s" % (name, N, n, scope_name, win_name))
     datas = [synth.random_bits(1000 + 10 * s + N, (N, n), finite_only=True, avoid=0xFFFF)
              for s in range(3)]
     with ar_context(N, n + 64, algo, proto, scope=scope) as ar:
+        ar.set_staging(window)
         outs = _run_calls(ar, datas, n, 6)
         check_status_clean()
     for k, out in enumerate(outs):

@@ -41,6 +41,7 @@ _SIGS = {
     "ar_set_options": (_c_int, [_c_int, _c_int]),
     "ar_set_launch": (_c_int, [_c_int, _c_int]),
     "ar_set_scope": (_c_int, [_c_int]),
+    "ar_set_staging": (_c_int, [_c_size]),
     "ar_set_watchdog": (_c_int, [_c_u32]),
     "ar_step_end": (_c_int, [_c_vp]),
     "ar_set_delays": (_c_int, [_c_vp, _c_size]),
@@ -187,6 +188,11 @@ def set_launch(wgs_per_rank=0, threads=0):
 
 def set_scope(scope=AR_SCOPE_AUTO):
     return _check("ar_set_scope", lib().ar_set_scope(int(scope)))
+
+
+def set_staging(window_bytes=0):
+    """Staging window (bytes per rank or inbox pair and buffer; 0 = all)."""
+    return _check("ar_set_staging", lib().ar_set_staging(int(window_bytes)))
 
 
 def set_watchdog(budget_us=0):

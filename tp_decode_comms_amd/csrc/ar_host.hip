@@ -44,6 +44,18 @@ constexpr uint64_t ONESHOT_DIRECT_MAX_PARTS = 128;
 constexpr size_t ONESHOT_UNIT4_MAX_BYTES = 64 * 1024;
 // rate of the constant clock the kernels' timers count (100 MHz)
 constexpr int WALL_CLOCK_KHZ = 100000;
+// Fixed-size staging (the double buffering of "微秒必争…", section
+// "四大核心机制", item 3; NCCL's bounded NCCL_BUFFSIZE on the "vLLM 分布式推理
+// 核心" page, section 四): each staged protocol gets a window per rank (LL,
+// LL128) or per (receiver, sender) pair (sentinel inboxes) and buffer, at
+// most these sizes, whatever max_elems is; larger messages are walked in
+// rounds through the two buffers.  One round of one part takes 1 KiB of a
+// window (LL: 64 chunks of 4 elements as 16-byte units; sentinel: 64 chunks
+// of 8 elements; LL128: one 1-KiB line group per wave of the batch).
+constexpr size_t STAGE_WINDOW_MAX = 1024 * 1024;       // LL, LL128: per rank and buffer
+constexpr size_t STAGE_INBOX_MAX = 256 * 1024;         // sentinel: per pair and buffer
+constexpr size_t STAGE_ROUND_BYTES = 1024;             // one part's round (per line group for LL128)
+constexpr size_t STAGE_WINDOW_MIN = 4096;              // a whole LL128 batch of 4 groups
 size_t oneshot_limit(int proto)
 {
     switch (proto) {
@@ -70,6 +82,7 @@ struct Context {
     uint32_t *stats = nullptr;          // fused norm: per-block sums of squares {sum, flag}
     char *acc = nullptr;  size_t acc_stride = 0;   // atomic lines, per parity
     size_t stats_stride = 0;            // entries per rank
+    size_t window = 0;                  // staging window in use (0: the whole allocation)
     // options
     int algo = AR_ALGO_AUTO;
     int proto = AR_PROTO_AUTO;
@@ -282,6 +295,23 @@ struct Plan {
 
 uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
+// The staging window a kind walks its rounds through (bytes per rank, or per
+// inbox pair, and buffer), 0 for kinds without staging.
+size_t window_of(int kind)
+{
+    size_t alloc = 0;
+    switch (kind) {
+    case ar::K_ONESHOT_LL:
+    case ar::K_ONESHOT_LL_NORM: alloc = g.ll_stride; break;
+    case ar::K_ONESHOT_LL128:
+    case ar::K_TWOSHOT_LL128: alloc = g.l128_stride; break;
+    case ar::K_ONESHOT_SENTINEL: alloc = g.s1_stride; break;
+    case ar::K_TWOSHOT_SENTINEL: alloc = g.s2_stride; break;
+    default: return 0;
+    }
+    return g.window != 0 && g.window < alloc ? g.window : alloc;
+}
+
 // Rounds a call walks: the loop count of its part 0 (every part walks at
 // most as many).  Kinds without rounds take one flag.
 uint32_t rounds_of(const Plan &p, size_t n)
@@ -320,7 +350,6 @@ int choose_kind(size_t n, int *kind)
         case AR_PROTO_LL: *kind = ar::K_ONESHOT_LL; return AR_OK;
         case AR_PROTO_LL128: *kind = ar::K_ONESHOT_LL128; return AR_OK;
         case AR_PROTO_SENTINEL:
-            if (g.s1 == nullptr) return AR_ERR_INVALID;   // inbox region too large
             *kind = ar::K_ONESHOT_SENTINEL; return AR_OK;
         case AR_PROTO_DIRECT: *kind = ar::K_ONESHOT_DIRECT; return AR_OK;
         case AR_PROTO_BARRIER: *kind = ar::K_ONESHOT_BARRIER; return AR_OK;
@@ -421,6 +450,14 @@ int plan_geometry(size_t n, bool f32, Plan *p)
         cap /= 2;
         if (cap > ar::DONE_STRIDE)
             cap = ar::DONE_STRIDE;
+    }
+    // one round of every part must fit the staging window
+    const size_t win = window_of(p->kind);
+    if (win != 0) {
+        const size_t round_bytes = STAGE_ROUND_BYTES * (l128 ? (size_t)p->gw : 1);
+        const size_t win_parts = win / round_bytes;
+        if (win_parts < cap)
+            cap = (uint32_t)win_parts;
     }
     if (cap == 0)
         return AR_ERR_INVALID;
@@ -739,28 +776,32 @@ int ar_init(int n_ranks, size_t max_elems)
     g.n_ranks = n_ranks;
     g.max_elems = round_up(max_elems, 8);
     const size_t me = g.max_elems;
-    g.ll_stride = round_up(me * 4, 256);
-    g.l128_stride = round_up((me + ar::L128_ELEMS - 1) / ar::L128_ELEMS * ar::L128_BYTES, 256);
-    g.s1_stride = round_up(me * 2, 256);
-    g.s2_stride = round_up(slice_len(me, n_ranks) * 2, 256);
+    // staging windows: what the largest message needs in one round, at most
+    // the fixed window sizes (larger messages take several rounds)
+    auto window = [](size_t need, size_t most) {
+        return std::max(STAGE_WINDOW_MIN, std::min(round_up(need, STAGE_WINDOW_MIN), most));
+    };
+    g.ll_stride = window(me * 4, STAGE_WINDOW_MAX);
+    g.l128_stride = window((me + ar::L128_ELEMS - 1) / ar::L128_ELEMS * ar::L128_BYTES,
+                           STAGE_WINDOW_MAX);
+    g.s1_stride = window(me * 2, STAGE_INBOX_MAX);
+    g.s2_stride = window(slice_len(me, n_ranks) * 2, STAGE_INBOX_MAX);
+    g.window = 0;
     g.stats_stride = (me + ar::NORM_BLOCK_ELEMS - 1) / ar::NORM_BLOCK_ELEMS;
     g.acc_stride = round_up((me + ar::ATOM_LINE_ELEMS - 1) / ar::ATOM_LINE_ELEMS * 128, 256);
-    // every staging region and the output tensor are addressed through one
-    // buffer descriptor with 32-bit offsets; a region that would not fit is
-    // not allocated and its protocol is unavailable for this context
-    if (me * (size_t)n_ranks * 4 > REGION_LIMIT || ll_bytes() > REGION_LIMIT ||
-        l128_bytes() > REGION_LIMIT || s2_bytes() > REGION_LIMIT || acc_bytes() > REGION_LIMIT)
-        return AR_ERR_INVALID;
     // the kernels skip a load or store by sending it to offset ar::OFF_NONE,
     // which must lie past the end of every input and output descriptor (the
-    // largest is all N output copies in binary32); the LL region bound above
-    // already implies it
-    if (me * (size_t)n_ranks * 4 > (size_t)ar::OFF_NONE)
+    // largest is all N output copies in binary32: the binding size limit);
+    // the staging windows are bounded far below it, and the atomic lines
+    // (128 bytes per 31 elements, two buffers) stay below it too
+    if (me * (size_t)n_ranks * 4 > (size_t)ar::OFF_NONE || acc_bytes() > (size_t)ar::OFF_NONE ||
+        ll_bytes() > REGION_LIMIT || l128_bytes() > REGION_LIMIT || s1_bytes() > REGION_LIMIT ||
+        s2_bytes() > REGION_LIMIT)
         return AR_ERR_INVALID;
     int rc;
     if ((rc = alloc(&g.ll, ll_bytes())) != AR_OK ||
         (rc = alloc(&g.l128, l128_bytes())) != AR_OK ||
-        (s1_bytes() <= REGION_LIMIT && (rc = alloc(&g.s1, s1_bytes())) != AR_OK) ||
+        (rc = alloc(&g.s1, s1_bytes())) != AR_OK ||
         (rc = alloc(&g.srs, s2_bytes())) != AR_OK ||
         (rc = alloc(&g.sag, s2_bytes())) != AR_OK ||
         (rc = alloc((char **)&g.ctl, ar::CTL_WORDS * 4)) != AR_OK ||
@@ -883,6 +924,16 @@ int ar_set_scope(int scope)
     if (scope != AR_SCOPE_AUTO && scope != AR_SCOPE_DEVICE)
         return AR_ERR_INVALID;
     g.scope = scope;
+    return AR_OK;
+}
+
+int ar_set_staging(size_t window_bytes)
+{
+    if (!g.live)
+        return AR_ERR_NOT_INIT;
+    if (window_bytes != 0 && (window_bytes < STAGE_WINDOW_MIN || window_bytes % STAGE_ROUND_BYTES))
+        return AR_ERR_INVALID;
+    g.window = window_bytes;            // each call plans its own rounds: any time
     return AR_OK;
 }
 
@@ -1054,6 +1105,11 @@ long long ar_query(int key, size_t n)
         return rc != AR_OK ? rc : (long long)p.rounds;
     }
     case 13: return (long long)g.step_rounds;
+    case 15: {
+        int kind;
+        if (n == 0 || choose_kind(n, &kind) != AR_OK) return AR_ERR_INVALID;
+        return (long long)window_of(kind);
+    }
     case 14: {
         uint32_t w[2] = {0, 0};
         hipError_t e = hipDeviceSynchronize();

@@ -281,8 +281,19 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
 // ============================================================ one-shot LL
 // Lane work unit: 4 elements (8 bytes of input) = one 16-byte LL store of
 // two units {2 bf16, flag}.  Rank r publishes once into its own mailbox
-// [r][parity]; every rank reads it.  All mailboxes sit in one region
-// [rank][parity] x ll_stride under one descriptor.
+// [r][buffer]; every rank reads it.  All mailboxes sit in one region
+// [rank][2 buffers] x ll_stride under one descriptor.
+//
+// Fixed-size staging, walked in rounds (the double buffering of the pages'
+// item 3): the host caps the parts so that one round of every part -- 64
+// chunks x 16 bytes each -- fits a rank's window; round j of part p uses
+// window bytes [1024 p, 1024 (p+1)) of buffer (flag + j) & 1 with flag
+// flag + j.  A part publishes round j+1 only after it has received round j
+// from every peer, and each peer published round j only after receiving
+// round j-1: so a receipt of round j is the permit to overwrite round j-1's
+// buffer, and no reader ever finds its round's data overwritten.  Every
+// round carries its own flag, so the stale round j-2 data a reader may find
+// in the buffer never validates.
 //
 // A workgroup of W >= N waves (one per rank, a power of two) owns 64
 // chunks per round.  Wave 0 loads the input and publishes it; once the
@@ -301,17 +312,19 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
 template <int NMAX, bool LOCAL, bool SPLIT, typename Epi>
 __device__ __forceinline__ bool ll_round(const Launch &a, Ctx0 &c, const Ctl &ctl,
                                          __amdgpu_buffer_rsrc_t llr, uint32_t ch, uint32_t C,
-                                         u32x2 x, u32x2 (*stage)[64], uint32_t *failed, Epi &&epi)
+                                         uint32_t j, u32x2 x, u32x2 (*stage)[64], uint32_t *failed,
+                                         Epi &&epi)
 {
     const uint32_t N = a.n_ranks;
     const uint32_t rb = a.ll_stride;
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const uint32_t lane_off = ch * 16u + c.par * rb;
+    const uint32_t fj = c.flag + j;                 // this round's flag and buffer
+    const uint32_t lane_off = (c.part * 64u + lane) * 16u + (fj & 1u) * rb;
     const bool active = ch < C;
     // publish (send/bcast): one copy, read by all N ranks
     if (wave == 0u) {
         if (active)
-            st16<Pol<LOCAL>::ST>(ll_pack(x.x, x.y, c.flag), llr, lane_off + c.rank * 2u * rb);
+            st16<Pol<LOCAL>::ST>(ll_pack(x.x, x.y, fj), llr, lane_off + c.rank * 2u * rb);
         stage[c.rank][lane] = x;
         wait_stores();
     }
@@ -333,7 +346,7 @@ __device__ __forceinline__ bool ll_round(const Launch &a, Ctx0 &c, const Ctl &ct
     while (true) {
         compiler_fence();
         A1 = ld16<Pol<LOCAL>::LD>(llr, pend ? src : OFF_NONE);
-        if (pend && ll_ready(A0, c.flag)) {
+        if (pend && ll_ready(A0, fj)) {
             pend = false;
             stage[wave][lane] = u32x2{A0.x, A0.z};
         }
@@ -345,7 +358,7 @@ __device__ __forceinline__ bool ll_round(const Launch &a, Ctx0 &c, const Ctl &ct
         }
         compiler_fence();
         A0 = ld16<Pol<LOCAL>::LD>(llr, pend ? src : OFF_NONE);
-        if (pend && ll_ready(A1, c.flag)) {
+        if (pend && ll_ready(A1, fj)) {
             pend = false;
             stage[wave][lane] = u32x2{A1.x, A1.z};
         }
@@ -435,14 +448,15 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll(const Launch a)
         if (cnt == 4) store4<F32>(o, cch * 4u, v);
         else store2<F32>(o, cch * 4u + 2u * w, v);
     };
-    if (!ll_round<NMAX, LOCAL, true>(a, c, ctl, llr, ch, C, x, stage, &failed, out))
+    if (!ll_round<NMAX, LOCAL, true>(a, c, ctl, llr, ch, C, 0u, x, stage, &failed, out))
         return;
     // later rounds while the workgroup has chunks left (the same rounds for
     // every peer of the part)
-    for (uint32_t base = c.part * 64u + step; base < C; base += step) {
+    uint32_t j = 1;
+    for (uint32_t base = c.part * 64u + step; base < C; base += step, ++j) {
         ch += step;
         x = (wave == 0u && ch < C) ? ld8<CP_PLAIN>(inr, ch * 8u) : u32x2{0u, 0u};
-        if (!ll_round<NMAX, LOCAL, true>(a, c, ctl, llr, ch, C, x, stage, &failed, out))
+        if (!ll_round<NMAX, LOCAL, true>(a, c, ctl, llr, ch, C, j, x, stage, &failed, out))
             return;
     }
     mark(a, c.t_data);
@@ -558,7 +572,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
             st8<CP_DEV>(e, sr, (c.rank * L.stats_stride + (cch >> 6)) * 8u);
         }
     };
-    if (!ll_round<NMAX, LOCAL, false>(a, c, ctl, llr, ch, C, x, stage, &failed, epi))
+    if (!ll_round<NMAX, LOCAL, false>(a, c, ctl, llr, ch, C, 0u, x, stage, &failed, epi))
         return;
     const u32x2 h0 = hk;
     for (uint32_t it = 1; it < rounds; ++it) {
@@ -566,7 +580,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
         const bool ld = wave == 0u && ch < C;
         x = ld ? ld8<CP_PLAIN>(inr, ch * 8u) : u32x2{0u, 0u};
         rw = ld ? ld8<CP_PLAIN>(resr, ch * 8u) : u32x2{0u, 0u};
-        if (!ll_round<NMAX, LOCAL, false>(a, c, ctl, llr, ch, C, x, stage, &failed, epi))
+        if (!ll_round<NMAX, LOCAL, false>(a, c, ctl, llr, ch, C, it, x, stage, &failed, epi))
             return;
     }
     // normalise (wave 0; the other waves go straight to finish's barrier)
@@ -846,10 +860,13 @@ __global__ __launch_bounds__(1024) void k_oneshot_rows_norm(const NormLaunch L)
 
 // ======================================================= one-shot sentinel
 // Push model: rank q writes chunk c of its input into every peer's inbox
-// [peer][q][parity]; each receiver polls its own inbox until no element is
-// the sentinel, reduces, and re-arms the slots it consumed.  The receipt of
-// a peer's call-k data proves the peer finished call k-1 (double buffering),
-// so the re-arm of parity k&1 always lands before the peer's call k+2 write.
+// [peer][q][buffer]; each receiver polls its own inbox until no element is
+// the sentinel, reduces, and re-arms the slots it consumed.  Inboxes are
+// fixed-size windows walked in rounds as in the LL kernel (round j of part p:
+// window bytes [1024 p, 1024 (p+1)) of buffer (flag + j) & 1).  The receipt
+// of a peer's round-j data proves the peer finished round j-1, re-arm
+// included (each round ends with its re-arm stores acknowledged), so the
+// re-arm of a buffer always lands before the peer's round j+2 write into it.
 //
 // As in the one-shot LL kernel, a workgroup of SENT_WAVES = 8 waves owns 64
 // chunks (of 8 elements) per round and the peers are split over the waves:
@@ -866,17 +883,17 @@ template <int NMAX, bool F32, bool LOCAL>
 __device__ __forceinline__ bool sent_round(const Launch &a, Ctx0 &c, const Ctl &ctl,
                                            __amdgpu_buffer_rsrc_t box,
                                            __amdgpu_buffer_rsrc_t o, uint32_t ch, uint32_t G,
-                                           u32x4 x, u32x4 (*stage)[64], uint32_t *failed)
+                                           uint32_t rnd, bool more, u32x4 x,
+                                           u32x4 (*stage)[64], uint32_t *failed)
 {
     constexpr int PW = (NMAX + SENT_WAVES - 1) / SENT_WAVES;
     const uint32_t N = a.n_ranks;
     const uint32_t sb = a.s1_stride;
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const bool active = ch < G;
-    // inboxes [recv][send][parity] x s1_stride under one descriptor
-    auto slot = [&](uint32_t recv, uint32_t send) {
-        return ch * 16u + c.par * sb + ((recv * N + send) * 2u) * sb;
-    };
+    // inboxes [recv][send][buffer] x s1_stride under one descriptor
+    const uint32_t win = (c.part * 64u + lane) * 16u + ((c.flag + rnd) & 1u) * sb;
+    auto slot = [&](uint32_t recv, uint32_t send) { return win + ((recv * N + send) * 2u) * sb; };
     uint32_t pend = 0;
 #pragma unroll
     for (int j = 0; j < PW; ++j) {
@@ -956,12 +973,16 @@ __device__ __forceinline__ bool sent_round(const Launch &a, Ctx0 &c, const Ctl &
     // flight, whose registers stay reserved until here) before the next
     // round's pushes
 #pragma unroll
-    for (int j = 0; j < PW; ++j)
-        if ((mine >> j) & 1u)
-            st16<Pol<LOCAL>::ST>(sentinel4(), box, slot(c.rank, wave + (uint32_t)(SENT_WAVES * j)));
+    for (int k = 0; k < PW; ++k)
+        if ((mine >> k) & 1u)
+            st16<Pol<LOCAL>::ST>(sentinel4(), box, slot(c.rank, wave + (uint32_t)(SENT_WAVES * k)));
 #pragma unroll
-    for (int j = 0; j < PW; ++j)
-        asm volatile("" ::"v"(A0[j]), "v"(A1[j]));
+    for (int k = 0; k < PW; ++k)
+        asm volatile("" ::"v"(A0[k]), "v"(A1[k]));
+    // before this part's next round pushes anything, its re-arms are
+    // performed: a peer's reuse of these slots follows its receipt of that push
+    if (more)
+        wait_stores();
     __syncthreads();                                // the tile is reused next round
     return true;
 }
@@ -989,12 +1010,14 @@ __global__ __launch_bounds__(512) void k_oneshot_sentinel(const Launch a)
     const __amdgpu_buffer_rsrc_t box = rsrc(a.s1, a.n_ranks * a.n_ranks * 2u * a.s1_stride);
     start_delay(a, c);
     // round 0 straight-line (see the one-shot LL kernel), later rounds looped
-    if (!sent_round<NMAX, F32, LOCAL>(a, c, ctl, box, o, ch, G, x, stage, &failed))
+    if (!sent_round<NMAX, F32, LOCAL>(a, c, ctl, box, o, ch, G, 0u, rounds > 1u, x, stage,
+                                      &failed))
         return;
     for (uint32_t it = 1; it < rounds; ++it) {
         ch += step;
         x = ch < G ? ld16<CP_PLAIN>(inr, ch * 16u) : u32x4{0u, 0u, 0u, 0u};
-        if (!sent_round<NMAX, F32, LOCAL>(a, c, ctl, box, o, ch, G, x, stage, &failed))
+        if (!sent_round<NMAX, F32, LOCAL>(a, c, ctl, box, o, ch, G, it, it + 1u < rounds, x, stage,
+                                          &failed))
             return;
     }
     mark(a, c.t_data);
@@ -1440,8 +1463,9 @@ __device__ __forceinline__ bool l128_flag_ok(u32x2 f, uint32_t flag)
     return f.x == flag && f.y == ~flag;
 }
 
-// Receives the GW line groups g[k] (valid when bit k of gvalid) from this
-// wave's peers s = wave + 4j (PW slots; bit j of pmask marks a real peer):
+// Receives the GW line groups g[k] (valid when bit k of gvalid; staged in
+// window slots slot0 + k of buffer `par`) from this wave's peers
+// s = wave + 4j (PW slots; bit j of pmask marks a real peer):
 // flag lanes poll the line flags of every (group, peer) still pending, the
 // wave votes, then every lane loads its payloads into V[k][j].  lim[j] is
 // the number of valid elements of peer j in group index space; a line is
@@ -1449,16 +1473,17 @@ __device__ __forceinline__ bool l128_flag_ok(u32x2 f, uint32_t flag)
 // expiry.
 template <int GW, int PW, bool LOCAL>
 __device__ __forceinline__ bool l128_recv(__amdgpu_buffer_rsrc_t reg, uint32_t rb, uint32_t par,
-                                          const uint32_t *g, uint32_t gvalid, uint32_t pmask,
+                                          uint32_t slot0, const uint32_t *g, uint32_t gvalid,
+                                          uint32_t pmask,
                                           uint32_t wave, uint32_t lane, const L128Lane &ln,
                                           const uint32_t *lim, uint32_t flag, const Ctl &ctl,
                                           uint32_t rank, uint32_t call, uint32_t budget,
                                           u32x4 (*V)[PW])
 {
-    // peer s's lines of group g: reg + (s*2 + par)*rb + g*1024 + lane*16
+    // peer s's lines of group k: reg + (s*2 + par)*rb + (slot0 + k)*1024 + lane*16
     auto off = [&](int k, int j) {
-        return ((wave + (uint32_t)(L128_WAVES * j)) * 2u + par) * rb + g[k] * L128_BYTES +
-               lane * 16u;
+        return ((wave + (uint32_t)(L128_WAVES * j)) * 2u + par) * rb +
+               (slot0 + (uint32_t)k) * L128_BYTES + lane * 16u;
     };
     // Flag polls and payload loads are issued by every lane for every
     // (group, peer) slot, those with nothing to read at OFF_NONE (zeros, no
@@ -1531,11 +1556,16 @@ __device__ __forceinline__ void store_lane(__amdgpu_buffer_rsrc_t o, uint32_t e,
 }
 
 // ====================================================== one-shot LL128
-// Rank r publishes its whole input as line groups.  Batch b of a workgroup
-// covers groups (part + b*parts)*GW + k, k < GW; wave k < GW publishes
+// Rank r publishes its whole input as line groups.  Batch j of a workgroup
+// covers groups (part + j*parts)*GW + k, k < GW; wave k < GW publishes
 // group k.  Every wave receives the batch from its peers into an LDS tile
 // [N][GW][64 lanes]; after a workgroup barrier each publishing wave reduces
-// its group in global rank order and writes it.
+// its group in global rank order and writes it.  Staging is a fixed window
+// per rank walked in rounds (one batch per part per round) as in the LL
+// kernel: batch j of part p sits in window slots p*GW .. p*GW + GW-1 of
+// buffer (flag + j) & 1 with flag flag + j, and the workgroup barrier that
+// ends a batch (every wave has received it) comes before the next batch's
+// publish, which is the double buffer's permit.
 template <int NMAX, bool F32, bool LOCAL, int GW>
 __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 {
@@ -1556,7 +1586,7 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
     const uint32_t rb = a.l128_stride;
     const __amdgpu_buffer_rsrc_t reg = rsrc(a.l128, N * 2u * rb);
-    const uint32_t mine_off = (c.rank * 2u + c.par) * rb;
+    const uint32_t slot0 = c.part * (uint32_t)GW;  // this part's window slots
     uint32_t pmask = 0, lim[PW];
 #pragma unroll
     for (int j = 0; j < PW; ++j) {
@@ -1569,7 +1599,10 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
         failed = 0u;
     start_delay(a, c);
 
-    for (uint32_t b = c.part; b < batches; b += a.parts) {
+    uint32_t rnd = 0;
+    for (uint32_t b = c.part; b < batches; b += a.parts, ++rnd) {
+        const uint32_t fj = c.flag + rnd, bj = fj & 1u;      // this round's flag and buffer
+        const uint32_t mine_off = (c.rank * 2u + bj) * rb;
         uint32_t g[GW];
         uint32_t gvalid = 0;
 #pragma unroll
@@ -1586,16 +1619,17 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
         if (pub) {
             if (em < a.n)
                 x = ld_elems(inr, em, ln.half);
-            l128_store_payload<LOCAL>(reg, mine_off + gm * L128_BYTES + lane * 16u, ln.half, x);
+            const uint32_t lo = mine_off + (slot0 + wave) * L128_BYTES + lane * 16u;
+            l128_store_payload<LOCAL>(reg, lo, ln.half, x);
             wait_stores();
             if (ln.half)
-                l128_store_flag<LOCAL>(reg, mine_off + gm * L128_BYTES + lane * 16u, c.flag);
+                l128_store_flag<LOCAL>(reg, lo, fj);
             stage[c.rank][wave][lane] = x;
         }
         // receive the batch from this wave's peers
         u32x4 V[GW][PW];
-        if (!l128_recv<GW, PW, LOCAL>(reg, rb, c.par, g, gvalid, pmask, wave, lane, ln, lim,
-                                      c.flag, ctl, c.rank, c.call, a.watchdog_ticks, V))
+        if (!l128_recv<GW, PW, LOCAL>(reg, rb, bj, slot0, g, gvalid, pmask, wave, lane, ln, lim,
+                                      fj, ctl, c.rank, c.call, a.watchdog_ticks, V))
             failed = 1u;                            // every wave still meets the barrier
         mark_once(a, c.t_sync);
 #pragma unroll
@@ -1632,9 +1666,11 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 // Reduce-scatter: rank q reduces slice q (elements [q*L, q*L + Lq)) reading
 // every rank's input in place after the arrival flags, and publishes the
 // bf16 result as line groups.  All-gather: rank q receives every slice's
-// groups (its own from registers) and writes them to out[q].  Batches and
-// publishing waves as in the one-shot kernel; wave w receives the batch of
-// the slices of the peers s with s % 4 == w straight into out[q].
+// groups (its own from registers) and writes them to out[q].  Batches,
+// publishing waves and the staging window as in the one-shot kernel; wave w
+// receives the batch of the slices of the peers s with s % 4 == w straight
+// into out[q], and the waves meet at a barrier before the next batch is
+// published (its permit: every wave has received this batch).
 template <int NMAX, bool F32, bool LOCAL, int GW>
 __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 {
@@ -1666,7 +1702,7 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, q, F32);
     const uint32_t rb = a.l128_stride;
     const __amdgpu_buffer_rsrc_t reg = rsrc(a.l128, N * 2u * rb);
-    const uint32_t mine_off = (q * 2u + c.par) * rb;
+    const uint32_t slot0 = c.part * (uint32_t)GW;  // this part's window slots
     uint32_t pmask = 0, lim[PW];
 #pragma unroll
     for (int j = 0; j < PW; ++j) {
@@ -1676,7 +1712,12 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
             pmask |= 1u << j;
     }
 
-    for (uint32_t b = c.part; b < batches; b += a.parts) {
+    uint32_t rnd = 0;
+    for (uint32_t b = c.part; b < batches; b += a.parts, ++rnd) {
+        const uint32_t fj = c.flag + rnd, bj = fj & 1u;      // this round's flag and buffer
+        const uint32_t mine_off = (q * 2u + bj) * rb;
+        if (rnd > 0u)
+            lds_barrier();          // every wave has received the previous batch: the permit
         uint32_t g[GW];
         uint32_t gvalid = 0;
 #pragma unroll
@@ -1731,18 +1772,19 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
                 }
             }
             if constexpr (!F32) {
-                l128_store_payload<LOCAL>(reg, mine_off + gm * L128_BYTES + lane * 16u, ln.half, red);
+                const uint32_t lo = mine_off + (slot0 + wave) * L128_BYTES + lane * 16u;
+                l128_store_payload<LOCAL>(reg, lo, ln.half, red);
                 wait_stores();
                 if (ln.half)
-                    l128_store_flag<LOCAL>(reg, mine_off + gm * L128_BYTES + lane * 16u, c.flag);
+                    l128_store_flag<LOCAL>(reg, lo, fj);
             }
         }
         if constexpr (F32)
             continue;
         // ---- all-gather of the batch from this wave's peers
         u32x4 V[GW][PW];
-        if (!l128_recv<GW, PW, LOCAL>(reg, rb, c.par, g, gvalid, pmask, wave, lane, ln, lim,
-                                      c.flag, ctl, q, c.call, a.watchdog_ticks, V))
+        if (!l128_recv<GW, PW, LOCAL>(reg, rb, bj, slot0, g, gvalid, pmask, wave, lane, ln, lim,
+                                      fj, ctl, q, c.call, a.watchdog_ticks, V))
             return;
 #pragma unroll
         for (int k = 0; k < GW; ++k) {
@@ -1772,7 +1814,11 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 // RS[s][q]; rank s polls RS[s][*], reduces in rank order, re-arms.
 // All-gather: rank q pushes its reduced chunk into AG[r][q] of every peer r
 // and writes it to out[q]; every rank polls AG[q][*], copies to out, re-arms.
-// Inbox regions [recv][send][parity] x s2_stride, one descriptor each.
+// Inbox regions [recv][send][buffer] x s2_stride, one descriptor each:
+// fixed-size windows walked in rounds as in the one-shot kernels (round j of
+// part p: window bytes [1024 p, 1024 (p+1)) of buffer (flag + j) & 1), every
+// round ending with its re-arm stores acknowledged before the next round's
+// pushes.
 //
 // A workgroup of SENT_WAVES waves owns 64 chunks of every slice per round,
 // and the peers are split over the waves as in the one-shot kernels: wave w
@@ -1783,8 +1829,8 @@ template <int NMAX, bool F32, bool LOCAL>
 __device__ __forceinline__ bool ts_round(const Launch &a, Ctx0 &c, const Ctl &ctl,
                                          __amdgpu_buffer_rsrc_t inq, __amdgpu_buffer_rsrc_t rsr,
                                          __amdgpu_buffer_rsrc_t agr, __amdgpu_buffer_rsrc_t oa,
-                                         uint32_t ch, u32x4 (*stage)[64], u32x4 *red,
-                                         uint32_t *failed)
+                                         uint32_t ch, uint32_t rnd, bool more, u32x4 (*stage)[64],
+                                         u32x4 *red, uint32_t *failed)
 {
     constexpr int PW = (NMAX + SENT_WAVES - 1) / SENT_WAVES;
     const uint32_t N = a.n_ranks;
@@ -1794,7 +1840,7 @@ __device__ __forceinline__ bool ts_round(const Launch &a, Ctx0 &c, const Ctl &ct
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t e = ch * 8u;                     // element offset inside a slice
     const uint32_t esz = F32 ? 4u : 2u;
-    const uint32_t lane_off = e * 2u + c.par * sb;
+    const uint32_t lane_off = (c.part * 64u + lane) * 16u + ((c.flag + rnd) & 1u) * sb;
     auto slice_len = [&](uint32_t s) -> uint32_t {
         const uint32_t lo = s * L;
         return lo >= a.n ? 0u : (a.n - lo < L ? a.n - lo : L);
@@ -1903,9 +1949,13 @@ __device__ __forceinline__ bool ts_round(const Launch &a, Ctx0 &c, const Ctl &ct
     for (int j = 0; j < PW; ++j)
         if ((mine >> j) & 1u)
             st16<Pol<LOCAL>::ST>(sentinel4(), rsr, box(q, peer(j)));
-    __syncthreads();
-    if constexpr (F32)
+    if constexpr (F32) {                            // the debug path has no all-gather
+        if (more)
+            wait_stores();
+        __syncthreads();
         return true;
+    }
+    __syncthreads();
     // ---- all-gather: push the reduced chunk to this wave's peers
     if (act) {
         const u32x4 rv = red[lane];
@@ -1929,6 +1979,10 @@ __device__ __forceinline__ bool ts_round(const Launch &a, Ctx0 &c, const Ctl &ct
             st16<CP_PLAIN>(V[j], oa, (q * a.n + peer(j) * L + e) * esz);
             st16<Pol<LOCAL>::ST>(sentinel4(), agr, box(q, peer(j)));
         }
+    // the round's re-arms (both inboxes) are performed before the next
+    // round's pushes: a peer reuses a slot only after receiving such a push
+    if (more)
+        wait_stores();
     __syncthreads();                                // the tiles are reused next round
     return *failed == 0u;
 }
@@ -1956,11 +2010,13 @@ __global__ __launch_bounds__(512) void k_twoshot_sentinel(const Launch a)
     uint32_t ch = c.part * 64u + (threadIdx.x & 63u);
     start_delay(a, c);
     // round 0 straight-line (see the one-shot LL kernel), later rounds looped
-    if (!ts_round<NMAX, F32, LOCAL>(a, c, ctl, inq, rsr, agr, oa, ch, stage, red, &failed))
+    if (!ts_round<NMAX, F32, LOCAL>(a, c, ctl, inq, rsr, agr, oa, ch, 0u, rounds > 1u, stage, red,
+                                    &failed))
         return;
     for (uint32_t it = 1; it < rounds; ++it) {
         ch += step;
-        if (!ts_round<NMAX, F32, LOCAL>(a, c, ctl, inq, rsr, agr, oa, ch, stage, red, &failed))
+        if (!ts_round<NMAX, F32, LOCAL>(a, c, ctl, inq, rsr, agr, oa, ch, it, it + 1u < rounds,
+                                        stage, red, &failed))
             return;
     }
     mark(a, c.t_data);
