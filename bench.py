@@ -160,6 +160,26 @@ class Epochs:
 US_PER_TICK = 1e6 / CLOCK_HZ
 
 
+def start_stats(tsh, calls_per_replay):
+    """Per-call periods from a [slots][records][4] table in which each
+    workgroup wrote only its start (field 0): call k's start is its first
+    workgroup's start, its period start(k+1) - start(k) between back-to-back
+    calls of one replay; also the spread from the first to the last
+    workgroup start of a call (dispatch)."""
+    t = tsh[:, :, 0].astype(np.float64)
+    live = tsh[:, :, 0] != 0
+    keep = live.any(axis=1)
+    t, live = t[keep], live[keep]
+    first = np.where(live, t, np.inf).min(axis=1)
+    lastw = np.where(live, t, -np.inf).max(axis=1)
+    order = np.argsort(first)
+    first, lastw = first[order], lastw[order]
+    within = np.ones(first.size - 1, dtype=bool)
+    within[calls_per_replay - 1::calls_per_replay] = False
+    intervals = np.diff(first)[within] * US_PER_TICK
+    return intervals, (lastw - first) * US_PER_TICK
+
+
 def timestamp_stats(tsh, calls_per_replay):
     """Per-call figures from a [slots][records][4] table of per-wave records
     {start, sync, data, end} (ticks; records never written stay 0): the
@@ -203,7 +223,7 @@ def instrumented_replays(torch, ar, capture, stream, n, calls, replays, phases=F
     the event time of the same replays (to compare with the uninstrumented
     figure).  With `phases` the kernels also mark their synchronisation and
     data phases (two more clock reads per wave, which lengthen the call)."""
-    records = ar.query(4, n) * ar.query(5, n) // 64          # waves per call
+    records = ar.query(4, n) * (ar.query(5, n) // 64 if phases else 1)   # waves or workgroups
     slots = calls * (replays + 1)
     ts = torch.zeros((slots, records, 4), dtype=torch.int64, device="cuda:0")
     ar.set_timestamps(ts, slots, records, phases)
@@ -221,25 +241,33 @@ def instrumented_replays(torch, ar, capture, stream, n, calls, replays, phases=F
         e1.record(stream)
     torch.cuda.synchronize()
     del gi
-    intervals, spans, gaps, ph = timestamp_stats(ts.cpu().numpy().view(np.uint64), calls)
+    tab = ts.cpu().numpy().view(np.uint64)
     del ts
-    out = {"interval_us": summary(intervals), "span_us": summary(spans),
-           "launch_gap_us": summary(gaps),
-           "event_us_per_call_instrumented": e0.elapsed_time(e1) * 1000.0 / (calls * replays),
+    out = {"event_us_per_call_instrumented": e0.elapsed_time(e1) * 1000.0 / (calls * replays),
            "records_per_call": records, "replays": replays, "phase_marks": bool(phases)}
-    keys = ph if phases else ("last_start_us", "median_start_us", "end_us")
-    out["phases_p50_us"] = {k: pct(ph[k], 50) for k in keys}
+    if phases:
+        intervals, spans, gaps, ph = timestamp_stats(tab, calls)
+        out.update({"interval_us": summary(intervals), "span_us": summary(spans),
+                    "launch_gap_us": summary(gaps),
+                    "phases_p50_us": {k: pct(v, 50) for k, v in ph.items()}})
+    else:
+        intervals, dispatch = start_stats(tab, calls)
+        out.update({"interval_us": summary(intervals), "dispatch_spread_us": summary(dispatch),
+                    "what": "call k's period = start(k+1) - start(k), start = its first "
+                            "workgroup's start (the launch gap included)"})
     return out
 
 
 def graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays=None,
-              instrumented=True, exact=True):
+              instrumented=True, exact=True, staging=0):
     """`calls` calls (+ step end) captured in one hipGraph and replayed.
 
     Returns event timings per replay, instrumented per-call intervals/spans,
-    and a bit-exact check of the last replay's outputs."""
+    and a bit-exact check of the last replay's outputs.  `staging` limits the
+    staged protocols' window (bytes per rank or inbox pair and buffer)."""
     ar.init(wl.N, wl.n)
     try:
+        ar.set_staging(staging)
         return _graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays,
                           instrumented, exact)
     finally:
@@ -291,6 +319,7 @@ def _graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays, instr
            "event_ms_per_replay": summary(per_replay_ms),
            "mismatches": bad, "status": list(status),
            "rounds_per_call": ar.query(12, wl.n),
+           "staging_window_bytes": ar.query(15, wl.n),
            "xcd_local_scope": bool(ar.query(8, wl.n)),
            "placement_verified": bool(ar.query(9, 0))}
     if worst is not None:
@@ -334,13 +363,14 @@ def bench_floor(torch, steps):
 
 
 def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact=True, graph_calls=160,
-                    graph_replays=3, instrumented=False):
+                    graph_replays=3, instrumented=False, staging=0):
     """Back-to-back stream calls over 8 rotating buffer sets, events per call;
     then the same calls captured in one hipGraph and replayed back to back
     (optionally once more with the per-wave timestamp table: the call's
     phases)."""
     ar.init(wl.N, wl.n)
     try:
+        ar.set_staging(staging)
         return _bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact,
                                 graph_calls, graph_replays, instrumented)
     finally:
@@ -430,6 +460,7 @@ def _bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact, gr
                     "sets (footprint %d MiB)" % (label, (2 * nsets * wl.N * 2 * wl.n) >> 20),
         "algo": label, "grid": grid, "threads": threads, "xcd_local_scope": local,
         "rounds_per_call": ar.query(12, wl.n),
+        "staging_window_bytes": ar.query(15, wl.n),
         "us_per_call": summary(us),
         "region_us_per_call": region_us,
         "gbps_region": wl.b_alg / (region_us * 1e-6) / 1e9,
@@ -863,10 +894,11 @@ def main():
         if lat is not None:
             lat["workload"] = ("8 ranks x [1x8192] bf16 (16 KiB/rank), N(0,0.5), one-shot LL, "
                                "160 calls/step in one hipGraph")
-            log("16 KiB p50 %.3f us/call (events), instrumented interval p50 %.3f us (mean %+.1f%% "
-                "vs events), span p50 %.3f" % (
+            log("16 KiB p50 %.3f us/call (events), instrumented per-call period p50 %.3f p99 %.3f "
+                "us (mean %+.1f%% vs events)" % (
                     lat["event_us_per_call"]["p50"], lat["instrumented"]["interval_us"]["p50"],
-                    100 * lat["instrumented"]["agreement"], lat["instrumented"]["span_us"]["p50"]))
+                    lat["instrumented"]["interval_us"]["p99"],
+                    100 * lat["instrumented"]["agreement"]))
         lat_d = legs.run("latency_16k_oneshot_direct", lambda: graph_run(
             torch, ar, wl2, ONE, DIRECT, CALLS_PER_STEP, args.steps, args.warmup,
             instrumented=False))

@@ -334,17 +334,24 @@ int ar_set_delays(const uint32_t *dev_ns, size_t calls);
 /*
  * ar_set_timestamps -- measurement hook (time completion at the consumer,
  * not at the asynchronous return: the small-message essay, section 6.2):
- * DEVICE uint64 table [slots][records_per_slot][4].  Every wave w (position
- * in dispatch order: workgroup index x waves per workgroup + wave) of the
- * call numbered c (calls counted from 1 since ar_init / ar_reset, across
- * steps) with w < records_per_slot writes record [(c - 1) mod slots][w] =
- * {start, first synchronisation satisfied, last data store issued, end}, in
- * ticks of the constant 100 MHz clock, with plain stores (no atomics, waits
- * or barriers).  The two middle fields are written only when `phases` is
- * nonzero (else 0): each is one more read of the clock, which lengthens the
- * call.  A call's start is the minimum of its records' starts, its end the
- * maximum of their ends.  NULL disables (the default).  records_per_slot
- * should be at least the launch's wave count (ar_query keys 4 and 5).
+ * DEVICE uint64 table [slots][records_per_slot][4], zeroed by the caller.
+ * For the call numbered c (calls counted from 1 since ar_init / ar_reset,
+ * across steps) the kernels write into slot (c - 1) mod slots, in ticks of
+ * the constant 100 MHz clock, with plain stores (no atomics, waits or
+ * barriers):
+ *   phases == 0: wave 0 of every workgroup writes its start time into field
+ *                0 of record w = the workgroup's position in dispatch order,
+ *                in the prologue (a store issued at a workgroup's end would
+ *                itself lengthen the call); the period of call k is then
+ *                start(k+1) - start(k), start = the earliest record;
+ *   phases != 0: every wave writes at its end record w = workgroup position
+ *                x waves per workgroup + wave = {start, first synchronisation
+ *                satisfied, last data store issued, end} (each mark is one
+ *                more read of the clock, and the late stores lengthen the
+ *                call).
+ * Records with w >= records_per_slot are not written.  NULL disables (the
+ * default).  records_per_slot should be at least the launch's workgroup
+ * count (ar_query key 4), or its wave count with phases (keys 4 and 5).
  * Errors: AR_ERR_NOT_INIT, AR_ERR_INVALID (zero sizes, or a table above
  * 2^40 records).
  */

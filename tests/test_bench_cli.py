@@ -124,3 +124,22 @@ def test_timestamp_stats_per_call_figures():
     assert b.headline_latency(lat)[:2] == (2.4, 2.5)
     lat["instrumented"]["agreement"] = 0.08
     assert b.headline_latency(lat)[:2] == (2.5, 2.6)
+
+
+def test_start_stats_periods():
+    """Starts only (no phases): periods are start(k+1) - start(k) within a
+    replay, and the dispatch spread is first to last workgroup start."""
+    import numpy as np
+    b = _bench()
+    calls, replays = 4, 2
+    tab = np.zeros((calls * (replays + 1), 3, 4), dtype=np.uint64)
+    t = 5000
+    for r in range(replays):
+        for k in range(calls):
+            slot = calls + r * calls + k
+            tab[slot, :, 0] = [t + 10, t, t + 30]      # workgroups start 0.1-0.3 us apart
+            t += 250                                   # 2.5 us per call
+        t += 10000
+    intervals, dispatch = b.start_stats(tab, calls)
+    assert intervals.size == replays * (calls - 1)
+    assert np.allclose(intervals, 2.5) and np.allclose(dispatch, 0.3)

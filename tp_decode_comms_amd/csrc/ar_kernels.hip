@@ -45,6 +45,7 @@ namespace ar {
 // status records); par: buffer parity of the first round (flag & 1).
 struct Ctx0 {
     uint32_t rank, part, flag, call, par;
+    bool phases;                    // a timestamp table with phase records is set
     uint64_t t0, t_sync, t_data;
 };
 
@@ -62,6 +63,8 @@ __device__ __forceinline__ uint32_t linear_id(const Launch &a)
 // memory: one scalar load, served by the scalar cache a CU's waves share
 // (every wave of the launch reads them; 8 x 16 KiB LL: 2.63 -> 2.58 us per
 // call against a vector load).
+__device__ __forceinline__ void stamp_start(const Launch &a, const Ctx0 &c);
+
 __device__ __forceinline__ void load_seq(const Launch &a, Ctx0 &c)
 {
     typedef const __attribute__((address_space(4))) u32x2 const_u32x2;
@@ -69,6 +72,7 @@ __device__ __forceinline__ void load_seq(const Launch &a, Ctx0 &c)
     c.flag = s.x + a.rbase + 1u;
     c.call = s.y + a.epoch;
     c.par = c.flag & 1u;
+    stamp_start(a, c);
 }
 
 __device__ __forceinline__ void start_delay(const Launch &a, const Ctx0 &c)
@@ -91,30 +95,47 @@ __device__ __forceinline__ void start_delay(const Launch &a, const Ctx0 &c)
 // wait also waits for, so marks on the critical path lengthen the call
 // (8 x 16 KiB LL: +0.37 us per call with both marks); a table without them
 // records only the start (read anyway) and the end.
-__device__ __forceinline__ void mark(const Launch &a, uint64_t &t)
+__device__ __forceinline__ void mark(const Ctx0 &c, uint64_t &t)
 {
-    if (a.ts != nullptr && a.ts_phases != 0u)
+    if (c.phases)
         t = clock100();
 }
-__device__ __forceinline__ void mark_once(const Launch &a, uint64_t &t)
+__device__ __forceinline__ void mark_once(const Ctx0 &c, uint64_t &t)
 {
-    if (a.ts != nullptr && a.ts_phases != 0u && t == 0u)
+    if (c.phases && t == 0u)
         t = clock100();
 }
 
-// Each wave's lane 0 writes its own record {start, first synchronisation
-// satisfied, last data store issued, end} with plain stores: no atomic, no
-// wait for earlier stores and no barrier, so the measured call runs as it
-// does without the table.  Record index: the wave's position in dispatch
-// order; slot (call - 1) mod slots.
+// Measurement records (only with a timestamp table).  Without phases, lane 0
+// of each workgroup's wave 0 writes its start time into record [slot][w]
+// (w: the workgroup's position in dispatch order, slot: (call - 1) mod
+// slots) as soon as the call number is known, with one plain store: no
+// atomic, wait or barrier.  The store completes long before the kernel ends,
+// so the call runs as it does without the table (a store issued as a
+// workgroup's last instruction measured 0.2 us longer per 16 KiB call:
+// the launch completes only once every store has been acknowledged).  Call
+// k's period is start(k+1) - start(k).  With phases every wave writes its
+// whole record {start, first synchronisation satisfied, last data store
+// issued, end} at its end instead, which lengthens the call.
+__device__ __forceinline__ void stamp_start(const Launch &a, const Ctx0 &c)
+{
+    if (a.ts == nullptr || a.ts_phases != 0u || threadIdx.x != 0u)
+        return;
+    const uint32_t w = linear_id(a);
+    if (w >= a.ts_stride)
+        return;
+    const uint32_t slot = (c.call - 1u) % a.ts_slots;
+    a.ts[((size_t)slot * a.ts_stride + w) * TS_FIELDS] = c.t0;
+}
+
 __device__ __forceinline__ void finish(const Launch &a, const Ctx0 &c)
 {
-    if (a.ts == nullptr)
-        return;
-    const uint32_t w = linear_id(a) * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if ((threadIdx.x & 63u) != 0u || w >= a.ts_stride)
+    if (!c.phases || (threadIdx.x & 63u) != 0u)
         return;
     const uint64_t t1 = clock100();
+    const uint32_t w = linear_id(a) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (w >= a.ts_stride)
+        return;
     const uint32_t slot = (c.call - 1u) % a.ts_slots;
     uint64_t *p = a.ts + ((size_t)slot * a.ts_stride + w) * TS_FIELDS;
     p[0] = c.t0;
@@ -129,6 +150,7 @@ __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
     c.t0 = clock100();
     c.t_sync = 0u;
     c.t_data = 0u;
+    c.phases = a.ts != nullptr && a.ts_phases != 0u;
     // The grid is (X, N, parts / X) with X = 2^xshift consecutive parts of
     // one rank along x (X = 8 when parts is a multiple of 8, else 1): the
     // rank is blockIdx.y and the part (blockIdx.z << xshift) + blockIdx.x.
@@ -159,7 +181,8 @@ __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
     // of them.)
     asm volatile("" ::"s"(a.in[c.rank]), "s"(a.out), "s"(a.ctl), "s"(a.n), "s"(a.n_ranks),
                  "s"(a.epoch), "s"(a.rbase), "s"(a.parts), "s"(a.slice), "s"(a.xshift),
-                 "s"(a.delays), "s"(blockDim.x));
+                 "s"(a.delays), "s"(a.ts), "s"(a.ts_slots), "s"(a.ts_stride), "s"(a.ts_phases),
+                 "s"(blockDim.x));
     c.part = (blockIdx.z << a.xshift) + lo;
 }
 
@@ -365,7 +388,7 @@ __device__ __forceinline__ bool ll_round(const Launch &a, Ctx0 &c, const Ctl &ct
         if (!wave_any(pend))
             break;
     }
-    mark_once(a, c.t_sync);
+    mark_once(c, c.t_sync);
     lds_barrier();
     if (*failed)
         return false;
@@ -459,7 +482,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll(const Launch a)
         if (!ll_round<NMAX, LOCAL, true>(a, c, ctl, llr, ch, C, j, x, stage, &failed, out))
             return;
     }
-    mark(a, c.t_data);
+    mark(c, c.t_data);
     finish(a, c);
 }
 
@@ -604,7 +627,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
             st8<CP_PLAIN>(scale4(hw, gw, r), oy, cc * 8u);
         }
     }
-    mark(a, c.t_data);
+    mark(c, c.t_data);
     finish(a, c);
 }
 
@@ -660,7 +683,7 @@ __global__ __launch_bounds__(256) void k_oneshot_direct_norm(const NormLaunch L)
     start_delay(a, c);
     raise_arrival<LOCAL>(a, c);
     bool ok = wait_arrivals<LOCAL>(a, c, ctl);
-    mark(a, c.t_sync);
+    mark(c, c.t_sync);
     __amdgpu_buffer_rsrc_t src[NMAX];
 #pragma unroll
     for (int s = 0; s < NMAX; ++s)
@@ -725,7 +748,7 @@ __global__ __launch_bounds__(256) void k_oneshot_direct_norm(const NormLaunch L)
         const u32x2 gw = b == bbeg ? g0 : b == bbeg + 1u ? g1 : ld8<CP_PLAIN>(gr, (e % L.hidden) * 2u);
         st8<CP_PLAIN>(scale4(hw, gw, r), oy, e * 2u);
     }
-    mark(a, c.t_data);
+    mark(c, c.t_data);
     finish(a, c);
 }
 
@@ -783,7 +806,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_rows_norm(const NormLaunch L)
     raise_arrival<LOCAL>(a, c);
     if (!wait_arrivals_wg<LOCAL>(a, c, ctl))
         return;                                           // every wave returns here
-    mark(a, c.t_sync);
+    mark(c, c.t_sync);
     if (poller) {
 #pragma unroll
         for (int k = 0; k < (int)ROWS_PER_WAVE; ++k) {
@@ -854,7 +877,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_rows_norm(const NormLaunch L)
         if (live && j < B)
             st8<CP_PLAIN>(scale4(hk[k], gk[k], r), oy, (row0 + j * NORM_BLOCK + lane * 4u) * 2u);
     }
-    mark(a, c.t_data);
+    mark(c, c.t_data);
     finish(a, c);
 }
 
@@ -950,7 +973,7 @@ __device__ __forceinline__ bool sent_round(const Launch &a, Ctx0 &c, const Ctl &
         if (!wave_any(pend != 0u))
             break;
     }
-    mark_once(a, c.t_sync);
+    mark_once(c, c.t_sync);
     lds_barrier();                  // the tile only: the polls in flight are waited for below
     if (*failed)
         return false;
@@ -1020,7 +1043,7 @@ __global__ __launch_bounds__(512) void k_oneshot_sentinel(const Launch a)
                                           &failed))
             return;
     }
-    mark(a, c.t_data);
+    mark(c, c.t_data);
     finish(a, c);
 }
 
@@ -1191,9 +1214,9 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
     if (!wait_arrivals<LOCAL>(a, c, ctl))
         return;
-    mark(a, c.t_sync);
+    mark(c, c.t_sync);
     oneshot_data<NMAX, F32>(a, src, o, G, c.part * blockDim.x + threadIdx.x, step);
-    mark(a, c.t_data);
+    mark(c, c.t_data);
     finish(a, c);
 }
 
@@ -1233,9 +1256,9 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
     if (!wait_arrivals_wg<LOCAL>(a, c, ctl))
         return;
-    mark(a, c.t_sync);
+    mark(c, c.t_sync);
     twoshot_data<NMAX, F32>(a, src, oa, lo, G, c.part * blockDim.x + threadIdx.x, step);
-    mark(a, c.t_data);
+    mark(c, c.t_data);
     // completion: my stores are at the coherence point, then my flag.  The
     // flags of the writers on one XCD (parts p with p % 8 == x) are packed
     // together: writer (s, p) owns word x*N*P8 + s*P8 + p/8, P8 = ceil(parts/8).
@@ -1373,9 +1396,9 @@ __global__ __launch_bounds__(256) void k_oneshot_barrier(const Launch a)
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
     if (!grid_barrier(a, c, ctl, CTL_BAR_TOP))
         return;
-    mark(a, c.t_sync);
+    mark(c, c.t_sync);
     oneshot_data<NMAX, F32>(a, src, o, G, c.part * blockDim.x + threadIdx.x, step);
-    mark(a, c.t_data);
+    mark(c, c.t_data);
     if (!grid_barrier(a, c, ctl, CTL_BAR_BOTTOM))
         return;
     finish(a, c);
@@ -1402,9 +1425,9 @@ __global__ __launch_bounds__(256) void k_twoshot_barrier(const Launch a)
     const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
     if (!grid_barrier(a, c, ctl, CTL_BAR_TOP))
         return;
-    mark(a, c.t_sync);
+    mark(c, c.t_sync);
     twoshot_data<NMAX, F32>(a, src, oa, lo, G, c.part * blockDim.x + threadIdx.x, step);
-    mark(a, c.t_data);
+    mark(c, c.t_data);
     if (!grid_barrier(a, c, ctl, CTL_BAR_BOTTOM))
         return;
     finish(a, c);
@@ -1631,7 +1654,7 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
         if (!l128_recv<GW, PW, LOCAL>(reg, rb, bj, slot0, g, gvalid, pmask, wave, lane, ln, lim,
                                       fj, ctl, c.rank, c.call, a.watchdog_ticks, V))
             failed = 1u;                            // every wave still meets the barrier
-        mark_once(a, c.t_sync);
+        mark_once(c, c.t_sync);
 #pragma unroll
         for (int k = 0; k < GW; ++k)
             if ((gvalid >> k) & 1u)
@@ -1658,7 +1681,7 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
         }
         lds_barrier();                              // the tile is reused next batch
     }
-    mark(a, c.t_data);
+    mark(c, c.t_data);
     finish(a, c);
 }
 
@@ -1693,7 +1716,7 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
     input_rsrcs<NMAX>(a, src);
     if (!wait_arrivals<LOCAL>(a, c, ctl))
         return;
-    mark(a, c.t_sync);
+    mark(c, c.t_sync);
     auto slice_len = [&](uint32_t s) -> uint32_t {
         const uint32_t lo = s * L;
         return (s >= N || lo >= a.n) ? 0u : (a.n - lo < L ? a.n - lo : L);
@@ -1805,7 +1828,7 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
             }
         }
     }
-    mark(a, c.t_data);
+    mark(c, c.t_data);
     finish(a, c);
 }
 
@@ -1913,7 +1936,7 @@ __device__ __forceinline__ bool ts_round(const Launch &a, Ctx0 &c, const Ctl &ct
             pend |= 1u << j;
     uint32_t mine = pend;
     receive(rsr);
-    mark_once(a, c.t_sync);
+    mark_once(c, c.t_sync);
 #pragma unroll
     for (int j = 0; j < PW; ++j)
         if ((mine >> j) & 1u)
@@ -2019,7 +2042,7 @@ __global__ __launch_bounds__(512) void k_twoshot_sentinel(const Launch a)
                                         stage, red, &failed))
             return;
     }
-    mark(a, c.t_data);
+    mark(c, c.t_data);
     finish(a, c);
 }
 
@@ -2107,7 +2130,7 @@ __global__ __launch_bounds__(256) void k_twoshot_atomic(const Launch a)
         }
         if (!ok)
             break;                      // status recorded; every wave still reaches finish()
-        mark_once(a, c.t_sync);
+        mark_once(c, c.t_sync);
         const uint32_t sb = data ? ld4<CP_DEV>(acc, base + 4u * j) : 0u;
         const float sum = __uint_as_float(sb);
         wait_stores();                                          // the read has returned
@@ -2126,7 +2149,7 @@ __global__ __launch_bounds__(256) void k_twoshot_atomic(const Launch a)
                     (uint16_t)__builtin_bit_cast(uint16_t, (__bf16)sum), o, e * 2u, 0, CP_PLAIN);
         }
     }
-    mark(a, c.t_data);
+    mark(c, c.t_data);
     finish(a, c);
 }
 
