@@ -173,8 +173,7 @@ void free_all()
         if (*b) (void)hipFree(*b);
         *b = nullptr;
     }
-    if (g.ctl) (void)hipFree(g.ctl);
-    g.ctl = nullptr;
+    g.ctl = nullptr;                    // the device's static control block
     if (g.done) (void)hipFree(g.done);
     g.done = nullptr;
     if (g.stats) (void)hipFree(g.stats);
@@ -804,7 +803,7 @@ int ar_init(int n_ranks, size_t max_elems)
         (rc = alloc(&g.s1, s1_bytes())) != AR_OK ||
         (rc = alloc(&g.srs, s2_bytes())) != AR_OK ||
         (rc = alloc(&g.sag, s2_bytes())) != AR_OK ||
-        (rc = alloc((char **)&g.ctl, ar::CTL_WORDS * 4)) != AR_OK ||
+        (rc = (ar::control_block(&g.ctl) == hipSuccess ? AR_OK : AR_ERR_HIP)) != AR_OK ||
         (rc = alloc((char **)&g.done, done_words() * 4)) != AR_OK ||
         (rc = alloc((char **)&g.stats, stats_bytes())) != AR_OK ||
         (rc = alloc(&g.acc, acc_bytes())) != AR_OK) {

@@ -67,5 +67,7 @@ hipError_t launch_step_end(uint32_t *ctl, uint32_t calls, uint32_t rounds, char 
                            uint32_t *stats, size_t stats_bytes, hipStream_t stream);
 hipError_t launch_set_seq(uint32_t *ctl, uint32_t seq, hipStream_t stream);
 hipError_t launch_fill(uint32_t *p, size_t words, uint32_t value, hipStream_t stream);
+// device address of the control block (CTL_WORDS words) on the current device
+hipError_t control_block(uint32_t **p);
 
 }  // namespace ar

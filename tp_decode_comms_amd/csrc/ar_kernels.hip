@@ -39,12 +39,29 @@
 
 namespace ar {
 
+// The control block (CTL_WORDS words: the sequence words, the status record,
+// the arrival and barrier words; layout in ar_proto.h).  A file-scope device
+// array rather than an allocation: its address is a link-time constant, so
+// a kernel's load of the sequence words does not wait for the launch record
+// to arrive first -- it goes out with the record's own loads, one memory
+// round trip earlier (the arrival flags of the in-place kernels depend on
+// it).  One block per device; the host takes its address with
+// hipGetSymbolAddress (control_block()) and the launch record carries it for
+// every other use.
+__device__ __align__(256) uint32_t ar_control[CTL_WORDS];
+
+hipError_t control_block(uint32_t **p)
+{
+    return hipGetSymbolAddress((void **)p, HIP_SYMBOL(ar_control));
+}
+
 // ------------------------------------------------------------------ common
 // flag: the flag of the call's first round (round j uses flag + j); call:
 // the call's number since the last reset (start delays, measurement slots,
 // status records); par: buffer parity of the first round (flag & 1).
 struct Ctx0 {
     uint32_t rank, part, flag, call, par;
+    uint32_t seq, calls;            // the sequence words, fetched in the prologue
     bool phases;                    // a timestamp table with phase records is set
     uint64_t t0, t_sync, t_data;
 };
@@ -62,15 +79,21 @@ __device__ __forceinline__ uint32_t linear_id(const Launch &a)
 // writes them while an AllReduce kernel runs, so they are read as constant
 // memory: one scalar load, served by the scalar cache a CU's waves share
 // (every wave of the launch reads them; 8 x 16 KiB LL: 2.63 -> 2.58 us per
-// call against a vector load).
-__device__ __forceinline__ void stamp_start(const Launch &a, const Ctx0 &c);
-
-__device__ __forceinline__ void load_seq(const Launch &a, Ctx0 &c)
+// call against a vector load), from the control block's fixed address, in
+// the prologue's load round (begin()).
+__device__ __forceinline__ u32x2 seq_words()
 {
     typedef const __attribute__((address_space(4))) u32x2 const_u32x2;
-    const u32x2 s = *((const_u32x2 *)a.ctl + CTL_SEQ / 2);
-    c.flag = s.x + a.rbase + 1u;
-    c.call = s.y + a.epoch;
+    return *((const_u32x2 *)ar_control + CTL_SEQ / 2);
+}
+
+__device__ __forceinline__ void stamp_start(const Launch &a, const Ctx0 &c);
+
+// The call's flag, number and first buffer parity from the sequence words.
+__device__ __forceinline__ void load_seq(const Launch &a, Ctx0 &c)
+{
+    c.flag = c.seq + a.rbase + 1u;
+    c.call = c.calls + a.epoch;
     c.par = c.flag & 1u;
     stamp_start(a, c);
 }
@@ -150,7 +173,6 @@ __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
     c.t0 = clock100();
     c.t_sync = 0u;
     c.t_data = 0u;
-    c.phases = a.ts != nullptr && a.ts_phases != 0u;
     // The grid is (X, N, parts / X) with X = 2^xshift consecutive parts of
     // one rank along x (X = 8 when parts is a multiple of 8, else 1): the
     // rank is blockIdx.y and the part (blockIdx.z << xshift) + blockIdx.x.
@@ -179,11 +201,18 @@ __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
     // blockIdx.y) behind a single wait.
     // (blockDim.x is read from the launch's hidden arguments, so it is one
     // of them.)
+    // (The sequence words come with them: their address is a constant.)
+    const u32x2 sq = seq_words();
     asm volatile("" ::"s"(a.in[c.rank]), "s"(a.out), "s"(a.ctl), "s"(a.n), "s"(a.n_ranks),
                  "s"(a.epoch), "s"(a.rbase), "s"(a.parts), "s"(a.slice), "s"(a.xshift),
                  "s"(a.delays), "s"(a.ts), "s"(a.ts_slots), "s"(a.ts_stride), "s"(a.ts_phases),
-                 "s"(blockDim.x));
+                 "s"(sq), "s"(blockDim.x));
+    c.seq = sq.x;
+    c.calls = sq.y;
     c.part = (blockIdx.z << a.xshift) + lo;
+    // after the fields' loads are issued (computed earlier, the test of a.ts
+    // made the compiler wait for it before issuing the others)
+    c.phases = a.ts != nullptr && a.ts_phases != 0u;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t in_rsrc(const Launch &a, uint32_t r)
