@@ -252,17 +252,17 @@ __device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t o, uint32_t elem, 
 }
 
 // 4 accumulated elements (in v[0..3]) -> out[rank][elem..elem+4)
-template <bool F32>
+template <bool F32, int CP = CP_PLAIN>
 __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t o, uint32_t elem, const float *v)
 {
     if constexpr (F32) {
         u32x4 lo;
         lo.x = __float_as_uint(v[0]); lo.y = __float_as_uint(v[1]);
         lo.z = __float_as_uint(v[2]); lo.w = __float_as_uint(v[3]);
-        st16<CP_PLAIN>(lo, o, elem * 4u);
+        st16<CP>(lo, o, elem * 4u);
     } else {
         u32x2 w; w.x = pack_bf16(v[0], v[1]); w.y = pack_bf16(v[2], v[3]);
-        st8<CP_PLAIN>(w, o, elem * 2u);
+        st8<CP>(w, o, elem * 2u);
     }
 }
 
@@ -328,6 +328,18 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
         if (!wave_any(need))
             return true;
     }
+}
+
+// Workgroup form: wave 0 polls, the workgroup barrier releases the others
+// (a quarter of the polling traffic of 4-wave workgroups).
+template <bool LOCAL>
+__device__ __forceinline__ bool wait_arrivals_wg(const Launch &a, const Ctx0 &c, const Ctl &ctl)
+{
+    __shared__ uint32_t ok;
+    if (threadIdx.x < 64u)
+        ok = wait_arrivals<LOCAL>(a, c, ctl) ? 1u : 0u;
+    __syncthreads();
+    return ok != 0u;
 }
 
 // ============================================================ one-shot LL
@@ -1076,17 +1088,6 @@ __global__ __launch_bounds__(512) void k_oneshot_sentinel(const Launch a)
     finish(a, c);
 }
 
-// Workgroup form: wave 0 polls, the workgroup barrier releases the others
-// (a quarter of the polling traffic of 4-wave workgroups).
-template <bool LOCAL>
-__device__ __forceinline__ bool wait_arrivals_wg(const Launch &a, const Ctx0 &c, const Ctl &ctl)
-{
-    __shared__ uint32_t ok;
-    if (threadIdx.x < 64u)
-        ok = wait_arrivals<LOCAL>(a, c, ctl) ? 1u : 0u;
-    __syncthreads();
-    return ok != 0u;
-}
 
 // ============================================== in-place data phases
 // Shared by the flag kernels (DIRECT) and their barrier-ful baselines, so
@@ -1478,6 +1479,18 @@ __global__ __launch_bounds__(256) void k_twoshot_barrier(const Launch a)
 // with 4).  At most 2 above 8 ranks (LDS tile budget).
 constexpr int L128_WAVES = 4;
 
+// Cache policies and the arrival-wait form of the LL128 kernels, measured at
+// 8 x 512 KiB and 8 x 4 MiB (graphs, same box): streaming device-scope
+// output stores in the two-shot cut the 4 MiB call 24.3 -> 23.1 us (no dirty
+// lines left for the launch boundary's write-back) but slow the 512 KiB
+// call 4.95 -> 5.2 us, the workload the line protocol serves, so they stay
+// plain; streaming reduce-scatter loads and a single polling wave per
+// workgroup move both within 1%.
+constexpr int L128_OUT1 = CP_PLAIN;     // one-shot output stores
+constexpr int L128_OUT2 = CP_PLAIN;     // two-shot output stores
+constexpr bool L128_ARRIVE_WG = false;  // two-shot arrival wait: one polling wave per workgroup
+constexpr int L128_RS_LD = CP_DEV;      // two-shot in-place reduce-scatter loads
+
 // reads 8 (or 4) elements of a bf16 buffer at element `e`
 template <int CP = CP_PLAIN>
 __device__ __forceinline__ u32x4 ld_elems(__amdgpu_buffer_rsrc_t r, uint32_t e, bool half)
@@ -1490,16 +1503,22 @@ __device__ __forceinline__ u32x4 ld_elems(__amdgpu_buffer_rsrc_t r, uint32_t e, 
     return ld16<CP>(r, e * 2u);
 }
 
+// The payload store covers the whole 128-byte line: the flag lane writes its
+// 8 payload bytes and zeros over the flag slot.  A store of part of a line
+// the L2 does not hold makes it fetch the line from memory first (8 x 4 MiB
+// two-shot: 4.7 MiB of extra reads per launch, the whole staging footprint);
+// a whole-line store needs no fetch, and the flag store that follows finds
+// the line in the L2.  A zero flag slot never validates ({f, ~f} needs the
+// second word to be the complement of the first).
 template <bool LOCAL>
 __device__ __forceinline__ void l128_store_payload(__amdgpu_buffer_rsrc_t dst, uint32_t off,
                                                    bool half, u32x4 payload)
 {
     if (half) {
-        u32x2 p; p.x = payload.x; p.y = payload.y;
-        st8<Pol<LOCAL>::ST>(p, dst, off);
-    } else {
-        st16<Pol<LOCAL>::ST>(payload, dst, off);
+        payload.z = 0u;
+        payload.w = 0u;
     }
+    st16<Pol<LOCAL>::ST>(payload, dst, off);
 }
 
 template <bool LOCAL>
@@ -1545,6 +1564,8 @@ __device__ __forceinline__ bool l128_recv(__amdgpu_buffer_rsrc_t reg, uint32_t r
     // 8 payload bytes, then the line flag) and clears the upper half.
     uint32_t pend[GW];
     u32x2 F[GW][PW];
+    Watch w;
+    w.begin(budget);
 #pragma unroll
     for (int k = 0; k < GW; ++k) {
         pend[k] = 0;
@@ -1558,8 +1579,6 @@ __device__ __forceinline__ bool l128_recv(__amdgpu_buffer_rsrc_t reg, uint32_t r
                 pend[k] |= 1u << j;
         }
     }
-    Watch w;
-    w.begin(budget);
     while (true) {
         uint32_t any = 0;
 #pragma unroll
@@ -1600,11 +1619,12 @@ __device__ __forceinline__ bool l128_recv(__amdgpu_buffer_rsrc_t reg, uint32_t r
     return true;
 }
 
-template <bool F32>
+
+template <bool F32, int CP = CP_PLAIN>
 __device__ __forceinline__ void store_lane(__amdgpu_buffer_rsrc_t o, uint32_t e, bool half,
                                            const Acc8 &acc)
 {
-    if (half) store4<F32>(o, e, acc.v); else store8<F32>(o, e, acc);
+    if (half) store4<F32, CP>(o, e, acc.v); else store8<F32, CP>(o, e, acc);
 }
 
 // ====================================================== one-shot LL128
@@ -1706,7 +1726,7 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
                 if ((uint32_t)s < N) {
                     if (s == 0) acc.init(t[s]); else acc.add(t[s]);
                 }
-            store_lane<F32>(o, em, ln.half, acc);
+            store_lane<F32, L128_OUT1>(o, em, ln.half, acc);
         }
         lds_barrier();                              // the tile is reused next batch
     }
@@ -1743,7 +1763,7 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
     raise_arrival<LOCAL>(a, c);
     __amdgpu_buffer_rsrc_t src[NMAX];
     input_rsrcs<NMAX>(a, src);
-    if (!wait_arrivals<LOCAL>(a, c, ctl))
+    if (!(L128_ARRIVE_WG ? wait_arrivals_wg<LOCAL>(a, c, ctl) : wait_arrivals<LOCAL>(a, c, ctl)))
         return;
     mark(c, c.t_sync);
     auto slice_len = [&](uint32_t s) -> uint32_t {
@@ -1793,7 +1813,7 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
                 u32x4 V[NMAX];
 #pragma unroll
                 for (int s = 0; s < NMAX; ++s)
-                    V[s] = ld16<CP_DEV>(src[s], (uint32_t)s < N ? eo : OFF_NONE);
+                    V[s] = ld16<L128_RS_LD>(src[s], (uint32_t)s < N ? eo : OFF_NONE);
                 if (ln.half) {
 #pragma unroll
                     for (int s = 0; s < NMAX; ++s) {
@@ -1817,9 +1837,9 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
                     red = acc.bf16();
                     if (ln.half) {
                         u32x2 p; p.x = red.x; p.y = red.y;
-                        st8<CP_PLAIN>(p, o, (q * L + em) * 2u);
+                        st8<L128_OUT2>(p, o, (q * L + em) * 2u);
                     } else {
-                        st16<CP_PLAIN>(red, o, (q * L + em) * 2u);
+                        st16<L128_OUT2>(red, o, (q * L + em) * 2u);
                     }
                 }
             }
@@ -1849,9 +1869,9 @@ __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
                 if (((pmask >> j) & 1u) && e < lim[j]) {
                     if (ln.half) {
                         u32x2 p; p.x = V[k][j].x; p.y = V[k][j].y;
-                        st8<CP_PLAIN>(p, o, (s * L + e) * 2u);
+                        st8<L128_OUT2>(p, o, (s * L + e) * 2u);
                     } else {
-                        st16<CP_PLAIN>(V[k][j], o, (s * L + e) * 2u);
+                        st16<L128_OUT2>(V[k][j], o, (s * L + e) * 2u);
                     }
                 }
             }
