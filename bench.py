@@ -259,15 +259,17 @@ def instrumented_replays(torch, ar, capture, stream, n, calls, replays, phases=F
 
 
 def graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays=None,
-              instrumented=True, exact=True, staging=0):
+              instrumented=True, exact=True, staging=0, scope=0):
     """`calls` calls (+ step end) captured in one hipGraph and replayed.
 
     Returns event timings per replay, instrumented per-call intervals/spans,
     and a bit-exact check of the last replay's outputs.  `staging` limits the
-    staged protocols' window (bytes per rank or inbox pair and buffer)."""
+    staged protocols' window (bytes per rank or inbox pair and buffer);
+    `scope` is the placement and coherence scope (ar_set_scope)."""
     ar.init(wl.N, wl.n)
     try:
         ar.set_staging(staging)
+        ar.set_scope(scope)
         return _graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays,
                           instrumented, exact)
     finally:
@@ -321,6 +323,7 @@ def _graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays, instr
            "rounds_per_call": ar.query(12, wl.n),
            "staging_window_bytes": ar.query(15, wl.n),
            "xcd_local_scope": bool(ar.query(8, wl.n)),
+           "rank_per_xcd_grid": bool(ar.query(16, wl.n)),
            "placement_verified": bool(ar.query(9, 0))}
     if worst is not None:
         res["max_ulp_vs_fixed_order"] = round(worst, 3)
@@ -913,6 +916,16 @@ def main():
             results["barrier_cost_16k_us"] = round(lat_b["event_us_per_call"]["p50"] -
                                                    lat_d["event_us_per_call"]["p50"], 4)
             log("16 KiB one-shot barrier-ful p50 %.3f us/call" % lat_b["event_us_per_call"]["p50"])
+        # the same calls with the ranks spread over the XCDs (rank r on XCD r,
+        # device scope): every exchange crosses L2s, the stand-in for a hop
+        # between GPUs
+        for key, proto, inst in (("latency_16k_cross_xcd", LL, True),
+                                 ("latency_16k_oneshot_direct_cross_xcd", DIRECT, False)):
+            r = legs.run(key, lambda: graph_run(torch, ar, wl2, ONE, proto, CALLS_PER_STEP,
+                                                args.steps, args.warmup, instrumented=inst,
+                                                scope=ar.AR_SCOPE_CROSS_XCD))
+            if r is not None:
+                log("16 KiB %s p50 %.3f us/call" % (key, r["event_us_per_call"]["p50"]))
     bws = []
     if only in ("all", "bw"):
         wl4 = Workload(torch, 4, 8)

@@ -66,7 +66,11 @@ enum ar_status {
 enum ar_scope {
     AR_SCOPE_AUTO = 0,      /* XCD-local when ar_init verified the placement and
                                the launch's part count is a multiple of 8 */
-    AR_SCOPE_DEVICE = 1     /* device scope always: correct on any placement */
+    AR_SCOPE_DEVICE = 1,    /* device scope always: correct on any placement */
+    AR_SCOPE_CROSS_XCD = 2  /* device scope with rank r's workgroups on XCD r mod 8
+                               (grid (1, N, parts)): every exchange between ranks on
+                               different XCDs crosses L2s -- the one-GPU stand-in
+                               for a hop between GPUs */
 };
 
 enum ar_algo { AR_ALGO_AUTO = 0, AR_ALGO_ONESHOT = 1, AR_ALGO_TWOSHOT = 2 };
@@ -264,8 +268,13 @@ int ar_set_launch(int wgs_per_rank, int threads);
  * bits of its part index from the XCD it runs on, which keeps the exchanges
  * XCD-local whichever XCD the round-robin dispatch starts from; ar_init
  * checks the round-robin order with probe launches (ar_query key 9) and
- * leaves the scope off if it does not hold.  The fp32 debug path always uses
- * device scope.  Returns AR_ERR_INVALID for other values.
+ * leaves the scope off if it does not hold.  AR_SCOPE_CROSS_XCD instead
+ * places the ranks across the XCDs (rank r on XCD r mod 8) with device-scope
+ * accesses, so that the ranks' exchanges cross the XCDs' L2s as a real
+ * tensor-parallel exchange crosses the fabric between GPUs ("微秒必争…",
+ * section "张量并行与AllReduce": the communication after each layer that the
+ * method speeds up).  The fp32 debug path always uses device scope.  Returns
+ * AR_ERR_INVALID for other values.
  */
 int ar_set_scope(int scope);
 
@@ -390,7 +399,9 @@ int ar_last_hip_error(void);
  * Returns the value, or a negative status.
  */
 long long ar_query(int key, size_t n);
-/*   (continued) 12 rounds (flags) a call of n elements would take, 13 rounds of
+/*   (continued) 16 1 if a call of n elements would place rank r on XCD r mod 8
+ *   (grid (1, N, parts)), 0 if part p of every rank on XCD p mod 8,
+ *   12 rounds (flags) a call of n elements would take, 13 rounds of
  *   the open step so far, 14 the device round sequence (n == 0) or call count
  *   (n != 0), read after a device synchronisation, 15 the staging window
  *   (bytes per rank or inbox pair and buffer) the protocol of a call of n

@@ -302,3 +302,42 @@ def test_staging_window_validation():
         assert ar.query(15, 8192) == 1 << 20                         # LL: 1 MiB per rank, buffer
         ar.set_options(TWO, DIRECT)
         assert ar.query(15, 8192) == 0                                # no staging
+
+
+@pytest.mark.parametrize("algo,proto,window", [(ONE, LL, 0), (ONE, LL, 4096), (TWO, LL128, 0),
+                                               (ONE, LL128, 16384), (TWO, DIRECT, 0),
+                                               (TWO, SENT, 4096)],
+                         ids=["oneshot-ll", "oneshot-ll-rounds", "twoshot-ll128",
+                              "oneshot-ll128-rounds", "twoshot-direct", "twoshot-sentinel-rounds"])
+def test_sequence_restart_across_steps(algo, proto, window):
+    """The step-end kernel restarts the round sequence (clearing every flag
+    word) once it passes 0xF0000000.  Started just below that with the test
+    hook, steps of 160 calls run across the restart; every call of every
+    step must stay bit-exact, the device sequence must be small afterwards
+    and the call count must have kept counting."""
+    import tp_decode_comms_amd as arm
+    torch = torch_mod()
+    log("sequence restart %d/%d window %d" % (algo, proto, window))
+    sets = Sets(2, 4)
+    with ar_context(8, sets.n, algo, proto) as ar:
+        ar.set_staging(window)
+        rounds = ar.query(12, sets.n)
+        per_step = 160 * rounds
+        start = 0xF0000000 - per_step - per_step // 2      # the second step crosses the limit
+        ar.set_sequence(start)
+        assert arm.lib().ar_set_sequence(0xF0000001, None) == arm.ar.AR_ERR_INVALID
+        outs = [torch.empty((8, sets.n), dtype=torch.int16, device="cuda:0") for _ in range(4)]
+        bad = torch.zeros((), dtype=torch.int64, device="cuda:0")
+        seqs = []
+        for step in range(4):
+            for k in range(160):
+                s = k % 4
+                ar.allreduce(sets.ins[s], outs[k % 4], sets.n, k + 1)
+                bad += _count_bad(outs[k % 4], sets.want[s])
+            ar.step_end()
+            seqs.append(ar.query(14, 0))
+        assert ar.query(14, 1) == 4 * 160                     # calls keep counting
+        check_status_clean()
+    assert int(bad.item()) == 0
+    assert seqs[0] == start + per_step
+    assert seqs[1] == 0 and seqs[2] == per_step and seqs[3] == 2 * per_step, seqs

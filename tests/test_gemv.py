@@ -84,3 +84,59 @@ def test_projection_feeds_allreduce_bit_exact():
         ys = [host_bits(y) for y in yd]
         _check(W, x, ys, K)
         assert_bits_equal(host_bits(out), oracle.allreduce(ys))
+
+
+@pytest.mark.parametrize("cap", [0, 1024], ids=["full-projection", "budgeted-projection"])
+def test_concurrent_overlap_graph(cap):
+    """The overlap harness's concurrent form (the compute stream behind one
+    event, the communication stream behind another, "vLLM 分布式推理核心"
+    page, sections 二 and 三): one hipGraph holds `layers` projections on one
+    stream and `layers` independent AllReduces (16 KiB per rank, one-shot LL)
+    on a second, forked from and joined back to the first with events.  The
+    graph is replayed three times, with the outputs poisoned before each
+    replay; every AllReduce output must be bit-exact against the oracle and
+    every projection within its binary32 bound, after every replay."""
+    import tp_decode_comms_amd as ar
+    log("concurrent overlap graph, projection cap %d" % cap)
+    torch = torch_mod()
+    N, M, K, layers = 8, 8192, 1024, 6
+    W, x = _problem(11, N, M, K)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16).copy()).to("cuda:0")
+    Wd = [dev(w) for w in W]
+    xd = [dev(v) for v in x]
+    yd = [torch.empty(M, dtype=torch.int16, device="cuda:0") for _ in range(N)]
+    sets = [synth.input_set(2, s) for s in range(3)]
+    ins = [[dev(d[r]) for r in range(N)] for d in sets]
+    want = [oracle.allreduce(list(d)) for d in sets]
+    outs = [torch.empty((N, M), dtype=torch.int16, device="cuda:0") for _ in range(layers)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with ar_context(N, M, 1, 1) as a:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s1):
+            with torch.cuda.graph(g, stream=s1):
+                fork = torch.cuda.Event()
+                fork.record(s1)
+                s2.wait_event(fork)
+                for _ in range(layers):
+                    ar.gemv(Wd, xd, yd, M, K, stream=s1, max_workgroups=cap)
+                for k in range(layers):
+                    a.allreduce(ins[k % 3], outs[k], M, k + 1, stream=s2)
+                a.step_end(stream=s2)
+                join = torch.cuda.Event()
+                join.record(s2)
+                s1.wait_event(join)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            with torch.cuda.stream(s1):
+                for o in outs:
+                    o.fill_(-1)
+                for y in yd:
+                    y.fill_(-1)
+                g.replay()
+            torch.cuda.synchronize()
+            for k in range(layers):
+                assert_bits_equal(host_bits(outs[k]), want[k % 3], "replay %d call %d" % (rep, k))
+            _check(W, x, [host_bits(y) for y in yd], K)
+        del g
+        st = a.get_status()
+    assert st[0] == 0, st

@@ -47,7 +47,7 @@ def _run_calls(ar, datas, n, calls, out_list=None, f32=False):
     return outs
 
 
-SCOPES = [("auto", 0), ("device", 1)]
+SCOPES = [("auto", 0), ("device", 1), ("cross-xcd", 2)]
 WINDOWS = [("window-all", 0), ("window-4k", 4096)]
 
 
@@ -57,8 +57,9 @@ WINDOWS = [("window-all", 0), ("window-4k", 4096)]
 @pytest.mark.parametrize("N,n", [(8, 8192), (8, 4096 + 8), (4, 20008), (2, 968), (16, 3592),
                                  (8, 262144 + 480 * 3 + 16)])
 def test_variant_matches_oracle(name, algo, proto, N, n, scope_name, scope, win_name, window):
-    """Every variant in both coherence scopes: XCD-local (auto, where the
-    placement allows it) and device scope; the staged protocols with their
+    """Every variant in every placement and coherence scope: XCD-local (auto,
+    where the placement allows it), device scope, and ranks spread over the
+    XCDs (rank r on XCD r mod 8, device scope); the staged protocols with their
     whole staging window and with a 4 KiB window, which walks the larger
     messages in many rounds through the two buffers (the window does not
     apply to the protocols without staging)."""
@@ -197,6 +198,19 @@ def test_rejects_bad_calls():
         assert a.allreduce(ins, out, n, 1) == 0
         torch.cuda.synchronize()
     assert_bits_equal(host_bits(out), expect(data))
+
+
+def test_cross_xcd_placement_is_selected():
+    """AR_SCOPE_CROSS_XCD launches every call on the rank-per-XCD grid with
+    device-scope accesses; the default keeps part p of every rank on XCD p."""
+    import tp_decode_comms_amd as ar
+    with ar_context(8, 1 << 21) as a:
+        for n in (8192, 32 * 8192, 256 * 8192):
+            assert a.query(16, n) == 0 and a.query(8, n) == 1, n
+        a.set_scope(ar.AR_SCOPE_CROSS_XCD)
+        for n in (8192, 32 * 8192, 256 * 8192):
+            assert a.query(16, n) == 1 and a.query(8, n) == 0, n
+        assert ar.lib().ar_set_scope(3) == ar.ar.AR_ERR_INVALID
 
 
 def test_xcd_local_scope_is_used():

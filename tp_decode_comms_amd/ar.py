@@ -17,7 +17,7 @@ AR_ERR_STATE = -3
 AR_ERR_OOM = -4
 AR_ERR_HIP = -5
 AR_ERR_TIMEOUT = -6
-AR_SCOPE_AUTO, AR_SCOPE_DEVICE = 0, 1
+AR_SCOPE_AUTO, AR_SCOPE_DEVICE, AR_SCOPE_CROSS_XCD = 0, 1, 2
 
 AR_ALGO_AUTO, AR_ALGO_ONESHOT, AR_ALGO_TWOSHOT = 0, 1, 2
 AR_PROTO_AUTO, AR_PROTO_LL, AR_PROTO_LL128, AR_PROTO_SENTINEL, AR_PROTO_DIRECT = 0, 1, 2, 3, 4

@@ -288,6 +288,7 @@ struct Plan {
     uint32_t threads;
     uint32_t slice;
     bool local;         // XCD-local coherence scope
+    bool rank_xcd = false; // grid (1, N, parts): rank r on XCD r mod 8 (cross-XCD exchanges)
     bool unit4 = false; // in-place one-shot: 4-element lane units
     uint32_t rounds = 1; // rounds of the call (each takes its own flag)
 };
@@ -482,6 +483,7 @@ int plan_geometry(size_t n, bool f32, Plan *p)
         want = ONESHOT_DIRECT_MAX_PARTS;
     p->parts = (uint32_t)want;
     p->local = !f32 && g.scope == AR_SCOPE_AUTO && g.placement_ok && p->parts % ar::XCDS == 0;
+    p->rank_xcd = g.scope == AR_SCOPE_CROSS_XCD;
     p->rounds = rounds_of(*p, n);
     return AR_OK;
 }
@@ -536,7 +538,8 @@ hipError_t verify_placement(bool *ok)
     std::vector<uint32_t> h(grid);
     bool good = true;
     const uint32_t N = (uint32_t)g.n_ranks;
-    const uint32_t shapes[2][3] = {{grid, 1, 1}, {ar::XCDS, N, grid / (ar::XCDS * N)}};
+    const uint32_t shapes[3][3] = {{grid, 1, 1}, {ar::XCDS, N, grid / (ar::XCDS * N)},
+                                   {1, N, grid / N}};
     for (const auto &sh : shapes) {
         const uint32_t total = sh[0] * sh[1] * sh[2];
         for (uint32_t threads : {64u, 256u}) {
@@ -591,8 +594,11 @@ void fill_launch(const void *const *rank_bufs, void *out, size_t n, uint32_t epo
     a.parts = p.parts;
     a.slice = p.slice;
     // workgroup layout: grid (8, N, parts / 8) when parts % 8 == 0 (blocks
-    // of 8 parts x N ranks, so part p runs on XCD p % 8), else (1, N, parts)
-    a.xshift = p.parts % ar::XCDS == 0 ? 3u : 0u;
+    // of 8 parts x N ranks, so part p runs on XCD p % 8), else -- and always
+    // for the cross-XCD scope -- (1, N, parts): workgroup (r, p) has linear
+    // index r + N p, so with 8 ranks rank r runs on XCD r (with 4, on XCDs
+    // r and r + 4; with 16, ranks r and r + 8 share XCD r mod 8)
+    a.xshift = !p.rank_xcd && p.parts % ar::XCDS == 0 ? 3u : 0u;
     a.unit4 = p.unit4 ? 1u : 0u;
     uint64_t ticks = (uint64_t)g.watchdog_us * 100u;   // 100 MHz clock
     a.watchdog_ticks = (uint32_t)std::min<uint64_t>(ticks, 0xFFFFFFFFu);
@@ -713,6 +719,7 @@ int do_allreduce_norm(const void *const *rank_bufs, const void *const *residual,
         p.parts = (uint32_t)rows;
         p.slice = (uint32_t)slice_len(n, g.n_ranks);
         p.local = g.scope == AR_SCOPE_AUTO && g.placement_ok && p.parts % ar::XCDS == 0;
+        p.rank_xcd = g.scope == AR_SCOPE_CROSS_XCD;
     } else {
         rc = plan_geometry(n, false, &p);
         if (rc != AR_OK)
@@ -920,7 +927,7 @@ int ar_set_scope(int scope)
 {
     if (!g.live)
         return AR_ERR_NOT_INIT;
-    if (scope != AR_SCOPE_AUTO && scope != AR_SCOPE_DEVICE)
+    if (scope != AR_SCOPE_AUTO && scope != AR_SCOPE_DEVICE && scope != AR_SCOPE_CROSS_XCD)
         return AR_ERR_INVALID;
     g.scope = scope;
     return AR_OK;
@@ -1104,6 +1111,12 @@ long long ar_query(int key, size_t n)
         return rc != AR_OK ? rc : (long long)p.rounds;
     }
     case 13: return (long long)g.step_rounds;
+    case 16: {
+        if (n == 0 || n > g.max_elems || n % 8)
+            return AR_ERR_INVALID;
+        int rc = make_plan(n, false, &p);
+        return rc != AR_OK ? rc : (p.rank_xcd || p.parts % ar::XCDS != 0 ? 1 : 0);
+    }
     case 15: {
         int kind;
         if (n == 0 || choose_kind(n, &kind) != AR_OK) return AR_ERR_INVALID;
