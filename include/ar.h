@@ -227,6 +227,36 @@ int ar_allreduce_f32_debug(const void *const *rank_bufs, float *out_f32,
                            size_t n, uint32_t epoch, hipStream_t stream);
 
 /*
+ * ar_allreduce_noalloc -- the same AllReduce for callers that cannot
+ * allocate: code under hipGraph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Neither this call nor any set-up allocates, and it
+ * needs no ar_init: it runs the one-shot sentinel protocol with its inboxes
+ * in a static device array of 4 MiB per device (held until the process
+ * ends), whose address it takes with hipGetSymbolAddress on its first call
+ * on each device.  Sentinel validity is in-band and every consumed inbox
+ * slot is re-armed within the call, so no flag sequence or step end is
+ * needed; the window per (receiver, sender) pair and buffer is
+ * 4 MiB / (2 n_ranks^2), at most 64 KiB, walked in rounds for larger
+ * messages.  Device-scope coherence (no placement probe runs).
+ *   rank_bufs, out, stream: as ar_allreduce; inputs must not hold 0xFFFF.
+ *   n:         elements per rank, a multiple of 8, with all n_ranks output
+ *              copies within 2^31 bytes (AR_ERR_INVALID beyond that); n == 0
+ *              re-arms this device's inboxes (needed only after a call that a
+ *              watchdog ended) and launches nothing else.
+ *   n_ranks:   1..16.
+ * The first call on a device also enqueues the arming of its inboxes (a
+ * fill kernel, capture-safe; inside a capture it is captured, and the next
+ * call outside one arms again).  Every call on a device shares its array:
+ * calls that overlap on one device (different streams, no ordering) race.
+ * Single host thread.  A watchdog failure is recorded in the status record
+ * that ar_get_status reads (when a context exists); that call's outputs
+ * are undefined until a call with n == 0.
+ * Errors: AR_ERR_INVALID (sizes, pointers, alignment, aliasing), AR_ERR_HIP.
+ */
+int ar_allreduce_noalloc(const void *const *rank_bufs, void *out, size_t n, int n_ranks,
+                         hipStream_t stream);
+
+/*
  * ar_destroy -- free all staging.  The caller must have synchronised every
  * stream that used the library.  AR_ERR_NOT_INIT if there is no context.
  */

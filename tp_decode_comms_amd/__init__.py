@@ -10,7 +10,8 @@ from .ar import (  # noqa: F401
     AR_PROTO_AUTO, AR_PROTO_LL, AR_PROTO_LL128, AR_PROTO_SENTINEL, AR_PROTO_DIRECT,
     AR_PROTO_BARRIER, AR_PROTO_ATOMIC,
     AR_SCOPE_AUTO, AR_SCOPE_DEVICE, AR_SCOPE_CROSS_XCD,
-    ArError, lib, lib_path, init, destroy, allreduce, allreduce_f32_debug, allreduce_add_rmsnorm,
+    ArError, lib, lib_path, init, destroy, allreduce, allreduce_noalloc, allreduce_f32_debug,
+    allreduce_add_rmsnorm,
     add_rmsnorm, gemv, set_options,
     set_launch, set_scope, set_staging, set_watchdog, step_end, set_sequence, set_delays, set_timestamps,
     get_status, reset,

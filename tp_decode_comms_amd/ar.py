@@ -37,6 +37,7 @@ _SIGS = {
                                           _c_vp]),
     "ar_add_rmsnorm": (_c_int, [_c_vp, ctypes.POINTER(_c_vp), _c_vp, ctypes.c_float, _c_vp, _c_vp,
                                 _c_size, _c_size, _c_vp]),
+    "ar_allreduce_noalloc": (_c_int, [ctypes.POINTER(_c_vp), _c_vp, _c_size, _c_int, _c_vp]),
     "ar_destroy": (_c_int, []),
     "ar_set_options": (_c_int, [_c_int, _c_int]),
     "ar_set_launch": (_c_int, [_c_int, _c_int]),
@@ -142,6 +143,14 @@ def allreduce(rank_bufs, out, n, epoch, stream=None, check=True):
     rc = lib().ar_allreduce(_rank_array(rank_bufs), _ptr(out), int(n), int(epoch),
                             _stream_handle(stream))
     return _check("ar_allreduce", rc) if check else rc
+
+
+def allreduce_noalloc(rank_bufs, out, n, stream=None, check=True):
+    """The allocation-free AllReduce (no ar_init needed): rank_bufs N bf16
+    device tensors, out bf16 [N, n]; n == 0 re-arms the device's inboxes."""
+    rc = lib().ar_allreduce_noalloc(_rank_array(rank_bufs), _ptr(out) if out is not None else None,
+                                    int(n), len(rank_bufs), _stream_handle(stream))
+    return _check("ar_allreduce_noalloc", rc) if check else rc
 
 
 def allreduce_add_rmsnorm(rank_bufs, residuals, gamma, eps, out_h, out_y, rows, hidden, epoch,

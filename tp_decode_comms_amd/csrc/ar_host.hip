@@ -751,6 +751,78 @@ int do_allreduce_norm(const void *const *rank_bufs, const void *const *residual,
 }
 
 
+// ---------------------------------------------------------------- no allocation
+// The allocation-free variant of ar_allreduce (ar_allreduce_noalloc): the
+// one-shot sentinel protocol with its inboxes in `scratch`, a file-scope
+// device array (one per device, held until the process ends), so neither
+// the call nor any set-up allocates.  Sentinel validity is in-band (an
+// element is data once it is not 0xFFFF) and every consumed slot is re-armed
+// within the call, so the inboxes need no flag sequence and are armed again
+// when each call ends.  The array starts zeroed -- zero is data, not the
+// sentinel -- so the first call on a device arms it first.
+constexpr size_t NOALLOC_BYTES = size_t(4) << 20;          // [recv][send][2 buffers] x window
+constexpr size_t NOALLOC_WINDOW_MAX = 64 * 1024;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static __device__ __align__(256) uint32_t scratch[NOALLOC_BYTES / 4];
+
+struct NoAllocDevice {
+    bool ready = false;                 // symbol address and device facts taken
+    bool armed = false;                 // an eager arming has been enqueued
+    uint32_t *ptr = nullptr;            // this device's copy of `scratch`
+    uint32_t *ctl = nullptr;            // this device's control block (status record)
+    int cu_count = 0;
+    int per_cu[2] = {0, 0};             // resident workgroups per CU: <= 8 ranks, <= 16 ranks
+};
+NoAllocDevice g_na[NOALLOC_MAX_DEVICES];
+
+// Window per (receiver, sender) pair and buffer: the largest multiple of
+// 1 KiB with N^2 pairs x 2 buffers in the array, at most 64 KiB.
+size_t noalloc_window(int n_ranks)
+{
+    const size_t w = NOALLOC_BYTES / (2 * (size_t)n_ranks * (size_t)n_ranks) / 1024 * 1024;
+    return std::min(w, NOALLOC_WINDOW_MAX);
+}
+
+int noalloc_setup(int dev, NoAllocDevice *d)
+{
+    if (d->ready)
+        return AR_OK;
+    // with `dev` current: the array's address on this device (the host-side
+    // name `scratch` is not a device address), the control block's, and the
+    // facts the grid is sized with
+    hipError_t e = hipGetSymbolAddress((void **)&d->ptr, HIP_SYMBOL(scratch));
+    if (e == hipSuccess)
+        e = ar::control_block(&d->ctl);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&d->cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+    for (int i = 0; e == hipSuccess && i < 2; ++i)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &d->per_cu[i], ar::kernel_for(ar::K_ONESHOT_SENTINEL, i == 0 ? 8 : 16, false, false, 0),
+            512, 0);
+    if (e != hipSuccess) {
+        d->ptr = nullptr;
+        return hip_fail(e);
+    }
+    d->ready = true;
+    return AR_OK;
+}
+
+// Arms every inbox slot with the sentinel (a fill kernel, no memset node:
+// capture-safe).  Marked armed only when enqueued eagerly: an arming
+// captured into a graph runs only when that graph does.
+int noalloc_arm(NoAllocDevice *d, hipStream_t stream)
+{
+    hipError_t e = ar::launch_fill(d->ptr, NOALLOC_BYTES / 4, ar::SENT_WORD, stream);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    d->armed = cs == hipStreamCaptureStatusNone;
+    return AR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1020,6 +1092,71 @@ int ar_get_status(uint32_t out[4])
     if (e != hipSuccess)
         return hip_fail(e);
     return out[0] == ar::STATUS_TIMEOUT ? AR_ERR_TIMEOUT : AR_OK;
+}
+
+int ar_allreduce_noalloc(const void *const *rank_bufs, void *out, size_t n, int n_ranks,
+                         hipStream_t stream)
+{
+    if (n_ranks < 1 || n_ranks > AR_MAX_RANKS)
+        return AR_ERR_INVALID;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+        return AR_ERR_INVALID;
+    NoAllocDevice &d = g_na[dev];
+    int rc = noalloc_setup(dev, &d);
+    if (rc != AR_OK)
+        return rc;
+    if (n == 0)                          // re-arm (after a call that a watchdog ended)
+        return noalloc_arm(&d, stream);
+    // sizes: 8-element vectors; all N output copies below 2^31 bytes (the
+    // kernels' skipped-access offset lies past every descriptor)
+    if (rank_bufs == nullptr || out == nullptr || n % 8 != 0 ||
+        n * (size_t)n_ranks * 2 > (size_t)ar::OFF_NONE)
+        return AR_ERR_INVALID;
+    const uintptr_t o = (uintptr_t)out, o_end = o + 2 * n * (size_t)n_ranks;
+    if (o % 16)
+        return AR_ERR_INVALID;
+    for (int r = 0; r < n_ranks; ++r) {
+        const uintptr_t b = (uintptr_t)rank_bufs[r];
+        if (b == 0 || b % 16 || (b < o_end && o < b + 2 * n))
+            return AR_ERR_INVALID;
+    }
+    if (!d.armed && (rc = noalloc_arm(&d, stream)) != AR_OK)
+        return rc;
+    // geometry: 64 chunks of 8 elements per workgroup and round, one round of
+    // every part within the window, the grid resident at once
+    const size_t win = noalloc_window(n_ranks);
+    const uint64_t chunks = n / 8;
+    uint64_t cap = (uint64_t)d.per_cu[n_ranks <= 8 ? 0 : 1] * (uint64_t)d.cu_count / (uint64_t)n_ranks;
+    cap = std::min<uint64_t>(cap, win / STAGE_ROUND_BYTES);
+    if (cap == 0)
+        return AR_ERR_INVALID;
+    uint64_t parts = std::max<uint64_t>(1, ceil_div(chunks, 64));
+    const uint64_t up = round_up(parts, ar::XCDS);
+    parts = up <= cap ? up : (cap >= ar::XCDS ? cap / ar::XCDS * ar::XCDS : cap);
+    parts = std::min(parts, cap);
+    Launch a;
+    memset(&a, 0, sizeof a);
+    for (int r = 0; r < n_ranks; ++r)
+        a.in[r] = rank_bufs[r];
+    a.out = out;
+    a.s1 = (char *)d.ptr;
+    a.s1_stride = (uint32_t)win;
+    a.ctl = d.ctl;                      // status record: the one ar_get_status reads
+    a.n = (uint32_t)n;
+    a.n_ranks = (uint32_t)n_ranks;
+    a.epoch = 1;                        // buffer parity and records only: no flags
+    a.parts = (uint32_t)parts;
+    a.slice = (uint32_t)slice_len(n, n_ranks);
+    a.xshift = parts % ar::XCDS == 0 ? 3u : 0u;
+    a.watchdog_ticks = DEFAULT_WATCHDOG_US * 100u;
+    e = ar::launch_ar(ar::K_ONESHOT_SENTINEL, false, false, 0, a, 512, stream);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    return AR_OK;
 }
 
 int ar_reset(hipStream_t stream)
