@@ -18,9 +18,11 @@
  *   - sentinel: receive buffers are pre-filled with the bf16 NaN pattern
  *     0xFFFF; any other value is data; the receiver re-fills what it read
  *     (item 2, Sentinel; reset()/resetRange() in section "统一原语与API设计");
- *   - double buffering: consecutive calls use buffer parity epoch & 1, so a
- *     receipt of call k from a peer proves the peer finished call k-1
- *     (item 3, double buffering);
+ *   - double buffering: a message is walked in rounds through two
+ *     fixed-size staging windows per rank; round j uses window (flag of
+ *     round j) & 1, and receiving round j from every peer proves each peer
+ *     finished reading round j-1, so its window may be overwritten (item 3,
+ *     double buffering);
  *   - LL128-style lines: 128-byte lines of 120 payload bytes and an 8-byte
  *     flag, the flag written after the payload (item 4 gives the 128-byte
  *     line; its NVLink atomic-add form has no counterpart here).
@@ -136,7 +138,13 @@ enum ar_proto {
 int ar_init(int n_ranks, size_t max_elems);
 
 /*
- * ar_allreduce -- one AllReduce call, enqueued on `stream` (asynchronous).
+ * ar_allreduce -- one AllReduce call, enqueued on `stream` (asynchronous):
+ * every rank's input summed element by element, the sum given to every rank
+ * ("微秒必争…", section "张量并行与AllReduce"); one-shot = each rank publishes
+ * its value, receives and reduces all N in registers (recvReduce) and writes,
+ * two-shot = reduce-scatter then all-gather (section "统一原语与API设计" and
+ * its table of variants), synchronised by the in-band mechanisms of section
+ * "四大核心机制" (see ar_set_options for the choice).
  *   rank_bufs: HOST array of n_ranks DEVICE pointers, rank r's bf16 input [n];
  *              copied by value into the launch, so the host array may be
  *              reused as soon as the call returns (graph-capture safe).
@@ -145,7 +153,11 @@ int ar_init(int n_ranks, size_t max_elems);
  *   n:         elements per rank, 1..max_elems, a multiple of 8.
  *   epoch:     call number within the current step: 1 for the first call
  *              after ar_init / ar_reset / ar_step_end, then previous + 1;
- *              at most 65535.  Buffer parity is epoch & 1.
+ *              at most 65535.  A call walks its message in rounds through the
+ *              staging windows (ar_set_staging); round j of a call uses flag
+ *              f + j and buffer (f + j) & 1, f following the previous call's
+ *              last flag (for one-round calls the buffer alternates call by
+ *              call).
  *   stream:    HIP stream (0 = legacy default stream).
  * All pointers 16-byte aligned.  Inputs must be finite bf16 values; with the
  * sentinel protocol an input equal to 0xFFFF breaks the contract (a receiver
@@ -220,8 +232,10 @@ int ar_add_rmsnorm(const void *a, const void *const *residual, const void *gamma
 /*
  * ar_allreduce_f32_debug -- the same call, but writes the binary32
  * accumulators (before the bf16 rounding) to out_f32, DEVICE float
- * [n_ranks][n].  Same contract otherwise; advances the epoch sequence like
- * ar_allreduce.
+ * [n_ranks][n]: the register sums of recvReduce ("微秒必争…", section
+ * "统一原语与API设计") made visible, for checking the fold itself.  Same
+ * contract otherwise (device scope always); advances the epoch sequence
+ * like ar_allreduce.
  */
 int ar_allreduce_f32_debug(const void *const *rank_bufs, float *out_f32,
                            size_t n, uint32_t epoch, hipStream_t stream);
@@ -257,8 +271,10 @@ int ar_allreduce_noalloc(const void *const *rank_bufs, void *out, size_t n, int 
                          hipStream_t stream);
 
 /*
- * ar_destroy -- free all staging.  The caller must have synchronised every
- * stream that used the library.  AR_ERR_NOT_INIT if there is no context.
+ * ar_destroy -- free all staging (the counterpart of ar_init; the pages'
+ * library is a drop-in behind the collective's interface, "SiFAR" page,
+ * section "实际部署考量").  The caller must have synchronised every stream
+ * that used the library.  AR_ERR_NOT_INIT if there is no context.
  */
 int ar_destroy(void);
 
@@ -278,8 +294,9 @@ int ar_destroy(void);
 int ar_set_options(int algo, int proto);
 
 /*
- * ar_set_launch -- tuning: workgroups per rank (0 = automatic) and threads
- * per workgroup (64, 128 or 256; 0 = automatic).  The LL kernel always
+ * ar_set_launch -- tuning (the per-optimisation controls of a drop-in
+ * collective, "SiFAR" page, section "实际部署考量"): workgroups per rank
+ * (0 = automatic) and threads per workgroup (64, 128 or 256; 0 = automatic).  The LL kernel always
  * uses one wave per rank (64 x the next power of two >= N threads), the
  * sentinel kernels 512 threads and the LL128 kernels 256: their waves share
  * the peers of a tile.  The
@@ -328,7 +345,11 @@ int ar_set_scope(int scope);
 int ar_set_staging(size_t window_bytes);
 
 /*
- * ar_set_watchdog -- per-poll time budget in microseconds (default 200000).
+ * ar_set_watchdog -- per-poll time budget in microseconds (default 200000,
+ * or AR_WATCHDOG_MS at ar_init).  It bounds the waits the flag protocols
+ * introduce: a sentinel receiver whose data never leaves the sentinel
+ * pattern would otherwise wait forever ("微秒必争…", section "四大核心机制",
+ * item 2).
  * A poll that exceeds it records {6, rank, source, flag} in the device status
  * record and its workgroup stops (in the fused norm's wait for the row's
  * block sums, source is the waiting rank itself); the other workgroups of
@@ -353,7 +374,9 @@ int ar_set_watchdog(uint32_t budget_us);
 int ar_step_end(hipStream_t stream);
 
 /*
- * ar_set_sequence -- test hook: sets the device round sequence to `seq`
+ * ar_set_sequence -- test hook for the flag sequence that tags every round
+ * (the double buffering of "微秒必争…", section "四大核心机制", item 3, needs
+ * a flag unique to each round): sets the device round sequence to `seq`
  * (<= 0xF0000000) with a kernel on `stream`, so that a test can run steps
  * across the sequence's restart.  Only between steps (AR_ERR_STATE after a
  * call of an open step).  Errors: AR_ERR_NOT_INIT, AR_ERR_STATE,
@@ -362,7 +385,10 @@ int ar_step_end(hipStream_t stream);
 int ar_set_sequence(uint32_t seq, hipStream_t stream);
 
 /*
- * ar_set_delays -- test hook: per (call, rank) start delays.  dev_ns is a
+ * ar_set_delays -- test hook: per (call, rank) start delays, so that ranks
+ * arrive at a call at different times as real GPUs do (the slowest one
+ * sets the pace: the small-message essay, section 4.2; "SiFAR" page,
+ * section "技术三").  dev_ns is a
  * DEVICE uint32 table [calls][n_ranks] of nanoseconds; call with flag f uses
  * row (f - 1) mod calls.  Every workgroup of rank r spins on the constant
  * 100 MHz clock for that long before its first step.  NULL disables.  The
@@ -397,10 +423,12 @@ int ar_set_delays(const uint32_t *dev_ns, size_t calls);
 int ar_set_timestamps(uint64_t *dev_ts, size_t slots, size_t records_per_slot, int phases);
 
 /*
- * ar_get_status -- copy the device status record {code, rank, source, flag}
+ * ar_get_status -- copy the device status record {code, rank, source, call}
  * into out[4] (synchronises the device first).  code is 0 or 6 (a watchdog
- * fired: rank that gave up, source it waited for, call flag).  Returns
- * AR_ERR_TIMEOUT if a watchdog fired, else AR_OK.
+ * fired -- the deadlock a lost sentinel would cause, "微秒必争…", section
+ * "四大核心机制", item 2 -- with the rank that gave up, the source it waited
+ * for and the call number, counted from 1 since ar_init / ar_reset).
+ * Returns AR_ERR_TIMEOUT if a watchdog fired, else AR_OK.
  */
 int ar_get_status(uint32_t out[4]);
 
@@ -412,14 +440,19 @@ int ar_get_status(uint32_t out[4]);
  */
 int ar_reset(hipStream_t stream);
 
-/* ar_strerror -- static description of a status code. */
+/* ar_strerror -- static description of a status code (the library reports
+ * rather than aborts, as a drop-in collective must: "SiFAR" page, section
+ * "实际部署考量"). */
 const char *ar_strerror(int status);
 
-/* ar_last_hip_error -- the hipError_t behind the last AR_ERR_HIP. */
+/* ar_last_hip_error -- the hipError_t behind the last AR_ERR_HIP (same
+ * reason as ar_strerror). */
 int ar_last_hip_error(void);
 
 /*
- * ar_query -- introspection for tests and benchmarks.  key:
+ * ar_query -- introspection for tests and benchmarks (what NCCL_DEBUG=INFO
+ * reports per collective -- chosen algorithm, protocol, geometry -- the
+ * small-message essay, section 4.4).  key:
  *   0 n_ranks, 1 max_elems, 2 algorithm a call of n elements would use,
  *   3 its protocol, 4 workgroups it would launch, 5 threads per workgroup,
  *   6 resident-workgroup capacity of the device for that kernel, 7 the host
