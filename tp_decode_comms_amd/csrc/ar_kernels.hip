@@ -278,12 +278,21 @@ __device__ __forceinline__ void store2(__amdgpu_buffer_rsrc_t o, uint32_t elem, 
     }
 }
 
-// Output-store cache policy of the one-shot LL and in-place one-shot kernels:
-// plain.  Streaming device-scope stores (no dirty lines for the launch
-// boundary to write back) measured 2.44 -> 2.99 us on 8 x 16 KiB LL,
-// 2.35 -> 2.46 on the in-place one-shot, and gained 1.3% only at 512 KiB.
+// Output-store cache policies.  Outputs are never read inside the launch,
+// and every line a launch leaves dirty in an L2 is written back at the
+// launch boundary before the next launch may start.  A non-temporal store
+// (nt, no scope bit) streams its line out without that write-back and
+// without waiting for memory on the way: 8 x 512 KiB in-place one-shot
+// 4.31 -> 4.10 us per call, and the line-protocol kernels below gain more;
+// 8 x 16 KiB one-shot LL is unchanged (2.43), and there it stays plain.
+// Streaming device-scope stores (nt with sc1, written through to memory
+// inside the launch) cost: 8 x 16 KiB LL 2.44 -> 2.99 us, 8 x 16 KiB
+// in-place one-shot 2.35 -> 2.46.
 constexpr int LL_OUT = CP_PLAIN;
-constexpr int D1_OUT = CP_PLAIN;
+constexpr int D1_OUT = CP_NT;
+constexpr int SENT_OUT = CP_NT;         // sentinel kernels (16 x 57344 two-shot 5.60 -> 5.49 us)
+// The fused-norm kernels store h and y non-temporal too (CP_NT at each
+// store): 8 x 512 KiB fused AllReduce + norm 6.64 -> 5.90 us per call.
 
 // ============================================================ arrivals
 // Rank s announces "my input for this call is final" by storing the call's
@@ -635,7 +644,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
         aw.x = pack_bf16(v[0], v[1]);
         aw.y = pack_bf16(v[2], v[3]);
         const u32x2 hw = add_round4(aw, rw);
-        st8<CP_PLAIN>(hw, oh, cch * 8u);
+        st8<CP_NT>(hw, oh, cch * 8u);
         hk = hw;
         const float s = wave_sum(sumsq4(hw));
         if (lane == 0u) {
@@ -672,7 +681,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
             const uint32_t cc = c0 + lane;
             const u32x2 hw = it == 0u ? h0 : ld8<CP_PLAIN>(oh, cc * 8u);
             const u32x2 gw = it == 0u ? g0 : ld8<CP_PLAIN>(gr, ((cc * 4u) % L.hidden) * 2u);
-            st8<CP_PLAIN>(scale4(hw, gw, r), oy, cc * 8u);
+            st8<CP_NT>(scale4(hw, gw, r), oy, cc * 8u);
         }
     }
     mark(c, c.t_data);
@@ -764,9 +773,9 @@ __global__ __launch_bounds__(256) void k_oneshot_direct_norm(const NormLaunch L)
         aw2.x = pack_bf16(acc2.v[0], acc2.v[1]);
         aw2.y = pack_bf16(acc2.v[2], acc2.v[3]);
         const u32x2 hw = add_round4(aw, rw), hw2 = add_round4(aw2, rw2);
-        st8<CP_PLAIN>(hw, oh, e * 2u);
+        st8<CP_NT>(hw, oh, e * 2u);
         if (two)
-            st8<CP_PLAIN>(hw2, oh, (e + NORM_BLOCK) * 2u);
+            st8<CP_NT>(hw2, oh, (e + NORM_BLOCK) * 2u);
         if (first) {
             h0 = hw;
             h1 = hw2;
@@ -794,7 +803,7 @@ __global__ __launch_bounds__(256) void k_oneshot_direct_norm(const NormLaunch L)
         const uint32_t e = b * NORM_BLOCK + lane * 4u;
         const u32x2 hw = b == bbeg ? h0 : b == bbeg + 1u ? h1 : ld8<CP_PLAIN>(oh, e * 2u);
         const u32x2 gw = b == bbeg ? g0 : b == bbeg + 1u ? g1 : ld8<CP_PLAIN>(gr, (e % L.hidden) * 2u);
-        st8<CP_PLAIN>(scale4(hw, gw, r), oy, e * 2u);
+        st8<CP_NT>(scale4(hw, gw, r), oy, e * 2u);
     }
     mark(c, c.t_data);
     finish(a, c);
@@ -897,13 +906,13 @@ __global__ __launch_bounds__(1024) void k_oneshot_rows_norm(const NormLaunch L)
         hk[k] = add_round4(aw, rk[k]);
         hk[k + 1] = add_round4(aw2, rk[k + 1]);
         if (in1) {
-            st8<CP_PLAIN>(hk[k], oh, e * 2u);
+            st8<CP_NT>(hk[k], oh, e * 2u);
             const float sq = wave_sum(sumsq4(hk[k]));
             if (lane == 0u)
                 bsum[j] = sq;
         }
         if (in2) {
-            st8<CP_PLAIN>(hk[k + 1], oh, e2 * 2u);
+            st8<CP_NT>(hk[k + 1], oh, e2 * 2u);
             const float sq = wave_sum(sumsq4(hk[k + 1]));
             if (lane == 0u)
                 bsum[j2] = sq;
@@ -923,7 +932,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_rows_norm(const NormLaunch L)
     for (int k = 0; k < (int)ROWS_PER_WAVE; ++k) {
         const uint32_t j = wave + ROWS_WAVES * k;
         if (live && j < B)
-            st8<CP_PLAIN>(scale4(hk[k], gk[k], r), oy, (row0 + j * NORM_BLOCK + lane * 4u) * 2u);
+            st8<CP_NT>(scale4(hk[k], gk[k], r), oy, (row0 + j * NORM_BLOCK + lane * 4u) * 2u);
     }
     mark(c, c.t_data);
     finish(a, c);
@@ -1037,7 +1046,7 @@ __device__ __forceinline__ bool sent_round(const Launch &a, Ctx0 &c, const Ctl &
             if ((uint32_t)s < N) {
                 if (s == 0) acc.init(t[s]); else acc.add(t[s]);
             }
-        store8<F32>(o, ch * 8u, acc);
+        store8<F32, SENT_OUT>(o, ch * 8u, acc);
     }
     // re-arm what was consumed (resetRange), off the path to the output;
     // the barrier below waits for these stores (and the polls still in
@@ -1487,14 +1496,16 @@ __global__ __launch_bounds__(256) void k_twoshot_barrier(const Launch a)
 constexpr int L128_WAVES = 4;
 
 // Cache policies and the arrival-wait form of the LL128 kernels, measured at
-// 8 x 512 KiB and 8 x 4 MiB (graphs, same box): streaming device-scope
-// output stores in the two-shot cut the 4 MiB call 24.3 -> 23.1 us (no dirty
-// lines left for the launch boundary's write-back) but slow the 512 KiB
-// call 4.95 -> 5.2 us, the workload the line protocol serves, so they stay
-// plain; streaming reduce-scatter loads and a single polling wave per
-// workgroup move both within 1%.
-constexpr int L128_OUT1 = CP_PLAIN;     // one-shot output stores
-constexpr int L128_OUT2 = CP_PLAIN;     // two-shot output stores
+// 8 x 512 KiB and 8 x 4 MiB (graphs, same box): non-temporal output stores
+// (see LL_OUT) cut the 512 KiB one-shot 8.29 -> 7.84 us, the 512 KiB
+// two-shot 4.95 -> 4.66 and the 4 MiB two-shot 24.2 -> 20.8; streaming
+// device-scope ones slow the 512 KiB two-shot to 5.2 (they wait for memory
+// inside the launch).  Non-temporal staging stores slow every line-protocol
+// call (512 KiB two-shot 5.62): the peers' polls then miss the L2.
+// Streaming reduce-scatter loads and a single polling wave per workgroup
+// move both within 1%.
+constexpr int L128_OUT1 = CP_NT;        // one-shot output stores
+constexpr int L128_OUT2 = CP_NT;        // two-shot output stores
 constexpr bool L128_ARRIVE_WG = false;  // two-shot arrival wait: one polling wave per workgroup
 constexpr int L128_RS_LD = CP_DEV;      // two-shot in-place reduce-scatter loads
 
@@ -2019,7 +2030,7 @@ __device__ __forceinline__ bool ts_round(const Launch &a, Ctx0 &c, const Ctl &ct
         } else {
             const u32x4 rv = acc.bf16();
             red[lane] = rv;
-            st16<CP_PLAIN>(rv, oa, (q * a.n + q * L + e) * esz);
+            st16<SENT_OUT>(rv, oa, (q * a.n + q * L + e) * esz);
         }
     }
     // re-arm the consumed reduce-scatter slots (resetRange); the round's
@@ -2055,7 +2066,7 @@ __device__ __forceinline__ bool ts_round(const Launch &a, Ctx0 &c, const Ctl &ct
 #pragma unroll
     for (int j = 0; j < PW; ++j)
         if ((mine >> j) & 1u) {
-            st16<CP_PLAIN>(V[j], oa, (q * a.n + peer(j) * L + e) * esz);
+            st16<SENT_OUT>(V[j], oa, (q * a.n + peer(j) * L + e) * esz);
             st16<Pol<LOCAL>::ST>(sentinel4(), agr, box(q, peer(j)));
         }
     // the round's re-arms (both inboxes) are performed before the next
