@@ -208,11 +208,19 @@ def timestamp_stats(tsh, calls_per_replay):
     gaps = (start[1:] - end[:-1])[within] * US_PER_TICK
     spans = (end - start) * US_PER_TICK
     starts = np.where(live, t[:, :, 0], np.nan)
-    waits = np.where(live & (t[:, :, 1] != 0), t[:, :, 1] - t[:, :, 0], np.nan)
+    marked = live & (t[:, :, 1] != 0) & (t[:, :, 2] != 0)
+    waits = np.where(marked, t[:, :, 1] - t[:, :, 0], np.nan)
+    datas = np.where(marked, t[:, :, 2] - t[:, :, 1], np.nan)
+    tails = np.where(marked, t[:, :, 3] - t[:, :, 2], np.nan)
+    ends = np.where(live, t[:, :, 3], np.nan)
     with np.errstate(all="ignore"):
         phases = {"last_start_us": (np.nanmax(starts, axis=1) - start) * US_PER_TICK,
                   "median_start_us": (np.nanmedian(starts, axis=1) - start) * US_PER_TICK,
                   "median_wave_sync_wait_us": np.nanmedian(waits, axis=1) * US_PER_TICK,
+                  "median_wave_data_us": np.nanmedian(datas, axis=1) * US_PER_TICK,
+                  "p90_wave_data_us": np.nanpercentile(datas, 90, axis=1) * US_PER_TICK,
+                  "median_wave_tail_us": np.nanmedian(tails, axis=1) * US_PER_TICK,
+                  "median_wave_end_us": (np.nanmedian(ends, axis=1) - start) * US_PER_TICK,
                   "last_sync_us": last(1), "last_data_us": last(2), "end_us": spans}
     return intervals, spans, gaps, phases
 
@@ -709,14 +717,20 @@ def recorded_traffic(kernel_key):
     return None
 
 
-def calib_copy(torch, reps=20):
-    """A plain copy of known size for scaling the FETCH_SIZE/WRITE_SIZE counters."""
-    src = torch.ones(16 * 1024 * 1024, dtype=torch.int16, device="cuda:0")   # 32 MiB
-    dst = torch.empty_like(src)
-    for _ in range(reps):
-        dst.copy_(src)
+def calib_copy(torch, pairs=16, passes=2):
+    """A plain copy of known size for scaling the FETCH_SIZE/WRITE_SIZE
+    counters: 32 MiB device-to-device copies rotating over `pairs` buffer
+    pairs (16 pairs: a 1 GiB footprint, four times the 256 MiB memory-side
+    cache, so every pass reads from HBM)."""
+    srcs = [torch.full((16 * 1024 * 1024,), k, dtype=torch.int16, device="cuda:0")
+            for k in range(pairs)]                                          # 32 MiB each
+    dsts = [torch.empty_like(x) for x in srcs]
+    for _ in range(passes):
+        for k in range(pairs):
+            dsts[k].copy_(srcs[k])
     torch.cuda.synchronize()
-    return {"bytes_read": 32 << 20, "bytes_written": 32 << 20, "reps": reps}
+    return {"bytes_read": 32 << 20, "bytes_written": 32 << 20, "pairs": pairs, "passes": passes,
+            "footprint_bytes": 2 * pairs * (32 << 20)}
 
 
 def _time_calls(fn, budget_s, min_reps, max_reps=None):

@@ -119,6 +119,12 @@ def test_timestamp_stats_per_call_figures():
     assert np.allclose(phases["last_sync_us"], 0.6)
     assert np.allclose(phases["last_data_us"], 1.3)
     assert np.allclose(phases["end_us"], 2.0)
+    # per wave: waits 50/40, data 50/70, tails 50/70 ticks; medians of two
+    assert np.allclose(phases["median_wave_sync_wait_us"], 0.45)
+    assert np.allclose(phases["median_wave_data_us"], 0.6)
+    assert np.allclose(phases["p90_wave_data_us"], 0.68)
+    assert np.allclose(phases["median_wave_tail_us"], 0.6)
+    assert np.allclose(phases["median_wave_end_us"], 1.75)
     lat = {"instrumented": {"agreement": 0.03, "interval_us": {"p50": 2.4, "p99": 2.5}},
            "event_us_per_call": {"p50": 2.5, "p99": 2.6}}
     assert b.headline_latency(lat)[:2] == (2.4, 2.5)
