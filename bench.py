@@ -31,7 +31,7 @@ Every leg runs under its own guard: a leg that fails records its error under
 device-side failure no further GPU leg runs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
-                       [--only latency|bw|overlap|configs|calib]
+                       [--only latency|bw|overlap|configs|c3|calib]
 """
 import argparse
 import json
@@ -870,7 +870,7 @@ def main():
     ap.add_argument("--quick", action="store_true")
     ap.add_argument("--only", default="all",
                     choices=["all", "latency", "bw", "overlap", "atomic", "norm", "configs",
-                             "calib"])
+                             "calib", "c3"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the N ranks are emulated as workgroup sets of one "
@@ -1007,8 +1007,8 @@ def main():
             r = legs.run(key, lambda: bench_norm(torch, ar, cid, replays=reps))
             if r is not None:
                 log("  %r" % {k: v for k, v in r.items() if k != "workload"})
+    reps = 3 if args.quick else 10
     if only in ("all", "configs"):
-        reps = 3 if args.quick else 10
         wl1 = Workload(torch, 1, 4)
         for proto, key in ((SENT, "c1_sentinel"), (LL, "c1_ll")):
             log("4 ranks x 4096, 1000-call graph, %s" % key)
@@ -1016,6 +1016,7 @@ def main():
             if r is not None:
                 r["workload"] = ("4 ranks x [1x4096] bf16, N(0,1), one-shot, 1000 calls in one "
                                  "hipGraph")
+    if only in ("all", "configs", "c3"):
         wl3 = Workload(torch, 3, 4)
         for algo, key in ((ONE, "c3_oneshot_ll128"), (TWO, "c3_twoshot_ll128")):
             log("8 ranks x 512 KiB LL128, 160-call graph, %s" % key)
@@ -1026,6 +1027,7 @@ def main():
                                  "LL128, 160 calls in one hipGraph")
                 r["gbps_p50"] = wl3.b_alg / (r["event_us_per_call"]["p50"] * 1e-6) / 1e9
         del wl3
+    if only in ("all", "configs"):
         import synth
         wl5 = Workload(torch, 5, 8)
         calls5 = 2000 if args.quick else 10000

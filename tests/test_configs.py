@@ -289,6 +289,21 @@ def test_config5_delays_small_window_10000_calls(algo):
     assert bad == 0
 
 
+@pytest.mark.parametrize("algo,proto,n", [(ONE, LL, 8200), (ONE, LL, 8192), (ONE, LL128, 65536),
+                                           (ONE, LL128, 131072), (TWO, LL128, 262144)])
+def test_default_window_takes_one_round(algo, proto, n):
+    """With the default windows a message that fits them runs in one round
+    even when its part count is rounded up to a multiple of 8 (the window
+    holds whole 8-part rounds)."""
+    log("default window, algo %d proto %d n %d" % (algo, proto, n))
+    sets = Sets(2, 2, n=n, n_ranks=8)
+    with ar_context(8, n, algo, proto) as ar:
+        assert _rounds(ar, n) == 1, (ar.query(15, n), ar.query(4, n))
+        bad = _stream_calls(ar, sets, 6)
+        check_status_clean()
+    assert bad == 0
+
+
 def test_staging_window_validation():
     import tp_decode_comms_amd as arm
     with ar_context(8, 1 << 20) as ar:

@@ -56,6 +56,11 @@ constexpr size_t STAGE_WINDOW_MAX = 1024 * 1024;       // LL, LL128: per rank an
 constexpr size_t STAGE_INBOX_MAX = 256 * 1024;         // sentinel: per pair and buffer
 constexpr size_t STAGE_ROUND_BYTES = 1024;             // one part's round (per line group for LL128)
 constexpr size_t STAGE_WINDOW_MIN = 4096;              // a whole LL128 batch of 4 groups
+// A window holds whole rounds of a multiple of 8 parts (the part count is
+// rounded up to one, so that part p runs on XCD p % 8): windows are sized in
+// multiples of 8 part-rounds (LL128: of batches of 4 groups).
+constexpr size_t STAGE_QUANTUM = 8 * STAGE_ROUND_BYTES;
+constexpr size_t STAGE_QUANTUM_L128 = 8 * 4 * STAGE_ROUND_BYTES;
 size_t oneshot_limit(int proto)
 {
     switch (proto) {
@@ -856,14 +861,14 @@ int ar_init(int n_ranks, size_t max_elems)
     const size_t me = g.max_elems;
     // staging windows: what the largest message needs in one round, at most
     // the fixed window sizes (larger messages take several rounds)
-    auto window = [](size_t need, size_t most) {
-        return std::max(STAGE_WINDOW_MIN, std::min(round_up(need, STAGE_WINDOW_MIN), most));
+    auto window = [](size_t need, size_t quantum, size_t most) {
+        return std::max(STAGE_WINDOW_MIN, std::min(round_up(need, quantum), most));
     };
-    g.ll_stride = window(me * 4, STAGE_WINDOW_MAX);
+    g.ll_stride = window(me * 4, STAGE_QUANTUM, STAGE_WINDOW_MAX);
     g.l128_stride = window((me + ar::L128_ELEMS - 1) / ar::L128_ELEMS * ar::L128_BYTES,
-                           STAGE_WINDOW_MAX);
-    g.s1_stride = window(me * 2, STAGE_INBOX_MAX);
-    g.s2_stride = window(slice_len(me, n_ranks) * 2, STAGE_INBOX_MAX);
+                           STAGE_QUANTUM_L128, STAGE_WINDOW_MAX);
+    g.s1_stride = window(me * 2, STAGE_QUANTUM, STAGE_INBOX_MAX);
+    g.s2_stride = window(slice_len(me, n_ranks) * 2, STAGE_QUANTUM, STAGE_INBOX_MAX);
     g.window = 0;
     g.stats_stride = (me + ar::NORM_BLOCK_ELEMS - 1) / ar::NORM_BLOCK_ELEMS;
     g.acc_stride = round_up((me + ar::ATOM_LINE_ELEMS - 1) / ar::ATOM_LINE_ELEMS * 128, 256);
