@@ -232,36 +232,36 @@ int thread_index(int threads)
 
 int compute_capacity()
 {
+    // The capacity of a kind is the minimum over the kernels a call of it may
+    // launch: both coherence scopes (bf16) and the measurement twins (bf16),
+    // so a grid sized by it is resident at once whichever runs.
     const int tcounts[5] = {64, 128, 256, 512, 1024};
+    auto occupancy = [](const void *fn, int threads, int *per_cu) -> hipError_t {
+        *per_cu = 0;
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, fn, threads, 0);
+    };
     for (int k = 0; k < ar::K_COUNT; ++k) {
         for (int f = 0; f < 2; ++f) {
             if (ar::kernel_for(k, g.n_ranks, f == 1, false, 0) == nullptr)
                 continue;                       // no such variant (capacity stays 0)
             for (int t = 0; t < 5; ++t) {
-                int per_cu = 0;
-                hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &per_cu, ar::kernel_for(k, g.n_ranks, f == 1, false, 0), tcounts[t], 0);
-                if (e != hipSuccess && t >= 3) {
-                    // block sizes above a kernel's launch bound: unusable
-                    (void)hipGetLastError();
-                    g.capacity[k][f][t] = 0;
-                    continue;
-                }
-                if (e != hipSuccess)
-                    return hip_fail(e);
-                if (f == 0) {           // bf16: the XCD-local variant too
-                    int per_cu_local = 0;
-                    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                        &per_cu_local, ar::kernel_for(k, g.n_ranks, false, true, 0), tcounts[t], 0);
+                int best = 1 << 30;
+                bool usable = true;
+                for (int v = 0; v < (f == 0 ? 4 : 1) && usable; ++v) {
+                    int per_cu = 0;
+                    const void *fn = ar::kernel_for(k, g.n_ranks, f == 1, (v & 1) != 0, 0,
+                                                    (v & 2) != 0);
+                    hipError_t e = occupancy(fn, tcounts[t], &per_cu);
                     if (e != hipSuccess && t >= 3) {
+                        // block sizes above a kernel's launch bound: unusable
                         (void)hipGetLastError();
-                        per_cu_local = 0;
+                        usable = false;
                     } else if (e != hipSuccess) {
                         return hip_fail(e);
                     }
-                    per_cu = std::min(per_cu, per_cu_local);
+                    best = std::min(best, per_cu);
                 }
-                g.capacity[k][f][t] = per_cu * g.cu_count;
+                g.capacity[k][f][t] = usable ? best * g.cu_count : 0;
             }
         }
     }
@@ -272,10 +272,11 @@ int compute_capacity()
             for (int i = 0; i < 3; ++i) {
                 const int kind = two ? ar::K_TWOSHOT_LL128 : ar::K_ONESHOT_LL128;
                 int best = 1 << 30;
-                for (int local = 0; local < (f ? 1 : 2); ++local) {
+                for (int v = 0; v < (f ? 1 : 4); ++v) {
                     int per_cu = 0;
-                    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                        &per_cu, ar::kernel_for(kind, g.n_ranks, f == 1, local == 1, gws[i]), 256, 0);
+                    hipError_t e = occupancy(ar::kernel_for(kind, g.n_ranks, f == 1, (v & 1) != 0,
+                                                            gws[i], (v & 2) != 0),
+                                             256, &per_cu);
                     if (e != hipSuccess)
                         return hip_fail(e);
                     best = std::min(best, per_cu);
