@@ -233,7 +233,7 @@ int thread_index(int threads)
 int compute_capacity()
 {
     // The capacity of a kind is the minimum over the kernels a call of it may
-    // launch: both coherence scopes (bf16) and the measurement twins (bf16),
+    // launch: both coherence scopes (bf16) and the test twins (bf16),
     // so a grid sized by it is resident at once whichever runs.
     const int tcounts[5] = {64, 128, 256, 512, 1024};
     auto occupancy = [](const void *fn, int threads, int *per_cu) -> hipError_t {

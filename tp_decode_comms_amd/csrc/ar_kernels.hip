@@ -62,6 +62,7 @@ hipError_t control_block(uint32_t **p)
 struct Ctx0 {
     uint32_t rank, part, flag, call, par;
     uint32_t seq, calls;            // the sequence words, fetched in the prologue
+    bool delay;                     // a start-delay table is set
     bool stamp;                     // a timestamp table of start records is set
     bool phases;                    // a timestamp table with phase records is set
     uint64_t t0, t_sync, t_data;
@@ -101,7 +102,7 @@ __device__ __forceinline__ void load_seq(const Launch &a, Ctx0 &c)
 
 __device__ __forceinline__ void start_delay(const Launch &a, const Ctx0 &c)
 {
-    if (a.delays == nullptr)
+    if (!c.delay)
         return;
     __amdgpu_buffer_rsrc_t d = rsrc(a.delays, a.delay_rows * a.n_ranks * 4u);
     uint32_t row = (c.call - 1u) % a.delay_rows;
@@ -168,12 +169,13 @@ __device__ __forceinline__ void finish(const Launch &a, const Ctx0 &c)
     p[3] = t1;
 }
 
-// TS: the kernel is the measurement twin, built to write the timestamp
-// records; the kernels without it carry no measurement code at all (even a
-// disabled record costs: 8 x 16 KiB LL 2.43 -> 2.38 us, 8 x 64 KiB LL
-// 3.86 -> 3.40, 8 x 16 KiB in-place one-shot 2.35 -> 2.26 once removed).
-// The host launches the twin while a timestamp table is set.
-template <bool LOCAL, bool TS>
+// HOOKS: the kernel is the test twin, built with the measurement and test
+// hooks (timestamp records, start delays); the kernels without it carry no
+// hook code at all (even a disabled timestamp record cost: 8 x 16 KiB LL
+// 2.43 -> 2.38 us, 8 x 64 KiB LL 3.86 -> 3.40, 8 x 16 KiB in-place
+// one-shot 2.35 -> 2.26 once removed).  The host launches the twin while a
+// timestamp or delay table is set.
+template <bool LOCAL, bool HOOKS>
 __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
 {
     c.t0 = clock100();
@@ -209,7 +211,7 @@ __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
     // of them.)
     // (The sequence words come with them: their address is a constant.)
     const u32x2 sq = seq_words();
-    if constexpr (TS)
+    if constexpr (HOOKS)
         asm volatile("" ::"s"(a.in[c.rank]), "s"(a.out), "s"(a.ctl), "s"(a.n), "s"(a.n_ranks),
                      "s"(a.epoch), "s"(a.rbase), "s"(a.parts), "s"(a.slice), "s"(a.xshift),
                      "s"(a.delays), "s"(a.ts), "s"(a.ts_slots), "s"(a.ts_stride),
@@ -217,14 +219,15 @@ __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
     else
         asm volatile("" ::"s"(a.in[c.rank]), "s"(a.out), "s"(a.ctl), "s"(a.n), "s"(a.n_ranks),
                      "s"(a.epoch), "s"(a.rbase), "s"(a.parts), "s"(a.slice), "s"(a.xshift),
-                     "s"(a.delays), "s"(sq), "s"(blockDim.x));
+                     "s"(sq), "s"(blockDim.x));
     c.seq = sq.x;
     c.calls = sq.y;
     c.part = (blockIdx.z << a.xshift) + lo;
     // after the fields' loads are issued (computed earlier, the test of a.ts
     // made the compiler wait for it before issuing the others)
-    c.stamp = TS && a.ts != nullptr && a.ts_phases == 0u;
-    c.phases = TS && a.ts != nullptr && a.ts_phases != 0u;
+    c.delay = HOOKS && a.delays != nullptr;
+    c.stamp = HOOKS && a.ts != nullptr && a.ts_phases == 0u;
+    c.phases = HOOKS && a.ts != nullptr && a.ts_phases != 0u;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t in_rsrc(const Launch &a, uint32_t r)
@@ -504,13 +507,13 @@ __device__ __forceinline__ bool ll_round(const Launch &a, Ctx0 &c, const Ctl &ct
     return true;
 }
 
-template <int NMAX, bool F32, bool LOCAL, bool TS>
+template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
 __global__ __launch_bounds__(1024) void k_oneshot_ll(const Launch a)
 {
     __shared__ u32x2 stage[NMAX][64];
     __shared__ uint32_t failed;
     Ctx0 c;
-    begin<LOCAL, TS>(a, c);
+    begin<LOCAL, HOOKS>(a, c);
     asm volatile("" ::"s"(a.ll), "s"(a.ll_stride));  // mailboxes: with the first load round
     const uint32_t C = a.n >> 2;                    // 4-element chunks per rank
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
@@ -613,14 +616,14 @@ __device__ __forceinline__ bool row_rinv(const NormLaunch &L, const Ctx0 &c, con
     return true;
 }
 
-template <int NMAX, bool LOCAL, bool TS>
+template <int NMAX, bool LOCAL, bool HOOKS>
 __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
 {
     const Launch &a = L.base;
     __shared__ u32x2 stage[NMAX][64];
     __shared__ uint32_t failed;
     Ctx0 c;
-    begin<LOCAL, TS>(a, c);
+    begin<LOCAL, HOOKS>(a, c);
     const uint32_t C = a.n >> 2;                    // 4-element chunks per rank
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t step = a.parts * 64u;
@@ -712,12 +715,12 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
 // the stand-alone kernels' bit for bit.  Waves work independently; a wave
 // whose wait gives up records it and skips its work but still reaches
 // finish().  All workgroups of a rank must be resident at once.
-template <int NMAX, bool LOCAL, bool TS>
+template <int NMAX, bool LOCAL, bool HOOKS>
 __global__ __launch_bounds__(256) void k_oneshot_direct_norm(const NormLaunch L)
 {
     const Launch &a = L.base;
     Ctx0 c;
-    begin<LOCAL, TS>(a, c);
+    begin<LOCAL, HOOKS>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t blocks = a.n / NORM_BLOCK;                  // per rank
@@ -836,14 +839,14 @@ __global__ __launch_bounds__(256) void k_oneshot_direct_norm(const NormLaunch L)
 constexpr uint32_t ROWS_WAVES = 16;
 constexpr uint32_t ROWS_PER_WAVE = 2;
 
-template <int NMAX, bool LOCAL, bool TS>
+template <int NMAX, bool LOCAL, bool HOOKS>
 __global__ __launch_bounds__(1024) void k_oneshot_rows_norm(const NormLaunch L)
 {
     const Launch &a = L.base;
     __shared__ float bsum[ROWS_WAVES * ROWS_PER_WAVE];
     __shared__ float rinv_s;
     Ctx0 c;
-    begin<LOCAL, TS>(a, c);
+    begin<LOCAL, HOOKS>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t row = c.part;                          // one part per row
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
@@ -1079,13 +1082,13 @@ __device__ __forceinline__ bool sent_round(const Launch &a, Ctx0 &c, const Ctl &
     return true;
 }
 
-template <int NMAX, bool F32, bool LOCAL, bool TS>
+template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
 __global__ __launch_bounds__(512) void k_oneshot_sentinel(const Launch a)
 {
     __shared__ u32x4 stage[NMAX][64];
     __shared__ uint32_t failed;
     Ctx0 c;
-    begin<LOCAL, TS>(a, c);
+    begin<LOCAL, HOOKS>(a, c);
     const uint32_t G = a.n >> 3;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t step = a.parts * 64u;
@@ -1256,11 +1259,11 @@ __device__ __forceinline__ void twoshot_data(const Launch &a, const __amdgpu_buf
 // unchanged until call k has completed on every rank (the application-level
 // A/B double buffering of the SiFAR page, "SiFAR：无同步All-Reduce技术突破低
 // 延迟LLM推理瓶颈", technique one).
-template <int NMAX, bool F32, bool LOCAL, bool TS>
+template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
 __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
 {
     Ctx0 c;
-    begin<LOCAL, TS>(a, c);
+    begin<LOCAL, HOOKS>(a, c);
     const uint32_t G = a.unit4 ? a.n >> 2 : a.n >> 3;          // lane units of 4 or 8 elements
     const uint32_t step = a.parts * blockDim.x;
     load_seq(a, c);
@@ -1288,11 +1291,11 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
 // slice of that rank's output is known to be complete.
 // Moves exactly the algorithmic bytes: N inputs read once, N outputs written
 // once.
-template <int NMAX, bool F32, bool LOCAL, bool TS>
+template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
 __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
 {
     Ctx0 c;
-    begin<LOCAL, TS>(a, c);
+    begin<LOCAL, HOOKS>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t q = c.rank;
     const uint32_t L = a.slice;
@@ -1439,11 +1442,11 @@ __device__ __forceinline__ bool grid_barrier(const Launch &a, const Ctx0 &c, con
 
 // One-shot: top barrier, every rank reads all N inputs in place and writes
 // its copy, bottom barrier.
-template <int NMAX, bool F32, bool LOCAL, bool TS>
+template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
 __global__ __launch_bounds__(256) void k_oneshot_barrier(const Launch a)
 {
     Ctx0 c;
-    begin<LOCAL, TS>(a, c);
+    begin<LOCAL, HOOKS>(a, c);
     const uint32_t G = a.unit4 ? a.n >> 2 : a.n >> 3;          // lane units of 4 or 8 elements
     const uint32_t step = a.parts * blockDim.x;
     load_seq(a, c);
@@ -1464,11 +1467,11 @@ __global__ __launch_bounds__(256) void k_oneshot_barrier(const Launch a)
 
 // Two-shot: top barrier, rank q reduces slice q of all inputs in place and
 // writes it into every rank's output, bottom barrier (every output complete).
-template <int NMAX, bool F32, bool LOCAL, bool TS>
+template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
 __global__ __launch_bounds__(256) void k_twoshot_barrier(const Launch a)
 {
     Ctx0 c;
-    begin<LOCAL, TS>(a, c);
+    begin<LOCAL, HOOKS>(a, c);
     const uint32_t q = c.rank;
     const uint32_t L = a.slice;
     const uint32_t lo = q * L;
@@ -1668,14 +1671,14 @@ __device__ __forceinline__ void store_lane(__amdgpu_buffer_rsrc_t o, uint32_t e,
 // buffer (flag + j) & 1 with flag flag + j, and the workgroup barrier that
 // ends a batch (every wave has received it) comes before the next batch's
 // publish, which is the double buffer's permit.
-template <int NMAX, bool F32, bool LOCAL, int GW, bool TS>
+template <int NMAX, bool F32, bool LOCAL, int GW, bool HOOKS>
 __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 {
     constexpr int PW = (NMAX + L128_WAVES - 1) / L128_WAVES;
     __shared__ u32x4 stage[NMAX][GW][64];
     __shared__ uint32_t failed;
     Ctx0 c;
-    begin<LOCAL, TS>(a, c);
+    begin<LOCAL, HOOKS>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
@@ -1773,12 +1776,12 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 // receives the batch of the slices of the peers s with s % 4 == w straight
 // into out[q], and the waves meet at a barrier before the next batch is
 // published (its permit: every wave has received this batch).
-template <int NMAX, bool F32, bool LOCAL, int GW, bool TS>
+template <int NMAX, bool F32, bool LOCAL, int GW, bool HOOKS>
 __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 {
     constexpr int PW = (NMAX + L128_WAVES - 1) / L128_WAVES;
     Ctx0 c;
-    begin<LOCAL, TS>(a, c);
+    begin<LOCAL, HOOKS>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t q = c.rank;
     const uint32_t L = a.slice;
@@ -2089,14 +2092,14 @@ __device__ __forceinline__ bool ts_round(const Launch &a, Ctx0 &c, const Ctl &ct
     return *failed == 0u;
 }
 
-template <int NMAX, bool F32, bool LOCAL, bool TS>
+template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
 __global__ __launch_bounds__(512) void k_twoshot_sentinel(const Launch a)
 {
     __shared__ u32x4 stage[NMAX][64];
     __shared__ u32x4 red[64];
     __shared__ uint32_t failed;
     Ctx0 c;
-    begin<LOCAL, TS>(a, c);
+    begin<LOCAL, HOOKS>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t G = a.slice >> 3;                // chunks per slice
     const uint32_t step = a.parts * 64u;
@@ -2150,11 +2153,11 @@ __global__ __launch_bounds__(512) void k_twoshot_sentinel(const Launch a)
 constexpr uint32_t ATOM_ELEMS = (uint32_t)ATOM_LINE_ELEMS;     // binary32 sums per 128-byte line
 constexpr uint32_t ATOM_LINE = 128;
 
-template <int NMAX, bool F32, bool LOCAL, bool TS>
+template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
 __global__ __launch_bounds__(256) void k_twoshot_atomic(const Launch a)
 {
     Ctx0 c;
-    begin<LOCAL, TS>(a, c);
+    begin<LOCAL, HOOKS>(a, c);
     const uint32_t N = a.n_ranks;
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t half = lane >> 5, j = lane & 31u;
@@ -2302,55 +2305,55 @@ __global__ __launch_bounds__(256) void k_xcc_map(uint32_t *out, uint32_t n, uint
 
 // ------------------------------------------------------------ dispatch
 // LL128 kernels by line groups per batch (1, 2, or 4 up to 8 ranks)
-template <int NMAX, bool F32, bool LOCAL, bool TS>
+template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
 static const void *pick_ll128(bool two, int gw)
 {
     if (gw == 1)
-        return two ? (const void *)k_twoshot_ll128<NMAX, F32, LOCAL, 1, TS>
-                   : (const void *)k_oneshot_ll128<NMAX, F32, LOCAL, 1, TS>;
+        return two ? (const void *)k_twoshot_ll128<NMAX, F32, LOCAL, 1, HOOKS>
+                   : (const void *)k_oneshot_ll128<NMAX, F32, LOCAL, 1, HOOKS>;
     if constexpr (NMAX > 8) {
-        return two ? (const void *)k_twoshot_ll128<NMAX, F32, LOCAL, 2, TS>
-                   : (const void *)k_oneshot_ll128<NMAX, F32, LOCAL, 2, TS>;
+        return two ? (const void *)k_twoshot_ll128<NMAX, F32, LOCAL, 2, HOOKS>
+                   : (const void *)k_oneshot_ll128<NMAX, F32, LOCAL, 2, HOOKS>;
     } else {
         if (gw == 2)
-            return two ? (const void *)k_twoshot_ll128<NMAX, F32, LOCAL, 2, TS>
-                       : (const void *)k_oneshot_ll128<NMAX, F32, LOCAL, 2, TS>;
-        return two ? (const void *)k_twoshot_ll128<NMAX, F32, LOCAL, 4, TS>
-                   : (const void *)k_oneshot_ll128<NMAX, F32, LOCAL, 4, TS>;
+            return two ? (const void *)k_twoshot_ll128<NMAX, F32, LOCAL, 2, HOOKS>
+                       : (const void *)k_oneshot_ll128<NMAX, F32, LOCAL, 2, HOOKS>;
+        return two ? (const void *)k_twoshot_ll128<NMAX, F32, LOCAL, 4, HOOKS>
+                   : (const void *)k_oneshot_ll128<NMAX, F32, LOCAL, 4, HOOKS>;
     }
 }
 
-template <int NMAX, bool F32, bool LOCAL, bool TS>
+template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
 static const void *pick(int kind, int gw)
 {
     switch (kind) {
-    case K_ONESHOT_LL: return (const void *)k_oneshot_ll<NMAX, F32, LOCAL, TS>;
-    case K_ONESHOT_SENTINEL: return (const void *)k_oneshot_sentinel<NMAX, F32, LOCAL, TS>;
-    case K_ONESHOT_DIRECT: return (const void *)k_oneshot_direct<NMAX, F32, LOCAL, TS>;
-    case K_ONESHOT_LL128: return pick_ll128<NMAX, F32, LOCAL, TS>(false, gw);
-    case K_TWOSHOT_LL128: return pick_ll128<NMAX, F32, LOCAL, TS>(true, gw);
-    case K_TWOSHOT_SENTINEL: return (const void *)k_twoshot_sentinel<NMAX, F32, LOCAL, TS>;
-    case K_TWOSHOT_DIRECT: return (const void *)k_twoshot_direct<NMAX, F32, LOCAL, TS>;
-    case K_ONESHOT_BARRIER: return (const void *)k_oneshot_barrier<NMAX, F32, LOCAL, TS>;
-    case K_TWOSHOT_BARRIER: return (const void *)k_twoshot_barrier<NMAX, F32, LOCAL, TS>;
-    case K_TWOSHOT_ATOMIC: return (const void *)k_twoshot_atomic<NMAX, F32, LOCAL, TS>;
+    case K_ONESHOT_LL: return (const void *)k_oneshot_ll<NMAX, F32, LOCAL, HOOKS>;
+    case K_ONESHOT_SENTINEL: return (const void *)k_oneshot_sentinel<NMAX, F32, LOCAL, HOOKS>;
+    case K_ONESHOT_DIRECT: return (const void *)k_oneshot_direct<NMAX, F32, LOCAL, HOOKS>;
+    case K_ONESHOT_LL128: return pick_ll128<NMAX, F32, LOCAL, HOOKS>(false, gw);
+    case K_TWOSHOT_LL128: return pick_ll128<NMAX, F32, LOCAL, HOOKS>(true, gw);
+    case K_TWOSHOT_SENTINEL: return (const void *)k_twoshot_sentinel<NMAX, F32, LOCAL, HOOKS>;
+    case K_TWOSHOT_DIRECT: return (const void *)k_twoshot_direct<NMAX, F32, LOCAL, HOOKS>;
+    case K_ONESHOT_BARRIER: return (const void *)k_oneshot_barrier<NMAX, F32, LOCAL, HOOKS>;
+    case K_TWOSHOT_BARRIER: return (const void *)k_twoshot_barrier<NMAX, F32, LOCAL, HOOKS>;
+    case K_TWOSHOT_ATOMIC: return (const void *)k_twoshot_atomic<NMAX, F32, LOCAL, HOOKS>;
     case K_ONESHOT_LL_NORM:         // bf16 only
-        return F32 ? nullptr : (const void *)k_oneshot_ll_norm<NMAX, LOCAL, TS>;
+        return F32 ? nullptr : (const void *)k_oneshot_ll_norm<NMAX, LOCAL, HOOKS>;
     case K_ONESHOT_DIRECT_NORM:     // bf16 only
-        return F32 ? nullptr : (const void *)k_oneshot_direct_norm<NMAX, LOCAL, TS>;
+        return F32 ? nullptr : (const void *)k_oneshot_direct_norm<NMAX, LOCAL, HOOKS>;
     case K_ONESHOT_ROWS_NORM:       // bf16 only
-        return F32 ? nullptr : (const void *)k_oneshot_rows_norm<NMAX, LOCAL, TS>;
+        return F32 ? nullptr : (const void *)k_oneshot_rows_norm<NMAX, LOCAL, HOOKS>;
     default: return nullptr;
     }
 }
 
-// The fp32 debug kernels always use device scope and have no measurement twin.
-const void *kernel_for(int kind, int n_ranks, bool f32, bool local, int gw, bool ts)
+// The fp32 debug kernels always use device scope and always carry the hooks.
+const void *kernel_for(int kind, int n_ranks, bool f32, bool local, int gw, bool hooks)
 {
     if (f32)
-        return n_ranks <= 8 ? pick<8, true, false, false>(kind, gw)
-                            : pick<16, true, false, false>(kind, gw);
-    if (ts) {
+        return n_ranks <= 8 ? pick<8, true, false, true>(kind, gw)
+                            : pick<16, true, false, true>(kind, gw);
+    if (hooks) {
         if (n_ranks <= 8)
             return local ? pick<8, false, true, true>(kind, gw)
                          : pick<8, false, false, true>(kind, gw);
@@ -2370,7 +2373,8 @@ static dim3 grid_of(const Launch &a)
 hipError_t launch_ar(int kind, bool f32, bool local, int gw, const Launch &a, uint32_t threads,
                      hipStream_t stream)
 {
-    const void *fn = kernel_for(kind, (int)a.n_ranks, f32, local, gw, a.ts != nullptr);
+    const void *fn = kernel_for(kind, (int)a.n_ranks, f32, local, gw,
+                                a.ts != nullptr || a.delays != nullptr);
     if (fn == nullptr || (a.parts & ((1u << a.xshift) - 1u)) != 0u)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&a};
@@ -2382,7 +2386,8 @@ hipError_t launch_norm(int kind, bool local, const NormLaunch &L, uint32_t threa
 {
     if (kind != K_ONESHOT_LL_NORM && kind != K_ONESHOT_DIRECT_NORM && kind != K_ONESHOT_ROWS_NORM)
         return hipErrorInvalidValue;
-    const void *fn = kernel_for(kind, (int)L.base.n_ranks, false, local, 0, L.base.ts != nullptr);
+    const void *fn = kernel_for(kind, (int)L.base.n_ranks, false, local, 0,
+                                L.base.ts != nullptr || L.base.delays != nullptr);
     if (fn == nullptr || (L.base.parts & ((1u << L.base.xshift) - 1u)) != 0u)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&L};
