@@ -430,7 +430,7 @@ __device__ __forceinline__ bool ll_round(const Launch &a, Ctx0 &c, const Ctl &ct
     const bool mine = wave < N && wave != c.rank && active;
     bool pend = mine;
     const uint32_t src = lane_off + wave * 2u * rb;
-    Watch w;
+    WatchT<false> w;
     w.begin(a.watchdog_ticks);
     // Poll loads are issued by every lane, those with nothing (left) to
     // receive at OFF_NONE (zeros, no traffic): a load under a branch would
