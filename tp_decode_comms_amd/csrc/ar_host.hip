@@ -247,10 +247,9 @@ int compute_capacity()
             for (int t = 0; t < 5; ++t) {
                 int best = 1 << 30;
                 bool usable = true;
-                for (int v = 0; v < (f == 0 ? 4 : 1) && usable; ++v) {
+                for (int v = 0; v < (f == 0 ? 6 : 1) && usable; ++v) {
                     int per_cu = 0;
-                    const void *fn = ar::kernel_for(k, g.n_ranks, f == 1, (v & 1) != 0, 0,
-                                                    (v & 2) != 0);
+                    const void *fn = ar::kernel_for(k, g.n_ranks, f == 1, (v & 1) != 0, 0, v >> 1);
                     hipError_t e = occupancy(fn, tcounts[t], &per_cu);
                     if (e != hipSuccess && t >= 3) {
                         // block sizes above a kernel's launch bound: unusable
@@ -272,10 +271,10 @@ int compute_capacity()
             for (int i = 0; i < 3; ++i) {
                 const int kind = two ? ar::K_TWOSHOT_LL128 : ar::K_ONESHOT_LL128;
                 int best = 1 << 30;
-                for (int v = 0; v < (f ? 1 : 4); ++v) {
+                for (int v = 0; v < (f ? 1 : 6); ++v) {
                     int per_cu = 0;
                     hipError_t e = occupancy(ar::kernel_for(kind, g.n_ranks, f == 1, (v & 1) != 0,
-                                                            gws[i], (v & 2) != 0),
+                                                            gws[i], v >> 1),
                                              256, &per_cu);
                     if (e != hipSuccess)
                         return hip_fail(e);

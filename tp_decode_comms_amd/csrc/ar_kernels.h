@@ -43,9 +43,10 @@ enum KernelKind {
 // local selects the XCD-local coherence scope (bf16 kernels only)
 // gw: line groups per batch of the LL128 kinds (1, 2 or 4; 0 = the largest
 // available), ignored by the others
-// hooks: the test twin, with the timestamp records and start delays (bf16;
-// the fp32 debug kernels always have them)
-const void *kernel_for(int kind, int n_ranks, bool f32, bool local, int gw, bool hooks = false);
+// hooks: the measurement and test hooks built in (0 none, 1 start records,
+// 2 all: start delays, start or phase records; bf16 -- the fp32 debug
+// kernels always have all)
+const void *kernel_for(int kind, int n_ranks, bool f32, bool local, int gw, int hooks = 0);
 
 // grid (2^xshift, N, parts >> xshift) from the launch record (parts must be a
 // multiple of 2^xshift)

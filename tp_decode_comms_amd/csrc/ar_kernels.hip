@@ -169,13 +169,14 @@ __device__ __forceinline__ void finish(const Launch &a, const Ctx0 &c)
     p[3] = t1;
 }
 
-// HOOKS: the kernel is the test twin, built with the measurement and test
-// hooks (timestamp records, start delays); the kernels without it carry no
-// hook code at all (even a disabled timestamp record cost: 8 x 16 KiB LL
-// 2.43 -> 2.38 us, 8 x 64 KiB LL 3.86 -> 3.40, 8 x 16 KiB in-place
-// one-shot 2.35 -> 2.26 once removed).  The host launches the twin while a
-// timestamp or delay table is set.
-template <bool LOCAL, bool HOOKS>
+// HOOKS: which measurement and test hooks the kernel is built with -- 0
+// none, 1 the start records only (a timestamp table without phases), 2 all
+// (start delays, start records or per-wave phase records).  A kernel built
+// without a hook carries none of its code: even a hook disabled at run time
+// cost (8 x 16 KiB LL 2.43 -> 2.38 us, 8 x 64 KiB LL 3.86 -> 3.40,
+// 8 x 16 KiB in-place one-shot 2.35 -> 2.26 once removed).  The host picks
+// the twin from the tables that are set.
+template <bool LOCAL, int HOOKS>
 __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
 {
     c.t0 = clock100();
@@ -211,11 +212,15 @@ __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
     // of them.)
     // (The sequence words come with them: their address is a constant.)
     const u32x2 sq = seq_words();
-    if constexpr (HOOKS)
+    if constexpr (HOOKS == 2)
         asm volatile("" ::"s"(a.in[c.rank]), "s"(a.out), "s"(a.ctl), "s"(a.n), "s"(a.n_ranks),
                      "s"(a.epoch), "s"(a.rbase), "s"(a.parts), "s"(a.slice), "s"(a.xshift),
                      "s"(a.delays), "s"(a.ts), "s"(a.ts_slots), "s"(a.ts_stride),
                      "s"(a.ts_phases), "s"(sq), "s"(blockDim.x));
+    else if constexpr (HOOKS == 1)
+        asm volatile("" ::"s"(a.in[c.rank]), "s"(a.out), "s"(a.ctl), "s"(a.n), "s"(a.n_ranks),
+                     "s"(a.epoch), "s"(a.rbase), "s"(a.parts), "s"(a.slice), "s"(a.xshift),
+                     "s"(a.ts), "s"(a.ts_slots), "s"(a.ts_stride), "s"(sq), "s"(blockDim.x));
     else
         asm volatile("" ::"s"(a.in[c.rank]), "s"(a.out), "s"(a.ctl), "s"(a.n), "s"(a.n_ranks),
                      "s"(a.epoch), "s"(a.rbase), "s"(a.parts), "s"(a.slice), "s"(a.xshift),
@@ -225,9 +230,9 @@ __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
     c.part = (blockIdx.z << a.xshift) + lo;
     // after the fields' loads are issued (computed earlier, the test of a.ts
     // made the compiler wait for it before issuing the others)
-    c.delay = HOOKS && a.delays != nullptr;
-    c.stamp = HOOKS && a.ts != nullptr && a.ts_phases == 0u;
-    c.phases = HOOKS && a.ts != nullptr && a.ts_phases != 0u;
+    c.delay = HOOKS == 2 && a.delays != nullptr;
+    c.stamp = HOOKS == 1 ? a.ts != nullptr : (HOOKS == 2 && a.ts != nullptr && a.ts_phases == 0u);
+    c.phases = HOOKS == 2 && a.ts != nullptr && a.ts_phases != 0u;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t in_rsrc(const Launch &a, uint32_t r)
@@ -507,7 +512,7 @@ __device__ __forceinline__ bool ll_round(const Launch &a, Ctx0 &c, const Ctl &ct
     return true;
 }
 
-template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
+template <int NMAX, bool F32, bool LOCAL, int HOOKS>
 __global__ __launch_bounds__(1024) void k_oneshot_ll(const Launch a)
 {
     __shared__ u32x2 stage[NMAX][64];
@@ -616,7 +621,7 @@ __device__ __forceinline__ bool row_rinv(const NormLaunch &L, const Ctx0 &c, con
     return true;
 }
 
-template <int NMAX, bool LOCAL, bool HOOKS>
+template <int NMAX, bool LOCAL, int HOOKS>
 __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
 {
     const Launch &a = L.base;
@@ -715,7 +720,7 @@ __global__ __launch_bounds__(1024) void k_oneshot_ll_norm(const NormLaunch L)
 // the stand-alone kernels' bit for bit.  Waves work independently; a wave
 // whose wait gives up records it and skips its work but still reaches
 // finish().  All workgroups of a rank must be resident at once.
-template <int NMAX, bool LOCAL, bool HOOKS>
+template <int NMAX, bool LOCAL, int HOOKS>
 __global__ __launch_bounds__(256) void k_oneshot_direct_norm(const NormLaunch L)
 {
     const Launch &a = L.base;
@@ -839,7 +844,7 @@ __global__ __launch_bounds__(256) void k_oneshot_direct_norm(const NormLaunch L)
 constexpr uint32_t ROWS_WAVES = 16;
 constexpr uint32_t ROWS_PER_WAVE = 2;
 
-template <int NMAX, bool LOCAL, bool HOOKS>
+template <int NMAX, bool LOCAL, int HOOKS>
 __global__ __launch_bounds__(1024) void k_oneshot_rows_norm(const NormLaunch L)
 {
     const Launch &a = L.base;
@@ -1082,7 +1087,7 @@ __device__ __forceinline__ bool sent_round(const Launch &a, Ctx0 &c, const Ctl &
     return true;
 }
 
-template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
+template <int NMAX, bool F32, bool LOCAL, int HOOKS>
 __global__ __launch_bounds__(512) void k_oneshot_sentinel(const Launch a)
 {
     __shared__ u32x4 stage[NMAX][64];
@@ -1259,7 +1264,7 @@ __device__ __forceinline__ void twoshot_data(const Launch &a, const __amdgpu_buf
 // unchanged until call k has completed on every rank (the application-level
 // A/B double buffering of the SiFAR page, "SiFAR：无同步All-Reduce技术突破低
 // 延迟LLM推理瓶颈", technique one).
-template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
+template <int NMAX, bool F32, bool LOCAL, int HOOKS>
 __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
 {
     Ctx0 c;
@@ -1291,7 +1296,7 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
 // slice of that rank's output is known to be complete.
 // Moves exactly the algorithmic bytes: N inputs read once, N outputs written
 // once.
-template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
+template <int NMAX, bool F32, bool LOCAL, int HOOKS>
 __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
 {
     Ctx0 c;
@@ -1442,7 +1447,7 @@ __device__ __forceinline__ bool grid_barrier(const Launch &a, const Ctx0 &c, con
 
 // One-shot: top barrier, every rank reads all N inputs in place and writes
 // its copy, bottom barrier.
-template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
+template <int NMAX, bool F32, bool LOCAL, int HOOKS>
 __global__ __launch_bounds__(256) void k_oneshot_barrier(const Launch a)
 {
     Ctx0 c;
@@ -1467,7 +1472,7 @@ __global__ __launch_bounds__(256) void k_oneshot_barrier(const Launch a)
 
 // Two-shot: top barrier, rank q reduces slice q of all inputs in place and
 // writes it into every rank's output, bottom barrier (every output complete).
-template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
+template <int NMAX, bool F32, bool LOCAL, int HOOKS>
 __global__ __launch_bounds__(256) void k_twoshot_barrier(const Launch a)
 {
     Ctx0 c;
@@ -1671,7 +1676,7 @@ __device__ __forceinline__ void store_lane(__amdgpu_buffer_rsrc_t o, uint32_t e,
 // buffer (flag + j) & 1 with flag flag + j, and the workgroup barrier that
 // ends a batch (every wave has received it) comes before the next batch's
 // publish, which is the double buffer's permit.
-template <int NMAX, bool F32, bool LOCAL, int GW, bool HOOKS>
+template <int NMAX, bool F32, bool LOCAL, int GW, int HOOKS>
 __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 {
     constexpr int PW = (NMAX + L128_WAVES - 1) / L128_WAVES;
@@ -1776,7 +1781,7 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 // receives the batch of the slices of the peers s with s % 4 == w straight
 // into out[q], and the waves meet at a barrier before the next batch is
 // published (its permit: every wave has received this batch).
-template <int NMAX, bool F32, bool LOCAL, int GW, bool HOOKS>
+template <int NMAX, bool F32, bool LOCAL, int GW, int HOOKS>
 __global__ __launch_bounds__(256) void k_twoshot_ll128(const Launch a)
 {
     constexpr int PW = (NMAX + L128_WAVES - 1) / L128_WAVES;
@@ -2092,7 +2097,7 @@ __device__ __forceinline__ bool ts_round(const Launch &a, Ctx0 &c, const Ctl &ct
     return *failed == 0u;
 }
 
-template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
+template <int NMAX, bool F32, bool LOCAL, int HOOKS>
 __global__ __launch_bounds__(512) void k_twoshot_sentinel(const Launch a)
 {
     __shared__ u32x4 stage[NMAX][64];
@@ -2153,7 +2158,7 @@ __global__ __launch_bounds__(512) void k_twoshot_sentinel(const Launch a)
 constexpr uint32_t ATOM_ELEMS = (uint32_t)ATOM_LINE_ELEMS;     // binary32 sums per 128-byte line
 constexpr uint32_t ATOM_LINE = 128;
 
-template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
+template <int NMAX, bool F32, bool LOCAL, int HOOKS>
 __global__ __launch_bounds__(256) void k_twoshot_atomic(const Launch a)
 {
     Ctx0 c;
@@ -2305,7 +2310,7 @@ __global__ __launch_bounds__(256) void k_xcc_map(uint32_t *out, uint32_t n, uint
 
 // ------------------------------------------------------------ dispatch
 // LL128 kernels by line groups per batch (1, 2, or 4 up to 8 ranks)
-template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
+template <int NMAX, bool F32, bool LOCAL, int HOOKS>
 static const void *pick_ll128(bool two, int gw)
 {
     if (gw == 1)
@@ -2323,7 +2328,7 @@ static const void *pick_ll128(bool two, int gw)
     }
 }
 
-template <int NMAX, bool F32, bool LOCAL, bool HOOKS>
+template <int NMAX, bool F32, bool LOCAL, int HOOKS>
 static const void *pick(int kind, int gw)
 {
     switch (kind) {
@@ -2347,21 +2352,32 @@ static const void *pick(int kind, int gw)
     }
 }
 
-// The fp32 debug kernels always use device scope and always carry the hooks.
-const void *kernel_for(int kind, int n_ranks, bool f32, bool local, int gw, bool hooks)
+template <int HOOKS>
+static const void *pick_bf16(int kind, int n_ranks, bool local, int gw)
+{
+    if (n_ranks <= 8)
+        return local ? pick<8, false, true, HOOKS>(kind, gw) : pick<8, false, false, HOOKS>(kind, gw);
+    return local ? pick<16, false, true, HOOKS>(kind, gw) : pick<16, false, false, HOOKS>(kind, gw);
+}
+
+// The fp32 debug kernels always use device scope and always carry every hook.
+const void *kernel_for(int kind, int n_ranks, bool f32, bool local, int gw, int hooks)
 {
     if (f32)
-        return n_ranks <= 8 ? pick<8, true, false, true>(kind, gw)
-                            : pick<16, true, false, true>(kind, gw);
-    if (hooks) {
-        if (n_ranks <= 8)
-            return local ? pick<8, false, true, true>(kind, gw)
-                         : pick<8, false, false, true>(kind, gw);
-        return local ? pick<16, false, true, true>(kind, gw) : pick<16, false, false, true>(kind, gw);
-    }
-    if (n_ranks <= 8)
-        return local ? pick<8, false, true, false>(kind, gw) : pick<8, false, false, false>(kind, gw);
-    return local ? pick<16, false, true, false>(kind, gw) : pick<16, false, false, false>(kind, gw);
+        return n_ranks <= 8 ? pick<8, true, false, 2>(kind, gw) : pick<16, true, false, 2>(kind, gw);
+    if (hooks <= 0)
+        return pick_bf16<0>(kind, n_ranks, local, gw);
+    if (hooks == 1)
+        return pick_bf16<1>(kind, n_ranks, local, gw);
+    return pick_bf16<2>(kind, n_ranks, local, gw);
+}
+
+// The hooks a launch record asks for (see begin).
+static int hooks_of(const Launch &a)
+{
+    if (a.delays != nullptr || (a.ts != nullptr && a.ts_phases != 0u))
+        return 2;
+    return a.ts != nullptr ? 1 : 0;
 }
 
 // The grid of a launch record: (X, N, parts / X), X = 2^xshift.
@@ -2373,8 +2389,7 @@ static dim3 grid_of(const Launch &a)
 hipError_t launch_ar(int kind, bool f32, bool local, int gw, const Launch &a, uint32_t threads,
                      hipStream_t stream)
 {
-    const void *fn = kernel_for(kind, (int)a.n_ranks, f32, local, gw,
-                                a.ts != nullptr || a.delays != nullptr);
+    const void *fn = kernel_for(kind, (int)a.n_ranks, f32, local, gw, hooks_of(a));
     if (fn == nullptr || (a.parts & ((1u << a.xshift) - 1u)) != 0u)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&a};
@@ -2386,8 +2401,7 @@ hipError_t launch_norm(int kind, bool local, const NormLaunch &L, uint32_t threa
 {
     if (kind != K_ONESHOT_LL_NORM && kind != K_ONESHOT_DIRECT_NORM && kind != K_ONESHOT_ROWS_NORM)
         return hipErrorInvalidValue;
-    const void *fn = kernel_for(kind, (int)L.base.n_ranks, false, local, 0,
-                                L.base.ts != nullptr || L.base.delays != nullptr);
+    const void *fn = kernel_for(kind, (int)L.base.n_ranks, false, local, 0, hooks_of(L.base));
     if (fn == nullptr || (L.base.parts & ((1u << L.base.xshift) - 1u)) != 0u)
         return hipErrorInvalidValue;
     void *args[] = {(void *)&L};
