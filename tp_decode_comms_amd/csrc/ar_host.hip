@@ -386,10 +386,12 @@ int plan_geometry(size_t n, bool f32, Plan *p)
     p->slice = (uint32_t)slice_len(n, g.n_ranks);
     const bool l128 = p->kind == ar::K_ONESHOT_LL128 || p->kind == ar::K_TWOSHOT_LL128;
     if (l128) {
-        // line groups per batch, from a sweep at 8 ranks (ar_kernels.hip)
+        // line groups per batch, from sweeps at 8 ranks (ar_kernels.hip; the
+        // one-shot from 1 MiB per rank: 4 against 2, 14.75 -> 13.4 us at
+        // 1 MiB, 24.4 -> 21.2 at 2 MiB, 43.2 -> 37.6 at 4 MiB)
         const size_t bytes = 2 * n;
         if (p->kind == ar::K_ONESHOT_LL128)
-            p->gw = bytes <= 64 * 1024 ? 1 : 2;
+            p->gw = bytes <= 64 * 1024 ? 1 : (bytes <= 512 * 1024 || N > 8) ? 2 : 4;
         else
             p->gw = bytes <= 1024 * 1024 ? 1 : (N <= 8 ? 4 : 2);
     }
