@@ -304,6 +304,19 @@ def test_default_window_takes_one_round(algo, proto, n):
     assert bad == 0
 
 
+@pytest.mark.parametrize("N,n", [(8, 524288 + 8), (4, 1048576 + 24)])
+def test_oneshot_ll128_four_groups_per_batch(N, n):
+    """One-shot LL128 above 512 KiB per rank takes batches of four line
+    groups (two above 8 ranks), several rounds through the default window."""
+    log("one-shot LL128, N=%d n=%d" % (N, n))
+    sets = Sets(2, 2, n=n, n_ranks=N)
+    with ar_context(N, n, ONE, LL128) as ar:
+        assert _rounds(ar, n) >= 1
+        bad = _stream_calls(ar, sets, 6)
+        check_status_clean()
+    assert bad == 0
+
+
 def test_staging_window_validation():
     import tp_decode_comms_amd as arm
     with ar_context(8, 1 << 20) as ar:

@@ -315,15 +315,19 @@ constexpr int SENT_OUT = CP_NT;         // sentinel kernels (16 x 57344 two-shot
 // store): 8 x 512 KiB fused AllReduce + norm 6.64 -> 5.90 us per call.
 
 // ============================================================ arrivals
-// Rank s announces "my input for this call is final" by storing the call's
-// flag f = seq + epoch into its arrival word, at its very start and with no
-// dependence on any load.  Flags grow monotonically between wraps, so a
-// reader needs word >= f (wrap-safe compare).  The word is replicated per
-// XCD: parts x < 8 of rank s write copy x, and part p reads copy p % 8,
-// which the same-XCD part of every peer wrote.  The N words of one copy
-// share one 128-byte line, so a reader polls a single line (polls of lines
-// written during the launch are costly for the L2).  Only kinds that read
-// peers' data in place (DIRECT) use arrivals.
+// Rank s announces "my input for this call is final" by storing the flag of
+// the call's first round f (sequence word + the step's earlier rounds + 1)
+// into its arrival word as soon as the prologue's load round has returned.
+// Flags grow monotonically between restarts, so a reader needs word >= f
+// (wrap-safe compare).  The word is replicated per XCD: parts x < 8 of rank
+// s write copy x, and part p reads copy p % 8, which the same-XCD part of
+// every peer wrote.  The N words of one copy share one 128-byte line, so a
+// reader polls a single line (polls of lines written during the launch are
+// costly for the L2).  Only kinds that read peers' data in place (DIRECT,
+// the in-place fused norms, the LL128 two-shot's reduce-scatter) use
+// arrivals.  (Raising them with atomics at the first instruction instead,
+// before the sequence word arrives, measured slower: the atomics complete
+// later than a store is seen by a poll in the XCD's L2.)
 __device__ __forceinline__ uint32_t arrive_off(uint32_t copy, uint32_t rank)
 {
     return (CTL_ARRIVE + 32u * copy + rank) * 4u;
