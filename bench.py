@@ -348,6 +348,44 @@ def _graph_run(torch, ar, wl, algo, proto, calls, replays, warmup, delays, instr
     return res
 
 
+def stream_run(torch, ar, wl, algo, proto, calls, steps, warmup):
+    """`calls` calls and the step end enqueued back to back from the host on
+    one stream per step (no graph), events around each step: the host's
+    enqueue path, against the graph figure of the same calls."""
+    ar.init(wl.N, wl.n)
+    try:
+        ar.set_options(algo, proto)
+        nsets = len(wl.ins)
+        outs = [torch.empty((wl.N, wl.n), dtype=torch.int16, device="cuda:0")
+                for _ in range(nsets)]
+        stream = torch.cuda.current_stream()
+
+        def step():
+            for k in range(calls):
+                ar.allreduce(wl.ins[k % nsets], outs[k % nsets], wl.n, k + 1)
+            ar.step_end()
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per_step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+        bad = wl.check([(outs[s], s) for s in range(nsets)])
+        return {"event_us_per_call": summary(per_step_ms * 1000.0 / calls),
+                "mismatches": bad, "status": list(ar.get_status()),
+                "what": "%d calls + step end per step enqueued from the host, events around "
+                        "each step" % calls}
+    finally:
+        torch.cuda.synchronize()
+        ar.destroy()
+
+
 def bench_floor(torch, steps):
     """A 160-node graph of minimal kernels (1-element fills): the launch floor."""
     t = torch.zeros(1, dtype=torch.int32, device="cuda:0")
@@ -916,6 +954,11 @@ def main():
                     lat["event_us_per_call"]["p50"], lat["instrumented"]["interval_us"]["p50"],
                     lat["instrumented"]["interval_us"]["p99"],
                     100 * lat["instrumented"]["agreement"]))
+        lat_s = legs.run("latency_16k_stream", lambda: stream_run(
+            torch, ar, wl2, ONE, LL, CALLS_PER_STEP, max(args.steps // 10, 3), 2))
+        if lat_s is not None:
+            log("16 KiB one-shot LL, stream back to back: p50 %.3f us/call"
+                % lat_s["event_us_per_call"]["p50"])
         lat_d = legs.run("latency_16k_oneshot_direct", lambda: graph_run(
             torch, ar, wl2, ONE, DIRECT, CALLS_PER_STEP, args.steps, args.warmup,
             instrumented=False))
