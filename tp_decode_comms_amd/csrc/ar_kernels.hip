@@ -1680,9 +1680,9 @@ __device__ __forceinline__ void store_lane(__amdgpu_buffer_rsrc_t o, uint32_t e,
 // its group in global rank order and writes it.  Staging is a fixed window
 // per rank walked in rounds (one batch per part per round) as in the LL
 // kernel: batch j of part p sits in window slots p*GW .. p*GW + GW-1 of
-// buffer (flag + j) & 1 with flag flag + j, and the workgroup barrier that
-// ends a batch (every wave has received it) comes before the next batch's
-// publish, which is the double buffer's permit.
+// buffer (flag + j) & 1 with flag flag + j, and the workgroup barrier after
+// a batch's receive (every wave has received it) comes before the next
+// batch's publish, which is the double buffer's permit.
 template <int NMAX, bool F32, bool LOCAL, int GW, int HOOKS>
 __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
 {
@@ -1716,33 +1716,45 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
         failed = 0u;
     start_delay(a, c);
 
-    uint32_t rnd = 0;
-    for (uint32_t b = c.part; b < batches; b += a.parts, ++rnd) {
-        const uint32_t fj = c.flag + rnd, bj = fj & 1u;      // this round's flag and buffer
-        const uint32_t mine_off = (c.rank * 2u + bj) * rb;
-        uint32_t g[GW];
-        uint32_t gvalid = 0;
+    // Batches are pipelined across rounds: the input of batch j+1 is loaded
+    // while batch j is received, and batch j+1 is published as soon as the
+    // workgroup has received batch j (its permit), before batch j is reduced
+    // (8 x 512 KiB 7.58 -> 7.19 us, 8 x 16 KiB 3.14 -> 2.89, 8 x 1 MiB
+    // 13.3 -> 12.45).  (Written without lambdas: a lambda form changed the
+    // compiled two-shot kernel too and cost it 4%.)
+    uint32_t b = c.part;
+    uint32_t g[GW];
+    uint32_t gvalid = 0;
 #pragma unroll
-        for (int k = 0; k < GW; ++k) {
-            g[k] = b * GW + (uint32_t)k;
-            if (g[k] < groups)
-                gvalid |= 1u << k;
-        }
-        // publish: wave k < GW owns group g[k]
-        const bool pub = wave < (uint32_t)GW && ((gvalid >> wave) & 1u);
-        const uint32_t gm = b * GW + wave;
-        const uint32_t em = gm * L128_ELEMS + ln.elem;
+    for (int k = 0; k < GW; ++k) {
+        g[k] = b * GW + (uint32_t)k;
+        if (b < batches && g[k] < groups)
+            gvalid |= 1u << k;
+    }
+    bool pub = wave < (uint32_t)GW && ((gvalid >> wave) & 1u);
+    uint32_t em = (b * GW + wave) * L128_ELEMS + ln.elem;
+    const uint32_t my_slot = (slot0 + wave) * L128_BYTES + lane * 16u;
+    if (pub) {
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (pub) {
-            if (em < a.n)
-                x = ld_elems(inr, em, ln.half);
-            const uint32_t lo = mine_off + (slot0 + wave) * L128_BYTES + lane * 16u;
-            l128_store_payload<LOCAL>(reg, lo, ln.half, x);
-            wait_stores();
-            if (ln.half)
-                l128_store_flag<LOCAL>(reg, lo, fj);
-            stage[c.rank][wave][lane] = x;
-        }
+        if (em < a.n)
+            x = ld_elems(inr, em, ln.half);
+        const uint32_t lo = (c.rank * 2u + (c.flag & 1u)) * rb + my_slot;
+        l128_store_payload<LOCAL>(reg, lo, ln.half, x);
+        wait_stores();
+        if (ln.half)
+            l128_store_flag<LOCAL>(reg, lo, c.flag);
+        stage[c.rank][wave][lane] = x;
+    }
+    uint32_t rnd = 0;
+    for (; b < batches; b += a.parts, ++rnd) {
+        const uint32_t fj = c.flag + rnd, bj = fj & 1u;      // this round's flag and buffer
+        // the next batch: its input is on its way during this receive
+        const uint32_t bn = b + a.parts;
+        const bool pubn = wave < (uint32_t)GW && bn < batches && bn * GW + wave < groups;
+        const uint32_t emn = (bn * GW + wave) * L128_ELEMS + ln.elem;
+        u32x4 xn = {0u, 0u, 0u, 0u};
+        if (pubn && emn < a.n)
+            xn = ld_elems(inr, emn, ln.half);
         // receive the batch from this wave's peers
         u32x4 V[GW][PW];
         if (!l128_recv<GW, PW, LOCAL>(reg, rb, bj, slot0, g, gvalid, pmask, wave, lane, ln, lim,
@@ -1759,6 +1771,14 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
         lds_barrier();
         if (failed)
             return;
+        // every wave has received this batch: the next one may be published
+        if (pubn) {
+            const uint32_t lo = (c.rank * 2u + ((fj + 1u) & 1u)) * rb + my_slot;
+            l128_store_payload<LOCAL>(reg, lo, ln.half, xn);
+            wait_stores();
+            if (ln.half)
+                l128_store_flag<LOCAL>(reg, lo, fj + 1u);
+        }
         if (pub && em < a.n) {
             // every row of the tile at once (rows of absent ranks are not folded)
             u32x4 t[NMAX];
@@ -1774,6 +1794,17 @@ __global__ __launch_bounds__(256) void k_oneshot_ll128(const Launch a)
             store_lane<F32, L128_OUT1>(o, em, ln.half, acc);
         }
         lds_barrier();                              // the tile is reused next batch
+        if (pubn)
+            stage[c.rank][wave][lane] = xn;
+        gvalid = 0;
+#pragma unroll
+        for (int k = 0; k < GW; ++k) {
+            g[k] = bn * GW + (uint32_t)k;
+            if (bn < batches && g[k] < groups)
+                gvalid |= 1u << k;
+        }
+        pub = pubn;
+        em = emn;
     }
     mark(c, c.t_data);
     finish(a, c);
