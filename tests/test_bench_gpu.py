@@ -1,6 +1,6 @@
 """bench.py end to end on the GPU with a short, odd warm-up: it must finish
 with exit status 0 and print one JSON line that carries the headline, the
-4 MiB roofline and the parity verdict (a bench leg that failed would be
+4 MiB roofline and the parity result (a bench leg that failed would be
 listed under failed_legs)."""
 import json
 import os

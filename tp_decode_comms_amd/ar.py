@@ -85,7 +85,7 @@ def lib():
             if not os.path.exists(path):
                 raise RuntimeError(
                     "HIP library %s is missing: build it with "
-                    "`python -m tp_decode_comms_amd.build` (or __graft_entry__.build())" % path)
+                    "`python -m tp_decode_comms_amd.build`" % path)
             # The process must run one HIP runtime: load torch's first so that
             # the library's libamdhip64 dependency binds to that same copy.
             import torch  # noqa: F401
