@@ -505,8 +505,8 @@ def _bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact, gr
         bad, worst = wl.check_bound([(outs[s], s) for s in range(nsets)])
     extra = {} if worst is None else {"max_ulp_vs_fixed_order": round(worst, 3)}
     return {**extra,
-        "workload": "8 ranks x [256x8192] bf16 (4 MiB/rank), U(-1,1), %s, 8 rotating buffer "
-                    "sets (footprint %d MiB)" % (label, (2 * nsets * wl.N * 2 * wl.n) >> 20),
+        "workload": "8 ranks x [256x8192] bf16 (4 MiB/rank), U(-1,1), %s, %d rotating buffer "
+                    "sets (footprint %d MiB)" % (label, nsets, (2 * nsets * wl.N * 2 * wl.n) >> 20),
         "algo": label, "grid": grid, "threads": threads, "xcd_local_scope": local,
         "rounds_per_call": ar.query(12, wl.n),
         "staging_window_bytes": ar.query(15, wl.n),
@@ -753,6 +753,48 @@ def recorded_traffic(kernel_key):
     except OSError:
         pass
     return None
+
+
+def bench_copy_reference(torch, ar, graph_calls=160, graph_replays=3, pairs=8):
+    """The library's plain copy (include/ar_copy.h) of the 4 MiB/rank
+    AllReduce's traffic: 32 MiB read and 32 MiB written per call, `pairs`
+    rotating buffer pairs (8: the 512 MiB footprint of the AllReduce's 8 sets),
+    graph_calls copies in one hipGraph replayed back to back, as the
+    AllReduce's graph pass is.  What this device's memory delivers for that
+    traffic at that launch cadence: the reference the AllReduce's bandwidth
+    is read against, beside the datasheet peak."""
+    elems = 16 * 1024 * 1024                                   # 32 MiB of int16
+    srcs = [torch.arange(elems, dtype=torch.int32, device="cuda:0").to(torch.int16) + k
+            for k in range(pairs)]
+    dsts = [torch.zeros_like(x) for x in srcs]
+    nbytes = 2 * elems
+    gs = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(g, stream=gs):
+            for k in range(graph_calls):
+                ar.copy(srcs[k % pairs], dsts[k % pairs], nbytes, stream=gs)
+    with torch.cuda.stream(gs):
+        g.replay()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(gs)
+        for _ in range(graph_replays):
+            g.replay()
+        g1.record(gs)
+    torch.cuda.synchronize()
+    us = g0.elapsed_time(g1) * 1000.0 / (graph_calls * graph_replays)
+    bad = sum(int(not torch.equal(srcs[k], dsts[k])) for k in range(pairs))
+    del g
+    moved = 2 * nbytes
+    return {"workload": "32 MiB -> 32 MiB device copy (the 64 MiB one 8 x 4 MiB/rank AllReduce "
+                        "moves), %d rotating buffer pairs (footprint %d MiB), %d copies in one "
+                        "hipGraph" % (pairs, (2 * pairs * nbytes) >> 20, graph_calls),
+            "graph_us_per_call": us, "bytes_per_call": moved,
+            "gbps_graph": moved / (us * 1e-6) / 1e9,
+            "frac_of_peak": moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "graph_calls": graph_calls, "graph_replays": graph_replays,
+            "mismatches": bad}
 
 
 def calib_copy(torch, pairs=16, passes=2):
@@ -1019,6 +1061,29 @@ def main():
             results["barrier_cost_4m_us_graph"] = round(tb["graph_us_per_call"] -
                                                         td["graph_us_per_call"], 4)
         del wl4
+        log("4 MiB/rank bandwidth reference: a plain copy of the same traffic")
+        r = legs.run("copy_reference_4m", lambda: bench_copy_reference(torch, ar))
+        if r is not None:
+            log("  %.1f GB/s in a graph (%.2f us/call)" % (r["gbps_graph"], r["graph_us_per_call"]))
+        # the same two measurements with twice the footprint (1 GiB, four
+        # times the 256 MB memory-side cache): at 512 MiB part of the
+        # rotating sets' traffic is served by that cache, at 1 GiB nearly
+        # none is
+        torch.cuda.empty_cache()
+        log("4 MiB/rank two-shot and copy at a 1 GiB footprint (16 sets)")
+        wl16 = Workload(torch, 4, 16)
+        r = legs.run("bw_4m_twoshot_direct_1gib", lambda: bench_bandwidth(
+            torch, ar, wl16, args.bw_calls, args.warmup, TWO, DIRECT,
+            "two-shot (in-place reduce-scatter, reduced slices written straight into every "
+            "output, completion flags)"))
+        if r is not None:
+            log("  %.1f GB/s in a graph (%.2f us/call)" % (r["gbps_graph"], r["graph_us_per_call"]))
+        del wl16
+        torch.cuda.empty_cache()
+        r = legs.run("copy_reference_4m_1gib", lambda: bench_copy_reference(torch, ar, pairs=16))
+        if r is not None:
+            log("  copy: %.1f GB/s in a graph (%.2f us/call)" % (r["gbps_graph"],
+                                                               r["graph_us_per_call"]))
     if only in ("all", "overlap"):
         log("overlap harness: projection GEMV and AllReduce")
         r = legs.run("overlap", lambda: bench_overlap(torch, ar, replays=10 if args.quick else 50))
@@ -1115,6 +1180,15 @@ def main():
                             "per_launch_bytes": best["b_alg_bytes"], "avg_launch_us": avg_us,
                             "avg_launch_us_stream_back_to_back": best["region_us_per_call"],
                             "avg_launch_us_with_per_call_events": best["us_per_call"]["mean"]}
+    cr = results.get("copy_reference_4m")
+    if "roofline" in line and isinstance(cr, dict) and "graph_us_per_call" in cr:
+        # the same traffic with no synchronisation, on this device: the share
+        # of its rate the AllReduce reaches
+        line["copy_reference"] = {"us_per_call": round(cr["graph_us_per_call"], 4),
+                                  "gbps": round(cr["gbps_graph"], 2),
+                                  "frac_of_peak": round(cr["frac_of_peak"], 4),
+                                  "allreduce_frac_of_copy": round(
+                                      cr["graph_us_per_call"] / line["roofline"]["avg_launch_us"], 4)}
     fl = results.get("floor")
     if lat is not None and fl is not None and "us_per_node_p50" in fl:
         # the latency kernel is bound by the launch floor plus its in-XCD

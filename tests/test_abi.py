@@ -87,3 +87,10 @@ def test_gemv_validation_without_device(lib):
     assert lib.ar_gemv_bf16(good, good, P(16), 8, 8, 1, 0, None) == a.AR_ERR_INVALID  # y aliases W
     assert lib.ar_gemv_bf16(good, good, P(4096), 8, 8, 1, -1, None) == a.AR_ERR_INVALID
     assert lib.ar_gemv_bf16(good, good, P(1 << 33), 1, (1 << 28) + 8, 1, 0, None) == a.AR_ERR_INVALID  # K
+    # the copy reference: alignment, size and overlap checks launch nothing
+    assert lib.ar_copy(None, 4096, 16, None) == a.AR_ERR_INVALID
+    assert lib.ar_copy(4096, 8192, 0, None) == a.AR_ERR_INVALID
+    assert lib.ar_copy(4096, 8192, 24, None) == a.AR_ERR_INVALID          # not whole vectors
+    assert lib.ar_copy(4104, 8192, 16, None) == a.AR_ERR_INVALID          # unaligned source
+    assert lib.ar_copy(4096, 4096 + 16, 32, None) == a.AR_ERR_INVALID     # overlap
+    assert lib.ar_copy(1 << 40, 1 << 41, 1 << 31, None) == a.AR_ERR_INVALID   # too large

@@ -56,6 +56,8 @@ _SIGS = {
     # include/ar_gemv.h (compute step of the overlap harness)
     "ar_gemv_bf16": (_c_int, [ctypes.POINTER(_c_vp), ctypes.POINTER(_c_vp), ctypes.POINTER(_c_vp),
                               _c_size, _c_size, _c_int, _c_int, _c_vp]),
+    # include/ar_copy.h (the bandwidth reference)
+    "ar_copy": (_c_int, [_c_vp, _c_vp, _c_size, _c_vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -179,6 +181,13 @@ def gemv(weights, xs, ys, M, K, stream=None, max_workgroups=0, check=True):
     rc = lib().ar_gemv_bf16(_rank_array(weights), _rank_array(xs), _rank_array(ys), int(M), int(K),
                             len(weights), int(max_workgroups), _stream_handle(stream))
     return _check("ar_gemv_bf16", rc) if check else rc
+
+
+def copy(src, dst, nbytes, stream=None, check=True):
+    """dst[0:nbytes) = src[0:nbytes) on the device (include/ar_copy.h): the
+    bandwidth reference of the large AllReduce calls."""
+    rc = lib().ar_copy(_ptr(src), _ptr(dst), int(nbytes), _stream_handle(stream))
+    return _check("ar_copy", rc) if check else rc
 
 
 def allreduce_f32_debug(rank_bufs, out_f32, n, epoch, stream=None, check=True):

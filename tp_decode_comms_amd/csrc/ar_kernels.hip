@@ -340,10 +340,23 @@ __device__ __forceinline__ void raise_arrival(const Launch &a, const Ctx0 &c)
         st4<Pol<LOCAL>::ST>(c.flag, rsrc(a.ctl, CTL_WORDS * 4u), arrive_off(c.part, c.rank));
 }
 
+// The first arrival poll of an XCD-local workgroup, issued at the launch's
+// first instruction: the control block's address is a link-time constant
+// and the copy the workgroup reads is the one of the XCD it runs on, so the
+// poll needs nothing from the launch record and travels with its loads.
+// Lane l reads rank (l mod 16)'s word; wait_arrivals checks it first.
+__device__ __forceinline__ uint32_t early_arrival_poll()
+{
+    return ld4<Pol<true>::LD>(rsrc(ar_control, CTL_WORDS * 4u),
+                              arrive_off(xcc_id(), (threadIdx.x & 63u) & (MAX_RANKS - 1u)));
+}
+
 // Every wave waits (two polls in flight) until all N arrival words of its
 // XCD's copy reach the call's flag.  Lanes 0..N-1 each watch one word.
+// `first`, if given, is the value of an early poll of the same word.
 template <bool LOCAL>
-__device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, const Ctl &ctl)
+__device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, const Ctl &ctl,
+                                              const uint32_t *first = nullptr)
 {
     const uint32_t lane = threadIdx.x & 63u;
     bool need = lane < a.n_ranks;
@@ -351,7 +364,7 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
     const __amdgpu_buffer_rsrc_t r = rsrc(a.ctl, CTL_WORDS * 4u);
     Watch w;
     w.begin(a.watchdog_ticks);
-    uint32_t v0 = need ? ld4<Pol<LOCAL>::LD>(r, off) : c.flag, v1;
+    uint32_t v0 = first != nullptr ? *first : (need ? ld4<Pol<LOCAL>::LD>(r, off) : c.flag), v1;
     while (true) {
         compiler_fence();
         v1 = need ? ld4<Pol<LOCAL>::LD>(r, off) : c.flag;
@@ -373,11 +386,12 @@ __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, co
 // Workgroup form: wave 0 polls, the workgroup barrier releases the others
 // (a quarter of the polling traffic of 4-wave workgroups).
 template <bool LOCAL>
-__device__ __forceinline__ bool wait_arrivals_wg(const Launch &a, const Ctx0 &c, const Ctl &ctl)
+__device__ __forceinline__ bool wait_arrivals_wg(const Launch &a, const Ctx0 &c, const Ctl &ctl,
+                                                 const uint32_t *first = nullptr)
 {
     __shared__ uint32_t ok;
     if (threadIdx.x < 64u)
-        ok = wait_arrivals<LOCAL>(a, c, ctl) ? 1u : 0u;
+        ok = wait_arrivals<LOCAL>(a, c, ctl, first) ? 1u : 0u;
     __syncthreads();
     return ok != 0u;
 }
@@ -1199,10 +1213,14 @@ __device__ __forceinline__ void oneshot_data(const Launch &a, const __amdgpu_buf
 // order and stored into that slice of every rank's output (streaming
 // device-scope stores), TS_CPI chunks per lane per round.
 constexpr uint32_t TS_CPI = TWOSHOT_DIRECT_CHUNKS;   // chunks per lane per round
-// input loads: streaming (each input byte is read once), device scope
-// (8 x 4 MiB: 13.30-13.41 -> 13.20-13.21 us against device scope alone,
-// 13.27-13.28 plain, same box)
-constexpr int TS_LD = CP_NT | CP_DEV;
+// input loads: plain.  The inputs are final before the launch, so no scope
+// is needed.  Streaming device-scope loads, taken while the kernel had more
+// rounds in its prologue (8 x 4 MiB: 13.20 against 13.27 plain then), now
+// cost 0.2-0.8 us per call on most boxes (12.81-12.93 -> 12.01-12.08 us,
+// three rounds of fresh processes on each of two boxes; one box within
+// noise); without the flags the plain-load data phase runs at 10.86 us per
+// call against 10.45 for a plain copy of the same 64 MiB.
+constexpr int TS_LD = CP_PLAIN;
 constexpr int TS_ST = CP_NT | CP_DEV;               // output stores (streaming)
 
 template <int NMAX, bool F32>
@@ -1306,6 +1324,16 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
 template <int NMAX, bool F32, bool LOCAL, int HOOKS>
 __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
 {
+    // The first arrival poll goes out with the launch record's loads: most
+    // workgroups of this large grid start after the arrival writers (parts
+    // 0..7, dispatched first), so it usually finds the flags and saves a
+    // poll round trip (8 x 4 MiB: 12.08-12.09 -> 11.97-12.06 us per call).
+    // The one-shot kernels start all their workgroups at once; there an
+    // early poll meets the line before the writers' stores have put it in
+    // the L2 and costs a memory round trip (8 x 16 KiB 2.18 -> 2.35 us).
+    uint32_t early = 0;
+    if constexpr (LOCAL)
+        early = early_arrival_poll();
     Ctx0 c;
     begin<LOCAL, HOOKS>(a, c);
     const uint32_t N = a.n_ranks;
@@ -1327,7 +1355,7 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     __amdgpu_buffer_rsrc_t src[NMAX];
     input_rsrcs<NMAX>(a, src);
     const __amdgpu_buffer_rsrc_t oa = out_all(a, F32);
-    if (!wait_arrivals_wg<LOCAL>(a, c, ctl))
+    if (!wait_arrivals_wg<LOCAL>(a, c, ctl, LOCAL ? &early : nullptr))
         return;
     mark(c, c.t_sync);
     twoshot_data<NMAX, F32>(a, src, oa, lo, G, c.part * blockDim.x + threadIdx.x, step);
