@@ -948,6 +948,9 @@ def main():
     ap.add_argument("--bw-calls", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quick", action="store_true")
+    ap.add_argument("--no-footprint", action="store_true",
+                    help="skip the 1 GiB-footprint two-shot and copy legs (profiler runs: keeps "
+                         "the 4 MiB kernel's dispatches to the 512 MiB workload)")
     ap.add_argument("--only", default="all",
                     choices=["all", "latency", "bw", "overlap", "atomic", "norm", "configs",
                              "calib", "c3"])
@@ -1065,7 +1068,8 @@ def main():
         r = legs.run("copy_reference_4m", lambda: bench_copy_reference(torch, ar))
         if r is not None:
             log("  %.1f GB/s in a graph (%.2f us/call)" % (r["gbps_graph"], r["graph_us_per_call"]))
-        # the same two measurements with twice the footprint (1 GiB, four
+    if only in ("all", "bw") and not args.no_footprint:
+        # the two-shot and the copy with twice the footprint (1 GiB, four
         # times the 256 MB memory-side cache): at 512 MiB part of the
         # rotating sets' traffic is served by that cache, at 1 GiB nearly
         # none is
