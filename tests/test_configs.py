@@ -153,6 +153,30 @@ def test_config4_rotating_sets(algo, proto):
     assert bad == 0
 
 
+@pytest.mark.parametrize("cid,algo,proto,calls", [
+    (4, TWO, DIRECT, 400), (4, ONE, DIRECT, 200), (4, TWO, LL128, 200),
+    (3, TWO, LL128, 1000), (3, ONE, LL128, 1000), (2, ONE, LL, 2000), (2, ONE, DIRECT, 2000)],
+    ids=["4mib-twoshot-direct", "4mib-oneshot-direct", "4mib-twoshot-ll128",
+         "512kib-twoshot-ll128", "512kib-oneshot-ll128", "16kib-ll", "16kib-oneshot-direct"])
+def test_start_delays_other_kinds(cid, algo, proto, calls):
+    """Config 5's seeded 0-5 us start delays per (call, rank) on the other
+    kinds and workloads: ranks that arrive late (the in-place kernels'
+    arrival flags, their first poll taken before the delay) or publish late
+    (LL units, LL128 lines) still give every call bit-exactly, with no
+    watchdog record."""
+    log("delays: workload %d, algo %d, proto %d, %d calls" % (cid, algo, proto, calls))
+    torch = torch_mod()
+    sets = Sets(cid, 8 if cid == 4 else 4)
+    delays = torch.from_numpy(synth.delays_ns(5, calls, n_ranks=sets.N).view(np.int32).copy()
+                              ).to("cuda:0")
+    with ar_context(sets.N, sets.n, algo, proto) as ar:
+        ar.set_delays(delays, calls)
+        bad = _stream_calls(ar, sets, calls, nbuf=len(sets))
+        ar.set_delays(None, 0)
+        check_status_clean()
+    assert bad == 0
+
+
 @pytest.mark.parametrize("algo", [TWO, ONE], ids=["twoshot", "oneshot"])
 def test_config5_delays_10000_calls(algo):
     log("config 5, sentinel, algo %d" % algo)
