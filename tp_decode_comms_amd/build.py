@@ -14,6 +14,9 @@ FLAGS = [
     "--offload-arch=" + ARCH,
     # keep the compiler from emitting packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first kernel argument arrives in a register (the in-place kernels'
+    # arrival value, stored before any load of the launch record returns)
+    "-mllvm", "-amdgpu-kernarg-preload-count=1",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -333,11 +333,41 @@ __device__ __forceinline__ uint32_t arrive_off(uint32_t copy, uint32_t rank)
     return (CTL_ARRIVE + 32u * copy + rank) * 4u;
 }
 
+// A call's arrival value: its first round's position in the step (the rounds
+// of the step's earlier calls, + 1).  It needs no sequence word; the step end
+// clears the arrival words, so within a step the values only grow.
+__device__ __forceinline__ uint32_t arrival_value(const Launch &a) { return a.rbase + 1u; }
+
 template <bool LOCAL>
 __device__ __forceinline__ void raise_arrival(const Launch &a, const Ctx0 &c)
 {
     if (c.part < (uint32_t)XCDS && threadIdx.x == 0)
-        st4<Pol<LOCAL>::ST>(c.flag, rsrc(a.ctl, CTL_WORDS * 4u), arrive_off(c.part, c.rank));
+        st4<Pol<LOCAL>::ST>(arrival_value(a), rsrc(a.ctl, CTL_WORDS * 4u), arrive_off(c.part, c.rank));
+}
+
+// The arrival raised at a launch's first instruction, for kernels that take
+// the value as a leading argument (the build preloads the first kernel
+// argument into a register): with the XCD-local scope the writers (parts
+// 0..7) are block 0, their copy is their XCD's and the control block's
+// address is a link-time constant, so the store waits for no load.  With
+// start delays (HOOKS 2) the rank arrives after its delay instead.  Same-box
+// A/B, 160-call graphs, against the sequence-based value raised after the
+// prologue: 8 x 4 MiB two-shot 13.18-13.29 -> 13.00-13.17 us (in three
+// fresh-allocation passes per process 11.95-12.11 -> 11.88-11.99 on the
+// faster allocations), 8 x 512 KiB LL128 two-shot (arrival value only)
+// 4.46-4.49 -> 4.35-4.37; the 16 KiB calls unchanged.
+template <bool LOCAL, int HOOKS>
+__device__ __forceinline__ void raise_arrival_first(uint32_t arr)
+{
+    if constexpr (LOCAL && HOOKS != 2)
+        if (blockIdx.z == 0u && threadIdx.x == 0u)
+            st4<Pol<true>::ST>(arr, rsrc(ar_control, CTL_WORDS * 4u), arrive_off(xcc_id(), blockIdx.y));
+}
+template <bool LOCAL, int HOOKS>
+__device__ __forceinline__ void raise_arrival_late(const Launch &a, const Ctx0 &c)
+{
+    if constexpr (!LOCAL || HOOKS == 2)
+        raise_arrival<LOCAL>(a, c);
 }
 
 // The first arrival poll of an XCD-local workgroup, issued at the launch's
@@ -358,25 +388,26 @@ template <bool LOCAL>
 __device__ __forceinline__ bool wait_arrivals(const Launch &a, const Ctx0 &c, const Ctl &ctl,
                                               const uint32_t *first = nullptr)
 {
+    const uint32_t tgt = arrival_value(a);
     const uint32_t lane = threadIdx.x & 63u;
     bool need = lane < a.n_ranks;
     const uint32_t off = arrive_off(c.part % (uint32_t)XCDS, lane & (MAX_RANKS - 1u));
     const __amdgpu_buffer_rsrc_t r = rsrc(a.ctl, CTL_WORDS * 4u);
     Watch w;
     w.begin(a.watchdog_ticks);
-    uint32_t v0 = first != nullptr ? *first : (need ? ld4<Pol<LOCAL>::LD>(r, off) : c.flag), v1;
+    uint32_t v0 = first != nullptr ? *first : (need ? ld4<Pol<LOCAL>::LD>(r, off) : tgt), v1;
     while (true) {
         compiler_fence();
-        v1 = need ? ld4<Pol<LOCAL>::LD>(r, off) : c.flag;
-        if (need && (int32_t)(v0 - c.flag) >= 0)
+        v1 = need ? ld4<Pol<LOCAL>::LD>(r, off) : tgt;
+        if (need && (int32_t)(v0 - tgt) >= 0)
             need = false;
         if (!wave_any(need))
             return true;
         if (w.expired(ctl, c.rank, lane, c.call))
             return false;
         compiler_fence();
-        v0 = need ? ld4<Pol<LOCAL>::LD>(r, off) : c.flag;
-        if (need && (int32_t)(v1 - c.flag) >= 0)
+        v0 = need ? ld4<Pol<LOCAL>::LD>(r, off) : tgt;
+        if (need && (int32_t)(v1 - tgt) >= 0)
             need = false;
         if (!wave_any(need))
             return true;
@@ -1290,8 +1321,9 @@ __device__ __forceinline__ void twoshot_data(const Launch &a, const __amdgpu_buf
 // A/B double buffering of the SiFAR page, "SiFAR：无同步All-Reduce技术突破低
 // 延迟LLM推理瓶颈", technique one).
 template <int NMAX, bool F32, bool LOCAL, int HOOKS>
-__global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
+__global__ __launch_bounds__(256) void k_oneshot_direct(const uint32_t arr, const Launch a)
 {
+    raise_arrival_first<LOCAL, HOOKS>(arr);
     Ctx0 c;
     begin<LOCAL, HOOKS>(a, c);
     const uint32_t G = a.unit4 ? a.n >> 2 : a.n >> 3;          // lane units of 4 or 8 elements
@@ -1299,7 +1331,7 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
     load_seq(a, c);
     const Ctl ctl{a.ctl};
     start_delay(a, c);
-    raise_arrival<LOCAL>(a, c);
+    raise_arrival_late<LOCAL, HOOKS>(a, c);
     __amdgpu_buffer_rsrc_t src[NMAX];
     input_rsrcs<NMAX>(a, src);
     const __amdgpu_buffer_rsrc_t o = out_rsrc(a, c.rank, F32);
@@ -1322,8 +1354,9 @@ __global__ __launch_bounds__(256) void k_oneshot_direct(const Launch a)
 // Moves exactly the algorithmic bytes: N inputs read once, N outputs written
 // once.
 template <int NMAX, bool F32, bool LOCAL, int HOOKS>
-__global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
+__global__ __launch_bounds__(256) void k_twoshot_direct(const uint32_t arr, const Launch a)
 {
+    raise_arrival_first<LOCAL, HOOKS>(arr);
     // The first arrival poll goes out with the launch record's loads: most
     // workgroups of this large grid start after the arrival writers (parts
     // 0..7, dispatched first), so it usually finds the flags and saves a
@@ -1346,7 +1379,7 @@ __global__ __launch_bounds__(256) void k_twoshot_direct(const Launch a)
     load_seq(a, c);
     const Ctl ctl{a.ctl};
     start_delay(a, c);
-    raise_arrival<LOCAL>(a, c);
+    raise_arrival_late<LOCAL, HOOKS>(a, c);
     // Every input is read after the arrival wait, the rank's own too: with
     // the prologue down to one launch-record round and the sequence load,
     // the flags arrive about when loads could first be issued, and loading
@@ -2337,6 +2370,10 @@ __global__ __launch_bounds__(256) void k_step_end(uint32_t *ctl, uint32_t calls,
             __hip_atomic_store(ctl + CTL_ARRIVE + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __threadfence();
     }
+    // the arrival words restart with every step (their values are positions
+    // in the step)
+    for (uint32_t i = threadIdx.x; i < 32u * (uint32_t)XCDS; i += blockDim.x)
+        __hip_atomic_store(ctl + CTL_ARRIVE + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t s = __hip_atomic_load(ctl + CTL_SEQ, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2458,6 +2495,11 @@ hipError_t launch_ar(int kind, bool f32, bool local, int gw, const Launch &a, ui
     const void *fn = kernel_for(kind, (int)a.n_ranks, f32, local, gw, hooks_of(a));
     if (fn == nullptr || (a.parts & ((1u << a.xshift) - 1u)) != 0u)
         return hipErrorInvalidValue;
+    if (kind == K_TWOSHOT_DIRECT || kind == K_ONESHOT_DIRECT) {
+        uint32_t arr = a.rbase + 1u;        // the call's arrival value, first argument
+        void *args2[] = {(void *)&arr, (void *)&a};
+        return hipLaunchKernel(fn, grid_of(a), dim3(threads), args2, 0, stream);
+    }
     void *args[] = {(void *)&a};
     return hipLaunchKernel(fn, grid_of(a), dim3(threads), args, 0, stream);
 }
