@@ -364,9 +364,10 @@ int ar_set_watchdog(uint32_t budget_us);
  * "vLLM 分布式推理核心" page, section 一).  Enqueues one tiny kernel on
  * `stream` that advances the device's round sequence by the rounds of the
  * step's calls and its call count by their number, so that the flags of a
- * captured hipGraph's replays never repeat; resets the host epoch counter to
- * 0.  Buffer parity follows the global round number, so a step may hold any
- * number of calls.  When the round sequence passes 0xF0000000 the kernel
+ * captured hipGraph's replays never repeat, and clears the arrival words of
+ * the in-place kinds (whose values are positions within the step); resets
+ * the host epoch counter to 0.  Buffer parity follows the global round
+ * number, so a step may hold any number of calls.  When the round sequence passes 0xF0000000 the kernel
  * clears every flag word and restarts it at 0.  A step holds at most 2^27
  * rounds (ar_allreduce refuses a call beyond that).
  * Errors: AR_ERR_NOT_INIT, AR_ERR_HIP.
