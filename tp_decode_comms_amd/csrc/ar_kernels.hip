@@ -214,22 +214,25 @@ __device__ __forceinline__ void begin(const Launch &a, Ctx0 &c)
     // (the rank's own input pointer included, whose address depends only on
     // blockIdx.y) behind a single wait.
     // (blockDim.x is read from the launch's hidden arguments, so it is one
-    // of them.)
+    // of them; so is the watchdog budget, which the first poll loop reads:
+    // loaded there, its scalar load was waited for with the LDS accesses
+    // after the first poll -- 8 x 16 KiB LL 2.37-2.38 -> 2.34 us, 8 x 512
+    // KiB LL128 two-shot 4.37 -> 4.31, same box.)
     // (The sequence words come with them: their address is a constant.)
     const u32x2 sq = seq_words();
     if constexpr (HOOKS == 2)
         asm volatile("" ::"s"(a.in[c.rank]), "s"(a.out), "s"(a.ctl), "s"(a.n), "s"(a.n_ranks),
                      "s"(a.epoch), "s"(a.rbase), "s"(a.parts), "s"(a.slice), "s"(a.xshift),
                      "s"(a.delays), "s"(a.ts), "s"(a.ts_slots), "s"(a.ts_stride),
-                     "s"(a.ts_phases), "s"(sq), "s"(blockDim.x));
+                     "s"(a.ts_phases), "s"(sq), "s"(blockDim.x), "s"(a.watchdog_ticks));
     else if constexpr (HOOKS == 1)
         asm volatile("" ::"s"(a.in[c.rank]), "s"(a.out), "s"(a.ctl), "s"(a.n), "s"(a.n_ranks),
                      "s"(a.epoch), "s"(a.rbase), "s"(a.parts), "s"(a.slice), "s"(a.xshift),
-                     "s"(a.ts), "s"(a.ts_slots), "s"(a.ts_stride), "s"(sq), "s"(blockDim.x));
+                     "s"(a.ts), "s"(a.ts_slots), "s"(a.ts_stride), "s"(sq), "s"(blockDim.x), "s"(a.watchdog_ticks));
     else
         asm volatile("" ::"s"(a.in[c.rank]), "s"(a.out), "s"(a.ctl), "s"(a.n), "s"(a.n_ranks),
                      "s"(a.epoch), "s"(a.rbase), "s"(a.parts), "s"(a.slice), "s"(a.xshift),
-                     "s"(sq), "s"(blockDim.x));
+                     "s"(sq), "s"(blockDim.x), "s"(a.watchdog_ticks));
     c.seq = sq.x;
     c.calls = sq.y;
     c.part = (blockIdx.z << a.xshift) + lo;
