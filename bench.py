@@ -386,7 +386,7 @@ def stream_run(torch, ar, wl, algo, proto, calls, steps, warmup):
         ar.destroy()
 
 
-def bench_floor(torch, steps):
+def bench_floor(torch, ar, steps):
     """A 160-node graph of minimal kernels (1-element fills): the launch floor."""
     t = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     stream = torch.cuda.Stream()
@@ -408,7 +408,30 @@ def bench_floor(torch, steps):
             ev[s][1].record(stream)
     torch.cuda.synchronize()
     us = [a.elapsed_time(b) * 1000.0 / CALLS_PER_STEP for a, b in ev]
-    return {"us_per_node_p50": pct(us, 50), "what": "160-node hipGraph of 1-element fill kernels"}
+    return {"us_per_node_p50": pct(us, 50), "what": "160-node hipGraph of 1-element fill kernels",
+            "flag_hop": bench_flag_hop(torch, ar)}
+
+
+def bench_flag_hop(torch, ar, rounds=2000, reps=5):
+    """The one-way flag hop between two workgroups (include/ar_ping.h), inside
+    one XCD's L2 and across two XCDs at device scope: the median over `reps`
+    kernels of `rounds` round trips each."""
+    out = torch.zeros(5, dtype=torch.int64, device="cuda:0")
+    res = {}
+    for name, cross in (("xcd_local", 0), ("cross_xcd", 1)):
+        hops, xcds = [], None
+        for _ in range(reps):
+            ar.flag_ping(rounds, cross, out)
+            torch.cuda.synchronize()
+            v = out.tolist()
+            if v[1] or v[4]:
+                raise RuntimeError("flag ping (%s): a wait ran out of its budget" % name)
+            xcds = (v[2], v[3])
+            hops.append(v[0] * 0.01 / (2 * rounds))        # 100 MHz ticks -> us, one way
+        res[name] = {"one_way_us": round(pct(hops, 50), 4), "rounds": rounds, "reps": reps,
+                     "xcds": list(xcds),
+                     "placement_ok": (xcds[0] != xcds[1]) if cross else (xcds[0] == xcds[1])}
+    return res
 
 
 def bench_bandwidth(torch, ar, wl, calls, warmup, algo, proto, label, exact=True, graph_calls=160,
@@ -1002,7 +1025,7 @@ def main():
     lat = None
     if only in ("all", "latency"):
         log("launch floor")
-        legs.run("floor", lambda: bench_floor(torch, args.steps))
+        legs.run("floor", lambda: bench_floor(torch, ar, args.steps))
         log("16 KiB/rank latency: %d steps x 160 calls" % args.steps)
         wl2 = Workload(torch, 2, 4)
         lat = legs.run("latency_16k", lambda: graph_run(torch, ar, wl2, ONE, LL, CALLS_PER_STEP,
@@ -1211,13 +1234,26 @@ def main():
                                       cr["graph_us_per_call"] / line["roofline"]["avg_launch_us"], 4)}
     fl = results.get("floor")
     if lat is not None and fl is not None and "us_per_node_p50" in fl:
-        # the latency kernel is bound by the launch floor plus its in-XCD
-        # hops, not by HBM: how close the call is to an empty graph node
-        f = fl["us_per_node_p50"]
-        line["latency_floor"] = {"bound": "launch", "floor_us": round(f, 4),
+        # the latency kernel is bound by the launch floor plus a flag hop
+        # between workgroups, not by HBM: an empty graph node plus one
+        # one-way hop inside an XCD's L2 (the layout the call runs in); the
+        # cross-XCD call against the node plus a device-scope hop
+        node = fl["us_per_node_p50"]
+        hop = fl["flag_hop"]["xcd_local"]["one_way_us"]
+        hop_x = fl["flag_hop"]["cross_xcd"]["one_way_us"]
+        f = node + hop
+        line["latency_floor"] = {"bound": "launch + flag hop", "floor_us": round(f, 4),
+                                 "graph_node_us": round(node, 4), "flag_hop_us": hop,
                                  "achieved_us": line["value"],
                                  "frac": round(f / line["value"], 4),
-                                 "kernel_work_us": round(line["value"] - f, 4)}
+                                 "kernel_work_us": round(line["value"] - f, 4),
+                                 "flag_hop_cross_xcd_us": hop_x}
+        xl = results.get("latency_16k_cross_xcd")
+        if isinstance(xl, dict) and "event_us_per_call" in xl:
+            fx = node + hop_x
+            line["latency_floor"]["cross_xcd"] = {
+                "floor_us": round(fx, 4), "achieved_us": round(xl["event_us_per_call"]["p50"], 4),
+                "frac": round(fx / xl["event_us_per_call"]["p50"], 4)}
     line["cpu_baseline"] = cpu
     line["parity_ok"] = parity_ok(results)
     line["failed_legs"] = sorted(k for k, r in results.items()

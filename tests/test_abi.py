@@ -94,3 +94,9 @@ def test_gemv_validation_without_device(lib):
     assert lib.ar_copy(4104, 8192, 16, None) == a.AR_ERR_INVALID          # unaligned source
     assert lib.ar_copy(4096, 4096 + 16, 32, None) == a.AR_ERR_INVALID     # overlap
     assert lib.ar_copy(1 << 40, 1 << 41, 1 << 31, None) == a.AR_ERR_INVALID   # too large
+    # the flag hop: round count, output pointer and placement are checked first
+    assert lib.ar_flag_ping(0, 0, 4096, None) == a.AR_ERR_INVALID                # no rounds
+    assert lib.ar_flag_ping((1 << 20) + 1, 0, 4096, None) == a.AR_ERR_INVALID    # too many
+    assert lib.ar_flag_ping(10, 0, None, None) == a.AR_ERR_INVALID               # no output
+    assert lib.ar_flag_ping(10, 1, 4100, None) == a.AR_ERR_INVALID               # unaligned
+    assert lib.ar_flag_ping(10, 2, 4096, None) == a.AR_ERR_INVALID               # placement

@@ -12,7 +12,7 @@ from .ar import (  # noqa: F401
     AR_SCOPE_AUTO, AR_SCOPE_DEVICE, AR_SCOPE_CROSS_XCD,
     ArError, lib, lib_path, init, destroy, allreduce, allreduce_noalloc, allreduce_f32_debug,
     allreduce_add_rmsnorm,
-    add_rmsnorm, gemv, copy, set_options,
+    add_rmsnorm, gemv, copy, flag_ping, set_options,
     set_launch, set_scope, set_staging, set_watchdog, step_end, set_sequence, set_delays, set_timestamps,
     get_status, reset,
     query, strerror, EXPORTED_SYMBOLS,

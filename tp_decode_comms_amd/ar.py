@@ -58,6 +58,8 @@ _SIGS = {
                               _c_size, _c_size, _c_int, _c_int, _c_vp]),
     # include/ar_copy.h (the bandwidth reference)
     "ar_copy": (_c_int, [_c_vp, _c_vp, _c_size, _c_vp]),
+    # include/ar_ping.h (the flag hop, the latency floor beside a graph node)
+    "ar_flag_ping": (_c_int, [_c_u32, _c_int, _c_vp, _c_vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -188,6 +190,14 @@ def copy(src, dst, nbytes, stream=None, check=True):
     bandwidth reference of the large AllReduce calls."""
     rc = lib().ar_copy(_ptr(src), _ptr(dst), int(nbytes), _stream_handle(stream))
     return _check("ar_copy", rc) if check else rc
+
+
+def flag_ping(rounds, cross_xcd, out, stream=None, check=True):
+    """`rounds` round trips of a flag between two workgroups (include/ar_ping.h);
+    `out` is a device buffer of 5 int64 words that receives the clock ticks,
+    the two statuses and the two workgroups' XCDs."""
+    rc = lib().ar_flag_ping(int(rounds), int(cross_xcd), _ptr(out), _stream_handle(stream))
+    return _check("ar_flag_ping", rc) if check else rc
 
 
 def allreduce_f32_debug(rank_bufs, out_f32, n, epoch, stream=None, check=True):

@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtpdc_ar.so")
-SOURCES = ["ar_kernels.hip", "ar_host.hip", "gemv.hip", "norm.hip", "copy.hip"]
+SOURCES = ["ar_kernels.hip", "ar_host.hip", "gemv.hip", "norm.hip", "copy.hip", "ping.hip"]
 ARCH = os.environ.get("TPDC_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
