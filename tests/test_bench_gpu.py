@@ -30,4 +30,11 @@ def test_bench_runs_to_its_json_line():
     assert line["value"] is not None and line["value"] > 0
     assert line["config"]["workload"]
     assert line["roofline"]["bound"] == "hbm" and 0 < line["roofline"]["frac"] < 1
-    assert "latency_floor" in line
+    fl = line["latency_floor"]
+    # the floor is a graph node plus one flag hop inside an XCD's L2; the
+    # device-scope hop between XCDs is the longer one
+    assert fl["floor_us"] == pytest.approx(fl["graph_node_us"] + fl["flag_hop_us"], abs=1e-3)
+    assert 0 < fl["flag_hop_us"] < fl["flag_hop_cross_xcd_us"]
+    assert 0 < fl["frac"] < 1.5
+    hops = line["results"]["floor"]["flag_hop"]
+    assert hops["xcd_local"]["placement_ok"] and hops["cross_xcd"]["placement_ok"]
